@@ -1,0 +1,438 @@
+"""fp64 CPU oracle for one batch-1 decode step -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+
+Only the tests, the bench's CPU-baseline leg and the package's smoke check may import this
+module. It shares no code with the HIP path: it is plain NumPy in float64, written from
+the textbook definitions of the operations.
+
+What the pages fix, and what they leave open
+--------------------------------------------
+The pages describe a persistent, tile-scheduled decode engine and name the fused
+operations it runs, but print no formula, listing or worked example:
+  * "Static Compilation for LLM Inference: from ASIC Graph Compile to Persistent Engine
+    Kernel", section 5.4 (table of XLA/TVM assumptions): at batch 1 every GEMM is
+    memory-bound and Norm+GEMM+Attention should be fused; the fused kernel
+    rmsnorm_projx_wqkvia is named there.
+  * same page, section 5.3 and the section 11 reference list: FlashAttention's IO-aware
+    tiling with online softmax (FA1) and sequence-dimension parallelism (FA2), the basis
+    of the split-K decode attention.
+  * same page, section 5.5 (static compile vs dynamic serving table): the KV cache grows
+    by one position per token; MoE routing is input dependent.
+  * the tile-ai/TileRT audit page, paragraphs on the fused-op names
+    (RMSNormProjxWqkvia, UnProjOAllReduce, ExpertDownAllReduce,
+    ExpertSelectUpGateSiLU), on batch 1 (max_batch_size = 1, FlashSparseMLA) and on
+    TokenSpeed's MLA q-head folding.
+So every formula below is the plain standard reading (Llama-style pre-norm GQA with
+rotate-half RoPE and SwiGLU; DeepSeek-style MLA with a latent KV cache and a sigmoid
+top-k router). The readings taken where the pages are silent:
+  R1  per-layer math: the textbook forms in this file.
+  R2  the cache holds kv_len past positions; the step writes slot kv_len and attends over
+      kv_len+1 positions; the RoPE position of the new token is p = kv_len.
+  R3  cached K (and the MLA k_pe) are stored post-RoPE; cached MLA c is stored normalised.
+  R4  RoPE pairs (i, i + d/2) ("rotate half"), theta_i = theta^(-2i/d), no scaling.
+  R7  softmax scale 1/sqrt(head_dim) (GQA) and 1/sqrt(qk_nope + qk_rope) (MLA).
+  R8  GQA head h reads KV head floor(h * n_kv / n_q).
+  R9  router: sigma = sigmoid(W_r x); selection on sigma + bias; top-k with ties to the
+      lower index; weights sigma_T / sum(sigma_T); shared experts with weight 1.
+  R11 the KV cache is bf16: the appended entry is the new k/v (or c/k_pe) rounded to
+      bf16 (round to nearest even), and attention reads the cache, new slot included.
+  R13 MLA/MoE configs have no LM head and no final norm: the output is the last hidden
+      state.
+Where floating point decides an integer (the top-k set), the decision is taken in fp32,
+the precision of the GPU kernel: fp64 router logits are rounded to fp32, and the
+sigmoid, the bias add and the comparisons run in fp32.
+
+Weights are passed as a callable W(name, index=None) returning a NumPy array: uint16 bf16
+bit patterns for bf16 tensors, float32 for the router bias. `index` selects one expert of
+a stacked expert tensor, so the MoE oracle reads only the experts it routes to.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------
+# bf16 bit patterns <-> float64
+# ----------------------------------------------------------------------------------------
+
+
+def widen_bf16(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (a bf16 is the top half of an fp32)."""
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        b = b.view(np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Round float64 values to the nearest bf16 (ties to even), directly from float64.
+
+    A bf16 keeps 8 significant bits. With x = m * 2^e, 0.5 <= |m| < 1 (frexp), the nearest
+    bf16 is round_half_even(m * 2^8) * 2^(e-8). Returns (values as float64, uint16 bits).
+    Valid for finite values inside the normal bf16 range, which is all this oracle needs.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    v = np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # np.round: half to even
+    bits = (v.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return v, bits
+
+
+def _w64(W: Callable, name: str, index=None) -> np.ndarray:
+    a = W(name) if index is None else W(name, index)
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return widen_bf16(a)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------
+# the operations (textbook definitions)
+# ----------------------------------------------------------------------------------------
+
+
+def rmsnorm(u: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm(u; g) = u / sqrt(mean(u^2) + eps) * g, mean over the whole vector.
+
+    The pages name the fused RMSNorm + QKV op ("Static Compilation ..." section 5.4;
+    the TileRT audit page's RMSNormProjxWqkvia) without a formula; this is the standard one.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    return u / math.sqrt(float(np.mean(u * u)) + eps) * g
+
+
+def rope(u: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of one head vector u (length d) at position pos.
+
+    theta_i = theta^(-2i/d) for i < d/2; the pair (u_i, u_{i+d/2}) is rotated by pos*theta_i:
+        u'_i       = u_i cos - u_{i+d/2} sin
+        u'_{i+d/2} = u_{i+d/2} cos + u_i sin
+    (reading R4; the pages do not define RoPE).
+    """
+    u = np.asarray(u, dtype=np.float64)
+    d = u.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = pos * theta ** (-2.0 * i / d)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = u[..., :half], u[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def linear(Wm: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y = W x with W row-major [out][in] (a library matrix-vector product)."""
+    return Wm @ x
+
+
+def linear_bits(W: Callable, name: str, x: np.ndarray, index=None,
+                rows_per_block: int = 1 << 16) -> np.ndarray:
+    """y = W x for a bf16 matrix given by name; rows are widened a block at a time so a
+    1 GB LM head never needs its whole fp64 copy in memory. Each output element is still
+    one full dot product of its row."""
+    bits = W(name) if index is None else W(name, index)
+    bits = np.asarray(bits)
+    n = bits.shape[0]
+    if n <= rows_per_block:
+        return linear(widen_bf16(bits), x)
+    out = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, rows_per_block):
+        r1 = min(n, r0 + rows_per_block)
+        out[r0:r1] = linear(widen_bf16(bits[r0:r1]), x)
+    return out
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """softmax over the last axis; the max is subtracted first (a value-preserving shift)."""
+    s = np.asarray(s, dtype=np.float64)
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """One query against n keys: o = softmax(scale * K q) V.  K [n][d], V [n][dv]."""
+    p = softmax(scale * (K @ q))
+    return p @ V
+
+
+def attend_partial(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Online-softmax partial of one chunk of positions (FlashAttention's tiling,
+    "Static Compilation ..." section 5.3): m = max s, l = sum e^(s-m), a = sum e^(s-m) V."""
+    s = scale * (K @ q)
+    m = float(np.max(s))
+    e = np.exp(s - m)
+    return m, float(np.sum(e)), e @ V
+
+
+def merge_partials(parts: Sequence[Tuple[float, float, np.ndarray]]) -> np.ndarray:
+    """Merge split-K partials: o = sum_c e^(m_c-M) a_c / sum_c e^(m_c-M) l_c, M = max m_c."""
+    M = max(p[0] for p in parts)
+    num = sum(math.exp(m - M) * a for (m, l, a) in parts)
+    den = sum(math.exp(m - M) * l for (m, l, a) in parts)
+    return num / den
+
+
+def attend_split(q, K, V, scale, bounds: Sequence[int]) -> np.ndarray:
+    """Split-K (flash-decoding) attention: positions cut at `bounds` (0 = b0 < ... < bk = n),
+    one partial per chunk, then the merge. Equal to attend() in exact arithmetic."""
+    parts = [attend_partial(q, K[a:b], V[a:b], scale) for a, b in zip(bounds[:-1], bounds[1:])]
+    return merge_partials(parts)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z / (1 + e^-z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, x: np.ndarray):
+    """SwiGLU FFN: a = silu(W_g x) * (W_u x); y = W_d a. Returns (a, y)."""
+    a = silu(Wg @ x) * (Wu @ x)
+    return a, Wd @ a
+
+
+def route(r: np.ndarray, bias: np.ndarray, top_k: int):
+    """Sigmoid top-k router (reading R9), decision in fp32.
+
+    sigma = sigmoid(r); z = sigma + bias; T = indices of the top_k largest z, ties to the
+    lower index, listed by decreasing z; w_e = sigma_e / sum_{T} sigma. The selection is
+    made on fp32 values (fp64 logits rounded to fp32, then fp32 sigmoid and add), as the
+    GPU makes it. The weights are computed in fp64.
+    Returns dict(sigma, z, topk, w, margin) where margin is the fp64 gap between the
+    k-th and (k+1)-th largest z (inf when top_k equals the expert count).
+    """
+    r = np.asarray(r, dtype=np.float64)
+    b = np.asarray(bias, dtype=np.float64)
+    r32 = r.astype(np.float32)
+    one = np.float32(1.0)
+    sig32 = one / (one + np.exp(-r32))
+    z32 = (sig32 + b.astype(np.float32)).astype(np.float32)
+    order = np.argsort(-z32, kind="stable")          # stable: equal z keep lower index first
+    T = order[:top_k].astype(np.int64)
+    sigma = 1.0 / (1.0 + np.exp(-r))
+    z = sigma + b
+    zs = np.sort(z)[::-1]
+    margin = float(zs[top_k - 1] - zs[top_k]) if top_k < len(z) else float("inf")
+    w = sigma[T] / np.sum(sigma[T])
+    return {"sigma": sigma, "z": z, "z32": z32, "topk": T, "w": w, "margin": margin}
+
+
+# ----------------------------------------------------------------------------------------
+# layers
+# ----------------------------------------------------------------------------------------
+
+
+def gqa_layer(cfg: dict, W: Callable, l: int, x: np.ndarray, kv_layer, kv_len: int):
+    """One pre-norm GQA decoder layer at position p = kv_len.
+
+    kv_layer: bf16 bits [2][n_kv][>=kv_len][head_dim] (positions [0, kv_len) are read).
+    Returns (x_next, trace dict).
+    """
+    p = f"layers.{l}."
+    d, nq, nkv, hd = cfg["hidden"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    eps, theta = cfg["rms_eps"], cfg["rope_theta"]
+    pos = kv_len
+    t: Dict[str, np.ndarray] = {"x_in": x}
+    xn = rmsnorm(x, _w64(W, p + "attn_norm"), eps)
+    t["xn"] = xn
+    q = linear_bits(W, p + "wq", xn).reshape(nq, hd)
+    k = linear_bits(W, p + "wk", xn).reshape(nkv, hd)
+    v = linear_bits(W, p + "wv", xn).reshape(nkv, hd)
+    q = rope(q, pos, theta)
+    k = rope(k, pos, theta)
+    t["q"], t["k_new"], t["v_new"] = q.reshape(-1), k.reshape(-1), v.reshape(-1)
+    k16, kbits = round_to_bf16(k)
+    v16, vbits = round_to_bf16(v)
+    t["k_new_bits"], t["v_new_bits"] = kbits.reshape(-1), vbits.reshape(-1)
+    kvl = np.asarray(kv_layer)
+    scale = 1.0 / math.sqrt(hd)
+    o = np.empty((nq, hd))
+    for g in range(nkv):
+        Kc = np.concatenate([widen_bf16(kvl[0, g, :kv_len]), k16[g][None, :]], axis=0)
+        Vc = np.concatenate([widen_bf16(kvl[1, g, :kv_len]), v16[g][None, :]], axis=0)
+        for h in range(nq):
+            if (h * nkv) // nq == g:
+                o[h] = attend(q[h], Kc, Vc, scale)
+    t["attn"] = o.reshape(-1)
+    h_ = x + linear_bits(W, p + "wo", t["attn"])
+    t["h"] = h_
+    hn = rmsnorm(h_, _w64(W, p + "ffn_norm"), eps)
+    t["hn"] = hn
+    a = silu(linear_bits(W, p + "w_gate", hn)) * linear_bits(W, p + "w_up", hn)
+    t["ffn_act"] = a
+    f = linear_bits(W, p + "w_down", a)
+    t["ffn_out"] = f
+    xo = h_ + f
+    t["x_out"] = xo
+    return xo, t
+
+
+def mla_attention(cfg: dict, W: Callable, l: int, xn: np.ndarray, kv_layer, kv_len: int,
+                  absorbed_trace: bool = True):
+    """MLA attention of one layer (naive definition), plus the absorbed-form intermediates.
+
+    Definition (naive): with latent cache rows [c_j || kpe_j],
+        k_{h,j} = [W_UK,h c_j || kpe_j],  v_{h,j} = W_UV,h c_j,
+        s_{h,j} = q_h . k_{h,j} / sqrt(qk_nope + qk_rope),  o_h = sum_j softmax(s_h)_j v_{h,j}.
+    Absorbed form (same value, what a decode kernel computes; TokenSpeed's q-head folding on
+    the TileRT audit page treats all heads as rows of one contraction over the latent):
+        qa_h = W_UK,h^T q_nope,h;  s_{h,j} = (qa_h . c_j + q_rope,h . kpe_j)/sqrt(...);
+        ol_h = sum_j p_{h,j} c_j;  o_h = W_UV,h ol_h.
+    Returns (o [n_heads*v_head], trace).
+    """
+    p = f"layers.{l}."
+    nh = cfg["n_q_heads"]
+    ql, kl = cfg["q_lora_rank"], cfg["kv_lora_rank"]
+    dn, dr, dv = cfg["qk_nope"], cfg["qk_rope"], cfg["v_head"]
+    eps, theta = cfg["rms_eps"], cfg["rope_theta"]
+    pos = kv_len
+    t: Dict[str, np.ndarray] = {}
+    cq_raw = linear_bits(W, p + "wq_a", xn)
+    cq = rmsnorm(cq_raw, _w64(W, p + "q_norm"), eps)
+    t["cq_raw"], t["cq"] = cq_raw, cq
+    qf = linear_bits(W, p + "wq_b", cq).reshape(nh, dn + dr)
+    q_nope = qf[:, :dn]
+    q_rope = rope(qf[:, dn:], pos, theta)
+    t["q_nope"], t["q_rope"] = q_nope.reshape(-1), q_rope.reshape(-1)
+    a = linear_bits(W, p + "wkv_a", xn)
+    t["kv_a"] = a
+    c_new = rmsnorm(a[:kl], _w64(W, p + "kv_norm"), eps)
+    kpe_new = rope(a[kl:], pos, theta)
+    t["c_new"], t["kpe_new"] = c_new, kpe_new
+    ent16, ent_bits = round_to_bf16(np.concatenate([c_new, kpe_new]))
+    t["kv_new_bits"] = ent_bits
+    kvl = np.asarray(kv_layer)
+    lat = np.concatenate([widen_bf16(kvl[:kv_len]), ent16[None, :]], axis=0)  # [n+1][kl+dr]
+    C, KPE = lat[:, :kl], lat[:, kl:]
+    Wuk = _w64(W, p + "w_uk")   # [nh][dn][kl]
+    Wuv = _w64(W, p + "w_uv")   # [nh][dv][kl]
+    scale = 1.0 / math.sqrt(dn + dr)
+    o = np.empty((nh, dv))
+    for h in range(nh):
+        Kh = np.concatenate([C @ Wuk[h].T, KPE], axis=1)     # [n+1][dn+dr]
+        Vh = C @ Wuv[h].T                                     # [n+1][dv]
+        o[h] = attend(np.concatenate([q_nope[h], q_rope[h]]), Kh, Vh, scale)
+    t["attn"] = o.reshape(-1)
+    if absorbed_trace:
+        qa = np.einsum("hdc,hd->hc", Wuk, q_nope)             # [nh][kl]
+        ol = np.empty((nh, kl))
+        for h in range(nh):
+            s = scale * (C @ qa[h] + KPE @ q_rope[h])
+            ol[h] = softmax(s) @ C
+        t["q_abs"] = qa.reshape(-1)
+        t["o_lat"] = ol.reshape(-1)
+    return o.reshape(-1), t
+
+
+def mla_attention_absorbed(cfg: dict, W: Callable, l: int, q_nope, q_rope, lat) -> np.ndarray:
+    """Absorbed-form MLA attention core from given q parts and latent rows lat [n][kl+dr]."""
+    p = f"layers.{l}."
+    nh, kl = cfg["n_q_heads"], cfg["kv_lora_rank"]
+    dn, dr = cfg["qk_nope"], cfg["qk_rope"]
+    Wuk = _w64(W, p + "w_uk")
+    Wuv = _w64(W, p + "w_uv")
+    C, KPE = lat[:, :kl], lat[:, kl:]
+    scale = 1.0 / math.sqrt(dn + dr)
+    qn = np.asarray(q_nope).reshape(nh, dn)
+    qr = np.asarray(q_rope).reshape(nh, dr)
+    out = []
+    for h in range(nh):
+        qa = Wuk[h].T @ qn[h]
+        pr = softmax(scale * (C @ qa + KPE @ qr[h]))
+        out.append(Wuv[h] @ (pr @ C))
+    return np.concatenate(out)
+
+
+def moe_ffn(cfg: dict, W: Callable, l: int, hn: np.ndarray):
+    """MoE FFN (reading R9): y = SwiGLU_shared(hn) + sum_{e in T} w_e SwiGLU_e(hn)."""
+    p = f"layers.{l}."
+    k = cfg["top_k"]
+    t: Dict[str, np.ndarray] = {}
+    r = linear_bits(W, p + "router", hn)
+    rt = route(r, np.asarray(W(p + "router_bias"), dtype=np.float64), k)
+    t["router_logits"] = r
+    t["topk"] = rt["topk"]
+    t["topk_w"] = rt["w"]
+    t["topk_margin"] = np.array([rt["margin"]])
+    a_s, y_s = swiglu(_w64(W, p + "shared.w_gate"), _w64(W, p + "shared.w_up"),
+                      _w64(W, p + "shared.w_down"), hn)
+    t["shared_act"], t["shared_out"] = a_s, y_s
+    y = y_s.copy()
+    acts = []
+    for e, we in zip(rt["topk"], rt["w"]):
+        a_e, y_e = swiglu(_w64(W, p + "experts.w_gate", int(e)), _w64(W, p + "experts.w_up", int(e)),
+                          _w64(W, p + "experts.w_down", int(e)), hn)
+        acts.append(a_e)
+        y = y + we * y_e
+    t["expert_act"] = np.concatenate(acts) if acts else np.zeros(0)
+    return y, t
+
+
+def mla_layer(cfg: dict, W: Callable, l: int, x: np.ndarray, kv_layer, kv_len: int):
+    """One MLA layer (config arch "mla": dense SwiGLU FFN; "moe": MoE FFN)."""
+    p = f"layers.{l}."
+    eps = cfg["rms_eps"]
+    t: Dict[str, np.ndarray] = {"x_in": x}
+    xn = rmsnorm(x, _w64(W, p + "attn_norm"), eps)
+    t["xn"] = xn
+    o, ta = mla_attention(cfg, W, l, xn, kv_layer, kv_len)
+    t.update(ta)
+    h_ = x + linear_bits(W, p + "wo", o)
+    t["h"] = h_
+    hn = rmsnorm(h_, _w64(W, p + "ffn_norm"), eps)
+    t["hn"] = hn
+    if cfg["arch"] == "mla":
+        a = silu(linear_bits(W, p + "w_gate", hn)) * linear_bits(W, p + "w_up", hn)
+        t["ffn_act"] = a
+        f = linear_bits(W, p + "w_down", a)
+    else:
+        f, tm = moe_ffn(cfg, W, l, hn)
+        t.update(tm)
+    t["ffn_out"] = f
+    xo = h_ + f
+    t["x_out"] = xo
+    return xo, t
+
+
+def layer(cfg: dict, W: Callable, l: int, x: np.ndarray, kv_layer, kv_len: int):
+    if cfg["arch"] == "gqa":
+        return gqa_layer(cfg, W, l, x, kv_layer, kv_len)
+    return mla_layer(cfg, W, l, x, kv_layer, kv_len)
+
+
+def head(cfg: dict, W: Callable, x: np.ndarray) -> Dict[str, np.ndarray]:
+    """Final RMSNorm + LM head (configs with a vocabulary); otherwise the output is x."""
+    if cfg.get("vocab", 0) > 0:
+        xn = rmsnorm(x, _w64(W, "final_norm"), cfg["rms_eps"])
+        return {"final_xn": xn, "out": linear_bits(W, "lm_head", xn)}
+    return {"out": np.asarray(x, dtype=np.float64)}
+
+
+def forward(cfg: dict, W: Callable, x_bits, kv, kv_len: Optional[int] = None,
+            layers: Optional[Sequence[int]] = None):
+    """One decode step. x_bits: bf16 bits [hidden]; kv: indexable by layer, giving that
+    layer's cache bits (see gqa_layer / mla_layer). Returns {"layers": [trace...], "out": ...}.
+
+    `layers` limits the run to a prefix of the stack (for bounded timing samples); the head
+    is applied only when the whole stack ran.
+    """
+    n = cfg["kv_len"] if kv_len is None else kv_len
+    L = cfg["n_layers"]
+    todo = list(range(L)) if layers is None else list(layers)
+    x = widen_bf16(x_bits)
+    traces: List[Dict[str, np.ndarray]] = []
+    for l in todo:
+        x, t = layer(cfg, W, l, x, kv[l], n)
+        traces.append(t)
+    res = {"layers": traces, "x_final": x}
+    if len(todo) == L:
+        res.update(head(cfg, W, x))
+    return res
+
+
+def dict_weights(d: Dict[str, np.ndarray]) -> Callable:
+    """Adapt a dict of arrays to the W(name, index=None) accessor."""
+    def W(name, index=None):
+        a = d[name]
+        return a if index is None else a[index]
+    return W

@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for batch-1 decode, shared by the oracle side and the HIP side.
+
+This module holds model shapes, the canonical tensor list (names, shapes, dtypes) and
+seeded random generators. It holds none of the decode arithmetic: nothing here
+normalises, rotates, multiplies or attends.
+
+The tensor list is the layout contract of the decode library: every matrix is bf16,
+row-major [out_features][in_features]; norm gains are bf16 [dim]; the MoE router bias is
+fp32 [n_routed]; per-head MLA up-projections are [heads][rows][kv_lora_rank].
+
+Input recipe (the pages run trained DeepSeek/GLM/MiMo checkpoints, which are not
+available; these shapes stand in for them):
+  * linear weights ~ N(0, weight_std) rounded to bf16 (round-to-nearest-even);
+  * norm gains = 1 ("ones") or ~ N(mean, std) for the gain-pinning variants;
+  * cached K/V (or latent c||k_pe) ~ N(0, kv_std) on positions [0, kv_len), slot kv_len = 0;
+  * x ~ N(0, x_std) in bf16; router bias ~ N(0, router_bias_std) in fp32.
+All tensors come from one torch.Generator seeded once, drawn in the canonical order.
+"""
+from __future__ import annotations
+
+import json
+import os
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+BF16 = "bf16"
+FP32 = "fp32"
+
+
+def load_configs() -> Dict[str, dict]:
+    with open(os.path.join(_HERE, "configs.json")) as f:
+        return json.load(f)["configs"]
+
+
+def get_config(name: str) -> dict:
+    cfgs = load_configs()
+    if name not in cfgs:
+        raise KeyError(f"unknown config {name!r}; known: {sorted(cfgs)}")
+    cfg = dict(cfgs[name])
+    cfg["name"] = name
+    return cfg
+
+
+@dataclass(frozen=True)
+class TensorSpec:
+    name: str
+    shape: Tuple[int, ...]
+    dtype: str          # "bf16" or "fp32"
+    init: str           # "weight", "gain", "router_bias"
+
+    @property
+    def numel(self) -> int:
+        n = 1
+        for d in self.shape:
+            n *= d
+        return n
+
+    @property
+    def nbytes(self) -> int:
+        return self.numel * (2 if self.dtype == BF16 else 4)
+
+
+def _mla_attn_specs(cfg: dict, p: str) -> List[TensorSpec]:
+    d = cfg["hidden"]
+    nh = cfg["n_q_heads"]
+    ql, kl = cfg["q_lora_rank"], cfg["kv_lora_rank"]
+    dn, dr, dv = cfg["qk_nope"], cfg["qk_rope"], cfg["v_head"]
+    return [
+        TensorSpec(p + "attn_norm", (d,), BF16, "gain"),
+        TensorSpec(p + "wq_a", (ql, d), BF16, "weight"),
+        TensorSpec(p + "q_norm", (ql,), BF16, "gain"),
+        TensorSpec(p + "wq_b", (nh * (dn + dr), ql), BF16, "weight"),
+        TensorSpec(p + "wkv_a", (kl + dr, d), BF16, "weight"),
+        TensorSpec(p + "kv_norm", (kl,), BF16, "gain"),
+        TensorSpec(p + "w_uk", (nh, dn, kl), BF16, "weight"),
+        TensorSpec(p + "w_uv", (nh, dv, kl), BF16, "weight"),
+        TensorSpec(p + "wo", (d, nh * dv), BF16, "weight"),
+    ]
+
+
+def weight_specs(cfg: dict) -> List[TensorSpec]:
+    """Canonical ordered tensor list of a config (the order weights are bound in)."""
+    arch = cfg["arch"]
+    d = cfg["hidden"]
+    out: List[TensorSpec] = []
+    for l in range(cfg["n_layers"]):
+        p = f"layers.{l}."
+        if arch == "gqa":
+            nq, nkv, hd = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+            out += [
+                TensorSpec(p + "attn_norm", (d,), BF16, "gain"),
+                TensorSpec(p + "wq", (nq * hd, d), BF16, "weight"),
+                TensorSpec(p + "wk", (nkv * hd, d), BF16, "weight"),
+                TensorSpec(p + "wv", (nkv * hd, d), BF16, "weight"),
+                TensorSpec(p + "wo", (d, nq * hd), BF16, "weight"),
+            ]
+        else:
+            out += _mla_attn_specs(cfg, p)
+        out.append(TensorSpec(p + "ffn_norm", (d,), BF16, "gain"))
+        if arch in ("gqa", "mla"):
+            f = cfg["ffn"]
+            out += [
+                TensorSpec(p + "w_gate", (f, d), BF16, "weight"),
+                TensorSpec(p + "w_up", (f, d), BF16, "weight"),
+                TensorSpec(p + "w_down", (d, f), BF16, "weight"),
+            ]
+        elif arch == "moe":
+            e, ef, ns = cfg["n_routed"], cfg["expert_ffn"], cfg["n_shared"]
+            out += [
+                TensorSpec(p + "router", (e, d), BF16, "weight"),
+                TensorSpec(p + "router_bias", (e,), FP32, "router_bias"),
+                TensorSpec(p + "experts.w_gate", (e, ef, d), BF16, "weight"),
+                TensorSpec(p + "experts.w_up", (e, ef, d), BF16, "weight"),
+                TensorSpec(p + "experts.w_down", (e, d, ef), BF16, "weight"),
+                TensorSpec(p + "shared.w_gate", (ns * ef, d), BF16, "weight"),
+                TensorSpec(p + "shared.w_up", (ns * ef, d), BF16, "weight"),
+                TensorSpec(p + "shared.w_down", (d, ns * ef), BF16, "weight"),
+            ]
+        else:
+            raise ValueError(f"unknown arch {arch!r}")
+    if cfg.get("vocab", 0) > 0:
+        out.append(TensorSpec("final_norm", (d,), BF16, "gain"))
+        out.append(TensorSpec("lm_head", (cfg["vocab"], d), BF16, "weight"))
+    return out
+
+
+def kv_shape(cfg: dict, kv_len: Optional[int] = None) -> Tuple[int, ...]:
+    """Cache layout: GQA [L][2][n_kv][kv_len+1][head_dim]; MLA/MoE [L][kv_len+1][kv_lora+rope]."""
+    n = cfg["kv_len"] if kv_len is None else kv_len
+    if cfg["arch"] == "gqa":
+        return (cfg["n_layers"], 2, cfg["n_kv_heads"], n + 1, cfg["head_dim"])
+    return (cfg["n_layers"], n + 1, cfg["kv_lora_rank"] + cfg["qk_rope"])
+
+
+def x_shape(cfg: dict) -> Tuple[int, ...]:
+    return (cfg["hidden"],)
+
+
+def out_shape(cfg: dict) -> Tuple[int, ...]:
+    return (cfg["vocab"],) if cfg.get("vocab", 0) > 0 else (cfg["hidden"],)
+
+
+def weight_bytes(cfg: dict) -> int:
+    return sum(s.nbytes for s in weight_specs(cfg))
+
+
+# ----------------------------------------------------------------------------------------
+# seeded generation (torch is used only as a random-number source and a container)
+# ----------------------------------------------------------------------------------------
+
+def _bf16_randn(torch, shape, std, gen, device, mean=0.0, chunk_elems=1 << 28):
+    """N(mean, std) drawn in fp32 then rounded to bf16, generated in row chunks."""
+    t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = t.view(-1)
+    n = flat.numel()
+    i = 0
+    while i < n:
+        m = min(chunk_elems, n - i)
+        tmp = torch.randn(m, generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            tmp.mul_(std)
+        if mean != 0.0:
+            tmp.add_(mean)
+        flat[i:i + m].copy_(tmp)
+        del tmp
+        i += m
+    return t
+
+
+def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = None):
+    """Return (weights: dict name->tensor, x: bf16 tensor, kv: bf16 tensor) on `device`.
+
+    Every tensor is drawn from one generator seeded with `seed`, in canonical order:
+    weights (weight_specs order), then the KV cache, then x.
+    """
+    import torch
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed))
+    init = cfg["init"]
+    weights = {}
+    for s in weight_specs(cfg):
+        if s.init == "weight":
+            weights[s.name] = _bf16_randn(torch, s.shape, init["weight_std"], gen, dev)
+        elif s.init == "gain":
+            g = init["gain"]
+            if g == "ones":
+                weights[s.name] = torch.ones(s.shape, dtype=torch.bfloat16, device=dev)
+            else:
+                weights[s.name] = _bf16_randn(torch, s.shape, g["std"], gen, dev, mean=g["mean"])
+        elif s.init == "router_bias":
+            weights[s.name] = torch.randn(s.shape, generator=gen, device=dev,
+                                          dtype=torch.float32) * init["router_bias_std"]
+        else:
+            raise ValueError(s.init)
+    n = cfg["kv_len"] if kv_len is None else kv_len
+    kvs = kv_shape(cfg, n)
+    kv = torch.zeros(kvs, dtype=torch.bfloat16, device=dev)
+    if n > 0:
+        if cfg["arch"] == "gqa":
+            kv[:, :, :, :n, :].copy_(_bf16_randn(torch, kvs[:3] + (n, kvs[4]),
+                                                 init["kv_std"], gen, dev))
+        else:
+            kv[:, :n, :].copy_(_bf16_randn(torch, (kvs[0], n, kvs[2]), init["kv_std"], gen, dev))
+    x = _bf16_randn(torch, x_shape(cfg), init["x_std"], gen, dev)
+    return weights, x, kv
+
+
+def bf16_bits(t):
+    """A bf16 torch tensor as a numpy uint16 array of its bit patterns (host copy)."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")
