@@ -1,0 +1,156 @@
+"""Benchmark of the batch-1 decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8b_4k] [--no-cpu-baseline]
+
+A step is one whole decode step (all layers, one kernel launch) over synthetic bf16
+weights and KV cache already resident in HBM. Prints ONE JSON line.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "bs=1 decode latency (us/token) + achieved HBM GB/s as % of 8 TB/s peak"
+WORKLOADS = {
+    "8b_4k": "Llama-3-8B-shaped decoder (32 layers, hidden 4096, 32x128 q heads, 8 KV heads, SwiGLU 14336, "
+             "vocab 128256), batch 1, one decode token over a 4096-position KV cache",
+    "8b_32k": "Llama-3-8B-shaped decoder, batch 1, one decode token over a 32768-position KV cache",
+    "tiny": "tiny decoder (2 layers, hidden 256), batch 1, KV 128",
+}
+
+
+def cpu_baseline(cfg, w, x, kv):
+    """The fp64 oracle, as it stands, timed on a bounded sample of the same step: layer 0 and
+    the final norm + LM head; the per-token figure extrapolates layer 0 to all layers."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    def W(name, index=None):
+        t = w[name] if index is None else w[name][index]
+        return workloads.bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+    cache = {}
+
+    def Wc(name, index=None):
+        k = (name, index)
+        if k not in cache:
+            cache[k] = W(name, index)
+        return cache[k]
+
+    n = cfg["kv_len"]
+    xb = workloads.bf16_bits(x)
+    kv0 = workloads.bf16_bits(kv[0])
+    # host copies first (not timed): the oracle's timed region starts from host bf16 arrays
+    for s in workloads.weight_specs(cfg):
+        if s.name.startswith("layers.0.") or s.name in ("final_norm", "lm_head"):
+            Wc(s.name)
+    t0 = time.perf_counter()
+    xo, _ = oracle.layer(cfg, Wc, 0, oracle.widen_bf16(xb), kv0, n)
+    t1 = time.perf_counter()
+    has_head = cfg.get("vocab", 0) > 0
+    if has_head:
+        oracle.head(cfg, Wc, xo)
+    t2 = time.perf_counter()
+    per_token = (t1 - t0) * cfg["n_layers"] + (t2 - t1)
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": per_token * 1e6, "unit": "us/token", "cores": int(cores), "kind": "oracle",
+            "sample": f"layer 0 of {cfg['n_layers']} ({(t1 - t0):.2f} s) extrapolated x{cfg['n_layers']}"
+                      + (f" + final norm and LM head ({(t2 - t1):.2f} s)" if has_head else "")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="8b_4k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this engine has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from persistent_tile_scheduled_amd.engine import DecodeEngine
+
+    cfg = workloads.get_config(args.config)
+    print(f"[bench] generating {args.config} inputs on cuda:0", file=sys.stderr, flush=True)
+    w, x, kv = workloads.generate(cfg, seed=args.seed, device="cuda")
+    eng = DecodeEngine(cfg, w)
+    alg_bytes = eng.sizes["algorithmic_bytes_per_step"]
+    stream = eng.stream
+    for _ in range(args.warmup):
+        eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        eng.step(x, kv)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.status()
+    per = [a.elapsed_time(b) * 1e3 for a, b in ev]  # us per launch
+    mean_us = statistics.mean(per)
+    med_us = statistics.median(per)
+    us_per_token = wall * 1e6 / args.steps
+    achieved = alg_bytes / (mean_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, w, x, kv)
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_per_token, 2),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_token / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 KV and input)",
+        "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
+                   "kv_len": cfg["kv_len"], "batch": 1},
+        "tokens_per_s": round(1e6 / us_per_token, 1),
+        "kernel_us_mean": round(mean_us, 2),
+        "kernel_us_median": round(med_us, 2),
+        "kernel_us_p10": round(sorted(per)[len(per) // 10], 2),
+        "kernel_us_p90": round(sorted(per)[(len(per) * 9) // 10], 2),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/* dec.h -- C ABI of a batch-1 LLM decode step run as ONE persistent, tile-scheduled
+ * kernel on an AMD Instinct MI355X (gfx950).
+ *
+ * What the calls implement. The pages behind this library ("Static Compilation for LLM
+ * Inference: from ASIC Graph Compile to Persistent Engine Kernel", sections 1, 5.6 and 6;
+ * the tile-ai/TileRT audit page, blog-vs-code table; the TileRT talk transcript, section on
+ * breaking kernel boundaries) describe a decode step that is statically compiled ahead of
+ * time: every shape is known, the whole layer stack is unrolled into tile-level tasks,
+ * and one long-lived kernel executes them, starting each task as soon as its producers
+ * are done instead of launching one kernel per operator. The TileRT audit page also fixes
+ * the interface habits followed here: prepare once and then run per token, weights bound
+ * before the first run, batch fixed at 1 (max_batch_size = 1), an externally produced KV
+ * cache passed in as a raw buffer (inject_cache), and any shape change meaning a rebuild.
+ *
+ * Call sequence:
+ *   dec_plan_create(shape, kv_len, &plan)     -- host-only planning (no device memory)
+ *   dec_plan_sizes / dec_plan_weight_desc     -- what the caller must allocate
+ *   dec_plan_bind(plan, weights, n, ws, bytes, stream)  -- once
+ *   dec_step(plan, x, kv, out, stream)        -- once per token: exactly one kernel launch
+ *   dec_plan_status(plan, stream)             -- optional: sync and read the device status
+ *   dec_plan_destroy(plan)
+ *
+ * Ownership: the caller allocates and frees every device buffer (weights, workspace, x,
+ * kv, out). The plan keeps the raw pointers given to bind until destroy or the next bind.
+ * The library never frees or allocates device memory. The only allocation the library
+ * makes is the opaque host-side plan object.
+ *
+ * Errors: every call validates synchronously and returns a negative dec_status on error
+ * without aborting; dec_last_error() then holds a message (thread-local). dec_step is
+ * asynchronous: a device-side failure (a dependency wait that exceeds the watchdog) is
+ * recorded in a sticky status word in the workspace; dec_plan_status reports it and
+ * dec_plan_reset clears it.
+ *
+ * Concurrency: the steps of one plan must be serialised (one stream, or explicit
+ * ordering): its dependency counters and epoch live in its workspace. Different plans
+ * with different workspaces may run concurrently.
+ *
+ * The `stream` arguments are hipStream_t values passed as void* (NULL = default stream).
+ */
+#ifndef DEC_H_
+#define DEC_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DEC_ABI_VERSION 1
+
+typedef struct dec_plan dec_plan;   /* opaque, library-owned host object */
+
+typedef enum {
+  DEC_OK = 0,
+  DEC_E_INVAL = -1,      /* null pointer, bad index, wrong abi_version, wrong weight count */
+  DEC_E_SHAPE = -2,      /* unsupported or inconsistent model shape */
+  DEC_E_CAPACITY = -3,   /* a size exceeds what the plan supports (kv_len, workspace) */
+  DEC_E_DEVICE = -4,     /* current device is not gfx950 / no device */
+  DEC_E_OCCUPANCY = -5,  /* the persistent grid cannot be co-resident on this device */
+  DEC_E_HIP = -6,        /* a HIP runtime call failed (message holds hipGetErrorString) */
+  DEC_E_TIMEOUT = -7,    /* device watchdog: a dependency wait exceeded its budget */
+  DEC_E_UNBOUND = -8,    /* dec_step before dec_plan_bind */
+  DEC_E_PLAN = -9        /* planner self-validation failed (internal error) */
+} dec_status;
+
+typedef enum {
+  DEC_ARCH_GQA = 0,      /* Llama-style pre-norm decoder: GQA attention + SwiGLU FFN */
+  DEC_ARCH_MLA = 1,      /* latent-KV (MLA) attention + dense SwiGLU FFN */
+  DEC_ARCH_MOE = 2       /* latent-KV (MLA) attention + routed/shared expert FFN */
+} dec_arch;
+
+/* Model shape (plain data, no pointers). Fields unused by an arch must be 0.
+ *   GQA: n_q_heads, n_kv_heads, head_dim, ffn.
+ *   MLA: n_q_heads, q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_head, ffn.
+ *   MOE: the MLA fields (ffn = 0) plus n_routed, n_shared, top_k, expert_ffn.
+ * vocab > 0 adds a final RMSNorm + LM head (out = fp32 logits); vocab == 0 means
+ * out = the last hidden state (fp32, no final norm). Batch is always 1. */
+typedef struct dec_model_shape {
+  int32_t abi_version;   /* must be DEC_ABI_VERSION */
+  int32_t arch;          /* dec_arch */
+  int32_t n_layers, hidden, vocab;
+  int32_t n_q_heads, n_kv_heads, head_dim, ffn;
+  int32_t q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_head;
+  int32_t n_routed, n_shared, top_k, expert_ffn;
+  float rms_eps;
+  int32_t reserved0;
+  double rope_theta;
+} dec_model_shape;
+
+/* Description of the device the plan is built for. dec_plan_create fills it from the
+ * current HIP device; dec_plan_create_for takes it explicitly (host-only planning). */
+typedef struct dec_device_info {
+  int32_t gfx_arch;            /* 950 for gfx950 */
+  int32_t n_cu;                /* compute units (256 on MI355X) */
+  int32_t n_xcd;               /* chiplets (8 on MI355X); workgroup w runs on XCD w % n_xcd */
+  int32_t lds_bytes_per_cu;    /* 163840 on gfx950 */
+  int32_t max_threads_per_cu;  /* waves per CU * 64 */
+  int32_t reserved0;
+} dec_device_info;
+
+typedef enum { DEC_DTYPE_BF16 = 0, DEC_DTYPE_FP32 = 1, DEC_DTYPE_I32 = 2 } dec_dtype;
+
+typedef struct dec_tensor_desc {
+  char name[64];           /* e.g. "layers.3.wq" */
+  int32_t dtype;           /* dec_dtype */
+  int32_t rank;            /* 1..4 */
+  int64_t dims[4];         /* row-major; unused dims = 0 */
+  int64_t bytes;
+} dec_tensor_desc;
+
+typedef struct dec_sizes {
+  int64_t x_bytes;         /* bf16 [hidden] */
+  int64_t kv_bytes;        /* see dec_step */
+  int64_t out_bytes;       /* fp32 [vocab] or fp32 [hidden] */
+  int64_t workspace_bytes; /* library-owned device scratch, caller-allocated, 256-B aligned */
+  int64_t weight_bytes;    /* sum over the weight list */
+  int64_t algorithmic_bytes_per_step; /* weights (active experts only) + KV positions read */
+} dec_sizes;
+
+/* One statically planned task, as the planner emitted it (for coverage checks). */
+typedef struct dec_task_desc {
+  int32_t id, type, layer, stage;
+  int32_t wg, xcd, list_pos;
+  int32_t unit_begin, unit_end;   /* rows / units / positions the task owns (type-specific) */
+  int32_t aux0, aux1;             /* type-specific: group, split, head, ... */
+  int32_t n_deps, dep_first;      /* counters waited on (see dec_plan_deps) */
+  int32_t signal;                 /* counter incremented on completion (-1: none) */
+  int32_t signal2;                /* second counter (ticket-merge tasks: merged counter) */
+  int32_t reserved0;
+} dec_task_desc;
+
+/* A named fp32 (or i32) buffer inside the workspace holding an intermediate of the last
+ * step (per-layer activations, router choice, task log). Offsets are in bytes. */
+typedef struct dec_buffer_desc {
+  char name[64];
+  int32_t dtype;
+  int32_t reserved0;
+  int64_t offset;
+  int64_t count;           /* elements */
+} dec_buffer_desc;
+
+/* ---- planning (host only; no device memory is touched) ---- */
+
+/* Plan for the current HIP device. Errors: SHAPE, CAPACITY (kv_len < 0 or too large),
+ * DEVICE (not gfx950), OCCUPANCY, INVAL (null). */
+dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, struct dec_plan** out);
+/* Plan for an explicitly described device (CPU-only testing and cross-planning). */
+dec_status dec_plan_create_for(const dec_model_shape* shape, int64_t kv_len,
+                               const dec_device_info* dev, struct dec_plan** out);
+dec_status dec_plan_destroy(struct dec_plan* plan);     /* NULL is a no-op */
+
+/* The weight list in bind order (the layout contract). */
+int64_t dec_plan_n_weights(const struct dec_plan* plan);
+dec_status dec_plan_weight_desc(const struct dec_plan* plan, int64_t i, dec_tensor_desc* out);
+dec_status dec_plan_sizes(const struct dec_plan* plan, dec_sizes* out);
+
+/* Introspection of the static schedule. */
+int64_t dec_plan_n_tasks(const struct dec_plan* plan);
+dec_status dec_plan_tasks(const struct dec_plan* plan, dec_task_desc* buf, int64_t cap, int64_t* n);
+/* counters: buf[2*i] = counter index, buf[2*i+1] = increments per step, for dep entry i */
+int64_t dec_plan_n_deps(const struct dec_plan* plan);
+dec_status dec_plan_deps(const struct dec_plan* plan, int32_t* buf, int64_t cap, int64_t* n);
+int64_t dec_plan_n_counters(const struct dec_plan* plan);
+int64_t dec_plan_n_buffers(const struct dec_plan* plan);
+dec_status dec_plan_buffer_desc(const struct dec_plan* plan, int64_t i, dec_buffer_desc* out);
+/* Grid the step launches: n_wg workgroups of `threads` threads, `lds` bytes of LDS each. */
+dec_status dec_plan_grid(const struct dec_plan* plan, int32_t* n_wg, int32_t* threads, int32_t* lds);
+
+/* ---- device side ---- */
+
+/* Bind caller-owned weight buffers (n == dec_plan_n_weights, in weight_desc order, each
+ * 16-byte aligned) and a workspace of >= workspace_bytes (256-byte aligned). Uploads the
+ * task table and zeroes counters/status on `stream` (asynchronously). Errors: INVAL, HIP. */
+dec_status dec_plan_bind(struct dec_plan* plan, const void* const* weights, int64_t n,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Run one decode step: ONE kernel launch on `stream`.
+ *   x   : bf16 [hidden], the new token's input hidden state (read only).
+ *   kv  : bf16 cache. GQA: [n_layers][2][n_kv_heads][kv_len+1][head_dim] (K then V);
+ *         MLA/MOE: [n_layers][kv_len+1][kv_lora_rank + qk_rope] (c || k_pe).
+ *         Positions [0, kv_len) are read; slot kv_len of every layer is written with the
+ *         new token's post-RoPE k / v (resp. normalised c || post-RoPE k_pe).
+ *   out : fp32 [vocab] logits, or fp32 [hidden] last hidden state when vocab == 0.
+ * Errors: UNBOUND, INVAL (null or misaligned), HIP (launch failure). */
+dec_status dec_step(struct dec_plan* plan, const void* x, void* kv, void* out, void* stream);
+
+/* Synchronise `stream` and read the sticky device status word: DEC_OK or DEC_E_TIMEOUT
+ * (the failing task id is in dec_last_error()). */
+dec_status dec_plan_status(struct dec_plan* plan, void* stream);
+/* Re-zero counters, epoch and status (after a timeout). */
+dec_status dec_plan_reset(struct dec_plan* plan, void* stream);
+/* Device watchdog budget for one dependency wait, in microseconds (default 2 000 000). */
+dec_status dec_plan_set_watchdog(struct dec_plan* plan, int64_t microseconds);
+
+const char* dec_last_error(void);
+/* Describe the current HIP device (gfx arch, CU/XCD counts, LDS). */
+dec_status dec_device_query(dec_device_info* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DEC_H_ */

@@ -1,0 +1,347 @@
+// api.cpp -- the C ABI declared in include/dec.h: plan lifecycle, binding, the per-token
+// launch and status reporting. The planner is host-only; this file is the only place that
+// calls the HIP runtime.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dec.h"
+#include "planner.h"
+
+extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream);
+extern "C" hipError_t dec_engine_occupancy(int lds_bytes, int* blocks_per_cu);
+
+struct dec_plan {
+  dec::PlanData P;
+  bool bound = false;
+  char* ws = nullptr;
+  std::vector<uint64_t> wptr;
+  dec::EngineArgs args{};
+  int64_t watchdog_us = 2000000;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+dec_status fail(dec_status s, const std::string& m) {
+  g_err = m;
+  return s;
+}
+
+dec_status hip_fail(hipError_t e, const char* what) {
+  return fail(DEC_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void fill_args(dec_plan* p) {
+  const dec::PlanData& P = p->P;
+  const dec_model_shape& s = P.shape;
+  dec::EngineArgs& a = p->args;
+  char* ws = p->ws;
+  a.ws = ws;
+  a.tasks = reinterpret_cast<const dec::TaskDesc*>(ws + P.off_tasks);
+  a.wg_begin = reinterpret_cast<const int32_t*>(ws + P.off_wgb);
+  a.deps = reinterpret_cast<const dec::DepEntry*>(ws + P.off_deps);
+  a.wptr = reinterpret_cast<const uint64_t*>(ws + P.off_wptr);
+  a.layers = reinterpret_cast<const dec::LayerDesc*>(ws + P.off_layers);
+  a.counters = reinterpret_cast<uint32_t*>(ws + P.off_counters);
+  a.ctl = reinterpret_cast<uint32_t*>(ws + P.off_ctl);
+  a.log = reinterpret_cast<dec::TaskLog*>(ws + P.off_log);
+  a.rope_cs = reinterpret_cast<const float*>(ws + P.off_rope);
+  a.act = reinterpret_cast<float*>(ws + P.off_act);
+  a.x = nullptr;
+  a.kv = nullptr;
+  a.out = nullptr;
+  a.watchdog_ticks = p->watchdog_us * 100;  // s_memrealtime runs at 100 MHz
+  a.arch = s.arch;
+  a.n_layers = s.n_layers;
+  a.hidden = s.hidden;
+  a.vocab = s.vocab;
+  a.nq = s.n_q_heads;
+  a.nkv = s.n_kv_heads;
+  a.hd = s.head_dim;
+  a.ffn = s.ffn;
+  a.ql = s.q_lora_rank;
+  a.kl = s.kv_lora_rank;
+  a.dn = s.qk_nope;
+  a.dr = s.qk_rope;
+  a.dv = s.v_head;
+  a.n_routed = s.n_routed;
+  a.n_shared = s.n_shared;
+  a.top_k = s.top_k;
+  a.eff = s.expert_ffn;
+  a.kv_len = (int32_t)P.kv_len;
+  a.n_wg = P.n_wg;
+  a.rope_half = P.rope_half;
+  a.w_final_norm = P.w_final_norm;
+  a.w_lm_head = P.w_lm_head;
+  a.x_final = P.x_final;
+  a.xs_floats = (int32_t)P.xs_floats;
+  a.eps = s.rms_eps;
+  a.attn_scale_log2 = P.attn_scale_log2;
+}
+
+void copy_name(char* dst, const std::string& s) {
+  std::memset(dst, 0, 64);
+  std::strncpy(dst, s.c_str(), 63);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dec_last_error(void) { return g_err.c_str(); }
+
+dec_status dec_device_query(dec_device_info* out) {
+  if (!out) return fail(DEC_E_INVAL, "null output");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t pr;
+  e = hipGetDeviceProperties(&pr, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  std::memset(out, 0, sizeof(*out));
+  int gfx = 0;
+  if (std::strncmp(pr.gcnArchName, "gfx", 3) == 0) gfx = (int)std::strtol(pr.gcnArchName + 3, nullptr, 10);
+  out->gfx_arch = gfx;
+  out->n_cu = pr.multiProcessorCount;
+  out->n_xcd = (pr.multiProcessorCount % 32 == 0 && pr.multiProcessorCount >= 32) ? pr.multiProcessorCount / 32 : 1;
+  out->lds_bytes_per_cu = (int32_t)pr.maxSharedMemoryPerMultiProcessor;
+  out->max_threads_per_cu = pr.maxThreadsPerMultiProcessor;
+  return DEC_OK;
+}
+
+dec_status dec_plan_create_for(const dec_model_shape* shape, int64_t kv_len, const dec_device_info* dev,
+                               dec_plan** out) {
+  if (!shape || !dev || !out) return fail(DEC_E_INVAL, "null argument");
+  *out = nullptr;
+  dec_plan* p = new dec_plan();
+  std::string err;
+  dec_status st = dec::build_plan(*shape, kv_len, *dev, &p->P, &err);
+  if (st != DEC_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *out = p;
+  return DEC_OK;
+}
+
+dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, dec_plan** out) {
+  if (!shape || !out) return fail(DEC_E_INVAL, "null argument");
+  dec_device_info dev;
+  dec_status st = dec_device_query(&dev);
+  if (st != DEC_OK) return st;
+  if (dev.gfx_arch != 950) return fail(DEC_E_DEVICE, "current device is gfx" + std::to_string(dev.gfx_arch) + ", need gfx950");
+  st = dec_plan_create_for(shape, kv_len, &dev, out);
+  if (st != DEC_OK) return st;
+  int per_cu = 0;
+  hipError_t e = dec_engine_occupancy((*out)->P.lds_bytes, &per_cu);
+  if (e != hipSuccess || per_cu < 1) {
+    dec_plan_destroy(*out);
+    *out = nullptr;
+    if (e != hipSuccess) return hip_fail(e, "occupancy query");
+    return fail(DEC_E_OCCUPANCY, "the engine kernel cannot be resident with the plan's LDS size");
+  }
+  return DEC_OK;
+}
+
+dec_status dec_plan_destroy(dec_plan* plan) {
+  delete plan;
+  return DEC_OK;
+}
+
+int64_t dec_plan_n_weights(const dec_plan* plan) { return plan ? (int64_t)plan->P.weights.size() : -1; }
+
+dec_status dec_plan_weight_desc(const dec_plan* plan, int64_t i, dec_tensor_desc* out) {
+  if (!plan || !out) return fail(DEC_E_INVAL, "null argument");
+  if (i < 0 || i >= (int64_t)plan->P.weights.size()) return fail(DEC_E_INVAL, "weight index out of range");
+  const dec::WeightSpec& w = plan->P.weights[i];
+  std::memset(out, 0, sizeof(*out));
+  copy_name(out->name, w.name);
+  out->dtype = w.dtype;
+  out->rank = (int32_t)w.dims.size();
+  for (size_t k = 0; k < w.dims.size() && k < 4; ++k) out->dims[k] = w.dims[k];
+  out->bytes = w.bytes;
+  return DEC_OK;
+}
+
+dec_status dec_plan_sizes(const dec_plan* plan, dec_sizes* out) {
+  if (!plan || !out) return fail(DEC_E_INVAL, "null argument");
+  const dec::PlanData& P = plan->P;
+  const dec_model_shape& s = P.shape;
+  out->x_bytes = (int64_t)s.hidden * 2;
+  if (s.arch == DEC_ARCH_GQA)
+    out->kv_bytes = (int64_t)s.n_layers * 2 * s.n_kv_heads * (P.kv_len + 1) * s.head_dim * 2;
+  else
+    out->kv_bytes = (int64_t)s.n_layers * (P.kv_len + 1) * (s.kv_lora_rank + s.qk_rope) * 2;
+  out->out_bytes = (int64_t)(s.vocab > 0 ? s.vocab : s.hidden) * 4;
+  out->workspace_bytes = P.ws_bytes;
+  out->weight_bytes = P.weight_bytes;
+  out->algorithmic_bytes_per_step = P.alg_bytes;
+  return DEC_OK;
+}
+
+int64_t dec_plan_n_tasks(const dec_plan* plan) { return plan ? (int64_t)plan->P.tasks.size() : -1; }
+
+dec_status dec_plan_tasks(const dec_plan* plan, dec_task_desc* buf, int64_t cap, int64_t* n) {
+  if (!plan || !n) return fail(DEC_E_INVAL, "null argument");
+  const dec::PlanData& P = plan->P;
+  *n = (int64_t)P.tasks.size();
+  if (!buf) return DEC_OK;
+  if (cap < *n) return fail(DEC_E_CAPACITY, "task buffer too small");
+  for (size_t i = 0; i < P.tasks.size(); ++i) {
+    const dec::TaskDesc& t = P.tasks[i];
+    dec_task_desc& d = buf[i];
+    std::memset(&d, 0, sizeof(d));
+    d.id = t.id;
+    d.type = t.type;
+    d.layer = t.layer;
+    d.stage = P.info[i].stage;
+    d.wg = P.info[i].wg;
+    d.xcd = P.info[i].wg % P.dev.n_xcd;
+    d.list_pos = P.info[i].list_pos;
+    d.unit_begin = t.u0;
+    d.unit_end = t.u1;
+    d.aux0 = t.a0;
+    d.aux1 = t.a1;
+    d.n_deps = t.dep_count;
+    d.dep_first = t.dep_first;
+    d.signal = t.signal;
+    d.signal2 = t.signal2;
+    d.reserved0 = t.a3;  // ticket-merge log id for attention splits
+  }
+  return DEC_OK;
+}
+
+int64_t dec_plan_n_deps(const dec_plan* plan) { return plan ? (int64_t)plan->P.deps.size() : -1; }
+
+dec_status dec_plan_deps(const dec_plan* plan, int32_t* buf, int64_t cap, int64_t* n) {
+  if (!plan || !n) return fail(DEC_E_INVAL, "null argument");
+  *n = (int64_t)plan->P.deps.size();
+  if (!buf) return DEC_OK;
+  if (cap < 2 * *n) return fail(DEC_E_CAPACITY, "dep buffer too small");
+  for (size_t i = 0; i < plan->P.deps.size(); ++i) {
+    buf[2 * i] = plan->P.deps[i].counter;
+    buf[2 * i + 1] = (int32_t)plan->P.deps[i].per_step;
+  }
+  return DEC_OK;
+}
+
+int64_t dec_plan_n_counters(const dec_plan* plan) { return plan ? (int64_t)plan->P.counter_total.size() : -1; }
+
+int64_t dec_plan_n_buffers(const dec_plan* plan) { return plan ? (int64_t)plan->P.buffers.size() : -1; }
+
+dec_status dec_plan_buffer_desc(const dec_plan* plan, int64_t i, dec_buffer_desc* out) {
+  if (!plan || !out) return fail(DEC_E_INVAL, "null argument");
+  if (i < 0 || i >= (int64_t)plan->P.buffers.size()) return fail(DEC_E_INVAL, "buffer index out of range");
+  const dec::BufferSpec& b = plan->P.buffers[i];
+  std::memset(out, 0, sizeof(*out));
+  copy_name(out->name, b.name);
+  out->dtype = b.dtype;
+  out->offset = b.offset;
+  out->count = b.count;
+  return DEC_OK;
+}
+
+dec_status dec_plan_grid(const dec_plan* plan, int32_t* n_wg, int32_t* threads, int32_t* lds) {
+  if (!plan || !n_wg || !threads || !lds) return fail(DEC_E_INVAL, "null argument");
+  *n_wg = plan->P.n_wg;
+  *threads = plan->P.threads;
+  *lds = plan->P.lds_bytes;
+  return DEC_OK;
+}
+
+dec_status dec_plan_bind(dec_plan* plan, const void* const* weights, int64_t n, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (!plan || !weights || !workspace) return fail(DEC_E_INVAL, "null argument");
+  dec::PlanData& P = plan->P;
+  if (n != (int64_t)P.weights.size())
+    return fail(DEC_E_INVAL, "expected " + std::to_string(P.weights.size()) + " weights, got " + std::to_string(n));
+  if (workspace_bytes < P.ws_bytes) return fail(DEC_E_CAPACITY, "workspace smaller than dec_sizes.workspace_bytes");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DEC_E_INVAL, "workspace not 256-byte aligned");
+  plan->wptr.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    if (!weights[i]) return fail(DEC_E_INVAL, "weight " + P.weights[i].name + " is null");
+    if (reinterpret_cast<uintptr_t>(weights[i]) % 16) return fail(DEC_E_INVAL, "weight " + P.weights[i].name + " not 16-byte aligned");
+    plan->wptr[i] = reinterpret_cast<uint64_t>(weights[i]);
+  }
+  // host image of the table region [0, off_act): control words, counters, tasks, lists,
+  // deps, weight pointers, layer descriptors, RoPE table, task log
+  std::vector<char> img((size_t)P.off_act, 0);
+  std::memcpy(img.data() + P.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(dec::TaskDesc));
+  std::memcpy(img.data() + P.off_wgb, P.wg_begin.data(), P.wg_begin.size() * 4);
+  if (!P.deps.empty()) std::memcpy(img.data() + P.off_deps, P.deps.data(), P.deps.size() * sizeof(dec::DepEntry));
+  std::memcpy(img.data() + P.off_wptr, plan->wptr.data(), plan->wptr.size() * 8);
+  std::memcpy(img.data() + P.off_layers, P.layers.data(), P.layers.size() * sizeof(dec::LayerDesc));
+  std::memcpy(img.data() + P.off_rope, P.rope_cs.data(), P.rope_cs.size() * 4);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "upload plan tables");
+  if (P.ws_bytes > P.off_act) {
+    e = hipMemsetAsync(static_cast<char*>(workspace) + P.off_act, 0, (size_t)(P.ws_bytes - P.off_act), s);
+    if (e != hipSuccess) return hip_fail(e, "clear activations");
+  }
+  e = hipStreamSynchronize(s);  // the host image is freed on return
+  if (e != hipSuccess) return hip_fail(e, "bind synchronise");
+  plan->ws = static_cast<char*>(workspace);
+  fill_args(plan);
+  plan->bound = true;
+  return DEC_OK;
+}
+
+dec_status dec_step(dec_plan* plan, const void* x, void* kv, void* out, void* stream) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (!plan->bound) return fail(DEC_E_UNBOUND, "dec_step before dec_plan_bind");
+  if (!x || !kv || !out) return fail(DEC_E_INVAL, "null x/kv/out");
+  if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
+  plan->args.x = static_cast<const uint16_t*>(x);
+  plan->args.kv = static_cast<uint16_t*>(kv);
+  plan->args.out = static_cast<float*>(out);
+  plan->args.watchdog_ticks = plan->watchdog_us * 100;
+  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");
+    return hip_fail(e, "engine launch");
+  }
+  return DEC_OK;
+}
+
+dec_status dec_plan_status(dec_plan* plan, void* stream) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (!plan->bound) return fail(DEC_E_UNBOUND, "plan not bound");
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "status synchronise");
+  uint32_t st[4] = {0, 0, 0, 0};
+  e = hipMemcpy(st, plan->ws + plan->P.off_ctl + dec::CTL_STATUS * 4, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "status read");
+  if (st[0] == 7u)
+    return fail(DEC_E_TIMEOUT, "watchdog: task " + std::to_string(st[1]) + " timed out waiting on counter " +
+                                   std::to_string(st[2]) + " (value " + std::to_string(st[3]) + ")");
+  if (st[0] != 0u) return fail(DEC_E_PLAN, "unknown device status " + std::to_string(st[0]));
+  return DEC_OK;
+}
+
+dec_status dec_plan_reset(dec_plan* plan, void* stream) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (!plan->bound) return fail(DEC_E_UNBOUND, "plan not bound");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dec::PlanData& P = plan->P;
+  hipError_t e = hipMemsetAsync(plan->ws + P.off_ctl, 0, (size_t)(P.off_tasks - P.off_ctl), s);  // ctl + counters
+  if (e == hipSuccess) e = hipMemsetAsync(plan->ws + P.off_log, 0, (size_t)(P.off_act - P.off_log), s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reset");
+  return DEC_OK;
+}
+
+dec_status dec_plan_set_watchdog(dec_plan* plan, int64_t microseconds) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (microseconds < 1) return fail(DEC_E_INVAL, "watchdog must be >= 1 us");
+  plan->watchdog_us = microseconds;
+  return DEC_OK;
+}
+
+}  // extern "C"

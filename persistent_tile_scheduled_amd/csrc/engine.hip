@@ -1,0 +1,766 @@
+// engine.hip -- the persistent, tile-scheduled decode engine for gfx950 (MI355X).
+//
+// One launch runs a whole batch-1 decode step. Every workgroup (one per CU, 8 wave64)
+// walks its statically planned task list. A task
+//   1. issues the loads of its static operand (weight rows, cached K/V) into registers,
+//   2. waits on its dependency counters (one wave polls with agent-scope loads; a workgroup
+//      barrier does not drain the loads issued in step 1, so they stay in flight),
+//   3. stages its dynamic input vector in LDS (with RMSNorm where the step needs it),
+//   4. streams the rest of its rows with a double-buffered register ring, reducing each
+//      row with wave-wide sums,
+//   5. runs its epilogue (RoPE + KV append, SwiGLU, residual), stores, and signals its
+//      counter after an agent-scope release.
+// This is the pages' execution model: ahead-of-time compiled tile tasks in one persistent
+// engine kernel that start as soon as their producers finish ("Static Compilation for LLM
+// Inference ...", sections 1, 5.6 and 6; the TileRT talk's section on breaking kernel
+// boundaries), with the cross-chiplet synchronisation done through memory with
+// release/acquire and atomic adds (same page, section 7.4, on AMD's buffer_wbl2 /
+// flat_atomic_add with scope bits). The first page's section 5.2 notes that a megakernel's
+// register budget is the maximum over its task types and leaves one wave per SIMD; this
+// engine runs two waves per SIMD and hides HBM latency with many outstanding 16-byte loads
+// per lane instead of occupancy. Batch-1 GEMVs are memory-bound (section 5.4), so the row
+// dot products run on the vector ALUs in fp32, not on MFMA.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan_types.h"
+
+namespace dec {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ small helpers
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// wave-uniform value (lets the compiler keep it in SGPRs and branch on it with scalar code)
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int wave_id() { return uni((int)(threadIdx.x >> 6)); }
+
+// 16-byte non-temporal load through the global (not flat) address space, so it counts only
+// against vmcnt and never against the LDS counter
+typedef const u4 __attribute__((address_space(1)))* gu4p;
+__device__ __forceinline__ u4 ldg_nt(const void* p) { return __builtin_nontemporal_load((gu4p)p); }
+
+__device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xfu;
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+// sum within aligned groups of `w` lanes (w a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int w) {
+  for (int m = 1; m < w; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ uint64_t uni64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <class T>
+__device__ __forceinline__ const T* wp(const EngineArgs& A, int idx) {
+  return reinterpret_cast<const T*>(uni64(A.wptr[idx]));
+}
+__device__ __forceinline__ float* actp(const EngineArgs& A, int off) { return A.act + off; }
+
+// ------------------------------------------------------------------ per-workgroup state
+
+struct Blk {
+  uint32_t epoch;
+  uint32_t t_ready;
+  int* flags;     // LDS: [0] wait status, [1] ticket result
+  float* xs;      // LDS: staged input vector
+  float* ys;      // LDS: per-row results of the current task
+  float* scr;     // LDS: reduction scratch
+  uint64_t* rowp; // LDS: row pointers of the current GEMV task
+  int* xoffp;     // LDS: per-row input offsets of the current GEMV task
+};
+
+// Wait until every dependency counter of `t` has reached this step's target. Wave 0 polls
+// (one lane per counter); the other waves wait at the barrier with their loads in flight.
+// Returns false when the step is being aborted (watchdog).
+__device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int status = 0;
+    if (t.dep_count > 0) {
+      const uint32_t* cp = A.ctl;  // any valid address for idle lanes
+      uint32_t target = 0;
+      if (lane < t.dep_count) {
+        const DepEntry d = A.deps[t.dep_first + lane];
+        cp = A.counters + (size_t)d.counter * kCounterStride;
+        target = (b.epoch + 1u) * d.per_step;
+      }
+      const uint64_t t0 = now();
+      uint32_t spins = 0;
+      while (true) {
+        const bool ok = (lane >= t.dep_count) || ((int32_t)(ld_agent(cp) - target) >= 0);
+        if (__all(ok)) break;
+        if ((++spins & 15u) == 0u) {
+          const uint32_t ab = ld_agent(A.ctl + CTL_ABORT);
+          const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
+          if (ab || late) {
+            if (!ab && lane == 0) {
+              uint32_t zero = 0;
+              if (__hip_atomic_compare_exchange_strong(A.ctl + CTL_STATUS, &zero, 7u, __ATOMIC_RELAXED,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                st_agent(A.ctl + CTL_STATUS + 1, (uint32_t)t.id);
+                st_agent(A.ctl + CTL_STATUS + 2, (uint32_t)A.deps[t.dep_first].counter);
+                st_agent(A.ctl + CTL_STATUS + 3, ld_agent(A.counters + (size_t)A.deps[t.dep_first].counter * kCounterStride));
+              }
+              st_agent(A.ctl + CTL_ABORT, 1u);
+            }
+            status = 1;
+            break;
+          }
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (status == 0) acquire();
+    }
+    if (lane == 0) b.flags[0] = status;
+  }
+  __syncthreads();
+  b.t_ready = (uint32_t)now();
+  return b.flags[0] == 0;
+}
+
+// All stores of the task are issued before the barrier; thread 0's agent-scope release
+// makes them visible before the counter increment.
+__device__ __forceinline__ void signal(const EngineArgs& A, int ctr) {
+  __syncthreads();
+  if (threadIdx.x == 0 && ctr >= 0) {
+    release();
+    add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
+  }
+}
+
+__device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
+
+__device__ __forceinline__ float block_sum(Blk& b, float v) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) b.scr[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) s += b.scr[i];
+  return s;
+}
+
+// Stage K values (fp32 `s32` or bf16 `s16`) into xs[0, K), zero xs[K, padK). With a gain,
+// apply RMSNorm: x / sqrt(mean(x^2) + eps) * g (eps inside the sqrt, mean over K).
+__device__ __forceinline__ void stage_vec(Blk& b, const float* s32, const uint16_t* s16, int K, int padK,
+                                          const uint16_t* gain, float eps) {
+  float ss = 0.f;
+  for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
+    f4 v;
+    if (s32) {
+      v = *(const f4*)(s32 + i);
+    } else {
+      const uint2 u = *(const uint2*)(s16 + i);
+      v = f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+    }
+    *(f4*)(b.xs + i) = v;
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  for (int i = K + threadIdx.x; i < padK; i += kThreads) b.xs[i] = 0.f;
+  if (gain) {
+    const float tot = block_sum(b, ss);
+    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+    for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
+      const uint2 g = *(const uint2*)(gain + i);
+      f4 v = *(f4*)(b.xs + i);
+      v.x *= inv * bf_lo(g.x);
+      v.y *= inv * bf_hi(g.x);
+      v.z *= inv * bf_lo(g.y);
+      v.w *= inv * bf_hi(g.y);
+      *(f4*)(b.xs + i) = v;
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ streaming row GEMV
+
+constexpr int NB = 8;  // 16-byte chunks per batch per lane (8 KB per wave per batch)
+
+// Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
+// columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
+// xs[xoff[j] + c].
+struct Stream {
+  const uint64_t* rowp;
+  const int* xoffp;
+  int jb, K, cpr, lane;
+  int lj, lc;
+  const uint16_t* lrow;
+  int cj, cc, cxo;
+  float acc0, acc1;
+
+  __device__ __forceinline__ void init(const uint64_t* rp, const int* xp, int ja, int jb_, int K_, int lane_) {
+    rowp = rp;
+    xoffp = xp;
+    jb = jb_;
+    K = K_;
+    lane = lane_;
+    cpr = (K + kChunkCols - 1) / kChunkCols;
+    lj = ja;
+    lc = 0;
+    lrow = (ja < jb) ? (const uint16_t*)uni64(rowp[ja]) : nullptr;
+    cj = ja;
+    cc = 0;
+    cxo = (ja < jb) ? uni(xoffp[ja]) : 0;
+    acc0 = acc1 = 0.f;
+  }
+  __device__ __forceinline__ void load(u4 (&bf)[NB]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (lj < jb) {
+        int col = lc * kChunkCols + lane * 8;
+        col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
+        bf[i] = ldg_nt(lrow + col);
+        if (++lc == cpr) {
+          lc = 0;
+          if (++lj < jb) lrow = (const uint16_t*)uni64(rowp[lj]);
+        }
+      }
+    }
+  }
+  template <class Emit>
+  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const float* xs, Emit& emit) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (cj < jb) {
+        const float* xp = xs + cxo + cc * kChunkCols + lane * 8;
+        const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
+        const u4 w = bf[i];
+        acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
+        acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
+        acc0 = fmaf(bf_lo(w.y), x0.z, acc0);
+        acc1 = fmaf(bf_hi(w.y), x0.w, acc1);
+        acc0 = fmaf(bf_lo(w.z), x1.x, acc0);
+        acc1 = fmaf(bf_hi(w.z), x1.y, acc1);
+        acc0 = fmaf(bf_lo(w.w), x1.z, acc0);
+        acc1 = fmaf(bf_hi(w.w), x1.w, acc1);
+        if (++cc == cpr) {
+          emit(cj, wave_sum(acc0 + acc1));
+          acc0 = acc1 = 0.f;
+          cc = 0;
+          if (++cj < jb) cxo = uni(xoffp[cj]);
+        }
+      }
+    }
+  }
+};
+
+// Each wave writes the row pointers / input offsets of its own rows (no barrier needed:
+// LDS accesses of one wave are ordered).
+template <class RM>
+__device__ __forceinline__ void fill_rows(const RM& rm, int ja, int jb, uint64_t* rowp, int* xoffp) {
+  for (int j = ja + (int)(threadIdx.x & 63); j < jb; j += 64) {
+    rowp[j] = (uint64_t)rm.row(j);
+    xoffp[j] = rm.xoff(j);
+  }
+}
+
+// The shared skeleton of every GEMV task. Rows are split over the waves in whole groups of
+// G rows (G consecutive rows are summed into one result ys[j / G]). With `prefetch`, the
+// row map may not depend on anything this task waits for: the first two batches are issued
+// before the dependency wait.
+template <class RM, class StageF, class EpiF>
+__device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
+                                         int K, int G, bool prefetch, StageF&& stage, EpiF&& epi) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int ng = nrows / G;
+  const int ja = (ng * wave / kWaves) * G, jb = (ng * (wave + 1) / kWaves) * G;
+  Stream s;
+  u4 b0[NB], b1[NB];
+  if (prefetch) {
+    fill_rows(rm, ja, jb, b.rowp, b.xoffp);
+    s.init(b.rowp, b.xoffp, ja, jb, K, lane);
+    s.load(b0);
+    s.load(b1);
+  }
+  if (!wait_deps(A, b, t)) return false;
+  stage();
+  if (!prefetch) {
+    fill_rows(rm, ja, jb, b.rowp, b.xoffp);
+    s.init(b.rowp, b.xoffp, ja, jb, K, lane);
+    s.load(b0);
+    s.load(b1);
+  }
+  float gacc = 0.f;
+  auto emit = [&](int j, float v) {
+    gacc += v;
+    if (j % G == G - 1) {
+      if (lane == 0) b.ys[j / G] = gacc;
+      gacc = 0.f;
+    }
+  };
+  while (s.cj < jb) {
+    s.consume(b0, b.xs, emit);
+    s.load(b0);
+    if (s.cj >= jb) break;
+    s.consume(b1, b.xs, emit);
+    s.load(b1);
+  }
+  __syncthreads();
+  epi();
+  return true;
+}
+
+// ------------------------------------------------------------------ row maps
+
+struct RmPlain {  // rows r0 + j of a [*, K] matrix
+  const uint16_t* W;
+  int K, r0;
+  __device__ __forceinline__ const uint16_t* row(int j) const { return W + (size_t)(r0 + j) * K; }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+struct RmGateUp {  // unit u -> (gate row u, up row u)
+  const uint16_t *Wg, *Wu;
+  int K, u0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const uintptr_t g = (uintptr_t)Wg;
+    const uintptr_t base = g + (uintptr_t)(j & 1) * ((uintptr_t)Wu - g);
+    return (const uint16_t*)base + (size_t)(u0 + (j >> 1)) * K;
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// GQA QKV: within KV group g, unit u = (slot, i): slot < r -> q head g*r+slot, slot == r ->
+// k head g, slot == r+1 -> v head g; the unit's two rows are i and i + hd/2 of that head
+// (the pair RoPE rotates together).
+struct RmQKV {
+  const uint16_t *wq, *wk, *wv;
+  int g, r, hd, hh, K, u0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const int u = u0 + (j >> 1);
+    const int slot = u / hh, i = u - slot * hh;
+    const int rr = i + (j & 1) * hh;
+    if (slot < r) return wq + ((size_t)(g * r + slot) * hd + rr) * K;
+    const uintptr_t k = (uintptr_t)wk;
+    const uintptr_t base = k + (uintptr_t)(slot - r) * ((uintptr_t)wv - k);
+    return (const uint16_t*)base + ((size_t)g * hd + rr) * K;
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// ------------------------------------------------------------------ GQA tasks
+
+__device__ __forceinline__ const float* layer_in32(const EngineArgs& A, const LayerDesc& L) {
+  return L.act[LA_X_IN] >= 0 ? actp(A, L.act[LA_X_IN]) : nullptr;
+}
+
+__device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
+  const RmQKV rm{wp<uint16_t>(A, L.w[LW_WQ]), wp<uint16_t>(A, L.w[LW_WK]), wp<uint16_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
+  const float* x32 = layer_in32(A, L);
+  return run_gemv(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
+      [&] { stage_vec(b, x32, x32 ? nullptr : A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] {
+        const int n = A.kv_len;
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
+          float a = b.ys[2 * i], c = b.ys[2 * i + 1];
+          if (slot <= r) {  // RoPE on q and k
+            const float cs = A.rope_cs[k], sn = A.rope_cs[A.rope_half + k];
+            const float a2 = a * cs - c * sn;
+            c = c * cs + a * sn;
+            a = a2;
+          }
+          if (slot < r) {
+            float* q = actp(A, L.act[LA_Q]) + (size_t)(g * r + slot) * hd;
+            q[k] = a;
+            q[k + hh] = c;
+          } else {
+            const int sel = slot - r;  // 0: k, 1: v
+            float* kn = actp(A, L.act[LA_KVNEW]) + (size_t)(sel * A.nkv + g) * hd;
+            kn[k] = a;
+            kn[k + hh] = c;
+            uint16_t* cache = A.kv + ((((size_t)t.layer * 2 + sel) * A.nkv + g) * (size_t)(n + 1) + n) * hd;
+            cache[k] = f2bf(a);
+            cache[k + hh] = f2bf(c);
+          }
+        }
+      });
+}
+
+// Split-K attention of one KV group over positions [u0, u1): the group's R query heads share
+// every K/V load. Each lane group of hd/8 lanes holds one position's row (8 dims per lane);
+// positions advance by a wave-instruction's worth of rows per iteration. Online softmax in
+// base 2 per head; partials are merged across lane groups, waves, and then -- by whichever
+// split task arrives last at the group's ticket -- across splits.
+template <int R>
+__device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int hd = A.hd, r = A.nq / A.nkv, g = t.a0, n = A.kv_len, n1 = n + 1;
+  const int LPP = hd >> 3, GPW = 64 / LPP;
+  const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
+  const int p0 = t.u0, np = t.u1 - t.u0;
+  const int q0 = p0 + np * wave / kWaves, q1 = p0 + np * (wave + 1) / kWaves;
+  const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
+  const uint16_t* Vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
+  constexpr int NP = 4;
+  const int per_blk = NP * GPW;
+  const int nblk = (q1 > q0) ? (q1 - q0 + per_blk - 1) / per_blk : 0;
+  u4 ka[NP], va[NP], kb2[NP], vb2[NP];
+  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      int pos = q0 + (blk * NP + i) * GPW + grp;
+      pos = pos < q1 ? pos : q1 - 1;
+      kk[i] = ldg_nt(Kb + (size_t)pos * hd);
+      vv[i] = ldg_nt(Vb + (size_t)pos * hd);
+    }
+  };
+  // the newest position (slot n) is written by this step's QKV tasks: only blocks that end
+  // before it may be loaded ahead of the dependency wait
+  const bool pre = nblk > 0 && (q0 + per_blk - 1 < n);
+  if (pre) load(0, ka, va);
+  if (!wait_deps(A, b, t)) return false;
+  if (nblk > 0 && !pre) load(0, ka, va);
+
+  float qv[R][8];
+  const float* qbase = actp(A, L.act[LA_Q]) + (size_t)g * r * hd + sub * 8;
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+#pragma unroll
+    for (int d = 0; d < 8; ++d) qv[h][d] = (h < r) ? qbase[h * hd + d] * A.attn_scale_log2 : 0.f;
+  }
+  float m[R], l[R], acc[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+  }
+  auto step = [&](int blk, const u4(&kk)[NP], const u4(&vv)[NP]) {
+    float s[R][NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const bool valid = q0 + (blk * NP + i) * GPW + grp < q1;
+      const u4 kw = kk[i];
+      const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
+                           bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        float p = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) p = fmaf(qv[h][d], kf[d], p);
+        p = group_sum(p, LPP);
+        s[h][i] = valid ? p : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      if (h >= r) continue;
+      float mb = s[h][0];
+#pragma unroll
+      for (int i = 1; i < NP; ++i) mb = fmaxf(mb, s[h][i]);
+      const float mn = fmaxf(m[h], mb);
+      if (mn == -INFINITY) continue;
+      const float alpha = exp2f(m[h] - mn);
+      l[h] *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const float p = exp2f(s[h][i] - mn);
+        l[h] += p;
+        const u4 vw = vv[i];
+        acc[h][0] = fmaf(p, bf_lo(vw.x), acc[h][0]);
+        acc[h][1] = fmaf(p, bf_hi(vw.x), acc[h][1]);
+        acc[h][2] = fmaf(p, bf_lo(vw.y), acc[h][2]);
+        acc[h][3] = fmaf(p, bf_hi(vw.y), acc[h][3]);
+        acc[h][4] = fmaf(p, bf_lo(vw.z), acc[h][4]);
+        acc[h][5] = fmaf(p, bf_hi(vw.z), acc[h][5]);
+        acc[h][6] = fmaf(p, bf_lo(vw.w), acc[h][6]);
+        acc[h][7] = fmaf(p, bf_hi(vw.w), acc[h][7]);
+      }
+      m[h] = mn;
+    }
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk + 1 < nblk) load(blk + 1, kb2, vb2);
+    step(blk, ka, va);
+    if (blk + 1 >= nblk) break;
+    if (blk + 2 < nblk) load(blk + 2, ka, va);
+    step(blk + 1, kb2, vb2);
+  }
+  // merge the lane groups of this wave (lanes with equal `sub` hold the same dims)
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    if (h >= r) continue;
+    for (int mask = LPP; mask < 64; mask <<= 1) {
+      const float mo = __shfl_xor(m[h], mask, 64), lo = __shfl_xor(l[h], mask, 64);
+      const float mn = fmaxf(m[h], mo);
+      const float ea = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - mn);
+      const float eb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      l[h] = l[h] * ea + lo * eb;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float ao = __shfl_xor(acc[h][d], mask, 64);
+        acc[h][d] = acc[h][d] * ea + ao * eb;
+      }
+      m[h] = mn;
+    }
+  }
+  // per-wave partials to LDS: scr[wave][h][2 + hd]
+  const int ps = hd + 2;
+  float* wpart = b.scr + (size_t)wave * r * ps;
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      if (h >= r) continue;
+      if (sub == 0) {
+        wpart[h * ps] = m[h];
+        wpart[h * ps + 1] = l[h];
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) wpart[h * ps + 2 + sub * 8 + d] = acc[h][d];
+    }
+  }
+  __syncthreads();
+  // workgroup partial -> global partial slot of this split
+  float* gpart = actp(A, t.a4) + (size_t)t.a1 * r * ps;
+  for (int i = threadIdx.x; i < r * hd; i += kThreads) {
+    const int h = i / hd, d = i - h * hd;
+    float M = -INFINITY;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, b.scr[(size_t)w * r * ps + h * ps]);
+    float num = 0.f, den = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float* pw = b.scr + (size_t)w * r * ps + h * ps;
+      const float e = (pw[0] == -INFINITY) ? 0.f : exp2f(pw[0] - M);
+      num += e * pw[2 + d];
+      den += e * pw[1];
+    }
+    gpart[h * ps + 2 + d] = num;
+    if (d == 0) {
+      gpart[h * ps] = M;
+      gpart[h * ps + 1] = den;
+    }
+  }
+  // ticket: the last split of the group merges all splits
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    release();
+    const uint32_t old = add_agent(A.counters + (size_t)t.signal * kCounterStride, 1u);
+    b.flags[1] = (old + 1u == (b.epoch + 1u) * (uint32_t)t.a2) ? 1 : 0;
+    if (b.flags[1]) acquire();
+  }
+  __syncthreads();
+  if (!b.flags[1]) return true;
+  const uint32_t tm0 = (uint32_t)now();
+  const float* parts = actp(A, t.a4);
+  float* o = actp(A, L.act[LA_ATTN]) + (size_t)g * r * hd;
+  for (int i = threadIdx.x; i < r * hd; i += kThreads) {
+    const int h = i / hd, d = i - h * hd;
+    float M = -INFINITY;
+    for (int sp = 0; sp < t.a2; ++sp) M = fmaxf(M, parts[(size_t)sp * r * ps + h * ps]);
+    float num = 0.f, den = 0.f;
+    for (int sp = 0; sp < t.a2; ++sp) {
+      const float* pp = parts + (size_t)sp * r * ps + h * ps;
+      const float e = exp2f(pp[0] - M);
+      num += e * pp[2 + d];
+      den += e * pp[1];
+    }
+    o[i] = num / den;
+  }
+  signal(A, t.signal2);
+  if (threadIdx.x == 0) {
+    TaskLog* lg = A.log + t.a3;
+    add_agent(&lg->execs, 1u);
+    lg->epoch = b.epoch;
+    lg->wg = blockIdx.x;
+    lg->xcd = xcc_id();
+    lg->t_start = tm0;
+    lg->t_ready = tm0;
+    lg->t_end = (uint32_t)now();
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = (A.arch == 0) ? A.nq * A.hd : A.nq * A.dv;
+  const RmPlain rm{wp<uint16_t>(A, L.w[LW_WO]), K, t.u0};
+  const float* x32 = layer_in32(A, L);
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_vec(b, actp(A, L.act[LA_ATTN]), nullptr, K, pad512(K), nullptr, 0.f); },
+      [&] {
+        float* h = actp(A, L.act[LA_H]);
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int rr = t.u0 + i;
+          const float res = x32 ? x32[rr] : bf16f(A.x[rr]);
+          h[rr] = res + b.ys[i];
+        }
+      });
+}
+
+__device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden;
+  const RmGateUp rm{wp<uint16_t>(A, L.w[LW_GATE]), wp<uint16_t>(A, L.w[LW_UP]), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
+      [&] { stage_vec(b, actp(A, L.act[LA_H]), nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      [&] {
+        float* a = actp(A, L.act[LA_ACT]);
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) a[t.u0 + i] = silu(b.ys[2 * i]) * b.ys[2 * i + 1];
+      });
+}
+
+__device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.ffn;
+  const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_vec(b, actp(A, L.act[LA_ACT]), nullptr, K, pad512(K), nullptr, 0.f); },
+      [&] {
+        float* fo = actp(A, L.act[LA_FFN_OUT]);
+        float* xo = actp(A, L.act[LA_X_OUT]);
+        const float* h = actp(A, L.act[LA_H]);
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int rr = t.u0 + i;
+          const float y = b.ys[i];
+          fo[rr] = y;
+          xo[rr] = h[rr] + y;
+          if (t.a0) A.out[rr] = h[rr] + y;
+        }
+      });
+}
+
+__device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const int K = A.hidden;
+  const RmPlain rm{wp<uint16_t>(A, A.w_lm_head), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_vec(b, actp(A, A.x_final), nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) A.out[t.u0 + i] = b.ys[i];
+      });
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ the engine
+
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs A) {
+  extern __shared__ f4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
+  Blk b;
+  b.flags = reinterpret_cast<int*>(lds);
+  b.xs = lds + 64;
+  b.ys = b.xs + A.xs_floats;
+  b.rowp = reinterpret_cast<uint64_t*>(b.ys + kYsFloats);
+  b.xoffp = reinterpret_cast<int*>(b.rowp + kMaxTaskRows);
+  b.scr = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
+  b.epoch = ld_agent(A.ctl + CTL_EPOCH);
+  b.t_ready = 0;
+  const uint32_t xcc = xcc_id();
+  const int wg = blockIdx.x;
+  const int rq = A.nkv > 0 ? A.nq / A.nkv : 1;
+  for (int ti = A.wg_begin[wg]; ti < A.wg_begin[wg + 1]; ++ti) {
+    const TaskDesc t = A.tasks[ti];
+    const uint32_t t0 = (uint32_t)now();
+    bool ok = true;
+    int sig = t.signal;
+    switch (t.type) {
+      case T_QKV: ok = task_qkv(A, b, t); break;
+      case T_ATTN:
+        ok = rq <= 1 ? task_attn<1>(A, b, t) : rq <= 2 ? task_attn<2>(A, b, t) : task_attn<4>(A, b, t);
+        sig = -1;  // signalled through the ticket
+        break;
+      case T_OPROJ: ok = task_oproj(A, b, t); break;
+      case T_GATEUP: ok = task_gateup(A, b, t); break;
+      case T_DOWN: ok = task_down(A, b, t); break;
+      case T_LMHEAD: ok = task_lmhead(A, b, t); break;
+      default: ok = false; break;
+    }
+    if (!ok) break;
+    signal(A, sig);
+    if (threadIdx.x == 0) {
+      TaskLog* lg = A.log + t.id;
+      add_agent(&lg->execs, 1u);
+      lg->epoch = b.epoch;
+      lg->wg = (uint32_t)wg;
+      lg->xcd = xcc;
+      lg->t_start = t0;
+      lg->t_ready = b.t_ready;
+      lg->t_end = (uint32_t)now();
+    }
+  }
+  // the last workgroup to finish advances the epoch for the next step
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    release();
+    const uint32_t d = add_agent(A.ctl + CTL_DONE, 1u);
+    if (d == (uint32_t)A.n_wg - 1u) {
+      st_agent(A.ctl + CTL_DONE, 0u);
+      add_agent(A.ctl + CTL_EPOCH, 1u);
+    }
+  }
+}
+
+}  // namespace dec
+
+// Host-side launch (used by the C ABI in api.cpp).
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream) {
+  static int configured_lds = -1;
+  if (configured_lds < lds_bytes) {
+    hipError_t e = hipFuncSetAttribute((const void*)dec::dec_engine, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    configured_lds = lds_bytes;
+  }
+  void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
+  return hipLaunchCooperativeKernel((const void*)dec::dec_engine, dim3(n_wg), dim3(dec::kThreads), kargs,
+                                    (unsigned)lds_bytes, stream);
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int lds_bytes, int* blocks_per_cu) {
+  hipError_t e = hipFuncSetAttribute((const void*)dec::dec_engine, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)dec::dec_engine, dec::kThreads,
+                                                      (size_t)lds_bytes);
+}

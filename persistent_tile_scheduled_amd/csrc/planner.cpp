@@ -1,0 +1,641 @@
+// planner.cpp -- ahead-of-time planner of one batch-1 decode step.
+//
+// The step is unrolled, layer by layer, into stages of tile tasks ("Static Compilation for
+// LLM Inference ...", section 1: the whole model is compiled ahead of time into one
+// persistent engine kernel; section 5.6: Fleet's task graph is fixed at compile time;
+// TileRT talk, section on breaking kernel boundaries: tile-level tasks start as soon as
+// their own dependencies are met). Each stage's work is cut into one task per workgroup
+// (one workgroup per CU), every task lists the dependency counters it waits on, and names
+// the counter it increments when done. Placement is chiplet-aware (the TileRT audit page's
+// Fleet paragraph: one XCD and its 4 MB L2 as an explicit scheduling unit): the tasks of
+// one KV-head group -- its QKV rows and its attention splits -- run on the workgroups of
+// one XCD, so the group's q/k/v stay in that XCD's L2.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <set>
+#include <tuple>
+#include <sstream>
+
+namespace dec {
+namespace {
+
+constexpr int kMinPosPerSplit = 16;
+constexpr int kRowsCap = kMaxTaskRows;     // rows of one GEMV task (LDS row tables)
+constexpr int kAbsorbBlock = 64;           // latent columns per absorb task
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct PTask {
+  TaskDesc d;
+  int stage;
+  std::vector<int32_t> deps;
+};
+
+struct Builder {
+  const dec_model_shape& s;
+  int64_t n;  // kv_len
+  const dec_device_info& dev;
+  PlanData& P;
+  std::string& err;
+  int n_wg = 0, n_xcd = 1;
+  int stage = 0;
+  int next_id = 0;
+  std::vector<std::vector<PTask>> per_wg;
+  std::vector<std::pair<std::string, std::pair<int64_t, int32_t>>> acts;  // name -> (float off, dtype)
+  std::vector<int64_t> act_counts;
+  int64_t act_floats = 0;
+  int64_t xs_floats_max = 0;  // largest staged input vector (padded)
+  int64_t scratch_floats = 1024;
+
+  Builder(const dec_model_shape& s_, int64_t n_, const dec_device_info& d_, PlanData& p_, std::string& e_)
+      : s(s_), n(n_), dev(d_), P(p_), err(e_) {}
+
+  int xcd(int w) const { return w % n_xcd; }
+
+  int counter(int count) {
+    int base = (int)P.counter_total.size();
+    P.counter_total.resize(base + count, 0);
+    return base;
+  }
+  std::vector<int32_t> all_of(int base, int count) const {
+    std::vector<int32_t> v;
+    for (int i = 0; i < count; ++i)
+      if (P.counter_total[base + i] > 0) v.push_back(base + i);
+    return v;
+  }
+  int64_t act(const std::string& name, int64_t count, int32_t dtype = DEC_DTYPE_FP32) {
+    int64_t off = act_floats;
+    acts.push_back({name, {off, dtype}});
+    act_counts.push_back(count);
+    act_floats += align_up(count, 64);  // 256-byte aligned buffers
+    return off;
+  }
+  void need_xs(int64_t K) { xs_floats_max = std::max<int64_t>(xs_floats_max, align_up(K, kChunkCols)); }
+
+  int add(int w, int32_t type, int layer, int u0, int u1, std::vector<int32_t> deps, int signal,
+          int signal2 = -1, int a0 = 0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0,
+          int a6 = 0) {
+    PTask t;
+    std::memset(&t.d, 0, sizeof(t.d));
+    t.d.type = type;
+    t.d.layer = layer;
+    t.d.signal = signal;
+    t.d.signal2 = signal2;
+    t.d.id = next_id++;
+    t.d.u0 = u0;
+    t.d.u1 = u1;
+    t.d.a0 = a0; t.d.a1 = a1; t.d.a2 = a2; t.d.a3 = a3; t.d.a4 = a4; t.d.a5 = a5; t.d.a6 = a6;
+    t.stage = stage;
+    t.deps = std::move(deps);
+    if (signal >= 0) P.counter_total[signal] += 1;
+    per_wg[w].push_back(std::move(t));
+    return per_wg[w].back().d.id;
+  }
+
+  // Cut `units` units over the workgroups in `wgs` (balanced, contiguous); a workgroup whose
+  // share exceeds `cap` gets several consecutive tasks.
+  template <class F>
+  void spread(const std::vector<int>& wgs, int units, int cap, F&& emit) {
+    int m = (int)wgs.size();
+    for (int i = 0; i < m; ++i) {
+      int u0 = (int)((int64_t)units * i / m), u1 = (int)((int64_t)units * (i + 1) / m);
+      for (int a = u0; a < u1; a += cap) emit(wgs[i], a, std::min(u1, a + cap));
+    }
+  }
+
+  std::vector<int> all_wgs() const {
+    std::vector<int> v(n_wg);
+    for (int i = 0; i < n_wg; ++i) v[i] = i;
+    return v;
+  }
+  // Workgroups ordered by XCD, cut into `g` contiguous sets (set i -> XCD-local when g | n_xcd).
+  std::vector<std::vector<int>> xcd_sets(int g) const {
+    std::vector<int> order = all_wgs();
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return xcd(a) < xcd(b); });
+    std::vector<std::vector<int>> sets(g);
+    for (int i = 0; i < g; ++i) {
+      int a = (int)((int64_t)n_wg * i / g), b = (int)((int64_t)n_wg * (i + 1) / g);
+      sets[i].assign(order.begin() + a, order.begin() + b);
+    }
+    return sets;
+  }
+
+  bool fail(dec_status st, const std::string& m, dec_status* out) {
+    err = m;
+    *out = st;
+    return false;
+  }
+
+  bool check_shape(dec_status* st) {
+    const dec_model_shape& q = s;
+    if (q.abi_version != DEC_ABI_VERSION) return fail(DEC_E_INVAL, "abi_version mismatch", st);
+    if (q.n_layers < 1 || q.hidden < 8 || q.hidden % 8) return fail(DEC_E_SHAPE, "need n_layers >= 1 and hidden a positive multiple of 8", st);
+    if (q.vocab < 0) return fail(DEC_E_SHAPE, "vocab < 0", st);
+    if (!(q.rms_eps > 0.f) || !(q.rope_theta > 1.0)) return fail(DEC_E_SHAPE, "need rms_eps > 0 and rope_theta > 1", st);
+    if (n < 0) return fail(DEC_E_CAPACITY, "kv_len < 0", st);
+    if (n > (1 << 22)) return fail(DEC_E_CAPACITY, "kv_len above 4194304", st);
+    if (q.arch == DEC_ARCH_GQA) {
+      if (q.n_q_heads < 1 || q.n_kv_heads < 1 || q.n_q_heads % q.n_kv_heads)
+        return fail(DEC_E_SHAPE, "GQA needs n_q_heads a positive multiple of n_kv_heads", st);
+      if (q.n_q_heads / q.n_kv_heads > 4) return fail(DEC_E_SHAPE, "more than 4 query heads per KV head", st);
+      int lpp = q.head_dim / 8;
+      if (q.head_dim % 8 || lpp < 1 || lpp > 64 || (lpp & (lpp - 1)))
+        return fail(DEC_E_SHAPE, "head_dim must be 8 * 2^k, at most 512", st);
+      if (q.ffn < 8 || q.ffn % 8) return fail(DEC_E_SHAPE, "ffn must be a positive multiple of 8", st);
+      if (q.q_lora_rank || q.kv_lora_rank || q.qk_nope || q.qk_rope || q.v_head || q.n_routed || q.n_shared || q.top_k || q.expert_ffn)
+        return fail(DEC_E_SHAPE, "GQA shape with MLA/MoE fields set", st);
+    } else if (q.arch == DEC_ARCH_MLA || q.arch == DEC_ARCH_MOE) {
+      if (q.n_q_heads < 1 || q.n_q_heads > 64) return fail(DEC_E_SHAPE, "MLA needs 1..64 heads", st);
+      if (q.n_kv_heads || q.head_dim) return fail(DEC_E_SHAPE, "MLA shape with GQA fields set", st);
+      if (q.q_lora_rank < 8 || q.q_lora_rank % 8) return fail(DEC_E_SHAPE, "q_lora_rank must be a positive multiple of 8", st);
+      if (q.kv_lora_rank < 8 || q.kv_lora_rank % 8 || (q.kv_lora_rank > kAbsorbBlock && q.kv_lora_rank % kAbsorbBlock))
+        return fail(DEC_E_SHAPE, "kv_lora_rank must be a multiple of 8 (and of 64 above 64)", st);
+      if (q.kv_lora_rank > 1024) return fail(DEC_E_SHAPE, "kv_lora_rank above 1024", st);
+      if (q.qk_nope < 2 || q.qk_nope % 2 || q.qk_rope < 2 || q.qk_rope % 8 || q.qk_rope > 128)
+        return fail(DEC_E_SHAPE, "qk_nope must be even and qk_rope a multiple of 8 (<= 128)", st);
+      if (q.v_head < 1) return fail(DEC_E_SHAPE, "v_head < 1", st);
+      if (q.arch == DEC_ARCH_MLA) {
+        if (q.ffn < 8 || q.ffn % 8) return fail(DEC_E_SHAPE, "ffn must be a positive multiple of 8", st);
+        if (q.n_routed || q.n_shared || q.top_k || q.expert_ffn) return fail(DEC_E_SHAPE, "MLA shape with MoE fields set", st);
+      } else {
+        if (q.ffn) return fail(DEC_E_SHAPE, "MoE shape with a dense ffn", st);
+        if (q.n_routed < 1 || q.top_k < 1 || q.top_k > q.n_routed || q.top_k > 64 || q.n_routed > 4096)
+          return fail(DEC_E_SHAPE, "MoE needs 1 <= top_k <= min(n_routed, 64), n_routed <= 4096", st);
+        if (q.n_shared < 0 || q.expert_ffn < 8 || q.expert_ffn % 8) return fail(DEC_E_SHAPE, "bad n_shared / expert_ffn", st);
+      }
+    } else {
+      return fail(DEC_E_SHAPE, "unknown arch", st);
+    }
+    return true;
+  }
+
+  void add_weight(const std::string& name, int32_t dtype, std::vector<int64_t> dims) {
+    int64_t e = 1;
+    for (auto d : dims) e *= d;
+    P.weights.push_back({name, dtype, dims, e * (dtype == DEC_DTYPE_BF16 ? 2 : 4)});
+  }
+
+  // Canonical weight order: the bind order of the ABI.
+  void weight_list(std::vector<LayerDesc>& L) {
+    const int d = s.hidden;
+    for (int l = 0; l < s.n_layers; ++l) {
+      std::string p = "layers." + std::to_string(l) + ".";
+      LayerDesc& ld = L[l];
+      for (int i = 0; i < LW_COUNT; ++i) ld.w[i] = -1;
+      auto W = [&](int slot, const std::string& nm, int32_t dt, std::vector<int64_t> dims) {
+        ld.w[slot] = (int)P.weights.size();
+        add_weight(p + nm, dt, dims);
+      };
+      if (s.arch == DEC_ARCH_GQA) {
+        W(LW_ATTN_NORM, "attn_norm", DEC_DTYPE_BF16, {d});
+        W(LW_WQ, "wq", DEC_DTYPE_BF16, {(int64_t)s.n_q_heads * s.head_dim, d});
+        W(LW_WK, "wk", DEC_DTYPE_BF16, {(int64_t)s.n_kv_heads * s.head_dim, d});
+        W(LW_WV, "wv", DEC_DTYPE_BF16, {(int64_t)s.n_kv_heads * s.head_dim, d});
+        W(LW_WO, "wo", DEC_DTYPE_BF16, {d, (int64_t)s.n_q_heads * s.head_dim});
+      } else {
+        const int nh = s.n_q_heads;
+        W(LW_ATTN_NORM, "attn_norm", DEC_DTYPE_BF16, {d});
+        W(LW_WQA, "wq_a", DEC_DTYPE_BF16, {s.q_lora_rank, d});
+        W(LW_QNORM, "q_norm", DEC_DTYPE_BF16, {s.q_lora_rank});
+        W(LW_WQB, "wq_b", DEC_DTYPE_BF16, {(int64_t)nh * (s.qk_nope + s.qk_rope), s.q_lora_rank});
+        W(LW_WKVA, "wkv_a", DEC_DTYPE_BF16, {s.kv_lora_rank + s.qk_rope, d});
+        W(LW_KVNORM, "kv_norm", DEC_DTYPE_BF16, {s.kv_lora_rank});
+        W(LW_WUK, "w_uk", DEC_DTYPE_BF16, {nh, s.qk_nope, s.kv_lora_rank});
+        W(LW_WUV, "w_uv", DEC_DTYPE_BF16, {nh, s.v_head, s.kv_lora_rank});
+        W(LW_WO, "wo", DEC_DTYPE_BF16, {d, (int64_t)nh * s.v_head});
+      }
+      W(LW_FFN_NORM, "ffn_norm", DEC_DTYPE_BF16, {d});
+      if (s.arch == DEC_ARCH_MOE) {
+        const int64_t E = s.n_routed, F = s.expert_ffn, S = (int64_t)s.n_shared * s.expert_ffn;
+        W(LW_ROUTER, "router", DEC_DTYPE_BF16, {E, d});
+        W(LW_RBIAS, "router_bias", DEC_DTYPE_FP32, {E});
+        W(LW_EGATE, "experts.w_gate", DEC_DTYPE_BF16, {E, F, d});
+        W(LW_EUP, "experts.w_up", DEC_DTYPE_BF16, {E, F, d});
+        W(LW_EDOWN, "experts.w_down", DEC_DTYPE_BF16, {E, d, F});
+        W(LW_SGATE, "shared.w_gate", DEC_DTYPE_BF16, {S, d});
+        W(LW_SUP, "shared.w_up", DEC_DTYPE_BF16, {S, d});
+        W(LW_SDOWN, "shared.w_down", DEC_DTYPE_BF16, {d, S});
+      } else {
+        W(LW_GATE, "w_gate", DEC_DTYPE_BF16, {s.ffn, d});
+        W(LW_UP, "w_up", DEC_DTYPE_BF16, {s.ffn, d});
+        W(LW_DOWN, "w_down", DEC_DTYPE_BF16, {d, s.ffn});
+      }
+    }
+    if (s.vocab > 0) {
+      P.w_final_norm = (int)P.weights.size();
+      add_weight("final_norm", DEC_DTYPE_BF16, {d});
+      P.w_lm_head = (int)P.weights.size();
+      add_weight("lm_head", DEC_DTYPE_BF16, {s.vocab, d});
+    }
+  }
+
+  // ---------------------------------------------------------------- GQA layer stages
+  std::vector<int32_t> build_gqa_layer(int l, std::vector<int32_t> prev, int64_t x_in) {
+    LayerDesc& L = P.layers[l];
+    const int d = s.hidden, nq = s.n_q_heads, nkv = s.n_kv_heads, hd = s.head_dim, f = s.ffn;
+    const int r = nq / nkv;
+    std::string p = "layers." + std::to_string(l) + ".";
+    for (int i = 0; i < LA_COUNT; ++i) L.act[i] = -1;
+    L.act[LA_X_IN] = (int)x_in;
+    L.act[LA_Q] = (int)act(p + "q", (int64_t)nq * hd);
+    L.act[LA_KVNEW] = (int)act(p + "kv_new", 2LL * nkv * hd);
+    L.act[LA_ATTN] = (int)act(p + "attn", (int64_t)nq * hd);
+    L.act[LA_H] = (int)act(p + "h", d);
+    L.act[LA_ACT] = (int)act(p + "ffn_act", f);
+    L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
+    L.act[LA_X_OUT] = (int)act(p + "x_out", d);
+    need_xs(d); need_xs((int64_t)nq * hd); need_xs(f);
+    auto sets = xcd_sets(nkv);
+
+    // QKV: per KV group g, units = (r q heads + k + v) * hd/2 RoPE row pairs.
+    ++stage;
+    const int qkv = counter(nkv);
+    const int U = (r + 2) * hd / 2;
+    for (int g = 0; g < nkv; ++g)
+      spread(sets[g], U, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_QKV, l, a, b, prev, qkv + g, -1, g); });
+
+    // attention splits (one per workgroup of the group's set) + ticket merge
+    ++stage;
+    const int tick = counter(nkv), merged = counter(nkv);
+    int smax = 1;
+    std::vector<int> S(nkv);
+    for (int g = 0; g < nkv; ++g) {
+      S[g] = (int)std::min<int64_t>((int64_t)sets[g].size(), std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit));
+      smax = std::max(smax, S[g]);
+    }
+    const int64_t pstride = (int64_t)r * (hd + 2);
+    const int64_t part = act(p + "attn_partials", (int64_t)nkv * smax * pstride);
+    L.act[LA_PART] = (int)part;
+    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * pstride + 64);
+    for (int g = 0; g < nkv; ++g) {
+      const int merge_id = next_id++;
+      for (int sp = 0; sp < S[g]; ++sp) {
+        int p0 = (int)((n + 1) * sp / S[g]), p1 = (int)((n + 1) * (sp + 1) / S[g]);
+        add(sets[g][sp], T_ATTN, l, p0, p1, {qkv + g}, tick + g, merged + g, g, sp, S[g], merge_id,
+            (int)(part + (int64_t)g * smax * pstride));
+      }
+      P.counter_total[merged + g] = 1;  // only the last split signals it
+    }
+
+    // O projection + residual
+    ++stage;
+    const int ctr_o = counter(n_xcd);
+    std::vector<int32_t> dm;
+    for (int g = 0; g < nkv; ++g) dm.push_back(merged + g);
+    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) { add(w, T_OPROJ, l, a, b, dm, ctr_o + xcd(w)); });
+    return ffn_dense(l, all_of(ctr_o, n_xcd));
+  }
+
+  std::vector<int32_t> ffn_dense(int l, std::vector<int32_t> deps_h) {
+    const int d = s.hidden, f = s.ffn;
+    ++stage;
+    const int ctr_gu = counter(n_xcd);
+    spread(all_wgs(), f, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_GATEUP, l, a, b, deps_h, ctr_gu + xcd(w)); });
+    ++stage;
+    const int ctr_dn = counter(n_xcd);
+    const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
+    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) {
+      add(w, T_DOWN, l, a, b, all_of(ctr_gu, n_xcd), ctr_dn + xcd(w), -1, last);
+    });
+    return all_of(ctr_dn, n_xcd);
+  }
+
+  // ---------------------------------------------------------------- MLA / MoE layer stages
+  std::vector<int32_t> build_mla_layer(int l, std::vector<int32_t> prev, int64_t x_in) {
+    LayerDesc& L = P.layers[l];
+    const int d = s.hidden, nh = s.n_q_heads, ql = s.q_lora_rank, kl = s.kv_lora_rank;
+    const int dn = s.qk_nope, dr = s.qk_rope, dv = s.v_head;
+    std::string p = "layers." + std::to_string(l) + ".";
+    for (int i = 0; i < LA_COUNT; ++i) L.act[i] = -1;
+    L.act[LA_X_IN] = (int)x_in;
+    L.act[LA_CQ] = (int)act(p + "cq_raw", ql);
+    L.act[LA_KVA] = (int)act(p + "kv_a", kl + dr);
+    L.act[LA_QNOPE] = (int)act(p + "q_nope", (int64_t)nh * dn);
+    L.act[LA_QROPE] = (int)act(p + "q_rope", (int64_t)nh * dr);
+    L.act[LA_KVNEW] = (int)act(p + "kv_new", kl + dr);
+    L.act[LA_QABS] = (int)act(p + "q_abs", (int64_t)nh * kl);
+    L.act[LA_OLAT] = (int)act(p + "o_lat", (int64_t)nh * kl);
+    L.act[LA_ATTN] = (int)act(p + "attn", (int64_t)nh * dv);
+    L.act[LA_H] = (int)act(p + "h", d);
+    L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
+    L.act[LA_X_OUT] = (int)act(p + "x_out", d);
+    need_xs(d); need_xs(ql); need_xs(kl + dr); need_xs((int64_t)nh * align_up(kl, kChunkCols)); need_xs((int64_t)nh * dv);
+
+    // A: [W_DQ; W_DKV] rows from the normalised layer input
+    ++stage;
+    const int ca = counter(n_xcd);
+    spread(all_wgs(), ql + kl + dr, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + xcd(w)); });
+    auto da = all_of(ca, n_xcd);
+
+    // B: W_UQ row pairs (nope pairs, then RoPE pairs, per head) + the latent-cache append
+    ++stage;
+    const int cb = counter(n_xcd), ckv = counter(1);
+    const int UH = dn / 2 + dr / 2;
+    add(n_wg - 1, T_MLA_KVAPP, l, 0, kl + dr, da, ckv);
+    spread(all_wgs(), nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + xcd(w)); });
+    auto db = all_of(cb, n_xcd);
+
+    // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h]
+    ++stage;
+    const int cabs = counter(n_xcd);
+    const int cbw = std::min(kAbsorbBlock, kl);
+    const int nblk = nh * (kl / cbw);
+    spread(all_wgs(), nblk, 1 << 30, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + xcd(w), -1, cbw); });
+
+    // latent attention splits + ticket merge
+    ++stage;
+    const int tick = counter(1), merged = counter(1);
+    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit));
+    const int64_t pstride = (int64_t)nh * (kl + 2);
+    const int64_t part = act(p + "attn_partials", (int64_t)S * pstride);
+    L.act[LA_PART] = (int)part;
+    std::vector<int32_t> dat = all_of(cabs, n_xcd);
+    dat.insert(dat.end(), db.begin(), db.end());
+    dat.push_back(ckv);
+    const int merge_id = next_id++;
+    for (int sp = 0; sp < S; ++sp) {
+      int p0 = (int)((n + 1) * sp / S), p1 = (int)((n + 1) * (sp + 1) / S);
+      add(sp % n_wg, T_MLA_ATTN, l, p0, p1, dat, tick, merged, 0, sp, S, merge_id, (int)part);
+    }
+    P.counter_total[merged] = 1;
+
+    // o[h] = W_UV[h] o_lat[h]
+    ++stage;
+    const int cuv = counter(n_xcd);
+    spread(all_wgs(), nh * dv, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_UV, l, a, b, {merged}, cuv + xcd(w)); });
+
+    // O projection + residual
+    ++stage;
+    const int co = counter(n_xcd);
+    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) { add(w, T_OPROJ, l, a, b, all_of(cuv, n_xcd), co + xcd(w)); });
+    auto dh = all_of(co, n_xcd);
+
+    if (s.arch == DEC_ARCH_MLA) {
+      L.act[LA_ACT] = (int)act(p + "ffn_act", s.ffn);
+      need_xs(s.ffn);
+      return ffn_dense(l, dh);
+    }
+    return ffn_moe(l, dh);
+  }
+
+  std::vector<int32_t> ffn_moe(int l, std::vector<int32_t> dh) {
+    LayerDesc& L = P.layers[l];
+    const int d = s.hidden, E = s.n_routed, K = s.top_k, F = s.expert_ffn, SF = s.n_shared * s.expert_ffn;
+    std::string p = "layers." + std::to_string(l) + ".";
+    L.act[LA_RLOGIT] = (int)act(p + "router_logits", E);
+    L.act[LA_TOPK] = (int)act(p + "topk", 2LL * K, DEC_DTYPE_I32);
+    L.act[LA_SACT] = (int)act(p + "shared_act", std::max(SF, 1));
+    L.act[LA_ACT] = (int)act(p + "expert_act", (int64_t)K * F);
+    need_xs((int64_t)(s.n_shared + K) * align_up(F, kChunkCols));
+
+    // E1: router rows on a few workgroups, the shared expert's gate/up on the rest
+    ++stage;
+    const int cr = counter(n_xcd), cs = counter(n_xcd);
+    int nr = std::max(1, std::min(n_wg / 4, (E + 3) / 4));
+    if (SF == 0) nr = n_wg;
+    std::vector<int> rw, sw;
+    for (int w = 0; w < n_wg; ++w) (w < nr ? rw : sw).push_back(w);
+    spread(rw, E, kRowsCap, [&](int w, int a, int b) { add(w, T_ROUTER, l, a, b, dh, cr + xcd(w)); });
+    if (SF > 0) spread(sw, SF, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_SHARED_GU, l, a, b, dh, cs + xcd(w)); });
+
+    // E2: top-k on one workgroup
+    ++stage;
+    const int ct = counter(1);
+    add(nr - 1, T_TOPK, l, 0, E, all_of(cr, n_xcd), ct);
+
+    // E3: routed experts' gate/up (the expert id is read from the top-k result)
+    ++stage;
+    const int ce = counter(n_xcd);
+    spread(all_wgs(), K * F, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_EXPERT_GU, l, a, b, {ct}, ce + xcd(w)); });
+
+    // E4: down projections of the shared and routed experts, weighted, + residual
+    ++stage;
+    const int cd = counter(n_xcd);
+    std::vector<int32_t> dd = all_of(ce, n_xcd);
+    auto ds_ = all_of(cs, n_xcd);
+    dd.insert(dd.end(), ds_.begin(), ds_.end());
+    dd.push_back(ct);
+    const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
+    spread(all_wgs(), d, kRowsCap / (s.n_shared + K), [&](int w, int a, int b) { add(w, T_MOE_DOWN, l, a, b, dd, cd + xcd(w), -1, last); });
+    return all_of(cd, n_xcd);
+  }
+
+  bool run(dec_status* st) {
+    if (!check_shape(st)) return false;
+    if (dev.gfx_arch != 950) return fail(DEC_E_DEVICE, "device is not gfx950", st);
+    if (dev.n_cu < 1 || dev.n_xcd < 1 || dev.n_cu % dev.n_xcd) return fail(DEC_E_DEVICE, "bad CU/XCD counts", st);
+    n_wg = dev.n_cu;
+    n_xcd = dev.n_xcd;
+    per_wg.assign(n_wg, {});
+    P.shape = s;
+    P.kv_len = n;
+    P.dev = dev;
+    P.n_wg = n_wg;
+    P.layers.assign(s.n_layers, LayerDesc{});
+    weight_list(P.layers);
+
+    std::vector<int32_t> prev;
+    int64_t x_in = -1;
+    for (int l = 0; l < s.n_layers; ++l) {
+      prev = (s.arch == DEC_ARCH_GQA) ? build_gqa_layer(l, prev, x_in) : build_mla_layer(l, prev, x_in);
+      x_in = P.layers[l].act[LA_X_OUT];
+    }
+    P.x_final = (int)x_in;
+    if (s.vocab > 0) {
+      ++stage;
+      spread(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
+    }
+
+    // flatten per-workgroup lists, resolve dependency entries
+    P.wg_begin.assign(n_wg + 1, 0);
+    for (int w = 0; w < n_wg; ++w) {
+      P.wg_begin[w] = (int)P.tasks.size();
+      int pos = 0;
+      for (auto& t : per_wg[w]) {
+        if ((int)t.deps.size() > kMaxDepsPerTask) return fail(DEC_E_PLAN, "too many dependencies", st);
+        t.d.dep_first = (int)P.deps.size();
+        t.d.dep_count = (int)t.deps.size();
+        for (int c : t.deps) P.deps.push_back({c, P.counter_total[c]});
+        P.tasks.push_back(t.d);
+        P.info.push_back({t.stage, w, pos++});
+      }
+    }
+    P.wg_begin[n_wg] = (int)P.tasks.size();
+    P.n_log = next_id;
+
+    // RoPE table at the step's position, in double precision
+    const int rope_dim = (s.arch == DEC_ARCH_GQA) ? s.head_dim : s.qk_rope;
+    P.rope_half = rope_dim / 2;
+    P.rope_cs.assign(2 * P.rope_half, 0.f);
+    for (int i = 0; i < P.rope_half; ++i) {
+      long double ang = (long double)n * powl((long double)s.rope_theta, -2.0L * i / rope_dim);
+      P.rope_cs[i] = (float)cosl(ang);
+      P.rope_cs[P.rope_half + i] = (float)sinl(ang);
+    }
+    const double qk = (s.arch == DEC_ARCH_GQA) ? s.head_dim : (s.qk_nope + s.qk_rope);
+    P.attn_scale_log2 = (float)(1.0 / std::sqrt(qk) * 1.4426950408889634);
+
+    // LDS: staged input vector + per-row results + reduction scratch
+    const int64_t tables = (int64_t)kMaxTaskRows * 12 / 4;  // row pointers + input offsets
+    const int64_t header = 64;  // LDS flag words ahead of the staged vector
+    int64_t lds = 4 * (header + xs_floats_max + kYsFloats + tables + scratch_floats);
+    if (s.arch != DEC_ARCH_GQA) {
+      // latent attention: q (heads x (kl+dr)) + per-wave partials
+      int64_t w = (int64_t)s.n_q_heads * (s.kv_lora_rank + s.qk_rope) + (int64_t)kWaves * s.n_q_heads * (s.kv_lora_rank + 2);
+      lds = std::max<int64_t>(lds, 4 * (header + w + kYsFloats + tables + 1024));
+    }
+    lds = std::max<int64_t>(align_up(lds, 1024), kLdsMin);
+    P.lds_bytes = (int32_t)lds;
+    P.xs_floats = xs_floats_max;
+    if (lds > dev.lds_bytes_per_cu) return fail(DEC_E_OCCUPANCY, "plan needs " + std::to_string(lds) + " B of LDS per workgroup", st);
+    if (kThreads > dev.max_threads_per_cu) return fail(DEC_E_OCCUPANCY, "device runs fewer than 512 threads per CU", st);
+
+    // workspace layout
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) { int64_t r = o; o = align_up(o + bytes, 256); return r; };
+    P.off_ctl = take(CTL_WORDS * 4);
+    P.off_counters = take((int64_t)P.counter_total.size() * kCounterStride * 4);
+    P.off_tasks = take((int64_t)P.tasks.size() * sizeof(TaskDesc));
+    P.off_wgb = take((int64_t)(n_wg + 1) * 4);
+    P.off_deps = take((int64_t)std::max<size_t>(P.deps.size(), 1) * sizeof(DepEntry));
+    P.off_wptr = take((int64_t)P.weights.size() * 8);
+    P.off_layers = take((int64_t)P.layers.size() * sizeof(LayerDesc));
+    P.off_rope = take((int64_t)P.rope_cs.size() * 4 + 4);
+    P.off_log = take((int64_t)P.n_log * sizeof(TaskLog));
+    P.off_act = take(act_floats * 4);
+    P.ws_bytes = o;
+    P.act_floats = act_floats;
+    for (size_t i = 0; i < acts.size(); ++i)
+      P.buffers.push_back({acts[i].first, acts[i].second.second, P.off_act + acts[i].second.first * 4, act_counts[i]});
+    P.buffers.push_back({"task_log", DEC_DTYPE_I32, P.off_log, (int64_t)P.n_log * 8});
+    P.buffers.push_back({"control", DEC_DTYPE_I32, P.off_ctl, CTL_WORDS});
+
+    // bytes the method must read per step: every dense weight once (routed experts: only
+    // the top_k chosen), and positions [0, kv_len] of the cache once
+    P.weight_bytes = 0;
+    for (auto& w : P.weights) P.weight_bytes += w.bytes;
+    int64_t alg = P.weight_bytes;
+    if (s.arch == DEC_ARCH_MOE) {
+      int64_t per_expert = 3LL * s.expert_ffn * s.hidden * 2;
+      alg -= (int64_t)s.n_layers * (s.n_routed - s.top_k) * per_expert;
+    }
+    int64_t kv_row = (s.arch == DEC_ARCH_GQA) ? 2LL * s.n_kv_heads * s.head_dim * 2 : (int64_t)(s.kv_lora_rank + s.qk_rope) * 2;
+    alg += (int64_t)s.n_layers * (n + 1) * kv_row;
+    P.alg_bytes = alg;
+
+    std::string v = validate_plan(P);
+    if (!v.empty()) return fail(DEC_E_PLAN, "plan validation: " + v, st);
+    return true;
+  }
+};
+
+}  // namespace
+
+dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev, PlanData* out,
+                      std::string* err) {
+  *out = PlanData{};
+  dec_status st = DEC_OK;
+  Builder b(shape, kv_len, dev, *out, *err);
+  if (!b.run(&st)) return st;
+  return DEC_OK;
+}
+
+std::string validate_plan(const PlanData& p) {
+  std::ostringstream e;
+  const int nt = (int)p.tasks.size();
+  // (1) each workgroup's list is in nondecreasing stage order
+  for (int w = 0; w < p.n_wg; ++w)
+    for (int i = p.wg_begin[w] + 1; i < p.wg_begin[w + 1]; ++i)
+      if (p.info[i].stage < p.info[i - 1].stage) { e << "wg " << w << " list not in stage order"; return e.str(); }
+  // (2) every counter waited on is produced only by tasks of earlier stages, and its
+  //     per-step total equals its producers' count (merged counters: exactly one merge)
+  std::vector<int> prod_stage_max(p.counter_total.size(), -1), prod_count(p.counter_total.size(), 0);
+  std::vector<int> merge_count(p.counter_total.size(), 0);
+  for (int i = 0; i < nt; ++i) {
+    const TaskDesc& t = p.tasks[i];
+    if (t.signal >= 0) {
+      prod_stage_max[t.signal] = std::max(prod_stage_max[t.signal], p.info[i].stage);
+      prod_count[t.signal]++;
+    }
+    if (t.signal2 >= 0) prod_stage_max[t.signal2] = std::max(prod_stage_max[t.signal2], p.info[i].stage);
+  }
+  std::set<int> merged;
+  for (int i = 0; i < nt; ++i) if (p.tasks[i].signal2 >= 0) merged.insert(p.tasks[i].signal2);
+  for (size_t c = 0; c < p.counter_total.size(); ++c) {
+    uint32_t want = merged.count((int)c) ? 1u : (uint32_t)prod_count[c];
+    if (p.counter_total[c] != want) { e << "counter " << c << " total " << p.counter_total[c] << " != producers " << want; return e.str(); }
+  }
+  for (int i = 0; i < nt; ++i) {
+    const TaskDesc& t = p.tasks[i];
+    if (t.dep_count > kMaxDepsPerTask) { e << "task " << t.id << " has too many deps"; return e.str(); }
+    for (int k = 0; k < t.dep_count; ++k) {
+      const DepEntry& d = p.deps[t.dep_first + k];
+      if (d.counter < 0 || d.counter >= (int)p.counter_total.size()) { e << "task " << t.id << " bad counter"; return e.str(); }
+      if (d.per_step == 0) { e << "task " << t.id << " waits on a counter nobody signals"; return e.str(); }
+      if (prod_stage_max[d.counter] >= p.info[i].stage) { e << "task " << t.id << " waits on a same-or-later stage"; return e.str(); }
+      if (d.per_step != p.counter_total[d.counter]) { e << "task " << t.id << " dep total mismatch"; return e.str(); }
+    }
+  }
+  // (3) unit coverage: for each (layer, type[, group]) the tasks' [u0, u1) ranges tile the
+  //     unit space exactly once
+  struct Key { int layer, type, grp; bool operator<(const Key& o) const { return std::tie(layer, type, grp) < std::tie(o.layer, o.type, o.grp); } };
+  std::map<Key, std::vector<std::pair<int, int>>> ranges;
+  for (int i = 0; i < nt; ++i) {
+    const TaskDesc& t = p.tasks[i];
+    int grp = (t.type == T_QKV || t.type == T_ATTN) ? t.a0 : 0;
+    ranges[{t.layer, t.type, grp}].push_back({t.u0, t.u1});
+  }
+  const dec_model_shape& s = p.shape;
+  const int64_t n1 = p.kv_len + 1;
+  auto expected = [&](int type) -> int64_t {
+    switch (type) {
+      case T_QKV: return (int64_t)(s.n_q_heads / s.n_kv_heads + 2) * s.head_dim / 2;
+      case T_ATTN: case T_MLA_ATTN: return n1;
+      case T_OPROJ: case T_DOWN: case T_MOE_DOWN: return s.hidden;
+      case T_GATEUP: return s.ffn;
+      case T_LMHEAD: return s.vocab;
+      case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope;
+      case T_MLA_B: return (int64_t)s.n_q_heads * (s.qk_nope / 2 + s.qk_rope / 2);
+      case T_MLA_KVAPP: return (int64_t)s.kv_lora_rank + s.qk_rope;
+      case T_MLA_ABSORB: return (int64_t)s.n_q_heads * (s.kv_lora_rank / std::min(kAbsorbBlock, s.kv_lora_rank));
+      case T_MLA_UV: return (int64_t)s.n_q_heads * s.v_head;
+      case T_ROUTER: case T_TOPK: return s.n_routed;
+      case T_SHARED_GU: return (int64_t)s.n_shared * s.expert_ffn;
+      case T_EXPERT_GU: return (int64_t)s.top_k * s.expert_ffn;
+    }
+    return -1;
+  };
+  std::set<std::pair<int, int>> seen;  // (layer, type) present
+  for (auto& kv : ranges) {
+    auto v = kv.second;
+    std::sort(v.begin(), v.end());
+    int64_t at = 0;
+    for (auto& r : v) {
+      if (r.first != at || r.second <= r.first) { e << "coverage gap/overlap in layer " << kv.first.layer << " type " << kv.first.type; return e.str(); }
+      at = r.second;
+    }
+    if (at != expected(kv.first.type)) { e << "coverage of type " << kv.first.type << " in layer " << kv.first.layer << " ends at " << at; return e.str(); }
+    seen.insert({kv.first.layer, kv.first.type});
+  }
+  // every layer has its full set of stages
+  std::vector<int> need;
+  if (s.arch == DEC_ARCH_GQA) need = {T_QKV, T_ATTN, T_OPROJ, T_GATEUP, T_DOWN};
+  else {
+    need = {T_MLA_A, T_MLA_B, T_MLA_KVAPP, T_MLA_ABSORB, T_MLA_ATTN, T_MLA_UV, T_OPROJ};
+    if (s.arch == DEC_ARCH_MLA) { need.push_back(T_GATEUP); need.push_back(T_DOWN); }
+    else { need.push_back(T_ROUTER); need.push_back(T_TOPK); need.push_back(T_EXPERT_GU); need.push_back(T_MOE_DOWN);
+           if (s.n_shared > 0) need.push_back(T_SHARED_GU); }
+  }
+  for (int l = 0; l < s.n_layers; ++l)
+    for (int t : need)
+      if (!seen.count({l, t})) { e << "layer " << l << " lacks task type " << t; return e.str(); }
+  if (s.vocab > 0 && !seen.count({s.n_layers, (int)T_LMHEAD})) return "no LM head tasks";
+  return "";
+}
+
+}  // namespace dec

@@ -1,0 +1,70 @@
+// planner.h -- ahead-of-time planner of one batch-1 decode step (host only, no HIP).
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dec.h"
+#include "plan_types.h"
+
+namespace dec {
+
+struct WeightSpec {
+  std::string name;
+  int32_t dtype;
+  std::vector<int64_t> dims;
+  int64_t bytes;
+};
+
+struct BufferSpec {
+  std::string name;
+  int32_t dtype;
+  int64_t offset;   // bytes from the workspace base
+  int64_t count;    // elements
+};
+
+struct TaskInfo {   // planner-side description of one task (introspection / validation)
+  int32_t stage;
+  int32_t wg;
+  int32_t list_pos;
+};
+
+struct PlanData {
+  dec_model_shape shape{};
+  int64_t kv_len = 0;
+  dec_device_info dev{};
+  int32_t n_wg = 0, threads = kThreads, lds_bytes = 0;
+
+  std::vector<WeightSpec> weights;
+  std::vector<TaskDesc> tasks;        // grouped by workgroup, in list order
+  std::vector<TaskInfo> info;         // parallel to tasks
+  std::vector<int32_t> wg_begin;      // n_wg + 1
+  std::vector<DepEntry> deps;
+  std::vector<uint32_t> counter_total;
+  std::vector<LayerDesc> layers;
+  std::vector<float> rope_cs;         // cos then sin, rope_half each
+  std::vector<BufferSpec> buffers;
+  int32_t n_log = 0;                  // task ids + ticket-merge ids
+  int64_t xs_floats = 0;              // LDS floats for the largest staged input vector
+  int32_t rope_half = 0;
+  int32_t w_final_norm = -1, w_lm_head = -1, x_final = -1;
+  float attn_scale_log2 = 0.f;
+
+  // workspace layout (bytes)
+  int64_t off_ctl = 0, off_counters = 0, off_tasks = 0, off_wgb = 0, off_deps = 0,
+          off_wptr = 0, off_layers = 0, off_rope = 0, off_log = 0, off_act = 0, ws_bytes = 0;
+  int64_t act_floats = 0;
+
+  int64_t weight_bytes = 0, alg_bytes = 0;
+};
+
+// Validate the shape and build the plan. Returns DEC_OK or an error (message in *err).
+dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev,
+                      PlanData* out, std::string* err);
+
+// Structural checks of a built plan: list order vs stage order, producers before
+// consumers, counter totals, unit coverage. Returns an empty string when all hold.
+std::string validate_plan(const PlanData& p);
+
+}  // namespace dec

@@ -1,0 +1,73 @@
+"""Torch-facing helper around the C ABI: PyTorch supplies device memory and streams only.
+
+Every step of the decode path runs in the HIP engine kernel of libdec.so; this module only
+allocates buffers, checks their shapes against the plan's layout contract and forwards
+pointers.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+from . import binding as B
+
+_TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32"}
+
+
+class DecodeEngine:
+    def __init__(self, cfg: dict, weights: Dict[str, "object"], kv_len: Optional[int] = None,
+                 stream=None, watchdog_us: Optional[int] = None):
+        import torch
+        if not torch.cuda.is_available():
+            raise RuntimeError("DecodeEngine needs a GPU (gfx950); there is no CPU path")
+        self.torch = torch
+        self.cfg = cfg
+        self.kv_len = cfg["kv_len"] if kv_len is None else int(kv_len)
+        self.plan = B.Plan(cfg, self.kv_len)
+        if watchdog_us is not None:
+            self.plan.set_watchdog(watchdog_us)
+        self.descs = self.plan.weight_descs()
+        ptrs = []
+        self._keep = []
+        for d in self.descs:
+            t = weights[d["name"]]
+            want = getattr(torch, _TORCH_DTYPE[d["dtype"]])
+            if t.dtype != want or tuple(t.shape) != tuple(d["shape"]) or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"weight {d['name']}: expected contiguous cuda {want} {d['shape']}, "
+                                 f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+            ptrs.append(t.data_ptr())
+            self._keep.append(t)
+        self.sizes = self.plan.sizes()
+        self.workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        self.plan.bind(ptrs, self.workspace.data_ptr(), self.workspace.numel(), self.stream.cuda_stream)
+        self.buffers = self.plan.buffers()
+        out_n = cfg["vocab"] if cfg.get("vocab", 0) > 0 else cfg["hidden"]
+        self.out = torch.empty(out_n, dtype=torch.float32, device="cuda")
+
+    def step(self, x, kv, out=None):
+        """One decode step: x bf16 [hidden], kv bf16 cache (written at slot kv_len)."""
+        torch = self.torch
+        out = self.out if out is None else out
+        if x.dtype != torch.bfloat16 or x.numel() * 2 != self.sizes["x_bytes"] or not x.is_contiguous():
+            raise ValueError("x must be a contiguous bf16 vector of length hidden")
+        if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
+            raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+        if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"]:
+            raise ValueError("out must be fp32 of length vocab (or hidden)")
+        self.plan.step(x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.stream.cuda_stream)
+        return out
+
+    def status(self):
+        self.plan.status(self.stream.cuda_stream)
+
+    def buffer(self, name: str):
+        """A view of a named workspace buffer (per-layer intermediates of the last step)."""
+        torch = self.torch
+        b = self.buffers[name]
+        nbytes = b["count"] * 4
+        raw = self.workspace[b["offset"]:b["offset"] + nbytes]
+        return raw.view(torch.int32 if b["dtype"] == "i32" else torch.float32)
+
+    def task_log(self):
+        """[n_log, 8] int64: execs, epoch, wg, xcd, t_start, t_ready, t_end, reserved."""
+        return self.buffer("task_log").view(-1, 8).to(self.torch.int64) & 0xFFFFFFFF

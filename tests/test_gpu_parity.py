@@ -1,0 +1,198 @@
+"""GPU parity of the persistent decode engine against the fp64 oracle (needs an MI355X).
+
+Inputs are generated on the device from one seed; the oracle reads the same bits after a
+device-to-host copy. Bars (from the benchmark spec of this engine): relative L2 error
+<= 1e-2 on every per-layer vector of the trace (attention output and FFN branch included)
+and <= 2e-2 on the final logits; the written KV slot matches the oracle's bf16 rounding to
+within one bf16 ulp (the two sides round values that differ by fp32 accumulation order);
+every planned task, and every ticket merge, executes exactly once per step.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+LAYER_TOL = 1e-2
+LOGIT_TOL = 2e-2
+
+
+def _engine():
+    from persistent_tile_scheduled_amd.engine import DecodeEngine
+    return DecodeEngine
+
+
+def rel_l2(got, want):
+    got = np.asarray(got, dtype=np.float64).ravel()
+    want = np.asarray(want, dtype=np.float64).ravel()
+    return float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+
+
+class HostWeights:
+    """Oracle weight accessor that copies device tensors to the host on demand."""
+
+    def __init__(self, w):
+        self.w = w
+        self.cache = {}
+
+    def __call__(self, name, index=None):
+        key = (name, index)
+        if key not in self.cache:
+            t = self.w[name] if index is None else self.w[name][index]
+            if t.dtype == torch.bfloat16:
+                self.cache[key] = workloads.bf16_bits(t)
+            else:
+                self.cache[key] = t.detach().cpu().numpy()
+        return self.cache[key]
+
+    def drop(self, prefix):
+        for k in [k for k in self.cache if k[0].startswith(prefix)]:
+            del self.cache[k]
+
+
+TRACE_GQA = {"q": "q", "attn": "attn", "h": "h", "ffn_act": "ffn_act", "ffn_out": "ffn_out", "x_out": "x_out"}
+
+
+def check_layer_trace(eng, l, t, names, tol=LAYER_TOL):
+    errs = {}
+    for buf, key in names.items():
+        got = eng.buffer(f"layers.{l}.{buf}").cpu().numpy()[: t[key].size]
+        errs[buf] = rel_l2(got, t[key])
+        assert errs[buf] <= tol, (l, buf, errs[buf])
+    return errs
+
+
+def check_kv_slot(cfg, kv_host_bits, l, t):
+    n = cfg["kv_len"]
+    if cfg["arch"] == "gqa":
+        got_k = kv_host_bits[l, 0, :, n, :].reshape(-1).astype(np.int32)
+        got_v = kv_host_bits[l, 1, :, n, :].reshape(-1).astype(np.int32)
+        want_k = t["k_new_bits"].astype(np.int32)
+        want_v = t["v_new_bits"].astype(np.int32)
+        # same sign and within one bf16 ulp (adjacent bit patterns)
+        assert np.max(np.abs(got_k - want_k)) <= 1, l
+        assert np.max(np.abs(got_v - want_v)) <= 1, l
+        assert np.mean(got_k == want_k) > 0.95 and np.mean(got_v == want_v) > 0.95
+    else:
+        got = kv_host_bits[l, n, :].astype(np.int32)
+        want = t["kv_new_bits"].astype(np.int32)
+        assert np.max(np.abs(got - want)) <= 1, l
+        assert np.mean(got == want) > 0.95
+
+
+def check_coverage(eng, steps=1):
+    log = eng.task_log().cpu().numpy()
+    execs = log[:, 0]
+    assert np.all(execs == steps), (np.unique(execs, return_counts=True))
+    # every task saw its dependencies before it finished
+    assert np.all(((log[:, 6] - log[:, 4]) & 0xFFFFFFFF) < (1 << 31))
+
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("tiny_gain", 2), ("tiny_kv0", 0),
+                                       ("tiny_mha_ragged", 0), ("small_gqa", 0)])
+def test_small_gqa_full_parity(name, seed):
+    print(f"[parity] {name} seed={seed}", flush=True)
+    cfg = workloads.get_config(name)
+    w, x, kv = workloads.generate(cfg, seed=seed, device="cuda")
+    eng = _engine()(cfg, w)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    kvb = workloads.bf16_bits(kv)
+    res = O.forward(cfg, W, workloads.bf16_bits(x), kvb)
+    for l, t in enumerate(res["layers"]):
+        check_layer_trace(eng, l, t, TRACE_GQA)
+        check_kv_slot(cfg, kvb, l, t)
+    assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
+    check_coverage(eng)
+
+
+def test_multi_step_changing_input():
+    """Three steps with different inputs: each matches the oracle (epochs, counters and the
+    cross-XCD visibility of activations are exercised across steps)."""
+    cfg = workloads.get_config("small_gqa")
+    w, x, kv = workloads.generate(cfg, seed=7, device="cuda")
+    eng = _engine()(cfg, w)
+    W = HostWeights(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    for step in range(3):
+        print(f"[multi-step] step {step}", flush=True)
+        xs = (torch.randn(cfg["hidden"], generator=g, device="cuda") * (1 + step)).to(torch.bfloat16)
+        out = eng.step(xs, kv).clone()
+        torch.cuda.synchronize()
+        eng.status()
+        kvb = workloads.bf16_bits(kv)
+        res = O.forward(cfg, W, workloads.bf16_bits(xs), kvb)
+        assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL, step
+        for l, t in enumerate(res["layers"]):
+            check_layer_trace(eng, l, t, TRACE_GQA)
+    check_coverage(eng, steps=3)
+
+
+def test_watchdog_timeout_then_reset():
+    """A host-forced 1 us watchdog makes dependency waits time out; every workgroup drains,
+    the sticky status reports DEC_E_TIMEOUT, and after a reset the next step is correct."""
+    from persistent_tile_scheduled_amd import binding as B
+    cfg = workloads.get_config("small_gqa")
+    w, x, kv = workloads.generate(cfg, seed=3, device="cuda")
+    eng = _engine()(cfg, w)
+    eng.plan.set_watchdog(1)
+    eng.step(x, kv)
+    torch.cuda.synchronize()
+    with pytest.raises(B.DecError) as e:
+        eng.status()
+    assert B.STATUS[e.value.status] == "DEC_E_TIMEOUT"
+    eng.plan.set_watchdog(2_000_000)
+    eng.plan.reset(eng.stream.cuda_stream)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    res = O.forward(cfg, HostWeights(w), workloads.bf16_bits(x), workloads.bf16_bits(kv))
+    assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
+
+
+def _teacher_forced_check(name, layers):
+    """Full-size config in the bench's launch configuration: for sampled layers, the oracle
+    recomputes the layer from the GPU's own layer input and every intermediate is compared;
+    the LM head is checked from the GPU's final hidden state."""
+    cfg = workloads.get_config(name)
+    print(f"[parity] {name}: generating", flush=True)
+    w, x, kv = workloads.generate(cfg, seed=0, device="cuda")
+    eng = _engine()(cfg, w)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    n = cfg["kv_len"]
+    for l in layers:
+        print(f"[parity] {name}: layer {l}", flush=True)
+        x_in = workloads.bf16_bits(x) if l == 0 else None
+        xin = O.widen_bf16(x_in) if l == 0 else eng.buffer(f"layers.{l - 1}.x_out").cpu().numpy().astype(np.float64)
+        kvl = workloads.bf16_bits(kv[l])
+        _, t = O.gqa_layer(cfg, W, l, xin, kvl, n)
+        errs = check_layer_trace(eng, l, t, TRACE_GQA)
+        print(f"[parity] layer {l} rel errors {errs}", flush=True)
+        check_kv_slot(cfg, kvl[None], 0, t)
+        W.drop(f"layers.{l}.")
+    print(f"[parity] {name}: LM head", flush=True)
+    xf = eng.buffer(f"layers.{cfg['n_layers'] - 1}.x_out").cpu().numpy().astype(np.float64)
+    hd = O.head(cfg, W, xf)
+    err = rel_l2(out.cpu().numpy(), hd["out"])
+    print(f"[parity] logits rel error {err:.3e}", flush=True)
+    assert err <= LOGIT_TOL
+    check_coverage(eng)
+
+
+def test_8b_4k_sampled_layers():
+    _teacher_forced_check("8b_4k", [0, 1, 31])
+
+
+def test_8b_32k_sampled_layers():
+    _teacher_forced_check("8b_32k", [0, 31])

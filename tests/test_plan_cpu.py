@@ -1,0 +1,241 @@
+"""Host-side tests of the C ABI and the ahead-of-time planner (no GPU needed).
+
+The library is loaded and its planner runs on a described device (dec_plan_create_for), so
+these run on a machine without a GPU. No compute entry point is called here.
+"""
+import collections
+import os
+import re
+
+import pytest
+
+import workloads
+from persistent_tile_scheduled_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MI355X = B.device_info()
+GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k"]
+
+
+def plan(name, dev=MI355X, **over):
+    cfg = dict(workloads.get_config(name))
+    cfg.update(over)
+    return B.Plan(cfg, device=dev), cfg
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "dec.h")).read()
+    declared = set(re.findall(r"^\s*(?:dec_status|int64_t|const char\*)\s+(dec_\w+)\s*\(", hdr, re.M))
+    assert len(declared) >= 20
+    L = B.lib()
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+    assert declared == set(B.ABI_SYMBOLS)
+
+
+@pytest.mark.parametrize("name", GQA_CONFIGS)
+def test_weight_list_matches_input_layout(name):
+    p, cfg = plan(name)
+    got = [(d["name"], d["shape"], d["dtype"]) for d in p.weight_descs()]
+    want = [(s.name, s.shape, s.dtype) for s in workloads.weight_specs(cfg)]
+    assert got == want
+    assert p.sizes()["weight_bytes"] == sum(s.nbytes for s in workloads.weight_specs(cfg))
+
+
+def test_algorithmic_bytes():
+    # weights once + KV positions [0, kv_len] once (the step attends over kv_len + 1 positions)
+    p, cfg = plan("8b_4k")
+    s = p.sizes()
+    assert s["weight_bytes"] == 15_009_849_344
+    assert s["algorithmic_bytes_per_step"] == 15_009_849_344 + 32 * 2 * 8 * 4097 * 128 * 2
+    p, cfg = plan("8b_32k")
+    assert p.sizes()["algorithmic_bytes_per_step"] == 15_009_849_344 + 32 * 2 * 8 * 32769 * 128 * 2
+    assert p.sizes()["kv_bytes"] == 32 * 2 * 8 * 32769 * 128 * 2
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"hidden": 260}, "DEC_E_SHAPE"),
+    ({"n_q_heads": 6, "n_kv_heads": 4}, "DEC_E_SHAPE"),
+    ({"n_q_heads": 16, "n_kv_heads": 2}, "DEC_E_SHAPE"),     # 8 q heads per KV head: unsupported
+    ({"head_dim": 48}, "DEC_E_SHAPE"),
+    ({"ffn": 0}, "DEC_E_SHAPE"),
+    ({"rms_eps": 0.0}, "DEC_E_SHAPE"),
+    ({"kv_len": -1}, "DEC_E_CAPACITY"),
+    ({"q_lora_rank": 64}, "DEC_E_SHAPE"),                      # MLA field on a GQA shape
+])
+def test_shape_errors(over, status):
+    with pytest.raises(B.DecError) as e:
+        plan("tiny", **over)
+    assert B.STATUS[e.value.status] == status
+
+
+def test_abi_version_and_device_errors():
+    cfg = workloads.get_config("tiny")
+    s = B.shape_from_config(cfg)
+    s.abi_version = 99
+    with pytest.raises(B.DecError) as e:
+        B.Plan(s, 128, device=MI355X)
+    assert B.STATUS[e.value.status] == "DEC_E_INVAL"
+    with pytest.raises(B.DecError) as e:
+        plan("tiny", dev=B.device_info(gfx_arch=942))
+    assert B.STATUS[e.value.status] == "DEC_E_DEVICE"
+    with pytest.raises(B.DecError) as e:
+        plan("tiny", dev=B.device_info(lds=64 * 1024))
+    assert B.STATUS[e.value.status] == "DEC_E_OCCUPANCY"
+    with pytest.raises(B.DecError) as e:
+        plan("tiny", dev=B.device_info(max_threads=256))
+    assert B.STATUS[e.value.status] == "DEC_E_OCCUPANCY"
+
+
+def test_step_before_bind_and_null_arguments():
+    p, _ = plan("tiny")
+    with pytest.raises(B.DecError) as e:
+        p.step(0x1000, 0x1000, 0x1000)
+    assert B.STATUS[e.value.status] == "DEC_E_UNBOUND"
+    L = B.lib()
+    import ctypes as C
+    assert L.dec_plan_create(None, 0, None) == -1
+    assert L.dec_plan_destroy(None) == 0
+    with pytest.raises(B.DecError) as e:
+        p.bind([0] * len(p.weight_descs()), 0, 0)
+    assert B.STATUS[e.value.status] == "DEC_E_INVAL"
+    with pytest.raises(B.DecError) as e:
+        p.bind([0x100] * 3, 0x1000, 1 << 30)
+    assert B.STATUS[e.value.status] == "DEC_E_INVAL"
+    with pytest.raises(B.DecError) as e:
+        p.set_watchdog(0)
+    assert B.STATUS[e.value.status] == "DEC_E_INVAL"
+
+
+def _expected_units(cfg, ttype):
+    n1 = cfg["kv_len"] + 1
+    return {
+        "QKV": (cfg["n_q_heads"] // max(cfg.get("n_kv_heads", 1), 1) + 2) * cfg.get("head_dim", 0) // 2,
+        "ATTN": n1, "OPROJ": cfg["hidden"], "DOWN": cfg["hidden"], "GATEUP": cfg.get("ffn", 0),
+        "LMHEAD": cfg["vocab"],
+    }[ttype]
+
+
+def simulate(p):
+    """Run one step of the static schedule on the CPU: every workgroup walks its list in order
+    and a task runs once all its counters have reached their per-step totals. Returns the
+    execution order; raises if the schedule stalls (a deadlock)."""
+    tasks = p.tasks()
+    deps = p.deps()
+    n_wg = p.grid()[0]
+    lists = collections.defaultdict(list)
+    for t in tasks:
+        lists[t["wg"]].append(t)
+    for w in lists:
+        lists[w].sort(key=lambda t: t["list_pos"])
+    ctr = collections.Counter()
+    tickets = collections.Counter()
+    pos = {w: 0 for w in range(n_wg)}
+    done = []
+    progress = True
+    while progress:
+        progress = False
+        for w in range(n_wg):
+            while pos[w] < len(lists[w]):
+                t = lists[w][pos[w]]
+                if not all(ctr[deps[t["dep_first"] + k][0]] >= deps[t["dep_first"] + k][1] for k in range(t["n_deps"])):
+                    break
+                if t["signal"] >= 0:
+                    ctr[t["signal"]] += 1
+                if t["signal2"] >= 0:  # ticket merge: the last of the group's splits signals
+                    tickets[t["signal"]] += 1
+                    n_splits = sum(1 for u in tasks if u["signal"] == t["signal"])
+                    if tickets[t["signal"]] == n_splits:
+                        ctr[t["signal2"]] += 1
+                done.append(t["id"])
+                pos[w] += 1
+                progress = True
+    stuck = [w for w in range(n_wg) if pos[w] < len(lists[w])]
+    if stuck:
+        raise AssertionError(f"schedule stalls: {len(stuck)} workgroups blocked")
+    return done
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k"])
+def test_schedule_drains_and_covers(name):
+    p, cfg = plan(name)
+    tasks = p.tasks()
+    order = simulate(p)
+    assert sorted(order) == sorted(t["id"] for t in tasks)  # each task exactly once
+    # unit coverage per (layer, type, group): ranges tile [0, expected) exactly once
+    cov = collections.defaultdict(list)
+    for t in tasks:
+        ty = B.TASK_TYPES[t["type"]]
+        grp = t["aux0"] if ty in ("QKV", "ATTN") else 0
+        cov[(t["layer"], ty, grp)].append((t["unit_begin"], t["unit_end"]))
+    for (layer, ty, grp), rs in cov.items():
+        rs.sort()
+        at = 0
+        for a, b in rs:
+            assert a == at and b > a, (layer, ty, grp)
+            at = b
+        assert at == _expected_units(cfg, ty), (layer, ty)
+    n_layers = cfg["n_layers"]
+    for layer in range(n_layers):
+        for ty in ("QKV", "ATTN", "OPROJ", "GATEUP", "DOWN"):
+            assert (layer, ty, 0) in cov
+    assert (n_layers, "LMHEAD", 0) in cov
+
+
+def test_lists_in_stage_order_and_deps_point_back():
+    p, _ = plan("small_gqa")
+    tasks = p.tasks()
+    deps = p.deps()
+    producers = collections.defaultdict(list)
+    for t in tasks:
+        if t["signal"] >= 0:
+            producers[t["signal"]].append(t)
+        if t["signal2"] >= 0:
+            producers[t["signal2"]].append(t)
+    by_wg = collections.defaultdict(list)
+    for t in tasks:
+        by_wg[t["wg"]].append(t)
+    for w, lst in by_wg.items():
+        lst.sort(key=lambda t: t["list_pos"])
+        assert [t["stage"] for t in lst] == sorted(t["stage"] for t in lst)
+    for t in tasks:
+        for k in range(t["n_deps"]):
+            c, total = deps[t["dep_first"] + k]
+            assert producers[c], "waits on a counter nobody signals"
+            assert all(pt["stage"] < t["stage"] for pt in producers[c])
+            n_sig = sum(1 for pt in producers[c] if pt["signal"] == c)
+            assert total == (1 if n_sig == 0 else n_sig)
+
+
+def test_chiplet_placement_8b():
+    """Each KV-head group's QKV rows and attention splits run on the workgroups of one XCD."""
+    p, cfg = plan("8b_4k")
+    for t in p.tasks():
+        ty = B.TASK_TYPES[t["type"]]
+        if ty in ("QKV", "ATTN"):
+            assert t["xcd"] == t["aux0"], t
+    # and every workgroup gets work in every dense stage
+    per_stage = collections.defaultdict(set)
+    for t in p.tasks():
+        per_stage[(t["layer"], B.TASK_TYPES[t["type"]])].add(t["wg"])
+    for (layer, ty), wgs in per_stage.items():
+        if ty in ("OPROJ", "GATEUP", "DOWN", "QKV", "ATTN", "LMHEAD"):
+            assert len(wgs) == 256, (layer, ty, len(wgs))
+
+
+@pytest.mark.parametrize("n_cu,n_xcd", [(64, 2), (80, 4), (8, 8), (304, 8)])
+def test_other_device_shapes(n_cu, n_xcd):
+    p, cfg = plan("small_gqa", dev=B.device_info(n_cu=n_cu, n_xcd=n_xcd))
+    assert p.grid()[0] == n_cu
+    simulate(p)
+
+
+def test_buffers_cover_trace():
+    p, cfg = plan("tiny")
+    bufs = p.buffers()
+    for l in range(cfg["n_layers"]):
+        for nm in ("q", "kv_new", "attn", "h", "ffn_act", "ffn_out", "x_out"):
+            assert f"layers.{l}.{nm}" in bufs
+    ws = p.sizes()["workspace_bytes"]
+    for b in bufs.values():
+        assert b["offset"] % 256 == 0 and b["offset"] + b["count"] * 4 <= ws
