@@ -73,15 +73,34 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ void acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 __device__ __forceinline__ void release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Cross-lane sums with DPP (VALU lane permutes, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm(1,0,3,2): lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm(2,3,0,1): lane ^ 2
+constexpr int kRowHalfMirror = 0x141; // reverse within 8-lane halves of a row
+constexpr int kRowMirror = 0x140;     // reverse within a 16-lane row
+
+// Sum over aligned groups of W lanes (W = 1..64, a power of two); every lane of a group
+// gets the group's sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if (W >= 2) v += dpp<kQuadSwap1>(v);
+  if (W >= 4) v += dpp<kQuadSwap2>(v);
+  if (W >= 8) v += dpp<kRowHalfMirror>(v);   // after the quad sums: quad q gets quad q^1
+  if (W >= 16) v += dpp<kRowMirror>(v);      // after the 8-lane sums: half h gets half h^1
+  if (W >= 32) v += __shfl_xor(v, 16, 64);
+  if (W >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
-// sum within aligned groups of `w` lanes (w a power of two <= 64)
-__device__ __forceinline__ float group_sum(float v, int w) {
-  for (int m = 1; m < w; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+// Full 64-lane sum, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const int b = __float_as_int(v);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -217,7 +236,7 @@ __device__ __forceinline__ void stage_vec(Blk& b, const float* s32, const uint16
 
 // ------------------------------------------------------------------ streaming row GEMV
 
-constexpr int NB = 8;  // 16-byte chunks per batch per lane (8 KB per wave per batch)
+constexpr int NB = 16;  // 16-byte chunks per batch per lane (16 KB per wave per batch)
 
 // Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
 // columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
@@ -297,6 +316,14 @@ __device__ __forceinline__ void fill_rows(const RM& rm, int ja, int jb, uint64_t
   }
 }
 
+// Work split over the waves of a workgroup. Wave 0 polls the dependency counters, and a
+// poll cannot complete before that wave's earlier loads (vmcnt counts in issue order), so
+// wave 0 streams nothing: it polls, helps stage the input vector and signals, while waves
+// 1..7 prefetch and stream. Returns the start of wave `w`'s part of [0, n).
+__device__ __forceinline__ int wave_start(int n, int w) {
+  return (w == 0) ? 0 : (int)(((int64_t)n * (w - 1)) / (kWaves - 1));
+}
+
 // The shared skeleton of every GEMV task. Rows are split over the waves in whole groups of
 // G rows (G consecutive rows are summed into one result ys[j / G]). With `prefetch`, the
 // row map may not depend on anything this task waits for: the first two batches are issued
@@ -306,7 +333,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
                                          int K, int G, bool prefetch, StageF&& stage, EpiF&& epi) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
-  const int ja = (ng * wave / kWaves) * G, jb = (ng * (wave + 1) / kWaves) * G;
+  const int ja = wave_start(ng, wave) * G, jb = wave_start(ng, wave + 1) * G;
   Stream s;
   u4 b0[NB], b1[NB];
   if (prefetch) {
@@ -423,47 +450,96 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
       });
 }
 
+// Merge S split partials (m, l, acc[hd]) of H heads into o[h][d] = sum_s e^(m_s-M) acc_s /
+// sum_s e^(m_s-M) l_s (base-2 exponents). All loads of a phase are independent 16-byte
+// loads issued together, so the merge costs a few memory round trips, not S of them.
+__device__ __forceinline__ void merge_splits(const EngineArgs& A, Blk& b, const float* parts, int S, int H, int hd,
+                                             float* o) {
+  const int ps = hd + 4;          // m, l, 2 pad, acc[hd]: acc stays 16-byte aligned
+  float* wts = b.scr;             // [S][H] weights e^(m_s - M_h)
+  float* den = b.scr + S * H;     // [H] sum of weighted l
+  float* acc = den + H;           // [4][H*hd] partial numerators per split quarter
+  for (int i = threadIdx.x; i < S * H; i += kThreads) wts[i] = parts[(size_t)(i / H) * H * ps + (i % H) * ps];
+  __syncthreads();
+  for (int h = threadIdx.x; h < H; h += kThreads) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wts[sp * H + h]);
+    float dsum = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float e = exp2f(wts[sp * H + h] - M);
+      wts[sp * H + h] = e;
+      dsum += e * parts[(size_t)sp * H * ps + h * ps + 1];
+    }
+    den[h] = dsum;
+  }
+  __syncthreads();
+  // thread -> (quarter of the splits, head, 4 consecutive dims)
+  const int nd4 = H * hd / 4;
+  for (int i = threadIdx.x; i < 4 * nd4; i += kThreads) {
+    const int q = i / nd4, j = i - q * nd4, h = (j * 4) / hd, d = j * 4 - h * hd;
+    f4 sum = f4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = q; sp < S; sp += 4) {
+      const f4 v = *(const f4*)(parts + (size_t)sp * H * ps + h * ps + 4 + d);
+      sum += v * wts[sp * H + h];
+    }
+    *(f4*)(acc + q * H * hd + j * 4) = sum;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < H * hd; i += kThreads) {
+    const int h = i / hd;
+    o[i] = (acc[i] + acc[H * hd + i] + acc[2 * H * hd + i] + acc[3 * H * hd + i]) / den[h];
+  }
+}
+
 // Split-K attention of one KV group over positions [u0, u1): the group's R query heads share
-// every K/V load. Each lane group of hd/8 lanes holds one position's row (8 dims per lane);
-// positions advance by a wave-instruction's worth of rows per iteration. Online softmax in
-// base 2 per head; partials are merged across lane groups, waves, and then -- by whichever
-// split task arrives last at the group's ticket -- across splits.
-template <int R>
+// every K/V load. A group of LPP = hd/8 lanes holds one position's row (8 dims per lane);
+// one wave instruction covers 64/LPP consecutive positions. Online softmax in base 2 per
+// head; partials are merged across lane groups, waves, and then -- by whichever split task
+// arrives last at the group's ticket -- across splits. The cached positions of the first two
+// blocks are loaded before the dependency wait; a block holding the new position (slot
+// kv_len, written by this step's QKV tasks) is loaded again after it.
+template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  constexpr int GPW = 64 / LPP, NP = 2, PER_BLK = NP * GPW;
   const LayerDesc& L = A.layers[t.layer];
-  const int hd = A.hd, r = A.nq / A.nkv, g = t.a0, n = A.kv_len, n1 = n + 1;
-  const int LPP = hd >> 3, GPW = 64 / LPP;
+  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = A.kv_len, n1 = n + 1;
   const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
   const int p0 = t.u0, np = t.u1 - t.u0;
-  const int q0 = p0 + np * wave / kWaves, q1 = p0 + np * (wave + 1) / kWaves;
+  const int q0 = p0 + wave_start(np, wave), q1 = p0 + wave_start(np, wave + 1);
   const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
   const uint16_t* Vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
-  constexpr int NP = 4;
-  const int per_blk = NP * GPW;
-  const int nblk = (q1 > q0) ? (q1 - q0 + per_blk - 1) / per_blk : 0;
-  u4 ka[NP], va[NP], kb2[NP], vb2[NP];
-  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
+  const int nblk = (q1 > q0) ? (q1 - q0 + PER_BLK - 1) / PER_BLK : 0;
+  u4 ka[NP], va[NP], kb[NP], vb[NP];
+  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP], int lim) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       int pos = q0 + (blk * NP + i) * GPW + grp;
-      pos = pos < q1 ? pos : q1 - 1;
+      pos = pos < lim ? pos : lim - 1;
+      pos = pos > 0 ? pos : 0;
       kk[i] = ldg_nt(Kb + (size_t)pos * hd);
       vv[i] = ldg_nt(Vb + (size_t)pos * hd);
     }
   };
-  // the newest position (slot n) is written by this step's QKV tasks: only blocks that end
-  // before it may be loaded ahead of the dependency wait
-  const bool pre = nblk > 0 && (q0 + per_blk - 1 < n);
-  if (pre) load(0, ka, va);
+  // cached rows only (positions < n) before the wait
+  const int pre_lim = (q1 < n) ? q1 : n;
+  load(0, ka, va, pre_lim);
+  load(1, kb, vb, pre_lim);
   if (!wait_deps(A, b, t)) return false;
-  if (nblk > 0 && !pre) load(0, ka, va);
+  if (nblk > 0 && q0 + PER_BLK > pre_lim) load(0, ka, va, q1);
+  if (nblk > 1 && q0 + 2 * PER_BLK > pre_lim) load(1, kb, vb, q1);
 
   float qv[R][8];
   const float* qbase = actp(A, L.act[LA_Q]) + (size_t)g * r * hd + sub * 8;
 #pragma unroll
   for (int h = 0; h < R; ++h) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) qv[h][d] = (h < r) ? qbase[h * hd + d] * A.attn_scale_log2 : 0.f;
+    f4 a = f4{0.f, 0.f, 0.f, 0.f}, c = a;
+    if (h < r) {
+      a = *(const f4*)(qbase + h * hd);
+      c = *(const f4*)(qbase + h * hd + 4);
+    }
+    const float sc = A.attn_scale_log2;
+    qv[h][0] = a.x * sc; qv[h][1] = a.y * sc; qv[h][2] = a.z * sc; qv[h][3] = a.w * sc;
+    qv[h][4] = c.x * sc; qv[h][5] = c.y * sc; qv[h][6] = c.z * sc; qv[h][7] = c.w * sc;
   }
   float m[R], l[R], acc[R][8];
 #pragma unroll
@@ -477,7 +553,6 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     float s[R][NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const bool valid = q0 + (blk * NP + i) * GPW + grp < q1;
       const u4 kw = kk[i];
       const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
                            bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
@@ -486,7 +561,15 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
         float p = 0.f;
 #pragma unroll
         for (int d = 0; d < 8; ++d) p = fmaf(qv[h][d], kf[d], p);
-        p = group_sum(p, LPP);
+        s[h][i] = p;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const bool valid = q0 + (blk * NP + i) * GPW + grp < q1;
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        const float p = group_sum<LPP>(s[h][i]);
         s[h][i] = valid ? p : -INFINITY;
       }
     }
@@ -520,16 +603,18 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     }
   };
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) load(blk + 1, kb2, vb2);
     step(blk, ka, va);
+    if (blk + 2 < nblk) load(blk + 2, ka, va, q1);
     if (blk + 1 >= nblk) break;
-    if (blk + 2 < nblk) load(blk + 2, ka, va);
-    step(blk + 1, kb2, vb2);
+    step(blk + 1, kb, vb);
+    if (blk + 3 < nblk) load(blk + 3, kb, vb, q1);
   }
+  const uint32_t t_mid = (uint32_t)now();
   // merge the lane groups of this wave (lanes with equal `sub` hold the same dims)
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     if (h >= r) continue;
+#pragma unroll
     for (int mask = LPP; mask < 64; mask <<= 1) {
       const float mo = __shfl_xor(m[h], mask, 64), lo = __shfl_xor(l[h], mask, 64);
       const float mn = fmaxf(m[h], mo);
@@ -544,8 +629,8 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
       m[h] = mn;
     }
   }
-  // per-wave partials to LDS: scr[wave][h][2 + hd]
-  const int ps = hd + 2;
+  // per-wave partials to LDS: scr[wave][h][4 + hd] (m, l, 2 pad, acc)
+  const int ps = hd + 4;
   float* wpart = b.scr + (size_t)wave * r * ps;
   if (grp == 0) {
 #pragma unroll
@@ -556,7 +641,7 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
         wpart[h * ps + 1] = l[h];
       }
 #pragma unroll
-      for (int d = 0; d < 8; ++d) wpart[h * ps + 2 + sub * 8 + d] = acc[h][d];
+      for (int d = 0; d < 8; ++d) wpart[h * ps + 4 + sub * 8 + d] = acc[h][d];
     }
   }
   __syncthreads();
@@ -565,15 +650,17 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
   for (int i = threadIdx.x; i < r * hd; i += kThreads) {
     const int h = i / hd, d = i - h * hd;
     float M = -INFINITY;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, b.scr[(size_t)w * r * ps + h * ps]);
     float num = 0.f, den = 0.f;
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float* pw = b.scr + (size_t)w * r * ps + h * ps;
       const float e = (pw[0] == -INFINITY) ? 0.f : exp2f(pw[0] - M);
-      num += e * pw[2 + d];
+      num += e * pw[4 + d];
       den += e * pw[1];
     }
-    gpart[h * ps + 2 + d] = num;
+    gpart[h * ps + 4 + d] = num;
     if (d == 0) {
       gpart[h * ps] = M;
       gpart[h * ps + 1] = den;
@@ -588,23 +675,12 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     if (b.flags[1]) acquire();
   }
   __syncthreads();
-  if (!b.flags[1]) return true;
-  const uint32_t tm0 = (uint32_t)now();
-  const float* parts = actp(A, t.a4);
-  float* o = actp(A, L.act[LA_ATTN]) + (size_t)g * r * hd;
-  for (int i = threadIdx.x; i < r * hd; i += kThreads) {
-    const int h = i / hd, d = i - h * hd;
-    float M = -INFINITY;
-    for (int sp = 0; sp < t.a2; ++sp) M = fmaxf(M, parts[(size_t)sp * r * ps + h * ps]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < t.a2; ++sp) {
-      const float* pp = parts + (size_t)sp * r * ps + h * ps;
-      const float e = exp2f(pp[0] - M);
-      num += e * pp[2 + d];
-      den += e * pp[1];
-    }
-    o[i] = num / den;
+  if (!b.flags[1]) {
+    if (threadIdx.x == 0) A.log[t.id].reserved = t_mid;
+    return true;
   }
+  const uint32_t tm0 = (uint32_t)now();
+  merge_splits(A, b, actp(A, t.a4), t.a2, r, hd, actp(A, L.act[LA_ATTN]) + (size_t)g * r * hd);
   signal(A, t.signal2);
   if (threadIdx.x == 0) {
     TaskLog* lg = A.log + t.a3;
@@ -617,6 +693,16 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     lg->t_end = (uint32_t)now();
   }
   return true;
+}
+
+template <int R>
+__device__ __forceinline__ bool task_attn_hd(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  switch (A.hd) {
+    case 32: return task_attn<R, 4>(A, b, t);
+    case 64: return task_attn<R, 8>(A, b, t);
+    case 128: return task_attn<R, 16>(A, b, t);
+    default: return task_attn<R, 32>(A, b, t);
+  }
 }
 
 __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const TaskDesc& t) {
@@ -709,7 +795,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
     switch (t.type) {
       case T_QKV: ok = task_qkv(A, b, t); break;
       case T_ATTN:
-        ok = rq <= 1 ? task_attn<1>(A, b, t) : rq <= 2 ? task_attn<2>(A, b, t) : task_attn<4>(A, b, t);
+        ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
         sig = -1;  // signalled through the ticket
         break;
       case T_OPROJ: ok = task_oproj(A, b, t); break;

@@ -143,9 +143,8 @@ struct Builder {
       if (q.n_q_heads < 1 || q.n_kv_heads < 1 || q.n_q_heads % q.n_kv_heads)
         return fail(DEC_E_SHAPE, "GQA needs n_q_heads a positive multiple of n_kv_heads", st);
       if (q.n_q_heads / q.n_kv_heads > 4) return fail(DEC_E_SHAPE, "more than 4 query heads per KV head", st);
-      int lpp = q.head_dim / 8;
-      if (q.head_dim % 8 || lpp < 1 || lpp > 64 || (lpp & (lpp - 1)))
-        return fail(DEC_E_SHAPE, "head_dim must be 8 * 2^k, at most 512", st);
+      if (q.head_dim != 32 && q.head_dim != 64 && q.head_dim != 128 && q.head_dim != 256)
+        return fail(DEC_E_SHAPE, "head_dim must be 32, 64, 128 or 256", st);
       if (q.ffn < 8 || q.ffn % 8) return fail(DEC_E_SHAPE, "ffn must be a positive multiple of 8", st);
       if (q.q_lora_rank || q.kv_lora_rank || q.qk_nope || q.qk_rope || q.v_head || q.n_routed || q.n_shared || q.top_k || q.expert_ffn)
         return fail(DEC_E_SHAPE, "GQA shape with MLA/MoE fields set", st);
@@ -268,10 +267,11 @@ struct Builder {
       S[g] = (int)std::min<int64_t>((int64_t)sets[g].size(), std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit));
       smax = std::max(smax, S[g]);
     }
-    const int64_t pstride = (int64_t)r * (hd + 2);
+    const int64_t pstride = (int64_t)r * (hd + 4);  // per split: r x (m, l, pad, pad, acc[hd])
     const int64_t part = act(p + "attn_partials", (int64_t)nkv * smax * pstride);
     L.act[LA_PART] = (int)part;
     scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * pstride + 64);
+    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)smax * r + r + 4LL * r * hd + 64);
     for (int g = 0; g < nkv; ++g) {
       const int merge_id = next_id++;
       for (int sp = 0; sp < S[g]; ++sp) {
