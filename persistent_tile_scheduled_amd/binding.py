@@ -21,7 +21,7 @@ DTYPE = {0: "bf16", 1: "fp32", 2: "i32"}
 # task type ids (mirror of the engine's TaskType enum)
 TASK_TYPES = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "MLA_A", 8: "MLA_B",
               9: "MLA_KVAPP", 10: "MLA_ABSORB", 11: "MLA_ATTN", 12: "MLA_UV", 13: "ROUTER", 14: "SHARED_GU",
-              15: "TOPK", 16: "EXPERT_GU", 17: "MOE_DOWN"}
+              15: "TOPK", 16: "EXPERT_GU", 17: "MOE_DOWN", 18: "OPROJ_G", 19: "HINIT"}
 
 
 class DecError(RuntimeError):
@@ -74,9 +74,10 @@ def lib() -> C.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: run `python -m persistent_tile_scheduled_amd.build` first")
-    L = C.CDLL(LIB_PATH)
+    path = os.environ.get("DEC_LIBRARY", LIB_PATH)  # an alternative build of the same ABI
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run `python -m persistent_tile_scheduled_amd.build` first")
+    L = C.CDLL(path)
     P = C.c_void_p
     sig = {
         "dec_last_error": (C.c_char_p, []),

@@ -24,21 +24,21 @@ def _run(cmd):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = True) -> str:
-    bdir = os.path.join(HERE, "_build")
+def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
+    bdir = os.path.join(HERE, "_build" + ("_" + "_".join(d.replace("=", "") for d in defines) if defines else ""))
     os.makedirs(bdir, exist_ok=True)
     objs = []
     for src, dev in [("engine.hip", True), ("planner.cpp", False), ("api.cpp", False)]:
         obj = os.path.join(bdir, src + ".o")
-        cmd = [HIPCC] + COMMON + (DEVICE + ["-x", "hip"] if dev else ["-x", "c++", "-D__HIP_PLATFORM_AMD__",
-                                                                       "-I/opt/rocm/include"])
+        cmd = [HIPCC] + COMMON + ["-D" + d for d in defines]
+        cmd += (DEVICE + ["-x", "hip"]) if dev else ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]
         cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + ["-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -80,6 +80,8 @@ void fill_args(dec_plan* p) {
   a.w_lm_head = P.w_lm_head;
   a.x_final = P.x_final;
   a.xs_floats = (int32_t)P.xs_floats;
+  a.act_bytes = (uint32_t)(P.act_floats * 4);
+  a.gs_floats = (int32_t)P.gs_floats;
   a.eps = s.rms_eps;
   a.attn_scale_log2 = P.attn_scale_log2;
 }

@@ -54,6 +54,57 @@ __device__ __forceinline__ int wave_id() { return uni((int)(threadIdx.x >> 6)); 
 typedef const u4 __attribute__((address_space(1)))* gu4p;
 __device__ __forceinline__ u4 ldg_nt(const void* p) { return __builtin_nontemporal_load((gu4p)p); }
 
+// Data exchanged between workgroups is written and read with agent-coherent (SC1) buffer
+// accesses: an SC1 store is complete only once it is visible at agent scope, and an SC1 load
+// never returns a stale line from this XCD's L2. A producer therefore publishes with
+// "s_waitcnt vmcnt(0); barrier; atomic add", and a consumer needs no cache invalidation --
+// neither the L2 write-back (buffer_wbl2) of an agent-scope release fence nor the L2
+// invalidate (buffer_inv) of an acquire fence, which measure 1-9 us each on MI355X.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSC1 = 16;          // cache-policy bit SC1 (agent scope)
+// Cache policy of loads of produced data. Every activation address is written once per step
+// (per-layer buffers, write-through SC1 stores) and read only after all of its writers have
+// signalled; lines cached by an earlier kernel are gone at the next launch (stream order).
+// So a reader's L2 never holds a stale copy, and plain L2-cached loads (0) are enough: the
+// 32 workgroups of an XCD then share one fetch of a broadcast vector.
+#ifndef DEC_ACT_CPOL
+#define DEC_ACT_CPOL 0
+#endif
+constexpr int kActCpol = DEC_ACT_CPOL;
+constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ float cld(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kActCpol));
+}
+__device__ __forceinline__ u4 cld4u(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kActCpol); }
+__device__ __forceinline__ f4 cld4(rsrc_t r, uint32_t off) { return __builtin_bit_cast(f4, cld4u(r, off)); }
+__device__ __forceinline__ void cst(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kSC1);
+}
+__device__ __forceinline__ void cst16(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kSC1);
+}
+__device__ __forceinline__ void cst4(rsrc_t r, uint32_t off, f4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kSC1);
+}
+
+// Wave-wide LDS DMA of `nfloats` floats (a multiple of 4) from global memory into LDS with
+// SC1 (coherent) loads; lane l of instruction j lands at dst[j*256 + 4l]. Lanes past the end
+// re-read the last 16 bytes and land in dst[nfloats, round_up(nfloats, 256)), which the
+// destination must have room for. Completion is tracked by vmcnt.
+typedef const void __attribute__((address_space(1)))* gvp;
+typedef void __attribute__((address_space(3)))* lvp;
+__device__ __forceinline__ void dma_to_lds(float* dst, const float* src, int nfloats) {
+  const int lane = threadIdx.x & 63;
+  for (int j = 0; j * 256 < nfloats; ++j) {
+    int i = j * 256 + lane * 4;
+    i = i < nfloats ? i : nfloats - 4;
+    __builtin_amdgcn_global_load_lds((gvp)(src + i), (lvp)(dst + j * 256), 16, 0, kActCpol);
+  }
+}
+
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
@@ -70,8 +121,6 @@ __device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 
 // Cross-lane sums with DPP (VALU lane permutes, no LDS round trip).
 template <int CTRL>
@@ -113,19 +162,21 @@ template <class T>
 __device__ __forceinline__ const T* wp(const EngineArgs& A, int idx) {
   return reinterpret_cast<const T*>(uni64(A.wptr[idx]));
 }
-__device__ __forceinline__ float* actp(const EngineArgs& A, int off) { return A.act + off; }
 
 // ------------------------------------------------------------------ per-workgroup state
 
 struct Blk {
+  rsrc_t act;     // coherent view of the activation region (byte offsets = 4 * float offsets)
   uint32_t epoch;
-  uint32_t t_ready;
+  uint32_t t_ready, t_staged, t_streamed;
   int* flags;     // LDS: [0] wait status, [1] ticket result
   float* xs;      // LDS: staged input vector
   float* ys;      // LDS: per-row results of the current task
   float* scr;     // LDS: reduction scratch
   uint64_t* rowp; // LDS: row pointers of the current GEMV task
   int* xoffp;     // LDS: per-row input offsets of the current GEMV task
+  float* gs;      // LDS: norm gains (bf16) of the current task
+  float* actp;    // the activation region (generic pointer, for LDS DMA)
 };
 
 // Wait until every dependency counter of `t` has reached this step's target. Wave 0 polls
@@ -148,9 +199,9 @@ __device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const Tas
       while (true) {
         const bool ok = (lane >= t.dep_count) || ((int32_t)(ld_agent(cp) - target) >= 0);
         if (__all(ok)) break;
-        if ((++spins & 15u) == 0u) {
+        const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
+        if (late || (++spins & 7u) == 0u) {
           const uint32_t ab = ld_agent(A.ctl + CTL_ABORT);
-          const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
           if (ab || late) {
             if (!ab && lane == 0) {
               uint32_t zero = 0;
@@ -168,7 +219,9 @@ __device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const Tas
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (status == 0) acquire();
+      // no cache invalidate: produced data is read with SC1 loads; the workgroup-scope fence
+      // only keeps the compiler from hoisting those loads above the poll
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
     if (lane == 0) b.flags[0] = status;
   }
@@ -177,14 +230,12 @@ __device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const Tas
   return b.flags[0] == 0;
 }
 
-// All stores of the task are issued before the barrier; thread 0's agent-scope release
-// makes them visible before the counter increment.
+// Every wave waits for its own SC1 stores to complete, then the barrier, then one counter
+// increment: the produced data is visible at agent scope before the counter moves.
 __device__ __forceinline__ void signal(const EngineArgs& A, int ctr) {
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  if (threadIdx.x == 0 && ctr >= 0) {
-    release();
-    add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
-  }
+  if (threadIdx.x == 0 && ctr >= 0) add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
 }
 
 __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
@@ -201,28 +252,51 @@ __device__ __forceinline__ float block_sum(Blk& b, float v) {
   return s;
 }
 
-// Stage K values (fp32 `s32` or bf16 `s16`) into xs[0, K), zero xs[K, padK). With a gain,
-// apply RMSNorm: x / sqrt(mean(x^2) + eps) * g (eps inside the sqrt, mean over K).
-__device__ __forceinline__ void stage_vec(Blk& b, const float* s32, const uint16_t* s16, int K, int padK,
+// Stage K values into xs[0, K) and zero xs[K, padK). The source is the activation buffer at
+// float offset `off`, or the bf16 step input `s16` when off < 0. With a gain, apply
+// RMSNorm: x / sqrt(mean(x^2) + eps) * g (eps inside the sqrt, mean over K).
+// All global loads are issued by wave 0, the wave that has no weight loads in flight (a
+// wave's loads complete in issue order, so waves 1..7 would wait for their prefetch first).
+__device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, int K, int padK,
                                           const uint16_t* gain, float eps) {
-  float ss = 0.f;
-  for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
-    f4 v;
-    if (s32) {
-      v = *(const f4*)(s32 + i);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (gain) dma_to_lds(b.gs, (const float*)gain, K / 2);
+    if (off >= 0) {
+      dma_to_lds(b.xs, b.actp + off, K);
     } else {
-      const uint2 u = *(const uint2*)(s16 + i);
-      v = f4{bf_lo(u.x), bf_hi(u.x), bf_lo(u.y), bf_hi(u.y)};
+      // the bf16 step input (layer 0): batched loads, converted to fp32
+      for (int i0 = lane * 4; i0 < K; i0 += 64 * 4 * 4) {
+        f4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + u * 256;
+          const uint2 x = *(const uint2*)(s16 + (i < K ? i : 0));
+          v[u] = f4{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (i0 + u * 256 < K) *(f4*)(b.xs + i0 + u * 256) = v[u];
+      }
     }
-    *(f4*)(b.xs + i) = v;
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    for (int i = K + lane; i < padK; i += 64) b.xs[i] = 0.f;
+    if (gain) {
+      float ss = 0.f;
+      for (int i = lane * 4; i < K; i += 256) {
+        const f4 v = *(const f4*)(b.xs + i);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+      ss = wave_sum(ss);
+      if (lane == 0) b.flags[2] = __float_as_int(1.0f / sqrtf(ss / (float)K + eps));
+    }
   }
-  for (int i = K + threadIdx.x; i < padK; i += kThreads) b.xs[i] = 0.f;
+  __syncthreads();
   if (gain) {
-    const float tot = block_sum(b, ss);
-    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+    const float inv = __int_as_float(b.flags[2]);
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(b.gs);
     for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
-      const uint2 g = *(const uint2*)(gain + i);
+      const uint2 g = *(const uint2*)(g16 + i);
       f4 v = *(f4*)(b.xs + i);
       v.x *= inv * bf_lo(g.x);
       v.y *= inv * bf_hi(g.x);
@@ -230,13 +304,16 @@ __device__ __forceinline__ void stage_vec(Blk& b, const float* s32, const uint16
       v.w *= inv * bf_hi(g.y);
       *(f4*)(b.xs + i) = v;
     }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------------ streaming row GEMV
 
-constexpr int NB = 16;  // 16-byte chunks per batch per lane (16 KB per wave per batch)
+#ifndef DEC_NB
+#define DEC_NB 16
+#endif
+constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (16 KB per wave per batch)
 
 // Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
 // columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
@@ -344,6 +421,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   if (!wait_deps(A, b, t)) return false;
   stage();
+  b.t_staged = (uint32_t)now();
   if (!prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
     s.init(b.rowp, b.xoffp, ja, jb, K, lane);
@@ -366,6 +444,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     s.load(b1);
   }
   __syncthreads();
+  b.t_streamed = (uint32_t)now();
   epi();
   return true;
 }
@@ -410,20 +489,19 @@ struct RmQKV {
 
 // ------------------------------------------------------------------ GQA tasks
 
-__device__ __forceinline__ const float* layer_in32(const EngineArgs& A, const LayerDesc& L) {
-  return L.act[LA_X_IN] >= 0 ? actp(A, L.act[LA_X_IN]) : nullptr;
-}
 
 __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
   const RmQKV rm{wp<uint16_t>(A, L.w[LW_WQ]), wp<uint16_t>(A, L.w[LW_WK]), wp<uint16_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
-  const float* x32 = layer_in32(A, L);
+  const int xin = L.act[LA_X_IN];
   return run_gemv(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, x32, x32 ? nullptr : A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] { stage_vec(b, xin, A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
         const int n = A.kv_len;
+        const size_t lay = (size_t)2 * A.nkv * (n + 1) * hd;  // cache elements per layer
+        const rsrc_t kvr = make_rsrc(A.kv + (size_t)t.layer * lay, (uint32_t)(lay * 2));
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
           const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
           float a = b.ys[2 * i], c = b.ys[2 * i + 1];
@@ -434,61 +512,71 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
             a = a2;
           }
           if (slot < r) {
-            float* q = actp(A, L.act[LA_Q]) + (size_t)(g * r + slot) * hd;
-            q[k] = a;
-            q[k + hh] = c;
+            const uint32_t q = (uint32_t)(L.act[LA_Q] + (g * r + slot) * hd);
+            cst(b.act, (q + k) * 4u, a);
+            cst(b.act, (q + k + hh) * 4u, c);
           } else {
             const int sel = slot - r;  // 0: k, 1: v
-            float* kn = actp(A, L.act[LA_KVNEW]) + (size_t)(sel * A.nkv + g) * hd;
-            kn[k] = a;
-            kn[k + hh] = c;
-            uint16_t* cache = A.kv + ((((size_t)t.layer * 2 + sel) * A.nkv + g) * (size_t)(n + 1) + n) * hd;
-            cache[k] = f2bf(a);
-            cache[k + hh] = f2bf(c);
+            const uint32_t kn = (uint32_t)(L.act[LA_KVNEW] + (sel * A.nkv + g) * hd);
+            cst(b.act, (kn + k) * 4u, a);
+            cst(b.act, (kn + k + hh) * 4u, c);
+            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * (n + 1) + n) * hd);
+            cst16(kvr, (row + k) * 2u, f2bf(a));
+            cst16(kvr, (row + k + hh) * 2u, f2bf(c));
           }
         }
       });
 }
 
-// Merge S split partials (m, l, acc[hd]) of H heads into o[h][d] = sum_s e^(m_s-M) acc_s /
-// sum_s e^(m_s-M) l_s (base-2 exponents). All loads of a phase are independent 16-byte
-// loads issued together, so the merge costs a few memory round trips, not S of them.
-__device__ __forceinline__ void merge_splits(const EngineArgs& A, Blk& b, const float* parts, int S, int H, int hd,
-                                             float* o) {
-  const int ps = hd + 4;          // m, l, 2 pad, acc[hd]: acc stays 16-byte aligned
-  float* wts = b.scr;             // [S][H] weights e^(m_s - M_h)
-  float* den = b.scr + S * H;     // [H] sum of weighted l
-  float* acc = den + H;           // [4][H*hd] partial numerators per split quarter
-  for (int i = threadIdx.x; i < S * H; i += kThreads) wts[i] = parts[(size_t)(i / H) * H * ps + (i % H) * ps];
-  __syncthreads();
-  for (int h = threadIdx.x; h < H; h += kThreads) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wts[sp * H + h]);
-    float dsum = 0.f;
-    for (int sp = 0; sp < S; ++sp) {
-      const float e = exp2f(wts[sp * H + h] - M);
-      wts[sp * H + h] = e;
-      dsum += e * parts[(size_t)sp * H * ps + h * ps + 1];
-    }
-    den[h] = dsum;
+// Merge S split partials (m, l, acc[hd]) of H heads into xs[h*hd + d] =
+// sum_s e^(m_s-M) acc_s[d] / sum_s e^(m_s-M) l_s (base-2 exponents), zero-padding xs up to
+// padK. Wave 0 copies the S*H partials into LDS with one burst of DMA; the merge then runs
+// from LDS. With o_off >= 0 wave 0 also stores the merged vector there.
+__device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H, int hd, int padK, int o_off) {
+  const int ps = hd + 4;                    // m, l, 2 pad, acc[hd]
+  const int n = S * H * ps;
+  float* P = b.scr;                         // [S][H][ps]
+  float* w = P + ((n + 255) & ~255);        // [S][H] merge weights
+  if (threadIdx.x < 64) {
+    dma_to_lds(P, b.actp + parts_off, n);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    for (int i = H * hd + (int)threadIdx.x; i < padK; i += 64) b.xs[i] = 0.f;
   }
   __syncthreads();
-  // thread -> (quarter of the splits, head, 4 consecutive dims)
-  const int nd4 = H * hd / 4;
-  for (int i = threadIdx.x; i < 4 * nd4; i += kThreads) {
-    const int q = i / nd4, j = i - q * nd4, h = (j * 4) / hd, d = j * 4 - h * hd;
-    f4 sum = f4{0.f, 0.f, 0.f, 0.f};
-    for (int sp = q; sp < S; sp += 4) {
-      const f4 v = *(const f4*)(parts + (size_t)sp * H * ps + h * ps + 4 + d);
-      sum += v * wts[sp * H + h];
-    }
-    *(f4*)(acc + q * H * hd + j * 4) = sum;
+  // wave h (h < 8) owns heads h, h + 8, ...: lanes run over the splits
+  for (int h = wave_id(); h < H; h += kWaves) {
+    const int lane = threadIdx.x & 63;
+    float M = -INFINITY;
+    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, P[(sp * H + h) * ps]);
+    M = fmaxf(M, __shfl_xor(M, 1, 64));
+    M = fmaxf(M, __shfl_xor(M, 2, 64));
+    M = fmaxf(M, __shfl_xor(M, 4, 64));
+    M = fmaxf(M, __shfl_xor(M, 8, 64));
+    M = fmaxf(M, __shfl_xor(M, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    float den = 0.f;
+    for (int sp = lane; sp < S; sp += 64) den += exp2f(P[(sp * H + h) * ps] - M) * P[(sp * H + h) * ps + 1];
+    den = wave_sum(den);
+    const float inv = 1.0f / den;
+    for (int sp = lane; sp < S; sp += 64) w[sp * H + h] = exp2f(P[(sp * H + h) * ps] - M) * inv;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < H * hd; i += kThreads) {
-    const int h = i / hd;
-    o[i] = (acc[i] + acc[H * hd + i] + acc[2 * H * hd + i] + acc[3 * H * hd + i]) / den[h];
+    const int h = i / hd, d = i - h * hd;
+    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    int sp = 0;
+    for (; sp + 4 <= S; sp += 4) {
+      v0 = fmaf(w[sp * H + h], P[(sp * H + h) * ps + 4 + d], v0);
+      v1 = fmaf(w[(sp + 1) * H + h], P[((sp + 1) * H + h) * ps + 4 + d], v1);
+      v2 = fmaf(w[(sp + 2) * H + h], P[((sp + 2) * H + h) * ps + 4 + d], v2);
+      v3 = fmaf(w[(sp + 3) * H + h], P[((sp + 3) * H + h) * ps + 4 + d], v3);
+    }
+    for (; sp < S; ++sp) v0 = fmaf(w[sp * H + h], P[(sp * H + h) * ps + 4 + d], v0);
+    b.xs[i] = (v0 + v1) + (v2 + v3);
   }
+  __syncthreads();
+  if (o_off >= 0 && threadIdx.x < 64)
+    for (int i = threadIdx.x * 4; i < H * hd; i += 256) cst4(b.act, (uint32_t)(o_off + i) * 4u, *(const f4*)(b.xs + i));
 }
 
 // Split-K attention of one KV group over positions [u0, u1): the group's R query heads share
@@ -500,7 +588,7 @@ __device__ __forceinline__ void merge_splits(const EngineArgs& A, Blk& b, const 
 // kv_len, written by this step's QKV tasks) is loaded again after it.
 template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
-  constexpr int GPW = 64 / LPP, NP = 2, PER_BLK = NP * GPW;
+  constexpr int GPW = 64 / LPP, NP = 3, PER_BLK = NP * GPW;
   const LayerDesc& L = A.layers[t.layer];
   const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = A.kv_len, n1 = n + 1;
   const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
@@ -520,22 +608,39 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
       vv[i] = ldg_nt(Vb + (size_t)pos * hd);
     }
   };
+  // blocks that hold the new slot are read coherently (it was written by other workgroups)
+  const rsrc_t kr = make_rsrc(Kb - sub * 8, (uint32_t)(n1 * hd * 2)), vr = make_rsrc(Vb - sub * 8, (uint32_t)(n1 * hd * 2));
+  auto load_coh = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      int pos = q0 + (blk * NP + i) * GPW + grp;
+      pos = pos < q1 ? pos : q1 - 1;
+      const uint32_t off = (uint32_t)(pos * hd + sub * 8) * 2u;
+      kk[i] = cld4u(kr, off);
+      vv[i] = cld4u(vr, off);
+    }
+  };
   // cached rows only (positions < n) before the wait
   const int pre_lim = (q1 < n) ? q1 : n;
   load(0, ka, va, pre_lim);
   load(1, kb, vb, pre_lim);
   if (!wait_deps(A, b, t)) return false;
-  if (nblk > 0 && q0 + PER_BLK > pre_lim) load(0, ka, va, q1);
-  if (nblk > 1 && q0 + 2 * PER_BLK > pre_lim) load(1, kb, vb, q1);
+  if (nblk > 0 && q0 + PER_BLK > pre_lim) load_coh(0, ka, va);
+  if (nblk > 1 && q0 + 2 * PER_BLK > pre_lim) load_coh(1, kb, vb);
 
+  // the group's queries, fetched by wave 0 (no loads in flight) into LDS
+  if (threadIdx.x < 64) {
+    dma_to_lds(b.ys, b.actp + L.act[LA_Q] + g * r * hd, r * hd);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  __syncthreads();
   float qv[R][8];
-  const float* qbase = actp(A, L.act[LA_Q]) + (size_t)g * r * hd + sub * 8;
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     f4 a = f4{0.f, 0.f, 0.f, 0.f}, c = a;
     if (h < r) {
-      a = *(const f4*)(qbase + h * hd);
-      c = *(const f4*)(qbase + h * hd + 4);
+      a = *(const f4*)(b.ys + h * hd + sub * 8);
+      c = *(const f4*)(b.ys + h * hd + sub * 8 + 4);
     }
     const float sc = A.attn_scale_log2;
     qv[h][0] = a.x * sc; qv[h][1] = a.y * sc; qv[h][2] = a.z * sc; qv[h][3] = a.w * sc;
@@ -604,94 +709,82 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
   };
   for (int blk = 0; blk < nblk; blk += 2) {
     step(blk, ka, va);
-    if (blk + 2 < nblk) load(blk + 2, ka, va, q1);
+    if (blk + 2 < nblk) {
+      if (q0 + (blk + 3) * PER_BLK > n) load_coh(blk + 2, ka, va); else load(blk + 2, ka, va, q1);
+    }
     if (blk + 1 >= nblk) break;
     step(blk + 1, kb, vb);
-    if (blk + 3 < nblk) load(blk + 3, kb, vb, q1);
+    if (blk + 3 < nblk) {
+      if (q0 + (blk + 4) * PER_BLK > n) load_coh(blk + 3, kb, vb); else load(blk + 3, kb, vb, q1);
+    }
   }
   const uint32_t t_mid = (uint32_t)now();
-  // merge the lane groups of this wave (lanes with equal `sub` hold the same dims)
+  // every lane group writes its partial to LDS: slot = wave * GPW + grp, [slot][h][ps] with
+  // ps = hd + 4 (m, l, 2 pad, acc[hd])
+  constexpr int NS = kWaves * GPW;
+  const int ps = hd + 4;
+  float* gp = b.scr + (size_t)(wave * GPW + grp) * r * ps;
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     if (h >= r) continue;
-#pragma unroll
-    for (int mask = LPP; mask < 64; mask <<= 1) {
-      const float mo = __shfl_xor(m[h], mask, 64), lo = __shfl_xor(l[h], mask, 64);
-      const float mn = fmaxf(m[h], mo);
-      const float ea = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - mn);
-      const float eb = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
-      l[h] = l[h] * ea + lo * eb;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const float ao = __shfl_xor(acc[h][d], mask, 64);
-        acc[h][d] = acc[h][d] * ea + ao * eb;
-      }
-      m[h] = mn;
+    if (sub == 0) {
+      gp[h * ps] = m[h];
+      gp[h * ps + 1] = l[h];
     }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) gp[h * ps + 4 + sub * 8 + d] = acc[h][d];
   }
-  // per-wave partials to LDS: scr[wave][h][4 + hd] (m, l, 2 pad, acc)
-  const int ps = hd + 4;
-  float* wpart = b.scr + (size_t)wave * r * ps;
-  if (grp == 0) {
+  __syncthreads();
+  const uint32_t t_lanes = (uint32_t)now();
+  // wave h: merge weights of head h over the NS slots (one slot per lane)
+  float* wts = b.scr + (size_t)NS * r * ps;  // [NS][r], then M[r], den[r]
+  if (wave < r) {
+    const int h = wave;
+    float M = -INFINITY;
+    for (int sl = lane; sl < NS; sl += 64) M = fmaxf(M, b.scr[((size_t)sl * r + h) * ps]);
 #pragma unroll
-    for (int h = 0; h < R; ++h) {
-      if (h >= r) continue;
-      if (sub == 0) {
-        wpart[h * ps] = m[h];
-        wpart[h * ps + 1] = l[h];
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) wpart[h * ps + 4 + sub * 8 + d] = acc[h][d];
+    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+    float dl = 0.f;
+    for (int sl = lane; sl < NS; sl += 64) {
+      const float ms = b.scr[((size_t)sl * r + h) * ps];
+      const float e = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      wts[sl * r + h] = e;
+      dl += e * b.scr[((size_t)sl * r + h) * ps + 1];
+    }
+    const float den = wave_sum(dl);
+    if (lane == 0) {
+      wts[NS * r + h] = M;
+      wts[NS * r + r + h] = den;
     }
   }
   __syncthreads();
-  // workgroup partial -> global partial slot of this split
-  float* gpart = actp(A, t.a4) + (size_t)t.a1 * r * ps;
+  // workgroup partial (M, den, sum of weighted acc) -> LDS (xs), then wave 0 stores it
   for (int i = threadIdx.x; i < r * hd; i += kThreads) {
     const int h = i / hd, d = i - h * hd;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, b.scr[(size_t)w * r * ps + h * ps]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* pw = b.scr + (size_t)w * r * ps + h * ps;
-      const float e = (pw[0] == -INFINITY) ? 0.f : exp2f(pw[0] - M);
-      num += e * pw[4 + d];
-      den += e * pw[1];
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll 4
+    for (int sl = 0; sl < NS; sl += 2) {
+      v0 = fmaf(wts[sl * r + h], b.scr[((size_t)sl * r + h) * ps + 4 + d], v0);
+      v1 = fmaf(wts[(sl + 1) * r + h], b.scr[((size_t)(sl + 1) * r + h) * ps + 4 + d], v1);
     }
-    gpart[h * ps + 4 + d] = num;
+    b.xs[h * ps + 4 + d] = v0 + v1;
     if (d == 0) {
-      gpart[h * ps] = M;
-      gpart[h * ps + 1] = den;
+      b.xs[h * ps] = wts[NS * r + h];
+      b.xs[h * ps + 1] = wts[NS * r + r + h];
+      b.xs[h * ps + 2] = 0.f;
+      b.xs[h * ps + 3] = 0.f;
     }
   }
-  // ticket: the last split of the group merges all splits
+  const uint32_t gpart = (uint32_t)(t.a4 + t.a1 * r * ps);
   __syncthreads();
+  const uint32_t t_merged = (uint32_t)now();
+  if (threadIdx.x < 64)
+    for (int i = threadIdx.x * 4; i < r * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
   if (threadIdx.x == 0) {
-    release();
-    const uint32_t old = add_agent(A.counters + (size_t)t.signal * kCounterStride, 1u);
-    b.flags[1] = (old + 1u == (b.epoch + 1u) * (uint32_t)t.a2) ? 1 : 0;
-    if (b.flags[1]) acquire();
+    A.log[t.id].reserved[0] = t_lanes;
+    A.log[t.id].reserved[1] = t_merged;
   }
-  __syncthreads();
-  if (!b.flags[1]) {
-    if (threadIdx.x == 0) A.log[t.id].reserved = t_mid;
-    return true;
-  }
-  const uint32_t tm0 = (uint32_t)now();
-  merge_splits(A, b, actp(A, t.a4), t.a2, r, hd, actp(A, L.act[LA_ATTN]) + (size_t)g * r * hd);
-  signal(A, t.signal2);
-  if (threadIdx.x == 0) {
-    TaskLog* lg = A.log + t.a3;
-    add_agent(&lg->execs, 1u);
-    lg->epoch = b.epoch;
-    lg->wg = blockIdx.x;
-    lg->xcd = xcc_id();
-    lg->t_start = tm0;
-    lg->t_ready = tm0;
-    lg->t_end = (uint32_t)now();
-  }
+  if (threadIdx.x == 0) A.log[t.id].t_mid = t_mid;
   return true;
 }
 
@@ -709,19 +802,49 @@ __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const Ta
   const LayerDesc& L = A.layers[t.layer];
   const int K = (A.arch == 0) ? A.nq * A.hd : A.nq * A.dv;
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_WO]), K, t.u0};
-  const float* x32 = layer_in32(A, L);
+  const int xin = L.act[LA_X_IN];
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, actp(A, L.act[LA_ATTN]), nullptr, K, pad512(K), nullptr, 0.f); },
+      [&] { stage_vec(b, L.act[LA_ATTN], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
-        float* h = actp(A, L.act[LA_H]);
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
           const int rr = t.u0 + i;
-          const float res = x32 ? x32[rr] : bf16f(A.x[rr]);
-          h[rr] = res + b.ys[i];
+          const float res = xin >= 0 ? cld(b.act, (uint32_t)(xin + rr) * 4u) : bf16f(A.x[rr]);
+          cst(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u, res + b.ys[i]);
         }
       });
 }
+
+struct RmCols {  // rows r0 + j of a [*, ld] matrix, columns starting at c0
+  const uint16_t* W;
+  int ld, r0, c0;
+  __device__ __forceinline__ const uint16_t* row(int j) const { return W + (size_t)(r0 + j) * ld + c0; }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// Rows [u0, u1) of W_o times the merged attention output of KV group g (its r*hd columns):
+// one term of h = x + sum_g W_o[:, g] o_g. The group's split partials are merged while
+// staging; the first task of the group also stores the merged o_g (the attention output).
+__device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int r = A.nq / A.nkv, hd = A.hd, g = t.a0, K = r * hd;
+  const RmCols rm{wp<uint16_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_merge(b, t.a4, t.a2, r, hd, pad512(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
+      [&] {
+        float* h = b.actp + L.act[LA_H] + t.u0;
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+          __hip_atomic_fetch_add(h + i, b.ys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      });
+}
+
+// Layer 0: h = x (widened), the accumulator the per-group O-projections add into.
+__device__ __forceinline__ bool task_hinit(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) cst(b.act, (uint32_t)(t.a0 + t.u0 + i) * 4u, bf16f(A.x[t.u0 + i]));
+  return true;
+}
+
 
 __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
@@ -729,10 +852,10 @@ __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const T
   const RmGateUp rm{wp<uint16_t>(A, L.w[LW_GATE]), wp<uint16_t>(A, L.w[LW_UP]), K, t.u0};
   return run_gemv(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, actp(A, L.act[LA_H]), nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
-        float* a = actp(A, L.act[LA_ACT]);
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) a[t.u0 + i] = silu(b.ys[2 * i]) * b.ys[2 * i + 1];
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+          cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
 }
 
@@ -742,17 +865,16 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, actp(A, L.act[LA_ACT]), nullptr, K, pad512(K), nullptr, 0.f); },
+      [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
-        float* fo = actp(A, L.act[LA_FFN_OUT]);
-        float* xo = actp(A, L.act[LA_X_OUT]);
-        const float* h = actp(A, L.act[LA_H]);
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
           const int rr = t.u0 + i;
           const float y = b.ys[i];
-          fo[rr] = y;
-          xo[rr] = h[rr] + y;
-          if (t.a0) A.out[rr] = h[rr] + y;
+          const float xo = cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) + y;
+          cst(b.act, (uint32_t)(L.act[LA_FFN_OUT] + rr) * 4u, y);
+          if (t.a1 >= 0) cst(b.act, (uint32_t)(t.a1 + rr) * 4u, xo);  // next layer's h starts at x
+          cst(b.act, (uint32_t)(L.act[LA_X_OUT] + rr) * 4u, xo);
+          if (t.a0) A.out[rr] = xo;
         }
       });
 }
@@ -762,7 +884,7 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
   const RmPlain rm{wp<uint16_t>(A, A.w_lm_head), K, t.u0};
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, actp(A, A.x_final), nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
+      [&] { stage_vec(b, A.x_final, nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) A.out[t.u0 + i] = b.ys[i];
       });
@@ -781,9 +903,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
   b.ys = b.xs + A.xs_floats;
   b.rowp = reinterpret_cast<uint64_t*>(b.ys + kYsFloats);
   b.xoffp = reinterpret_cast<int*>(b.rowp + kMaxTaskRows);
-  b.scr = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
+  b.gs = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
+  b.scr = b.gs + A.gs_floats;
+  b.actp = A.act;
+  b.act = make_rsrc(A.act, A.act_bytes);
   b.epoch = ld_agent(A.ctl + CTL_EPOCH);
-  b.t_ready = 0;
+  b.t_ready = b.t_staged = b.t_streamed = 0;
   const uint32_t xcc = xcc_id();
   const int wg = blockIdx.x;
   const int rq = A.nkv > 0 ? A.nq / A.nkv : 1;
@@ -796,8 +921,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
       case T_QKV: ok = task_qkv(A, b, t); break;
       case T_ATTN:
         ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
-        sig = -1;  // signalled through the ticket
         break;
+      case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
+      case T_HINIT: ok = task_hinit(A, b, t); break;
       case T_OPROJ: ok = task_oproj(A, b, t); break;
       case T_GATEUP: ok = task_gateup(A, b, t); break;
       case T_DOWN: ok = task_down(A, b, t); break;
@@ -815,12 +941,14 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
       lg->t_start = t0;
       lg->t_ready = b.t_ready;
       lg->t_end = (uint32_t)now();
+      lg->t_staged = b.t_staged;
+      lg->t_streamed = b.t_streamed;
     }
   }
   // the last workgroup to finish advances the epoch for the next step
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    release();
     const uint32_t d = add_agent(A.ctl + CTL_DONE, 1u);
     if (d == (uint32_t)A.n_wg - 1u) {
       st_agent(A.ctl + CTL_DONE, 0u);

@@ -38,6 +38,9 @@ enum TaskType : int32_t {
   T_TOPK = 15,       // sigmoid, top-k selection, normalised weights
   T_EXPERT_GU = 16,  // routed-expert gate/up rows + SwiGLU (expert chosen at run time)
   T_MOE_DOWN = 17,   // shared + routed down rows, weighted sum + residual
+  T_OPROJ_G = 18,    // GQA: merge one KV group's attention splits + W_o rows x that group's columns,
+                     // added into h with agent-scope atomics
+  T_HINIT = 19,      // GQA layer 0: h = x (the accumulator the per-group O-projections add into)
   T_NUM_TYPES
 };
 
@@ -91,16 +94,20 @@ struct LayerDesc {
   int32_t act[LA_COUNT];
 };
 
-// Per-task execution log written by the engine (one slot per task id, 32 bytes).
+// Per-task execution log written by the engine (one slot per task id, 64 bytes). Times are
+// s_memrealtime (100 MHz) low words.
 struct TaskLog {
   uint32_t execs;      // incremented once per execution (atomic)
   uint32_t epoch;      // epoch of the last execution
   uint32_t wg;         // workgroup that ran it
   uint32_t xcd;        // hardware XCC id read by that workgroup
-  uint32_t t_start;    // s_memrealtime (100 MHz) low bits at task start
-  uint32_t t_ready;    // ... when its dependencies were satisfied
-  uint32_t t_end;      // ... at completion
-  uint32_t reserved;
+  uint32_t t_start;    // task start (static loads issued just after)
+  uint32_t t_ready;    // dependencies satisfied
+  uint32_t t_end;      // completion (after the counter increment)
+  uint32_t t_mid;      // attention: end of the position loop
+  uint32_t t_staged;   // input vector staged in LDS
+  uint32_t t_streamed; // all rows streamed
+  uint32_t reserved[6];
 };
 
 // Control words at the start of the workspace (each on its own 128-byte line).
@@ -135,6 +142,8 @@ struct EngineArgs {
   int32_t n_routed, n_shared, top_k, eff;
   int32_t kv_len, n_wg, rope_half, w_final_norm, w_lm_head, x_final;
   int32_t xs_floats;           // LDS floats reserved for the staged input vector
+  uint32_t act_bytes;          // size of the activation region
+  int32_t gs_floats;           // LDS floats reserved for norm gains
   float eps, attn_scale_log2;  // softmax scale * log2(e)
 };
 

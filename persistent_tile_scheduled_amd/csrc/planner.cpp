@@ -27,6 +27,7 @@ namespace {
 constexpr int kMinPosPerSplit = 16;
 constexpr int kRowsCap = kMaxTaskRows;     // rows of one GEMV task (LDS row tables)
 constexpr int kAbsorbBlock = 64;           // latent columns per absorb task
+constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -234,6 +235,9 @@ struct Builder {
   }
 
   // ---------------------------------------------------------------- GQA layer stages
+  std::vector<int32_t> hinit_deps;  // layer 0: counters of the h = x init tasks
+  std::vector<int64_t> h_acc;       // GQA: per-layer h accumulators
+
   std::vector<int32_t> build_gqa_layer(int l, std::vector<int32_t> prev, int64_t x_in) {
     LayerDesc& L = P.layers[l];
     const int d = s.hidden, nq = s.n_q_heads, nkv = s.n_kv_heads, hd = s.head_dim, f = s.ffn;
@@ -244,7 +248,7 @@ struct Builder {
     L.act[LA_Q] = (int)act(p + "q", (int64_t)nq * hd);
     L.act[LA_KVNEW] = (int)act(p + "kv_new", 2LL * nkv * hd);
     L.act[LA_ATTN] = (int)act(p + "attn", (int64_t)nq * hd);
-    L.act[LA_H] = (int)act(p + "h", d);
+    L.act[LA_H] = (int)h_acc[l];
     L.act[LA_ACT] = (int)act(p + "ffn_act", f);
     L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
     L.act[LA_X_OUT] = (int)act(p + "x_out", d);
@@ -258,36 +262,43 @@ struct Builder {
     for (int g = 0; g < nkv; ++g)
       spread(sets[g], U, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_QKV, l, a, b, prev, qkv + g, -1, g); });
 
-    // attention splits (one per workgroup of the group's set) + ticket merge
+    // attention splits (one per workgroup of the group's set)
     ++stage;
-    const int tick = counter(nkv), merged = counter(nkv);
+    const int att = counter(nkv);
     int smax = 1;
     std::vector<int> S(nkv);
     for (int g = 0; g < nkv; ++g) {
-      S[g] = (int)std::min<int64_t>((int64_t)sets[g].size(), std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit));
+      // the O-projection merges a group's partials from one LDS burst: cap the split count
+      const int64_t cap = std::max<int64_t>(1, kMergeFloats / ((int64_t)r * (hd + 4)));
+      S[g] = (int)std::min<int64_t>({(int64_t)sets[g].size(), cap,
+                                     std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit)});
       smax = std::max(smax, S[g]);
     }
     const int64_t pstride = (int64_t)r * (hd + 4);  // per split: r x (m, l, pad, pad, acc[hd])
     const int64_t part = act(p + "attn_partials", (int64_t)nkv * smax * pstride);
     L.act[LA_PART] = (int)part;
-    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * pstride + 64);
-    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)smax * r + r + 4LL * r * hd + 64);
-    for (int g = 0; g < nkv; ++g) {
-      const int merge_id = next_id++;
+    const int64_t gpw = 512 / hd;  // lane groups per wave in the attention task
+    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * gpw * (pstride + r) + 2 * r + 64);
+    scratch_floats = std::max<int64_t>(scratch_floats, align_up((int64_t)smax * pstride, 256) + (int64_t)smax * r + 64);
+    for (int g = 0; g < nkv; ++g)
       for (int sp = 0; sp < S[g]; ++sp) {
         int p0 = (int)((n + 1) * sp / S[g]), p1 = (int)((n + 1) * (sp + 1) / S[g]);
-        add(sets[g][sp], T_ATTN, l, p0, p1, {qkv + g}, tick + g, merged + g, g, sp, S[g], merge_id,
+        add(sets[g][sp], T_ATTN, l, p0, p1, {qkv + g}, att + g, -1, g, sp, S[g], 0,
             (int)(part + (int64_t)g * smax * pstride));
       }
-      P.counter_total[merged + g] = 1;  // only the last split signals it
-    }
 
-    // O projection + residual
+    // per group: merge the group's splits, then W_o rows x the group's r*hd columns (split-K
+    // over groups), added into h, which holds the residual x already (written by the previous
+    // layer's down tasks, or by the layer-0 init tasks)
     ++stage;
     const int ctr_o = counter(n_xcd);
-    std::vector<int32_t> dm;
-    for (int g = 0; g < nkv; ++g) dm.push_back(merged + g);
-    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) { add(w, T_OPROJ, l, a, b, dm, ctr_o + xcd(w)); });
+    for (int g = 0; g < nkv; ++g) {
+      std::vector<int32_t> dg = {att + g};
+      dg.insert(dg.end(), hinit_deps.begin(), hinit_deps.end());
+      spread(sets[g], d, kRowsCap, [&](int w, int a, int b) {
+        add(w, T_OPROJ_G, l, a, b, dg, ctr_o + xcd(w), -1, g, 0, S[g], 0, (int)(part + (int64_t)g * smax * pstride));
+      });
+    }
     return ffn_dense(l, all_of(ctr_o, n_xcd));
   }
 
@@ -299,8 +310,9 @@ struct Builder {
     ++stage;
     const int ctr_dn = counter(n_xcd);
     const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
+    const int hnext = (s.arch == DEC_ARCH_GQA && l + 1 < s.n_layers) ? (int)h_acc[l + 1] : -1;
     spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) {
-      add(w, T_DOWN, l, a, b, all_of(ctr_gu, n_xcd), ctr_dn + xcd(w), -1, last);
+      add(w, T_DOWN, l, a, b, all_of(ctr_gu, n_xcd), ctr_dn + xcd(w), -1, last, hnext);
     });
     return all_of(ctr_dn, n_xcd);
   }
@@ -441,6 +453,15 @@ struct Builder {
 
     std::vector<int32_t> prev;
     int64_t x_in = -1;
+    if (s.arch == DEC_ARCH_GQA) {
+      // h accumulators: allocated up front so each layer's down tasks can initialise the next
+      for (int l = 0; l < s.n_layers; ++l) P.layers[l].act[LA_H] = -1;
+      for (int l = 0; l < s.n_layers; ++l) h_acc.push_back(act("layers." + std::to_string(l) + ".h", s.hidden));
+      ++stage;
+      const int ci = counter(n_xcd);
+      spread(all_wgs(), s.hidden, kRowsCap, [&](int w, int a, int b) { add(w, T_HINIT, 0, a, b, {}, ci + xcd(w), -1, (int)h_acc[0]); });
+      hinit_deps = all_of(ci, n_xcd);
+    }
     for (int l = 0; l < s.n_layers; ++l) {
       prev = (s.arch == DEC_ARCH_GQA) ? build_gqa_layer(l, prev, x_in) : build_mla_layer(l, prev, x_in);
       x_in = P.layers[l].act[LA_X_OUT];
@@ -483,11 +504,14 @@ struct Builder {
     // LDS: staged input vector + per-row results + reduction scratch
     const int64_t tables = (int64_t)kMaxTaskRows * 12 / 4;  // row pointers + input offsets
     const int64_t header = 64;  // LDS flag words ahead of the staged vector
-    int64_t lds = 4 * (header + xs_floats_max + kYsFloats + tables + scratch_floats);
+    const int64_t gmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.q_lora_rank, (int64_t)s.kv_lora_rank});
+    const int64_t gs = align_up(gmax / 2, 256);  // bf16 gains, DMA granularity 256 floats
+    P.gs_floats = gs;
+    int64_t lds = 4 * (header + xs_floats_max + kYsFloats + tables + gs + scratch_floats);
     if (s.arch != DEC_ARCH_GQA) {
       // latent attention: q (heads x (kl+dr)) + per-wave partials
       int64_t w = (int64_t)s.n_q_heads * (s.kv_lora_rank + s.qk_rope) + (int64_t)kWaves * s.n_q_heads * (s.kv_lora_rank + 2);
-      lds = std::max<int64_t>(lds, 4 * (header + w + kYsFloats + tables + 1024));
+      lds = std::max<int64_t>(lds, 4 * (header + w + kYsFloats + tables + gs + 1024));
     }
     lds = std::max<int64_t>(align_up(lds, 1024), kLdsMin);
     P.lds_bytes = (int32_t)lds;
@@ -512,7 +536,7 @@ struct Builder {
     P.act_floats = act_floats;
     for (size_t i = 0; i < acts.size(); ++i)
       P.buffers.push_back({acts[i].first, acts[i].second.second, P.off_act + acts[i].second.first * 4, act_counts[i]});
-    P.buffers.push_back({"task_log", DEC_DTYPE_I32, P.off_log, (int64_t)P.n_log * 8});
+    P.buffers.push_back({"task_log", DEC_DTYPE_I32, P.off_log, (int64_t)P.n_log * (int64_t)(sizeof(TaskLog) / 4)});
     P.buffers.push_back({"control", DEC_DTYPE_I32, P.off_ctl, CTL_WORDS});
 
     // bytes the method must read per step: every dense weight once (routed experts: only
@@ -587,7 +611,7 @@ std::string validate_plan(const PlanData& p) {
   std::map<Key, std::vector<std::pair<int, int>>> ranges;
   for (int i = 0; i < nt; ++i) {
     const TaskDesc& t = p.tasks[i];
-    int grp = (t.type == T_QKV || t.type == T_ATTN) ? t.a0 : 0;
+    int grp = (t.type == T_QKV || t.type == T_ATTN || t.type == T_OPROJ_G) ? t.a0 : 0;
     ranges[{t.layer, t.type, grp}].push_back({t.u0, t.u1});
   }
   const dec_model_shape& s = p.shape;
@@ -596,7 +620,7 @@ std::string validate_plan(const PlanData& p) {
     switch (type) {
       case T_QKV: return (int64_t)(s.n_q_heads / s.n_kv_heads + 2) * s.head_dim / 2;
       case T_ATTN: case T_MLA_ATTN: return n1;
-      case T_OPROJ: case T_DOWN: case T_MOE_DOWN: return s.hidden;
+      case T_OPROJ: case T_OPROJ_G: case T_DOWN: case T_MOE_DOWN: case T_HINIT: return s.hidden;
       case T_GATEUP: return s.ffn;
       case T_LMHEAD: return s.vocab;
       case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope;
@@ -624,7 +648,7 @@ std::string validate_plan(const PlanData& p) {
   }
   // every layer has its full set of stages
   std::vector<int> need;
-  if (s.arch == DEC_ARCH_GQA) need = {T_QKV, T_ATTN, T_OPROJ, T_GATEUP, T_DOWN};
+  if (s.arch == DEC_ARCH_GQA) need = {T_QKV, T_ATTN, T_OPROJ_G, T_GATEUP, T_DOWN};
   else {
     need = {T_MLA_A, T_MLA_B, T_MLA_KVAPP, T_MLA_ABSORB, T_MLA_ATTN, T_MLA_UV, T_OPROJ};
     if (s.arch == DEC_ARCH_MLA) { need.push_back(T_GATEUP); need.push_back(T_DOWN); }

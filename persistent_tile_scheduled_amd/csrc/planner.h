@@ -47,6 +47,7 @@ struct PlanData {
   std::vector<BufferSpec> buffers;
   int32_t n_log = 0;                  // task ids + ticket-merge ids
   int64_t xs_floats = 0;              // LDS floats for the largest staged input vector
+  int64_t gs_floats = 0;              // LDS floats for norm gains (bf16 pairs)
   int32_t rope_half = 0;
   int32_t w_final_norm = -1, w_lm_head = -1, x_final = -1;
   float attn_scale_log2 = 0.f;

@@ -69,5 +69,6 @@ class DecodeEngine:
         return raw.view(torch.int32 if b["dtype"] == "i32" else torch.float32)
 
     def task_log(self):
-        """[n_log, 8] int64: execs, epoch, wg, xcd, t_start, t_ready, t_end, reserved."""
-        return self.buffer("task_log").view(-1, 8).to(self.torch.int64) & 0xFFFFFFFF
+        """[n_log, 16] int64: execs, epoch, wg, xcd, t_start, t_ready, t_end, t_mid, t_staged,
+        t_streamed, reserved... (times: 100 MHz counter, low 32 bits)."""
+        return self.buffer("task_log").view(-1, 16).to(self.torch.int64) & 0xFFFFFFFF

@@ -113,10 +113,12 @@ def test_small_gqa_full_parity(name, seed):
     check_coverage(eng)
 
 
-def test_multi_step_changing_input():
+@pytest.mark.parametrize("name", ["small_gqa", "tiny"])
+def test_multi_step_changing_input(name):
     """Three steps with different inputs: each matches the oracle (epochs, counters and the
-    cross-XCD visibility of activations are exercised across steps)."""
-    cfg = workloads.get_config("small_gqa")
+    cross-XCD visibility of activations are exercised across steps; the tiny model's weights
+    fit in L2, so a line left over from an earlier step would be hit, not evicted)."""
+    cfg = workloads.get_config(name)
     w, x, kv = workloads.generate(cfg, seed=7, device="cuda")
     eng = _engine()(cfg, w)
     W = HostWeights(w)

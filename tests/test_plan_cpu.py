@@ -111,7 +111,8 @@ def _expected_units(cfg, ttype):
     n1 = cfg["kv_len"] + 1
     return {
         "QKV": (cfg["n_q_heads"] // max(cfg.get("n_kv_heads", 1), 1) + 2) * cfg.get("head_dim", 0) // 2,
-        "ATTN": n1, "OPROJ": cfg["hidden"], "DOWN": cfg["hidden"], "GATEUP": cfg.get("ffn", 0),
+        "ATTN": n1, "OPROJ": cfg["hidden"], "OPROJ_G": cfg["hidden"], "DOWN": cfg["hidden"],
+        "GATEUP": cfg.get("ffn", 0), "HINIT": cfg["hidden"],
         "LMHEAD": cfg["vocab"],
     }[ttype]
 
@@ -166,7 +167,7 @@ def test_schedule_drains_and_covers(name):
     cov = collections.defaultdict(list)
     for t in tasks:
         ty = B.TASK_TYPES[t["type"]]
-        grp = t["aux0"] if ty in ("QKV", "ATTN") else 0
+        grp = t["aux0"] if ty in ("QKV", "ATTN", "OPROJ_G") else 0
         cov[(t["layer"], ty, grp)].append((t["unit_begin"], t["unit_end"]))
     for (layer, ty, grp), rs in cov.items():
         rs.sort()
@@ -177,7 +178,7 @@ def test_schedule_drains_and_covers(name):
         assert at == _expected_units(cfg, ty), (layer, ty)
     n_layers = cfg["n_layers"]
     for layer in range(n_layers):
-        for ty in ("QKV", "ATTN", "OPROJ", "GATEUP", "DOWN"):
+        for ty in ("QKV", "ATTN", "OPROJ_G", "GATEUP", "DOWN"):
             assert (layer, ty, 0) in cov
     assert (n_layers, "LMHEAD", 0) in cov
 
@@ -212,14 +213,14 @@ def test_chiplet_placement_8b():
     p, cfg = plan("8b_4k")
     for t in p.tasks():
         ty = B.TASK_TYPES[t["type"]]
-        if ty in ("QKV", "ATTN"):
+        if ty in ("QKV", "ATTN", "OPROJ_G"):
             assert t["xcd"] == t["aux0"], t
     # and every workgroup gets work in every dense stage
     per_stage = collections.defaultdict(set)
     for t in p.tasks():
         per_stage[(t["layer"], B.TASK_TYPES[t["type"]])].add(t["wg"])
     for (layer, ty), wgs in per_stage.items():
-        if ty in ("OPROJ", "GATEUP", "DOWN", "QKV", "ATTN", "LMHEAD"):
+        if ty in ("OPROJ_G", "GATEUP", "DOWN", "QKV", "ATTN", "LMHEAD"):
             assert len(wgs) == 256, (layer, ty, len(wgs))
 
 
