@@ -311,7 +311,7 @@ __device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, 
 // ------------------------------------------------------------------ streaming row GEMV
 
 #ifndef DEC_NB
-#define DEC_NB 16
+#define DEC_NB 8
 #endif
 constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (16 KB per wave per batch)
 
