@@ -12,7 +12,7 @@
 #include "planner.h"
 
 extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream);
-extern "C" hipError_t dec_engine_occupancy(int lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu);
 
 struct dec_plan {
   dec::PlanData P;
@@ -140,7 +140,7 @@ dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, dec_pla
   st = dec_plan_create_for(shape, kv_len, &dev, out);
   if (st != DEC_OK) return st;
   int per_cu = 0;
-  hipError_t e = dec_engine_occupancy((*out)->P.lds_bytes, &per_cu);
+  hipError_t e = dec_engine_occupancy((*out)->P.shape.arch, (*out)->P.lds_bytes, &per_cu);
   if (e != hipSuccess || per_cu < 1) {
     dec_plan_destroy(*out);
     *out = nullptr;

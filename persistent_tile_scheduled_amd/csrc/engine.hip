@@ -608,7 +608,9 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
       vv[i] = ldg_nt(Vb + (size_t)pos * hd);
     }
   };
-  // blocks that hold the new slot are read coherently (it was written by other workgroups)
+  // Blocks that hold the new slot are read with agent-coherent (SC1) loads: the slot was
+  // written by other workgroups in this step, and a short row can share its cache line with
+  // a row read (and cached in this XCD's L2) before the wait.
   const rsrc_t kr = make_rsrc(Kb - sub * 8, (uint32_t)(n1 * hd * 2)), vr = make_rsrc(Vb - sub * 8, (uint32_t)(n1 * hd * 2));
   auto load_coh = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
 #pragma unroll
@@ -616,8 +618,8 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
       int pos = q0 + (blk * NP + i) * GPW + grp;
       pos = pos < q1 ? pos : q1 - 1;
       const uint32_t off = (uint32_t)(pos * hd + sub * 8) * 2u;
-      kk[i] = cld4u(kr, off);
-      vv[i] = cld4u(vr, off);
+      kk[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, kSC1);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, kSC1);
     }
   };
   // cached rows only (positions < n) before the wait
@@ -890,11 +892,639 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
       });
 }
 
+
+// ------------------------------------------------------------------ MLA tasks
+//
+// Latent attention in the absorbed form (TileRT audit page, TokenSpeed MLA paragraph: the
+// query heads are folded into the rows of one contraction over the shared latent cache):
+//   q_abs[h] = W_UK[h]^T q_nope[h];  s[h][j] = (q_abs[h] . c_j + q_rope[h] . kpe_j) / sqrt(dn + dr)
+//   o_lat[h] = sum_j softmax(s[h])_j c_j;  o[h] = W_UV[h] o_lat[h]
+// At 16 heads x (kl + dr) the attention does ~30 flop per latent byte, so it runs on the
+// matrix cores: bf16 MFMA 16x16x32, with the fp32 operands that are not bf16 (the scaled
+// query and the probabilities) split into bf16 hi + lo parts so that the products keep
+// about 16 mantissa bits.
+
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f4 mfma_bf16(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t bf_pair(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// The scaled query q~ = [q_abs | q_rope] * softmax scale * log2(e), as the B operand of the
+// score MFMA (k = latent dimension, n = head): lane L of k-step ks holds k = 32 ks + 8 (L/16)
+// + 0..7 of head L % 16, first the bf16 hi parts (block 2 ks), then the lo parts (2 ks + 1).
+__device__ __forceinline__ void qop_store(const Blk& b, int qop, int h, int k, float v) {
+  const int ks = k >> 5, L = h + 16 * ((k & 31) >> 3), j = k & 7;
+  const uint16_t hi = f2bf(v), lo = f2bf(v - bf16f(hi));
+  const uint32_t i0 = (uint32_t)(((ks * 2) * 64 + L) * 8 + j);
+  cst16(b.act, (uint32_t)qop * 4u + i0 * 2u, hi);
+  cst16(b.act, (uint32_t)qop * 4u + (i0 + 512u) * 2u, lo);
+}
+
+struct RmMlaA {  // rows [0, ql) of W_DQ, then the rows of W_DKV
+  const uint16_t *wqa, *wkva;
+  int K, ql, r0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const int r = r0 + j, sel = r >= ql ? 1 : 0;
+    const uintptr_t a = (uintptr_t)wqa;
+    const uintptr_t base = a + (uintptr_t)sel * ((uintptr_t)wkva - a);
+    return (const uint16_t*)base + (size_t)(r - sel * ql) * K;
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// x^ = RMSNorm(x); [cq_raw | kv_a] = [W_DQ; W_DKV] x^
+__device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden, ql = A.ql;
+  const RmMlaA rm{wp<uint16_t>(A, L.w[LW_WQA]), wp<uint16_t>(A, L.w[LW_WKVA]), K, ql, t.u0};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_vec(b, L.act[LA_X_IN], A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int r = t.u0 + i;
+          const int off = r < ql ? L.act[LA_CQ] + r : L.act[LA_KVA] + (r - ql);
+          cst(b.act, (uint32_t)off * 4u, b.ys[i]);
+        }
+      });
+}
+
+// W_UQ row pairs: unit (head h, i) is rows (i, i + dn/2) of the head's nope part for
+// i < dn/2, else the RoPE pair (dn + k, dn + k + dr/2), k = i - dn/2.
+struct RmMlaB {
+  const uint16_t* W;
+  int K, dn, dr, uh, u0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const int u = u0 + (j >> 1), h = u / uh, i = u - h * uh, hn = dn >> 1;
+    const int rr = i < hn ? i + (j & 1) * hn : dn + (i - hn) + (j & 1) * (dr >> 1);
+    return W + ((size_t)h * (dn + dr) + rr) * K;
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// cq = RMSNorm(cq_raw); [q_nope | q_rope] = W_UQ cq, RoPE on q_rope
+__device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.ql, dn = A.dn, dr = A.dr, uh = dn / 2 + dr / 2;
+  const RmMlaB rm{wp<uint16_t>(A, L.w[LW_WQB]), K, dn, dr, uh, t.u0};
+  return run_gemv(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
+      [&] { stage_vec(b, L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps); },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int u = t.u0 + i, h = u / uh, k = u - h * uh;
+          const float a = b.ys[2 * i], c = b.ys[2 * i + 1];
+          if (k < dn / 2) {
+            cst(b.act, (uint32_t)(L.act[LA_QNOPE] + h * dn + k) * 4u, a);
+            cst(b.act, (uint32_t)(L.act[LA_QNOPE] + h * dn + k + dn / 2) * 4u, c);
+          } else {
+            const int kk = k - dn / 2;
+            const float cs = A.rope_cs[kk], sn = A.rope_cs[A.rope_half + kk];
+            const float a2 = a * cs - c * sn, c2 = c * cs + a * sn;
+            cst(b.act, (uint32_t)(L.act[LA_QROPE] + h * dr + kk) * 4u, a2);
+            cst(b.act, (uint32_t)(L.act[LA_QROPE] + h * dr + kk + dr / 2) * 4u, c2);
+            qop_store(b, L.act[LA_QOP], h, A.kl + kk, a2 * A.attn_scale_log2);
+            qop_store(b, L.act[LA_QOP], h, A.kl + kk + dr / 2, c2 * A.attn_scale_log2);
+          }
+        }
+      });
+}
+
+// The new latent row: c = RMSNorm(kv_a[:kl]), kpe = RoPE(kv_a[kl:]), appended to the cache at
+// position kv_len as bf16. Also clears o (the W_UV tasks accumulate into it).
+__device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int kl = A.kl, dr = A.dr, KR = kl + dr, n = A.kv_len;
+  if (!wait_deps(A, b, t)) return false;
+  stage_vec(b, L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps);
+  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (n + 1) + n) * KR, (uint32_t)KR * 2u);
+  for (int i = threadIdx.x; i < kl; i += kThreads) {
+    const float v = b.xs[i];
+    cst(b.act, (uint32_t)(L.act[LA_KVNEW] + i) * 4u, v);
+    cst16(rowr, (uint32_t)i * 2u, f2bf(v));
+  }
+  for (int k = threadIdx.x; k < dr / 2; k += kThreads) {
+    const float a = cld(b.act, (uint32_t)(L.act[LA_KVA] + kl + k) * 4u);
+    const float c = cld(b.act, (uint32_t)(L.act[LA_KVA] + kl + k + dr / 2) * 4u);
+    const float cs = A.rope_cs[k], sn = A.rope_cs[A.rope_half + k];
+    const float a2 = a * cs - c * sn, c2 = c * cs + a * sn;
+    cst(b.act, (uint32_t)(L.act[LA_KVNEW] + kl + k) * 4u, a2);
+    cst(b.act, (uint32_t)(L.act[LA_KVNEW] + kl + k + dr / 2) * 4u, c2);
+    cst16(rowr, (uint32_t)(kl + k) * 2u, f2bf(a2));
+    cst16(rowr, (uint32_t)(kl + k + dr / 2) * 2u, f2bf(c2));
+  }
+  for (int i = threadIdx.x; i < A.nq * A.dv; i += kThreads) cst(b.act, (uint32_t)(L.act[LA_ATTN] + i) * 4u, 0.f);
+  return true;
+}
+
+// q_abs[h][c0, c0 + 64) = sum_d W_UK[h][d][c0 + c] q_nope[h][d]. Thread t owns 8 columns
+// (t % 8) of rows d = t / 8 + 64 i; the 64 row groups are summed through LDS.
+__device__ __forceinline__ bool task_mla_absorb(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int kl = A.kl, dn = A.dn, nb = kl / kMlaColBlock;
+  const int h = t.u0 / nb, c0 = (t.u0 - h * nb) * kMlaColBlock;
+  const uint16_t* W = wp<uint16_t>(A, L.w[LW_WUK]) + (size_t)h * dn * kl + c0;
+  const int q = threadIdx.x & 7, dg = threadIdx.x >> 3;
+  u4 w0 = u4{0u, 0u, 0u, 0u}, w1 = w0;
+  if (dg < dn) w0 = ldg_nt(W + (size_t)dg * kl + 8 * q);
+  if (dg + 64 < dn) w1 = ldg_nt(W + (size_t)(dg + 64) * kl + 8 * q);
+  if (!wait_deps(A, b, t)) return false;
+  float* qn = b.xs;                                   // [align_up(dn, 256)]
+  float* red = b.xs + ((dn + 255) & ~255);            // [64][64]
+  if (threadIdx.x < 64) {
+    dma_to_lds(qn, b.actp + L.act[LA_QNOPE] + h * dn, dn);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  __syncthreads();
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  auto fma8 = [&](u4 w, float x) {
+    acc[0] = fmaf(bf_lo(w.x), x, acc[0]); acc[1] = fmaf(bf_hi(w.x), x, acc[1]);
+    acc[2] = fmaf(bf_lo(w.y), x, acc[2]); acc[3] = fmaf(bf_hi(w.y), x, acc[3]);
+    acc[4] = fmaf(bf_lo(w.z), x, acc[4]); acc[5] = fmaf(bf_hi(w.z), x, acc[5]);
+    acc[6] = fmaf(bf_lo(w.w), x, acc[6]); acc[7] = fmaf(bf_hi(w.w), x, acc[7]);
+  };
+  if (dg < dn) fma8(w0, qn[dg]);
+  if (dg + 64 < dn) fma8(w1, qn[dg + 64]);
+  for (int d = dg + 128; d < dn; d += 64) fma8(ldg_nt(W + (size_t)d * kl + 8 * q), qn[d]);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[dg * 64 + 8 * q + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x;
+    float v0 = 0.f, v1 = 0.f;
+    for (int g = 0; g < 64; g += 2) {
+      v0 += red[g * 64 + c];
+      v1 += red[(g + 1) * 64 + c];
+    }
+    const float v = v0 + v1;
+    cst(b.act, (uint32_t)(L.act[LA_QABS] + h * kl + c0 + c) * 4u, v);
+    qop_store(b, L.act[LA_QOP], h, c0 + c, v * A.attn_scale_log2);
+  }
+  return true;
+}
+
+// One split of the latent attention: positions [u0, u1) of the layer's latent cache, all
+// heads at once. Per chunk of kMlaChunk positions (DMA'd into LDS, row stride KP = kl + dr
+// rounded up to 32):
+//   scores  S^T[pos][h] = LAT[pos][:] . q~[h][:]   (waves 0..3, one 16-position tile each)
+//   online softmax per head in base 2 (running max M and sum Lr in LDS)
+//   PV      O[h][c] += P[h][pos] LAT[pos][c]       (wave w: latent column tiles w + 8 i)
+// P goes through LDS in the A-operand order; the latent's B operand for PV (8 positions of
+// one column per lane) is gathered from the LDS chunk. The unnormalised split partial
+// (O, M, Lr) is stored for the W_UV tasks, which merge the splits.
+__device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int kl = A.kl, KR = kl + A.dr, KP = (KR + 31) & ~31, NKS = KP >> 5, nh = A.nq;
+  const int n = A.kv_len, p0 = t.u0, p1 = t.u1;
+  const int wave = wave_id(), lane = threadIdx.x & 63, hl = lane & 15, g = lane >> 4;
+  const uint16_t* lat = A.kv + (size_t)t.layer * (n + 1) * KR;
+  u4* QL = reinterpret_cast<u4*>(b.xs);                                   // [NKS][2][64]
+  uint16_t* LAT = reinterpret_cast<uint16_t*>(b.xs + NKS * 512);          // [kMlaChunk][KP]
+  u4* PA = reinterpret_cast<u4*>(b.xs + NKS * 512 + kMlaChunk * KP / 2);  // [kMlaChunk/32][2][64]
+  float* ST = b.xs + NKS * 512 + kMlaChunk * KP / 2 + (kMlaChunk / 32) * 512;
+  float* TMAX = ST;            // [4][16]
+  float* TSUM = ST + 64;       // [4][16]
+  float* MR = ST + 128;        // [16] running max
+  float* LR = ST + 144;        // [16] running sum
+  float* AL = ST + 160;        // [16] rescale of the previous chunks
+  const int segs_row = KP >> 3, nseg = kMlaChunk * segs_row;
+  // positions [c0, c0 + kMlaChunk) into LAT; rows past the split repeat its last position
+  // (finite values: their probabilities are 0); pad columns are zeroed after arrival
+  // A chunk that holds the new position (written by another workgroup in this step) is read
+  // with agent-coherent (SC1) loads: a short latent row can share its cache line with rows
+  // this XCD read, and cached, earlier in the step.
+  auto dma_chunk = [&](int c0, int w0) {  // issued by waves w0..7
+    if (wave < w0) return;
+    const bool coh = (c0 + kMlaChunk < p1 ? c0 + kMlaChunk : p1) > n;
+    for (int j = wave - w0; j * 64 < nseg; j += kWaves - w0) {
+      const int q = j * 64 + lane, row = q / segs_row, sc = q - row * segs_row;
+      int pos = c0 + row;
+      pos = pos < p1 ? pos : p1 - 1;
+      const int col = (sc * 8 < KR) ? sc * 8 : 0;
+      if (coh)
+        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kSC1);
+      else
+        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kActCpol);
+    }
+  };
+  auto zero_pad = [&](int w0) {  // each wave zeroes the pad slots of its own copies
+    if (KP == KR || wave < w0) return;
+    for (int j = wave - w0; j * 64 < nseg; j += kWaves - w0) {
+      const int q = j * 64 + lane, row = q / segs_row, sc = q - row * segs_row;
+      if (sc * 8 >= KR) *reinterpret_cast<u4*>(LAT + (size_t)q * 8) = u4{0u, 0u, 0u, 0u};
+    }
+  };
+  // a chunk of cached positions only (< kv_len) can be fetched before the wait (not by
+  // wave 0, whose dependency polls would queue behind the copies)
+  const bool pre = (p0 + kMlaChunk < p1 ? p0 + kMlaChunk : p1) <= n;
+  if (pre) dma_chunk(p0, 1);
+  if (!wait_deps(A, b, t)) return false;
+  if (!pre) dma_chunk(p0, 0);
+  if (wave == 0) dma_to_lds(reinterpret_cast<float*>(QL), b.actp + L.act[LA_QOP], NKS * 512);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  zero_pad(pre ? 1 : 0);
+  if (threadIdx.x < 16) {
+    MR[threadIdx.x] = -INFINITY;
+    LR[threadIdx.x] = 0.f;
+  }
+  __syncthreads();
+  const int nct = kl >> 4;  // latent column tiles of 16
+  f4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = p0; c0 < p1; c0 += kMlaChunk) {
+    if (c0 != p0) {
+      __syncthreads();  // the previous chunk's LAT and PA are no longer read
+      dma_chunk(c0, 0);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      zero_pad(0);
+      __syncthreads();
+    }
+    const int nt = (p1 - c0 < kMlaChunk) ? p1 - c0 : kMlaChunk;
+    float sv[4];
+    if (wave < kMlaChunk / 16) {
+      f4 d = f4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* arow = LAT + (size_t)(16 * wave + hl) * KP + 8 * g;
+#pragma unroll 2
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u4 a = *reinterpret_cast<const u4*>(arow + ks * 32);
+        d = mfma_bf16(a, QL[(ks * 2) * 64 + lane], d);
+        d = mfma_bf16(a, QL[(ks * 2 + 1) * 64 + lane], d);
+      }
+      // lane: head hl, chunk positions 16 wave + 4 g + i
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (16 * wave + 4 * g + i < nt) ? d[i] : -INFINITY;
+        mx = fmaxf(mx, sv[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      if (lane < 16) TMAX[wave * 16 + lane] = mx;
+    }
+    __syncthreads();
+    if (wave < kMlaChunk / 16) {
+      float mn = MR[hl];
+#pragma unroll
+      for (int tt = 0; tt < kMlaChunk / 16; ++tt) mn = fmaxf(mn, TMAX[tt * 16 + hl]);
+      float pv[4], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+        ps += pv[i];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      if (lane < 16) TSUM[wave * 16 + lane] = ps;
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = f2bf(pv[i]);
+        lo[i] = f2bf(pv[i] - bf16f(hi[i]));
+      }
+      // A operand of PV: k-step wave/2, lane hl + 16 * (position / 8), element position % 8
+      const int Lp = hl + 16 * (2 * (wave & 1) + (g >> 1));
+      uint16_t* pa = reinterpret_cast<uint16_t*>(PA) + ((size_t)((wave >> 1) * 2) * 64 + Lp) * 8 + 4 * (g & 1);
+      *reinterpret_cast<uint2*>(pa) = uint2{bf_pair(hi[0], hi[1]), bf_pair(hi[2], hi[3])};
+      *reinterpret_cast<uint2*>(pa + 64 * 8) = uint2{bf_pair(lo[0], lo[1]), bf_pair(lo[2], lo[3])};
+    }
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      const int h = threadIdx.x;
+      const float mo = MR[h];
+      float mn = mo, ts = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < kMlaChunk / 16; ++tt) {
+        mn = fmaxf(mn, TMAX[tt * 16 + h]);
+        ts += TSUM[tt * 16 + h];
+      }
+      const float al = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      LR[h] = LR[h] * al + ts;
+      MR[h] = mn;
+      AL[h] = al;
+    }
+    __syncthreads();
+    // PV: D rows = heads 4 g + i, column = latent 16 ct + hl
+    const f4 al4 = *reinterpret_cast<const f4*>(AL + 4 * g);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) acc[jt] *= al4;
+#pragma unroll 1
+    for (int kk = 0; kk < kMlaChunk / 32; ++kk) {
+      if (32 * kk >= nt) break;
+      const u4 ah = PA[(kk * 2) * 64 + lane], alo = PA[(kk * 2 + 1) * 64 + lane];
+      const uint16_t* bcol = LAT + (size_t)(32 * kk + 8 * g) * KP + hl;
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int ct = wave + kWaves * jt;
+        if (ct < nct) {
+          const uint16_t* bp = bcol + 16 * ct;
+          const u4 bb = u4{bf_pair(bp[0], bp[KP]), bf_pair(bp[2 * KP], bp[3 * KP]),
+                           bf_pair(bp[4 * KP], bp[5 * KP]), bf_pair(bp[6 * KP], bp[7 * KP])};
+          acc[jt] = mfma_bf16(ah, bb, acc[jt]);
+          acc[jt] = mfma_bf16(alo, bb, acc[jt]);
+        }
+      }
+    }
+  }
+  // unnormalised split partial: O[s][h][c], and (M, Lr) per head
+  const int sidx = t.a1, S = t.a2;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int ct = wave + kWaves * jt;
+    if (ct < nct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * g + i;
+        if (h < nh) cst(b.act, (uint32_t)(t.a5 + (sidx * nh + h) * kl + 16 * ct + hl) * 4u, acc[jt][i]);
+      }
+    }
+  }
+  const int Sp = (S + 1) & ~1;  // per-head stride of the (M, Lr) table
+  if (threadIdx.x < nh) {
+    cst(b.act, (uint32_t)(t.a4 + (threadIdx.x * Sp + sidx) * 2) * 4u, MR[threadIdx.x]);
+    cst(b.act, (uint32_t)(t.a4 + (threadIdx.x * Sp + sidx) * 2 + 1) * 4u, LR[threadIdx.x]);
+  }
+  return true;
+}
+
+// Merge of head h's S split partials over the latent columns [c0, c0 + 64):
+//   o_lat[h][c] = sum_s 2^(M_s - M) O_s[h][c] / sum_s 2^(M_s - M) Lr_s[h]
+// then o[h] += W_UV[h][:, c0:c0+64] o_lat[h][c0:c0+64] with agent-scope float atomics.
+__device__ __forceinline__ bool task_mla_uv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int kl = A.kl, dv = A.dv, nh = A.nq, S = t.a2, nb = kl / kMlaColBlock;
+  const int h = t.u0 / nb, c0 = (t.u0 - h * nb) * kMlaColBlock;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const uint16_t* W = wp<uint16_t>(A, L.w[LW_WUV]) + (size_t)h * dv * kl + c0;
+  const int nitems = dv * 8;  // (row j, 8 columns q) items
+  const int i0 = threadIdx.x, i1 = threadIdx.x + kThreads;
+  u4 w0 = u4{0u, 0u, 0u, 0u}, w1 = w0;
+  if (i0 < nitems) w0 = ldg_nt(W + (size_t)(i0 >> 3) * kl + 8 * (i0 & 7));
+  if (i1 < nitems) w1 = ldg_nt(W + (size_t)(i1 >> 3) * kl + 8 * (i1 & 7));
+  if (!wait_deps(A, b, t)) return false;
+  const int Sp = (S + 1) & ~1;
+  float* MLs = b.xs;                                  // [2 Sp] (M, Lr) of head h per split
+  float* ACs = MLs + ((2 * Sp + 255) & ~255);         // [S][64] split partials of this block
+  float* Ws = ACs + ((S + 3) / 4) * 256;              // [S] merge weights
+  float* red = Ws + ((S + 63) & ~63);                 // [8][64]
+  float* ol = red + 512;                              // [64]
+  if (wave == 0) dma_to_lds(MLs, b.actp + t.a4 + h * Sp * 2, 2 * Sp);
+  for (int j = wave; j * 4 < S; j += kWaves) {
+    int sp = 4 * j + (lane >> 4);
+    sp = sp < S ? sp : S - 1;
+    const float* src = b.actp + t.a5 + ((size_t)sp * nh + h) * kl + c0 + 4 * (lane & 15);
+    __builtin_amdgcn_global_load_lds((gvp)src, (lvp)(ACs + j * 256), 16, 0, kActCpol);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  __syncthreads();
+  if (wave == 0) {
+    float M = -INFINITY;
+    for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, MLs[2 * sp]);
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+    float den = 0.f;
+    for (int sp = lane; sp < S; sp += 64) {
+      const float e = exp2f(MLs[2 * sp] - M);
+      Ws[sp] = e;
+      den += e * MLs[2 * sp + 1];
+    }
+    den = wave_sum(den);
+    if (lane == 0) b.flags[2] = __float_as_int(1.0f / den);
+  }
+  __syncthreads();
+  {
+    const int c = threadIdx.x & 63;
+    float v = 0.f;
+    for (int sp = threadIdx.x >> 6; sp < S; sp += kWaves) v = fmaf(Ws[sp], ACs[sp * 64 + c], v);
+    red[(threadIdx.x >> 6) * 64 + c] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) v += red[k * 64 + threadIdx.x];
+    v *= __int_as_float(b.flags[2]);
+    ol[threadIdx.x] = v;
+    cst(b.act, (uint32_t)(L.act[LA_OLAT] + h * kl + c0 + threadIdx.x) * 4u, v);
+  }
+  __syncthreads();
+  float* o = b.actp + L.act[LA_ATTN] + h * dv;
+  auto item = [&](int i, u4 w) {
+    const float* x = ol + 8 * (i & 7);
+    float v = bf_lo(w.x) * x[0];
+    v = fmaf(bf_hi(w.x), x[1], v);
+    v = fmaf(bf_lo(w.y), x[2], v);
+    v = fmaf(bf_hi(w.y), x[3], v);
+    v = fmaf(bf_lo(w.z), x[4], v);
+    v = fmaf(bf_hi(w.z), x[5], v);
+    v = fmaf(bf_lo(w.w), x[6], v);
+    v = fmaf(bf_hi(w.w), x[7], v);
+    v = group_sum<8>(v);
+    if ((i & 7) == 0) __hip_atomic_fetch_add(o + (i >> 3), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (i0 < nitems) item(i0, w0);
+  if (i1 < nitems) item(i1, w1);
+  for (int i = threadIdx.x + 2 * kThreads; i < nitems; i += kThreads) item(i, ldg_nt(W + (size_t)(i >> 3) * kl + 8 * (i & 7)));
+  return true;
+}
+
+
+// ------------------------------------------------------------------ MoE tasks
+//
+// Sparse FFN of the MoE layers: a sigmoid router picks top_k of n_routed experts (TileRT
+// audit page, the MoE-routing paragraph: the expert choice is made on the device, so the
+// expert tasks read their weight pointers from the router's output at run time); one or
+// more shared experts run on every token, during the routing wait.
+
+// hn = RMSNorm(h); r = W_router hn
+__device__ __forceinline__ bool task_router(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden;
+  const RmPlain rm{wp<uint16_t>(A, L.w[LW_ROUTER]), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) cst(b.act, (uint32_t)(L.act[LA_RLOGIT] + t.u0 + i) * 4u, b.ys[i]);
+      });
+}
+
+// shared experts' gate/up rows (rows of [ns * eff, hidden] matrices) + SwiGLU
+__device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden;
+  const RmGateUp rm{wp<uint16_t>(A, L.w[LW_SGATE]), wp<uint16_t>(A, L.w[LW_SUP]), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
+      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+          cst(b.act, (uint32_t)(L.act[LA_SACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
+      });
+}
+
+// sigma = sigmoid(r), z = sigma + bias (fp32). The top_k experts by z, ties to the lower
+// index, in decreasing order of z: expert e goes to slot rank(e) = #{f : z_f > z_e or
+// (z_f == z_e and f < e)} when that is below top_k. Weights w = sigma_T / sum(sigma_T).
+// Output: int32 ids[top_k], then fp32 w[top_k].
+__device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int E = A.n_routed, K = A.top_k;
+  if (!wait_deps(A, b, t)) return false;
+  float* z = b.xs;                       // [E]
+  float* sg = b.xs + ((E + 255) & ~255);  // [E]
+  float* bias = sg + ((E + 255) & ~255);  // [E]
+  float* sel = b.ys;                      // [top_k] sigma of the chosen experts
+  int* ids = reinterpret_cast<int*>(b.ys + 64);
+  if (threadIdx.x < 64) {
+    dma_to_lds(z, b.actp + L.act[LA_RLOGIT], E & ~3);
+    dma_to_lds(bias, wp<float>(A, L.w[LW_RBIAS]), E & ~3);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    for (int e = (E & ~3) + (int)threadIdx.x; e < E; e += 64) {
+      z[e] = cld(b.act, (uint32_t)(L.act[LA_RLOGIT] + e) * 4u);
+      bias[e] = wp<float>(A, L.w[LW_RBIAS])[e];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const float s = 1.0f / (1.0f + expf(-z[e]));
+    sg[e] = s;
+    z[e] = s + bias[e];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const float ze = z[e];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const float zf = z[f];
+      rank += (zf > ze || (zf == ze && f < e)) ? 1 : 0;
+    }
+    if (rank < K) {
+      ids[rank] = e;
+      sel[rank] = sg[e];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += sel[k];  // fixed order: by rank
+    for (int k = threadIdx.x; k < K; k += 64) {
+      cst(b.act, (uint32_t)(L.act[LA_TOPK] + k) * 4u, __int_as_float(ids[k]));
+      cst(b.act, (uint32_t)(L.act[LA_TOPK] + K + k) * 4u, sel[k] / sum);
+    }
+  }
+  return true;
+}
+
+// Routed experts' gate/up: unit u = (slot k, row i) -> rows i of W_gate[e_k], W_up[e_k];
+// the expert ids are read after the wait, so nothing is prefetched.
+struct RmExpertGU {
+  const uint16_t *Wg, *Wu;
+  const int* ids;  // LDS
+  int K, F, u0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const int u = u0 + (j >> 1), k = u / F, i = u - k * F;
+    const uintptr_t g = (uintptr_t)Wg;
+    const uintptr_t base = g + (uintptr_t)(j & 1) * ((uintptr_t)Wu - g);
+    return (const uint16_t*)base + ((size_t)ids[k] * F + i) * K;
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
+// The chosen expert ids into LDS (clamped to the expert range so that a bad id cannot
+// address outside the weights).
+__device__ __forceinline__ void stage_ids(const EngineArgs& A, const LayerDesc& L, Blk& b, int* ids) {
+  if (threadIdx.x < (unsigned)A.top_k) {
+    int e = __float_as_int(cld(b.act, (uint32_t)(L.act[LA_TOPK] + threadIdx.x) * 4u));
+    e = e < 0 ? 0 : (e >= A.n_routed ? A.n_routed - 1 : e);
+    ids[threadIdx.x] = e;
+  }
+}
+
+__device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden, F = A.eff;
+  int* ids = reinterpret_cast<int*>(b.scr);
+  const RmExpertGU rm{wp<uint16_t>(A, L.w[LW_EGATE]), wp<uint16_t>(A, L.w[LW_EUP]), ids, K, F, t.u0};
+  return run_gemv(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, false,
+      [&] {
+        stage_ids(A, L, b, ids);
+        stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps);
+      },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+          cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
+      });
+}
+
+// Down projections: output row r sums G = ns + top_k segments of eff columns: segment s < ns
+// is shared expert s (columns s*eff.. of W_sdown[r]), segment ns + k is W_down[e_k][r]. The
+// staged input holds the shared activations and the routed ones pre-scaled by w_k, one
+// segment per 512-aligned slot.
+struct RmMoeDown {
+  const uint16_t *Ws, *Wd;
+  const int* ids;  // LDS
+  int ns, G, F, Fp, d, r0;
+  __device__ __forceinline__ const uint16_t* row(int j) const {
+    const int q = j / G, sgm = j - q * G, r = r0 + q;
+    if (sgm < ns) return Ws + (size_t)r * ns * F + (size_t)sgm * F;
+    return Wd + ((size_t)ids[sgm - ns] * d + r) * F;
+  }
+  __device__ __forceinline__ int xoff(int j) const { return (j % G) * Fp; }
+};
+
+__device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int F = A.eff, Fp = pad512(F), ns = A.n_shared, Kt = A.top_k, G = ns + Kt, d = A.hidden;
+  int* ids = reinterpret_cast<int*>(b.scr);
+  float* wk = b.scr + 64;
+  const RmMoeDown rm{wp<uint16_t>(A, L.w[LW_SDOWN]), wp<uint16_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0};
+  return run_gemv(
+      A, b, t, rm, G * (t.u1 - t.u0), F, G, false,
+      [&] {
+        stage_ids(A, L, b, ids);
+        if (threadIdx.x < 64) {
+          for (int k = threadIdx.x; k < Kt; k += 64) wk[k] = cld(b.act, (uint32_t)(L.act[LA_TOPK] + Kt + k) * 4u);
+          for (int sg = 0; sg < G; ++sg) {
+            const float* src = b.actp + (sg < ns ? L.act[LA_SACT] + sg * F : L.act[LA_ACT] + (sg - ns) * F);
+            dma_to_lds(b.xs + sg * Fp, src, F);
+          }
+          __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        }
+        __syncthreads();
+        for (int sg = 0; sg < G; ++sg) {
+          const float w = sg < ns ? 1.0f : wk[sg - ns];
+          for (int c = threadIdx.x; c < Fp; c += kThreads) {
+            float* x = b.xs + sg * Fp + c;
+            *x = c < F ? *x * w : 0.f;
+          }
+        }
+        __syncthreads();
+      },
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+          const int rr = t.u0 + i;
+          const float y = b.ys[i];
+          const float xo = cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) + y;
+          cst(b.act, (uint32_t)(L.act[LA_FFN_OUT] + rr) * 4u, y);
+          cst(b.act, (uint32_t)(L.act[LA_X_OUT] + rr) * 4u, xo);
+          if (t.a0) A.out[rr] = xo;
+        }
+      });
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ the engine
 
-extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs A) {
+// The task walk, instantiated once per model family so that each kernel's register
+// allocation covers only the task types it runs: GQA (MLA = false) and MLA / MLA + MoE.
+template <bool MLA>
+__device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
   Blk b;
@@ -917,18 +1547,43 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
     const uint32_t t0 = (uint32_t)now();
     bool ok = true;
     int sig = t.signal;
-    switch (t.type) {
-      case T_QKV: ok = task_qkv(A, b, t); break;
-      case T_ATTN:
-        ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
-        break;
-      case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
-      case T_HINIT: ok = task_hinit(A, b, t); break;
-      case T_OPROJ: ok = task_oproj(A, b, t); break;
-      case T_GATEUP: ok = task_gateup(A, b, t); break;
-      case T_DOWN: ok = task_down(A, b, t); break;
-      case T_LMHEAD: ok = task_lmhead(A, b, t); break;
-      default: ok = false; break;
+    if constexpr (!MLA) {
+      switch (t.type) {
+        case T_QKV: ok = task_qkv(A, b, t); break;
+        case T_ATTN:
+          ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
+          break;
+        case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
+        case T_HINIT: ok = task_hinit(A, b, t); break;
+        case T_GATEUP: ok = task_gateup(A, b, t); break;
+        case T_DOWN: ok = task_down(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead(A, b, t); break;
+        case T_ROUTER: ok = task_router(A, b, t); break;
+        case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
+        case T_TOPK: ok = task_topk(A, b, t); break;
+        case T_EXPERT_GU: ok = task_expert_gu(A, b, t); break;
+        case T_MOE_DOWN: ok = task_moe_down(A, b, t); break;
+        default: ok = false; break;
+      }
+    } else {
+      switch (t.type) {
+        case T_MLA_A: ok = task_mla_a(A, b, t); break;
+        case T_MLA_B: ok = task_mla_b(A, b, t); break;
+        case T_MLA_KVAPP: ok = task_mla_kvapp(A, b, t); break;
+        case T_MLA_ABSORB: ok = task_mla_absorb(A, b, t); break;
+        case T_MLA_ATTN: ok = task_mla_attn(A, b, t); break;
+        case T_MLA_UV: ok = task_mla_uv(A, b, t); break;
+        case T_OPROJ: ok = task_oproj(A, b, t); break;
+        case T_GATEUP: ok = task_gateup(A, b, t); break;
+        case T_DOWN: ok = task_down(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead(A, b, t); break;
+        case T_ROUTER: ok = task_router(A, b, t); break;
+        case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
+        case T_TOPK: ok = task_topk(A, b, t); break;
+        case T_EXPERT_GU: ok = task_expert_gu(A, b, t); break;
+        case T_MOE_DOWN: ok = task_moe_down(A, b, t); break;
+        default: ok = false; break;
+      }
     }
     if (!ok) break;
     signal(A, sig);
@@ -957,24 +1612,30 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine(EngineArgs 
   }
 }
 
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa(EngineArgs A) { engine_body<false>(A); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla(EngineArgs A) { engine_body<true>(A); }
+
 }  // namespace dec
 
 // Host-side launch (used by the C ABI in api.cpp).
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream) {
-  static int configured_lds = -1;
-  if (configured_lds < lds_bytes) {
-    hipError_t e = hipFuncSetAttribute((const void*)dec::dec_engine, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    configured_lds = lds_bytes;
-  }
-  void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
-  return hipLaunchCooperativeKernel((const void*)dec::dec_engine, dim3(n_wg), dim3(dec::kThreads), kargs,
-                                    (unsigned)lds_bytes, stream);
+static const void* engine_fn(int arch) {
+  return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int lds_bytes, int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute((const void*)dec::dec_engine, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream) {
+  static int configured_lds[2] = {-1, -1};
+  const int k = args->arch == 0 ? 0 : 1;
+  if (configured_lds[k] < lds_bytes) {
+    hipError_t e = hipFuncSetAttribute(engine_fn(args->arch), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    configured_lds[k] = lds_bytes;
+  }
+  void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
+  return hipLaunchCooperativeKernel(engine_fn(args->arch), dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
+}
+
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu) {
+  hipError_t e = hipFuncSetAttribute(engine_fn(arch), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)dec::dec_engine, dec::kThreads,
-                                                      (size_t)lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch), dec::kThreads, (size_t)lds_bytes);
 }

@@ -16,6 +16,11 @@ constexpr int kMaxDepsPerTask = 64;    // one poller lane per dependency counter
 constexpr int kYsFloats = 1024;        // per-task GEMV row results staged in LDS
 constexpr int kMaxTaskRows = 1024;     // rows of one GEMV task (row-pointer table in LDS)
 constexpr int kLdsMin = 96 * 1024;     // > half a CU's LDS: forces one workgroup per CU
+// Latent (MLA) attention on the matrix cores: all query heads (at most 16) are the 16 columns
+// of one bf16 MFMA 16x16x32 tile, positions its rows, the latent dimension its contraction.
+constexpr int kMlaHeads = 16;          // query heads folded into one MFMA tile
+constexpr int kMlaChunk = 64;          // positions per LDS-resident latent chunk
+constexpr int kMlaColBlock = 64;       // latent columns per absorb / W_UV task
 
 // Task types. Every type runs the same five phases: issue loads of its static operand
 // (weights, cached KV) -> wait on its dependency counters -> stage its dynamic input
@@ -31,8 +36,9 @@ enum TaskType : int32_t {
   T_MLA_B = 8,       // q RMSNorm + W_UQ row pairs + RoPE on the q_rope part
   T_MLA_KVAPP = 9,   // kv RMSNorm + RoPE on k_pe + latent-cache append
   T_MLA_ABSORB = 10, // q_abs[h] = W_UK[h]^T q_nope[h], one column block per task
-  T_MLA_ATTN = 11,   // latent attention partial over a position range + ticket merge
-  T_MLA_UV = 12,     // o[h] = W_UV[h] o_lat[h]
+  T_MLA_ATTN = 11,   // latent attention partial over a position range (MFMA)
+  T_MLA_UV = 12,     // merge of one head's splits over a latent column block + W_UV[h] times
+                     // that block, added into o[h] with agent-scope atomics
   T_ROUTER = 13,     // FFN RMSNorm + router rows
   T_SHARED_GU = 14,  // FFN RMSNorm + shared-expert gate/up rows + SwiGLU
   T_TOPK = 15,       // sigmoid, top-k selection, normalised weights
@@ -86,6 +92,8 @@ enum LayerA : int32_t {
   LA_RLOGIT,     // MoE: router logits [n_routed]
   LA_TOPK,       // MoE: int32 [top_k] expert ids, then fp32 [top_k] weights
   LA_SACT,       // MoE: shared-expert activation [ns*eff]
+  LA_QOP,        // MLA: scaled [q_abs | q_rope] as bf16 hi/lo pairs in MFMA B-operand order
+  LA_PML,        // MLA: split partial (m, l) [nh][S][2]
   LA_COUNT
 };
 

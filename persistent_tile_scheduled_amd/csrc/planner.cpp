@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kMinPosPerSplit = 16;
 constexpr int kRowsCap = kMaxTaskRows;     // rows of one GEMV task (LDS row tables)
-constexpr int kAbsorbBlock = 64;           // latent columns per absorb task
+constexpr int kMinPosMla = 64;             // positions per latent-attention split (at least)
 constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -52,6 +52,7 @@ struct Builder {
   int64_t act_floats = 0;
   int64_t xs_floats_max = 0;  // largest staged input vector (padded)
   int64_t scratch_floats = 1024;
+  int64_t mla_lds = 0;        // LDS floats (after the header) the latent-attention tasks use
 
   Builder(const dec_model_shape& s_, int64_t n_, const dec_device_info& d_, PlanData& p_, std::string& e_)
       : s(s_), n(n_), dev(d_), P(p_), err(e_) {}
@@ -150,15 +151,14 @@ struct Builder {
       if (q.q_lora_rank || q.kv_lora_rank || q.qk_nope || q.qk_rope || q.v_head || q.n_routed || q.n_shared || q.top_k || q.expert_ffn)
         return fail(DEC_E_SHAPE, "GQA shape with MLA/MoE fields set", st);
     } else if (q.arch == DEC_ARCH_MLA || q.arch == DEC_ARCH_MOE) {
-      if (q.n_q_heads < 1 || q.n_q_heads > 64) return fail(DEC_E_SHAPE, "MLA needs 1..64 heads", st);
+      if (q.n_q_heads < 1 || q.n_q_heads > kMlaHeads) return fail(DEC_E_SHAPE, "MLA needs 1..16 query heads", st);
       if (q.n_kv_heads || q.head_dim) return fail(DEC_E_SHAPE, "MLA shape with GQA fields set", st);
       if (q.q_lora_rank < 8 || q.q_lora_rank % 8) return fail(DEC_E_SHAPE, "q_lora_rank must be a positive multiple of 8", st);
-      if (q.kv_lora_rank < 8 || q.kv_lora_rank % 8 || (q.kv_lora_rank > kAbsorbBlock && q.kv_lora_rank % kAbsorbBlock))
-        return fail(DEC_E_SHAPE, "kv_lora_rank must be a multiple of 8 (and of 64 above 64)", st);
-      if (q.kv_lora_rank > 1024) return fail(DEC_E_SHAPE, "kv_lora_rank above 1024", st);
-      if (q.qk_nope < 2 || q.qk_nope % 2 || q.qk_rope < 2 || q.qk_rope % 8 || q.qk_rope > 128)
-        return fail(DEC_E_SHAPE, "qk_nope must be even and qk_rope a multiple of 8 (<= 128)", st);
-      if (q.v_head < 1) return fail(DEC_E_SHAPE, "v_head < 1", st);
+      if (q.kv_lora_rank < kMlaColBlock || q.kv_lora_rank % kMlaColBlock || q.kv_lora_rank > 512)
+        return fail(DEC_E_SHAPE, "kv_lora_rank must be a multiple of 64, at most 512", st);
+      if (q.qk_nope < 8 || q.qk_nope % 8 || q.qk_rope < 8 || q.qk_rope % 8 || q.qk_rope > 128)
+        return fail(DEC_E_SHAPE, "qk_nope and qk_rope must be multiples of 8 (qk_rope <= 128)", st);
+      if (q.v_head < 8 || q.v_head % 8) return fail(DEC_E_SHAPE, "v_head must be a positive multiple of 8", st);
       if (q.arch == DEC_ARCH_MLA) {
         if (q.ffn < 8 || q.ffn % 8) return fail(DEC_E_SHAPE, "ffn must be a positive multiple of 8", st);
         if (q.n_routed || q.n_shared || q.top_k || q.expert_ffn) return fail(DEC_E_SHAPE, "MLA shape with MoE fields set", st);
@@ -322,64 +322,72 @@ struct Builder {
     LayerDesc& L = P.layers[l];
     const int d = s.hidden, nh = s.n_q_heads, ql = s.q_lora_rank, kl = s.kv_lora_rank;
     const int dn = s.qk_nope, dr = s.qk_rope, dv = s.v_head;
+    const int KR = kl + dr, KP = (int)align_up(KR, 32), NKS = KP / 32;
     std::string p = "layers." + std::to_string(l) + ".";
     for (int i = 0; i < LA_COUNT; ++i) L.act[i] = -1;
     L.act[LA_X_IN] = (int)x_in;
     L.act[LA_CQ] = (int)act(p + "cq_raw", ql);
-    L.act[LA_KVA] = (int)act(p + "kv_a", kl + dr);
+    L.act[LA_KVA] = (int)act(p + "kv_a", KR);
     L.act[LA_QNOPE] = (int)act(p + "q_nope", (int64_t)nh * dn);
     L.act[LA_QROPE] = (int)act(p + "q_rope", (int64_t)nh * dr);
-    L.act[LA_KVNEW] = (int)act(p + "kv_new", kl + dr);
+    L.act[LA_KVNEW] = (int)act(p + "kv_new", KR);
     L.act[LA_QABS] = (int)act(p + "q_abs", (int64_t)nh * kl);
+    L.act[LA_QOP] = (int)act(p + "q_operand", (int64_t)NKS * 512, DEC_DTYPE_I32);
     L.act[LA_OLAT] = (int)act(p + "o_lat", (int64_t)nh * kl);
     L.act[LA_ATTN] = (int)act(p + "attn", (int64_t)nh * dv);
     L.act[LA_H] = (int)act(p + "h", d);
     L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
     L.act[LA_X_OUT] = (int)act(p + "x_out", d);
-    need_xs(d); need_xs(ql); need_xs(kl + dr); need_xs((int64_t)nh * align_up(kl, kChunkCols)); need_xs((int64_t)nh * dv);
+    need_xs(d); need_xs(ql); need_xs(KR); need_xs((int64_t)nh * dv);
 
     // A: [W_DQ; W_DKV] rows from the normalised layer input
     ++stage;
     const int ca = counter(n_xcd);
-    spread(all_wgs(), ql + kl + dr, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + xcd(w)); });
+    spread(all_wgs(), ql + KR, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + xcd(w)); });
     auto da = all_of(ca, n_xcd);
 
-    // B: W_UQ row pairs (nope pairs, then RoPE pairs, per head) + the latent-cache append
+    // B: W_UQ row pairs (nope pairs, then RoPE pairs, per head); the latent-cache append
+    // (which also clears the attention output that the W_UV tasks accumulate into)
     ++stage;
     const int cb = counter(n_xcd), ckv = counter(1);
     const int UH = dn / 2 + dr / 2;
-    add(n_wg - 1, T_MLA_KVAPP, l, 0, kl + dr, da, ckv);
+    add(n_wg - 1, T_MLA_KVAPP, l, 0, KR, da, ckv);
     spread(all_wgs(), nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + xcd(w)); });
     auto db = all_of(cb, n_xcd);
 
-    // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h]
+    // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h], one (head, 64-column block) per task
     ++stage;
     const int cabs = counter(n_xcd);
-    const int cbw = std::min(kAbsorbBlock, kl);
-    const int nblk = nh * (kl / cbw);
-    spread(all_wgs(), nblk, 1 << 30, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + xcd(w), -1, cbw); });
+    const int nblk = nh * (kl / kMlaColBlock);
+    spread(all_wgs(), nblk, 1, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + xcd(w)); });
 
-    // latent attention splits + ticket merge
+    // latent attention: S position splits, all heads folded into one MFMA tile
     ++stage;
-    const int tick = counter(1), merged = counter(1);
-    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit));
-    const int64_t pstride = (int64_t)nh * (kl + 2);
-    const int64_t part = act(p + "attn_partials", (int64_t)S * pstride);
+    const int catt = counter(n_xcd);
+    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kMinPosMla - 1) / kMinPosMla));
+    const int Sp = (S + 1) & ~1;  // per-head stride of the (M, Lr) table (16-byte rows)
+    const int64_t pml = act(p + "attn_ml", (int64_t)nh * Sp * 2);
+    const int64_t part = act(p + "attn_partials", (int64_t)S * nh * kl);
+    L.act[LA_PML] = (int)pml;
     L.act[LA_PART] = (int)part;
     std::vector<int32_t> dat = all_of(cabs, n_xcd);
     dat.insert(dat.end(), db.begin(), db.end());
     dat.push_back(ckv);
-    const int merge_id = next_id++;
     for (int sp = 0; sp < S; ++sp) {
+      const int w = (int)((int64_t)sp * n_wg / S);
       int p0 = (int)((n + 1) * sp / S), p1 = (int)((n + 1) * (sp + 1) / S);
-      add(sp % n_wg, T_MLA_ATTN, l, p0, p1, dat, tick, merged, 0, sp, S, merge_id, (int)part);
+      add(w, T_MLA_ATTN, l, p0, p1, dat, catt + xcd(w), -1, 0, sp, S, 0, (int)pml, (int)part);
     }
-    P.counter_total[merged] = 1;
+    // LDS: q operand + one latent chunk + P operand + softmax statistics
+    mla_lds = std::max<int64_t>(mla_lds, (int64_t)NKS * 512 + (int64_t)kMlaChunk * KP / 2 + (kMlaChunk / 32) * 512 + 256);
 
-    // o[h] = W_UV[h] o_lat[h]
+    // W_UV: per (head, column block) merge the splits, multiply, add into o[h]
     ++stage;
     const int cuv = counter(n_xcd);
-    spread(all_wgs(), nh * dv, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_UV, l, a, b, {merged}, cuv + xcd(w)); });
+    spread(all_wgs(), nblk, 1, [&](int w, int a, int b) {
+      add(w, T_MLA_UV, l, a, b, all_of(catt, n_xcd), cuv + xcd(w), -1, 0, 0, S, 0, (int)pml, (int)part);
+    });
+    mla_lds = std::max<int64_t>(mla_lds, align_up(2LL * Sp, 256) + align_up(S, 4) / 4 * 256 + align_up(S, 64) + 8 * 64 + 64);
 
     // O projection + residual
     ++stage;
@@ -404,6 +412,7 @@ struct Builder {
     L.act[LA_SACT] = (int)act(p + "shared_act", std::max(SF, 1));
     L.act[LA_ACT] = (int)act(p + "expert_act", (int64_t)K * F);
     need_xs((int64_t)(s.n_shared + K) * align_up(F, kChunkCols));
+    need_xs(3 * align_up(E, 256));  // top-k: z, sigma, bias
 
     // E1: router rows on a few workgroups, the shared expert's gate/up on the rest
     ++stage;
@@ -509,9 +518,9 @@ struct Builder {
     P.gs_floats = gs;
     int64_t lds = 4 * (header + xs_floats_max + kYsFloats + tables + gs + scratch_floats);
     if (s.arch != DEC_ARCH_GQA) {
-      // latent attention: q (heads x (kl+dr)) + per-wave partials
-      int64_t w = (int64_t)s.n_q_heads * (s.kv_lora_rank + s.qk_rope) + (int64_t)kWaves * s.n_q_heads * (s.kv_lora_rank + 2);
-      lds = std::max<int64_t>(lds, 4 * (header + w + kYsFloats + tables + gs + 1024));
+      // the latent-attention, absorb and W_UV tasks use the whole region after the header
+      const int64_t absorb = align_up(s.qk_nope, 256) + (int64_t)kMlaColBlock * 64 + 64;
+      lds = std::max<int64_t>(lds, 4 * (header + std::max(mla_lds, absorb)));
     }
     lds = std::max<int64_t>(align_up(lds, 1024), kLdsMin);
     P.lds_bytes = (int32_t)lds;
@@ -626,8 +635,7 @@ std::string validate_plan(const PlanData& p) {
       case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope;
       case T_MLA_B: return (int64_t)s.n_q_heads * (s.qk_nope / 2 + s.qk_rope / 2);
       case T_MLA_KVAPP: return (int64_t)s.kv_lora_rank + s.qk_rope;
-      case T_MLA_ABSORB: return (int64_t)s.n_q_heads * (s.kv_lora_rank / std::min(kAbsorbBlock, s.kv_lora_rank));
-      case T_MLA_UV: return (int64_t)s.n_q_heads * s.v_head;
+      case T_MLA_ABSORB: case T_MLA_UV: return (int64_t)s.n_q_heads * (s.kv_lora_rank / kMlaColBlock);
       case T_ROUTER: case T_TOPK: return s.n_routed;
       case T_SHARED_GU: return (int64_t)s.n_shared * s.expert_ffn;
       case T_EXPERT_GU: return (int64_t)s.top_k * s.expert_ffn;

@@ -1,0 +1,163 @@
+"""GPU parity of the MLA and MLA + MoE engine paths against the fp64 oracle (needs an MI355X).
+
+Bars as for the GQA path: relative L2 error <= 1e-2 on every per-layer vector of the trace
+and <= 2e-2 on the step output (these models have no LM head: the output is the last
+hidden state); the appended latent row within one bf16 ulp of the oracle's rounding.
+Expert selection is integer work: the engine's top-k must equal the oracle's selection made
+in fp32 from the engine's own router logits, element by element; against the oracle's fully
+fp64 forward it must match wherever the oracle's top-k margin exceeds what fp32 logits can
+move (near-ties may resolve either way).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from test_gpu_parity import HostWeights, LAYER_TOL, LOGIT_TOL, check_coverage, check_kv_slot, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+MLA_TRACE = ["cq_raw", "kv_a", "q_nope", "q_rope", "q_abs", "o_lat", "attn", "h", "ffn_out", "x_out"]
+DENSE_FFN = ["ffn_act"]
+MOE_FFN = ["router_logits", "shared_act"]
+TIE_MARGIN = 1e-4   # z = sigmoid(r) + b; fp32 logits move z by well under this
+
+
+def _engine(cfg, w, **kw):
+    from persistent_tile_scheduled_amd.engine import DecodeEngine
+    return DecodeEngine(cfg, w, **kw)
+
+
+def engine_topk(eng, cfg, l):
+    k = cfg["top_k"]
+    raw = eng.buffer(f"layers.{l}.topk").cpu()
+    ids = raw[:k].numpy().astype(np.int64)
+    wts = raw[k:2 * k].view(torch.float32).numpy().astype(np.float64)
+    return ids, wts
+
+
+def check_moe_layer(eng, cfg, l, t, W):
+    """Top-k exactness on the engine's own logits, near-tie rule against the oracle's, and
+    the routed activations compared expert by expert."""
+    k = cfg["top_k"]
+    ids, wts = engine_topk(eng, cfg, l)
+    r_gpu = eng.buffer(f"layers.{l}.router_logits").cpu().numpy().astype(np.float64)
+    bias = W(f"layers.{l}.router_bias")
+    same = O.route(r_gpu, bias, k)
+    assert np.array_equal(ids, same["topk"]), (l, ids, same["topk"])
+    assert rel_l2(wts, same["w"]) <= 1e-5
+    if t["topk_margin"][0] > TIE_MARGIN:
+        assert set(ids.tolist()) == set(t["topk"].tolist()), (l, ids, t["topk"])
+    acts = eng.buffer(f"layers.{l}.expert_act").cpu().numpy()
+    F = cfg["expert_ffn"]
+    want = {int(e): t["expert_act"][i * F:(i + 1) * F] for i, e in enumerate(t["topk"])}
+    for i, e in enumerate(ids.tolist()):
+        if e in want:
+            assert rel_l2(acts[i * F:(i + 1) * F], want[e]) <= LAYER_TOL, (l, e)
+
+
+def check_mla_layer(eng, cfg, l, t, W, kv_bits, tol=LAYER_TOL, same_input=None):
+    names = MLA_TRACE + (DENSE_FFN if cfg["arch"] == "mla" else MOE_FFN)
+    errs = {}
+    for nm in names:
+        got = eng.buffer(f"layers.{l}.{nm}").cpu().numpy()[: t[nm].size]
+        errs[nm] = rel_l2(got, t[nm])
+    kvn = eng.buffer(f"layers.{l}.kv_new").cpu().numpy()
+    errs["kv_new"] = rel_l2(kvn, np.concatenate([t["c_new"], t["kpe_new"]]))
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, (l, bad)
+    check_kv_slot(cfg, kv_bits, l, t, same_input=(l == 0) if same_input is None else same_input)
+    if cfg["arch"] == "moe":
+        check_moe_layer(eng, cfg, l, t, W)
+    return errs
+
+
+CASES = [("mla_tiny", 0, None), ("mla_tiny", 1, None), ("mla_tiny", 2, 0), ("mla_tiny", 3, 20000),
+         ("mla_small", 0, None), ("moe_tiny", 0, None), ("moe_tiny", 5, 1), ("moe_small", 0, None)]
+
+
+@pytest.mark.parametrize("name,seed,kv_len", CASES)
+def test_small_mla_full_parity(name, seed, kv_len):
+    """Whole step, oracle end to end from the same inputs. kv_len 0 (a single position),
+    1, and 20000 (more than 64 positions per split: several LDS chunks per split) cover the
+    edges of the latent-attention tiling."""
+    cfg = dict(workloads.get_config(name))
+    if kv_len is not None:
+        cfg["kv_len"] = kv_len
+    print(f"[parity] {name} seed={seed} kv_len={cfg['kv_len']}", flush=True)
+    w, x, kv = workloads.generate(cfg, seed=seed, device="cuda")
+    eng = _engine(cfg, w)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    kvb = workloads.bf16_bits(kv)
+    res = O.forward(cfg, W, workloads.bf16_bits(x), kvb)
+    for l, t in enumerate(res["layers"]):
+        errs = check_mla_layer(eng, cfg, l, t, W, kvb)
+        print(f"[parity] layer {l}: max rel error {max(errs.values()):.2e}", flush=True)
+    assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
+    check_coverage(eng)
+
+
+@pytest.mark.parametrize("name", ["mla_small", "moe_small"])
+def test_mla_multi_step_changing_input(name):
+    cfg = workloads.get_config(name)
+    w, x, kv = workloads.generate(cfg, seed=11, device="cuda")
+    eng = _engine(cfg, w)
+    W = HostWeights(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    for step in range(3):
+        print(f"[multi-step] {name} step {step}", flush=True)
+        xs = (torch.randn(cfg["hidden"], generator=g, device="cuda") * (1 + step)).to(torch.bfloat16)
+        out = eng.step(xs, kv).clone()
+        torch.cuda.synchronize()
+        eng.status()
+        kvb = workloads.bf16_bits(kv)
+        res = O.forward(cfg, W, workloads.bf16_bits(xs), kvb)
+        assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL, step
+        for l, t in enumerate(res["layers"]):
+            check_mla_layer(eng, cfg, l, t, W, kvb)
+    check_coverage(eng, steps=3)
+
+
+def _teacher_forced_mla(name, layers):
+    """Full-size config in the bench's launch configuration: for sampled layers the oracle
+    recomputes the layer from the engine's own layer input."""
+    cfg = workloads.get_config(name)
+    print(f"[parity] {name}: generating", flush=True)
+    w, x, kv = workloads.generate(cfg, seed=0, device="cuda")
+    eng = _engine(cfg, w)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    n = cfg["kv_len"]
+    for l in layers:
+        print(f"[parity] {name}: layer {l}", flush=True)
+        xin = (O.widen_bf16(workloads.bf16_bits(x)) if l == 0
+               else eng.buffer(f"layers.{l - 1}.x_out").cpu().numpy().astype(np.float64))
+        kvl = workloads.bf16_bits(kv[l])
+        _, t = O.mla_layer(cfg, W, l, xin, kvl, n)
+        names = MLA_TRACE + (DENSE_FFN if cfg["arch"] == "mla" else MOE_FFN)
+        errs = {nm: rel_l2(eng.buffer(f"layers.{l}.{nm}").cpu().numpy()[: t[nm].size], t[nm]) for nm in names}
+        print(f"[parity] layer {l} rel errors {errs}", flush=True)
+        assert all(v <= LAYER_TOL for v in errs.values()), errs
+        check_kv_slot(cfg, kvl[None], 0, t)
+        if cfg["arch"] == "moe":
+            check_moe_layer(eng, cfg, l, t, W)
+        W.drop(f"layers.{l}.")
+    last = cfg["n_layers"] - 1
+    xo = eng.buffer(f"layers.{last}.x_out").cpu().numpy()
+    assert np.array_equal(out.cpu().numpy(), xo)   # no LM head: the output is the last hidden state
+    check_coverage(eng)
+
+
+def test_mla_8k_sampled_layers():
+    _teacher_forced_mla("mla_8k", [0, 7])
+
+
+def test_moe_4k_sampled_layers():
+    _teacher_forced_mla("moe_4k", [0, 3])

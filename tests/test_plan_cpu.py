@@ -15,6 +15,7 @@ from persistent_tile_scheduled_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MI355X = B.device_info()
 GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k"]
+MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k"]
 
 
 def plan(name, dev=MI355X, **over):
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     assert declared == set(B.ABI_SYMBOLS)
 
 
-@pytest.mark.parametrize("name", GQA_CONFIGS)
+@pytest.mark.parametrize("name", GQA_CONFIGS + MLA_CONFIGS)
 def test_weight_list_matches_input_layout(name):
     p, cfg = plan(name)
     got = [(d["name"], d["shape"], d["dtype"]) for d in p.weight_descs()]
@@ -109,11 +110,23 @@ def test_step_before_bind_and_null_arguments():
 
 def _expected_units(cfg, ttype):
     n1 = cfg["kv_len"] + 1
+    g = cfg.get
     return {
-        "QKV": (cfg["n_q_heads"] // max(cfg.get("n_kv_heads", 1), 1) + 2) * cfg.get("head_dim", 0) // 2,
+        "QKV": (cfg["n_q_heads"] // max(g("n_kv_heads", 1), 1) + 2) * g("head_dim", 0) // 2,
         "ATTN": n1, "OPROJ": cfg["hidden"], "OPROJ_G": cfg["hidden"], "DOWN": cfg["hidden"],
-        "GATEUP": cfg.get("ffn", 0), "HINIT": cfg["hidden"],
+        "GATEUP": g("ffn", 0), "HINIT": cfg["hidden"],
         "LMHEAD": cfg["vocab"],
+        # MLA: [W_DQ; W_DKV] rows, W_UQ row pairs, the latent row, (head, 64-column) blocks
+        "MLA_A": g("q_lora_rank", 0) + g("kv_lora_rank", 0) + g("qk_rope", 0),
+        "MLA_B": cfg["n_q_heads"] * (g("qk_nope", 0) // 2 + g("qk_rope", 0) // 2),
+        "MLA_KVAPP": g("kv_lora_rank", 0) + g("qk_rope", 0),
+        "MLA_ABSORB": cfg["n_q_heads"] * g("kv_lora_rank", 0) // 64,
+        "MLA_UV": cfg["n_q_heads"] * g("kv_lora_rank", 0) // 64,
+        "MLA_ATTN": n1,
+        # MoE: router rows, shared gate/up pairs, the top-k over all experts, routed pairs
+        "ROUTER": g("n_routed", 0), "TOPK": g("n_routed", 0),
+        "SHARED_GU": g("n_shared", 0) * g("expert_ffn", 0),
+        "EXPERT_GU": g("top_k", 0) * g("expert_ffn", 0), "MOE_DOWN": cfg["hidden"],
     }[ttype]
 
 
@@ -157,7 +170,15 @@ def simulate(p):
     return done
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k"])
+STAGES = {
+    "gqa": ("QKV", "ATTN", "OPROJ_G", "GATEUP", "DOWN"),
+    "mla": ("MLA_A", "MLA_B", "MLA_KVAPP", "MLA_ABSORB", "MLA_ATTN", "MLA_UV", "OPROJ", "GATEUP", "DOWN"),
+    "moe": ("MLA_A", "MLA_B", "MLA_KVAPP", "MLA_ABSORB", "MLA_ATTN", "MLA_UV", "OPROJ", "ROUTER", "SHARED_GU",
+            "TOPK", "EXPERT_GU", "MOE_DOWN"),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k"] + MLA_CONFIGS)
 def test_schedule_drains_and_covers(name):
     p, cfg = plan(name)
     tasks = p.tasks()
@@ -178,9 +199,12 @@ def test_schedule_drains_and_covers(name):
         assert at == _expected_units(cfg, ty), (layer, ty)
     n_layers = cfg["n_layers"]
     for layer in range(n_layers):
-        for ty in ("QKV", "ATTN", "OPROJ_G", "GATEUP", "DOWN"):
-            assert (layer, ty, 0) in cov
-    assert (n_layers, "LMHEAD", 0) in cov
+        for ty in STAGES[cfg["arch"]]:
+            assert (layer, ty, 0) in cov, (layer, ty)
+    if cfg["vocab"] > 0:
+        assert (n_layers, "LMHEAD", 0) in cov
+    else:
+        assert not any(k[1] == "LMHEAD" for k in cov)
 
 
 def test_lists_in_stage_order_and_deps_point_back():
@@ -240,3 +264,66 @@ def test_buffers_cover_trace():
     ws = p.sizes()["workspace_bytes"]
     for b in bufs.values():
         assert b["offset"] % 256 == 0 and b["offset"] + b["count"] * 4 <= ws
+
+
+@pytest.mark.parametrize("over,status", [
+    ({"n_q_heads": 17}, "DEC_E_SHAPE"),          # more heads than one MFMA tile folds
+    ({"kv_lora_rank": 96}, "DEC_E_SHAPE"),       # latent width not a multiple of 64
+    ({"kv_lora_rank": 1024}, "DEC_E_SHAPE"),     # above 512
+    ({"qk_rope": 12}, "DEC_E_SHAPE"),
+    ({"v_head": 12}, "DEC_E_SHAPE"),
+    ({"head_dim": 64}, "DEC_E_SHAPE"),            # GQA field on an MLA shape
+    ({"n_routed": 16}, "DEC_E_SHAPE"),            # MoE field on a dense MLA shape
+])
+def test_mla_shape_errors(over, status):
+    with pytest.raises(B.DecError) as e:
+        plan("mla_tiny", **over)
+    assert B.STATUS[e.value.status] == status
+
+
+@pytest.mark.parametrize("over", [{"top_k": 17}, {"top_k": 0}, {"expert_ffn": 12}, {"ffn": 64}])
+def test_moe_shape_errors(over):
+    with pytest.raises(B.DecError) as e:
+        plan("moe_tiny", **over)
+    assert B.STATUS[e.value.status] == "DEC_E_SHAPE"
+
+
+def test_mla_algorithmic_bytes():
+    """MLA: every weight once + latent rows [0, kv_len]; MoE: routed experts count top_k of
+    n_routed per layer."""
+    p, cfg = plan("mla_8k")
+    s = p.sizes()
+    row = (cfg["kv_lora_rank"] + cfg["qk_rope"]) * 2
+    assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+    assert s["kv_bytes"] == cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+    p, cfg = plan("moe_4k")
+    s = p.sizes()
+    per_expert = 3 * cfg["expert_ffn"] * cfg["hidden"] * 2
+    unused = cfg["n_layers"] * (cfg["n_routed"] - cfg["top_k"]) * per_expert
+    row = (cfg["kv_lora_rank"] + cfg["qk_rope"]) * 2
+    assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+
+
+def test_mla_attention_splits():
+    """Latent attention splits tile the positions, at least 64 per split where the cache
+    allows, at most one per workgroup, and the W_UV merge tasks cover every (head, block)."""
+    for name in ("mla_tiny", "mla_8k", "moe_4k"):
+        p, cfg = plan(name)
+        n1 = cfg["kv_len"] + 1
+        for layer in range(cfg["n_layers"]):
+            sp = sorted((t["unit_begin"], t["unit_end"]) for t in p.tasks()
+                        if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "MLA_ATTN")
+            S = len(sp)
+            assert S == min(256, max(1, -(-n1 // 64)))
+            assert sp[0][0] == 0 and sp[-1][1] == n1
+            assert len({t["wg"] for t in p.tasks() if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "MLA_ATTN"}) == S
+
+
+def test_moe_topk_after_router_on_one_workgroup():
+    p, cfg = plan("moe_4k")
+    tasks = p.tasks()
+    for layer in range(cfg["n_layers"]):
+        tk = [t for t in tasks if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "TOPK"]
+        assert len(tk) == 1
+        routers = [t for t in tasks if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "ROUTER"]
+        assert tk[0]["wg"] == max(t["wg"] for t in routers)
