@@ -21,11 +21,60 @@ WORKLOADS = {
     "8b_4k": "Llama-3-8B-shaped decoder (32 layers, hidden 4096, 32x128 q heads, 8 KV heads, SwiGLU 14336, "
              "vocab 128256), batch 1, one decode token over a 4096-position KV cache",
     "8b_32k": "Llama-3-8B-shaped decoder, batch 1, one decode token over a 32768-position KV cache",
+    "mla_8k": "MLA decoder stack (8 layers, hidden 7168, 16 heads, q/kv ranks 1536/512, 128+64 qk, v 128, "
+              "SwiGLU 18432), batch 1, one decode token over an 8192-position latent cache",
+    "moe_4k": "MLA + MoE decoder stack (4 layers, hidden 7168, MLA as above, 256 routed experts of 2048 + 1 "
+              "shared, sigmoid top-8), batch 1, one decode token over a 4096-position latent cache",
     "tiny": "tiny decoder (2 layers, hidden 256), batch 1, KV 128",
 }
+# Sources whose content decides the engine's memory traffic: a stored counter reading is
+# reported only while their hash matches.
+TRAFFIC_SOURCES = ["persistent_tile_scheduled_amd/csrc/engine.hip", "persistent_tile_scheduled_amd/csrc/plan_types.h",
+                   "persistent_tile_scheduled_amd/csrc/planner.cpp"]
 
 
-def cpu_baseline(cfg, w, x, kv):
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config):
+    """HBM bytes per launch from the committed counter summary of this workload
+    (profiles/dec_engine_<config>_traffic.md: a line `traffic_bytes_per_launch: N` and a line
+    `source_hash: H`), or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"dec_engine_{config}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip().strip("`")
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_hash") != source_hash() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
+
+
+def copy_calibration(nbytes, reps):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters:
+    each launch reads and writes `nbytes`."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written": nbytes,
+                      "launches": reps}), flush=True)
+
+
+def cpu_baseline(cfg, w, x, kv, eng=None):
     """The fp64 oracle, as it stands, timed on a bounded sample of the same step: layer 0 and
     the final norm + LM head; the per-token figure extrapolates layer 0 to all layers."""
     import numpy as np
@@ -49,10 +98,19 @@ def cpu_baseline(cfg, w, x, kv):
     n = cfg["kv_len"]
     xb = workloads.bf16_bits(x)
     kv0 = workloads.bf16_bits(kv[0])
-    # host copies first (not timed): the oracle's timed region starts from host bf16 arrays
+    # host copies first (not timed): the oracle's timed region starts from host bf16 arrays.
+    # Routed experts: only those layer 0 selects (the engine's choice; the oracle fetches any
+    # other it picks itself)
     for s in workloads.weight_specs(cfg):
+        if s.name.startswith("layers.0.experts."):
+            continue
         if s.name.startswith("layers.0.") or s.name in ("final_norm", "lm_head"):
             Wc(s.name)
+    if eng is not None and cfg["arch"] == "moe":
+        k = cfg["top_k"]
+        for e in eng.buffer("layers.0.topk")[:k].cpu().tolist():
+            for m in ("w_gate", "w_up", "w_down"):
+                Wc(f"layers.0.experts.{m}", int(e))
     t0 = time.perf_counter()
     xo, _ = oracle.layer(cfg, Wc, 0, oracle.widen_bf16(xb), kv0, n)
     t1 = time.perf_counter()
@@ -80,6 +138,8 @@ def main():
     ap.add_argument("--config", default="8b_4k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this engine has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -87,6 +147,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
 
     import workloads
     from persistent_tile_scheduled_amd.engine import DecodeEngine
@@ -122,7 +186,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, w, x, kv)
+        cpu = cpu_baseline(cfg, w, x, kv, eng)
 
     line = {
         "metric": METRIC,
@@ -146,7 +210,8 @@ def main():
         "kernel_us_p90": round(sorted(per)[(len(per) * 9) // 10], 2),
         "algorithmic_bytes_per_step": alg_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.config)},
+        "source_hash": source_hash(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
