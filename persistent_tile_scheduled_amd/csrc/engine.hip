@@ -313,7 +313,15 @@ __device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, 
 #ifndef DEC_NB
 #define DEC_NB 8
 #endif
-constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (16 KB per wave per batch)
+constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (NB KB per wave per batch)
+#ifndef DEC_RING_QKV
+#define DEC_RING_QKV 2
+#endif
+#ifndef DEC_RING_OPROJ
+#define DEC_RING_OPROJ 2
+#endif
+constexpr int kRingQKV = DEC_RING_QKV;      // register ring depth of the QKV tasks
+constexpr int kRingOproj = DEC_RING_OPROJ;  // register ring depth of the per-group O-projection
 
 // Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
 // columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
@@ -405,19 +413,23 @@ __device__ __forceinline__ int wave_start(int n, int w) {
 // G rows (G consecutive rows are summed into one result ys[j / G]). With `prefetch`, the
 // row map may not depend on anything this task waits for: the first two batches are issued
 // before the dependency wait.
-template <class RM, class StageF, class EpiF>
+// R is the depth of the register ring (batches of NB chunks): all R batches are in flight when
+// the wait begins. The big FFN and LM-head stages use R = 2; the small, latency-bound stages
+// of the attention block use a deeper ring, so that most or all of a workgroup's rows are
+// already loading while it waits.
+template <int R = 2, class RM, class StageF, class EpiF>  // R in [2, 4]
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
                                          int K, int G, bool prefetch, StageF&& stage, EpiF&& epi) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
   const int ja = wave_start(ng, wave) * G, jb = wave_start(ng, wave + 1) * G;
   Stream s;
-  u4 b0[NB], b1[NB];
+  u4 buf[R][NB];
   if (prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
     s.init(b.rowp, b.xoffp, ja, jb, K, lane);
-    s.load(b0);
-    s.load(b1);
+#pragma unroll
+    for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
   if (!wait_deps(A, b, t)) return false;
   stage();
@@ -425,8 +437,8 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   if (!prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
     s.init(b.rowp, b.xoffp, ja, jb, K, lane);
-    s.load(b0);
-    s.load(b1);
+#pragma unroll
+    for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
   float gacc = 0.f;
   auto emit = [&](int j, float v) {
@@ -437,11 +449,21 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     }
   };
   while (s.cj < jb) {
-    s.consume(b0, b.xs, emit);
-    s.load(b0);
+    s.consume(buf[0], b.xs, emit);
+    s.load(buf[0]);
     if (s.cj >= jb) break;
-    s.consume(b1, b.xs, emit);
-    s.load(b1);
+    s.consume(buf[1], b.xs, emit);
+    s.load(buf[1]);
+    if constexpr (R > 2) {
+      if (s.cj >= jb) break;
+      s.consume(buf[2], b.xs, emit);
+      s.load(buf[2]);
+    }
+    if constexpr (R > 3) {
+      if (s.cj >= jb) break;
+      s.consume(buf[3], b.xs, emit);
+      s.load(buf[3]);
+    }
   }
   __syncthreads();
   b.t_streamed = (uint32_t)now();
@@ -495,7 +517,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
   const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
   const RmQKV rm{wp<uint16_t>(A, L.w[LW_WQ]), wp<uint16_t>(A, L.w[LW_WK]), wp<uint16_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
   const int xin = L.act[LA_X_IN];
-  return run_gemv(
+  return run_gemv<kRingQKV>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, xin, A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
@@ -831,7 +853,7 @@ __device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const 
   const LayerDesc& L = A.layers[t.layer];
   const int r = A.nq / A.nkv, hd = A.hd, g = t.a0, K = r * hd;
   const RmCols rm{wp<uint16_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K};
-  return run_gemv(
+  return run_gemv<kRingOproj>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_merge(b, t.a4, t.a2, r, hd, pad512(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
       [&] {

@@ -26,6 +26,14 @@ namespace {
 
 constexpr int kMinPosPerSplit = 16;
 constexpr int kRowsCap = kMaxTaskRows;     // rows of one GEMV task (LDS row tables)
+#ifndef DEC_STAGE_COUNTERS
+#define DEC_STAGE_COUNTERS 8
+#endif
+constexpr int kStageCounters = DEC_STAGE_COUNTERS;  // completion counters per stage (at least one per XCD)
+#ifndef DEC_ODD_XCD_SPEED
+#define DEC_ODD_XCD_SPEED 0.92
+#endif
+constexpr double kOddXcdSpeed = DEC_ODD_XCD_SPEED;  // relative streaming speed of XCDs 1, 3, 5, 7
 constexpr int kMinPosMla = 64;             // positions per latent-attention split (at least)
 constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
@@ -58,6 +66,11 @@ struct Builder {
       : s(s_), n(n_), dev(d_), P(p_), err(e_) {}
 
   int xcd(int w) const { return w % n_xcd; }
+  // Completion counters of a stage: nsc of them, workgroup w signalling counter w % nsc (so a
+  // counter's producers share an XCD). More counters mean fewer atomic increments queued on
+  // one address when a stage's workgroups finish together; consumers poll one lane each.
+  int nsc = 8;
+  int slot(int w) const { return w % nsc; }
 
   int counter(int count) {
     int base = (int)P.counter_total.size();
@@ -109,6 +122,22 @@ struct Builder {
       for (int a = u0; a < u1; a += cap) emit(wgs[i], a, std::min(u1, a + cap));
     }
   }
+
+  // Like spread, but workgroup i's share is proportional to speed(i). Used for the long
+  // 4096-column streams (gate/up, LM head), which run measurably slower on the odd XCDs of
+  // MI355X (about 8 %, independent of which rows an XCD gets); equal finishing times shorten
+  // the wait of the stage that follows.
+  template <class F>
+  void spread_weighted(const std::vector<int>& wgs, int units, int cap, F&& emit) {
+    const int m = (int)wgs.size();
+    std::vector<double> c(m + 1, 0.0);
+    for (int i = 0; i < m; ++i) c[i + 1] = c[i] + speed(wgs[i]);
+    for (int i = 0; i < m; ++i) {
+      int u0 = (int)std::llround(units * c[i] / c[m]), u1 = (int)std::llround(units * c[i + 1] / c[m]);
+      for (int a = u0; a < u1; a += cap) emit(wgs[i], a, std::min(u1, a + cap));
+    }
+  }
+  double speed(int w) const { return (n_xcd == 8 && (xcd(w) & 1)) ? kOddXcdSpeed : 1.0; }
 
   std::vector<int> all_wgs() const {
     std::vector<int> v(n_wg);
@@ -291,30 +320,30 @@ struct Builder {
     // over groups), added into h, which holds the residual x already (written by the previous
     // layer's down tasks, or by the layer-0 init tasks)
     ++stage;
-    const int ctr_o = counter(n_xcd);
+    const int ctr_o = counter(nsc);
     for (int g = 0; g < nkv; ++g) {
       std::vector<int32_t> dg = {att + g};
       dg.insert(dg.end(), hinit_deps.begin(), hinit_deps.end());
       spread(sets[g], d, kRowsCap, [&](int w, int a, int b) {
-        add(w, T_OPROJ_G, l, a, b, dg, ctr_o + xcd(w), -1, g, 0, S[g], 0, (int)(part + (int64_t)g * smax * pstride));
+        add(w, T_OPROJ_G, l, a, b, dg, ctr_o + slot(w), -1, g, 0, S[g], 0, (int)(part + (int64_t)g * smax * pstride));
       });
     }
-    return ffn_dense(l, all_of(ctr_o, n_xcd));
+    return ffn_dense(l, all_of(ctr_o, nsc));
   }
 
   std::vector<int32_t> ffn_dense(int l, std::vector<int32_t> deps_h) {
     const int d = s.hidden, f = s.ffn;
     ++stage;
-    const int ctr_gu = counter(n_xcd);
-    spread(all_wgs(), f, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_GATEUP, l, a, b, deps_h, ctr_gu + xcd(w)); });
+    const int ctr_gu = counter(nsc);
+    spread_weighted(all_wgs(), f, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_GATEUP, l, a, b, deps_h, ctr_gu + slot(w)); });
     ++stage;
-    const int ctr_dn = counter(n_xcd);
+    const int ctr_dn = counter(nsc);
     const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
     const int hnext = (s.arch == DEC_ARCH_GQA && l + 1 < s.n_layers) ? (int)h_acc[l + 1] : -1;
     spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) {
-      add(w, T_DOWN, l, a, b, all_of(ctr_gu, n_xcd), ctr_dn + xcd(w), -1, last, hnext);
+      add(w, T_DOWN, l, a, b, all_of(ctr_gu, nsc), ctr_dn + slot(w), -1, last, hnext);
     });
-    return all_of(ctr_dn, n_xcd);
+    return all_of(ctr_dn, nsc);
   }
 
   // ---------------------------------------------------------------- MLA / MoE layer stages
@@ -342,58 +371,58 @@ struct Builder {
 
     // A: [W_DQ; W_DKV] rows from the normalised layer input
     ++stage;
-    const int ca = counter(n_xcd);
-    spread(all_wgs(), ql + KR, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + xcd(w)); });
-    auto da = all_of(ca, n_xcd);
+    const int ca = counter(nsc);
+    spread(all_wgs(), ql + KR, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + slot(w)); });
+    auto da = all_of(ca, nsc);
 
     // B: W_UQ row pairs (nope pairs, then RoPE pairs, per head); the latent-cache append
     // (which also clears the attention output that the W_UV tasks accumulate into)
     ++stage;
-    const int cb = counter(n_xcd), ckv = counter(1);
+    const int cb = counter(nsc), ckv = counter(1);
     const int UH = dn / 2 + dr / 2;
     add(n_wg - 1, T_MLA_KVAPP, l, 0, KR, da, ckv);
-    spread(all_wgs(), nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + xcd(w)); });
-    auto db = all_of(cb, n_xcd);
+    spread(all_wgs(), nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + slot(w)); });
+    auto db = all_of(cb, nsc);
 
     // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h], one (head, 64-column block) per task
     ++stage;
-    const int cabs = counter(n_xcd);
+    const int cabs = counter(nsc);
     const int nblk = nh * (kl / kMlaColBlock);
-    spread(all_wgs(), nblk, 1, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + xcd(w)); });
+    spread(all_wgs(), nblk, 1, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + slot(w)); });
 
     // latent attention: S position splits, all heads folded into one MFMA tile
     ++stage;
-    const int catt = counter(n_xcd);
+    const int catt = counter(nsc);
     const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kMinPosMla - 1) / kMinPosMla));
     const int Sp = (S + 1) & ~1;  // per-head stride of the (M, Lr) table (16-byte rows)
     const int64_t pml = act(p + "attn_ml", (int64_t)nh * Sp * 2);
     const int64_t part = act(p + "attn_partials", (int64_t)S * nh * kl);
     L.act[LA_PML] = (int)pml;
     L.act[LA_PART] = (int)part;
-    std::vector<int32_t> dat = all_of(cabs, n_xcd);
+    std::vector<int32_t> dat = all_of(cabs, nsc);
     dat.insert(dat.end(), db.begin(), db.end());
     dat.push_back(ckv);
     for (int sp = 0; sp < S; ++sp) {
       const int w = (int)((int64_t)sp * n_wg / S);
       int p0 = (int)((n + 1) * sp / S), p1 = (int)((n + 1) * (sp + 1) / S);
-      add(w, T_MLA_ATTN, l, p0, p1, dat, catt + xcd(w), -1, 0, sp, S, 0, (int)pml, (int)part);
+      add(w, T_MLA_ATTN, l, p0, p1, dat, catt + slot(w), -1, 0, sp, S, 0, (int)pml, (int)part);
     }
     // LDS: q operand + one latent chunk + P operand + softmax statistics
     mla_lds = std::max<int64_t>(mla_lds, (int64_t)NKS * 512 + (int64_t)kMlaChunk * KP / 2 + (kMlaChunk / 32) * 512 + 256);
 
     // W_UV: per (head, column block) merge the splits, multiply, add into o[h]
     ++stage;
-    const int cuv = counter(n_xcd);
+    const int cuv = counter(nsc);
     spread(all_wgs(), nblk, 1, [&](int w, int a, int b) {
-      add(w, T_MLA_UV, l, a, b, all_of(catt, n_xcd), cuv + xcd(w), -1, 0, 0, S, 0, (int)pml, (int)part);
+      add(w, T_MLA_UV, l, a, b, all_of(catt, nsc), cuv + slot(w), -1, 0, 0, S, 0, (int)pml, (int)part);
     });
     mla_lds = std::max<int64_t>(mla_lds, align_up(2LL * Sp, 256) + align_up(S, 4) / 4 * 256 + align_up(S, 64) + 8 * 64 + 64);
 
     // O projection + residual
     ++stage;
-    const int co = counter(n_xcd);
-    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) { add(w, T_OPROJ, l, a, b, all_of(cuv, n_xcd), co + xcd(w)); });
-    auto dh = all_of(co, n_xcd);
+    const int co = counter(nsc);
+    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) { add(w, T_OPROJ, l, a, b, all_of(cuv, nsc), co + slot(w)); });
+    auto dh = all_of(co, nsc);
 
     if (s.arch == DEC_ARCH_MLA) {
       L.act[LA_ACT] = (int)act(p + "ffn_act", s.ffn);
@@ -416,34 +445,34 @@ struct Builder {
 
     // E1: router rows on a few workgroups, the shared expert's gate/up on the rest
     ++stage;
-    const int cr = counter(n_xcd), cs = counter(n_xcd);
+    const int cr = counter(nsc), cs = counter(nsc);
     int nr = std::max(1, std::min(n_wg / 4, (E + 3) / 4));
     if (SF == 0) nr = n_wg;
     std::vector<int> rw, sw;
     for (int w = 0; w < n_wg; ++w) (w < nr ? rw : sw).push_back(w);
-    spread(rw, E, kRowsCap, [&](int w, int a, int b) { add(w, T_ROUTER, l, a, b, dh, cr + xcd(w)); });
-    if (SF > 0) spread(sw, SF, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_SHARED_GU, l, a, b, dh, cs + xcd(w)); });
+    spread(rw, E, kRowsCap, [&](int w, int a, int b) { add(w, T_ROUTER, l, a, b, dh, cr + slot(w)); });
+    if (SF > 0) spread(sw, SF, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_SHARED_GU, l, a, b, dh, cs + slot(w)); });
 
     // E2: top-k on one workgroup
     ++stage;
     const int ct = counter(1);
-    add(nr - 1, T_TOPK, l, 0, E, all_of(cr, n_xcd), ct);
+    add(nr - 1, T_TOPK, l, 0, E, all_of(cr, nsc), ct);
 
     // E3: routed experts' gate/up (the expert id is read from the top-k result)
     ++stage;
-    const int ce = counter(n_xcd);
-    spread(all_wgs(), K * F, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_EXPERT_GU, l, a, b, {ct}, ce + xcd(w)); });
+    const int ce = counter(nsc);
+    spread(all_wgs(), K * F, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_EXPERT_GU, l, a, b, {ct}, ce + slot(w)); });
 
     // E4: down projections of the shared and routed experts, weighted, + residual
     ++stage;
-    const int cd = counter(n_xcd);
-    std::vector<int32_t> dd = all_of(ce, n_xcd);
-    auto ds_ = all_of(cs, n_xcd);
+    const int cd = counter(nsc);
+    std::vector<int32_t> dd = all_of(ce, nsc);
+    auto ds_ = all_of(cs, nsc);
     dd.insert(dd.end(), ds_.begin(), ds_.end());
     dd.push_back(ct);
     const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
-    spread(all_wgs(), d, kRowsCap / (s.n_shared + K), [&](int w, int a, int b) { add(w, T_MOE_DOWN, l, a, b, dd, cd + xcd(w), -1, last); });
-    return all_of(cd, n_xcd);
+    spread(all_wgs(), d, kRowsCap / (s.n_shared + K), [&](int w, int a, int b) { add(w, T_MOE_DOWN, l, a, b, dd, cd + slot(w), -1, last); });
+    return all_of(cd, nsc);
   }
 
   bool run(dec_status* st) {
@@ -452,6 +481,7 @@ struct Builder {
     if (dev.n_cu < 1 || dev.n_xcd < 1 || dev.n_cu % dev.n_xcd) return fail(DEC_E_DEVICE, "bad CU/XCD counts", st);
     n_wg = dev.n_cu;
     n_xcd = dev.n_xcd;
+    nsc = (int)std::min<int64_t>(n_wg, align_up(std::max(n_xcd, kStageCounters), n_xcd));
     per_wg.assign(n_wg, {});
     P.shape = s;
     P.kv_len = n;
@@ -467,9 +497,9 @@ struct Builder {
       for (int l = 0; l < s.n_layers; ++l) P.layers[l].act[LA_H] = -1;
       for (int l = 0; l < s.n_layers; ++l) h_acc.push_back(act("layers." + std::to_string(l) + ".h", s.hidden));
       ++stage;
-      const int ci = counter(n_xcd);
-      spread(all_wgs(), s.hidden, kRowsCap, [&](int w, int a, int b) { add(w, T_HINIT, 0, a, b, {}, ci + xcd(w), -1, (int)h_acc[0]); });
-      hinit_deps = all_of(ci, n_xcd);
+      const int ci = counter(nsc);
+      spread(all_wgs(), s.hidden, kRowsCap, [&](int w, int a, int b) { add(w, T_HINIT, 0, a, b, {}, ci + slot(w), -1, (int)h_acc[0]); });
+      hinit_deps = all_of(ci, nsc);
     }
     for (int l = 0; l < s.n_layers; ++l) {
       prev = (s.arch == DEC_ARCH_GQA) ? build_gqa_layer(l, prev, x_in) : build_mla_layer(l, prev, x_in);
@@ -478,7 +508,7 @@ struct Builder {
     P.x_final = (int)x_in;
     if (s.vocab > 0) {
       ++stage;
-      spread(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
+      spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
     }
 
     // flatten per-workgroup lists, resolve dependency entries
