@@ -238,6 +238,17 @@ __device__ __forceinline__ void signal(const EngineArgs& A, int ctr) {
   if (threadIdx.x == 0 && ctr >= 0) add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
 }
 
+// After a GEMV task, whose results wave 0 stored alone: wave 0 waits for its stores and
+// increments the counter, while the other waves go straight on to the next task and issue
+// its prefetch (the next task's barriers keep the LDS hand-over in order: its input is
+// staged by wave 0, and its row results are written only after its staging barrier).
+__device__ __forceinline__ void signal_w0(const EngineArgs& A, int ctr) {
+  if (threadIdx.x < 64) {
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if (threadIdx.x == 0 && ctr >= 0) add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
+  }
+}
+
 __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
 
 __device__ __forceinline__ float block_sum(Blk& b, float v) {
@@ -467,7 +478,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   __syncthreads();
   b.t_streamed = (uint32_t)now();
-  epi();
+  if (threadIdx.x < 64) epi();  // wave 0 stores the results (see signal_w0)
   return true;
 }
 
@@ -524,7 +535,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
         const int n = A.kv_len;
         const size_t lay = (size_t)2 * A.nkv * (n + 1) * hd;  // cache elements per layer
         const rsrc_t kvr = make_rsrc(A.kv + (size_t)t.layer * lay, (uint32_t)(lay * 2));
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
           float a = b.ys[2 * i], c = b.ys[2 * i + 1];
           if (slot <= r) {  // RoPE on q and k
@@ -831,7 +842,7 @@ __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const Ta
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_ATTN], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
           const float res = xin >= 0 ? cld(b.act, (uint32_t)(xin + rr) * 4u) : bf16f(A.x[rr]);
           cst(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u, res + b.ys[i]);
@@ -858,7 +869,7 @@ __device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const 
       [&] { stage_merge(b, t.a4, t.a2, r, hd, pad512(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
       [&] {
         float* h = b.actp + L.act[LA_H] + t.u0;
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           __hip_atomic_fetch_add(h + i, b.ys[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       });
 }
@@ -878,7 +889,7 @@ __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const T
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
 }
@@ -891,7 +902,7 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
           const float y = b.ys[i];
           const float xo = cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) + y;
@@ -910,7 +921,7 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, A.x_final, nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) A.out[t.u0 + i] = b.ys[i];
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) A.out[t.u0 + i] = b.ys[i];
       });
 }
 
@@ -964,7 +975,7 @@ __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const Ta
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_X_IN], A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int r = t.u0 + i;
           const int off = r < ql ? L.act[LA_CQ] + r : L.act[LA_KVA] + (r - ql);
           cst(b.act, (uint32_t)off * 4u, b.ys[i]);
@@ -994,7 +1005,7 @@ __device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const Ta
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, h = u / uh, k = u - h * uh;
           const float a = b.ys[2 * i], c = b.ys[2 * i + 1];
           if (k < dn / 2) {
@@ -1370,7 +1381,7 @@ __device__ __forceinline__ bool task_router(const EngineArgs& A, Blk& b, const T
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) cst(b.act, (uint32_t)(L.act[LA_RLOGIT] + t.u0 + i) * 4u, b.ys[i]);
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) cst(b.act, (uint32_t)(L.act[LA_RLOGIT] + t.u0 + i) * 4u, b.ys[i]);
       });
 }
 
@@ -1383,7 +1394,7 @@ __device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, cons
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_SACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
 }
@@ -1478,7 +1489,7 @@ __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, cons
         stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps);
       },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
 }
@@ -1528,7 +1539,7 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
         __syncthreads();
       },
       [&] {
-        for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
           const float y = b.ys[i];
           const float xo = cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) + y;
@@ -1567,48 +1578,45 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   for (int ti = A.wg_begin[wg]; ti < A.wg_begin[wg + 1]; ++ti) {
     const TaskDesc t = A.tasks[ti];
     const uint32_t t0 = (uint32_t)now();
-    bool ok = true;
+    bool ok = true, gemv = true;
     int sig = t.signal;
     if constexpr (!MLA) {
       switch (t.type) {
         case T_QKV: ok = task_qkv(A, b, t); break;
         case T_ATTN:
+          gemv = false;
           ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
           break;
         case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
-        case T_HINIT: ok = task_hinit(A, b, t); break;
+        case T_HINIT: gemv = false; ok = task_hinit(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
         case T_DOWN: ok = task_down(A, b, t); break;
         case T_LMHEAD: ok = task_lmhead(A, b, t); break;
-        case T_ROUTER: ok = task_router(A, b, t); break;
-        case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
-        case T_TOPK: ok = task_topk(A, b, t); break;
-        case T_EXPERT_GU: ok = task_expert_gu(A, b, t); break;
-        case T_MOE_DOWN: ok = task_moe_down(A, b, t); break;
         default: ok = false; break;
       }
     } else {
       switch (t.type) {
         case T_MLA_A: ok = task_mla_a(A, b, t); break;
         case T_MLA_B: ok = task_mla_b(A, b, t); break;
-        case T_MLA_KVAPP: ok = task_mla_kvapp(A, b, t); break;
-        case T_MLA_ABSORB: ok = task_mla_absorb(A, b, t); break;
-        case T_MLA_ATTN: ok = task_mla_attn(A, b, t); break;
-        case T_MLA_UV: ok = task_mla_uv(A, b, t); break;
+        case T_MLA_KVAPP: gemv = false; ok = task_mla_kvapp(A, b, t); break;
+        case T_MLA_ABSORB: gemv = false; ok = task_mla_absorb(A, b, t); break;
+        case T_MLA_ATTN: gemv = false; ok = task_mla_attn(A, b, t); break;
+        case T_MLA_UV: gemv = false; ok = task_mla_uv(A, b, t); break;
         case T_OPROJ: ok = task_oproj(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
         case T_DOWN: ok = task_down(A, b, t); break;
         case T_LMHEAD: ok = task_lmhead(A, b, t); break;
         case T_ROUTER: ok = task_router(A, b, t); break;
         case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
-        case T_TOPK: ok = task_topk(A, b, t); break;
+        case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
         case T_EXPERT_GU: ok = task_expert_gu(A, b, t); break;
         case T_MOE_DOWN: ok = task_moe_down(A, b, t); break;
         default: ok = false; break;
       }
     }
     if (!ok) break;
-    signal(A, sig);
+    if (gemv) signal_w0(A, sig);
+    else signal(A, sig);
     if (threadIdx.x == 0) {
       TaskLog* lg = A.log + t.id;
       add_agent(&lg->execs, 1u);
