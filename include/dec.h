@@ -125,8 +125,10 @@ typedef struct dec_task_desc {
   int32_t aux0, aux1;             /* type-specific: group, split, head, ... */
   int32_t n_deps, dep_first;      /* counters waited on (see dec_plan_deps) */
   int32_t signal;                 /* counter incremented on completion (-1: none) */
-  int32_t signal2;                /* second counter (ticket-merge tasks: merged counter) */
-  int32_t reserved0;
+  int32_t signal2;                /* second counter (-1: none) */
+  int32_t aux2;                   /* type-specific: split count; for the routed-expert tasks the
+                                     number of leading dependencies (the router) that decide
+                                     their rows */
 } dec_task_desc;
 
 /* A named fp32 (or i32) buffer inside the workspace holding an intermediate of the last

@@ -213,7 +213,7 @@ dec_status dec_plan_tasks(const dec_plan* plan, dec_task_desc* buf, int64_t cap,
     d.dep_first = t.dep_first;
     d.signal = t.signal;
     d.signal2 = t.signal2;
-    d.reserved0 = t.a3;  // ticket-merge log id for attention splits
+    d.aux2 = t.a2;
   }
   return DEC_OK;
 }

@@ -182,22 +182,24 @@ struct Blk {
 // Wait until every dependency counter of `t` has reached this step's target. Wave 0 polls
 // (one lane per counter); the other waves wait at the barrier with their loads in flight.
 // Returns false when the step is being aborted (watchdog).
-__device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+__device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const TaskDesc& t, int d0 = 0, int d1 = -1) {
+  if (d1 < 0) d1 = t.dep_count;
+  const int nd = d1 - d0;  // waits on dependencies [d0, d1) of the task
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int status = 0;
-    if (t.dep_count > 0) {
+    if (nd > 0) {
       const uint32_t* cp = A.ctl;  // any valid address for idle lanes
       uint32_t target = 0;
-      if (lane < t.dep_count) {
-        const DepEntry d = A.deps[t.dep_first + lane];
+      if (lane < nd) {
+        const DepEntry d = A.deps[t.dep_first + d0 + lane];
         cp = A.counters + (size_t)d.counter * kCounterStride;
         target = (b.epoch + 1u) * d.per_step;
       }
       const uint64_t t0 = now();
       uint32_t spins = 0;
       while (true) {
-        const bool ok = (lane >= t.dep_count) || ((int32_t)(ld_agent(cp) - target) >= 0);
+        const bool ok = (lane >= nd) || ((int32_t)(ld_agent(cp) - target) >= 0);
         if (__all(ok)) break;
         const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
         if (late || (++spins & 7u) == 0u) {
@@ -428,21 +430,36 @@ __device__ __forceinline__ int wave_start(int n, int w) {
 // the wait begins. The big FFN and LM-head stages use R = 2; the small, latency-bound stages
 // of the attention block use a deeper ring, so that most or all of a workgroup's rows are
 // already loading while it waits.
-template <int R = 2, class RM, class StageF, class EpiF>  // R in [2, 4]
+// `pre_deps` > 0: the row map depends on the task's first pre_deps dependencies (the MoE
+// expert choice). The task waits for those, runs `pre` (wave 0 puts what the row map reads
+// into LDS), then issues its prefetch (such a task passes prefetch = true) before waiting
+// for the rest. `prefetch` must be a compile-time constant at every call: with loads issued
+// on two alternative paths the compiler cannot count the loads in flight, and the stream
+// loop would wait for all of them before every batch.
+struct NoPre {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <int R = 2, class RM, class StageF, class EpiF, class PreF = NoPre>  // R in [2, 4]
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
-                                         int K, int G, bool prefetch, StageF&& stage, EpiF&& epi) {
+                                         int K, int G, bool prefetch, StageF&& stage, EpiF&& epi, int pre_deps = 0,
+                                         PreF&& pre = PreF{}) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
   const int ja = wave_start(ng, wave) * G, jb = wave_start(ng, wave + 1) * G;
   Stream s;
   u4 buf[R][NB];
+  if (pre_deps > 0) {
+    if (!wait_deps(A, b, t, 0, pre_deps)) return false;
+    pre();
+    __syncthreads();
+  }
   if (prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
     s.init(b.rowp, b.xoffp, ja, jb, K, lane);
 #pragma unroll
     for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
-  if (!wait_deps(A, b, t)) return false;
+  if (!wait_deps(A, b, t, pre_deps)) return false;
   stage();
   b.t_staged = (uint32_t)now();
   if (!prefetch) {
@@ -1422,19 +1439,31 @@ __device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const Tas
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const float s = 1.0f / (1.0f + expf(-z[e]));
-    sg[e] = s;
-    z[e] = s + bias[e];
+  for (int e = threadIdx.x; e < ((E + 3) & ~3); e += kThreads) {
+    if (e < E) {
+      const float s = 1.0f / (1.0f + expf(-z[e]));
+      sg[e] = s;
+      z[e] = s + bias[e];
+    } else {
+      z[e] = -INFINITY;  // padding: never ranks above a real expert
+    }
   }
   __syncthreads();
+  // z is padded with -inf to a multiple of 4, so the comparison loop reads 4 scores per LDS
+  // access; the loads of an unrolled block are independent
+  const int E4 = (E + 3) & ~3;
   for (int e = threadIdx.x; e < E; e += kThreads) {
     const float ze = z[e];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const float zf = z[f];
-      rank += (zf > ze || (zf == ze && f < e)) ? 1 : 0;
+    int r0 = 0, r1 = 0;
+#pragma unroll 8
+    for (int f = 0; f < E4; f += 4) {
+      const f4 v = *reinterpret_cast<const f4*>(z + f);
+      r0 += (v.x > ze || (v.x == ze && f < e)) ? 1 : 0;
+      r1 += (v.y > ze || (v.y == ze && f + 1 < e)) ? 1 : 0;
+      r0 += (v.z > ze || (v.z == ze && f + 2 < e)) ? 1 : 0;
+      r1 += (v.w > ze || (v.w == ze && f + 3 < e)) ? 1 : 0;
     }
+    const int rank = r0 + r1;
     if (rank < K) {
       ids[rank] = e;
       sel[rank] = sg[e];
@@ -1453,7 +1482,7 @@ __device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const Tas
 }
 
 // Routed experts' gate/up: unit u = (slot k, row i) -> rows i of W_gate[e_k], W_up[e_k];
-// the expert ids are read after the wait, so nothing is prefetched.
+// the expert ids are read once the top-k task has signalled, then the rows are prefetched.
 struct RmExpertGU {
   const uint16_t *Wg, *Wu;
   const int* ids;  // LDS
@@ -1483,15 +1512,13 @@ __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, cons
   int* ids = reinterpret_cast<int*>(b.scr);
   const RmExpertGU rm{wp<uint16_t>(A, L.w[LW_EGATE]), wp<uint16_t>(A, L.w[LW_EUP]), ids, K, F, t.u0};
   return run_gemv(
-      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, false,
-      [&] {
-        stage_ids(A, L, b, ids);
-        stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps);
-      },
+      A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
+      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
-      });
+      },
+      t.a2, [&] { stage_ids(A, L, b, ids); });
 }
 
 // Down projections: output row r sums G = ns + top_k segments of eff columns: segment s < ns
@@ -1517,9 +1544,8 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
   float* wk = b.scr + 64;
   const RmMoeDown rm{wp<uint16_t>(A, L.w[LW_SDOWN]), wp<uint16_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0};
   return run_gemv(
-      A, b, t, rm, G * (t.u1 - t.u0), F, G, false,
+      A, b, t, rm, G * (t.u1 - t.u0), F, G, true,
       [&] {
-        stage_ids(A, L, b, ids);
         if (threadIdx.x < 64) {
           for (int k = threadIdx.x; k < Kt; k += 64) wk[k] = cld(b.act, (uint32_t)(L.act[LA_TOPK] + Kt + k) * 4u);
           for (int sg = 0; sg < G; ++sg) {
@@ -1547,7 +1573,8 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
           cst(b.act, (uint32_t)(L.act[LA_X_OUT] + rr) * 4u, xo);
           if (t.a0) A.out[rr] = xo;
         }
-      });
+      },
+      t.a2, [&] { stage_ids(A, L, b, ids); });
 }
 
 }  // namespace

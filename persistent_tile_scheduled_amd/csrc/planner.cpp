@@ -380,8 +380,12 @@ struct Builder {
     ++stage;
     const int cb = counter(nsc), ckv = counter(1);
     const int UH = dn / 2 + dr / 2;
+    // the append runs alone on the last workgroup, so that no W_UQ task (which every absorb
+    // task waits for) queues behind it
     add(n_wg - 1, T_MLA_KVAPP, l, 0, KR, da, ckv);
-    spread(all_wgs(), nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + slot(w)); });
+    std::vector<int> bw = all_wgs();
+    if (n_wg > 1) bw.pop_back();
+    spread(bw, nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + slot(w)); });
     auto db = all_of(cb, nsc);
 
     // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h], one (head, 64-column block) per task
@@ -461,17 +465,19 @@ struct Builder {
     // E3: routed experts' gate/up (the expert id is read from the top-k result)
     ++stage;
     const int ce = counter(nsc);
-    spread(all_wgs(), K * F, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_EXPERT_GU, l, a, b, {ct}, ce + slot(w)); });
+    // a2 = 1: the first dependency (the top-k) decides the rows, which are prefetched before
+    // the rest of the wait
+    spread(all_wgs(), K * F, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_EXPERT_GU, l, a, b, {ct}, ce + slot(w), -1, 0, 0, 1); });
 
     // E4: down projections of the shared and routed experts, weighted, + residual
     ++stage;
     const int cd = counter(nsc);
-    std::vector<int32_t> dd = all_of(ce, nsc);
-    auto ds_ = all_of(cs, nsc);
+    std::vector<int32_t> dd = {ct};  // first: the top-k, which decides the rows (a2 = 1)
+    auto de_ = all_of(ce, nsc), ds_ = all_of(cs, nsc);
+    dd.insert(dd.end(), de_.begin(), de_.end());
     dd.insert(dd.end(), ds_.begin(), ds_.end());
-    dd.push_back(ct);
     const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
-    spread(all_wgs(), d, kRowsCap / (s.n_shared + K), [&](int w, int a, int b) { add(w, T_MOE_DOWN, l, a, b, dd, cd + slot(w), -1, last); });
+    spread(all_wgs(), d, kRowsCap / (s.n_shared + K), [&](int w, int a, int b) { add(w, T_MOE_DOWN, l, a, b, dd, cd + slot(w), -1, last, 0, 1); });
     return all_of(cd, nsc);
   }
 

@@ -327,3 +327,19 @@ def test_moe_topk_after_router_on_one_workgroup():
         assert len(tk) == 1
         routers = [t for t in tasks if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "ROUTER"]
         assert tk[0]["wg"] == max(t["wg"] for t in routers)
+        # the routed-expert tasks wait for the top-k first (aux2 = 1 leading dependency), so
+        # they can prefetch their rows before the rest of their wait
+        deps = p.deps()
+        for t in tasks:
+            if t["layer"] == layer and B.TASK_TYPES[t["type"]] in ("EXPERT_GU", "MOE_DOWN"):
+                assert t["aux2"] == 1 and deps[t["dep_first"]][0] == tk[0]["signal"], t
+
+
+def test_mla_append_runs_alone():
+    """The latent-cache append's workgroup has no W_UQ rows in the same stage."""
+    p, cfg = plan("mla_8k")
+    for layer in range(cfg["n_layers"]):
+        app = [t for t in p.tasks() if t["layer"] == layer and B.TASK_TYPES[t["type"]] == "MLA_KVAPP"]
+        assert len(app) == 1
+        assert not any(t["wg"] == app[0]["wg"] and t["layer"] == layer and B.TASK_TYPES[t["type"]] == "MLA_B"
+                       for t in p.tasks())
