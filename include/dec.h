@@ -129,6 +129,9 @@ typedef struct dec_task_desc {
   int32_t aux2;                   /* type-specific: split count; for the routed-expert tasks the
                                      number of leading dependencies (the router) that decide
                                      their rows */
+  int32_t kv_staged;              /* GQA QKV and attention tasks: cached K/V rows of the
+                                     attention split that the workgroup's QKV task copies into
+                                     LDS for the attention task right after it (0: none) */
 } dec_task_desc;
 
 /* A named fp32 (or i32) buffer inside the workspace holding an intermediate of the last

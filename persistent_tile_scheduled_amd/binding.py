@@ -58,7 +58,7 @@ class Sizes(C.Structure):
 class TaskDescC(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("id", "type", "layer", "stage", "wg", "xcd", "list_pos", "unit_begin",
                                          "unit_end", "aux0", "aux1", "n_deps", "dep_first", "signal", "signal2",
-                                         "aux2")]
+                                         "aux2", "kv_staged")]
 
 
 class BufferDesc(C.Structure):

@@ -214,6 +214,7 @@ dec_status dec_plan_tasks(const dec_plan* plan, dec_task_desc* buf, int64_t cap,
     d.signal = t.signal;
     d.signal2 = t.signal2;
     d.aux2 = t.a2;
+    d.kv_staged = (t.type == dec::T_QKV) ? t.a5 : (t.type == dec::T_ATTN) ? t.a3 : 0;
   }
   return DEC_OK;
 }

@@ -37,12 +37,13 @@ __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v <<
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950's v_cvt_pk_bf16_f32
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values -> one bf16 pair (a in the low half), one instruction
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const bf2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // wave-uniform value (lets the compiler keep it in SGPRs and branch on it with scalar code)
@@ -436,13 +437,16 @@ __device__ __forceinline__ int wave_start(int n, int w) {
 // for the rest. `prefetch` must be a compile-time constant at every call: with loads issued
 // on two alternative paths the compiler cannot count the loads in flight, and the stream
 // loop would wait for all of them before every batch.
+// `issue` runs on every wave once the input is staged, before the stream: it may start loads
+// of data the next task needs. (Issued earlier, such loads would sit in the compute unit's
+// memory queue ahead of the staging loads, which wait for the dependency.)
 struct NoPre {
   __device__ __forceinline__ void operator()() const {}
 };
-template <int R = 2, class RM, class StageF, class EpiF, class PreF = NoPre>  // R in [2, 4]
+template <int R = 2, class RM, class StageF, class EpiF, class PreF = NoPre, class IssueF = NoPre>  // R in [2, 4]
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
                                          int K, int G, bool prefetch, StageF&& stage, EpiF&& epi, int pre_deps = 0,
-                                         PreF&& pre = PreF{}) {
+                                         PreF&& pre = PreF{}, IssueF&& issue = IssueF{}) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
   const int ja = wave_start(ng, wave) * G, jb = wave_start(ng, wave + 1) * G;
@@ -462,6 +466,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   if (!wait_deps(A, b, t, pre_deps)) return false;
   stage();
   b.t_staged = (uint32_t)now();
+  issue();
   if (!prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
     s.init(b.rowp, b.xoffp, ja, jb, K, lane);
@@ -540,11 +545,39 @@ struct RmQKV {
 // ------------------------------------------------------------------ GQA tasks
 
 
+// With KV (a5 > 0 rows): the streaming waves also put cached K/V rows [a4, a4 + a5) of KV
+// group a3 -- the attention split this workgroup runs next -- into LDS, behind their row
+// prefetch. Every streaming wave issues exactly kKvStageDma 1-KB chunks (indices past the
+// end repeat the last chunk; lanes past a region's end re-read its last 16 bytes), so the
+// number of loads in flight is the same on every path through the stream loop.
+template <bool KV>
 __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
   const RmQKV rm{wp<uint16_t>(A, L.w[LW_WQ]), wp<uint16_t>(A, L.w[LW_WK]), wp<uint16_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
   const int xin = L.act[LA_X_IN];
+  auto issue = [&] {
+    if constexpr (KV) {
+      const int wave = wave_id(), lane = threadIdx.x & 63;
+      if (wave == 0) return;  // wave 0 stages the input vector: no loads ahead of it
+      const int hw = hd / 2, nfl = t.a5 * hw, nch = (nfl + 255) / 256;
+      const size_t n1 = (size_t)A.kv_len + 1;
+      const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + t.a3) * n1 * hd) + (size_t)t.a4 * hw;
+      const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + t.a3) * n1 * hd) + (size_t)t.a4 * hw;
+      float* kd = b.xs + kv_stage_k_off(A.hidden);
+      float* vd = b.scr + kv_stage_v_off(hd);
+#pragma unroll
+      for (int k = 0; k < kKvStageDma; ++k) {
+        int c = (wave - 1) + (kWaves - 1) * k;
+        c = c < 2 * nch ? c : 2 * nch - 1;
+        const bool isv = c >= nch;
+        const int cc = isv ? c - nch : c;
+        int f = cc * 256 + lane * 4;
+        f = f < nfl ? f : nfl - 4;
+        __builtin_amdgcn_global_load_lds((gvp)((isv ? vs : ks) + f), (lvp)((isv ? vd : kd) + cc * 256), 16, 0, 0);
+      }
+    }
+  };
   return run_gemv<kRingQKV>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, xin, A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
@@ -575,7 +608,8 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
             cst16(kvr, (row + k + hh) * 2u, f2bf(c));
           }
         }
-      });
+      },
+      0, NoPre{}, issue);
 }
 
 // Merge S split partials (m, l, acc[hd]) of H heads into xs[h*hd + d] =
@@ -632,10 +666,10 @@ __device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H,
 // Split-K attention of one KV group over positions [u0, u1): the group's R query heads share
 // every K/V load. A group of LPP = hd/8 lanes holds one position's row (8 dims per lane);
 // one wave instruction covers 64/LPP consecutive positions. Online softmax in base 2 per
-// head; partials are merged across lane groups, waves, and then -- by whichever split task
-// arrives last at the group's ticket -- across splits. The cached positions of the first two
-// blocks are loaded before the dependency wait; a block holding the new position (slot
-// kv_len, written by this step's QKV tasks) is loaded again after it.
+// head; partials are merged across the lane groups of a wave (cross-lane exchanges), then
+// across waves (LDS); the O-projection tasks merge the splits. The cached positions of the
+// first two blocks are loaded before the dependency wait; a block holding the new position
+// (slot kv_len, written by this step's QKV tasks) is loaded again after it.
 template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   constexpr int GPW = 64 / LPP, NP = 3, PER_BLK = NP * GPW;
@@ -771,58 +805,64 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     }
   }
   const uint32_t t_mid = (uint32_t)now();
-  // every lane group writes its partial to LDS: slot = wave * GPW + grp, [slot][h][ps] with
-  // ps = hd + 4 (m, l, 2 pad, acc[hd])
-  constexpr int NS = kWaves * GPW;
-  const int ps = hd + 4;
-  float* gp = b.scr + (size_t)(wave * GPW + grp) * r * ps;
+  // merge the wave's lane groups (the same dims of different positions) with cross-lane
+  // exchanges: partials (m, l, acc) of lanes L and L ^ X combine as
+  // M = max, l = l e^(m - M) + l' e^(m' - M), acc likewise (base 2); afterwards every lane
+  // group holds the wave's partial
+#pragma unroll 1
+  for (int X = LPP; X < 64; X <<= 1) {
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    if (h >= r) continue;
-    if (sub == 0) {
-      gp[h * ps] = m[h];
-      gp[h * ps + 1] = l[h];
+    for (int h = 0; h < R; ++h) {
+      if (h >= r) continue;
+      const float om = __shfl_xor(m[h], X, 64), ol = __shfl_xor(l[h], X, 64);
+      const float M = fmaxf(m[h], om);
+      const float ca = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - M);
+      const float cb = (om == -INFINITY) ? 0.f : exp2f(om - M);
+      l[h] = l[h] * ca + ol * cb;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] = acc[h][d] * ca + __shfl_xor(acc[h][d], X, 64) * cb;
+      m[h] = M;
     }
+  }
+  // lane group 0 of each wave writes the wave's partial: slot = wave, [slot][R][ps] with
+  // ps = hd + 4 (m, l, 2 pad, acc[hd]); the compile-time slot stride keeps the merge's LDS
+  // addresses in instruction offsets
+  constexpr int NS = kWaves, ps = hd + 4, SS = R * ps;
+  if (grp == 0) {
+    float* gp = b.scr + wave * SS;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) gp[h * ps + 4 + sub * 8 + d] = acc[h][d];
+    for (int h = 0; h < R; ++h) {
+      if (h >= r) continue;
+      if (sub == 0) {
+        gp[h * ps] = m[h];
+        gp[h * ps + 1] = l[h];
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) gp[h * ps + 4 + sub * 8 + d] = acc[h][d];
+    }
   }
   __syncthreads();
   const uint32_t t_lanes = (uint32_t)now();
-  // wave h: merge weights of head h over the NS slots (one slot per lane)
-  float* wts = b.scr + (size_t)NS * r * ps;  // [NS][r], then M[r], den[r]
-  if (wave < r) {
-    const int h = wave;
-    float M = -INFINITY;
-    for (int sl = lane; sl < NS; sl += 64) M = fmaxf(M, b.scr[((size_t)sl * r + h) * ps]);
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
-    float dl = 0.f;
-    for (int sl = lane; sl < NS; sl += 64) {
-      const float ms = b.scr[((size_t)sl * r + h) * ps];
-      const float e = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      wts[sl * r + h] = e;
-      dl += e * b.scr[((size_t)sl * r + h) * ps + 1];
-    }
-    const float den = wave_sum(dl);
-    if (lane == 0) {
-      wts[NS * r + h] = M;
-      wts[NS * r + r + h] = den;
-    }
-  }
-  __syncthreads();
-  // workgroup partial (M, den, sum of weighted acc) -> LDS (xs), then wave 0 stores it
+  // workgroup partial (M, den, sum of weighted acc) -> LDS (xs), then wave 0 stores it; each
+  // thread recomputes its head's merge weights over the NS wave slots
+#pragma unroll 1
   for (int i = threadIdx.x; i < r * hd; i += kThreads) {
     const int h = i / hd, d = i - h * hd;
-    float v0 = 0.f, v1 = 0.f;
-#pragma unroll 4
-    for (int sl = 0; sl < NS; sl += 2) {
-      v0 = fmaf(wts[sl * r + h], b.scr[((size_t)sl * r + h) * ps + 4 + d], v0);
-      v1 = fmaf(wts[(sl + 1) * r + h], b.scr[((size_t)(sl + 1) * r + h) * ps + 4 + d], v1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) M = fmaxf(M, b.scr[sl * SS + h * ps]);
+    float v = 0.f, den = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const float ms = b.scr[sl * SS + h * ps];
+      const float e = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      v = fmaf(e, b.scr[sl * SS + h * ps + 4 + d], v);
+      den = fmaf(e, b.scr[sl * SS + h * ps + 1], den);
     }
-    b.xs[h * ps + 4 + d] = v0 + v1;
+    b.xs[h * ps + 4 + d] = v;
     if (d == 0) {
-      b.xs[h * ps] = wts[NS * r + h];
-      b.xs[h * ps + 1] = wts[NS * r + r + h];
+      b.xs[h * ps] = M;
+      b.xs[h * ps + 1] = den;
       b.xs[h * ps + 2] = 0.f;
       b.xs[h * ps + 3] = 0.f;
     }
@@ -959,6 +999,183 @@ __device__ __forceinline__ f4 mfma_bf16(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ uint32_t bf_pair(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// fp32 x as a bf16 pair hi + lo (hi = x rounded, lo = the rest rounded): about 16 mantissa
+// bits of x, enough for operands whose other side is exact bf16
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(x0, x1);
+  lo = pk_bf16(x0 - bf_lo(hi), x1 - bf_hi(hi));
+}
+// eight values (a, then b) times s as the hi and lo halves of one bf16 MFMA operand
+__device__ __forceinline__ void split_bf16x8(f4 a, f4 b, float s, u4& hi, u4& lo) {
+  uint32_t h[4], l[4];
+  split_bf16(a.x * s, a.y * s, h[0], l[0]);
+  split_bf16(a.z * s, a.w * s, h[1], l[1]);
+  split_bf16(b.x * s, b.y * s, h[2], l[2]);
+  split_bf16(b.z * s, b.w * s, h[3], l[3]);
+  hi = u4{h[0], h[1], h[2], h[3]};
+  lo = u4{l[0], l[1], l[2], l[3]};
+}
+
+// GQA attention of one KV group over a split whose K/V rows are in LDS -- the cached rows
+// copied by the workgroup's QKV task, the new position (when the split holds it) copied in
+// by wave 0 after the dependency wait -- on the matrix cores. Each wave takes 16-position
+// tiles of the split in turn and keeps a flash-style running softmax per head:
+//   scores S = K q~^T (bf16 MFMA 16x16x32): rows = the tile's positions, columns = the group's
+//     r <= 4 query heads (the rest zero), q~ = q * scale * log2(e) as hi + lo bf16 operands,
+//     K exact;
+//   m = running max, P = 2^(S - m), l = running sum, O rescaled by 2^(m_old - m);
+//   O += P V (bf16 MFMA 16x16x16): the score tile's registers are, element for element, the
+//     A operand (rows = heads, k = positions), P as hi + lo parts; V gathered from its rows.
+// The eight waves' (m, l, O) are then merged through LDS into the split partial
+// (m, l, 0, 0, unnormalised o[hd]) per head -- the record the lane-group path writes -- which
+// wave 0 alone stores (the task signals like a GEMV). Positions past the split read its last
+// row (finite values, probability 0).
+typedef short s4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4 mfma_bf16_k16(uint2 a, uint2 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
+}
+template <int HD>
+__device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  constexpr int NKS = HD / 32, NCT = HD / 16, ps = HD + 4, SS = 4 * ps;
+  const LayerDesc& L = A.layers[t.layer];
+  const int r = A.nq / A.nkv, g = t.a0;
+  const int p0 = t.u0, np = t.u1 - t.u0, c = t.a3;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // keeps lane-derived LDS addresses inside the task (not hoisted and spilled)
+  const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden));  // [np][HD]
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(b.scr + kv_stage_v_off(HD));       // [np][HD]
+  // this wave's LDS DMA of the staged rows (issued during the QKV task) has landed; the
+  // barrier in the wait publishes it to the other waves
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  if (!wait_deps(A, b, t)) return false;
+  // every wave loads q~ in B-operand order itself: lane L of k-step ks holds head L % 16,
+  // dims 32 ks + 8 (L / 16) + e (zero past r)
+  f4 qa[NKS], qb[NKS];
+  const uint32_t qo = (uint32_t)(L.act[LA_Q] + (g * r + (hl < r ? hl : 0)) * HD + 8 * q4) * 4u;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qa[ks] = cld4(b.act, qo + ks * 128u);
+    qb[ks] = cld4(b.act, qo + ks * 128u + 16u);
+  }
+  if (wave == 0 && c < np && lane < HD / 8) {  // row c: the new position, written by this step's QKV tasks
+    const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
+    const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
+    const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
+    __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
+    __builtin_amdgcn_global_load_lds((gvp)(vb + off), (lvp)(Vs + (size_t)c * HD), 16, 0, kSC1);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  u4 qh[NKS], ql[NKS];
+  const float sc = (hl < r) ? A.attn_scale_log2 : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) split_bf16x8(qa[ks], qb[ks], sc, qh[ks], ql[ks]);
+  __syncthreads();
+
+  // lane: head hl of the running (m, l); O rows = heads 4 q4 + i, column 16 ct + hl
+  float m = -INFINITY, l = 0.f;
+  f4 o[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) o[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  const int ntile = (np + 15) >> 4;
+  for (int tile = wave; tile < ntile; tile += kWaves) {
+    int pos = 16 * tile + hl;
+    pos = pos < np ? pos : np - 1;
+    const uint16_t* arow = Ks + (size_t)pos * HD + 8 * q4;
+    f4 dh = f4{0.f, 0.f, 0.f, 0.f}, dl = dh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const u4 a = *reinterpret_cast<const u4*>(arow + 32 * ks);
+      dh = mfma_bf16(a, qh[ks], dh);
+      dl = mfma_bf16(a, ql[ks], dl);
+    }
+    const f4 d = dh + dl;  // S[position 16 tile + 4 q4 + i][head hl]
+    const int pq = 16 * tile + 4 * q4;
+    float sv[4], mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = (pq + i < np && hl < r) ? d[i] : -INFINITY;
+      mt = fmaxf(mt, sv[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);  // -inf only for heads past r
+    const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
+    float pv[4], ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+      ls += pv[i];
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * al + ls;
+    m = mn;
+    // rescale O rows (heads 0..3 live in lanes q4 = 0; lane i holds head i's factor)
+    const int alb = __float_as_int(al);
+    const f4 a4 = f4{__int_as_float(__builtin_amdgcn_readlane(alb, 0)), __int_as_float(__builtin_amdgcn_readlane(alb, 1)),
+                     __int_as_float(__builtin_amdgcn_readlane(alb, 2)), __int_as_float(__builtin_amdgcn_readlane(alb, 3))};
+    uint2 ph, plo;
+    {
+      uint32_t h0, h1, l0, l1;
+      split_bf16(pv[0], pv[1], h0, l0);
+      split_bf16(pv[2], pv[3], h1, l1);
+      ph = uint2{h0, h1};
+      plo = uint2{l0, l1};
+    }
+    const uint16_t* vrow = Vs + hl;
+    int vp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vp[i] = (pq + i < np ? pq + i : np - 1) * HD;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint16_t* vc = vrow + 16 * ct;
+      const uint2 bv = uint2{bf_pair(vc[vp[0]], vc[vp[1]]), bf_pair(vc[vp[2]], vc[vp[3]])};
+      o[ct] *= a4;
+      o[ct] = mfma_bf16_k16(ph, bv, o[ct]);
+      o[ct] = mfma_bf16_k16(plo, bv, o[ct]);
+    }
+  }
+  // this wave's (m, l, O) -> slot `wave`: [wave][head < 4][m, l, 0, 0, o[HD]]
+  float* slot = b.scr + wave * SS;
+  if (q4 == 0 && hl < r) {
+    slot[hl * ps] = m;
+    slot[hl * ps + 1] = l;
+  }
+  if (q4 == 0) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < r) slot[i * ps + 4 + 16 * ct + hl] = o[ct][i];
+  }
+  __syncthreads();
+  // merge the waves: xs[h * ps] = (M, sum_w e_w l_w, 0, 0, sum_w e_w O_w), e_w = 2^(m_w - M)
+  for (int i = threadIdx.x; i < r * HD; i += kThreads) {
+    const int h = i / HD, d = i - h * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, b.scr[w * SS + h * ps]);
+    float v = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = b.scr[w * SS + h * ps];
+      const float e = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      v = fmaf(e, b.scr[w * SS + h * ps + 4 + d], v);
+      den = fmaf(e, b.scr[w * SS + h * ps + 1], den);
+    }
+    b.xs[h * ps + 4 + d] = v;
+    if (d == 0) *reinterpret_cast<f4*>(b.xs + h * ps) = f4{M, den, 0.f, 0.f};
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) A.log[t.id].t_mid = (uint32_t)now();
+  if (threadIdx.x < 64) {  // wave 0 stores the partial (see signal_w0)
+    const uint32_t gpart = (uint32_t)(t.a4 + t.a1 * r * ps);
+    for (int i = threadIdx.x * 4; i < r * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
+  }
+  return true;
+}
 
 // The scaled query q~ = [q_abs | q_rope] * softmax scale * log2(e), as the B operand of the
 // score MFMA (k = latent dimension, n = head): lane L of k-step ks holds k = 32 ks + 8 (L/16)
@@ -1609,10 +1826,19 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
     int sig = t.signal;
     if constexpr (!MLA) {
       switch (t.type) {
-        case T_QKV: ok = task_qkv(A, b, t); break;
+        case T_QKV: ok = t.a5 > 0 ? task_qkv<true>(A, b, t) : task_qkv<false>(A, b, t); break;
         case T_ATTN:
           gemv = false;
-          ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
+          if (t.a3 > 0) {
+            gemv = true;  // wave 0 alone stores the partial
+            switch (A.hd) {
+              case 32: ok = task_attn_mfma<32>(A, b, t); break;
+              case 64: ok = task_attn_mfma<64>(A, b, t); break;
+              case 128: ok = task_attn_mfma<128>(A, b, t); break;
+              default: ok = task_attn_mfma<256>(A, b, t); break;
+            }
+          }
+          else ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
           break;
         case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
         case T_HINIT: gemv = false; ok = task_hinit(A, b, t); break;

@@ -21,13 +21,21 @@ constexpr int kLdsMin = 96 * 1024;     // > half a CU's LDS: forces one workgrou
 constexpr int kMlaHeads = 16;          // query heads folded into one MFMA tile
 constexpr int kMlaChunk = 64;          // positions per LDS-resident latent chunk
 constexpr int kMlaColBlock = 64;       // latent columns per absorb / W_UV task
+// GQA: a workgroup's QKV task can put the cached K/V rows of the attention split that
+// follows it into LDS (issued by the streaming waves with their row prefetch, ahead of the
+// dependency wait). Each streaming wave issues kKvStageDma 1-KB LDS DMA chunks (K and V
+// together). K rows go after the staged hidden vector in xs, V rows after the attention merge
+// slots in the scratch region; both offsets are in floats.
+constexpr int kKvStageDma = 12;
+constexpr int kv_stage_k_off(int hidden) { return (hidden + kChunkCols - 1) / kChunkCols * kChunkCols; }
+constexpr int kv_stage_v_off(int hd) { return kWaves * 4 * (hd + 4) + 64; }
 
 // Task types. Every type runs the same five phases: issue loads of its static operand
 // (weights, cached KV) -> wait on its dependency counters -> stage its dynamic input
 // (activations) in LDS -> compute while streaming -> store and signal.
 enum TaskType : int32_t {
   T_QKV = 1,         // GQA: attention RMSNorm + W_q/W_k/W_v row pairs + RoPE + KV append
-  T_ATTN = 2,        // GQA: split-K attention partial over a position range + ticket merge
+  T_ATTN = 2,        // GQA: split-K attention partial over a position range
   T_OPROJ = 3,       // W_o rows + residual (GQA and MLA)
   T_GATEUP = 4,      // FFN RMSNorm + W_gate/W_up rows + SwiGLU
   T_DOWN = 5,        // W_down rows + residual

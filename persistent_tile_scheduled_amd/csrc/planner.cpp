@@ -263,6 +263,55 @@ struct Builder {
     }
   }
 
+  // An attention split whose workgroup runs the same layer's QKV task just before it gets
+  // its cached K/V rows staged into LDS by that task (QKV: a3 = group, a4 = first position,
+  // a5 = rows; attention: a3 = rows staged). Only where both LDS regions are already there
+  // and the rows fit the fixed DMA count; the split's other rows (at most the new position)
+  // are loaded after the dependency wait.
+  // The regions grow the LDS plan when the whole plan still fits the device; otherwise only
+  // splits that fit the regions other stages already need are staged.
+  void stage_attention_kv() {
+    const int hd = s.head_dim;
+    const int64_t koff = kv_stage_k_off(s.hidden), voff = kv_stage_v_off(hd);
+    auto candidate = [&](const TaskDesc& q, const TaskDesc& a) -> int64_t {  // LDS floats per region, or 0
+      if (a.type != T_ATTN || q.type != T_QKV || q.layer != a.layer) return 0;
+      const int64_t cnt = std::min<int64_t>(a.u1, n) - a.u0;
+      if (cnt <= 0 || a.u1 - a.u0 - cnt > 1) return 0;
+      if (2 * ((cnt * hd / 2 + 255) / 256) > (int64_t)(kWaves - 1) * kKvStageDma) return 0;
+      // the matrix-core attention merges its waves below the V rows (kWaves x 4 x (hd + 4)
+      // floats, the region's offset) and assembles the partial (r x (hd + 4)) below the K rows
+      const int64_t r = s.n_q_heads / s.n_kv_heads;
+      if (r * (hd + 4) > koff) return 0;
+      return align_up((cnt + 1) * hd / 2, 256);  // + the new row; DMA granularity
+    };
+    int64_t need = 0;
+    for (int w = 0; w < n_wg; ++w)
+      for (size_t i = 1; i < per_wg[w].size(); ++i)
+        need = std::max(need, candidate(per_wg[w][i - 1].d, per_wg[w][i].d));
+    if (need == 0) return;
+    const int64_t xs2 = std::max(xs_floats_max, koff + need), scr2 = std::max(scratch_floats, voff + need);
+    if (align_up(4 * lds_floats(xs2, scr2), 1024) <= dev.lds_bytes_per_cu) {
+      xs_floats_max = xs2;
+      scratch_floats = scr2;
+    }
+    for (int w = 0; w < n_wg; ++w)
+      for (size_t i = 1; i < per_wg[w].size(); ++i) {
+        TaskDesc& a = per_wg[w][i].d;
+        TaskDesc& q = per_wg[w][i - 1].d;
+        const int64_t fl = candidate(q, a);
+        if (fl == 0 || koff + fl > xs_floats_max || voff + fl > scratch_floats) continue;
+        q.a3 = a.a0;
+        q.a4 = a.u0;
+        q.a5 = (int)(std::min<int64_t>(a.u1, n) - a.u0);
+        a.a3 = q.a5;
+      }
+  }
+  // LDS floats of the GQA plan: header, staged vector, row results, row tables, gains, scratch
+  int64_t lds_floats(int64_t xs, int64_t scr) const {
+    const int64_t gmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.q_lora_rank, (int64_t)s.kv_lora_rank});
+    return 64 + xs + kYsFloats + (int64_t)kMaxTaskRows * 12 / 4 + align_up(gmax / 2, 256) + scr;
+  }
+
   // ---------------------------------------------------------------- GQA layer stages
   std::vector<int32_t> hinit_deps;  // layer 0: counters of the h = x init tasks
   std::vector<int64_t> h_acc;       // GQA: per-layer h accumulators
@@ -306,8 +355,8 @@ struct Builder {
     const int64_t pstride = (int64_t)r * (hd + 4);  // per split: r x (m, l, pad, pad, acc[hd])
     const int64_t part = act(p + "attn_partials", (int64_t)nkv * smax * pstride);
     L.act[LA_PART] = (int)part;
-    const int64_t gpw = 512 / hd;  // lane groups per wave in the attention task
-    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * gpw * (pstride + r) + 2 * r + 64);
+    // attention task: one partial per wave, per-wave stride sized for up to 4 heads
+    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * 4 * (hd + 4) + 64);
     scratch_floats = std::max<int64_t>(scratch_floats, align_up((int64_t)smax * pstride, 256) + (int64_t)smax * r + 64);
     for (int g = 0; g < nkv; ++g)
       for (int sp = 0; sp < S[g]; ++sp) {
@@ -517,6 +566,8 @@ struct Builder {
       spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
     }
 
+    if (s.arch == DEC_ARCH_GQA) stage_attention_kv();
+
     // flatten per-workgroup lists, resolve dependency entries
     P.wg_begin.assign(n_wg + 1, 0);
     for (int w = 0; w < n_wg; ++w) {
@@ -547,12 +598,11 @@ struct Builder {
     P.attn_scale_log2 = (float)(1.0 / std::sqrt(qk) * 1.4426950408889634);
 
     // LDS: staged input vector + per-row results + reduction scratch
-    const int64_t tables = (int64_t)kMaxTaskRows * 12 / 4;  // row pointers + input offsets
     const int64_t header = 64;  // LDS flag words ahead of the staged vector
     const int64_t gmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.q_lora_rank, (int64_t)s.kv_lora_rank});
     const int64_t gs = align_up(gmax / 2, 256);  // bf16 gains, DMA granularity 256 floats
     P.gs_floats = gs;
-    int64_t lds = 4 * (header + xs_floats_max + kYsFloats + tables + gs + scratch_floats);
+    int64_t lds = 4 * lds_floats(xs_floats_max, scratch_floats);
     if (s.arch != DEC_ARCH_GQA) {
       // the latent-attention, absorb and W_UV tasks use the whole region after the header
       const int64_t absorb = align_up(s.qk_nope, 256) + (int64_t)kMlaColBlock * 64 + 64;
@@ -621,6 +671,19 @@ std::string validate_plan(const PlanData& p) {
   for (int w = 0; w < p.n_wg; ++w)
     for (int i = p.wg_begin[w] + 1; i < p.wg_begin[w + 1]; ++i)
       if (p.info[i].stage < p.info[i - 1].stage) { e << "wg " << w << " list not in stage order"; return e.str(); }
+  // (1b) an attention split with staged K/V rows directly follows the QKV task that stages
+  //      them, in the same workgroup, for the same group, first position and row count
+  for (int w = 0; w < p.n_wg; ++w)
+    for (int i = p.wg_begin[w]; i < p.wg_begin[w + 1]; ++i) {
+      const TaskDesc& a = p.tasks[i];
+      if (a.type != T_ATTN || a.a3 == 0) continue;
+      const TaskDesc* q = (i > p.wg_begin[w]) ? &p.tasks[i - 1] : nullptr;
+      if (!q || q->type != T_QKV || q->layer != a.layer || q->a3 != a.a0 || q->a4 != a.u0 || q->a5 != a.a3 ||
+          a.a3 < 0 || a.a3 > a.u1 - a.u0 || a.u0 + a.a3 > p.kv_len || a.u1 - a.u0 - a.a3 > 1) {
+        e << "task " << a.id << ": staged K/V rows without a matching QKV task";
+        return e.str();
+      }
+    }
   // (2) every counter waited on is produced only by tasks of earlier stages, and its
   //     per-step total equals its producers' count (merged counters: exactly one merge)
   std::vector<int> prod_stage_max(p.counter_total.size(), -1), prod_count(p.counter_total.size(), 0);

@@ -343,3 +343,31 @@ def test_mla_append_runs_alone():
         assert len(app) == 1
         assert not any(t["wg"] == app[0]["wg"] and t["layer"] == layer and B.TASK_TYPES[t["type"]] == "MLA_B"
                        for t in p.tasks())
+
+
+@pytest.mark.parametrize("name,expect", [("8b_4k", "all"), ("small_gqa", "all"), ("tiny_mha_ragged", "some"),
+                                         ("8b_32k", "none"), ("tiny_kv0", "none")])
+def test_attention_kv_staging(name, expect):
+    """A staged attention split directly follows, in its workgroup's list, the QKV task that
+    copies its cached K/V rows into LDS; the rows staged are exactly the split's cached
+    positions (the new position, if the split holds it, is the one row left)."""
+    p, cfg = plan(name)
+    n = cfg["kv_len"]
+    tasks = sorted(p.tasks(), key=lambda t: (t["wg"], t["list_pos"]))
+    att = [t for t in tasks if B.TASK_TYPES[t["type"]] == "ATTN"]
+    staged = 0
+    for i, t in enumerate(tasks):
+        if B.TASK_TYPES[t["type"]] != "ATTN" or t["kv_staged"] == 0:
+            continue
+        staged += 1
+        q = tasks[i - 1]
+        assert q["wg"] == t["wg"] and B.TASK_TYPES[q["type"]] == "QKV" and q["layer"] == t["layer"]
+        assert q["kv_staged"] == t["kv_staged"] == min(t["unit_end"], n) - t["unit_begin"]
+    n_qkv = sum(1 for t in tasks if B.TASK_TYPES[t["type"]] == "QKV" and t["kv_staged"] > 0)
+    assert n_qkv == staged
+    if expect == "all":
+        assert staged == len(att)
+    elif expect == "some":
+        assert 0 < staged < len(att)
+    else:
+        assert staged == 0
