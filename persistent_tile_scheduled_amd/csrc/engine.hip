@@ -22,6 +22,7 @@
 // dot products run on the vector ALUs in fp32, not on MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "plan_types.h"
 
@@ -405,6 +406,84 @@ struct Stream {
   }
 };
 
+// Like Stream, but over a range of the task's flattened (row, chunk) sequence: chunk f is
+// chunk f % cpr of row f / cpr, and a wave's range [fa, fb) may start and end inside a row.
+// Each row's partial dot product over the chunks the wave holds is emitted when its part of
+// the row ends. Used where a task has few, long rows: whole rows per wave would leave the
+// waves up to a row apart (3 rows against 2 for 16 rows over 7 waves), and the last waves
+// alone could not keep enough loads in flight.
+struct StreamFlat {
+  const uint64_t* rowp;
+  const int* xoffp;
+  int fb, K, cpr, lane;
+  int lf, lj, lc;
+  const uint16_t* lrow;
+  int cf, cj, cc, cxo;
+  float acc0, acc1;
+
+  __device__ __forceinline__ void init(const uint64_t* rp, const int* xp, int fa, int fb_, int K_, int lane_) {
+    rowp = rp;
+    xoffp = xp;
+    fb = fb_;
+    K = K_;
+    lane = lane_;
+    cpr = (K + kChunkCols - 1) / kChunkCols;
+    const int j0 = fa / cpr, c0 = fa - j0 * cpr;
+    lf = cf = fa;
+    lj = cj = j0;
+    lc = cc = c0;
+    lrow = (fa < fb) ? (const uint16_t*)uni64(rowp[j0]) : nullptr;
+    cxo = (fa < fb) ? uni(xoffp[j0]) : 0;
+    acc0 = acc1 = 0.f;
+  }
+  __device__ __forceinline__ void load(u4 (&bf)[NB]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (lf < fb) {
+        int col = lc * kChunkCols + lane * 8;
+        col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
+        bf[i] = ldg_nt(lrow + col);
+        ++lf;
+        if (++lc == cpr) {
+          lc = 0;
+          ++lj;
+          if (lf < fb) lrow = (const uint16_t*)uni64(rowp[lj]);
+        }
+      }
+    }
+  }
+  template <class Emit>
+  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const float* xs, Emit& emit) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (cf < fb) {
+        const float* xp = xs + cxo + cc * kChunkCols + lane * 8;
+        const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
+        const u4 w = bf[i];
+        acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
+        acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
+        acc0 = fmaf(bf_lo(w.y), x0.z, acc0);
+        acc1 = fmaf(bf_hi(w.y), x0.w, acc1);
+        acc0 = fmaf(bf_lo(w.z), x1.x, acc0);
+        acc1 = fmaf(bf_hi(w.z), x1.y, acc1);
+        acc0 = fmaf(bf_lo(w.w), x1.z, acc0);
+        acc1 = fmaf(bf_hi(w.w), x1.w, acc1);
+        ++cf;
+        const bool row_end = ++cc == cpr;
+        if (row_end || cf == fb) {
+          emit(cj, wave_sum(acc0 + acc1));
+          acc0 = acc1 = 0.f;
+          if (row_end) {
+            cc = 0;
+            ++cj;
+            if (cf < fb) cxo = uni(xoffp[cj]);
+          }
+        }
+      }
+    }
+  }
+};
+
 // Each wave writes the row pointers / input offsets of its own rows (no barrier needed:
 // LDS accesses of one wave are ordered).
 template <class RM>
@@ -443,14 +522,30 @@ __device__ __forceinline__ int wave_start(int n, int w) {
 struct NoPre {
   __device__ __forceinline__ void operator()() const {}
 };
-template <int R = 2, class RM, class StageF, class EpiF, class PreF = NoPre, class IssueF = NoPre>  // R in [2, 4]
+// FLAT: the waves split the rows' chunks evenly (StreamFlat; G must be 1) and the partial
+// row sums meet in ys through LDS float atomics (two waves at most share a row, so the sum
+// does not depend on their order); otherwise each wave streams whole groups of G rows.
+template <int R = 2, bool FLAT = false, class RM, class StageF, class EpiF, class PreF = NoPre,
+          class IssueF = NoPre>  // R in [2, 4]
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
                                          int K, int G, bool prefetch, StageF&& stage, EpiF&& epi, int pre_deps = 0,
                                          PreF&& pre = PreF{}, IssueF&& issue = IssueF{}) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
-  const int ja = wave_start(ng, wave) * G, jb = wave_start(ng, wave + 1) * G;
-  Stream s;
+  int ja, jb, fa, fb;
+  if constexpr (FLAT) {
+    const int cpr = (K + kChunkCols - 1) / kChunkCols, nf = nrows * cpr;
+    fa = wave_start(nf, wave);
+    fb = wave_start(nf, wave + 1);
+    ja = fa / cpr;
+    jb = (fb + cpr - 1) / cpr;
+  } else {
+    ja = wave_start(ng, wave) * G;
+    jb = wave_start(ng, wave + 1) * G;
+    fa = ja;
+    fb = jb;
+  }
+  typename std::conditional<FLAT, StreamFlat, Stream>::type s;
   u4 buf[R][NB];
   if (pre_deps > 0) {
     if (!wait_deps(A, b, t, 0, pre_deps)) return false;
@@ -459,41 +554,51 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   if (prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
-    s.init(b.rowp, b.xoffp, ja, jb, K, lane);
+    s.init(b.rowp, b.xoffp, fa, fb, K, lane);
 #pragma unroll
     for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
   if (!wait_deps(A, b, t, pre_deps)) return false;
+  if constexpr (FLAT)
+    for (int i = threadIdx.x; i < ng; i += kThreads) b.ys[i] = 0.f;  // row sums (the stage's barrier orders this)
   stage();
   b.t_staged = (uint32_t)now();
   issue();
   if (!prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
-    s.init(b.rowp, b.xoffp, ja, jb, K, lane);
+    s.init(b.rowp, b.xoffp, fa, fb, K, lane);
 #pragma unroll
     for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
   float gacc = 0.f;
   auto emit = [&](int j, float v) {
-    gacc += v;
-    if (j % G == G - 1) {
-      if (lane == 0) b.ys[j / G] = gacc;
-      gacc = 0.f;
+    if constexpr (FLAT) {
+      if (lane == 0) atomicAdd(b.ys + j, v);
+    } else {
+      gacc += v;
+      if (j % G == G - 1) {
+        if (lane == 0) b.ys[j / G] = gacc;
+        gacc = 0.f;
+      }
     }
   };
-  while (s.cj < jb) {
+  auto more = [&] {
+    if constexpr (FLAT) return s.cf < fb;
+    else return s.cj < jb;
+  };
+  while (more()) {
     s.consume(buf[0], b.xs, emit);
     s.load(buf[0]);
-    if (s.cj >= jb) break;
+    if (!more()) break;
     s.consume(buf[1], b.xs, emit);
     s.load(buf[1]);
     if constexpr (R > 2) {
-      if (s.cj >= jb) break;
+      if (!more()) break;
       s.consume(buf[2], b.xs, emit);
       s.load(buf[2]);
     }
     if constexpr (R > 3) {
-      if (s.cj >= jb) break;
+      if (!more()) break;
       s.consume(buf[3], b.xs, emit);
       s.load(buf[3]);
     }
@@ -955,7 +1060,7 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.ffn;
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
-  return run_gemv(
+  return run_gemv<2, true>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
