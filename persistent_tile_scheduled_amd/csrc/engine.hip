@@ -1056,11 +1056,12 @@ __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const T
       });
 }
 
+template <bool FLAT>
 __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.ffn;
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
-  return run_gemv<2, true>(
+  return run_gemv<2, FLAT>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
@@ -1948,7 +1949,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
         case T_HINIT: gemv = false; ok = task_hinit(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
-        case T_DOWN: ok = task_down(A, b, t); break;
+        case T_DOWN: ok = task_down<true>(A, b, t); break;
         case T_LMHEAD: ok = task_lmhead(A, b, t); break;
         default: ok = false; break;
       }
@@ -1962,7 +1963,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_MLA_UV: gemv = false; ok = task_mla_uv(A, b, t); break;
         case T_OPROJ: ok = task_oproj(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
-        case T_DOWN: ok = task_down(A, b, t); break;
+        case T_DOWN: ok = task_down<false>(A, b, t); break;
         case T_LMHEAD: ok = task_lmhead(A, b, t); break;
         case T_ROUTER: ok = task_router(A, b, t); break;
         case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
