@@ -64,6 +64,7 @@ __device__ __forceinline__ u4 ldg_nt(const void* p) { return __builtin_nontempor
 // invalidate (buffer_inv) of an acquire fence, which measure 1-9 us each on MI355X.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kSC1 = 16;          // cache-policy bit SC1 (agent scope)
+constexpr int kNT = 2;            // cache-policy bit NT (streamed once: non-temporal)
 // Cache policy of loads of produced data. Every activation address is written once per step
 // (per-layer buffers, write-through SC1 stores) and read only after all of its writers have
 // signalled; lines cached by an earlier kernel are gone at the next launch (stream order).
@@ -153,6 +154,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
          (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
+
+// 2^x with the hardware instruction alone (no denormal-range scaling): results below 2^-126
+// come out as 0. The softmax weights use it with x <= 0 relative to a running maximum, so it
+// only drops terms smaller than 2^-126 of the largest one.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -772,9 +778,11 @@ __device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H,
 // every K/V load. A group of LPP = hd/8 lanes holds one position's row (8 dims per lane);
 // one wave instruction covers 64/LPP consecutive positions. Online softmax in base 2 per
 // head; partials are merged across the lane groups of a wave (cross-lane exchanges), then
-// across waves (LDS); the O-projection tasks merge the splits. The cached positions of the
-// first two blocks are loaded before the dependency wait; a block holding the new position
-// (slot kv_len, written by this step's QKV tasks) is loaded again after it.
+// across waves (LDS); the O-projection tasks merge the splits. The cached positions stream
+// through two register blocks with one kind of load and no divergent branch, so the
+// compiler's wait for a block does not also wait for the other block in flight; the first
+// two blocks are loaded before the dependency wait. The new position (slot kv_len, written
+// by this step's QKV tasks) is folded in after the loop, read with agent-coherent loads.
 template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   constexpr int GPW = 64 / LPP, NP = 3, PER_BLK = NP * GPW;
@@ -783,60 +791,36 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
   const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
   const int p0 = t.u0, np = t.u1 - t.u0;
   const int q0 = p0 + wave_start(np, wave), q1 = p0 + wave_start(np, wave + 1);
-  const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
-  const uint16_t* Vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * (size_t)n1 * hd + sub * 8;
-  const int nblk = (q1 > q0) ? (q1 - q0 + PER_BLK - 1) / PER_BLK : 0;
+  const int qc = q1 < n ? q1 : n;  // cached positions [q0, qc)
+  const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd;
+  const uint16_t* Vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * (size_t)n1 * hd;
+  const int nblk = (qc > q0) ? (qc - q0 + PER_BLK - 1) / PER_BLK : 0;
+  // buffer loads bounded at row qc: rows past the wave's cached range read as zero (and are
+  // masked), so a block needs one lane offset and a uniform block offset, nothing clamped
+  const rsrc_t kr = make_rsrc(Kb, (uint32_t)(qc * hd * 2)), vr = make_rsrc(Vb, (uint32_t)(qc * hd * 2));
+  const uint32_t lo = (uint32_t)(((q0 + grp) * hd + sub * 8) * 2);
   u4 ka[NP], va[NP], kb[NP], vb[NP];
-  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP], int lim) {
+  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      int pos = q0 + (blk * NP + i) * GPW + grp;
-      pos = pos < lim ? pos : lim - 1;
-      pos = pos > 0 ? pos : 0;
-      kk[i] = ldg_nt(Kb + (size_t)pos * hd);
-      vv[i] = ldg_nt(Vb + (size_t)pos * hd);
+      const int so = (blk * NP + i) * GPW * hd * 2;
+      kk[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lo, so, kNT);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lo, so, kNT);
     }
   };
-  // Blocks that hold the new slot are read with agent-coherent (SC1) loads: the slot was
-  // written by other workgroups in this step, and a short row can share its cache line with
-  // a row read (and cached in this XCD's L2) before the wait.
-  const rsrc_t kr = make_rsrc(Kb - sub * 8, (uint32_t)(n1 * hd * 2)), vr = make_rsrc(Vb - sub * 8, (uint32_t)(n1 * hd * 2));
-  auto load_coh = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      int pos = q0 + (blk * NP + i) * GPW + grp;
-      pos = pos < q1 ? pos : q1 - 1;
-      const uint32_t off = (uint32_t)(pos * hd + sub * 8) * 2u;
-      kk[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, kSC1);
-      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, kSC1);
-    }
-  };
-  // cached rows only (positions < n) before the wait
-  const int pre_lim = (q1 < n) ? q1 : n;
-  load(0, ka, va, pre_lim);
-  load(1, kb, vb, pre_lim);
+  load(0, ka, va);
+  load(1, kb, vb);
   if (!wait_deps(A, b, t)) return false;
-  if (nblk > 0 && q0 + PER_BLK > pre_lim) load_coh(0, ka, va);
-  if (nblk > 1 && q0 + 2 * PER_BLK > pre_lim) load_coh(1, kb, vb);
 
-  // the group's queries, fetched by wave 0 (no loads in flight) into LDS
+  // the group's queries, fetched by wave 0 (no loads in flight) into LDS and scaled there by
+  // softmax scale * log2(e); the blocks read them from LDS (no registers held across the loop)
   if (threadIdx.x < 64) {
     dma_to_lds(b.ys, b.actp + L.act[LA_Q] + g * r * hd, r * hd);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
   }
   __syncthreads();
-  float qv[R][8];
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    f4 a = f4{0.f, 0.f, 0.f, 0.f}, c = a;
-    if (h < r) {
-      a = *(const f4*)(b.ys + h * hd + sub * 8);
-      c = *(const f4*)(b.ys + h * hd + sub * 8 + 4);
-    }
-    const float sc = A.attn_scale_log2;
-    qv[h][0] = a.x * sc; qv[h][1] = a.y * sc; qv[h][2] = a.z * sc; qv[h][3] = a.w * sc;
-    qv[h][4] = c.x * sc; qv[h][5] = c.y * sc; qv[h][6] = c.z * sc; qv[h][7] = c.w * sc;
-  }
+  for (int i = threadIdx.x; i < r * hd; i += kThreads) b.ys[i] *= A.attn_scale_log2;
+  __syncthreads();
   float m[R], l[R], acc[R][8];
 #pragma unroll
   for (int h = 0; h < R; ++h) {
@@ -845,24 +829,32 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
 #pragma unroll
     for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
   }
-  auto step = [&](int blk, const u4(&kk)[NP], const u4(&vv)[NP]) {
+  // fold one block in: lane group grp's row i is position base + i GPW + grp, part of the
+  // wave's work when it lies in [lo, hi). Heads past r repeat head r - 1 and are never stored.
+  auto step = [&](int base, int lo, int hi, const u4(&kk)[NP], const u4(&vv)[NP]) {
     float s[R][NP];
+    int qo = sub * 8;
+    asm volatile("" : "+v"(qo));  // re-read q per block: keeps the reads from being hoisted into registers
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      const u4 kw = kk[i];
-      const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
-                           bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
+    for (int h = 0; h < R; ++h) {
+      const float* qh = b.ys + (h < r ? h : r - 1) * hd + qo;
+      const f4 qa = *(const f4*)qh, qb = *(const f4*)(qh + 4);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
-      for (int h = 0; h < R; ++h) {
+      for (int i = 0; i < NP; ++i) {
+        const u4 kw = kk[i];
+        const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y),
+                             bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
         float p = 0.f;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) p = fmaf(qv[h][d], kf[d], p);
+        for (int d = 0; d < 8; ++d) p = fmaf(qv[d], kf[d], p);
         s[h][i] = p;
       }
     }
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      const bool valid = q0 + (blk * NP + i) * GPW + grp < q1;
+      const int pos = base + i * GPW + grp;
+      const bool valid = pos >= lo && pos < hi;
 #pragma unroll
       for (int h = 0; h < R; ++h) {
         const float p = group_sum<LPP>(s[h][i]);
@@ -871,19 +863,18 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     }
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      if (h >= r) continue;
       float mb = s[h][0];
 #pragma unroll
       for (int i = 1; i < NP; ++i) mb = fmaxf(mb, s[h][i]);
       const float mn = fmaxf(m[h], mb);
-      if (mn == -INFINITY) continue;
-      const float alpha = exp2f(m[h] - mn);
+      const float mr = (mn == -INFINITY) ? 0.f : mn;  // nothing seen yet: every factor is 0
+      const float alpha = ex2(m[h] - mr);
       l[h] *= alpha;
 #pragma unroll
       for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const float p = exp2f(s[h][i] - mn);
+        const float p = ex2(s[h][i] - mr);
         l[h] += p;
         const u4 vw = vv[i];
         acc[h][0] = fmaf(p, bf_lo(vw.x), acc[h][0]);
@@ -898,16 +889,28 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
       m[h] = mn;
     }
   };
+  // the loads are unconditional (blocks past the end read zeros without touching memory) and
+  // the scheduler may not move one block's work across the other's loads, so the compiler's
+  // wait before each block leaves the next block in flight
   for (int blk = 0; blk < nblk; blk += 2) {
-    step(blk, ka, va);
-    if (blk + 2 < nblk) {
-      if (q0 + (blk + 3) * PER_BLK > n) load_coh(blk + 2, ka, va); else load(blk + 2, ka, va, q1);
+    step(q0 + blk * PER_BLK, q0, qc, ka, va);
+    load(blk + 2, ka, va);
+    __builtin_amdgcn_sched_barrier(0);
+    step(q0 + (blk + 1) * PER_BLK, q0, qc, kb, vb);
+    load(blk + 3, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (q0 <= n && n < q1) {
+    // the new position: every lane group reads row n (agent scope: other workgroups wrote it
+    // in this step), lane group 0 of row 0 folds it in
+    const rsrc_t kn = make_rsrc(Kb, (uint32_t)(n1 * hd * 2)), vn = make_rsrc(Vb, (uint32_t)(n1 * hd * 2));
+    const uint32_t off = (uint32_t)(n * hd + sub * 8) * 2u;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      ka[i] = __builtin_amdgcn_raw_buffer_load_b128(kn, off, 0, kSC1);
+      va[i] = __builtin_amdgcn_raw_buffer_load_b128(vn, off, 0, kSC1);
     }
-    if (blk + 1 >= nblk) break;
-    step(blk + 1, kb, vb);
-    if (blk + 3 < nblk) {
-      if (q0 + (blk + 4) * PER_BLK > n) load_coh(blk + 3, kb, vb); else load(blk + 3, kb, vb, q1);
-    }
+    step(n, n, n + 1, ka, va);
   }
   const uint32_t t_mid = (uint32_t)now();
   // merge the wave's lane groups (the same dims of different positions) with cross-lane
@@ -1141,108 +1144,80 @@ typedef short s4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f4 mfma_bf16_k16(uint2 a, uint2 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a), __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
 }
+// One 16-position tile of an attention split on the matrix cores, folded into the calling
+// wave's running softmax state (m, l: lane's head hl; o: rows = heads 4 q4 + i, column
+// 16 ct + hl). K and V hold the tile's rows from row 16 tile on (rows of HD bf16); rows at or
+// past nv are not part of the split (read as row nv - 1, probability 0).
 template <int HD>
-__device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, const TaskDesc& t) {
-  constexpr int NKS = HD / 32, NCT = HD / 16, ps = HD + 4, SS = 4 * ps;
-  const LayerDesc& L = A.layers[t.layer];
-  const int r = A.nq / A.nkv, g = t.a0;
-  const int p0 = t.u0, np = t.u1 - t.u0, c = t.a3;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // keeps lane-derived LDS addresses inside the task (not hoisted and spilled)
-  const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden));  // [np][HD]
-  uint16_t* Vs = reinterpret_cast<uint16_t*>(b.scr + kv_stage_v_off(HD));       // [np][HD]
-  // this wave's LDS DMA of the staged rows (issued during the QKV task) has landed; the
-  // barrier in the wait publishes it to the other waves
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  if (!wait_deps(A, b, t)) return false;
-  // every wave loads q~ in B-operand order itself: lane L of k-step ks holds head L % 16,
-  // dims 32 ks + 8 (L / 16) + e (zero past r)
-  f4 qa[NKS], qb[NKS];
-  const uint32_t qo = (uint32_t)(L.act[LA_Q] + (g * r + (hl < r ? hl : 0)) * HD + 8 * q4) * 4u;
+__device__ __forceinline__ void attn_tile(const uint16_t* Ks, const uint16_t* Vs, int tile, int nv, int r, int hl, int q4,
+                                          const u4 (&qh)[HD / 32], const u4 (&ql)[HD / 32], float& m, float& l,
+                                          f4 (&o)[HD / 16]) {
+  constexpr int NKS = HD / 32, NCT = HD / 16;
+  int pos = 16 * tile + hl;
+  pos = pos < nv ? pos : nv - 1;
+  const uint16_t* arow = Ks + (size_t)pos * HD + 8 * q4;
+  f4 dh = f4{0.f, 0.f, 0.f, 0.f}, dl = dh;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    qa[ks] = cld4(b.act, qo + ks * 128u);
-    qb[ks] = cld4(b.act, qo + ks * 128u + 16u);
+    const u4 a = *reinterpret_cast<const u4*>(arow + 32 * ks);
+    dh = mfma_bf16(a, qh[ks], dh);
+    dl = mfma_bf16(a, ql[ks], dl);
   }
-  if (wave == 0 && c < np && lane < HD / 8) {  // row c: the new position, written by this step's QKV tasks
-    const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
-    const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
-    const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
-    __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
-    __builtin_amdgcn_global_load_lds((gvp)(vb + off), (lvp)(Vs + (size_t)c * HD), 16, 0, kSC1);
-  }
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  u4 qh[NKS], ql[NKS];
-  const float sc = (hl < r) ? A.attn_scale_log2 : 0.f;
+  const f4 d = dh + dl;  // S[position 16 tile + 4 q4 + i][head hl]
+  const int pq = 16 * tile + 4 * q4;
+  float sv[4], mt = -INFINITY;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) split_bf16x8(qa[ks], qb[ks], sc, qh[ks], ql[ks]);
-  __syncthreads();
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (pq + i < nv && hl < r) ? d[i] : -INFINITY;
+    mt = fmaxf(mt, sv[i]);
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(m, mt);  // -inf only for heads past r
+  const float al = (m == -INFINITY) ? 0.f : ex2(m - mn);
+  float pv[4], ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = (sv[i] == -INFINITY) ? 0.f : ex2(sv[i] - mn);
+    ls += pv[i];
+  }
+  ls += __shfl_xor(ls, 16, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  l = l * al + ls;
+  m = mn;
+  // rescale O rows (heads 0..3 live in lanes q4 = 0; lane i holds head i's factor)
+  const int alb = __float_as_int(al);
+  const f4 a4 = f4{__int_as_float(__builtin_amdgcn_readlane(alb, 0)), __int_as_float(__builtin_amdgcn_readlane(alb, 1)),
+                   __int_as_float(__builtin_amdgcn_readlane(alb, 2)), __int_as_float(__builtin_amdgcn_readlane(alb, 3))};
+  uint2 ph, plo;
+  {
+    uint32_t h0, h1, l0, l1;
+    split_bf16(pv[0], pv[1], h0, l0);
+    split_bf16(pv[2], pv[3], h1, l1);
+    ph = uint2{h0, h1};
+    plo = uint2{l0, l1};
+  }
+  const uint16_t* vrow = Vs + hl;
+  int vp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vp[i] = (pq + i < nv ? pq + i : nv - 1) * HD;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const uint16_t* vc = vrow + 16 * ct;
+    const uint2 bv = uint2{bf_pair(vc[vp[0]], vc[vp[1]]), bf_pair(vc[vp[2]], vc[vp[3]])};
+    o[ct] *= a4;
+    o[ct] = mfma_bf16_k16(ph, bv, o[ct]);
+    o[ct] = mfma_bf16_k16(plo, bv, o[ct]);
+  }
+}
 
-  // lane: head hl of the running (m, l); O rows = heads 4 q4 + i, column 16 ct + hl
-  float m = -INFINITY, l = 0.f;
-  f4 o[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) o[ct] = f4{0.f, 0.f, 0.f, 0.f};
-  const int ntile = (np + 15) >> 4;
-  for (int tile = wave; tile < ntile; tile += kWaves) {
-    int pos = 16 * tile + hl;
-    pos = pos < np ? pos : np - 1;
-    const uint16_t* arow = Ks + (size_t)pos * HD + 8 * q4;
-    f4 dh = f4{0.f, 0.f, 0.f, 0.f}, dl = dh;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const u4 a = *reinterpret_cast<const u4*>(arow + 32 * ks);
-      dh = mfma_bf16(a, qh[ks], dh);
-      dl = mfma_bf16(a, ql[ks], dl);
-    }
-    const f4 d = dh + dl;  // S[position 16 tile + 4 q4 + i][head hl]
-    const int pq = 16 * tile + 4 * q4;
-    float sv[4], mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (pq + i < np && hl < r) ? d[i] : -INFINITY;
-      mt = fmaxf(mt, sv[i]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);  // -inf only for heads past r
-    const float al = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-    float pv[4], ls = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
-      ls += pv[i];
-    }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    l = l * al + ls;
-    m = mn;
-    // rescale O rows (heads 0..3 live in lanes q4 = 0; lane i holds head i's factor)
-    const int alb = __float_as_int(al);
-    const f4 a4 = f4{__int_as_float(__builtin_amdgcn_readlane(alb, 0)), __int_as_float(__builtin_amdgcn_readlane(alb, 1)),
-                     __int_as_float(__builtin_amdgcn_readlane(alb, 2)), __int_as_float(__builtin_amdgcn_readlane(alb, 3))};
-    uint2 ph, plo;
-    {
-      uint32_t h0, h1, l0, l1;
-      split_bf16(pv[0], pv[1], h0, l0);
-      split_bf16(pv[2], pv[3], h1, l1);
-      ph = uint2{h0, h1};
-      plo = uint2{l0, l1};
-    }
-    const uint16_t* vrow = Vs + hl;
-    int vp[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vp[i] = (pq + i < np ? pq + i : np - 1) * HD;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint16_t* vc = vrow + 16 * ct;
-      const uint2 bv = uint2{bf_pair(vc[vp[0]], vc[vp[1]]), bf_pair(vc[vp[2]], vc[vp[3]])};
-      o[ct] *= a4;
-      o[ct] = mfma_bf16_k16(ph, bv, o[ct]);
-      o[ct] = mfma_bf16_k16(plo, bv, o[ct]);
-    }
-  }
+// The eight waves' (m, l, O) -> LDS slots -> the split partial (m, l, 0, 0, unnormalised o) per
+// head, which wave 0 stores.
+template <int HD>
+__device__ __forceinline__ void attn_finish(const EngineArgs& A, Blk& b, const TaskDesc& t, int r, int hl, int q4, float m,
+                                            float l, const f4 (&o)[HD / 16]) {
+  constexpr int NCT = HD / 16, ps = HD + 4, SS = 4 * ps;
+  const int wave = wave_id();
   // this wave's (m, l, O) -> slot `wave`: [wave][head < 4][m, l, 0, 0, o[HD]]
   float* slot = b.scr + wave * SS;
   if (q4 == 0 && hl < r) {
@@ -1280,6 +1255,52 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
     const uint32_t gpart = (uint32_t)(t.a4 + t.a1 * r * ps);
     for (int i = threadIdx.x * 4; i < r * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
   }
+}
+
+template <int HD>
+__device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  constexpr int NKS = HD / 32, NCT = HD / 16, ps = HD + 4, SS = 4 * ps;
+  const LayerDesc& L = A.layers[t.layer];
+  const int r = A.nq / A.nkv, g = t.a0;
+  const int p0 = t.u0, np = t.u1 - t.u0, c = t.a3;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // keeps lane-derived LDS addresses inside the task (not hoisted and spilled)
+  const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden));  // [np][HD]
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(b.scr + kv_stage_v_off(HD));       // [np][HD]
+  // this wave's LDS DMA of the staged rows (issued during the QKV task) has landed; the
+  // barrier in the wait publishes it to the other waves
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  if (!wait_deps(A, b, t)) return false;
+  // every wave loads q~ in B-operand order itself: lane L of k-step ks holds head L % 16,
+  // dims 32 ks + 8 (L / 16) + e (zero past r)
+  f4 qa[NKS], qb[NKS];
+  const uint32_t qo = (uint32_t)(L.act[LA_Q] + (g * r + (hl < r ? hl : 0)) * HD + 8 * q4) * 4u;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    qa[ks] = cld4(b.act, qo + ks * 128u);
+    qb[ks] = cld4(b.act, qo + ks * 128u + 16u);
+  }
+  if (wave == 0 && c < np && lane < HD / 8) {  // row c: the new position, written by this step's QKV tasks
+    const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
+    const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
+    const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
+    __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
+    __builtin_amdgcn_global_load_lds((gvp)(vb + off), (lvp)(Vs + (size_t)c * HD), 16, 0, kSC1);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  u4 qh[NKS], ql[NKS];
+  const float sc = (hl < r) ? A.attn_scale_log2 : 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) split_bf16x8(qa[ks], qb[ks], sc, qh[ks], ql[ks]);
+  __syncthreads();
+  float m = -INFINITY, l = 0.f;
+  f4 o[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) o[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  const int ntile = (np + 15) >> 4;
+  for (int tile = wave; tile < ntile; tile += kWaves) attn_tile<HD>(Ks, Vs, tile, np, r, hl, q4, qh, ql, m, l, o);
+  attn_finish<HD>(A, b, t, r, hl, q4, m, l, o);
   return true;
 }
 
@@ -1546,7 +1567,7 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
       float pv[4], ps = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pv[i] = (sv[i] == -INFINITY) ? 0.f : exp2f(sv[i] - mn);
+        pv[i] = (sv[i] == -INFINITY) ? 0.f : ex2(sv[i] - mn);
         ps += pv[i];
       }
       ps += __shfl_xor(ps, 16, 64);
@@ -1574,7 +1595,7 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
         mn = fmaxf(mn, TMAX[tt * 16 + h]);
         ts += TSUM[tt * 16 + h];
       }
-      const float al = (mo == -INFINITY) ? 0.f : exp2f(mo - mn);
+      const float al = (mo == -INFINITY) ? 0.f : ex2(mo - mn);
       LR[h] = LR[h] * al + ts;
       MR[h] = mn;
       AL[h] = al;
