@@ -3,7 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8b_4k] [--no-cpu-baseline]
 
 A step is one whole decode step (all layers, one kernel launch) over synthetic bf16
-weights and KV cache already resident in HBM. Prints ONE JSON line.
+weights and KV cache already resident in HBM. Prints ONE JSON line. --launch stages|graph
+times the same step split into one launch per stage (eagerly, or replayed from a HIP graph),
+the launch-per-operator execution the persistent engine replaces.
 """
 import argparse
 import json
@@ -138,6 +140,9 @@ def main():
     ap.add_argument("--config", default="8b_4k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=["persistent", "stages", "graph"], default="persistent",
+                    help="persistent: the step as one engine launch (the product); stages: one launch per "
+                         "stage of the same tasks; graph: those launches replayed from a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -161,10 +166,20 @@ def main():
     eng = DecodeEngine(cfg, w)
     alg_bytes = eng.sizes["algorithmic_bytes_per_step"]
     stream = eng.stream
+    if args.launch == "persistent":
+        run = lambda: eng.step(x, kv)
+    else:
+        run = lambda: eng.step_stages(x, kv)
     for _ in range(args.warmup):
-        eng.step(x, kv)
+        run()
     torch.cuda.synchronize()
     eng.status()
+    if args.launch == "graph":
+        graph = eng.capture_stages(x, kv)
+        run = graph.replay
+        run()
+        torch.cuda.synchronize()
+        eng.status()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -172,7 +187,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        eng.step(x, kv)
+        run()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -203,6 +218,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 KV and input)",
         "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
                    "kv_len": cfg["kv_len"], "batch": 1},
+        "launch": args.launch if args.launch == "persistent" else
+        f"{args.launch}: {eng.n_stages} launches per step",
         "tokens_per_s": round(1e6 / us_per_token, 1),
         "kernel_us_mean": round(mean_us, 2),
         "kernel_us_median": round(med_us, 2),

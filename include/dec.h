@@ -189,6 +189,23 @@ dec_status dec_plan_bind(struct dec_plan* plan, const void* const* weights, int6
  * Errors: UNBOUND, INVAL (null or misaligned), HIP (launch failure). */
 dec_status dec_step(struct dec_plan* plan, const void* x, void* kv, void* out, void* stream);
 
+/* The same step split into several launches, for measuring what the single persistent launch
+ * saves (the launch-per-operator execution that the Static Compilation page and the TileRT
+ * talk, section on breaking kernel boundaries, set against one engine kernel). The plan's tasks
+ * fall into dec_plan_n_stages() stages in dependency order: every task waits only on tasks of
+ * earlier stages. dec_step_stages runs the tasks of stages [stage_lo, stage_hi) in ONE launch
+ * on `stream`: a plain launch for a single stage (nothing in it waits on anything in the same
+ * launch), a cooperative one for several. One step is either one dec_step, or calls covering
+ * [0, n_stages) in increasing, consecutive ranges on one stream with nothing of another step in
+ * between; the step's last call (stage_hi == n_stages) completes it. The x, kv and out arguments
+ * must be the same for all calls of a step. The launches read and write the same buffers as
+ * dec_step and give the same results; they contain no host synchronisation or memory set, so
+ * a stream capture of them (a HIP graph) replays a whole step.
+ * Errors: UNBOUND, INVAL (null, misaligned, or a range outside [0, n_stages) or empty), HIP. */
+int64_t dec_plan_n_stages(const struct dec_plan* plan);
+dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo,
+                           int32_t stage_hi, void* stream);
+
 /* Synchronise `stream` and read the sticky device status word: DEC_OK or DEC_E_TIMEOUT
  * (the failing task id is in dec_last_error()). */
 dec_status dec_plan_status(struct dec_plan* plan, void* stream);

@@ -98,6 +98,8 @@ def lib() -> C.CDLL:
         "dec_plan_grid": (C.c_int, [P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
         "dec_plan_bind": (C.c_int, [P, C.POINTER(P), C.c_int64, P, C.c_int64, P]),
         "dec_step": (C.c_int, [P, P, P, P, P]),
+        "dec_plan_n_stages": (C.c_int64, [P]),
+        "dec_step_stages": (C.c_int, [P, P, P, P, C.c_int32, C.c_int32, P]),
         "dec_plan_status": (C.c_int, [P, P]),
         "dec_plan_reset": (C.c_int, [P, P]),
         "dec_plan_set_watchdog": (C.c_int, [P, C.c_int64]),
@@ -114,8 +116,8 @@ def lib() -> C.CDLL:
 ABI_SYMBOLS = ["dec_last_error", "dec_device_query", "dec_plan_create", "dec_plan_create_for", "dec_plan_destroy",
                "dec_plan_n_weights", "dec_plan_weight_desc", "dec_plan_sizes", "dec_plan_n_tasks", "dec_plan_tasks",
                "dec_plan_n_deps", "dec_plan_deps", "dec_plan_n_counters", "dec_plan_n_buffers",
-               "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_step", "dec_plan_status",
-               "dec_plan_reset", "dec_plan_set_watchdog"]
+               "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_step", "dec_plan_n_stages",
+               "dec_step_stages", "dec_plan_status", "dec_plan_reset", "dec_plan_set_watchdog"]
 
 
 def _check(status: int):
@@ -235,6 +237,13 @@ class Plan:
     def step(self, x_ptr: int, kv_ptr: int, out_ptr: int, stream: int = 0):
         _check(lib().dec_step(self.h, C.c_void_p(int(x_ptr)), C.c_void_p(int(kv_ptr)), C.c_void_p(int(out_ptr)),
                               C.c_void_p(int(stream))))
+
+    def n_stages(self) -> int:
+        return lib().dec_plan_n_stages(self.h)
+
+    def step_stages(self, x_ptr: int, kv_ptr: int, out_ptr: int, stage_lo: int, stage_hi: int, stream: int = 0):
+        _check(lib().dec_step_stages(self.h, C.c_void_p(int(x_ptr)), C.c_void_p(int(kv_ptr)), C.c_void_p(int(out_ptr)),
+                                     int(stage_lo), int(stage_hi), C.c_void_p(int(stream))))
 
     def status(self, stream: int = 0):
         _check(lib().dec_plan_status(self.h, C.c_void_p(int(stream))))

@@ -11,7 +11,8 @@
 #include "../../include/dec.h"
 #include "planner.h"
 
-extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream);
+extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, bool cooperative,
+                                        hipStream_t stream);
 extern "C" hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu);
 
 struct dec_plan {
@@ -44,6 +45,7 @@ void fill_args(dec_plan* p) {
   a.ws = ws;
   a.tasks = reinterpret_cast<const dec::TaskDesc*>(ws + P.off_tasks);
   a.wg_begin = reinterpret_cast<const int32_t*>(ws + P.off_wgb);
+  a.stage_first = reinterpret_cast<const int32_t*>(ws + P.off_stf);
   a.deps = reinterpret_cast<const dec::DepEntry*>(ws + P.off_deps);
   a.wptr = reinterpret_cast<const uint64_t*>(ws + P.off_wptr);
   a.layers = reinterpret_cast<const dec::LayerDesc*>(ws + P.off_layers);
@@ -80,6 +82,9 @@ void fill_args(dec_plan* p) {
   a.w_lm_head = P.w_lm_head;
   a.x_final = P.x_final;
   a.xs_floats = (int32_t)P.xs_floats;
+  a.n_stages = P.n_stages;
+  a.stage_lo = 0;
+  a.stage_hi = P.n_stages;
   a.act_bytes = (uint32_t)(P.act_floats * 4);
   a.gs_floats = (int32_t)P.gs_floats;
   a.eps = s.rms_eps;
@@ -89,6 +94,36 @@ void fill_args(dec_plan* p) {
 void copy_name(char* dst, const std::string& s) {
   std::memset(dst, 0, 64);
   std::strncpy(dst, s.c_str(), 63);
+}
+
+}  // namespace
+
+namespace {
+
+// One launch of the tasks of stages [lo, hi): cooperative (co-resident grid) when it spans
+// several stages, whose tasks wait on each other; a plain launch for one stage.
+dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t lo, int32_t hi, void* stream) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (!plan->bound) return fail(DEC_E_UNBOUND, "step before dec_plan_bind");
+  if (!x || !kv || !out) return fail(DEC_E_INVAL, "null x/kv/out");
+  if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
+  if (lo < 0 || hi > plan->P.n_stages || lo >= hi)
+    return fail(DEC_E_INVAL, "stage range [" + std::to_string(lo) + ", " + std::to_string(hi) + ") not inside [0, " +
+                                 std::to_string(plan->P.n_stages) + ")");
+  plan->args.x = static_cast<const uint16_t*>(x);
+  plan->args.kv = static_cast<uint16_t*>(kv);
+  plan->args.out = static_cast<float*>(out);
+  plan->args.watchdog_ticks = plan->watchdog_us * 100;
+  plan->args.stage_lo = lo;
+  plan->args.stage_hi = hi;
+  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, hi - lo > 1,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");
+    return hip_fail(e, "engine launch");
+  }
+  return DEC_OK;
 }
 
 }  // namespace
@@ -276,6 +311,7 @@ dec_status dec_plan_bind(dec_plan* plan, const void* const* weights, int64_t n, 
   std::vector<char> img((size_t)P.off_act, 0);
   std::memcpy(img.data() + P.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(dec::TaskDesc));
   std::memcpy(img.data() + P.off_wgb, P.wg_begin.data(), P.wg_begin.size() * 4);
+  std::memcpy(img.data() + P.off_stf, P.stage_first.data(), P.stage_first.size() * 4);
   if (!P.deps.empty()) std::memcpy(img.data() + P.off_deps, P.deps.data(), P.deps.size() * sizeof(dec::DepEntry));
   std::memcpy(img.data() + P.off_wptr, plan->wptr.data(), plan->wptr.size() * 8);
   std::memcpy(img.data() + P.off_layers, P.layers.data(), P.layers.size() * sizeof(dec::LayerDesc));
@@ -295,22 +331,17 @@ dec_status dec_plan_bind(dec_plan* plan, const void* const* weights, int64_t n, 
   return DEC_OK;
 }
 
+
 dec_status dec_step(dec_plan* plan, const void* x, void* kv, void* out, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
-  if (!plan->bound) return fail(DEC_E_UNBOUND, "dec_step before dec_plan_bind");
-  if (!x || !kv || !out) return fail(DEC_E_INVAL, "null x/kv/out");
-  if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
-    return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
-  plan->args.x = static_cast<const uint16_t*>(x);
-  plan->args.kv = static_cast<uint16_t*>(kv);
-  plan->args.out = static_cast<float*>(out);
-  plan->args.watchdog_ticks = plan->watchdog_us * 100;
-  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");
-    return hip_fail(e, "engine launch");
-  }
-  return DEC_OK;
+  return launch_stages(plan, x, kv, out, 0, plan->P.n_stages, stream);
+}
+
+int64_t dec_plan_n_stages(const dec_plan* plan) { return plan ? (int64_t)plan->P.n_stages : -1; }
+
+dec_status dec_step_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo, int32_t stage_hi,
+                           void* stream) {
+  return launch_stages(plan, x, kv, out, stage_lo, stage_hi, stream);
 }
 
 dec_status dec_plan_status(dec_plan* plan, void* stream) {

@@ -661,6 +661,30 @@ struct RmQKV {
 // prefetch. Every streaming wave issues exactly kKvStageDma 1-KB chunks (indices past the
 // end repeat the last chunk; lanes past a region's end re-read its last 16 bytes), so the
 // number of loads in flight is the same on every path through the stream loop.
+// LDS DMA of the cached K and V rows [p0, p0 + rows) of KV group g of a layer: K rows to
+// xs + kv_stage_k_off(hidden), V rows to scr + kv_stage_v_off(hd), as 1-KB chunks. Called by
+// waves 1..7 (slot = wave - 1); each issues kKvStageDma chunks (slots past the last chunk
+// re-load it), which covers up to 7 * kKvStageDma chunks of K and V together.
+__device__ __forceinline__ void kv_stage_dma(const EngineArgs& A, Blk& b, int layer, int g, int p0, int rows, int slot) {
+  const int lane = threadIdx.x & 63, hd = A.hd;
+  const int hw = hd / 2, nfl = rows * hw, nch = (nfl + 255) / 256;
+  const size_t n1 = (size_t)A.kv_len + 1;
+  const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 0) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
+  const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 1) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
+  float* kd = b.xs + kv_stage_k_off(A.hidden);
+  float* vd = b.scr + kv_stage_v_off(hd);
+#pragma unroll
+  for (int k = 0; k < kKvStageDma; ++k) {
+    int c = slot + (kWaves - 1) * k;
+    c = c < 2 * nch ? c : 2 * nch - 1;
+    const bool isv = c >= nch;
+    const int cc = isv ? c - nch : c;
+    int f = cc * 256 + lane * 4;
+    f = f < nfl ? f : nfl - 4;
+    __builtin_amdgcn_global_load_lds((gvp)((isv ? vs : ks) + f), (lvp)((isv ? vd : kd) + cc * 256), 16, 0, 0);
+  }
+}
+
 template <bool KV>
 __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
@@ -669,24 +693,9 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
   const int xin = L.act[LA_X_IN];
   auto issue = [&] {
     if constexpr (KV) {
-      const int wave = wave_id(), lane = threadIdx.x & 63;
+      const int wave = wave_id();
       if (wave == 0) return;  // wave 0 stages the input vector: no loads ahead of it
-      const int hw = hd / 2, nfl = t.a5 * hw, nch = (nfl + 255) / 256;
-      const size_t n1 = (size_t)A.kv_len + 1;
-      const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + t.a3) * n1 * hd) + (size_t)t.a4 * hw;
-      const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + t.a3) * n1 * hd) + (size_t)t.a4 * hw;
-      float* kd = b.xs + kv_stage_k_off(A.hidden);
-      float* vd = b.scr + kv_stage_v_off(hd);
-#pragma unroll
-      for (int k = 0; k < kKvStageDma; ++k) {
-        int c = (wave - 1) + (kWaves - 1) * k;
-        c = c < 2 * nch ? c : 2 * nch - 1;
-        const bool isv = c >= nch;
-        const int cc = isv ? c - nch : c;
-        int f = cc * 256 + lane * 4;
-        f = f < nfl ? f : nfl - 4;
-        __builtin_amdgcn_global_load_lds((gvp)((isv ? vs : ks) + f), (lvp)((isv ? vd : kd) + cc * 256), 16, 0, 0);
-      }
+      kv_stage_dma(A, b, t.layer, t.a3, t.a4, t.a5, wave - 1);
     }
   };
   return run_gemv<kRingQKV>(
@@ -1258,8 +1267,8 @@ __device__ __forceinline__ void attn_finish(const EngineArgs& A, Blk& b, const T
 }
 
 template <int HD>
-__device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, const TaskDesc& t) {
-  constexpr int NKS = HD / 32, NCT = HD / 16, ps = HD + 4, SS = 4 * ps;
+__device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, const TaskDesc& t, bool self_stage) {
+  constexpr int NKS = HD / 32, NCT = HD / 16;
   const LayerDesc& L = A.layers[t.layer];
   const int r = A.nq / A.nkv, g = t.a0;
   const int p0 = t.u0, np = t.u1 - t.u0, c = t.a3;
@@ -1268,8 +1277,10 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
   const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
   uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden));  // [np][HD]
   uint16_t* Vs = reinterpret_cast<uint16_t*>(b.scr + kv_stage_v_off(HD));       // [np][HD]
-  // this wave's LDS DMA of the staged rows (issued during the QKV task) has landed; the
-  // barrier in the wait publishes it to the other waves
+  // the cached rows were copied into LDS by the QKV task just before this one, or, in a launch
+  // that does not run that task, are copied here; this wave's DMA has landed once vmcnt is 0,
+  // and the barrier in the wait publishes it to the other waves
+  if (self_stage && wave > 0) kv_stage_dma(A, b, t.layer, g, p0, c, wave - 1);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   if (!wait_deps(A, b, t)) return false;
   // every wave loads q~ in B-operand order itself: lane L of k-step ks holds head L % 16,
@@ -1946,23 +1957,35 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   const uint32_t xcc = xcc_id();
   const int wg = blockIdx.x;
   const int rq = A.nkv > 0 ? A.nq / A.nkv : 1;
-  for (int ti = A.wg_begin[wg]; ti < A.wg_begin[wg + 1]; ++ti) {
+  // a launch runs the tasks of stages [stage_lo, stage_hi) of this workgroup's list; a step is
+  // one launch of all stages, or launches of consecutive ranges in order (every dependency
+  // lies in an earlier stage, so a one-stage launch never waits on its own tasks)
+  const bool all_stages = A.stage_lo == 0 && A.stage_hi == A.n_stages;
+  int ti0 = A.wg_begin[wg], ti1 = A.wg_begin[wg + 1];
+  if (!all_stages) {
+    const int32_t* sf = A.stage_first + (size_t)wg * (A.n_stages + 1);
+    ti0 = sf[A.stage_lo];
+    ti1 = sf[A.stage_hi];
+  }
+  for (int ti = ti0; ti < ti1; ++ti) {
     const TaskDesc t = A.tasks[ti];
     const uint32_t t0 = (uint32_t)now();
     bool ok = true, gemv = true;
     int sig = t.signal;
     if constexpr (!MLA) {
       switch (t.type) {
-        case T_QKV: ok = t.a5 > 0 ? task_qkv<true>(A, b, t) : task_qkv<false>(A, b, t); break;
+        // K/V rows pass from a QKV task to the attention split after it through LDS only when
+        // one launch runs both (a launch of all stages)
+        case T_QKV: ok = (t.a5 > 0 && all_stages) ? task_qkv<true>(A, b, t) : task_qkv<false>(A, b, t); break;
         case T_ATTN:
           gemv = false;
           if (t.a3 > 0) {
             gemv = true;  // wave 0 alone stores the partial
             switch (A.hd) {
-              case 32: ok = task_attn_mfma<32>(A, b, t); break;
-              case 64: ok = task_attn_mfma<64>(A, b, t); break;
-              case 128: ok = task_attn_mfma<128>(A, b, t); break;
-              default: ok = task_attn_mfma<256>(A, b, t); break;
+              case 32: ok = task_attn_mfma<32>(A, b, t, !all_stages); break;
+              case 64: ok = task_attn_mfma<64>(A, b, t, !all_stages); break;
+              case 128: ok = task_attn_mfma<128>(A, b, t, !all_stages); break;
+              default: ok = task_attn_mfma<256>(A, b, t, !all_stages); break;
             }
           }
           else ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
@@ -2010,10 +2033,10 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       lg->t_streamed = b.t_streamed;
     }
   }
-  // the last workgroup to finish advances the epoch for the next step
+  // the last workgroup to finish the step's last launch advances the epoch for the next step
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && A.stage_hi == A.n_stages) {
     const uint32_t d = add_agent(A.ctl + CTL_DONE, 1u);
     if (d == (uint32_t)A.n_wg - 1u) {
       st_agent(A.ctl + CTL_DONE, 0u);
@@ -2032,7 +2055,8 @@ static const void* engine_fn(int arch) {
   return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, hipStream_t stream) {
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
+                                                                         bool cooperative, hipStream_t stream) {
   static int configured_lds[2] = {-1, -1};
   const int k = args->arch == 0 ? 0 : 1;
   if (configured_lds[k] < lds_bytes) {
@@ -2041,6 +2065,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
     configured_lds[k] = lds_bytes;
   }
   void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
+  if (!cooperative)  // one stage: no task waits on another of the same launch
+    return hipLaunchKernel(engine_fn(args->arch), dim3(n_wg), dim3(dec::kThreads), kargs, (size_t)lds_bytes, stream);
   return hipLaunchCooperativeKernel(engine_fn(args->arch), dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
 }
 

@@ -140,6 +140,7 @@ struct EngineArgs {
   char* ws;                    // workspace base
   const TaskDesc* tasks;
   const int32_t* wg_begin;     // [n_wg + 1] task ranges per workgroup
+  const int32_t* stage_first;  // [n_wg][n_stages + 1]: first task of each stage in a workgroup's list
   const DepEntry* deps;
   const uint64_t* wptr;        // bound weight pointers
   const LayerDesc* layers;
@@ -157,6 +158,8 @@ struct EngineArgs {
   int32_t ql, kl, dn, dr, dv;
   int32_t n_routed, n_shared, top_k, eff;
   int32_t kv_len, n_wg, rope_half, w_final_norm, w_lm_head, x_final;
+  int32_t n_stages;            // stages of the plan
+  int32_t stage_lo, stage_hi;  // this launch runs the tasks of stages [stage_lo, stage_hi)
   int32_t xs_floats;           // LDS floats reserved for the staged input vector
   uint32_t act_bytes;          // size of the activation region
   int32_t gs_floats;           // LDS floats reserved for norm gains

@@ -584,6 +584,25 @@ struct Builder {
     }
     P.wg_begin[n_wg] = (int)P.tasks.size();
     P.n_log = next_id;
+    // number the stages that hold tasks 0, 1, ...; then, per workgroup, where each stage's
+    // tasks begin in its list (lists are in stage order), so that a launch can run a range of
+    // stages only
+    {
+      std::vector<int> used;
+      for (auto& i : P.info) used.push_back(i.stage);
+      std::sort(used.begin(), used.end());
+      used.erase(std::unique(used.begin(), used.end()), used.end());
+      for (auto& i : P.info) i.stage = (int32_t)(std::lower_bound(used.begin(), used.end(), i.stage) - used.begin());
+      P.n_stages = (int32_t)used.size();
+    }
+    P.stage_first.assign((size_t)n_wg * (P.n_stages + 1), 0);
+    for (int w = 0; w < n_wg; ++w) {
+      int i = P.wg_begin[w];
+      for (int sg = 0; sg <= P.n_stages; ++sg) {
+        while (i < P.wg_begin[w + 1] && P.info[i].stage < sg) ++i;
+        P.stage_first[(size_t)w * (P.n_stages + 1) + sg] = i;
+      }
+    }
 
     // RoPE table at the step's position, in double precision
     const int rope_dim = (s.arch == DEC_ARCH_GQA) ? s.head_dim : s.qk_rope;
@@ -621,6 +640,7 @@ struct Builder {
     P.off_counters = take((int64_t)P.counter_total.size() * kCounterStride * 4);
     P.off_tasks = take((int64_t)P.tasks.size() * sizeof(TaskDesc));
     P.off_wgb = take((int64_t)(n_wg + 1) * 4);
+    P.off_stf = take((int64_t)P.stage_first.size() * 4);
     P.off_deps = take((int64_t)std::max<size_t>(P.deps.size(), 1) * sizeof(DepEntry));
     P.off_wptr = take((int64_t)P.weights.size() * 8);
     P.off_layers = take((int64_t)P.layers.size() * sizeof(LayerDesc));

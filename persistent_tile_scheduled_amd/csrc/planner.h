@@ -40,6 +40,8 @@ struct PlanData {
   std::vector<TaskDesc> tasks;        // grouped by workgroup, in list order
   std::vector<TaskInfo> info;         // parallel to tasks
   std::vector<int32_t> wg_begin;      // n_wg + 1
+  int32_t n_stages = 0;
+  std::vector<int32_t> stage_first;   // [n_wg][n_stages + 1]: first task index of each stage
   std::vector<DepEntry> deps;
   std::vector<uint32_t> counter_total;
   std::vector<LayerDesc> layers;
@@ -53,7 +55,7 @@ struct PlanData {
   float attn_scale_log2 = 0.f;
 
   // workspace layout (bytes)
-  int64_t off_ctl = 0, off_counters = 0, off_tasks = 0, off_wgb = 0, off_deps = 0,
+  int64_t off_ctl = 0, off_counters = 0, off_tasks = 0, off_wgb = 0, off_stf = 0, off_deps = 0,
           off_wptr = 0, off_layers = 0, off_rope = 0, off_log = 0, off_act = 0, ws_bytes = 0;
   int64_t act_floats = 0;
 

@@ -44,18 +44,48 @@ class DecodeEngine:
         out_n = cfg["vocab"] if cfg.get("vocab", 0) > 0 else cfg["hidden"]
         self.out = torch.empty(out_n, dtype=torch.float32, device="cuda")
 
-    def step(self, x, kv, out=None):
-        """One decode step: x bf16 [hidden], kv bf16 cache (written at slot kv_len)."""
+    def _check_io(self, x, kv, out):
         torch = self.torch
-        out = self.out if out is None else out
         if x.dtype != torch.bfloat16 or x.numel() * 2 != self.sizes["x_bytes"] or not x.is_contiguous():
             raise ValueError("x must be a contiguous bf16 vector of length hidden")
         if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
             raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
         if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"]:
             raise ValueError("out must be fp32 of length vocab (or hidden)")
+
+    def step(self, x, kv, out=None):
+        """One decode step: x bf16 [hidden], kv bf16 cache (written at slot kv_len)."""
+        out = self.out if out is None else out
+        self._check_io(x, kv, out)
         self.plan.step(x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.stream.cuda_stream)
         return out
+
+    @property
+    def n_stages(self) -> int:
+        return self.plan.n_stages()
+
+    def step_stages(self, x, kv, out=None, stream=None):
+        """The same step as one launch per stage (the launch-per-operator baseline), on
+        `stream` (default: the engine's stream)."""
+        out = self.out if out is None else out
+        self._check_io(x, kv, out)
+        h = (self.stream if stream is None else stream).cuda_stream
+        for sg in range(self.plan.n_stages()):
+            self.plan.step_stages(x.data_ptr(), kv.data_ptr(), out.data_ptr(), sg, sg + 1, h)
+        return out
+
+    def capture_stages(self, x, kv, out=None):
+        """A torch CUDA (HIP) graph of one step's per-stage launches; replay() runs a step."""
+        torch = self.torch
+        out = self.out if out is None else out
+        self._check_io(x, kv, out)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(self.stream)
+        with torch.cuda.graph(g, stream=side):
+            self.step_stages(x, kv, out, stream=side)
+        self.stream.wait_stream(side)
+        return g
 
     def status(self):
         self.plan.status(self.stream.cuda_stream)

@@ -232,6 +232,29 @@ def test_lists_in_stage_order_and_deps_point_back():
             assert total == (1 if n_sig == 0 else n_sig)
 
 
+@pytest.mark.parametrize("name", ["tiny", "8b_4k", "mla_small", "moe_small"])
+def test_stage_count_for_stage_launches(name):
+    """dec_step_stages launches stage ranges: the plan's stage count covers every task's
+    stage, every stage holds tasks, and a one-stage launch never waits on its own tasks
+    (the dependency check above, over all configurations' stage numbers)."""
+    p, _ = plan(name)
+    tasks = p.tasks()
+    ns = p.n_stages()
+    stages = {t["stage"] for t in tasks}
+    assert ns == max(stages) + 1
+    assert stages == set(range(ns))
+    producers = collections.defaultdict(list)
+    for t in tasks:
+        for c in (t["signal"], t["signal2"]):
+            if c >= 0:
+                producers[c].append(t["stage"])
+    deps = p.deps()
+    for t in tasks:
+        for k in range(t["n_deps"]):
+            c, _ = deps[t["dep_first"] + k]
+            assert max(producers[c]) < t["stage"]
+
+
 def test_chiplet_placement_8b():
     """Each KV-head group's QKV rows and attention splits run on the workgroups of one XCD."""
     p, cfg = plan("8b_4k")
