@@ -132,6 +132,49 @@ def cpu_baseline(cfg, w, x, kv, eng=None):
                       + (f" + final norm and LM head ({(t2 - t1):.2f} s)" if has_head else "")}
 
 
+def generation(args, cfg, w, kv):
+    """Greedy generation with one plan for the largest position: T steps issued back to back,
+    each at the position and with the token the previous step left in the device state."""
+    import torch
+    import workloads
+    from persistent_tile_scheduled_amd.engine import DecodeEngine
+
+    T, W = args.generate, args.warmup
+    n = cfg["kv_len"]
+    if T + W > n:
+        raise SystemExit("--generate T needs T + warmup <= kv_len")
+    if cfg.get("vocab", 0) > 0:
+        w["embed"] = workloads.generate_embedding(cfg, seed=args.seed, device="cuda")
+    eng = DecodeEngine(cfg, w, max_len=n)
+    p0 = n - T - W
+    eng.set_state(p0, 0)
+    for _ in range(W):
+        eng.step_dynamic(kv)
+    torch.cuda.synchronize()
+    eng.status()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(eng.stream)
+    for _ in range(T):
+        eng.step_dynamic(kv)
+    b.record(eng.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.status()
+    st = eng.read_state()
+    assert st[0] == n and st[2] == T + W, st
+    us = wall * 1e6 / T
+    print(json.dumps({
+        "metric": "greedy generation latency (us/token), steps issued back to back",
+        "value": round(us, 2), "unit": "us/token", "n_gpus": 1, "steps": T, "warmup": W,
+        "higher_is_better": False, "tokens_per_s": round(1e6 / us, 1),
+        "gpu_us_per_token": round(a.elapsed_time(b) * 1e3 / T, 2),
+        "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
+                   "positions": [n - T, n - 1], "batch": 1},
+        "launch": "dynamic plan (max_len = kv_len), one launch per token, no host work between tokens",
+        "dtype": "bf16", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +186,9 @@ def main():
     ap.add_argument("--launch", choices=["persistent", "stages", "graph"], default="persistent",
                     help="persistent: the step as one engine launch (the product); stages: one launch per "
                          "stage of the same tasks; graph: those launches replayed from a HIP graph")
+    ap.add_argument("--generate", type=int, default=0, metavar="T",
+                    help="time T greedy steps of a plan with a per-step length, issued back to back "
+                         "(positions kv_len - T .. kv_len - 1, each step's token from the last)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -163,6 +209,9 @@ def main():
     cfg = workloads.get_config(args.config)
     print(f"[bench] generating {args.config} inputs on cuda:0", file=sys.stderr, flush=True)
     w, x, kv = workloads.generate(cfg, seed=args.seed, device="cuda")
+    if args.generate:
+        generation(args, cfg, w, kv)
+        return
     eng = DecodeEngine(cfg, w)
     alg_bytes = eng.sizes["algorithmic_bytes_per_step"]
     stream = eng.stream

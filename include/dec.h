@@ -206,8 +206,44 @@ int64_t dec_plan_n_stages(const struct dec_plan* plan);
 dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo,
                            int32_t stage_hi, void* stream);
 
-/* Synchronise `stream` and read the sticky device status word: DEC_OK or DEC_E_TIMEOUT
- * (the failing task id is in dec_last_error()). */
+/* ---- a plan whose length is read per step (GQA models) ----
+ * The pages fix every shape ahead of time, while the cache grows by one position per token
+ * (Static Compilation page, sections 5.5 and 7.1: static shapes against a growing KV cache;
+ * TileRT audit page: any shape change means a rebuild). This plan is built once for a largest
+ * position max_len; each step reads its position from device memory, so one plan and one
+ * bound workspace serve a whole generation.
+ *
+ * dec_plan_create_dynamic: as dec_plan_create_for (dev == NULL: the current device, which must
+ * be gfx950), with kv_len replaced by max_len. The attention split count is planned for
+ * max_len; at a shorter position the same splits are shorter (a split may be empty and
+ * contributes nothing). dec_plan_sizes reports kv_bytes for max_len + 1 slots and the
+ * algorithmic bytes of a step at position max_len. When vocab > 0 the weight list ends with
+ * "embed" bf16 [vocab][hidden], the token embedding. Errors: as dec_plan_create_for; SHAPE for
+ * the latent-attention (MLA, MoE) families, whose plans have a fixed length.
+ *
+ * dec_step_dynamic: one step, ONE kernel launch on `stream`.
+ *   state : device int32[4], 16-byte aligned, caller-owned: {position p, token, steps, 0}.
+ *           The step reads p (0 <= p <= max_len): positions [0, p) of the cache are read and
+ *           slot p is written, with RoPE at position p. When x is NULL the input vector is
+ *           the embedding row of `token` (0 <= token < vocab). At the end of the step the
+ *           kernel writes p + 1 to state[0], adds 1 to state[2] and, when vocab > 0, writes
+ *           the greedy choice (the index of the largest logit, the lowest among equals) to
+ *           state[1]. Consecutive calls therefore run a greedy generation loop on the device
+ *           with no host work between tokens.
+ *   x     : bf16 [hidden] or NULL (needs vocab > 0).
+ *   kv    : bf16 [n_layers][2][n_kv_heads][max_len + 1][head_dim].
+ *   out   : as dec_step.
+ * An out-of-range position or token makes the whole step do nothing (state unchanged); the
+ * sticky status then reports DEC_E_CAPACITY with the values read (dec_plan_status).
+ * dec_step and dec_step_stages reject these plans, and dec_step_dynamic other plans (INVAL).
+ * Errors: UNBOUND, INVAL (null kv/out/state, x NULL without an embedding, misalignment), HIP. */
+dec_status dec_plan_create_dynamic(const dec_model_shape* shape, int64_t max_len, const dec_device_info* dev,
+                                   struct dec_plan** out);
+dec_status dec_step_dynamic(struct dec_plan* plan, const void* x, void* kv, void* out, int32_t* state, void* stream);
+
+/* Synchronise `stream` and read the sticky device status word: DEC_OK, DEC_E_TIMEOUT (the
+ * failing task id is in dec_last_error()) or DEC_E_CAPACITY (a dec_step_dynamic state out of
+ * range). */
 dec_status dec_plan_status(struct dec_plan* plan, void* stream);
 /* Re-zero counters, epoch and status (after a timeout). */
 dec_status dec_plan_reset(struct dec_plan* plan, void* stream);

@@ -99,6 +99,8 @@ def lib() -> C.CDLL:
         "dec_plan_bind": (C.c_int, [P, C.POINTER(P), C.c_int64, P, C.c_int64, P]),
         "dec_step": (C.c_int, [P, P, P, P, P]),
         "dec_plan_n_stages": (C.c_int64, [P]),
+        "dec_plan_create_dynamic": (C.c_int, [C.POINTER(ModelShape), C.c_int64, C.POINTER(DeviceInfo), C.POINTER(P)]),
+        "dec_step_dynamic": (C.c_int, [P, P, P, P, P, P]),
         "dec_step_stages": (C.c_int, [P, P, P, P, C.c_int32, C.c_int32, P]),
         "dec_plan_status": (C.c_int, [P, P]),
         "dec_plan_reset": (C.c_int, [P, P]),
@@ -117,7 +119,8 @@ ABI_SYMBOLS = ["dec_last_error", "dec_device_query", "dec_plan_create", "dec_pla
                "dec_plan_n_weights", "dec_plan_weight_desc", "dec_plan_sizes", "dec_plan_n_tasks", "dec_plan_tasks",
                "dec_plan_n_deps", "dec_plan_deps", "dec_plan_n_counters", "dec_plan_n_buffers",
                "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_step", "dec_plan_n_stages",
-               "dec_step_stages", "dec_plan_status", "dec_plan_reset", "dec_plan_set_watchdog"]
+               "dec_step_stages", "dec_plan_create_dynamic", "dec_step_dynamic", "dec_plan_status",
+               "dec_plan_reset", "dec_plan_set_watchdog"]
 
 
 def _check(status: int):
@@ -152,7 +155,10 @@ def device_query() -> DeviceInfo:
 class Plan:
     """Owner of one dec_plan (host object). All device memory belongs to the caller."""
 
-    def __init__(self, cfg_or_shape, kv_len: Optional[int] = None, device: Optional[DeviceInfo] = None):
+    def __init__(self, cfg_or_shape, kv_len: Optional[int] = None, device: Optional[DeviceInfo] = None,
+                 max_len: Optional[int] = None):
+        """A plan for one kv_len, or, with max_len, a plan whose position is read per step
+        (dec_plan_create_dynamic)."""
         L = lib()
         if isinstance(cfg_or_shape, dict):
             self.shape = shape_from_config(cfg_or_shape)
@@ -160,9 +166,13 @@ class Plan:
                 kv_len = cfg_or_shape["kv_len"]
         else:
             self.shape = cfg_or_shape
-        self.kv_len = int(kv_len)
+        self.dynamic = max_len is not None
+        self.kv_len = int(max_len if self.dynamic else kv_len)
         h = C.c_void_p()
-        if device is None:
+        if self.dynamic:
+            dev = C.byref(device) if device is not None else None
+            _check(L.dec_plan_create_dynamic(C.byref(self.shape), self.kv_len, dev, C.byref(h)))
+        elif device is None:
             _check(L.dec_plan_create(C.byref(self.shape), self.kv_len, C.byref(h)))
         else:
             _check(L.dec_plan_create_for(C.byref(self.shape), self.kv_len, C.byref(device), C.byref(h)))
@@ -244,6 +254,12 @@ class Plan:
     def step_stages(self, x_ptr: int, kv_ptr: int, out_ptr: int, stage_lo: int, stage_hi: int, stream: int = 0):
         _check(lib().dec_step_stages(self.h, C.c_void_p(int(x_ptr)), C.c_void_p(int(kv_ptr)), C.c_void_p(int(out_ptr)),
                                      int(stage_lo), int(stage_hi), C.c_void_p(int(stream))))
+
+    def step_dynamic(self, x_ptr: int, kv_ptr: int, out_ptr: int, state_ptr: int, stream: int = 0):
+        """x_ptr 0: start from the embedding row of the state's token."""
+        x = C.c_void_p(int(x_ptr)) if x_ptr else None
+        _check(lib().dec_step_dynamic(self.h, x, C.c_void_p(int(kv_ptr)), C.c_void_p(int(out_ptr)),
+                                      C.c_void_p(int(state_ptr)), C.c_void_p(int(stream))))
 
     def status(self, stream: int = 0):
         _check(lib().dec_plan_status(self.h, C.c_void_p(int(stream))))

@@ -85,6 +85,9 @@ void fill_args(dec_plan* p) {
   a.n_stages = P.n_stages;
   a.stage_lo = 0;
   a.stage_hi = P.n_stages;
+  a.state = nullptr;
+  a.kv_cap = (int32_t)(P.kv_len + 1);
+  a.w_embed = P.w_embed;
   a.act_bytes = (uint32_t)(P.act_floats * 4);
   a.gs_floats = (int32_t)P.gs_floats;
   a.eps = s.rms_eps;
@@ -108,6 +111,7 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   if (!x || !kv || !out) return fail(DEC_E_INVAL, "null x/kv/out");
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
+  if (plan->P.dynamic) return fail(DEC_E_INVAL, "a plan with a per-step length runs with dec_step_dynamic");
   if (lo < 0 || hi > plan->P.n_stages || lo >= hi)
     return fail(DEC_E_INVAL, "stage range [" + std::to_string(lo) + ", " + std::to_string(hi) + ") not inside [0, " +
                                  std::to_string(plan->P.n_stages) + ")");
@@ -117,6 +121,7 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   plan->args.watchdog_ticks = plan->watchdog_us * 100;
   plan->args.stage_lo = lo;
   plan->args.stage_hi = hi;
+  plan->args.state = nullptr;
   hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, hi - lo > 1,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -249,7 +254,9 @@ dec_status dec_plan_tasks(const dec_plan* plan, dec_task_desc* buf, int64_t cap,
     d.signal = t.signal;
     d.signal2 = t.signal2;
     d.aux2 = t.a2;
-    d.kv_staged = (t.type == dec::T_QKV) ? t.a5 : (t.type == dec::T_ATTN) ? t.a3 : 0;
+    d.kv_staged = (t.type == dec::T_QKV && t.a5 > 0)    ? dec::split_cached(plan->P.kv_len, t.a4, t.a5)
+                  : (t.type == dec::T_ATTN && t.a3 > 0) ? dec::split_cached(plan->P.kv_len, t.a1, t.a2)
+                                                        : 0;
   }
   return DEC_OK;
 }
@@ -339,6 +346,53 @@ dec_status dec_step(dec_plan* plan, const void* x, void* kv, void* out, void* st
 
 int64_t dec_plan_n_stages(const dec_plan* plan) { return plan ? (int64_t)plan->P.n_stages : -1; }
 
+dec_status dec_plan_create_dynamic(const dec_model_shape* shape, int64_t max_len, const dec_device_info* dev,
+                                   dec_plan** out) {
+  if (!shape || !out) return fail(DEC_E_INVAL, "null argument");
+  *out = nullptr;
+  dec_device_info cur;
+  if (!dev) {
+    dec_status st = dec_device_query(&cur);
+    if (st != DEC_OK) return st;
+    if (cur.gfx_arch != 950) return fail(DEC_E_DEVICE, "current device is gfx" + std::to_string(cur.gfx_arch) + ", need gfx950");
+    dev = &cur;
+  }
+  dec_plan* p = new dec_plan();
+  std::string err;
+  dec_status st = dec::build_plan(*shape, max_len, *dev, &p->P, &err, true);
+  if (st != DEC_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *out = p;
+  return DEC_OK;
+}
+
+dec_status dec_step_dynamic(dec_plan* plan, const void* x, void* kv, void* out, int32_t* state, void* stream) {
+  if (!plan) return fail(DEC_E_INVAL, "null plan");
+  if (!plan->bound) return fail(DEC_E_UNBOUND, "step before dec_plan_bind");
+  if (!plan->P.dynamic) return fail(DEC_E_INVAL, "dec_step_dynamic needs a plan from dec_plan_create_dynamic");
+  if (!kv || !out || !state) return fail(DEC_E_INVAL, "null kv/out/state");
+  if (!x && plan->P.w_embed < 0) return fail(DEC_E_INVAL, "no input vector and no token embedding (vocab == 0)");
+  if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4 ||
+      reinterpret_cast<uintptr_t>(state) % 16)
+    return fail(DEC_E_INVAL, "x must be 8-byte, kv and state 16-byte and out 4-byte aligned");
+  plan->args.x = static_cast<const uint16_t*>(x);
+  plan->args.kv = static_cast<uint16_t*>(kv);
+  plan->args.out = static_cast<float*>(out);
+  plan->args.watchdog_ticks = plan->watchdog_us * 100;
+  plan->args.stage_lo = 0;
+  plan->args.stage_hi = plan->P.n_stages;
+  plan->args.state = state;
+  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, true, reinterpret_cast<hipStream_t>(stream));
+  plan->args.state = nullptr;
+  if (e != hipSuccess) {
+    if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");
+    return hip_fail(e, "engine launch");
+  }
+  return DEC_OK;
+}
+
 dec_status dec_step_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo, int32_t stage_hi,
                            void* stream) {
   return launch_stages(plan, x, kv, out, stage_lo, stage_hi, stream);
@@ -355,6 +409,9 @@ dec_status dec_plan_status(dec_plan* plan, void* stream) {
   if (st[0] == 7u)
     return fail(DEC_E_TIMEOUT, "watchdog: task " + std::to_string(st[1]) + " timed out waiting on counter " +
                                    std::to_string(st[2]) + " (value " + std::to_string(st[3]) + ")");
+  if (st[0] == 8u)
+    return fail(DEC_E_CAPACITY, "step state out of range: position " + std::to_string((int32_t)st[1]) + " (largest " +
+                                    std::to_string(plan->P.kv_len) + "), token " + std::to_string((int32_t)st[2]));
   if (st[0] != 0u) return fail(DEC_E_PLAN, "unknown device status " + std::to_string(st[0]));
   return DEC_OK;
 }

@@ -185,7 +185,14 @@ struct Blk {
   int* xoffp;     // LDS: per-row input offsets of the current GEMV task
   float* gs;      // LDS: norm gains (bf16) of the current task
   float* actp;    // the activation region (generic pointer, for LDS DMA)
+  int n;                // the step's position: cached positions [0, n), the new token's slot n
+  const uint16_t* x;    // the step's input vector (bf16 [hidden])
+  const float* rope;    // RoPE (cos, sin) row of position n
 };
+
+// Positions [split_pos(n, sp, S), split_pos(n, sp + 1, S)) of attention split sp of S over
+// the positions 0..n (the planner cuts static plans the same way).
+__device__ __forceinline__ int split_pos(int n, int sp, int S) { return (int)(((int64_t)n + 1) * sp / S); }
 
 // Wait until every dependency counter of `t` has reached this step's target. Wave 0 polls
 // (one lane per counter); the other waves wait at the barrier with their loads in flight.
@@ -668,7 +675,8 @@ struct RmQKV {
 __device__ __forceinline__ void kv_stage_dma(const EngineArgs& A, Blk& b, int layer, int g, int p0, int rows, int slot) {
   const int lane = threadIdx.x & 63, hd = A.hd;
   const int hw = hd / 2, nfl = rows * hw, nch = (nfl + 255) / 256;
-  const size_t n1 = (size_t)A.kv_len + 1;
+  if (rows <= 0) return;
+  const size_t n1 = (size_t)A.kv_cap;
   const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 0) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
   const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 1) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
   float* kd = b.xs + kv_stage_k_off(A.hidden);
@@ -695,21 +703,22 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
     if constexpr (KV) {
       const int wave = wave_id();
       if (wave == 0) return;  // wave 0 stages the input vector: no loads ahead of it
-      kv_stage_dma(A, b, t.layer, t.a3, t.a4, t.a5, wave - 1);
+      const int p0 = split_pos(b.n, t.a4, t.a5), p1 = split_pos(b.n, t.a4 + 1, t.a5);
+      kv_stage_dma(A, b, t.layer, t.a3, p0, (p1 < b.n ? p1 : b.n) - p0, wave - 1);
     }
   };
   return run_gemv<kRingQKV>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, xin, A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] { stage_vec(b, xin, b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
-        const int n = A.kv_len;
-        const size_t lay = (size_t)2 * A.nkv * (n + 1) * hd;  // cache elements per layer
+        const int n = b.n;
+        const size_t lay = (size_t)2 * A.nkv * A.kv_cap * hd;  // cache elements per layer
         const rsrc_t kvr = make_rsrc(A.kv + (size_t)t.layer * lay, (uint32_t)(lay * 2));
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
           float a = b.ys[2 * i], c = b.ys[2 * i + 1];
           if (slot <= r) {  // RoPE on q and k
-            const float cs = A.rope_cs[k], sn = A.rope_cs[A.rope_half + k];
+            const float cs = b.rope[k], sn = b.rope[A.rope_half + k];
             const float a2 = a * cs - c * sn;
             c = c * cs + a * sn;
             a = a2;
@@ -723,7 +732,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
             const uint32_t kn = (uint32_t)(L.act[LA_KVNEW] + (sel * A.nkv + g) * hd);
             cst(b.act, (kn + k) * 4u, a);
             cst(b.act, (kn + k + hh) * 4u, c);
-            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * (n + 1) + n) * hd);
+            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * A.kv_cap + n) * hd);
             cst16(kvr, (row + k) * 2u, f2bf(a));
             cst16(kvr, (row + k + hh) * 2u, f2bf(c));
           }
@@ -796,9 +805,9 @@ template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   constexpr int GPW = 64 / LPP, NP = 3, PER_BLK = NP * GPW;
   const LayerDesc& L = A.layers[t.layer];
-  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = A.kv_len, n1 = n + 1;
+  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = b.n, n1 = A.kv_cap;
   const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
-  const int p0 = t.u0, np = t.u1 - t.u0;
+  const int p0 = split_pos(n, t.a1, t.a2), np = split_pos(n, t.a1 + 1, t.a2) - p0;
   const int q0 = p0 + wave_start(np, wave), q1 = p0 + wave_start(np, wave + 1);
   const int qc = q1 < n ? q1 : n;  // cached positions [q0, qc)
   const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd;
@@ -1018,7 +1027,7 @@ __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const Ta
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
-          const float res = xin >= 0 ? cld(b.act, (uint32_t)(xin + rr) * 4u) : bf16f(A.x[rr]);
+          const float res = xin >= 0 ? cld(b.act, (uint32_t)(xin + rr) * 4u) : bf16f(b.x[rr]);
           cst(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u, res + b.ys[i]);
         }
       });
@@ -1050,7 +1059,7 @@ __device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const 
 
 // Layer 0: h = x (widened), the accumulator the per-group O-projections add into.
 __device__ __forceinline__ bool task_hinit(const EngineArgs& A, Blk& b, const TaskDesc& t) {
-  for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) cst(b.act, (uint32_t)(t.a0 + t.u0 + i) * 4u, bf16f(A.x[t.u0 + i]));
+  for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads) cst(b.act, (uint32_t)(t.a0 + t.u0 + i) * 4u, bf16f(b.x[t.u0 + i]));
   return true;
 }
 
@@ -1089,6 +1098,16 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
       });
 }
 
+// Wave-wide (value, index) maximum, ties to the lower index; every lane ends with the result.
+__device__ __forceinline__ void best_pair(float& v, int& i) {
+#pragma unroll
+  for (int x = 1; x < 64; x <<= 1) {
+    const float ov = __shfl_xor(v, x, 64);
+    const int oi = __shfl_xor(i, x, 64);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
 __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const int K = A.hidden;
   const RmPlain rm{wp<uint16_t>(A, A.w_lm_head), K, t.u0};
@@ -1097,7 +1116,36 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
       [&] { stage_vec(b, A.x_final, nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) A.out[t.u0 + i] = b.ys[i];
+        if (A.state) {  // this task's largest logit (lowest index among equals) -> slot a0
+          float bv = -INFINITY;
+          int bi = 0x7fffffff;
+          for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
+            if (b.ys[i] > bv) { bv = b.ys[i]; bi = t.u0 + i; }
+          best_pair(bv, bi);
+          if (threadIdx.x == 0) {
+            cst(b.act, (uint32_t)(t.a1 + 2 * t.a0) * 4u, bv);
+            cst(b.act, (uint32_t)(t.a1 + 2 * t.a0 + 1) * 4u, __int_as_float(bi));
+          }
+        }
       });
+}
+
+// Greedy choice of the next token: the largest of the LM-head tasks' best logits (the lowest
+// index among equal values), written to the step state as the next step's token.
+__device__ __forceinline__ bool task_argmax(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  if (!wait_deps(A, b, t)) return false;
+  if (threadIdx.x < 64) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = threadIdx.x; i < t.a0; i += 64) {
+      const float v = cld(b.act, (uint32_t)(t.a1 + 2 * i) * 4u);
+      const int k = __float_as_int(cld(b.act, (uint32_t)(t.a1 + 2 * i + 1) * 4u));
+      if (v > bv || (v == bv && k < bi)) { bv = v; bi = k; }
+    }
+    best_pair(bv, bi);
+    if (threadIdx.x == 0) st_agent(reinterpret_cast<uint32_t*>(A.state) + 1, (uint32_t)(bi == 0x7fffffff ? 0 : bi));
+  }
+  return true;
 }
 
 
@@ -1271,7 +1319,8 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
   constexpr int NKS = HD / 32, NCT = HD / 16;
   const LayerDesc& L = A.layers[t.layer];
   const int r = A.nq / A.nkv, g = t.a0;
-  const int p0 = t.u0, np = t.u1 - t.u0, c = t.a3;
+  const int p0 = split_pos(b.n, t.a1, t.a2), p1 = split_pos(b.n, t.a1 + 1, t.a2), np = p1 - p0;
+  const int c = (p1 < b.n ? p1 : b.n) - p0;  // cached rows, staged in LDS; row c (if < np) is the new position
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // keeps lane-derived LDS addresses inside the task (not hoisted and spilled)
   const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
@@ -1293,7 +1342,7 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
     qb[ks] = cld4(b.act, qo + ks * 128u + 16u);
   }
   if (wave == 0 && c < np && lane < HD / 8) {  // row c: the new position, written by this step's QKV tasks
-    const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
+    const size_t n1 = (size_t)A.kv_cap, off = (size_t)(p0 + c) * HD + lane * 8;
     const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
     const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
     __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
@@ -1345,7 +1394,7 @@ __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const Ta
   const RmMlaA rm{wp<uint16_t>(A, L.w[LW_WQA]), wp<uint16_t>(A, L.w[LW_WKVA]), K, ql, t.u0};
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_X_IN], A.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] { stage_vec(b, L.act[LA_X_IN], b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int r = t.u0 + i;
@@ -1385,7 +1434,7 @@ __device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const Ta
             cst(b.act, (uint32_t)(L.act[LA_QNOPE] + h * dn + k + dn / 2) * 4u, c);
           } else {
             const int kk = k - dn / 2;
-            const float cs = A.rope_cs[kk], sn = A.rope_cs[A.rope_half + kk];
+            const float cs = b.rope[kk], sn = b.rope[A.rope_half + kk];
             const float a2 = a * cs - c * sn, c2 = c * cs + a * sn;
             cst(b.act, (uint32_t)(L.act[LA_QROPE] + h * dr + kk) * 4u, a2);
             cst(b.act, (uint32_t)(L.act[LA_QROPE] + h * dr + kk + dr / 2) * 4u, c2);
@@ -1400,10 +1449,10 @@ __device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const Ta
 // position kv_len as bf16. Also clears o (the W_UV tasks accumulate into it).
 __device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
-  const int kl = A.kl, dr = A.dr, KR = kl + dr, n = A.kv_len;
+  const int kl = A.kl, dr = A.dr, KR = kl + dr, n = b.n;
   if (!wait_deps(A, b, t)) return false;
   stage_vec(b, L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps);
-  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (n + 1) + n) * KR, (uint32_t)KR * 2u);
+  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * A.kv_cap + n) * KR, (uint32_t)KR * 2u);
   for (int i = threadIdx.x; i < kl; i += kThreads) {
     const float v = b.xs[i];
     cst(b.act, (uint32_t)(L.act[LA_KVNEW] + i) * 4u, v);
@@ -1412,7 +1461,7 @@ __device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, cons
   for (int k = threadIdx.x; k < dr / 2; k += kThreads) {
     const float a = cld(b.act, (uint32_t)(L.act[LA_KVA] + kl + k) * 4u);
     const float c = cld(b.act, (uint32_t)(L.act[LA_KVA] + kl + k + dr / 2) * 4u);
-    const float cs = A.rope_cs[k], sn = A.rope_cs[A.rope_half + k];
+    const float cs = b.rope[k], sn = b.rope[A.rope_half + k];
     const float a2 = a * cs - c * sn, c2 = c * cs + a * sn;
     cst(b.act, (uint32_t)(L.act[LA_KVNEW] + kl + k) * 4u, a2);
     cst(b.act, (uint32_t)(L.act[LA_KVNEW] + kl + k + dr / 2) * 4u, c2);
@@ -1483,9 +1532,9 @@ __device__ __forceinline__ bool task_mla_absorb(const EngineArgs& A, Blk& b, con
 __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int kl = A.kl, KR = kl + A.dr, KP = (KR + 31) & ~31, NKS = KP >> 5, nh = A.nq;
-  const int n = A.kv_len, p0 = t.u0, p1 = t.u1;
+  const int n = b.n, p0 = t.u0, p1 = t.u1;  // latent plans have a fixed length: the planned split
   const int wave = wave_id(), lane = threadIdx.x & 63, hl = lane & 15, g = lane >> 4;
-  const uint16_t* lat = A.kv + (size_t)t.layer * (n + 1) * KR;
+  const uint16_t* lat = A.kv + (size_t)t.layer * A.kv_cap * KR;
   u4* QL = reinterpret_cast<u4*>(b.xs);                                   // [NKS][2][64]
   uint16_t* LAT = reinterpret_cast<uint16_t*>(b.xs + NKS * 512);          // [kMlaChunk][KP]
   u4* PA = reinterpret_cast<u4*>(b.xs + NKS * 512 + kMlaChunk * KP / 2);  // [kMlaChunk/32][2][64]
@@ -1954,6 +2003,30 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   b.act = make_rsrc(A.act, A.act_bytes);
   b.epoch = ld_agent(A.ctl + CTL_EPOCH);
   b.t_ready = b.t_staged = b.t_streamed = 0;
+  b.n = A.kv_len;
+  b.x = A.x;
+  b.rope = A.rope_cs;
+  if (A.state) {
+    // the step's position (and, without an input vector, its token), written by the
+    // previous step's last workgroup or by the caller; every workgroup reads the same values
+    // and, if they are out of range, the whole step does nothing (sticky status 8)
+    const int n = (int)ld_agent(reinterpret_cast<const uint32_t*>(A.state));
+    const int tok = (int)ld_agent(reinterpret_cast<const uint32_t*>(A.state) + 1);
+    if (n < 0 || n > A.kv_len || (!A.x && (tok < 0 || tok >= A.vocab))) {
+      if (blockIdx.x == 0 && threadIdx.x == 0) {
+        uint32_t zero = 0;
+        if (__hip_atomic_compare_exchange_strong(A.ctl + CTL_STATUS, &zero, 8u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          st_agent(A.ctl + CTL_STATUS + 1, (uint32_t)n);
+          st_agent(A.ctl + CTL_STATUS + 2, (uint32_t)tok);
+        }
+      }
+      return;
+    }
+    b.n = n;
+    if (!A.x) b.x = wp<uint16_t>(A, A.w_embed) + (size_t)tok * A.hidden;
+    b.rope = A.rope_cs + (size_t)n * 2 * A.rope_half;
+  }
   const uint32_t xcc = xcc_id();
   const int wg = blockIdx.x;
   const int rq = A.nkv > 0 ? A.nq / A.nkv : 1;
@@ -1995,6 +2068,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_GATEUP: ok = task_gateup(A, b, t); break;
         case T_DOWN: ok = task_down<true>(A, b, t); break;
         case T_LMHEAD: ok = task_lmhead(A, b, t); break;
+        case T_ARGMAX: gemv = false; ok = task_argmax(A, b, t); break;
         default: ok = false; break;
       }
     } else {
@@ -2041,6 +2115,11 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
     if (d == (uint32_t)A.n_wg - 1u) {
       st_agent(A.ctl + CTL_DONE, 0u);
       add_agent(A.ctl + CTL_EPOCH, 1u);
+      if (A.state) {  // every workgroup has read the position: advance it for the next step
+        uint32_t* st = reinterpret_cast<uint32_t*>(A.state);
+        st_agent(st, (uint32_t)(b.n + 1));
+        st_agent(st + 2, ld_agent(st + 2) + 1u);
+      }
     }
   }
 }

@@ -55,6 +55,8 @@ enum TaskType : int32_t {
   T_OPROJ_G = 18,    // GQA: merge one KV group's attention splits + W_o rows x that group's columns,
                      // added into h with agent-scope atomics
   T_HINIT = 19,      // GQA layer 0: h = x (the accumulator the per-group O-projections add into)
+  T_ARGMAX = 20,     // greedy choice: the largest logit over the LM-head tasks' best (value,
+                     // index) pairs, written to the step state (length-per-step plans)
   T_NUM_TYPES
 };
 
@@ -147,7 +149,9 @@ struct EngineArgs {
   uint32_t* counters;
   uint32_t* ctl;
   TaskLog* log;
-  const float* rope_cs;        // cos[rope_half], sin[rope_half] at the step's position
+  const float* rope_cs;        // rows of (cos[rope_half], sin[rope_half]): one row, at the step's
+                               // position, or (length-per-step plans) one per position 0..max_len
+  int32_t* state;              // length-per-step plans: {position, token, steps, 0}; else null
   const uint16_t* x;           // step input, bf16 [hidden]
   uint16_t* kv;                // KV cache, bf16
   float* out;                  // logits / last hidden
@@ -159,6 +163,8 @@ struct EngineArgs {
   int32_t n_routed, n_shared, top_k, eff;
   int32_t kv_len, n_wg, rope_half, w_final_norm, w_lm_head, x_final;
   int32_t n_stages;            // stages of the plan
+  int32_t kv_cap;              // cache slots per (layer, K/V, head): kv_len + 1, or max_len + 1
+  int32_t w_embed;             // weight index of the token embedding (-1: none)
   int32_t stage_lo, stage_hi;  // this launch runs the tasks of stages [stage_lo, stage_hi)
   int32_t xs_floats;           // LDS floats reserved for the staged input vector
   uint32_t act_bytes;          // size of the activation region

@@ -47,7 +47,8 @@ struct PTask {
 
 struct Builder {
   const dec_model_shape& s;
-  int64_t n;  // kv_len
+  int64_t n;  // kv_len (dynamic plans: the largest position a step may have)
+  bool dyn;
   const dec_device_info& dev;
   PlanData& P;
   std::string& err;
@@ -62,8 +63,8 @@ struct Builder {
   int64_t scratch_floats = 1024;
   int64_t mla_lds = 0;        // LDS floats (after the header) the latent-attention tasks use
 
-  Builder(const dec_model_shape& s_, int64_t n_, const dec_device_info& d_, PlanData& p_, std::string& e_)
-      : s(s_), n(n_), dev(d_), P(p_), err(e_) {}
+  Builder(const dec_model_shape& s_, int64_t n_, bool dyn_, const dec_device_info& d_, PlanData& p_, std::string& e_)
+      : s(s_), n(n_), dyn(dyn_), dev(d_), P(p_), err(e_) {}
 
   int xcd(int w) const { return w % n_xcd; }
   // Completion counters of a stage: nsc of them, workgroup w signalling counter w % nsc (so a
@@ -260,14 +261,19 @@ struct Builder {
       add_weight("final_norm", DEC_DTYPE_BF16, {d});
       P.w_lm_head = (int)P.weights.size();
       add_weight("lm_head", DEC_DTYPE_BF16, {s.vocab, d});
+      if (dyn) {  // a step without an input vector starts from its token's embedding row
+        P.w_embed = (int)P.weights.size();
+        add_weight("embed", DEC_DTYPE_BF16, {s.vocab, d});
+      }
     }
   }
 
   // An attention split whose workgroup runs the same layer's QKV task just before it gets
-  // its cached K/V rows staged into LDS by that task (QKV: a3 = group, a4 = first position,
-  // a5 = rows; attention: a3 = rows staged). Only where both LDS regions are already there
-  // and the rows fit the fixed DMA count; the split's other rows (at most the new position)
-  // are loaded after the dependency wait.
+  // its cached K/V rows staged into LDS by that task (QKV: a3 = group, a4 = split index,
+  // a5 = split count; attention: a3 = 1). Only where both LDS regions are already there and
+  // the rows fit the fixed DMA count -- for a dynamic plan, the most rows a split has at any
+  // position up to the largest; the split's other rows (at most the new position) are loaded
+  // after the dependency wait.
   // The regions grow the LDS plan when the whole plan still fits the device; otherwise only
   // splits that fit the regions other stages already need are staged.
   void stage_attention_kv() {
@@ -275,8 +281,8 @@ struct Builder {
     const int64_t koff = kv_stage_k_off(s.hidden), voff = kv_stage_v_off(hd);
     auto candidate = [&](const TaskDesc& q, const TaskDesc& a) -> int64_t {  // LDS floats per region, or 0
       if (a.type != T_ATTN || q.type != T_QKV || q.layer != a.layer) return 0;
-      const int64_t cnt = std::min<int64_t>(a.u1, n) - a.u0;
-      if (cnt <= 0 || a.u1 - a.u0 - cnt > 1) return 0;
+      const int64_t cnt = dyn ? (n + 1 + a.a2 - 1) / a.a2 : (int64_t)split_cached(n, a.a1, a.a2);
+      if (cnt <= 0) return 0;
       if (2 * ((cnt * hd / 2 + 255) / 256) > (int64_t)(kWaves - 1) * kKvStageDma) return 0;
       // the matrix-core attention merges its waves below the V rows (kWaves x 4 x (hd + 4)
       // floats, the region's offset) and assembles the partial (r x (hd + 4)) below the K rows
@@ -301,9 +307,9 @@ struct Builder {
         const int64_t fl = candidate(q, a);
         if (fl == 0 || koff + fl > xs_floats_max || voff + fl > scratch_floats) continue;
         q.a3 = a.a0;
-        q.a4 = a.u0;
-        q.a5 = (int)(std::min<int64_t>(a.u1, n) - a.u0);
-        a.a3 = q.a5;
+        q.a4 = a.a1;
+        q.a5 = a.a2;
+        a.a3 = 1;
       }
   }
   // LDS floats of the GQA plan: header, staged vector, row results, row tables, gains, scratch
@@ -540,6 +546,8 @@ struct Builder {
     per_wg.assign(n_wg, {});
     P.shape = s;
     P.kv_len = n;
+    P.dynamic = dyn;
+    if (dyn && s.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "plans with a per-step length support the GQA family only", st);
     P.dev = dev;
     P.n_wg = n_wg;
     P.layers.assign(s.n_layers, LayerDesc{});
@@ -563,7 +571,22 @@ struct Builder {
     P.x_final = (int)x_in;
     if (s.vocab > 0) {
       ++stage;
-      spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
+      if (!dyn) {
+        spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
+      } else {
+        // each LM-head task also leaves its best (logit, index) in slot a0; one task then
+        // picks the step's token from those pairs
+        const int ctr_lm = counter(nsc);
+        int n_lm = 0;
+        std::vector<std::tuple<int, int, int>> parts;
+        spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { parts.emplace_back(w, a, b); });
+        const int64_t best = act("lm_best", 2LL * (int64_t)parts.size());
+        for (auto& pt : parts)
+          add(std::get<0>(pt), T_LMHEAD, s.n_layers, std::get<1>(pt), std::get<2>(pt), prev,
+              ctr_lm + slot(std::get<0>(pt)), -1, n_lm++, (int)best);
+        ++stage;
+        add(0, T_ARGMAX, s.n_layers, 0, 1, all_of(ctr_lm, nsc), -1, -1, n_lm, (int)best);
+      }
     }
 
     if (s.arch == DEC_ARCH_GQA) stage_attention_kv();
@@ -604,14 +627,20 @@ struct Builder {
       }
     }
 
-    // RoPE table at the step's position, in double precision
+    // RoPE table in double precision: the row of the step's position, or (dynamic) one row
+    // per position 0..max_len
     const int rope_dim = (s.arch == DEC_ARCH_GQA) ? s.head_dim : s.qk_rope;
     P.rope_half = rope_dim / 2;
-    P.rope_cs.assign(2 * P.rope_half, 0.f);
-    for (int i = 0; i < P.rope_half; ++i) {
-      long double ang = (long double)n * powl((long double)s.rope_theta, -2.0L * i / rope_dim);
-      P.rope_cs[i] = (float)cosl(ang);
-      P.rope_cs[P.rope_half + i] = (float)sinl(ang);
+    P.rope_rows = dyn ? (int32_t)(n + 1) : 1;
+    P.rope_cs.assign((size_t)P.rope_rows * 2 * P.rope_half, 0.f);
+    for (int64_t row = 0; row < P.rope_rows; ++row) {
+      const int64_t pos = dyn ? row : n;
+      float* cs = P.rope_cs.data() + (size_t)row * 2 * P.rope_half;
+      for (int i = 0; i < P.rope_half; ++i) {
+        long double ang = (long double)pos * powl((long double)s.rope_theta, -2.0L * i / rope_dim);
+        cs[i] = (float)cosl(ang);
+        cs[P.rope_half + i] = (float)sinl(ang);
+      }
     }
     const double qk = (s.arch == DEC_ARCH_GQA) ? s.head_dim : (s.qk_nope + s.qk_rope);
     P.attn_scale_log2 = (float)(1.0 / std::sqrt(qk) * 1.4426950408889634);
@@ -676,10 +705,10 @@ struct Builder {
 }  // namespace
 
 dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev, PlanData* out,
-                      std::string* err) {
+                      std::string* err, bool dynamic) {
   *out = PlanData{};
   dec_status st = DEC_OK;
-  Builder b(shape, kv_len, dev, *out, *err);
+  Builder b(shape, kv_len, dynamic, dev, *out, *err);
   if (!b.run(&st)) return st;
   return DEC_OK;
 }
@@ -698,8 +727,8 @@ std::string validate_plan(const PlanData& p) {
       const TaskDesc& a = p.tasks[i];
       if (a.type != T_ATTN || a.a3 == 0) continue;
       const TaskDesc* q = (i > p.wg_begin[w]) ? &p.tasks[i - 1] : nullptr;
-      if (!q || q->type != T_QKV || q->layer != a.layer || q->a3 != a.a0 || q->a4 != a.u0 || q->a5 != a.a3 ||
-          a.a3 < 0 || a.a3 > a.u1 - a.u0 || a.u0 + a.a3 > p.kv_len || a.u1 - a.u0 - a.a3 > 1) {
+      if (!q || q->type != T_QKV || q->layer != a.layer || q->a3 != a.a0 || q->a4 != a.a1 || q->a5 != a.a2 ||
+          a.a3 != 1 || a.u0 != split_begin(p.kv_len, a.a1, a.a2) || a.u1 != split_begin(p.kv_len, a.a1 + 1, a.a2)) {
         e << "task " << a.id << ": staged K/V rows without a matching QKV task";
         return e.str();
       }
@@ -751,6 +780,7 @@ std::string validate_plan(const PlanData& p) {
       case T_OPROJ: case T_OPROJ_G: case T_DOWN: case T_MOE_DOWN: case T_HINIT: return s.hidden;
       case T_GATEUP: return s.ffn;
       case T_LMHEAD: return s.vocab;
+      case T_ARGMAX: return 1;
       case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope;
       case T_MLA_B: return (int64_t)s.n_q_heads * (s.qk_nope / 2 + s.qk_rope / 2);
       case T_MLA_KVAPP: return (int64_t)s.kv_lora_rank + s.qk_rope;

@@ -51,7 +51,9 @@ struct PlanData {
   int64_t xs_floats = 0;              // LDS floats for the largest staged input vector
   int64_t gs_floats = 0;              // LDS floats for norm gains (bf16 pairs)
   int32_t rope_half = 0;
-  int32_t w_final_norm = -1, w_lm_head = -1, x_final = -1;
+  int32_t rope_rows = 1;              // rows of the RoPE table (positions 0..max_len when dynamic)
+  bool dynamic = false;               // the step's position is read from device memory
+  int32_t w_final_norm = -1, w_lm_head = -1, x_final = -1, w_embed = -1;
   float attn_scale_log2 = 0.f;
 
   // workspace layout (bytes)
@@ -63,8 +65,18 @@ struct PlanData {
 };
 
 // Validate the shape and build the plan. Returns DEC_OK or an error (message in *err).
+// dynamic: kv_len is the largest position a step may have (max_len); each step reads its
+// position (and, without an input vector, its token) from device memory.
 dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev,
-                      PlanData* out, std::string* err);
+                      PlanData* out, std::string* err, bool dynamic = false);
+
+// Positions [p0, p1) of attention split sp of S over the positions 0..n (n + 1 of them).
+inline int split_begin(int64_t n, int sp, int S) { return (int)((n + 1) * sp / S); }
+// Cached rows of that split (positions below n) an attention task can have staged in LDS.
+inline int split_cached(int64_t n, int sp, int S) {
+  const int p0 = split_begin(n, sp, S), p1 = split_begin(n, sp + 1, S);
+  return (int)std::min<int64_t>(p1, n) - p0;
+}
 
 // Structural checks of a built plan: list order vs stage order, producers before
 // consumers, counter totals, unit coverage. Returns an empty string when all hold.

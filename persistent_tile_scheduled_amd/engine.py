@@ -15,14 +15,17 @@ _TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32"}
 
 class DecodeEngine:
     def __init__(self, cfg: dict, weights: Dict[str, "object"], kv_len: Optional[int] = None,
-                 stream=None, watchdog_us: Optional[int] = None):
+                 stream=None, watchdog_us: Optional[int] = None, max_len: Optional[int] = None):
+        """A plan for kv_len (default: the config's), or, with max_len, a plan whose position
+        is read per step from a device state (step_dynamic)."""
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("DecodeEngine needs a GPU (gfx950); there is no CPU path")
         self.torch = torch
         self.cfg = cfg
-        self.kv_len = cfg["kv_len"] if kv_len is None else int(kv_len)
-        self.plan = B.Plan(cfg, self.kv_len)
+        self.dynamic = max_len is not None
+        self.kv_len = int(max_len) if self.dynamic else (cfg["kv_len"] if kv_len is None else int(kv_len))
+        self.plan = B.Plan(cfg, self.kv_len, max_len=max_len)
         if watchdog_us is not None:
             self.plan.set_watchdog(watchdog_us)
         self.descs = self.plan.weight_descs()
@@ -43,6 +46,32 @@ class DecodeEngine:
         self.buffers = self.plan.buffers()
         out_n = cfg["vocab"] if cfg.get("vocab", 0) > 0 else cfg["hidden"]
         self.out = torch.empty(out_n, dtype=torch.float32, device="cuda")
+        # {position, token, steps, 0}: read and advanced by every dynamic step
+        self.state = torch.zeros(4, dtype=torch.int32, device="cuda") if self.dynamic else None
+
+    def set_state(self, position: int, token: int = 0):
+        """Set the dynamic plan's next position and token (on the engine's stream)."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            self.state.copy_(torch.tensor([int(position), int(token), 0, 0], dtype=torch.int32), non_blocking=False)
+
+    def read_state(self):
+        self.stream.synchronize()
+        return [int(v) for v in self.state.cpu().tolist()]
+
+    def step_dynamic(self, kv, x=None, out=None):
+        """One step at the position in the device state (advanced by the step); without x the
+        input is the embedding row of the state's token, and the step leaves its greedy choice
+        there. No host synchronisation."""
+        torch = self.torch
+        out = self.out if out is None else out
+        if x is not None:
+            self._check_io(x, kv, out)
+        elif kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
+            raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+        self.plan.step_dynamic(0 if x is None else x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.state.data_ptr(),
+                               self.stream.cuda_stream)
+        return out
 
     def _check_io(self, x, kv, out):
         torch = self.torch

@@ -255,6 +255,48 @@ def test_stage_count_for_stage_launches(name):
             assert max(producers[c]) < t["stage"]
 
 
+@pytest.mark.parametrize("name,max_len", [("tiny", 200), ("small_gqa", 3000), ("8b_4k", 4096), ("8b_32k", 32768)])
+def test_dynamic_plan_layout(name, max_len):
+    """A plan with a per-step length: the fixed plan's weight list plus the token embedding
+    (when there is an LM head), the cache sized for max_len + 1 slots, the LM-head tasks
+    signalling one argmax task that comes last, and the attention splits planned over
+    max_len + 1 positions (staged in LDS where the largest split fits)."""
+    cfg = dict(workloads.get_config(name))
+    p = B.Plan(cfg, device=MI355X, max_len=max_len)
+    fixed = B.Plan(dict(cfg, kv_len=max_len), device=MI355X)
+    names = [d["name"] for d in p.weight_descs()]
+    want = [d["name"] for d in fixed.weight_descs()] + (["embed"] if cfg["vocab"] > 0 else [])
+    assert names == want
+    if cfg["vocab"] > 0:
+        e = p.weight_descs()[-1]
+        assert tuple(e["shape"]) == (cfg["vocab"], cfg["hidden"]) and e["dtype"] == "bf16"
+    sz = p.sizes()
+    assert sz["kv_bytes"] == 2 * cfg["n_layers"] * 2 * cfg["n_kv_heads"] * (max_len + 1) * cfg["head_dim"]
+    tasks = p.tasks()
+    am = [t for t in tasks if t["type"] == 20]
+    lm = [t for t in tasks if t["type"] == 6]
+    if cfg["vocab"] > 0:
+        assert len(am) == 1 and am[0]["stage"] == max(t["stage"] for t in tasks)
+        assert all(t["signal"] >= 0 for t in lm)
+        assert sorted(t["aux0"] for t in lm) == list(range(len(lm)))
+        assert am[0]["aux0"] == len(lm)
+    else:
+        assert not am
+    att = [t for t in tasks if t["type"] == 2]
+    ends = sorted((t["layer"], t["aux0"], t["unit_begin"], t["unit_end"]) for t in att if t["layer"] == 0)
+    assert max(e[3] for e in ends) == max_len + 1
+    if name in ("8b_4k", "small_gqa"):
+        assert any(t["kv_staged"] > 0 for t in att)
+
+
+def test_dynamic_plan_errors():
+    with pytest.raises(B.DecError) as ei:
+        B.Plan(workloads.get_config("mla_tiny"), device=MI355X, max_len=100)
+    assert ei.value.status == -2
+    with pytest.raises(B.DecError):
+        B.Plan(workloads.get_config("tiny"), device=MI355X, max_len=-1)
+
+
 def test_chiplet_placement_8b():
     """Each KV-head group's QKV rows and attention splits run on the workgroups of one XCD."""
     p, cfg = plan("8b_4k")

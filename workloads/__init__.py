@@ -208,6 +208,17 @@ def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = Non
     return weights, x, kv
 
 
+def generate_embedding(cfg: dict, seed: int = 0, device="cpu"):
+    """The token embedding [vocab][hidden] (bf16 ~ N(0, x_std), the distribution of x) that a
+    plan with a per-step length reads its input row from when it is given no input vector.
+    Drawn from its own generator (seed + 1_000_003), so `generate` stays unchanged."""
+    import torch
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed) + 1_000_003)
+    return _bf16_randn(torch, (cfg["vocab"], cfg["hidden"]), cfg["init"]["x_std"], gen, dev)
+
+
 def bf16_bits(t):
     """A bf16 torch tensor as a numpy uint16 array of its bit patterns (host copy)."""
     import torch
