@@ -11,7 +11,7 @@
 #include "../../include/dec.h"
 #include "planner.h"
 
-extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, bool cooperative,
+extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, int run, bool cooperative,
                                         hipStream_t stream);
 extern "C" hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu);
 
@@ -86,7 +86,6 @@ void fill_args(dec_plan* p) {
   a.stage_lo = 0;
   a.stage_hi = P.n_stages;
   a.state = nullptr;
-  a.kv_cap = (int32_t)(P.kv_len + 1);
   a.w_embed = P.w_embed;
   a.act_bytes = (uint32_t)(P.act_floats * 4);
   a.gs_floats = (int32_t)P.gs_floats;
@@ -122,7 +121,8 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   plan->args.stage_lo = lo;
   plan->args.stage_hi = hi;
   plan->args.state = nullptr;
-  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, hi - lo > 1,
+  const bool whole = lo == 0 && hi == plan->P.n_stages;
+  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, whole ? 0 : 1, hi - lo > 1,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");
@@ -384,7 +384,7 @@ dec_status dec_step_dynamic(dec_plan* plan, const void* x, void* kv, void* out, 
   plan->args.stage_lo = 0;
   plan->args.stage_hi = plan->P.n_stages;
   plan->args.state = state;
-  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, true, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = dec_engine_launch(&plan->args, plan->P.n_wg, plan->P.lds_bytes, 2, true, reinterpret_cast<hipStream_t>(stream));
   plan->args.state = nullptr;
   if (e != hipSuccess) {
     if (e == hipErrorCooperativeLaunchTooLarge) return fail(DEC_E_OCCUPANCY, "persistent grid cannot be co-resident");

@@ -676,7 +676,7 @@ __device__ __forceinline__ void kv_stage_dma(const EngineArgs& A, Blk& b, int la
   const int lane = threadIdx.x & 63, hd = A.hd;
   const int hw = hd / 2, nfl = rows * hw, nch = (nfl + 255) / 256;
   if (rows <= 0) return;
-  const size_t n1 = (size_t)A.kv_cap;
+  const size_t n1 = (size_t)A.kv_len + 1;
   const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 0) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
   const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 1) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
   float* kd = b.xs + kv_stage_k_off(A.hidden);
@@ -712,7 +712,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
       [&] { stage_vec(b, xin, b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
         const int n = b.n;
-        const size_t lay = (size_t)2 * A.nkv * A.kv_cap * hd;  // cache elements per layer
+        const size_t lay = (size_t)2 * A.nkv * (A.kv_len + 1) * hd;  // cache elements per layer
         const rsrc_t kvr = make_rsrc(A.kv + (size_t)t.layer * lay, (uint32_t)(lay * 2));
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
@@ -732,7 +732,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
             const uint32_t kn = (uint32_t)(L.act[LA_KVNEW] + (sel * A.nkv + g) * hd);
             cst(b.act, (kn + k) * 4u, a);
             cst(b.act, (kn + k + hh) * 4u, c);
-            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * A.kv_cap + n) * hd);
+            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * (A.kv_len + 1) + n) * hd);
             cst16(kvr, (row + k) * 2u, f2bf(a));
             cst16(kvr, (row + k + hh) * 2u, f2bf(c));
           }
@@ -805,7 +805,7 @@ template <int R, int LPP>
 __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   constexpr int GPW = 64 / LPP, NP = 3, PER_BLK = NP * GPW;
   const LayerDesc& L = A.layers[t.layer];
-  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = b.n, n1 = A.kv_cap;
+  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = b.n, n1 = A.kv_len + 1;
   const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
   const int p0 = split_pos(n, t.a1, t.a2), np = split_pos(n, t.a1 + 1, t.a2) - p0;
   const int q0 = p0 + wave_start(np, wave), q1 = p0 + wave_start(np, wave + 1);
@@ -1108,6 +1108,7 @@ __device__ __forceinline__ void best_pair(float& v, int& i) {
   }
 }
 
+template <bool GREEDY>
 __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const int K = A.hidden;
   const RmPlain rm{wp<uint16_t>(A, A.w_lm_head), K, t.u0};
@@ -1116,7 +1117,7 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
       [&] { stage_vec(b, A.x_final, nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) A.out[t.u0 + i] = b.ys[i];
-        if (A.state) {  // this task's largest logit (lowest index among equals) -> slot a0
+        if constexpr (GREEDY) {  // this task's largest logit (lowest index among equals) -> slot a0
           float bv = -INFINITY;
           int bi = 0x7fffffff;
           for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
@@ -1342,7 +1343,7 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
     qb[ks] = cld4(b.act, qo + ks * 128u + 16u);
   }
   if (wave == 0 && c < np && lane < HD / 8) {  // row c: the new position, written by this step's QKV tasks
-    const size_t n1 = (size_t)A.kv_cap, off = (size_t)(p0 + c) * HD + lane * 8;
+    const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
     const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
     const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
     __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
@@ -1452,7 +1453,7 @@ __device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, cons
   const int kl = A.kl, dr = A.dr, KR = kl + dr, n = b.n;
   if (!wait_deps(A, b, t)) return false;
   stage_vec(b, L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps);
-  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * A.kv_cap + n) * KR, (uint32_t)KR * 2u);
+  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (A.kv_len + 1) + n) * KR, (uint32_t)KR * 2u);
   for (int i = threadIdx.x; i < kl; i += kThreads) {
     const float v = b.xs[i];
     cst(b.act, (uint32_t)(L.act[LA_KVNEW] + i) * 4u, v);
@@ -1534,7 +1535,7 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
   const int kl = A.kl, KR = kl + A.dr, KP = (KR + 31) & ~31, NKS = KP >> 5, nh = A.nq;
   const int n = b.n, p0 = t.u0, p1 = t.u1;  // latent plans have a fixed length: the planned split
   const int wave = wave_id(), lane = threadIdx.x & 63, hl = lane & 15, g = lane >> 4;
-  const uint16_t* lat = A.kv + (size_t)t.layer * A.kv_cap * KR;
+  const uint16_t* lat = A.kv + (size_t)t.layer * (A.kv_len + 1) * KR;
   u4* QL = reinterpret_cast<u4*>(b.xs);                                   // [NKS][2][64]
   uint16_t* LAT = reinterpret_cast<uint16_t*>(b.xs + NKS * 512);          // [kMlaChunk][KP]
   u4* PA = reinterpret_cast<u4*>(b.xs + NKS * 512 + kMlaChunk * KP / 2);  // [kMlaChunk/32][2][64]
@@ -1987,7 +1988,12 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
 
 // The task walk, instantiated once per model family so that each kernel's register
 // allocation covers only the task types it runs: GQA (MLA = false) and MLA / MLA + MoE.
-template <bool MLA>
+// What one launch runs: a whole step of a fixed-length plan (the product path), a range of
+// stages of one, or a whole step of a plan with a per-step length. Each is its own kernel, so
+// the one-launch step carries none of the others' code.
+enum RunKind : int { kRunStep = 0, kRunStages = 1, kRunDynamic = 2 };
+
+template <bool MLA, int RUN>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -2006,12 +2012,14 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   b.n = A.kv_len;
   b.x = A.x;
   b.rope = A.rope_cs;
-  if (A.state) {
+  if constexpr (RUN == kRunDynamic) {
     // the step's position (and, without an input vector, its token), written by the
     // previous step's last workgroup or by the caller; every workgroup reads the same values
     // and, if they are out of range, the whole step does nothing (sticky status 8)
-    const int n = (int)ld_agent(reinterpret_cast<const uint32_t*>(A.state));
-    const int tok = (int)ld_agent(reinterpret_cast<const uint32_t*>(A.state) + 1);
+    // (wave-uniform values: every lane loads the same word; readfirstlane lets the compiler
+    // keep them, and everything computed from them, in scalar registers)
+    const int n = __builtin_amdgcn_readfirstlane((int)ld_agent(reinterpret_cast<const uint32_t*>(A.state)));
+    const int tok = __builtin_amdgcn_readfirstlane((int)ld_agent(reinterpret_cast<const uint32_t*>(A.state) + 1));
     if (n < 0 || n > A.kv_len || (!A.x && (tok < 0 || tok >= A.vocab))) {
       if (blockIdx.x == 0 && threadIdx.x == 0) {
         uint32_t zero = 0;
@@ -2033,9 +2041,9 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   // a launch runs the tasks of stages [stage_lo, stage_hi) of this workgroup's list; a step is
   // one launch of all stages, or launches of consecutive ranges in order (every dependency
   // lies in an earlier stage, so a one-stage launch never waits on its own tasks)
-  const bool all_stages = A.stage_lo == 0 && A.stage_hi == A.n_stages;
+  const bool all_stages = RUN != kRunStages || (A.stage_lo == 0 && A.stage_hi == A.n_stages);
   int ti0 = A.wg_begin[wg], ti1 = A.wg_begin[wg + 1];
-  if (!all_stages) {
+  if (RUN == kRunStages && !all_stages) {
     const int32_t* sf = A.stage_first + (size_t)wg * (A.n_stages + 1);
     ti0 = sf[A.stage_lo];
     ti1 = sf[A.stage_hi];
@@ -2067,8 +2075,12 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_HINIT: gemv = false; ok = task_hinit(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
         case T_DOWN: ok = task_down<true>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead(A, b, t); break;
-        case T_ARGMAX: gemv = false; ok = task_argmax(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic>(A, b, t); break;
+        case T_ARGMAX:
+          gemv = false;
+          if constexpr (RUN == kRunDynamic) ok = task_argmax(A, b, t);
+          else ok = false;
+          break;
         default: ok = false; break;
       }
     } else {
@@ -2082,7 +2094,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_OPROJ: ok = task_oproj(A, b, t); break;
         case T_GATEUP: ok = task_gateup(A, b, t); break;
         case T_DOWN: ok = task_down<false>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<false>(A, b, t); break;
         case T_ROUTER: ok = task_router(A, b, t); break;
         case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
         case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
@@ -2110,12 +2122,12 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   // the last workgroup to finish the step's last launch advances the epoch for the next step
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
-  if (threadIdx.x == 0 && A.stage_hi == A.n_stages) {
+  if (threadIdx.x == 0 && (RUN != kRunStages || A.stage_hi == A.n_stages)) {
     const uint32_t d = add_agent(A.ctl + CTL_DONE, 1u);
     if (d == (uint32_t)A.n_wg - 1u) {
       st_agent(A.ctl + CTL_DONE, 0u);
       add_agent(A.ctl + CTL_EPOCH, 1u);
-      if (A.state) {  // every workgroup has read the position: advance it for the next step
+      if constexpr (RUN == kRunDynamic) {  // every workgroup has read the position: advance it
         uint32_t* st = reinterpret_cast<uint32_t*>(A.state);
         st_agent(st, (uint32_t)(b.n + 1));
         st_agent(st + 2, ld_agent(st + 2) + 1u);
@@ -2124,33 +2136,47 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   }
 }
 
-extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa(EngineArgs A) { engine_body<false>(A); }
-extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla(EngineArgs A) { engine_body<true>(A); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa(EngineArgs A) { engine_body<false, kRunStep>(A); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla(EngineArgs A) { engine_body<true, kRunStep>(A); }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_stages(EngineArgs A) {
+  engine_body<false, kRunStages>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_stages(EngineArgs A) {
+  engine_body<true, kRunStages>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(EngineArgs A) {
+  engine_body<false, kRunDynamic>(A);
+}
 
 }  // namespace dec
 
-// Host-side launch (used by the C ABI in api.cpp).
-static const void* engine_fn(int arch) {
+// Host-side launch (used by the C ABI in api.cpp). run: 0 a whole step, 1 a range of stages,
+// 2 a whole step of a plan with a per-step length.
+static const void* engine_fn(int arch, int run) {
+  if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
+  if (run == 2) return (const void*)dec::dec_engine_gqa_dyn;
   return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
 }
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
-                                                                         bool cooperative, hipStream_t stream) {
-  static int configured_lds[2] = {-1, -1};
+                                                                         int run, bool cooperative, hipStream_t stream) {
+  static int configured_lds[2][3] = {{-1, -1, -1}, {-1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  if (configured_lds[k] < lds_bytes) {
-    hipError_t e = hipFuncSetAttribute(engine_fn(args->arch), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (run < 0 || run > 2 || (run == 2 && k != 0)) return hipErrorInvalidValue;
+  const void* fn = engine_fn(args->arch, run);
+  if (configured_lds[k][run] < lds_bytes) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
-    configured_lds[k] = lds_bytes;
+    configured_lds[k][run] = lds_bytes;
   }
   void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
   if (!cooperative)  // one stage: no task waits on another of the same launch
-    return hipLaunchKernel(engine_fn(args->arch), dim3(n_wg), dim3(dec::kThreads), kargs, (size_t)lds_bytes, stream);
-  return hipLaunchCooperativeKernel(engine_fn(args->arch), dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
+    return hipLaunchKernel(fn, dim3(n_wg), dim3(dec::kThreads), kargs, (size_t)lds_bytes, stream);
+  return hipLaunchCooperativeKernel(fn, dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
 }
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute(engine_fn(arch), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  hipError_t e = hipFuncSetAttribute(engine_fn(arch, 0), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch), dec::kThreads, (size_t)lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0), dec::kThreads, (size_t)lds_bytes);
 }

@@ -161,9 +161,10 @@ struct EngineArgs {
   int32_t nq, nkv, hd, ffn;
   int32_t ql, kl, dn, dr, dv;
   int32_t n_routed, n_shared, top_k, eff;
-  int32_t kv_len, n_wg, rope_half, w_final_norm, w_lm_head, x_final;
+  int32_t kv_len;              // the plan's length (a plan with a per-step length: its largest
+                               // position); cache slots per (layer, K/V, head) = kv_len + 1
+  int32_t n_wg, rope_half, w_final_norm, w_lm_head, x_final;
   int32_t n_stages;            // stages of the plan
-  int32_t kv_cap;              // cache slots per (layer, K/V, head): kv_len + 1, or max_len + 1
   int32_t w_embed;             // weight index of the token embedding (-1: none)
   int32_t stage_lo, stage_hi;  // this launch runs the tasks of stages [stage_lo, stage_hi)
   int32_t xs_floats;           // LDS floats reserved for the staged input vector
