@@ -283,15 +283,27 @@ __device__ __forceinline__ float block_sum(Blk& b, float v) {
 // Stage K values into xs[0, K) and zero xs[K, padK). The source is the activation buffer at
 // float offset `off`, or the bf16 step input `s16` when off < 0. With a gain, apply
 // RMSNorm: x / sqrt(mean(x^2) + eps) * g (eps inside the sqrt, mean over K).
-// All global loads are issued by wave 0, the wave that has no weight loads in flight (a
-// wave's loads complete in issue order, so waves 1..7 would wait for their prefetch first).
+// The loads of a short vector are issued by wave 0, the wave that has no weight loads in
+// flight (a wave's loads complete in issue order, so waves 1..7 would wait for their prefetch
+// first). A long one (the down projections' input) is copied by all waves, one 1-KB chunk in
+// turn each: one wave alone would issue more copies than it can keep in flight.
 __device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, int K, int padK,
                                           const uint16_t* gain, float eps) {
+  if (off >= 0 && K >= 8192) {
+    const int wave = wave_id(), lane = threadIdx.x & 63, nch = (K + 255) / 256;
+    for (int j = wave; j < nch; j += kWaves) {
+      int i = j * 256 + lane * 4;
+      i = i < K ? i : K - 4;
+      __builtin_amdgcn_global_load_lds((gvp)(b.actp + off + i), (lvp)(b.xs + j * 256), 16, 0, kActCpol);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+  }
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     if (gain) dma_to_lds(b.gs, (const float*)gain, K / 2);
     if (off >= 0) {
-      dma_to_lds(b.xs, b.actp + off, K);
+      if (K < 8192) dma_to_lds(b.xs, b.actp + off, K);
     } else {
       // the bf16 step input (layer 0): batched loads, converted to fp32
       for (int i0 = lane * 4; i0 < K; i0 += 64 * 4 * 4) {
@@ -1951,13 +1963,17 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
   return run_gemv(
       A, b, t, rm, G * (t.u1 - t.u0), F, G, true,
       [&] {
-        if (threadIdx.x < 64) {
-          for (int k = threadIdx.x; k < Kt; k += 64) wk[k] = cld(b.act, (uint32_t)(L.act[LA_TOPK] + Kt + k) * 4u);
-          for (int sg = 0; sg < G; ++sg) {
+        {
+          // the G input segments (8 KB each at eff = 2048) are copied by the waves in turn: one
+          // wave alone would issue more copies than it can keep in flight
+          const int wave = wave_id();
+          if (threadIdx.x < 64)
+            for (int k = threadIdx.x; k < Kt; k += 64) wk[k] = cld(b.act, (uint32_t)(L.act[LA_TOPK] + Kt + k) * 4u);
+          for (int sg = wave; sg < G; sg += kWaves) {
             const float* src = b.actp + (sg < ns ? L.act[LA_SACT] + sg * F : L.act[LA_ACT] + (sg - ns) * F);
             dma_to_lds(b.xs + sg * Fp, src, F);
           }
-          __builtin_amdgcn_s_waitcnt(kVmcnt0);
+          __builtin_amdgcn_s_waitcnt(kVmcnt0);  // (a wave's copies land after its own prefetch)
         }
         __syncthreads();
         for (int sg = 0; sg < G; ++sg) {
