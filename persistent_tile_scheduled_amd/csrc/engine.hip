@@ -2009,6 +2009,16 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
 // the one-launch step carries none of the others' code.
 enum RunKind : int { kRunStep = 0, kRunStages = 1, kRunDynamic = 2 };
 
+// The kernel argument block, re-read through a pointer the compiler cannot see through: each
+// task loads the arguments it uses (scalar loads, cached) instead of keeping every argument
+// of the persistent loop live in scalar registers.
+__device__ __forceinline__ const EngineArgs& args_view() {
+  typedef const EngineArgs __attribute__((address_space(4)))* CArgsP;
+  CArgsP p = (CArgsP)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const EngineArgs*)p;
+}
+
 template <bool MLA, int RUN>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
@@ -2065,6 +2075,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
     ti1 = sf[A.stage_hi];
   }
   for (int ti = ti0; ti < ti1; ++ti) {
+    const EngineArgs& A = args_view();
     const TaskDesc t = A.tasks[ti];
     const uint32_t t0 = (uint32_t)now();
     bool ok = true, gemv = true;
