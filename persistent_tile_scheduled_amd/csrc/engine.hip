@@ -108,6 +108,19 @@ __device__ __forceinline__ void dma_to_lds(float* dst, const float* src, int nfl
   }
 }
 
+// The same copy split over all waves of the workgroup (1-KB chunk j by wave j % 8): for copies
+// longer than one wave keeps in flight. Every wave must call it; each waits for its own part
+// (after its own loads issued earlier), and the caller's barrier publishes the whole.
+__device__ __forceinline__ void dma_to_lds_all(float* dst, const float* src, int nfloats) {
+  const int lane = threadIdx.x & 63;
+  for (int j = (int)(threadIdx.x >> 6); j * 256 < nfloats; j += kWaves) {
+    int i = j * 256 + lane * 4;
+    i = i < nfloats ? i : nfloats - 4;
+    __builtin_amdgcn_global_load_lds((gvp)(src + i), (lvp)(dst + j * 256), 16, 0, kActCpol);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+}
+
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
@@ -290,13 +303,7 @@ __device__ __forceinline__ float block_sum(Blk& b, float v) {
 __device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, int K, int padK,
                                           const uint16_t* gain, float eps) {
   if (off >= 0 && K >= 8192) {
-    const int wave = wave_id(), lane = threadIdx.x & 63, nch = (K + 255) / 256;
-    for (int j = wave; j < nch; j += kWaves) {
-      int i = j * 256 + lane * 4;
-      i = i < K ? i : K - 4;
-      __builtin_amdgcn_global_load_lds((gvp)(b.actp + off + i), (lvp)(b.xs + j * 256), 16, 0, kActCpol);
-    }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    dma_to_lds_all(b.xs, b.actp + off, K);
     __syncthreads();
   }
   if (threadIdx.x < 64) {
@@ -755,18 +762,15 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
 
 // Merge S split partials (m, l, acc[hd]) of H heads into xs[h*hd + d] =
 // sum_s e^(m_s-M) acc_s[d] / sum_s e^(m_s-M) l_s (base-2 exponents), zero-padding xs up to
-// padK. Wave 0 copies the S*H partials into LDS with one burst of DMA; the merge then runs
+// padK. All waves copy the S*H partials into LDS (one burst of DMA each); the merge then runs
 // from LDS. With o_off >= 0 wave 0 also stores the merged vector there.
 __device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H, int hd, int padK, int o_off) {
   const int ps = hd + 4;                    // m, l, 2 pad, acc[hd]
   const int n = S * H * ps;
   float* P = b.scr;                         // [S][H][ps]
   float* w = P + ((n + 255) & ~255);        // [S][H] merge weights
-  if (threadIdx.x < 64) {
-    dma_to_lds(P, b.actp + parts_off, n);
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    for (int i = H * hd + (int)threadIdx.x; i < padK; i += 64) b.xs[i] = 0.f;
-  }
+  dma_to_lds_all(P, b.actp + parts_off, n);
+  for (int i = H * hd + (int)threadIdx.x; i < padK; i += kThreads) b.xs[i] = 0.f;
   __syncthreads();
   // wave h (h < 8) owns heads h, h + 8, ...: lanes run over the splits
   for (int h = wave_id(); h < H; h += kWaves) {
