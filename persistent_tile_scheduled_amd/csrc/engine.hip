@@ -369,6 +369,7 @@ constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (NB KB per wave
 #endif
 constexpr int kRingQKV = DEC_RING_QKV;      // register ring depth of the QKV tasks
 constexpr int kRingOproj = DEC_RING_OPROJ;  // register ring depth of the per-group O-projection
+constexpr int kRingFfn = 3;  // gate/up and (GQA) down: three batches in flight cover more of the stage boundary
 
 // Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
 // columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
@@ -1084,7 +1085,7 @@ __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const T
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden;
   const RmGateUp rm{wp<uint16_t>(A, L.w[LW_GATE]), wp<uint16_t>(A, L.w[LW_UP]), K, t.u0};
-  return run_gemv(
+  return run_gemv<kRingFfn>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
@@ -1098,7 +1099,7 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.ffn;
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
-  return run_gemv<2, FLAT>(
+  return run_gemv<FLAT ? kRingFfn : 2, FLAT>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
       [&] {
