@@ -6,7 +6,7 @@ pinned by tests/test_oracle_pins.py against closed forms, invariants, brute forc
 independent library routines.
 """
 from .decode_oracle import (  # noqa: F401
-    widen_bf16, round_to_bf16, rmsnorm, rope, linear, linear_bits, softmax, attend,
+    widen_bf16, decode_e4m3, round_to_bf16, rmsnorm, rope, linear, linear_bits, softmax, attend,
     attend_partial, merge_partials, attend_split, silu, swiglu, route, gqa_layer,
     mla_attention, mla_attention_absorbed, moe_ffn, mla_layer, layer, head, forward,
     dict_weights,

@@ -44,6 +44,11 @@ sigmoid, the bias add and the comparisons run in fp32.
 Weights are passed as a callable W(name, index=None) returning a NumPy array: uint16 bf16
 bit patterns for bf16 tensors, float32 for the router bias. `index` selects one expert of
 a stacked expert tensor, so the MoE oracle reads only the experts it routes to.
+
+Low-precision weights (the survey's "next" row on cutting bytes per token; the pages name
+the lever -- fewer bytes per token -- not a format): a linear matrix given as uint8 is OCP
+FP8 E4M3 bytes, and W(name + ".scale") holds one fp32 scale per row; the matrix the layer
+multiplies by is scale[r] * e4m3(bytes[r, c]), decoded exactly (decode_e4m3).
 """
 from __future__ import annotations
 
@@ -63,6 +68,19 @@ def widen_bf16(bits) -> np.ndarray:
     if b.dtype != np.uint16:
         b = b.view(np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    """OCP FP8 E4M3 ("FN") byte -> float64, exactly: sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent 0 encodes subnormals m/8 * 2^-6; S.1111.111 is NaN; there are
+    no infinities (the largest finite magnitude is 1.75 * 2^8 = 448)."""
+    b = np.asarray(bits).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    out = sign * mag
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, out)
 
 
 def round_to_bf16(x) -> Tuple[np.ndarray, np.ndarray]:
@@ -127,18 +145,24 @@ def linear(Wm: np.ndarray, x: np.ndarray) -> np.ndarray:
 
 def linear_bits(W: Callable, name: str, x: np.ndarray, index=None,
                 rows_per_block: int = 1 << 16) -> np.ndarray:
-    """y = W x for a bf16 matrix given by name; rows are widened a block at a time so a
-    1 GB LM head never needs its whole fp64 copy in memory. Each output element is still
-    one full dot product of its row."""
+    """y = W x for a matrix given by name: bf16 bits, or FP8 E4M3 bytes with one fp32 scale
+    per row (W(name + ".scale")). Rows are widened a block at a time so a 1 GB LM head never
+    needs its whole fp64 copy in memory. Each output element is still one full dot product
+    of its row."""
     bits = W(name) if index is None else W(name, index)
     bits = np.asarray(bits)
+    if bits.dtype == np.uint8:
+        scale = np.asarray(W(name + ".scale") if index is None else W(name + ".scale", index), dtype=np.float64)
+        widen = lambda r0, r1: decode_e4m3(bits[r0:r1]) * scale[r0:r1, None]
+    else:
+        widen = lambda r0, r1: widen_bf16(bits[r0:r1])
     n = bits.shape[0]
     if n <= rows_per_block:
-        return linear(widen_bf16(bits), x)
+        return linear(widen(0, n), x)
     out = np.empty(n, dtype=np.float64)
     for r0 in range(0, n, rows_per_block):
         r1 = min(n, r0 + rows_per_block)
-        out[r0:r1] = linear(widen_bf16(bits[r0:r1]), x)
+        out[r0:r1] = linear(widen(r0, r1), x)
     return out
 
 

@@ -104,6 +104,89 @@ def test_linear_bits_blocks_and_transposition():
 
 
 # ----------------------------------------------------------------------------------------
+# FP8 E4M3 weights
+# ----------------------------------------------------------------------------------------
+
+def check_decode_e4m3(o):
+    codes = np.arange(256, dtype=np.uint8)
+    d = o.decode_e4m3(codes)
+    # the format's fixed points: 1.0, the largest finite value, the smallest subnormal and
+    # normal, the largest subnormal, signed zero, the two NaN codes
+    assert d[0x38] == 1.0 and d[0xB8] == -1.0
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0
+    assert d[0x01] == 2.0 ** -9 and d[0x08] == 2.0 ** -6 and d[0x07] == 7 * 2.0 ** -9
+    assert d[0x00] == 0.0 and d[0x80] == 0.0 and math.copysign(1.0, d[0x80]) == -1.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF]) and np.sum(np.isnan(d)) == 2
+    # codes 0x00..0x7E are increasing; every finite value is a multiple of 2^-9
+    assert np.all(np.diff(d[:0x7F]) > 0)
+    fin = d[~np.isnan(d)]
+    assert np.all(fin * 512 == np.round(fin * 512))
+    # a library routine: torch's float8_e4m3fn dtype, all 256 codes
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ref), np.isnan(d))
+    assert np.array_equal(ref[~np.isnan(ref)], d[~np.isnan(d)])
+
+
+def test_decode_e4m3():
+    check_decode_e4m3(O)
+
+
+def check_linear_fp8(o):
+    """uint8 weights are E4M3 bytes scaled per ROW: brute-force loop, and exact small-integer
+    arithmetic (a per-column scale or a transposed matrix fails both)."""
+    codes = RNG.integers(0, 0x7F, size=(5, 7)).astype(np.uint8) | (RNG.integers(0, 2, size=(5, 7)) << 7).astype(np.uint8)
+    scale = np.array([0.5, 2.0, 3.0, 0.25, 1.5], dtype=np.float32)
+    x = RNG.standard_normal(7)
+    W = o.dict_weights({"m": codes, "m.scale": scale})
+    y = o.linear_bits(W, "m", x)
+    for r in range(5):
+        acc = 0.0
+        for c in range(7):
+            acc += float(scale[r]) * float(o.decode_e4m3(codes[r, c])) * x[c]
+        assert abs(y[r] - acc) <= 1e-12 * max(1.0, abs(acc))
+    # codes of small integers (0x40 = 2, 0x48 = 4, 0x44 = 3, 0xC0 = -2) with integer x: exact
+    ci = np.array([[0x40, 0x48], [0x44, 0xC0], [0x38, 0x00]], dtype=np.uint8)
+    Wi = o.dict_weights({"m": ci, "m.scale": np.array([1.0, 2.0, 4.0], dtype=np.float32)})
+    assert np.array_equal(o.linear_bits(Wi, "m", np.array([3.0, 5.0])), np.array([26.0, -2.0, 12.0]))
+    # row blocks give the same result
+    assert np.allclose(o.linear_bits(W, "m", x, rows_per_block=2), y, rtol=1e-13, atol=0)
+
+
+def test_linear_fp8():
+    check_linear_fp8(O)
+
+
+def test_fp8_forward_equals_bf16_forward_on_the_same_values():
+    """A tiny GQA model whose FP8 rows times power-of-two scales are exactly bf16 values:
+    the oracle's FP8 forward equals its (independently pinned) bf16 forward on those values,
+    layer trace and logits, exactly."""
+    cfg = workloads.get_config("tiny_fp8")
+    w, x, kv = workloads.generate(cfg, seed=3)
+    f8, b16 = {}, {}
+    rng = np.random.default_rng(5)
+    for s in workloads.weight_specs(cfg):
+        if s.name.endswith(".scale"):
+            continue
+        t = w[s.name]
+        if s.dtype == "fp8":
+            codes = t.numpy()
+            sc = np.ldexp(1.0, rng.integers(-9, -4, size=codes.shape[0])).astype(np.float32)
+            f8[s.name], f8[s.name + ".scale"] = codes, sc
+            vals = O.decode_e4m3(codes) * sc[:, None]
+            b16[s.name] = _bits_of(torch.from_numpy(vals).to(torch.bfloat16))
+            assert np.array_equal(O.widen_bf16(b16[s.name]), vals)  # exactly representable
+        else:
+            f8[s.name] = b16[s.name] = workloads.bf16_bits(t) if t.dtype == torch.bfloat16 else t.numpy()
+    xb, kvb = workloads.bf16_bits(x), workloads.bf16_bits(kv)
+    a = O.forward(cfg, O.dict_weights(f8), xb, kvb)
+    b = O.forward(cfg, O.dict_weights(b16), xb, kvb)
+    assert np.array_equal(a["out"], b["out"])
+    for ta, tb in zip(a["layers"], b["layers"]):
+        for k in ta:
+            assert np.array_equal(np.asarray(ta[k]), np.asarray(tb[k])), k
+
+
+# ----------------------------------------------------------------------------------------
 # RMSNorm
 # ----------------------------------------------------------------------------------------
 

@@ -14,6 +14,11 @@ available; these shapes stand in for them):
   * norm gains = 1 ("ones") or ~ N(mean, std) for the gain-pinning variants;
   * cached K/V (or latent c||k_pe) ~ N(0, kv_std) on positions [0, kv_len), slot kv_len = 0;
   * x ~ N(0, x_std) in bf16; router bias ~ N(0, router_bias_std) in fp32.
+  * configs with "weights": "fp8" (GQA only): every linear matrix is drawn the same way in
+    fp32, then each row r is stored as E4M3 bytes of row / scale[r] (round to nearest
+    even) with scale[r] = max|row| / 448 in fp32, so the row's largest value maps to the
+    largest finite E4M3 magnitude. Quantisation is input generation: the decode path only
+    reads bytes and scales.
 All tensors come from one torch.Generator seeded once, drawn in the canonical order.
 """
 from __future__ import annotations
@@ -27,6 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 BF16 = "bf16"
 FP32 = "fp32"
+FP8 = "fp8"     # OCP FP8 E4M3 bytes (with a per-row fp32 "<name>.scale" tensor after it)
 
 
 def load_configs() -> Dict[str, dict]:
@@ -59,7 +65,7 @@ class TensorSpec:
 
     @property
     def nbytes(self) -> int:
-        return self.numel * (2 if self.dtype == BF16 else 4)
+        return self.numel * {BF16: 2, FP8: 1}.get(self.dtype, 4)
 
 
 def _mla_attn_specs(cfg: dict, p: str) -> List[TensorSpec]:
@@ -81,7 +87,22 @@ def _mla_attn_specs(cfg: dict, p: str) -> List[TensorSpec]:
 
 
 def weight_specs(cfg: dict) -> List[TensorSpec]:
-    """Canonical ordered tensor list of a config (the order weights are bound in)."""
+    """Canonical ordered tensor list of a config (the order weights are bound in). With
+    "weights": "fp8" each linear matrix is FP8 and followed by its fp32 row scales."""
+    out = _weight_specs_bf16(cfg)
+    if cfg.get("weights", "bf16") != "fp8":
+        return out
+    q: List[TensorSpec] = []
+    for s in out:
+        if s.init == "weight":
+            q.append(TensorSpec(s.name, s.shape, FP8, "weight"))
+            q.append(TensorSpec(s.name + ".scale", (s.shape[0],), FP32, "scale"))
+        else:
+            q.append(s)
+    return q
+
+
+def _weight_specs_bf16(cfg: dict) -> List[TensorSpec]:
     arch = cfg["arch"]
     d = cfg["hidden"]
     out: List[TensorSpec] = []
@@ -142,6 +163,14 @@ def out_shape(cfg: dict) -> Tuple[int, ...]:
     return (cfg["vocab"],) if cfg.get("vocab", 0) > 0 else (cfg["hidden"],)
 
 
+def _quantize_e4m3_rows(torch, w32):
+    """Per-row E4M3 quantisation of an fp32 [rows][cols] tensor: (bytes as uint8, fp32 scales)."""
+    amax = w32.abs().amax(dim=1)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (w32 / scale[:, None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), scale.to(torch.float32)
+
+
 def weight_bytes(cfg: dict) -> int:
     return sum(s.nbytes for s in weight_specs(cfg))
 
@@ -182,7 +211,21 @@ def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = Non
     init = cfg["init"]
     weights = {}
     for s in weight_specs(cfg):
-        if s.init == "weight":
+        if s.init == "scale":
+            continue  # produced with its matrix
+        if s.init == "weight" and s.dtype == FP8:
+            q = torch.empty(s.shape, dtype=torch.uint8, device=dev)
+            sc = torch.empty(s.shape[0], dtype=torch.float32, device=dev)
+            rows = max(1, (1 << 26) // s.shape[1])
+            for r0 in range(0, s.shape[0], rows):
+                r1 = min(s.shape[0], r0 + rows)
+                w32 = torch.randn((r1 - r0, s.shape[1]), generator=gen, device=dev, dtype=torch.float32)
+                w32.mul_(init["weight_std"])
+                q[r0:r1], sc[r0:r1] = _quantize_e4m3_rows(torch, w32)
+                del w32
+            weights[s.name] = q
+            weights[s.name + ".scale"] = sc
+        elif s.init == "weight":
             weights[s.name] = _bf16_randn(torch, s.shape, init["weight_std"], gen, dev)
         elif s.init == "gain":
             g = init["gain"]
