@@ -28,6 +28,8 @@ WORKLOADS = {
     "moe_4k": "MLA + MoE decoder stack (4 layers, hidden 7168, MLA as above, 256 routed experts of 2048 + 1 "
               "shared, sigmoid top-8), batch 1, one decode token over a 4096-position latent cache",
     "tiny": "tiny decoder (2 layers, hidden 256), batch 1, KV 128",
+    "8b_4k_fp8": "the 8B-shaped decoder with every linear matrix in FP8 E4M3 (one fp32 scale per row), "
+                 "batch 1, one decode token over a 4096-position bf16 KV cache",
 }
 # Sources whose content decides the engine's memory traffic: a stored counter reading is
 # reported only while their hash matches.
@@ -263,8 +265,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) bf16 KV and input)",
+        "dtype": "fp8" if cfg.get("weights") == "fp8" else "bf16",
+        "data": "synthetic (seeded N(0,0.02) " + ("weights quantised per row to FP8 E4M3" if cfg.get("weights") == "fp8"
+                                                  else "bf16 weights") + ", N(0,1) bf16 KV and input)",
         "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
                    "kv_len": cfg["kv_len"], "batch": 1},
         "launch": args.launch if args.launch == "persistent" else

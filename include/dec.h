@@ -64,6 +64,17 @@ typedef enum {
 } dec_status;
 
 typedef enum {
+  DEC_WEIGHTS_BF16 = 0,      /* every matrix bf16 */
+  DEC_WEIGHTS_FP8_E4M3 = 1   /* GQA only: each linear matrix (wq, wk, wv, wo, w_gate, w_up,
+                                w_down, lm_head) as OCP FP8 E4M3 bytes [rows][cols], followed in
+                                the weight list by "<name>.scale", fp32 [rows]: row r of the
+                                matrix is scale[r] * e4m3(bytes[r][:]). cols must be a multiple
+                                of 16. Norm gains (and "embed") stay bf16. This is the survey's
+                                next lever on bytes per token; the pages name the lever (fewer
+                                bytes moved per token), not a format. */
+} dec_weight_format;
+
+typedef enum {
   DEC_ARCH_GQA = 0,      /* Llama-style pre-norm decoder: GQA attention + SwiGLU FFN */
   DEC_ARCH_MLA = 1,      /* latent-KV (MLA) attention + dense SwiGLU FFN */
   DEC_ARCH_MOE = 2       /* latent-KV (MLA) attention + routed/shared expert FFN */
@@ -83,7 +94,7 @@ typedef struct dec_model_shape {
   int32_t q_lora_rank, kv_lora_rank, qk_nope, qk_rope, v_head;
   int32_t n_routed, n_shared, top_k, expert_ffn;
   float rms_eps;
-  int32_t reserved0;
+  int32_t weight_format; /* dec_weight_format (0: bf16) */
   double rope_theta;
 } dec_model_shape;
 
@@ -98,7 +109,7 @@ typedef struct dec_device_info {
   int32_t reserved0;
 } dec_device_info;
 
-typedef enum { DEC_DTYPE_BF16 = 0, DEC_DTYPE_FP32 = 1, DEC_DTYPE_I32 = 2 } dec_dtype;
+typedef enum { DEC_DTYPE_BF16 = 0, DEC_DTYPE_FP32 = 1, DEC_DTYPE_I32 = 2, DEC_DTYPE_FP8 = 3 } dec_dtype;
 
 typedef struct dec_tensor_desc {
   char name[64];           /* e.g. "layers.3.wq" */

@@ -16,7 +16,8 @@ DEC_ABI_VERSION = 1
 ARCH = {"gqa": 0, "mla": 1, "moe": 2}
 STATUS = {0: "DEC_OK", -1: "DEC_E_INVAL", -2: "DEC_E_SHAPE", -3: "DEC_E_CAPACITY", -4: "DEC_E_DEVICE",
           -5: "DEC_E_OCCUPANCY", -6: "DEC_E_HIP", -7: "DEC_E_TIMEOUT", -8: "DEC_E_UNBOUND", -9: "DEC_E_PLAN"}
-DTYPE = {0: "bf16", 1: "fp32", 2: "i32"}
+DTYPE = {0: "bf16", 1: "fp32", 2: "i32", 3: "fp8"}
+WEIGHT_FORMAT = {"bf16": 0, "fp8": 1}
 
 # task type ids (mirror of the engine's TaskType enum)
 TASK_TYPES = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "MLA_A", 8: "MLA_B",
@@ -35,7 +36,7 @@ class ModelShape(C.Structure):
                 ("vocab", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("ffn", C.c_int32), ("q_lora_rank", C.c_int32), ("kv_lora_rank", C.c_int32), ("qk_nope", C.c_int32),
                 ("qk_rope", C.c_int32), ("v_head", C.c_int32), ("n_routed", C.c_int32), ("n_shared", C.c_int32),
-                ("top_k", C.c_int32), ("expert_ffn", C.c_int32), ("rms_eps", C.c_float), ("reserved0", C.c_int32),
+                ("top_k", C.c_int32), ("expert_ffn", C.c_int32), ("rms_eps", C.c_float), ("weight_format", C.c_int32),
                 ("rope_theta", C.c_double)]
 
 
@@ -137,6 +138,7 @@ def shape_from_config(cfg: dict) -> ModelShape:
         setattr(s, k, int(cfg.get(k, 0) or 0))
     s.rms_eps = float(cfg["rms_eps"])
     s.rope_theta = float(cfg["rope_theta"])
+    s.weight_format = WEIGHT_FORMAT[cfg.get("weights", "bf16")]
     return s
 
 

@@ -13,7 +13,7 @@
 
 extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, int run, bool cooperative,
                                         hipStream_t stream);
-extern "C" hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu);
 
 struct dec_plan {
   dec::PlanData P;
@@ -87,6 +87,7 @@ void fill_args(dec_plan* p) {
   a.stage_hi = P.n_stages;
   a.state = nullptr;
   a.w_embed = P.w_embed;
+  a.wfmt = s.weight_format;
   a.act_bytes = (uint32_t)(P.act_floats * 4);
   a.gs_floats = (int32_t)P.gs_floats;
   a.eps = s.rms_eps;
@@ -111,6 +112,8 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
   if (plan->P.dynamic) return fail(DEC_E_INVAL, "a plan with a per-step length runs with dec_step_dynamic");
+  if (plan->P.shape.weight_format != DEC_WEIGHTS_BF16 && (lo != 0 || hi != plan->P.n_stages))
+    return fail(DEC_E_INVAL, "FP8-weight plans run whole steps only (dec_step)");
   if (lo < 0 || hi > plan->P.n_stages || lo >= hi)
     return fail(DEC_E_INVAL, "stage range [" + std::to_string(lo) + ", " + std::to_string(hi) + ") not inside [0, " +
                                  std::to_string(plan->P.n_stages) + ")");
@@ -180,7 +183,7 @@ dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, dec_pla
   st = dec_plan_create_for(shape, kv_len, &dev, out);
   if (st != DEC_OK) return st;
   int per_cu = 0;
-  hipError_t e = dec_engine_occupancy((*out)->P.shape.arch, (*out)->P.lds_bytes, &per_cu);
+  hipError_t e = dec_engine_occupancy((*out)->P.shape.arch, (*out)->P.shape.weight_format, (*out)->P.lds_bytes, &per_cu);
   if (e != hipSuccess || per_cu < 1) {
     dec_plan_destroy(*out);
     *out = nullptr;

@@ -30,6 +30,7 @@ namespace dec {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ small helpers
@@ -196,6 +197,7 @@ struct Blk {
   float* scr;     // LDS: reduction scratch
   uint64_t* rowp; // LDS: row pointers of the current GEMV task
   int* xoffp;     // LDS: per-row input offsets of the current GEMV task
+  float* scl;     // LDS: per-row weight scales of the current GEMV task (FP8 weights)
   float* gs;      // LDS: norm gains (bf16) of the current task
   float* actp;    // the activation region (generic pointer, for LDS DMA)
   int n;                // the step's position: cached positions [0, n), the new token's slot n
@@ -280,6 +282,12 @@ __device__ __forceinline__ void signal_w0(const EngineArgs& A, int ctr) {
 }
 
 __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
+// A staged input padded to whole GEMV chunks of weights with ES bytes each (512 or 1024 columns).
+template <int ES>
+__device__ __forceinline__ int padc(int k) { return (k + 1024 / ES - 1) / (1024 / ES) * (1024 / ES); }
+// The fp32 row scales of an FP8 matrix: the weight after it in the bound list.
+template <int ES>
+__device__ __forceinline__ const float* wscale(const EngineArgs& A, int idx) { return ES == 1 ? wp<float>(A, idx + 1) : nullptr; }
 
 __device__ __forceinline__ float block_sum(Blk& b, float v) {
   v = wave_sum(v);
@@ -371,15 +379,53 @@ constexpr int kRingQKV = DEC_RING_QKV;      // register ring depth of the QKV ta
 constexpr int kRingOproj = DEC_RING_OPROJ;  // register ring depth of the per-group O-projection
 constexpr int kRingFfn = 3;  // gate/up and (GQA) down: three batches in flight cover more of the stage boundary
 
-// Streams the rows [ja, jb) of a task through a register double buffer. Row j has K bf16
-// columns starting at rowp[j] (an LDS table filled by fill_rows) and is dotted with
-// xs[xoff[j] + c].
-struct Stream {
+// One wave load is 16 bytes per lane: 8 bf16 or 16 FP8 (E4M3) weights. ES = bytes per
+// weight; a chunk (one wave load) spans 1024 / ES columns.
+template <int ES>
+struct Chunk {
+  static constexpr int kCols = 1024 / ES;  // columns per chunk
+  static constexpr int kLane = 16 / ES;    // columns per lane
+  // acc0/acc1 += the lane's weights . x (xp: the lane's kLane inputs in LDS)
+  __device__ static __forceinline__ void dot(const u4& w, const float* xp, float& acc0, float& acc1) {
+    if constexpr (ES == 2) {
+      const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
+      acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
+      acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
+      acc0 = fmaf(bf_lo(w.y), x0.z, acc0);
+      acc1 = fmaf(bf_hi(w.y), x0.w, acc1);
+      acc0 = fmaf(bf_lo(w.z), x1.x, acc0);
+      acc1 = fmaf(bf_hi(w.z), x1.y, acc1);
+      acc0 = fmaf(bf_lo(w.w), x1.z, acc0);
+      acc1 = fmaf(bf_hi(w.w), x1.w, acc1);
+    } else {
+      // hardware E4M3 -> fp32 conversion, two bytes per instruction (bytes 0, 1 of the
+      // selected 16-bit half are the lower two columns)
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 x = *(const f4*)(xp + 4 * q);
+        const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], false);
+        const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[q], true);
+        acc0 = fmaf(lo.x, x.x, acc0);
+        acc1 = fmaf(lo.y, x.y, acc1);
+        acc0 = fmaf(hi.x, x.z, acc0);
+        acc1 = fmaf(hi.y, x.w, acc1);
+      }
+    }
+  }
+};
+
+// Streams the rows [ja, jb) of a task through a register double buffer. Row j has K
+// columns (ES bytes each) starting at rowp[j] (an LDS table filled by fill_rows) and is
+// dotted with xs[xoff[j] + c].
+template <int ES>
+struct StreamT {
+  using C = Chunk<ES>;
   const uint64_t* rowp;
   const int* xoffp;
   int jb, K, cpr, lane;
   int lj, lc;
-  const uint16_t* lrow;
+  const uint8_t* lrow;
   int cj, cc, cxo;
   float acc0, acc1;
 
@@ -389,10 +435,10 @@ struct Stream {
     jb = jb_;
     K = K_;
     lane = lane_;
-    cpr = (K + kChunkCols - 1) / kChunkCols;
+    cpr = (K + C::kCols - 1) / C::kCols;
     lj = ja;
     lc = 0;
-    lrow = (ja < jb) ? (const uint16_t*)uni64(rowp[ja]) : nullptr;
+    lrow = (ja < jb) ? (const uint8_t*)uni64(rowp[ja]) : nullptr;
     cj = ja;
     cc = 0;
     cxo = (ja < jb) ? uni(xoffp[ja]) : 0;
@@ -402,12 +448,12 @@ struct Stream {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (lj < jb) {
-        int col = lc * kChunkCols + lane * 8;
+        int col = lc * C::kCols + lane * C::kLane;
         col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
-        bf[i] = ldg_nt(lrow + col);
+        bf[i] = ldg_nt(lrow + (size_t)col * ES);
         if (++lc == cpr) {
           lc = 0;
-          if (++lj < jb) lrow = (const uint16_t*)uni64(rowp[lj]);
+          if (++lj < jb) lrow = (const uint8_t*)uni64(rowp[lj]);
         }
       }
     }
@@ -417,17 +463,7 @@ struct Stream {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (cj < jb) {
-        const float* xp = xs + cxo + cc * kChunkCols + lane * 8;
-        const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
-        const u4 w = bf[i];
-        acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
-        acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
-        acc0 = fmaf(bf_lo(w.y), x0.z, acc0);
-        acc1 = fmaf(bf_hi(w.y), x0.w, acc1);
-        acc0 = fmaf(bf_lo(w.z), x1.x, acc0);
-        acc1 = fmaf(bf_hi(w.z), x1.y, acc1);
-        acc0 = fmaf(bf_lo(w.w), x1.z, acc0);
-        acc1 = fmaf(bf_hi(w.w), x1.w, acc1);
+        C::dot(bf[i], xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
         if (++cc == cpr) {
           emit(cj, wave_sum(acc0 + acc1));
           acc0 = acc1 = 0.f;
@@ -445,12 +481,14 @@ struct Stream {
 // the row ends. Used where a task has few, long rows: whole rows per wave would leave the
 // waves up to a row apart (3 rows against 2 for 16 rows over 7 waves), and the last waves
 // alone could not keep enough loads in flight.
-struct StreamFlat {
+template <int ES>
+struct StreamFlatT {
+  using C = Chunk<ES>;
   const uint64_t* rowp;
   const int* xoffp;
   int fb, K, cpr, lane;
   int lf, lj, lc;
-  const uint16_t* lrow;
+  const uint8_t* lrow;
   int cf, cj, cc, cxo;
   float acc0, acc1;
 
@@ -460,12 +498,12 @@ struct StreamFlat {
     fb = fb_;
     K = K_;
     lane = lane_;
-    cpr = (K + kChunkCols - 1) / kChunkCols;
+    cpr = (K + C::kCols - 1) / C::kCols;
     const int j0 = fa / cpr, c0 = fa - j0 * cpr;
     lf = cf = fa;
     lj = cj = j0;
     lc = cc = c0;
-    lrow = (fa < fb) ? (const uint16_t*)uni64(rowp[j0]) : nullptr;
+    lrow = (fa < fb) ? (const uint8_t*)uni64(rowp[j0]) : nullptr;
     cxo = (fa < fb) ? uni(xoffp[j0]) : 0;
     acc0 = acc1 = 0.f;
   }
@@ -473,14 +511,14 @@ struct StreamFlat {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (lf < fb) {
-        int col = lc * kChunkCols + lane * 8;
+        int col = lc * C::kCols + lane * C::kLane;
         col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
-        bf[i] = ldg_nt(lrow + col);
+        bf[i] = ldg_nt(lrow + (size_t)col * ES);
         ++lf;
         if (++lc == cpr) {
           lc = 0;
           ++lj;
-          if (lf < fb) lrow = (const uint16_t*)uni64(rowp[lj]);
+          if (lf < fb) lrow = (const uint8_t*)uni64(rowp[lj]);
         }
       }
     }
@@ -490,17 +528,7 @@ struct StreamFlat {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (cf < fb) {
-        const float* xp = xs + cxo + cc * kChunkCols + lane * 8;
-        const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
-        const u4 w = bf[i];
-        acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
-        acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
-        acc0 = fmaf(bf_lo(w.y), x0.z, acc0);
-        acc1 = fmaf(bf_hi(w.y), x0.w, acc1);
-        acc0 = fmaf(bf_lo(w.z), x1.x, acc0);
-        acc1 = fmaf(bf_hi(w.z), x1.y, acc1);
-        acc0 = fmaf(bf_lo(w.w), x1.z, acc0);
-        acc1 = fmaf(bf_hi(w.w), x1.w, acc1);
+        C::dot(bf[i], xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
         ++cf;
         const bool row_end = ++cc == cpr;
         if (row_end || cf == fb) {
@@ -517,12 +545,15 @@ struct StreamFlat {
   }
 };
 
+using Stream = StreamT<2>;
+using StreamFlat = StreamFlatT<2>;
+
 // Each wave writes the row pointers / input offsets of its own rows (no barrier needed:
 // LDS accesses of one wave are ordered).
 template <class RM>
 __device__ __forceinline__ void fill_rows(const RM& rm, int ja, int jb, uint64_t* rowp, int* xoffp) {
   for (int j = ja + (int)(threadIdx.x & 63); j < jb; j += 64) {
-    rowp[j] = (uint64_t)rm.row(j);
+    rowp[j] = (uint64_t)(uintptr_t)rm.row(j);
     xoffp[j] = rm.xoff(j);
   }
 }
@@ -558,8 +589,8 @@ struct NoPre {
 // FLAT: the waves split the rows' chunks evenly (StreamFlat; G must be 1) and the partial
 // row sums meet in ys through LDS float atomics (two waves at most share a row, so the sum
 // does not depend on their order); otherwise each wave streams whole groups of G rows.
-template <int R = 2, bool FLAT = false, class RM, class StageF, class EpiF, class PreF = NoPre,
-          class IssueF = NoPre>  // R in [2, 4]
+template <int R = 2, bool FLAT = false, int ES = 2, class RM, class StageF, class EpiF, class PreF = NoPre,
+          class IssueF = NoPre>  // R in [2, 4]; ES: bytes per weight (2 bf16, 1 FP8 with row scales)
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
                                          int K, int G, bool prefetch, StageF&& stage, EpiF&& epi, int pre_deps = 0,
                                          PreF&& pre = PreF{}, IssueF&& issue = IssueF{}) {
@@ -567,7 +598,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   const int ng = nrows / G;
   int ja, jb, fa, fb;
   if constexpr (FLAT) {
-    const int cpr = (K + kChunkCols - 1) / kChunkCols, nf = nrows * cpr;
+    const int cpr = (K + Chunk<ES>::kCols - 1) / Chunk<ES>::kCols, nf = nrows * cpr;
     fa = wave_start(nf, wave);
     fb = wave_start(nf, wave + 1);
     ja = fa / cpr;
@@ -578,8 +609,14 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     fa = ja;
     fb = jb;
   }
-  typename std::conditional<FLAT, StreamFlat, Stream>::type s;
+  typename std::conditional<FLAT, StreamFlatT<ES>, StreamT<ES>>::type s;
   u4 buf[R][NB];
+  if constexpr (ES == 1) {
+    // FP8 rows: wave 0 (no weight loads in flight) puts the task's row scales into LDS; the
+    // barrier of the dependency wait publishes them
+    if (threadIdx.x < 64)
+      for (int j = (int)threadIdx.x; j < nrows; j += 64) b.scl[j] = rm.scale(j);
+  }
   if (pre_deps > 0) {
     if (!wait_deps(A, b, t, 0, pre_deps)) return false;
     pre();
@@ -605,6 +642,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   float gacc = 0.f;
   auto emit = [&](int j, float v) {
+    if constexpr (ES == 1) v *= b.scl[j];  // G == 1 for FP8 rows
     if constexpr (FLAT) {
       if (lane == 0) atomicAdd(b.ys + j, v);
     } else {
@@ -644,21 +682,29 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
 
 // ------------------------------------------------------------------ row maps
 
+// Row maps give each task row's address; es = bytes per weight (2 bf16, 1 FP8), and for FP8
+// rows `scale` reads the row's fp32 scale.
 struct RmPlain {  // rows r0 + j of a [*, K] matrix
-  const uint16_t* W;
+  const void* W;
   int K, r0;
-  __device__ __forceinline__ const uint16_t* row(int j) const { return W + (size_t)(r0 + j) * K; }
+  int es = 2;
+  const float* S = nullptr;
+  __device__ __forceinline__ const void* row(int j) const { return (const uint8_t*)W + (size_t)(r0 + j) * K * es; }
+  __device__ __forceinline__ float scale(int j) const { return S[r0 + j]; }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
 struct RmGateUp {  // unit u -> (gate row u, up row u)
-  const uint16_t *Wg, *Wu;
+  const void *Wg, *Wu;
   int K, u0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  int es = 2;
+  const float *Sg = nullptr, *Su = nullptr;
+  __device__ __forceinline__ const void* row(int j) const {
     const uintptr_t g = (uintptr_t)Wg;
     const uintptr_t base = g + (uintptr_t)(j & 1) * ((uintptr_t)Wu - g);
-    return (const uint16_t*)base + (size_t)(u0 + (j >> 1)) * K;
+    return (const uint8_t*)base + (size_t)(u0 + (j >> 1)) * K * es;
   }
+  __device__ __forceinline__ float scale(int j) const { return ((j & 1) ? Su : Sg)[u0 + (j >> 1)]; }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
@@ -666,16 +712,33 @@ struct RmGateUp {  // unit u -> (gate row u, up row u)
 // k head g, slot == r+1 -> v head g; the unit's two rows are i and i + hd/2 of that head
 // (the pair RoPE rotates together).
 struct RmQKV {
-  const uint16_t *wq, *wk, *wv;
+  const void *wq, *wk, *wv;
   int g, r, hd, hh, K, u0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  int es = 2;
+  const float *sq = nullptr, *sk = nullptr, *sv = nullptr;
+  // the matrix (0 q, 1 k, 2 v) and row of task row j
+  __device__ __forceinline__ void where(int j, int& m, int& row) const {
     const int u = u0 + (j >> 1);
     const int slot = u / hh, i = u - slot * hh;
     const int rr = i + (j & 1) * hh;
-    if (slot < r) return wq + ((size_t)(g * r + slot) * hd + rr) * K;
-    const uintptr_t k = (uintptr_t)wk;
-    const uintptr_t base = k + (uintptr_t)(slot - r) * ((uintptr_t)wv - k);
-    return (const uint16_t*)base + ((size_t)g * hd + rr) * K;
+    m = slot < r ? 0 : slot - r + 1;
+    row = slot < r ? (g * r + slot) * hd + rr : g * hd + rr;
+  }
+  // (the matrix is picked by arithmetic on the addresses, not by indexing a pointer table,
+  // which the compiler would place in scratch memory)
+  static __device__ __forceinline__ uintptr_t pick(int m, const void* a, const void* b, const void* c) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b, z = (uintptr_t)c;
+    return x + (uintptr_t)(m >= 1) * (y - x) + (uintptr_t)(m >= 2) * (z - y);
+  }
+  __device__ __forceinline__ const void* row(int j) const {
+    int m, rw;
+    where(j, m, rw);
+    return (const uint8_t*)pick(m, wq, wk, wv) + (size_t)rw * K * es;
+  }
+  __device__ __forceinline__ float scale(int j) const {
+    int m, rw;
+    where(j, m, rw);
+    return ((const float*)pick(m, sq, sk, sv))[rw];
   }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
@@ -699,7 +762,7 @@ __device__ __forceinline__ void kv_stage_dma(const EngineArgs& A, Blk& b, int la
   const size_t n1 = (size_t)A.kv_len + 1;
   const float* ks = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 0) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
   const float* vs = reinterpret_cast<const float*>(A.kv + (((size_t)layer * 2 + 1) * A.nkv + g) * n1 * hd) + (size_t)p0 * hw;
-  float* kd = b.xs + kv_stage_k_off(A.hidden);
+  float* kd = b.xs + kv_stage_k_off(A.hidden, A.wfmt ? 2 * kChunkCols : kChunkCols);
   float* vd = b.scr + kv_stage_v_off(hd);
 #pragma unroll
   for (int k = 0; k < kKvStageDma; ++k) {
@@ -713,11 +776,12 @@ __device__ __forceinline__ void kv_stage_dma(const EngineArgs& A, Blk& b, int la
   }
 }
 
-template <bool KV>
+template <bool KV, int ES>
 __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
-  const RmQKV rm{wp<uint16_t>(A, L.w[LW_WQ]), wp<uint16_t>(A, L.w[LW_WK]), wp<uint16_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
+  const RmQKV rm{wp<uint8_t>(A, L.w[LW_WQ]), wp<uint8_t>(A, L.w[LW_WK]), wp<uint8_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0,
+                 ES, wscale<ES>(A, L.w[LW_WQ]), wscale<ES>(A, L.w[LW_WK]), wscale<ES>(A, L.w[LW_WV])};
   const int xin = L.act[LA_X_IN];
   auto issue = [&] {
     if constexpr (KV) {
@@ -727,9 +791,9 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
       kv_stage_dma(A, b, t.layer, t.a3, p0, (p1 < b.n ? p1 : b.n) - p0, wave - 1);
     }
   };
-  return run_gemv<kRingQKV>(
+  return run_gemv<kRingQKV, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, xin, b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      [&] { stage_vec(b, xin, b.x, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
       [&] {
         const int n = b.n;
         const size_t lay = (size_t)2 * A.nkv * (A.kv_len + 1) * hd;  // cache elements per layer
@@ -1051,22 +1115,26 @@ __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const Ta
 }
 
 struct RmCols {  // rows r0 + j of a [*, ld] matrix, columns starting at c0
-  const uint16_t* W;
+  const void* W;
   int ld, r0, c0;
-  __device__ __forceinline__ const uint16_t* row(int j) const { return W + (size_t)(r0 + j) * ld + c0; }
+  int es = 2;
+  const float* S = nullptr;
+  __device__ __forceinline__ const void* row(int j) const { return (const uint8_t*)W + ((size_t)(r0 + j) * ld + c0) * es; }
+  __device__ __forceinline__ float scale(int j) const { return S[r0 + j]; }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
 // Rows [u0, u1) of W_o times the merged attention output of KV group g (its r*hd columns):
 // one term of h = x + sum_g W_o[:, g] o_g. The group's split partials are merged while
 // staging; the first task of the group also stores the merged o_g (the attention output).
+template <int ES>
 __device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int r = A.nq / A.nkv, hd = A.hd, g = t.a0, K = r * hd;
-  const RmCols rm{wp<uint16_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K};
-  return run_gemv<kRingOproj>(
+  const RmCols rm{wp<uint8_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K, ES, wscale<ES>(A, L.w[LW_WO])};
+  return run_gemv<kRingOproj, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_merge(b, t.a4, t.a2, r, hd, pad512(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
+      [&] { stage_merge(b, t.a4, t.a2, r, hd, padc<ES>(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
       [&] {
         float* h = b.actp + L.act[LA_H] + t.u0;
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
@@ -1081,27 +1149,29 @@ __device__ __forceinline__ bool task_hinit(const EngineArgs& A, Blk& b, const Ta
 }
 
 
+template <int ES>
 __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden;
-  const RmGateUp rm{wp<uint16_t>(A, L.w[LW_GATE]), wp<uint16_t>(A, L.w[LW_UP]), K, t.u0};
-  return run_gemv<kRingFfn>(
+  const RmGateUp rm{wp<uint8_t>(A, L.w[LW_GATE]), wp<uint8_t>(A, L.w[LW_UP]), K, t.u0, ES, wscale<ES>(A, L.w[LW_GATE]),
+                    wscale<ES>(A, L.w[LW_UP])};
+  return run_gemv<kRingFfn, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      [&] { stage_vec(b, L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
 }
 
-template <bool FLAT>
+template <bool FLAT, int ES>
 __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.ffn;
-  const RmPlain rm{wp<uint16_t>(A, L.w[LW_DOWN]), K, t.u0};
-  return run_gemv<FLAT ? kRingFfn : 2, FLAT>(
+  const RmPlain rm{wp<uint8_t>(A, L.w[LW_DOWN]), K, t.u0, ES, wscale<ES>(A, L.w[LW_DOWN])};
+  return run_gemv<FLAT ? kRingFfn : 2, FLAT, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, pad512(K), nullptr, 0.f); },
+      [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, padc<ES>(K), nullptr, 0.f); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
@@ -1125,13 +1195,13 @@ __device__ __forceinline__ void best_pair(float& v, int& i) {
   }
 }
 
-template <bool GREEDY>
+template <bool GREEDY, int ES>
 __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const int K = A.hidden;
-  const RmPlain rm{wp<uint16_t>(A, A.w_lm_head), K, t.u0};
-  return run_gemv(
+  const RmPlain rm{wp<uint8_t>(A, A.w_lm_head), K, t.u0, ES, wscale<ES>(A, A.w_lm_head)};
+  return run_gemv<2, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, A.x_final, nullptr, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
+      [&] { stage_vec(b, A.x_final, nullptr, K, padc<ES>(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) A.out[t.u0 + i] = b.ys[i];
         if constexpr (GREEDY) {  // this task's largest logit (lowest index among equals) -> slot a0
@@ -1342,7 +1412,7 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // keeps lane-derived LDS addresses inside the task (not hoisted and spilled)
   const int wave = wave_id(), hl = lane & 15, q4 = lane >> 4;
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden));  // [np][HD]
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(b.xs + kv_stage_k_off(A.hidden, A.wfmt ? 2 * kChunkCols : kChunkCols));  // [np][HD]
   uint16_t* Vs = reinterpret_cast<uint16_t*>(b.scr + kv_stage_v_off(HD));       // [np][HD]
   // the cached rows were copied into LDS by the QKV task just before this one, or, in a launch
   // that does not run that task, are copied here; this wave's DMA has landed once vmcnt is 0,
@@ -2024,7 +2094,7 @@ __device__ __forceinline__ const EngineArgs& args_view() {
   return *(const EngineArgs*)p;
 }
 
-template <bool MLA, int RUN>
+template <bool MLA, int RUN, int ES = 2>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -2034,7 +2104,8 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   b.ys = b.xs + A.xs_floats;
   b.rowp = reinterpret_cast<uint64_t*>(b.ys + kYsFloats);
   b.xoffp = reinterpret_cast<int*>(b.rowp + kMaxTaskRows);
-  b.gs = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
+  b.scl = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
+  b.gs = b.scl + (ES == 1 ? kMaxTaskRows : 0);
   b.scr = b.gs + A.gs_floats;
   b.actp = A.act;
   b.act = make_rsrc(A.act, A.act_bytes);
@@ -2089,7 +2160,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       switch (t.type) {
         // K/V rows pass from a QKV task to the attention split after it through LDS only when
         // one launch runs both (a launch of all stages)
-        case T_QKV: ok = (t.a5 > 0 && all_stages) ? task_qkv<true>(A, b, t) : task_qkv<false>(A, b, t); break;
+        case T_QKV: ok = (t.a5 > 0 && all_stages) ? task_qkv<true, ES>(A, b, t) : task_qkv<false, ES>(A, b, t); break;
         case T_ATTN:
           gemv = false;
           if (t.a3 > 0) {
@@ -2103,11 +2174,11 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
           }
           else ok = rq <= 1 ? task_attn_hd<1>(A, b, t) : rq <= 2 ? task_attn_hd<2>(A, b, t) : task_attn_hd<4>(A, b, t);
           break;
-        case T_OPROJ_G: ok = task_oproj_g(A, b, t); break;
+        case T_OPROJ_G: ok = task_oproj_g<ES>(A, b, t); break;
         case T_HINIT: gemv = false; ok = task_hinit(A, b, t); break;
-        case T_GATEUP: ok = task_gateup(A, b, t); break;
-        case T_DOWN: ok = task_down<true>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic>(A, b, t); break;
+        case T_GATEUP: ok = task_gateup<ES>(A, b, t); break;
+        case T_DOWN: ok = task_down<true, ES>(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic, ES>(A, b, t); break;
         case T_ARGMAX:
           gemv = false;
           if constexpr (RUN == kRunDynamic) ok = task_argmax(A, b, t);
@@ -2124,9 +2195,9 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_MLA_ATTN: gemv = false; ok = task_mla_attn(A, b, t); break;
         case T_MLA_UV: gemv = false; ok = task_mla_uv(A, b, t); break;
         case T_OPROJ: ok = task_oproj(A, b, t); break;
-        case T_GATEUP: ok = task_gateup(A, b, t); break;
-        case T_DOWN: ok = task_down<false>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead<false>(A, b, t); break;
+        case T_GATEUP: ok = task_gateup<2>(A, b, t); break;
+        case T_DOWN: ok = task_down<false, 2>(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<false, 2>(A, b, t); break;
         case T_ROUTER: ok = task_router(A, b, t); break;
         case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
         case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
@@ -2179,12 +2250,16 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_stages(
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(EngineArgs A) {
   engine_body<false, kRunDynamic>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(EngineArgs A) {
+  engine_body<false, kRunStep, 1>(A);
+}
 
 }  // namespace dec
 
 // Host-side launch (used by the C ABI in api.cpp). run: 0 a whole step, 1 a range of stages,
 // 2 a whole step of a plan with a per-step length.
-static const void* engine_fn(int arch, int run) {
+static const void* engine_fn(int arch, int run, int wfmt = 0) {
+  if (wfmt) return (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
   if (run == 2) return (const void*)dec::dec_engine_gqa_dyn;
   return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
@@ -2192,14 +2267,15 @@ static const void* engine_fn(int arch, int run) {
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
                                                                          int run, bool cooperative, hipStream_t stream) {
-  static int configured_lds[2][3] = {{-1, -1, -1}, {-1, -1, -1}};
+  static int configured_lds[2][4] = {{-1, -1, -1, -1}, {-1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  if (run < 0 || run > 2 || (run == 2 && k != 0)) return hipErrorInvalidValue;
-  const void* fn = engine_fn(args->arch, run);
-  if (configured_lds[k][run] < lds_bytes) {
+  if (run < 0 || run > 2 || (run == 2 && k != 0) || (args->wfmt && (k != 0 || run != 0))) return hipErrorInvalidValue;
+  const void* fn = engine_fn(args->arch, run, args->wfmt);
+  const int slot = args->wfmt ? 3 : run;
+  if (configured_lds[k][slot] < lds_bytes) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
-    configured_lds[k][run] = lds_bytes;
+    configured_lds[k][slot] = lds_bytes;
   }
   void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
   if (!cooperative)  // one stage: no task waits on another of the same launch
@@ -2207,8 +2283,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
   return hipLaunchCooperativeKernel(fn, dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int lds_bytes, int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute(engine_fn(arch, 0), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu) {
+  hipError_t e = hipFuncSetAttribute(engine_fn(arch, 0, wfmt), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0), dec::kThreads, (size_t)lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0, wfmt), dec::kThreads, (size_t)lds_bytes);
 }

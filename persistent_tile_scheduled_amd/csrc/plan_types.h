@@ -27,7 +27,8 @@ constexpr int kMlaColBlock = 64;       // latent columns per absorb / W_UV task
 // together). K rows go after the staged hidden vector in xs, V rows after the attention merge
 // slots in the scratch region; both offsets are in floats.
 constexpr int kKvStageDma = 12;
-constexpr int kv_stage_k_off(int hidden) { return (hidden + kChunkCols - 1) / kChunkCols * kChunkCols; }
+// (cc: the staged vector's padding, kChunkCols columns for bf16 weights, twice that for FP8)
+constexpr int kv_stage_k_off(int hidden, int cc = kChunkCols) { return (hidden + cc - 1) / cc * cc; }
 constexpr int kv_stage_v_off(int hd) { return kWaves * 4 * (hd + 4) + 64; }
 
 // Task types. Every type runs the same five phases: issue loads of its static operand
@@ -166,6 +167,7 @@ struct EngineArgs {
   int32_t n_wg, rope_half, w_final_norm, w_lm_head, x_final;
   int32_t n_stages;            // stages of the plan
   int32_t w_embed;             // weight index of the token embedding (-1: none)
+  int32_t wfmt;                // weight format: 0 bf16, 1 FP8 E4M3 rows with fp32 row scales
   int32_t stage_lo, stage_hi;  // this launch runs the tasks of stages [stage_lo, stage_hi)
   int32_t xs_floats;           // LDS floats reserved for the staged input vector
   uint32_t act_bytes;          // size of the activation region

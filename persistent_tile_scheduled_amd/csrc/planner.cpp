@@ -91,7 +91,9 @@ struct Builder {
     act_floats += align_up(count, 64);  // 256-byte aligned buffers
     return off;
   }
-  void need_xs(int64_t K) { xs_floats_max = std::max<int64_t>(xs_floats_max, align_up(K, kChunkCols)); }
+  // staged input vectors are zero-padded to the GEMV's chunk: 512 bf16 or 1024 FP8 columns
+  int64_t chunk_cols() const { return fp8() ? 2 * kChunkCols : kChunkCols; }
+  void need_xs(int64_t K) { xs_floats_max = std::max<int64_t>(xs_floats_max, align_up(K, chunk_cols())); }
 
   int add(int w, int32_t type, int layer, int u0, int u1, std::vector<int32_t> deps, int signal,
           int signal2 = -1, int a0 = 0, int a1 = 0, int a2 = 0, int a3 = 0, int a4 = 0, int a5 = 0,
@@ -168,6 +170,14 @@ struct Builder {
     if (q.abi_version != DEC_ABI_VERSION) return fail(DEC_E_INVAL, "abi_version mismatch", st);
     if (q.n_layers < 1 || q.hidden < 8 || q.hidden % 8) return fail(DEC_E_SHAPE, "need n_layers >= 1 and hidden a positive multiple of 8", st);
     if (q.vocab < 0) return fail(DEC_E_SHAPE, "vocab < 0", st);
+    if (q.weight_format != DEC_WEIGHTS_BF16 && q.weight_format != DEC_WEIGHTS_FP8_E4M3)
+      return fail(DEC_E_SHAPE, "unknown weight_format", st);
+    if (q.weight_format == DEC_WEIGHTS_FP8_E4M3) {
+      if (q.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "FP8 weights: GQA family only", st);
+      if (q.hidden % 16 || q.ffn % 16 || (q.n_q_heads * q.head_dim) % 16)
+        return fail(DEC_E_SHAPE, "FP8 weights need hidden, ffn and n_q_heads * head_dim multiples of 16", st);
+      if (dyn) return fail(DEC_E_SHAPE, "FP8 weights: fixed-length plans only", st);
+    }
     if (!(q.rms_eps > 0.f) || !(q.rope_theta > 1.0)) return fail(DEC_E_SHAPE, "need rms_eps > 0 and rope_theta > 1", st);
     if (n < 0) return fail(DEC_E_CAPACITY, "kv_len < 0", st);
     if (n > (1 << 22)) return fail(DEC_E_CAPACITY, "kv_len above 4194304", st);
@@ -207,7 +217,18 @@ struct Builder {
   void add_weight(const std::string& name, int32_t dtype, std::vector<int64_t> dims) {
     int64_t e = 1;
     for (auto d : dims) e *= d;
-    P.weights.push_back({name, dtype, dims, e * (dtype == DEC_DTYPE_BF16 ? 2 : 4)});
+    P.weights.push_back({name, dtype, dims, e * (dtype == DEC_DTYPE_BF16 ? 2 : dtype == DEC_DTYPE_FP8 ? 1 : 4)});
+  }
+  bool fp8() const { return s.weight_format == DEC_WEIGHTS_FP8_E4M3; }
+  // A linear matrix [rows][cols]: bf16, or FP8 bytes followed by the fp32 row scales (the
+  // engine finds the scales at the matrix's weight index + 1).
+  void add_matrix(const std::string& name, int64_t rows, int64_t cols) {
+    if (!fp8()) {
+      add_weight(name, DEC_DTYPE_BF16, {rows, cols});
+      return;
+    }
+    add_weight(name, DEC_DTYPE_FP8, {rows, cols});
+    add_weight(name + ".scale", DEC_DTYPE_FP32, {rows});
   }
 
   // Canonical weight order: the bind order of the ABI.
@@ -221,12 +242,16 @@ struct Builder {
         ld.w[slot] = (int)P.weights.size();
         add_weight(p + nm, dt, dims);
       };
+      auto M = [&](int slot, const std::string& nm, int64_t rows, int64_t cols) {
+        ld.w[slot] = (int)P.weights.size();
+        add_matrix(p + nm, rows, cols);
+      };
       if (s.arch == DEC_ARCH_GQA) {
         W(LW_ATTN_NORM, "attn_norm", DEC_DTYPE_BF16, {d});
-        W(LW_WQ, "wq", DEC_DTYPE_BF16, {(int64_t)s.n_q_heads * s.head_dim, d});
-        W(LW_WK, "wk", DEC_DTYPE_BF16, {(int64_t)s.n_kv_heads * s.head_dim, d});
-        W(LW_WV, "wv", DEC_DTYPE_BF16, {(int64_t)s.n_kv_heads * s.head_dim, d});
-        W(LW_WO, "wo", DEC_DTYPE_BF16, {d, (int64_t)s.n_q_heads * s.head_dim});
+        M(LW_WQ, "wq", (int64_t)s.n_q_heads * s.head_dim, d);
+        M(LW_WK, "wk", (int64_t)s.n_kv_heads * s.head_dim, d);
+        M(LW_WV, "wv", (int64_t)s.n_kv_heads * s.head_dim, d);
+        M(LW_WO, "wo", d, (int64_t)s.n_q_heads * s.head_dim);
       } else {
         const int nh = s.n_q_heads;
         W(LW_ATTN_NORM, "attn_norm", DEC_DTYPE_BF16, {d});
@@ -251,16 +276,16 @@ struct Builder {
         W(LW_SUP, "shared.w_up", DEC_DTYPE_BF16, {S, d});
         W(LW_SDOWN, "shared.w_down", DEC_DTYPE_BF16, {d, S});
       } else {
-        W(LW_GATE, "w_gate", DEC_DTYPE_BF16, {s.ffn, d});
-        W(LW_UP, "w_up", DEC_DTYPE_BF16, {s.ffn, d});
-        W(LW_DOWN, "w_down", DEC_DTYPE_BF16, {d, s.ffn});
+        M(LW_GATE, "w_gate", s.ffn, d);
+        M(LW_UP, "w_up", s.ffn, d);
+        M(LW_DOWN, "w_down", d, s.ffn);
       }
     }
     if (s.vocab > 0) {
       P.w_final_norm = (int)P.weights.size();
       add_weight("final_norm", DEC_DTYPE_BF16, {d});
       P.w_lm_head = (int)P.weights.size();
-      add_weight("lm_head", DEC_DTYPE_BF16, {s.vocab, d});
+      add_matrix("lm_head", s.vocab, d);
       if (dyn) {  // a step without an input vector starts from its token's embedding row
         P.w_embed = (int)P.weights.size();
         add_weight("embed", DEC_DTYPE_BF16, {s.vocab, d});
@@ -278,7 +303,7 @@ struct Builder {
   // splits that fit the regions other stages already need are staged.
   void stage_attention_kv() {
     const int hd = s.head_dim;
-    const int64_t koff = kv_stage_k_off(s.hidden), voff = kv_stage_v_off(hd);
+    const int64_t koff = kv_stage_k_off(s.hidden, (int)chunk_cols()), voff = kv_stage_v_off(hd);
     auto candidate = [&](const TaskDesc& q, const TaskDesc& a) -> int64_t {  // LDS floats per region, or 0
       if (a.type != T_ATTN || q.type != T_QKV || q.layer != a.layer) return 0;
       const int64_t cnt = dyn ? (n + 1 + a.a2 - 1) / a.a2 : (int64_t)split_cached(n, a.a1, a.a2);
@@ -315,7 +340,8 @@ struct Builder {
   // LDS floats of the GQA plan: header, staged vector, row results, row tables, gains, scratch
   int64_t lds_floats(int64_t xs, int64_t scr) const {
     const int64_t gmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.q_lora_rank, (int64_t)s.kv_lora_rank});
-    return 64 + xs + kYsFloats + (int64_t)kMaxTaskRows * 12 / 4 + align_up(gmax / 2, 256) + scr;
+    // (+ the FP8 row-scale table: kMaxTaskRows floats)
+    return 64 + xs + kYsFloats + (int64_t)kMaxTaskRows * (fp8() ? 16 : 12) / 4 + align_up(gmax / 2, 256) + scr;
   }
 
   // ---------------------------------------------------------------- GQA layer stages

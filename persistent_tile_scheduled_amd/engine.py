@@ -10,7 +10,7 @@ from typing import Dict, Optional
 
 from . import binding as B
 
-_TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32"}
+_TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32", "fp8": "uint8"}  # FP8 bytes as uint8
 
 
 class DecodeEngine:

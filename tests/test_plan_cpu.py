@@ -14,7 +14,8 @@ from persistent_tile_scheduled_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MI355X = B.device_info()
-GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k"]
+GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k",
+               "tiny_fp8", "tiny_ragged_fp8", "small_gqa_fp8", "8b_4k_fp8"]
 MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k"]
 
 
@@ -295,6 +296,32 @@ def test_dynamic_plan_errors():
     assert ei.value.status == -2
     with pytest.raises(B.DecError):
         B.Plan(workloads.get_config("tiny"), device=MI355X, max_len=-1)
+
+
+def test_fp8_weights_plan():
+    """FP8 plans: each linear matrix is uint8 E4M3 followed by its fp32 row scales; the bytes
+    per step drop accordingly; other families, unaligned widths and per-step-length plans are
+    refused."""
+    p, cfg = plan("8b_4k_fp8")
+    q, _ = plan("8b_4k")
+    d = {x["name"]: x for x in p.weight_descs()}
+    assert d["layers.0.wq"]["dtype"] == "fp8" and tuple(d["layers.0.wq.scale"]["shape"]) == (4096,)
+    assert d["layers.0.attn_norm"]["dtype"] == "bf16" and d["lm_head"]["dtype"] == "fp8"
+    names = [x["name"] for x in p.weight_descs()]
+    assert names.index("layers.0.w_down.scale") == names.index("layers.0.w_down") + 1
+    a, b = p.sizes()["algorithmic_bytes_per_step"], q.sizes()["algorithmic_bytes_per_step"]
+    kv = 32 * 4097 * 2 * 8 * 128 * 2
+    assert a - kv == (b - kv - sum(x["bytes"] for x in p.weight_descs() if x["dtype"] == "bf16")) // 2 + \
+        sum(x["bytes"] for x in p.weight_descs() if x["dtype"] != "fp8")
+    for over in [{"hidden": 520}, {"ffn": 1000}]:
+        with pytest.raises(B.DecError) as ei:
+            plan("tiny_fp8", **over)
+        assert ei.value.status == -2
+    with pytest.raises(B.DecError) as ei:
+        plan("mla_tiny", weights="fp8")
+    assert ei.value.status == -2
+    with pytest.raises(B.DecError):
+        B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=200)
 
 
 def test_chiplet_placement_8b():
