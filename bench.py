@@ -78,9 +78,12 @@ def copy_calibration(nbytes, reps):
                       "launches": reps}), flush=True)
 
 
-def cpu_baseline(cfg, w, x, kv, eng=None):
-    """The fp64 oracle, as it stands, timed on a bounded sample of the same step: layer 0 and
-    the final norm + LM head; the per-token figure extrapolates layer 0 to all layers."""
+def cpu_baseline(cfg, w, x, kv, eng=None, budget_s=10.0):
+    """The fp64 oracle, as it stands, timed on a bounded sample of the same step: layers 0,
+    1, ... in order (each from the previous layer's oracle output) until about `budget_s`
+    seconds of oracle time or the whole stack, then the final norm + LM head; the per-token
+    figure extrapolates the mean layer time to all layers. Weights are copied to the host
+    before each layer's timed region."""
     import numpy as np
     import torch
 
@@ -100,29 +103,39 @@ def cpu_baseline(cfg, w, x, kv, eng=None):
         return cache[k]
 
     n = cfg["kv_len"]
-    xb = workloads.bf16_bits(x)
-    kv0 = workloads.bf16_bits(kv[0])
-    # host copies first (not timed): the oracle's timed region starts from host bf16 arrays.
-    # Routed experts: only those layer 0 selects (the engine's choice; the oracle fetches any
-    # other it picks itself)
-    for s in workloads.weight_specs(cfg):
-        if s.name.startswith("layers.0.experts."):
-            continue
-        if s.name.startswith("layers.0.") or s.name in ("final_norm", "lm_head"):
-            Wc(s.name)
-    if eng is not None and cfg["arch"] == "moe":
-        k = cfg["top_k"]
-        for e in eng.buffer("layers.0.topk")[:k].cpu().tolist():
-            for m in ("w_gate", "w_up", "w_down"):
-                Wc(f"layers.0.experts.{m}", int(e))
-    t0 = time.perf_counter()
-    xo, _ = oracle.layer(cfg, Wc, 0, oracle.widen_bf16(xb), kv0, n)
-    t1 = time.perf_counter()
+    specs = workloads.weight_specs(cfg)
+    xo = oracle.widen_bf16(workloads.bf16_bits(x))
+    layer_s, done = 0.0, 0
+    for l in range(cfg["n_layers"]):
+        # host copies first (not timed). Routed experts: those the GPU selected for this
+        # layer (the oracle fetches any other it picks itself)
+        cache.clear()
+        for s in specs:
+            if s.name.startswith(f"layers.{l}.") and not s.name.startswith(f"layers.{l}.experts."):
+                Wc(s.name)
+        if eng is not None and cfg["arch"] == "moe":
+            k = cfg["top_k"]
+            for e in eng.buffer(f"layers.{l}.topk")[:k].view(torch.int32).cpu().tolist():
+                for m in ("w_gate", "w_up", "w_down"):
+                    Wc(f"layers.{l}.experts.{m}", int(e))
+        kvl = workloads.bf16_bits(kv[l])
+        t0 = time.perf_counter()
+        xo, _ = oracle.layer(cfg, Wc, l, xo, kvl, n)
+        layer_s += time.perf_counter() - t0
+        done += 1
+        if layer_s >= budget_s:
+            break
+    head_s = 0.0
     has_head = cfg.get("vocab", 0) > 0
     if has_head:
+        cache.clear()
+        for s in specs:
+            if s.name.startswith("final_norm") or s.name.startswith("lm_head"):
+                Wc(s.name)
+        t0 = time.perf_counter()
         oracle.head(cfg, Wc, xo)
-    t2 = time.perf_counter()
-    per_token = (t1 - t0) * cfg["n_layers"] + (t2 - t1)
+        head_s = time.perf_counter() - t0
+    per_token = layer_s / done * cfg["n_layers"] + head_s
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
@@ -130,8 +143,8 @@ def cpu_baseline(cfg, w, x, kv, eng=None):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     return {"value": per_token * 1e6, "unit": "us/token", "cores": int(cores), "kind": "oracle",
-            "sample": f"layer 0 of {cfg['n_layers']} ({(t1 - t0):.2f} s) extrapolated x{cfg['n_layers']}"
-                      + (f" + final norm and LM head ({(t2 - t1):.2f} s)" if has_head else "")}
+            "sample": f"layers 0..{done - 1} of {cfg['n_layers']} ({layer_s:.2f} s) extrapolated x{cfg['n_layers'] / done:.2f}"
+                      + (f" + final norm and LM head ({head_s:.2f} s)" if has_head else "")}
 
 
 def generation(args, cfg, w, kv):
