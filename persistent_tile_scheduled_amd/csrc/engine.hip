@@ -1195,6 +1195,41 @@ __device__ __forceinline__ void best_pair(float& v, int& i) {
   }
 }
 
+// Selection keys: one unsigned 64-bit key per (score, index) whose order is the order of the
+// scores, the lower index first among equal scores. High word: the fp32 bits mapped to an
+// unsigned order (negative values bit-inverted, positive values with the sign bit set; -0
+// taken as +0, as the float compare does); low word: the inverted index. NaN gets key 0,
+// which is also the mark of an empty or retired slot, so a maximum is one 64-bit compare
+// with no tie branch.
+__device__ __forceinline__ uint64_t sel_key(float v, int i) {
+  const uint32_t u = __float_as_uint(v) == 0x80000000u ? 0u : __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t m = v == v ? 0xffffffffu : 0u;
+  return ((uint64_t)(o & m) << 32) | ((uint32_t)~i & m);
+}
+__device__ __forceinline__ int sel_index(uint64_t k) { return (int)~(uint32_t)k; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t k) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, true);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Largest key of the wave, returned wave-uniform: DPP exchanges within each 16-lane row (the
+// lane pairings of group_sum), then the four row maxima.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = umax64(k, dpp64<kQuadSwap1>(k));
+  k = umax64(k, dpp64<kQuadSwap2>(k));
+  k = umax64(k, dpp64<kRowHalfMirror>(k));
+  k = umax64(k, dpp64<kRowMirror>(k));
+  uint64_t r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * q) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * q);
+  return umax64(umax64(r[0], r[1]), umax64(r[2], r[3]));
+}
+
 template <bool GREEDY, int ES>
 __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const int K = A.hidden;
@@ -1919,8 +1954,7 @@ __device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const Tas
   float* z = b.xs;                       // [E]
   float* sg = b.xs + ((E + 255) & ~255);  // [E]
   float* bias = sg + ((E + 255) & ~255);  // [E]
-  float* sel = b.ys;                      // [top_k] sigma of the chosen experts
-  int* ids = reinterpret_cast<int*>(b.ys + 64);
+  int* ids = reinterpret_cast<int*>(b.ys);  // [top_k] chosen experts in rank order
   if (threadIdx.x < 64) {
     dma_to_lds(z, b.actp + L.act[LA_RLOGIT], E & ~3);
     dma_to_lds(bias, wp<float>(A, L.w[LW_RBIAS]), E & ~3);
@@ -1941,33 +1975,45 @@ __device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const Tas
     }
   }
   __syncthreads();
-  // z is padded with -inf to a multiple of 4, so the comparison loop reads 4 scores per LDS
-  // access; the loads of an unrolled block are independent
-  const int E4 = (E + 3) & ~3;
-  for (int e = threadIdx.x; e < E; e += kThreads) {
-    const float ze = z[e];
-    int r0 = 0, r1 = 0;
-#pragma unroll 8
-    for (int f = 0; f < E4; f += 4) {
-      const f4 v = *reinterpret_cast<const f4*>(z + f);
-      r0 += (v.x > ze || (v.x == ze && f < e)) ? 1 : 0;
-      r1 += (v.y > ze || (v.y == ze && f + 1 < e)) ? 1 : 0;
-      r0 += (v.z > ze || (v.z == ze && f + 2 < e)) ? 1 : 0;
-      r1 += (v.w > ze || (v.w == ze && f + 3 < e)) ? 1 : 0;
-    }
-    const int rank = r0 + r1;
-    if (rank < K) {
-      ids[rank] = e;
-      sel[rank] = sg[e];
+  // wave 0 picks the K largest z in K rounds. Each lane keeps the largest selection key of the
+  // scores it owns (e = lane, lane + 64, ...); the wave-wide maximum names the round's
+  // winner, whose owner retires it (NaN in LDS: key 0) and rescans its own scores. The picks
+  // come out in decreasing z, lower index first among equal values.
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // a lane's scores four at a time: z spans E rounded up to 256 floats, so the four reads
+    // stay inside it, and slots at or past E count as empty
+    auto scan = [&]() {
+      uint64_t m = 0;
+      for (int e0 = lane; e0 < E; e0 += 256) {
+        float a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = z[e0 + 64 * j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m = umax64(m, e0 + 64 * j < E ? sel_key(a[j], e0 + 64 * j) : 0ull);
+      }
+      return m;
+    };
+    uint64_t lk = scan();
+    for (int k = 0; k < K; ++k) {
+      const uint64_t w = wave_max_key(lk);
+      const int bi = w == 0 ? 0 : sel_index(w);  // (key 0 only if every remaining score is NaN)
+      if (lane == 0) ids[k] = bi;
+      if (lane == (bi & 63)) {
+        z[bi] = __int_as_float(0x7fc00000);
+        lk = scan();
+      }
     }
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    float sum = 0.f;
-    for (int k = 0; k < K; ++k) sum += sel[k];  // fixed order: by rank
-    for (int k = threadIdx.x; k < K; k += 64) {
-      cst(b.act, (uint32_t)(L.act[LA_TOPK] + k) * 4u, __int_as_float(ids[k]));
-      cst(b.act, (uint32_t)(L.act[LA_TOPK] + K + k) * 4u, sel[k] / sum);
+  if (threadIdx.x < 64) {  // lane k < K holds pick k (top_k <= 64)
+    const int k = threadIdx.x;
+    const int id = k < K ? ids[k] : 0;
+    const float s = k < K ? sg[id] : 0.f;
+    const float sum = wave_sum(s);
+    if (k < K) {
+      cst(b.act, (uint32_t)(L.act[LA_TOPK] + k) * 4u, __int_as_float(id));
+      cst(b.act, (uint32_t)(L.act[LA_TOPK] + K + k) * 4u, s / sum);
     }
   }
   return true;

@@ -74,7 +74,8 @@ def check_mla_layer(eng, cfg, l, t, W, kv_bits, tol=LAYER_TOL, same_input=None):
 
 
 CASES = [("mla_tiny", 0, None), ("mla_tiny", 1, None), ("mla_tiny", 2, 0), ("mla_tiny", 3, 20000),
-         ("mla_small", 0, None), ("moe_tiny", 0, None), ("moe_tiny", 5, 1), ("moe_small", 0, None)]
+         ("mla_small", 0, None), ("moe_tiny", 0, None), ("moe_tiny", 5, 1), ("moe_small", 0, None),
+         ("moe_wide_tiny", 0, None)]  # 301 experts: several score passes per lane, ragged tail
 
 
 @pytest.mark.parametrize("name,seed,kv_len", CASES)
@@ -99,6 +100,42 @@ def test_small_mla_full_parity(name, seed, kv_len):
         print(f"[parity] layer {l}: max rel error {max(errs.values()):.2e}", flush=True)
     assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
     check_coverage(eng)
+
+
+def test_topk_exact_ties_go_to_the_lower_index():
+    """Exactly equal scores from duplicated router rows and biases. Layer 0: experts 0..39 in
+    20 equal pairs (2i, 2i+1), raised above the rest, so the top 13 split a pair at the
+    boundary; layer 1: experts 40..300 all equal and on top, so the picks are 40..52. The
+    selection must be the oracle rule's on the engine's own logits: decreasing score, the lower
+    index first among equals."""
+    cfg = dict(workloads.get_config("moe_wide_tiny"))
+    w, x, kv = workloads.generate(cfg, seed=2, device="cuda")
+    r, b = w["layers.0.router"], w["layers.0.router_bias"]
+    r[1:40:2].copy_(r[0:40:2])
+    b[0:40:2] += 1.0
+    b[1:40:2].copy_(b[0:40:2])
+    r, b = w["layers.1.router"], w["layers.1.router_bias"]
+    r[40:].copy_(r[7].expand_as(r[40:]))
+    b[40:].fill_(float(b[7]) + 1.0)
+    eng = _engine(cfg, w)
+    eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    k = cfg["top_k"]
+    for l in range(cfg["n_layers"]):
+        ids, wts = engine_topk(eng, cfg, l)
+        r_gpu = eng.buffer(f"layers.{l}.router_logits").cpu().numpy().astype(np.float64)
+        if l == 0:  # identical rows give identical logits
+            assert np.array_equal(r_gpu[1:40:2], r_gpu[0:40:2])
+            assert len(set(ids.tolist()) & set(range(40))) == k, ids
+            assert k % 2 == 1 and sum((e ^ 1) in ids.tolist() for e in ids.tolist()) == k - 1
+        else:
+            assert np.all(r_gpu[40:] == r_gpu[40])
+            assert ids.tolist() == list(range(40, 40 + k)), ids
+        same = O.route(r_gpu, W(f"layers.{l}.router_bias"), k)
+        assert np.array_equal(ids, same["topk"]), (l, ids, same["topk"])
+        assert rel_l2(wts, same["w"]) <= 1e-5
 
 
 @pytest.mark.parametrize("name", ["mla_small", "moe_small"])

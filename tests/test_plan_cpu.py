@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MI355X = B.device_info()
 GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k",
                "tiny_fp8", "tiny_ragged_fp8", "small_gqa_fp8", "8b_4k_fp8"]
-MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k"]
+MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k", "moe_wide_tiny"]
 
 
 def plan(name, dev=MI355X, **over):
