@@ -132,6 +132,30 @@ def test_small_gqa_full_parity(name, seed):
     check_coverage(eng)
 
 
+@pytest.mark.parametrize("kv_len,staged", [(700, True), (40000, False)])
+def test_head_dim_256_three_heads_per_group(kv_len, staged):
+    """The largest head size (256) with 3 query heads per KV head (a group that fills neither
+    a power of two nor the 4-head tile): short splits take the matrix-core path from LDS,
+    splits too long to stage take the vector-ALU path."""
+    cfg = dict(workloads.get_config("tiny_hd256_g3"), kv_len=kv_len)
+    print(f"[parity] tiny_hd256_g3 kv_len={kv_len}", flush=True)
+    w, x, kv = workloads.generate(cfg, seed=4, device="cuda")
+    eng = _engine()(cfg, w)
+    attn = [t for t in eng.plan.tasks() if t["type"] == 2]
+    assert any((t["kv_staged"] > 0) == staged for t in attn), staged
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    kvb = workloads.bf16_bits(kv)
+    res = O.forward(cfg, W, workloads.bf16_bits(x), kvb)
+    for l, t in enumerate(res["layers"]):
+        check_layer_trace(eng, l, t, TRACE_GQA)
+        check_kv_slot(cfg, kvb, l, t, same_input=(l == 0))
+    assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
+    check_coverage(eng)
+
+
 @pytest.mark.parametrize("name", ["small_gqa", "tiny"])
 def test_multi_step_changing_input(name):
     """Three steps with different inputs: each matches the oracle (epochs, counters and the

@@ -75,7 +75,8 @@ def check_mla_layer(eng, cfg, l, t, W, kv_bits, tol=LAYER_TOL, same_input=None):
 
 CASES = [("mla_tiny", 0, None), ("mla_tiny", 1, None), ("mla_tiny", 2, 0), ("mla_tiny", 3, 20000),
          ("mla_small", 0, None), ("moe_tiny", 0, None), ("moe_tiny", 5, 1), ("moe_small", 0, None),
-         ("moe_wide_tiny", 0, None)]  # 301 experts: several score passes per lane, ragged tail
+         ("moe_wide_tiny", 0, None),  # 301 experts: several score passes per lane, ragged tail
+         ("moe_max_route", 0, None)]  # the router's limits: 4096 experts, top 64
 
 
 @pytest.mark.parametrize("name,seed,kv_len", CASES)
