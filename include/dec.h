@@ -217,7 +217,7 @@ int64_t dec_plan_n_stages(const struct dec_plan* plan);
 dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo,
                            int32_t stage_hi, void* stream);
 
-/* ---- a plan whose length is read per step (GQA models) ----
+/* ---- a plan whose length is read per step ----
  * The pages fix every shape ahead of time, while the cache grows by one position per token
  * (Static Compilation page, sections 5.5 and 7.1: static shapes against a growing KV cache;
  * TileRT audit page: any shape change means a rebuild). This plan is built once for a largest
@@ -229,8 +229,8 @@ dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void*
  * max_len; at a shorter position the same splits are shorter (a split may be empty and
  * contributes nothing). dec_plan_sizes reports kv_bytes for max_len + 1 slots and the
  * algorithmic bytes of a step at position max_len. When vocab > 0 the weight list ends with
- * "embed" bf16 [vocab][hidden], the token embedding. Errors: as dec_plan_create_for; SHAPE for
- * the latent-attention (MLA, MoE) families, whose plans have a fixed length.
+ * "embed" bf16 [vocab][hidden], the token embedding. Every family (GQA, MLA, MLA + MoE) has
+ * these plans; FP8 weights do not (SHAPE). Errors: as dec_plan_create_for.
  *
  * dec_step_dynamic: one step, ONE kernel launch on `stream`.
  *   state : device int32[4], 16-byte aligned, caller-owned: {position p, token, steps, 0}.
@@ -242,7 +242,8 @@ dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void*
  *           state[1]. Consecutive calls therefore run a greedy generation loop on the device
  *           with no host work between tokens.
  *   x     : bf16 [hidden] or NULL (needs vocab > 0).
- *   kv    : bf16 [n_layers][2][n_kv_heads][max_len + 1][head_dim].
+ *   kv    : bf16 [n_layers][2][n_kv_heads][max_len + 1][head_dim] (GQA), or the latent
+ *           cache bf16 [n_layers][max_len + 1][kv_lora_rank + qk_rope] (MLA, MoE).
  *   out   : as dec_step.
  * An out-of-range position or token makes the whole step do nothing (state unchanged); the
  * sticky status then reports DEC_E_CAPACITY with the values read (dec_plan_status).

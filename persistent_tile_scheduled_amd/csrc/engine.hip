@@ -1655,7 +1655,9 @@ __device__ __forceinline__ bool task_mla_absorb(const EngineArgs& A, Blk& b, con
 __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int kl = A.kl, KR = kl + A.dr, KP = (KR + 31) & ~31, NKS = KP >> 5, nh = A.nq;
-  const int n = b.n, p0 = t.u0, p1 = t.u1;  // latent plans have a fixed length: the planned split
+  // split a1 of a2 over positions [0, n]; a plan with a per-step length can leave a split
+  // empty at small positions: it then stores the neutral partial (M = -inf, Lr = 0, O = 0)
+  const int n = b.n, p0 = split_pos(n, t.a1, t.a2), p1 = split_pos(n, t.a1 + 1, t.a2);
   const int wave = wave_id(), lane = threadIdx.x & 63, hl = lane & 15, g = lane >> 4;
   const uint16_t* lat = A.kv + (size_t)t.layer * (A.kv_len + 1) * KR;
   u4* QL = reinterpret_cast<u4*>(b.xs);                                   // [NKS][2][64]
@@ -1697,9 +1699,9 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
   // a chunk of cached positions only (< kv_len) can be fetched before the wait (not by
   // wave 0, whose dependency polls would queue behind the copies)
   const bool pre = (p0 + kMlaChunk < p1 ? p0 + kMlaChunk : p1) <= n;
-  if (pre) dma_chunk(p0, 1);
+  if (pre && p1 > p0) dma_chunk(p0, 1);
   if (!wait_deps(A, b, t)) return false;
-  if (!pre) dma_chunk(p0, 0);
+  if (!pre && p1 > p0) dma_chunk(p0, 0);
   if (wave == 0) dma_to_lds(reinterpret_cast<float*>(QL), b.actp + L.act[LA_QOP], NKS * 512);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   zero_pad(pre ? 1 : 0);
@@ -2243,7 +2245,12 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_OPROJ: ok = task_oproj(A, b, t); break;
         case T_GATEUP: ok = task_gateup<2>(A, b, t); break;
         case T_DOWN: ok = task_down<false, 2>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead<false, 2>(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic, 2>(A, b, t); break;
+        case T_ARGMAX:
+          gemv = false;
+          if constexpr (RUN == kRunDynamic) ok = task_argmax(A, b, t);
+          else ok = false;
+          break;
         case T_ROUTER: ok = task_router(A, b, t); break;
         case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
         case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
@@ -2296,6 +2303,9 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_stages(
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(EngineArgs A) {
   engine_body<false, kRunDynamic>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_dyn(EngineArgs A) {
+  engine_body<true, kRunDynamic>(A);
+}
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(EngineArgs A) {
   engine_body<false, kRunStep, 1>(A);
 }
@@ -2307,7 +2317,7 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(Engi
 static const void* engine_fn(int arch, int run, int wfmt = 0) {
   if (wfmt) return (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
-  if (run == 2) return (const void*)dec::dec_engine_gqa_dyn;
+  if (run == 2) return arch == 0 ? (const void*)dec::dec_engine_gqa_dyn : (const void*)dec::dec_engine_mla_dyn;
   return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
 }
 
@@ -2315,7 +2325,7 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
                                                                          int run, bool cooperative, hipStream_t stream) {
   static int configured_lds[2][4] = {{-1, -1, -1, -1}, {-1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  if (run < 0 || run > 2 || (run == 2 && k != 0) || (args->wfmt && (k != 0 || run != 0))) return hipErrorInvalidValue;
+  if (run < 0 || run > 2 || (args->wfmt && (k != 0 || run != 0))) return hipErrorInvalidValue;
   const void* fn = engine_fn(args->arch, run, args->wfmt);
   const int slot = args->wfmt ? 3 : run;
   if (configured_lds[k][slot] < lds_bytes) {

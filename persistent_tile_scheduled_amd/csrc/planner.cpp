@@ -573,7 +573,6 @@ struct Builder {
     P.shape = s;
     P.kv_len = n;
     P.dynamic = dyn;
-    if (dyn && s.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "plans with a per-step length support the GQA family only", st);
     P.dev = dev;
     P.n_wg = n_wg;
     P.layers.assign(s.n_layers, LayerDesc{});

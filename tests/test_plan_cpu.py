@@ -290,9 +290,28 @@ def test_dynamic_plan_layout(name, max_len):
         assert any(t["kv_staged"] > 0 for t in att)
 
 
+@pytest.mark.parametrize("name,max_len", [("mla_tiny", 300), ("moe_tiny", 100), ("mla_8k", 8192)])
+def test_dynamic_latent_plan_layout(name, max_len):
+    """Latent-attention plans with a per-step length: the fixed plan's weights, a latent cache
+    of max_len + 1 slots, and the attention splits planned over max_len + 1 positions, split
+    a1 of a2 covering [(n+1) a1 / a2, (n+1) (a1+1) / a2) at position n."""
+    cfg = dict(workloads.get_config(name))
+    p = B.Plan(cfg, device=MI355X, max_len=max_len)
+    fixed = B.Plan(dict(cfg, kv_len=max_len), device=MI355X)
+    assert [d["name"] for d in p.weight_descs()] == [d["name"] for d in fixed.weight_descs()]
+    KR = cfg["kv_lora_rank"] + cfg["qk_rope"]
+    assert p.sizes()["kv_bytes"] == 2 * cfg["n_layers"] * (max_len + 1) * KR
+    att = sorted((t["aux1"], t["unit_begin"], t["unit_end"], t["aux2"])
+                 for t in p.tasks() if t["type"] == 11 and t["layer"] == 0)
+    S = att[0][3]
+    assert [a[0] for a in att] == list(range(S))
+    for sp, u0, u1, s_ in att:
+        assert s_ == S and u0 == (max_len + 1) * sp // S and u1 == (max_len + 1) * (sp + 1) // S
+
+
 def test_dynamic_plan_errors():
     with pytest.raises(B.DecError) as ei:
-        B.Plan(workloads.get_config("mla_tiny"), device=MI355X, max_len=100)
+        B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=100)
     assert ei.value.status == -2
     with pytest.raises(B.DecError):
         B.Plan(workloads.get_config("tiny"), device=MI355X, max_len=-1)
