@@ -229,8 +229,9 @@ dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void*
  * max_len; at a shorter position the same splits are shorter (a split may be empty and
  * contributes nothing). dec_plan_sizes reports kv_bytes for max_len + 1 slots and the
  * algorithmic bytes of a step at position max_len. When vocab > 0 the weight list ends with
- * "embed" bf16 [vocab][hidden], the token embedding. Every family (GQA, MLA, MLA + MoE) has
- * these plans; FP8 weights do not (SHAPE). Errors: as dec_plan_create_for.
+ * "embed" bf16 [vocab][hidden], the token embedding (bf16 also with FP8 weights: a row is
+ * read, not multiplied). Every family (GQA, MLA, MLA + MoE) and both weight formats have these
+ * plans. Errors: as dec_plan_create_for.
  *
  * dec_step_dynamic: one step, ONE kernel launch on `stream`.
  *   state : device int32[4], 16-byte aligned, caller-owned: {position p, token, steps, 0}.

@@ -2309,13 +2309,16 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_dyn(Eng
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(EngineArgs A) {
   engine_body<false, kRunStep, 1>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8_dyn(EngineArgs A) {
+  engine_body<false, kRunDynamic, 1>(A);
+}
 
 }  // namespace dec
 
 // Host-side launch (used by the C ABI in api.cpp). run: 0 a whole step, 1 a range of stages,
 // 2 a whole step of a plan with a per-step length.
 static const void* engine_fn(int arch, int run, int wfmt = 0) {
-  if (wfmt) return (const void*)dec::dec_engine_gqa_f8;
+  if (wfmt) return run == 2 ? (const void*)dec::dec_engine_gqa_f8_dyn : (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
   if (run == 2) return arch == 0 ? (const void*)dec::dec_engine_gqa_dyn : (const void*)dec::dec_engine_mla_dyn;
   return arch == 0 ? (const void*)dec::dec_engine_gqa : (const void*)dec::dec_engine_mla;
@@ -2323,11 +2326,11 @@ static const void* engine_fn(int arch, int run, int wfmt = 0) {
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
                                                                          int run, bool cooperative, hipStream_t stream) {
-  static int configured_lds[2][4] = {{-1, -1, -1, -1}, {-1, -1, -1, -1}};
+  static int configured_lds[2][5] = {{-1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  if (run < 0 || run > 2 || (args->wfmt && (k != 0 || run != 0))) return hipErrorInvalidValue;
+  if (run < 0 || run > 2 || (args->wfmt && (k != 0 || run == 1))) return hipErrorInvalidValue;
   const void* fn = engine_fn(args->arch, run, args->wfmt);
-  const int slot = args->wfmt ? 3 : run;
+  const int slot = args->wfmt ? 3 + (run == 2) : run;
   if (configured_lds[k][slot] < lds_bytes) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;

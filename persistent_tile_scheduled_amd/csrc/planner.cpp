@@ -176,7 +176,6 @@ struct Builder {
       if (q.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "FP8 weights: GQA family only", st);
       if (q.hidden % 16 || q.ffn % 16 || (q.n_q_heads * q.head_dim) % 16)
         return fail(DEC_E_SHAPE, "FP8 weights need hidden, ffn and n_q_heads * head_dim multiples of 16", st);
-      if (dyn) return fail(DEC_E_SHAPE, "FP8 weights: fixed-length plans only", st);
     }
     if (!(q.rms_eps > 0.f) || !(q.rope_theta > 1.0)) return fail(DEC_E_SHAPE, "need rms_eps > 0 and rope_theta > 1", st);
     if (n < 0) return fail(DEC_E_CAPACITY, "kv_len < 0", st);

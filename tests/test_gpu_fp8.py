@@ -53,3 +53,47 @@ def test_fp8_plan_rejects_stage_launches():
 
 def test_8b_4k_fp8_sampled_layers():
     _teacher_forced_check("8b_4k_fp8", [0, 1, 31])
+
+
+def test_fp8_plan_with_per_step_length():
+    """FP8 weights in a plan that reads its position per step: positions 0, 1, L/2 and L
+    against the oracle decoding the same bytes, then three greedy steps that start from the
+    embedding row of the token the previous step chose (teacher-forced on the engine's tokens
+    and cache). The token is the argmax of the engine's own fp32 logits, lowest index first."""
+    from persistent_tile_scheduled_amd.engine import DecodeEngine
+    cfg = workloads.get_config("tiny_fp8")
+    M = cfg["kv_len"]
+    w, x, kv = workloads.generate(cfg, seed=6, device="cuda", kv_len=M)
+    w["embed"] = workloads.generate_embedding(cfg, seed=6, device="cuda")
+    eng = DecodeEngine(cfg, w, max_len=M)
+    W = HostWeights(w)
+    argmax_low = lambda v: int(np.flatnonzero(v == v.max())[0])
+    steps = 0
+    for p in [0, 1, M // 2, M]:
+        print(f"[fp8 dynamic] position {p}", flush=True)
+        kvb = workloads.bf16_bits(kv)
+        eng.set_state(p, 3)
+        got = eng.step_dynamic(kv, x).clone().cpu().numpy()
+        eng.status()
+        steps += 1
+        st = eng.read_state()
+        assert st[0] == p + 1 and st[2] == 1 and st[1] == argmax_low(got), st
+        res = O.forward(dict(cfg, kv_len=p), W, workloads.bf16_bits(x), kvb, kv_len=p)
+        for l, t in enumerate(res["layers"]):
+            check_layer_trace(eng, l, t, TRACE_GQA)
+        assert rel_l2(got, res["out"]) <= LOGIT_TOL, p
+    emb = workloads.bf16_bits(w["embed"])
+    tok, p0 = 5, M - 3
+    eng.set_state(p0, tok)
+    for i in range(3):
+        print(f"[fp8 greedy] step {i} token {tok}", flush=True)
+        kvb = workloads.bf16_bits(kv)
+        got = eng.step_dynamic(kv).clone().cpu().numpy()
+        eng.status()
+        steps += 1
+        st = eng.read_state()
+        assert st[0] == p0 + i + 1 and st[1] == argmax_low(got), st
+        res = O.forward(dict(cfg, kv_len=p0 + i), W, emb[tok], kvb, kv_len=p0 + i)
+        assert rel_l2(got, res["out"]) <= LOGIT_TOL, i
+        tok = st[1]
+    check_coverage(eng, steps=steps)

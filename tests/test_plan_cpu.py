@@ -311,7 +311,7 @@ def test_dynamic_latent_plan_layout(name, max_len):
 
 def test_dynamic_plan_errors():
     with pytest.raises(B.DecError) as ei:
-        B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=100)
+        B.Plan(dict(workloads.get_config("mla_tiny"), weights="fp8"), device=MI355X, max_len=100)
     assert ei.value.status == -2
     with pytest.raises(B.DecError):
         B.Plan(workloads.get_config("tiny"), device=MI355X, max_len=-1)
@@ -319,8 +319,8 @@ def test_dynamic_plan_errors():
 
 def test_fp8_weights_plan():
     """FP8 plans: each linear matrix is uint8 E4M3 followed by its fp32 row scales; the bytes
-    per step drop accordingly; other families, unaligned widths and per-step-length plans are
-    refused."""
+    per step drop accordingly; other families and unaligned widths are refused. A plan with a
+    per-step length has the same matrices plus a bf16 token embedding."""
     p, cfg = plan("8b_4k_fp8")
     q, _ = plan("8b_4k")
     d = {x["name"]: x for x in p.weight_descs()}
@@ -339,8 +339,9 @@ def test_fp8_weights_plan():
     with pytest.raises(B.DecError) as ei:
         plan("mla_tiny", weights="fp8")
     assert ei.value.status == -2
-    with pytest.raises(B.DecError):
-        B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=200)
+    dyn = B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=200)
+    dd = {x["name"]: x for x in dyn.weight_descs()}
+    assert dd["layers.0.wq"]["dtype"] == "fp8" and dd["embed"]["dtype"] == "bf16"
 
 
 def test_chiplet_placement_8b():
