@@ -106,6 +106,7 @@ def test_latent_dynamic_equals_fixed_plan_at_its_length():
     """At position kv_len the latent plan with a per-step length computes what the fixed plan
     for kv_len does (same split count when max_len + 1 rounds to the same number of splits)."""
     from persistent_tile_scheduled_amd.engine import DecodeEngine
+    print("[dynamic] mla_small: per-step-length plan against the fixed plan", flush=True)
     cfg = workloads.get_config("mla_small")
     n = cfg["kv_len"]
     w, x, kv = workloads.generate(cfg, seed=5, device="cuda")

@@ -109,6 +109,7 @@ def test_topk_exact_ties_go_to_the_lower_index():
     boundary; layer 1: experts 40..300 all equal and on top, so the picks are 40..52. The
     selection must be the oracle rule's on the engine's own logits: decreasing score, the lower
     index first among equals."""
+    print("[ties] moe_wide_tiny seed=2", flush=True)
     cfg = dict(workloads.get_config("moe_wide_tiny"))
     w, x, kv = workloads.generate(cfg, seed=2, device="cuda")
     r, b = w["layers.0.router"], w["layers.0.router_bias"]
