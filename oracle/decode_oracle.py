@@ -173,6 +173,12 @@ def softmax(s: np.ndarray) -> np.ndarray:
     return e / np.sum(e, axis=-1, keepdims=True)
 
 
+def kv_group(h: int, n_q: int, n_kv: int) -> int:
+    """The KV head query head h reads under grouped-query attention: contiguous groups of
+    n_q / n_kv query heads share one KV head (reading R8)."""
+    return (h * n_kv) // n_q
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
     """One query against n keys: o = softmax(scale * K q) V.  K [n][d], V [n][dv]."""
     p = softmax(scale * (K @ q))
@@ -275,7 +281,7 @@ def gqa_layer(cfg: dict, W: Callable, l: int, x: np.ndarray, kv_layer, kv_len: i
         Kc = np.concatenate([widen_bf16(kvl[0, g, :kv_len]), k16[g][None, :]], axis=0)
         Vc = np.concatenate([widen_bf16(kvl[1, g, :kv_len]), v16[g][None, :]], axis=0)
         for h in range(nq):
-            if (h * nkv) // nq == g:
+            if kv_group(h, nq, nkv) == g:
                 o[h] = attend(q[h], Kc, Vc, scale)
     t["attn"] = o.reshape(-1)
     h_ = x + linear_bits(W, p + "wo", t["attn"])

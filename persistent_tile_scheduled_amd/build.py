@@ -2,8 +2,13 @@
 
     python -m persistent_tile_scheduled_amd.build
 
-Every source is compiled with hipcc for gfx950 only. Packed fp32 instructions are switched
-off for the device code (-packed-fp32-ops).
+Every source is compiled with hipcc for gfx950 only. Packed fp32 instructions (v_pk_fma_f32,
+v_pk_mul_f32, v_pk_add_f32) are switched off for the device code with
+`-Xclang -target-feature -Xclang -packed-fp32-ops`. hipcc passes that flag to both of its
+compilation passes: the gfx950 device pass honours it (a float2 multiply-add compiles to one
+v_pk_fma_f32 without it and to two v_fma_f32 with it), while the x86 host pass, which has no
+such feature, prints "'-packed-fp32-ops' is not a recognized feature for this target
+(ignoring feature)" and ignores it.
 """
 import os
 import subprocess

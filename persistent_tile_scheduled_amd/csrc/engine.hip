@@ -64,17 +64,24 @@ __device__ __forceinline__ u4 ldg_nt(const void* p) { return __builtin_nontempor
 // neither the L2 write-back (buffer_wbl2) of an agent-scope release fence nor the L2
 // invalidate (buffer_inv) of an acquire fence, which measure 1-9 us each on MI355X.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kSC0 = 1;           // cache-policy bit SC0: the load misses in the compute unit's L1
 constexpr int kSC1 = 16;          // cache-policy bit SC1 (agent scope)
+constexpr int kCoh = kSC0 | kSC1; // loads of the new cache row: agent-coherent, and missing in L1
 constexpr int kNT = 2;            // cache-policy bit NT (streamed once: non-temporal)
-// Cache policy of loads of produced data. Every activation address is written once per step
-// (per-layer buffers, write-through SC1 stores) and read only after all of its writers have
-// signalled; lines cached by an earlier kernel are gone at the next launch (stream order).
-// So a reader's L2 never holds a stale copy, and plain L2-cached loads (0) are enough: the
-// 32 workgroups of an XCD then share one fetch of a broadcast vector.
-#ifndef DEC_ACT_CPOL
-#define DEC_ACT_CPOL 0
-#endif
-constexpr int kActCpol = DEC_ACT_CPOL;
+// Cache policy of loads of produced data (activations written in this step). A reader reads an
+// address only after all of its writers have signalled. A value written once per step by plain
+// (SC1, write-through) stores may sit in the writer's L1 and its XCD's L2, but only as the value
+// itself: such data is loaded with SC0 (missing in L1, which could also hold lines of this
+// workgroup's earlier steps' tasks) and served by the XCD's L2, where the 32 workgroups of an XCD
+// share one fetch of a broadcast vector. A buffer that is first stored and then accumulated with
+// agent-scope atomics -- the GQA residual h (initialised by the previous layer's down
+// projection, then added into by the per-group O-projections) and the latent-attention output
+// (cleared by the latent-row append, then added into by the W_UV tasks) -- can leave the stored,
+// pre-atomic line in the storing workgroup's L1 and its XCD's L2, since the atomics of the other
+// workgroups do not update those copies: its readers load it agent-coherently (kCoh), from
+// beyond every L2. (Found as one O-projection row that read whole heads of the latent output as
+// the zeros its own workgroup had stored.)
+constexpr int kActCpol = kSC0;
 constexpr int kVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -83,6 +90,10 @@ __device__ __forceinline__ float cld(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kActCpol));
 }
 __device__ __forceinline__ u4 cld4u(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kActCpol); }
+// a word of an atomically accumulated buffer (see kActCpol)
+__device__ __forceinline__ float cld_coh(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoh));
+}
 __device__ __forceinline__ f4 cld4(rsrc_t r, uint32_t off) { return __builtin_bit_cast(f4, cld4u(r, off)); }
 __device__ __forceinline__ void cst(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, kSC1);
@@ -94,35 +105,77 @@ __device__ __forceinline__ void cst4(rsrc_t r, uint32_t off, f4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kSC1);
 }
 
-// Wave-wide LDS DMA of `nfloats` floats (a multiple of 4) from global memory into LDS with
-// SC1 (coherent) loads; lane l of instruction j lands at dst[j*256 + 4l]. Lanes past the end
-// re-read the last 16 bytes and land in dst[nfloats, round_up(nfloats, 256)), which the
-// destination must have room for. Completion is tracked by vmcnt.
 typedef const void __attribute__((address_space(1)))* gvp;
 typedef void __attribute__((address_space(3)))* lvp;
+
+// One wave instruction of LDS DMA (16 bytes per lane from `src` to LDS at lds_dst + 16 * lane),
+// written so that the compiler does not track it: each caller waits for it explicitly
+// (s_waitcnt vmcnt) before the copied data is read. Tracked, the compiler would make every wave
+// wait at the next barrier for all of its own loads in flight (a barrier publishes LDS writes),
+// which would drain the weight prefetch that the other waves hold across the staging step. The
+// instruction has no destination register; M0 (the LDS base) is saved and restored around it,
+// and one wait state separates its write from the DMA that reads it. COH selects the cache
+// policy: false -- SC0, missing in L1 and served by the XCD's L2 (produced data written once per
+// step); true -- SC0 SC1, agent-coherent (data that other XCDs update with atomics, see kActCpol).
+static_assert(kActCpol == kSC0, "the untracked LDS DMA is written with the SC0 cache policy");
+template <bool COH = false>
+__device__ __forceinline__ void lds_dma16(const void* src, float* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lvp)lds_dst);
+  uint32_t saved;
+  if constexpr (COH)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc0 sc1\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(base)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(base)
+                 : "memory");
+}
+
+// Wave-wide LDS DMA of `nfloats` floats (a multiple of 4) of produced data from global memory
+// into LDS; lane l of instruction j lands at dst[j*256 + 4l]. Lanes past the end re-read the
+// last 16 bytes and land in dst[nfloats, round_up(nfloats, 256)), which the destination must
+// have room for. Completion is counted by vmcnt, which the caller waits for.
+template <bool COH = false>
 __device__ __forceinline__ void dma_to_lds(float* dst, const float* src, int nfloats) {
   const int lane = threadIdx.x & 63;
   for (int j = 0; j * 256 < nfloats; ++j) {
     int i = j * 256 + lane * 4;
     i = i < nfloats ? i : nfloats - 4;
-    __builtin_amdgcn_global_load_lds((gvp)(src + i), (lvp)(dst + j * 256), 16, 0, kActCpol);
+    lds_dma16<COH>(src + i, dst + j * 256);
   }
 }
 
 // The same copy split over all waves of the workgroup (1-KB chunk j by wave j % 8): for copies
 // longer than one wave keeps in flight. Every wave must call it; each waits for its own part
 // (after its own loads issued earlier), and the caller's barrier publishes the whole.
+template <bool COH = false>
 __device__ __forceinline__ void dma_to_lds_all(float* dst, const float* src, int nfloats) {
   const int lane = threadIdx.x & 63;
   for (int j = (int)(threadIdx.x >> 6); j * 256 < nfloats; j += kWaves) {
     int i = j * 256 + lane * 4;
     i = i < nfloats ? i : nfloats - 4;
-    __builtin_amdgcn_global_load_lds((gvp)(src + i), (lvp)(dst + j * 256), 16, 0, kActCpol);
+    lds_dma16<COH>(src + i, dst + j * 256);
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
 }
 
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
+
+// The per-task execution log (one 64-byte record per task and step). Level 1 (the default)
+// records what the coverage and dependency-order checks read: the execution count, the
+// workgroup and XCD, and three clock reads by wave 0 -- task start, the moment its dependency
+// wait succeeded, and its completion stamp just before its counter increment. Each clock read
+// is a scalar memory operation whose result is awaited only where the wave waits anyway.
+// Level 2 adds the per-phase stamps used to analyse a step (staged, streamed, sub-phases, end);
+// those sit on the critical path. Level 0 leaves the log out.
+#ifndef DEC_TASK_LOG
+#define DEC_TASK_LOG 1
+#endif
+constexpr bool kTaskLog = DEC_TASK_LOG >= 1;
+constexpr bool kTaskLogDetail = DEC_TASK_LOG >= 2;
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -191,6 +244,8 @@ struct Blk {
   rsrc_t act;     // coherent view of the activation region (byte offsets = 4 * float offsets)
   uint32_t epoch;
   uint32_t t_ready, t_staged, t_streamed;
+  uint32_t t_sub[3];  // sub-phase stamps of the current task (thread 0; logged as t_aux[2..4])
+  float norm;         // 1 / rms of the staged input (RMSNorm applied to the row results), else 1
   int* flags;     // LDS: [0] wait status, [1] ticket result
   float* xs;      // LDS: staged input vector
   float* ys;      // LDS: per-row results of the current task
@@ -209,20 +264,29 @@ struct Blk {
 // the positions 0..n (the planner cuts static plans the same way).
 __device__ __forceinline__ int split_pos(int n, int sp, int S) { return (int)(((int64_t)n + 1) * sp / S); }
 
+struct NoEarly {
+  __device__ __forceinline__ void operator()() const {}
+};
+
 // Wait until every dependency counter of `t` has reached this step's target. Wave 0 polls
-// (one lane per counter); the other waves wait at the barrier with their loads in flight.
+// (one lane per counter, agent-scope loads); the other waves wait at the barrier with their
+// loads in flight. `early` runs on wave 0 once the wait has succeeded, before that barrier:
+// loads it issues enter the memory queue ahead of whatever the released waves issue next.
 // Returns false when the step is being aborted (watchdog).
-__device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const TaskDesc& t, int d0 = 0, int d1 = -1) {
+template <class EarlyF = NoEarly>
+__device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const TaskDesc& t, int d0 = 0, int d1 = -1,
+                                          EarlyF&& early = EarlyF{}) {
   if (d1 < 0) d1 = t.dep_count;
   const int nd = d1 - d0;  // waits on dependencies [d0, d1) of the task
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int status = 0;
     if (nd > 0) {
+      const DepEntry* dl = A.deps + t.dep_first + d0;
       const uint32_t* cp = A.ctl;  // any valid address for idle lanes
       uint32_t target = 0;
       if (lane < nd) {
-        const DepEntry d = A.deps[t.dep_first + d0 + lane];
+        const DepEntry d = dl[lane];
         cp = A.counters + (size_t)d.counter * kCounterStride;
         target = (b.epoch + 1u) * d.per_step;
       }
@@ -231,8 +295,8 @@ __device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const Tas
       while (true) {
         const bool ok = (lane >= nd) || ((int32_t)(ld_agent(cp) - target) >= 0);
         if (__all(ok)) break;
-        const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
-        if (late || (++spins & 7u) == 0u) {
+        if ((++spins & 7u) == 0u) {  // the clock and the abort word every 8th round
+          const bool late = (now() - t0) > (uint64_t)A.watchdog_ticks;
           const uint32_t ab = ld_agent(A.ctl + CTL_ABORT);
           if (ab || late) {
             if (!ab && lane == 0) {
@@ -255,30 +319,47 @@ __device__ __forceinline__ bool wait_deps(const EngineArgs& A, Blk& b, const Tas
       // only keeps the compiler from hoisting those loads above the poll
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
+    if (kTaskLog) b.t_ready = (uint32_t)now();  // the wait has succeeded (wave 0)
+    if (__builtin_amdgcn_readfirstlane(status) == 0) early();
     if (lane == 0) b.flags[0] = status;
   }
   __syncthreads();
-  b.t_ready = (uint32_t)now();
   return b.flags[0] == 0;
 }
 
+// The producer's completion stamp (wave 0): the clock is read before the wait for the task's
+// stores, and that wait also covers the read (lgkmcnt), so the read has returned -- and the time
+// it holds has passed -- before the counter increment is issued: every consumer that sees the
+// increment passed its wait (and stamped t_ready) after this time.
+constexpr int kVmLgkm0 = 0x0070;  // s_waitcnt vmcnt(0) lgkmcnt(0)
+__device__ __forceinline__ uint32_t store_wait_stamp() {
+  uint32_t ts = 0;
+  if (kTaskLog) ts = (uint32_t)now();
+  __builtin_amdgcn_s_waitcnt(kTaskLog ? kVmLgkm0 : kVmcnt0);
+  return ts;
+}
+
 // Every wave waits for its own SC1 stores to complete, then the barrier, then one counter
-// increment: the produced data is visible at agent scope before the counter moves.
-__device__ __forceinline__ void signal(const EngineArgs& A, int ctr) {
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+// increment: the produced data is visible at agent scope before the counter moves. Returns
+// the completion stamp (meaningful in wave 0).
+__device__ __forceinline__ uint32_t signal(const EngineArgs& A, int ctr) {
+  const uint32_t ts = store_wait_stamp();
   __syncthreads();
   if (threadIdx.x == 0 && ctr >= 0) add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
+  return ts;
 }
 
 // After a GEMV task, whose results wave 0 stored alone: wave 0 waits for its stores and
 // increments the counter, while the other waves go straight on to the next task and issue
 // its prefetch (the next task's barriers keep the LDS hand-over in order: its input is
 // staged by wave 0, and its row results are written only after its staging barrier).
-__device__ __forceinline__ void signal_w0(const EngineArgs& A, int ctr) {
+__device__ __forceinline__ uint32_t signal_w0(const EngineArgs& A, int ctr) {
   if (threadIdx.x < 64) {
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    const uint32_t ts = store_wait_stamp();
     if (threadIdx.x == 0 && ctr >= 0) add_agent(A.counters + (size_t)ctr * kCounterStride, 1u);
+    return ts;
   }
+  return 0u;
 }
 
 __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
@@ -289,79 +370,132 @@ __device__ __forceinline__ int padc(int k) { return (k + 1024 / ES - 1) / (1024 
 template <int ES>
 __device__ __forceinline__ const float* wscale(const EngineArgs& A, int idx) { return ES == 1 ? wp<float>(A, idx + 1) : nullptr; }
 
-__device__ __forceinline__ float block_sum(Blk& b, float v) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) b.scr[wave] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) s += b.scr[i];
-  return s;
-}
+// The longest input one wave copies alone, the moment its wait succeeds (32 1-KB chunks of LDS
+// DMA); a longer one (the down projections' 14336 floats, the per-group merge of 32 split
+// partials) is copied by all waves in turn, which was measured faster on the 8B model (3130
+// against 3182 us per step with 60-chunk single-wave copies).
+#ifndef DEC_EARLY_DMA_FLOATS
+#define DEC_EARLY_DMA_FLOATS 8192
+#endif
+constexpr int kEarlyDmaFloats = DEC_EARLY_DMA_FLOATS;
 
-// Stage K values into xs[0, K) and zero xs[K, padK). The source is the activation buffer at
-// float offset `off`, or the bf16 step input `s16` when off < 0. With a gain, apply
-// RMSNorm: x / sqrt(mean(x^2) + eps) * g (eps inside the sqrt, mean over K).
-// The loads of a short vector are issued by wave 0, the wave that has no weight loads in
-// flight (a wave's loads complete in issue order, so waves 1..7 would wait for their prefetch
-// first). A long one (the down projections' input) is copied by all waves, one 1-KB chunk in
-// turn each: one wave alone would issue more copies than it can keep in flight.
-__device__ __forceinline__ void stage_vec(Blk& b, int off, const uint16_t* s16, int K, int padK,
-                                          const uint16_t* gain, float eps) {
-  if (off >= 0 && K >= 8192) {
-    dma_to_lds_all(b.xs, b.actp + off, K);
-    __syncthreads();
-  }
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+// Staging of a task's input vector into xs[0, K) (zero-padded to padK), in three parts so that
+// every load goes out as early as it may:
+//   before -- wave 0, ahead of the dependency wait: the norm gains (weights, known statically);
+//   early  -- wave 0, the moment the wait succeeds and before the barrier that releases the
+//             other waves: the LDS DMA of the activation vector, which thus enters the compute
+//             unit's memory queue ahead of the ring batch those waves issue next (the unit
+//             returns its loads roughly in issue order);
+//   finish -- every wave: completes the copy, zero-pads, and with a gain g stores g * x.
+// The source is the activation region at float offset `off`, or the bf16 step input s16 when
+// off < 0 (converted to fp32 by wave 0 in `finish`). With a gain the step's RMSNorm,
+// x / sqrt(mean(x^2) + eps) * g (eps inside the square root, mean over K), is applied as
+// 1 / rms to each row result of the GEMV (W (g x) / rms = W RMSNorm(x)); the sum of squares
+// is taken by all waves while they apply the gains. `inplace` instead leaves the normalised
+// vector itself in xs (a consumer that reads the vector, not a GEMV).
+struct StageVec {
+  int off;
+  const uint16_t* s16;
+  int K, padK;
+  const uint16_t* gain;
+  float eps;
+  bool inplace;
+  bool coh;  // the vector is an atomically accumulated buffer: read it agent-coherently (kActCpol)
+  __device__ __forceinline__ bool early_ok() const { return off >= 0 && K <= kEarlyDmaFloats; }
+  __device__ __forceinline__ void before(Blk& b) const {  // wave 0
     if (gain) dma_to_lds(b.gs, (const float*)gain, K / 2);
-    if (off >= 0) {
-      if (K < 8192) dma_to_lds(b.xs, b.actp + off, K);
-    } else {
-      // the bf16 step input (layer 0): batched loads, converted to fp32
-      for (int i0 = lane * 4; i0 < K; i0 += 64 * 4 * 4) {
-        f4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u * 256;
-          const uint2 x = *(const uint2*)(s16 + (i < K ? i : 0));
-          v[u] = f4{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)};
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (i0 + u * 256 < K) *(f4*)(b.xs + i0 + u * 256) = v[u];
-      }
+  }
+  __device__ __forceinline__ void early(Blk& b) const {  // wave 0
+    if (early_ok()) {
+      if (coh) dma_to_lds<true>(b.xs, b.actp + off, K);
+      else dma_to_lds(b.xs, b.actp + off, K);
     }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    for (int i = K + lane; i < padK; i += 64) b.xs[i] = 0.f;
+  }
+  __device__ __forceinline__ void finish(Blk& b) const {
+    if (off >= 0 && !early_ok()) {  // too long for one wave
+      if (coh) dma_to_lds_all<true>(b.xs, b.actp + off, K);
+      else dma_to_lds_all(b.xs, b.actp + off, K);
+    }
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      if (off < 0) {
+        // the bf16 step input (layer 0): batched loads, converted to fp32
+        for (int i0 = lane * 4; i0 < K; i0 += 64 * 4 * 4) {
+          f4 v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * 256;
+            const uint2 x = *(const uint2*)(s16 + (i < K ? i : 0));
+            v[u] = f4{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)};
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (i0 + u * 256 < K) *(f4*)(b.xs + i0 + u * 256) = v[u];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // wave 0's copies (vector, gains) have landed
+      if (kTaskLogDetail && lane == 0) b.t_sub[0] = (uint32_t)now();
+      for (int i = K + lane; i < padK; i += 64) b.xs[i] = 0.f;
+    }
+    __syncthreads();
+    b.norm = 1.f;
     if (gain) {
+      const uint16_t* g16 = reinterpret_cast<const uint16_t*>(b.gs);
       float ss = 0.f;
-      for (int i = lane * 4; i < K; i += 256) {
-        const f4 v = *(const f4*)(b.xs + i);
+      for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
+        const uint2 g = *(const uint2*)(g16 + i);
+        f4 v = *(f4*)(b.xs + i);
         ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        v.x *= bf_lo(g.x);
+        v.y *= bf_hi(g.x);
+        v.z *= bf_lo(g.y);
+        v.w *= bf_hi(g.y);
+        *(f4*)(b.xs + i) = v;
       }
       ss = wave_sum(ss);
-      if (lane == 0) b.flags[2] = __float_as_int(1.0f / sqrtf(ss / (float)K + eps));
+      float* part = reinterpret_cast<float*>(b.flags) + 8;  // per-wave sums of squares
+      if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+      __syncthreads();
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += part[w];
+      b.norm = 1.0f / sqrtf(tot / (float)K + eps);
+      if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[1] = (uint32_t)now();
+      if (inplace) {
+        for (int i = threadIdx.x; i < K; i += kThreads) b.xs[i] *= b.norm;
+        __syncthreads();
+      }
     }
   }
-  __syncthreads();
-  if (gain) {
-    const float inv = __int_as_float(b.flags[2]);
-    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(b.gs);
-    for (int i = threadIdx.x * 4; i < K; i += kThreads * 4) {
-      const uint2 g = *(const uint2*)(g16 + i);
-      f4 v = *(f4*)(b.xs + i);
-      v.x *= inv * bf_lo(g.x);
-      v.y *= inv * bf_hi(g.x);
-      v.z *= inv * bf_lo(g.y);
-      v.w *= inv * bf_hi(g.y);
-      *(f4*)(b.xs + i) = v;
-    }
-    __syncthreads();
-  }
+};
+
+__device__ __forceinline__ StageVec stage_vec(int off, const uint16_t* s16, int K, int padK, const uint16_t* gain, float eps,
+                                              bool inplace = false, bool coh = false) {
+  return StageVec{off, s16, K, padK, gain, eps, inplace, coh};
 }
+
+// All three parts in a row, for a task that is not a GEMV (it calls wait_deps itself).
+__device__ __forceinline__ void stage_now(Blk& b, const StageVec& sv) {
+  if (threadIdx.x < 64) {
+    sv.before(b);
+    sv.early(b);
+  }
+  sv.finish(b);
+}
+
+// A custom staging step (all in `finish`); the GEMV's row results are not rescaled.
+template <class F>
+struct StageFn {
+  F f;
+  __device__ __forceinline__ void before(Blk&) const {}
+  __device__ __forceinline__ void early(Blk&) const {}
+  __device__ __forceinline__ void finish(Blk& b) const {
+    f();
+    b.norm = 1.f;
+  }
+};
+template <class F>
+__device__ __forceinline__ StageFn<F> stage_fn(F f) { return StageFn<F>{f}; }
 
 // ------------------------------------------------------------------ streaming row GEMV
 
@@ -378,6 +512,7 @@ constexpr int NB = DEC_NB;  // 16-byte chunks per batch per lane (NB KB per wave
 constexpr int kRingQKV = DEC_RING_QKV;      // register ring depth of the QKV tasks
 constexpr int kRingOproj = DEC_RING_OPROJ;  // register ring depth of the per-group O-projection
 constexpr int kRingFfn = 3;  // gate/up and (GQA) down: three batches in flight cover more of the stage boundary
+
 
 // One wave load is 16 bytes per lane: 8 bf16 or 16 FP8 (E4M3) weights. ES = bytes per
 // weight; a chunk (one wave load) spans 1024 / ES columns.
@@ -589,10 +724,10 @@ struct NoPre {
 // FLAT: the waves split the rows' chunks evenly (StreamFlat; G must be 1) and the partial
 // row sums meet in ys through LDS float atomics (two waves at most share a row, so the sum
 // does not depend on their order); otherwise each wave streams whole groups of G rows.
-template <int R = 2, bool FLAT = false, int ES = 2, class RM, class StageF, class EpiF, class PreF = NoPre,
+template <int R = 2, bool FLAT = false, int ES = 2, class RM, class StageT, class EpiF, class PreF = NoPre,
           class IssueF = NoPre>  // R in [2, 4]; ES: bytes per weight (2 bf16, 1 FP8 with row scales)
 __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows,
-                                         int K, int G, bool prefetch, StageF&& stage, EpiF&& epi, int pre_deps = 0,
+                                         int K, int G, bool prefetch, const StageT& stage, EpiF&& epi, int pre_deps = 0,
                                          PreF&& pre = PreF{}, IssueF&& issue = IssueF{}) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int ng = nrows / G;
@@ -617,6 +752,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     if (threadIdx.x < 64)
       for (int j = (int)threadIdx.x; j < nrows; j += 64) b.scl[j] = rm.scale(j);
   }
+  if (threadIdx.x < 64) stage.before(b);
   if (pre_deps > 0) {
     if (!wait_deps(A, b, t, 0, pre_deps)) return false;
     pre();
@@ -628,11 +764,13 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
 #pragma unroll
     for (int k = 0; k < R; ++k) s.load(buf[k]);
   }
-  if (!wait_deps(A, b, t, pre_deps)) return false;
+  // wave 0 issues the input's copy the moment the wait succeeds (StageVec::early)
+  if (!wait_deps(A, b, t, pre_deps, -1, [&] { stage.early(b); })) return false;
   if constexpr (FLAT)
     for (int i = threadIdx.x; i < ng; i += kThreads) b.ys[i] = 0.f;  // row sums (the stage's barrier orders this)
-  stage();
-  b.t_staged = (uint32_t)now();
+  stage.finish(b);
+  const float nrm = b.norm;
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_staged = (uint32_t)now();
   issue();
   if (!prefetch) {
     fill_rows(rm, ja, jb, b.rowp, b.xoffp);
@@ -642,6 +780,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   float gacc = 0.f;
   auto emit = [&](int j, float v) {
+    v *= nrm;                              // 1 / rms of a normalised input (else 1)
     if constexpr (ES == 1) v *= b.scl[j];  // G == 1 for FP8 rows
     if constexpr (FLAT) {
       if (lane == 0) atomicAdd(b.ys + j, v);
@@ -675,7 +814,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     }
   }
   __syncthreads();
-  b.t_streamed = (uint32_t)now();
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_streamed = (uint32_t)now();
   if (threadIdx.x < 64) epi();  // wave 0 stores the results (see signal_w0)
   return true;
 }
@@ -793,7 +932,7 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
   };
   return run_gemv<kRingQKV, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, xin, b.x, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      stage_vec(xin, b.x, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps),
       [&] {
         const int n = b.n;
         const size_t lay = (size_t)2 * A.nkv * (A.kv_len + 1) * hd;  // cache elements per layer
@@ -827,16 +966,32 @@ __device__ __forceinline__ bool task_qkv(const EngineArgs& A, Blk& b, const Task
 
 // Merge S split partials (m, l, acc[hd]) of H heads into xs[h*hd + d] =
 // sum_s e^(m_s-M) acc_s[d] / sum_s e^(m_s-M) l_s (base-2 exponents), zero-padding xs up to
-// padK. All waves copy the S*H partials into LDS (one burst of DMA each); the merge then runs
-// from LDS. With o_off >= 0 wave 0 also stores the merged vector there.
-__device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H, int hd, int padK, int o_off) {
+// padK: the staging step of the per-group O-projection (a StageVec-like step: `early` is wave
+// 0's LDS DMA of all S*H partials the moment the wait succeeds, when they fit one wave's
+// outstanding loads; otherwise every wave copies a part in `finish`). The merge then runs from
+// LDS. With o_off >= 0 wave 0 also stores the merged vector there.
+struct StageMerge {
+  int parts_off, S, H, hd, padK, o_off;
+  __device__ __forceinline__ int n() const { return S * H * (hd + 4); }
+  __device__ __forceinline__ void before(Blk&) const {}
+  __device__ __forceinline__ void early(Blk& b) const {  // wave 0
+    if (n() <= kEarlyDmaFloats) dma_to_lds(b.scr, b.actp + parts_off, n());
+  }
+  __device__ __forceinline__ void finish(Blk& b) const;
+};
+
+__device__ __forceinline__ void StageMerge::finish(Blk& b) const {
   const int ps = hd + 4;                    // m, l, 2 pad, acc[hd]
   const int n = S * H * ps;
   float* P = b.scr;                         // [S][H][ps]
   float* w = P + ((n + 255) & ~255);        // [S][H] merge weights
-  dma_to_lds_all(P, b.actp + parts_off, n);
+  b.norm = 1.f;
+  if (n > kEarlyDmaFloats) dma_to_lds_all(P, b.actp + parts_off, n);
+  else if (threadIdx.x < 64) __builtin_amdgcn_s_waitcnt(kVmcnt0);  // wave 0's early copy
   for (int i = H * hd + (int)threadIdx.x; i < padK; i += kThreads) b.xs[i] = 0.f;
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[0] = (uint32_t)now();
   __syncthreads();
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[1] = (uint32_t)now();
   // wave h (h < 8) owns heads h, h + 8, ...: lanes run over the splits
   for (int h = wave_id(); h < H; h += kWaves) {
     const int lane = threadIdx.x & 63;
@@ -855,6 +1010,7 @@ __device__ __forceinline__ void stage_merge(Blk& b, int parts_off, int S, int H,
     for (int sp = lane; sp < S; sp += 64) w[sp * H + h] = exp2f(P[(sp * H + h) * ps] - M) * inv;
   }
   __syncthreads();
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[2] = (uint32_t)now();
   for (int i = threadIdx.x; i < H * hd; i += kThreads) {
     const int h = i / hd, d = i - h * hd;
     float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
@@ -1006,12 +1162,12 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     const uint32_t off = (uint32_t)(n * hd + sub * 8) * 2u;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      ka[i] = __builtin_amdgcn_raw_buffer_load_b128(kn, off, 0, kSC1);
-      va[i] = __builtin_amdgcn_raw_buffer_load_b128(vn, off, 0, kSC1);
+      ka[i] = __builtin_amdgcn_raw_buffer_load_b128(kn, off, 0, kCoh);
+      va[i] = __builtin_amdgcn_raw_buffer_load_b128(vn, off, 0, kCoh);
     }
     step(n, n, n + 1, ka, va);
   }
-  const uint32_t t_mid = (uint32_t)now();
+  const uint32_t t_mid = kTaskLogDetail ? (uint32_t)now() : 0u;
   // merge the wave's lane groups (the same dims of different positions) with cross-lane
   // exchanges: partials (m, l, acc) of lanes L and L ^ X combine as
   // M = max, l = l e^(m - M) + l' e^(m' - M), acc likewise (base 2); afterwards every lane
@@ -1049,7 +1205,7 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
     }
   }
   __syncthreads();
-  const uint32_t t_lanes = (uint32_t)now();
+  const uint32_t t_lanes = kTaskLogDetail ? (uint32_t)now() : 0u;
   // workgroup partial (M, den, sum of weighted acc) -> LDS (xs), then wave 0 stores it; each
   // thread recomputes its head's merge weights over the NS wave slots
 #pragma unroll 1
@@ -1076,14 +1232,14 @@ __device__ __forceinline__ bool task_attn(const EngineArgs& A, Blk& b, const Tas
   }
   const uint32_t gpart = (uint32_t)(t.a4 + t.a1 * r * ps);
   __syncthreads();
-  const uint32_t t_merged = (uint32_t)now();
+  const uint32_t t_merged = kTaskLogDetail ? (uint32_t)now() : 0u;
   if (threadIdx.x < 64)
     for (int i = threadIdx.x * 4; i < r * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
-  if (threadIdx.x == 0) {
-    A.log[t.id].reserved[0] = t_lanes;
-    A.log[t.id].reserved[1] = t_merged;
+  if (kTaskLogDetail && threadIdx.x == 0) {
+    A.log[t.id].t_aux[0] = t_lanes;
+    A.log[t.id].t_aux[1] = t_merged;
+    A.log[t.id].t_mid = t_mid;
   }
-  if (threadIdx.x == 0) A.log[t.id].t_mid = t_mid;
   return true;
 }
 
@@ -1104,7 +1260,7 @@ __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const Ta
   const int xin = L.act[LA_X_IN];
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_ATTN], nullptr, K, pad512(K), nullptr, 0.f); },
+      stage_vec(L.act[LA_ATTN], nullptr, K, pad512(K), nullptr, 0.f, false, A.arch != 0),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
@@ -1134,7 +1290,7 @@ __device__ __forceinline__ bool task_oproj_g(const EngineArgs& A, Blk& b, const 
   const RmCols rm{wp<uint8_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K, ES, wscale<ES>(A, L.w[LW_WO])};
   return run_gemv<kRingOproj, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_merge(b, t.a4, t.a2, r, hd, padc<ES>(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1); },
+      StageMerge{t.a4, t.a2, r, hd, padc<ES>(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1},
       [&] {
         float* h = b.actp + L.act[LA_H] + t.u0;
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
@@ -1157,7 +1313,7 @@ __device__ __forceinline__ bool task_gateup(const EngineArgs& A, Blk& b, const T
                     wscale<ES>(A, L.w[LW_UP])};
   return run_gemv<kRingFfn, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      stage_vec(L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps, false, A.arch == 0),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
@@ -1171,12 +1327,13 @@ __device__ __forceinline__ bool task_down(const EngineArgs& A, Blk& b, const Tas
   const RmPlain rm{wp<uint8_t>(A, L.w[LW_DOWN]), K, t.u0, ES, wscale<ES>(A, L.w[LW_DOWN])};
   return run_gemv<FLAT ? kRingFfn : 2, FLAT, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_ACT], nullptr, K, padc<ES>(K), nullptr, 0.f); },
+      stage_vec(L.act[LA_ACT], nullptr, K, padc<ES>(K), nullptr, 0.f),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
           const float y = b.ys[i];
-          const float xo = cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) + y;
+          const float hr = A.arch == 0 ? cld_coh(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u) : cld(b.act, (uint32_t)(L.act[LA_H] + rr) * 4u);
+          const float xo = hr + y;
           cst(b.act, (uint32_t)(L.act[LA_FFN_OUT] + rr) * 4u, y);
           if (t.a1 >= 0) cst(b.act, (uint32_t)(t.a1 + rr) * 4u, xo);  // next layer's h starts at x
           cst(b.act, (uint32_t)(L.act[LA_X_OUT] + rr) * 4u, xo);
@@ -1236,7 +1393,7 @@ __device__ __forceinline__ bool task_lmhead(const EngineArgs& A, Blk& b, const T
   const RmPlain rm{wp<uint8_t>(A, A.w_lm_head), K, t.u0, ES, wscale<ES>(A, A.w_lm_head)};
   return run_gemv<2, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, A.x_final, nullptr, K, padc<ES>(K), wp<uint16_t>(A, A.w_final_norm), A.eps); },
+      stage_vec(A.x_final, nullptr, K, padc<ES>(K), wp<uint16_t>(A, A.w_final_norm), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) A.out[t.u0 + i] = b.ys[i];
         if constexpr (GREEDY) {  // this task's largest logit (lowest index among equals) -> slot a0
@@ -1430,7 +1587,7 @@ __device__ __forceinline__ void attn_finish(const EngineArgs& A, Blk& b, const T
     if (d == 0) *reinterpret_cast<f4*>(b.xs + h * ps) = f4{M, den, 0.f, 0.f};
   }
   __syncthreads();
-  if (threadIdx.x == 0) A.log[t.id].t_mid = (uint32_t)now();
+  if (kTaskLogDetail && threadIdx.x == 0) A.log[t.id].t_mid = (uint32_t)now();
   if (threadIdx.x < 64) {  // wave 0 stores the partial (see signal_w0)
     const uint32_t gpart = (uint32_t)(t.a4 + t.a1 * r * ps);
     for (int i = threadIdx.x * 4; i < r * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
@@ -1468,10 +1625,11 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
     const size_t n1 = (size_t)A.kv_len + 1, off = (size_t)(p0 + c) * HD + lane * 8;
     const uint16_t* kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * n1 * HD;
     const uint16_t* vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * n1 * HD;
-    __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kSC1);
-    __builtin_amdgcn_global_load_lds((gvp)(vb + off), (lvp)(Vs + (size_t)c * HD), 16, 0, kSC1);
+    __builtin_amdgcn_global_load_lds((gvp)(kb + off), (lvp)(Ks + (size_t)c * HD), 16, 0, kCoh);
+    __builtin_amdgcn_global_load_lds((gvp)(vb + off), (lvp)(Vs + (size_t)c * HD), 16, 0, kCoh);
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[0] = (uint32_t)now();
   u4 qh[NKS], ql[NKS];
   const float sc = (hl < r) ? A.attn_scale_log2 : 0.f;
 #pragma unroll
@@ -1483,6 +1641,7 @@ __device__ __forceinline__ bool task_attn_mfma(const EngineArgs& A, Blk& b, cons
   for (int ct = 0; ct < NCT; ++ct) o[ct] = f4{0.f, 0.f, 0.f, 0.f};
   const int ntile = (np + 15) >> 4;
   for (int tile = wave; tile < ntile; tile += kWaves) attn_tile<HD>(Ks, Vs, tile, np, r, hl, q4, qh, ql, m, l, o);
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[1] = (uint32_t)now();
   attn_finish<HD>(A, b, t, r, hl, q4, m, l, o);
   return true;
 }
@@ -1517,7 +1676,7 @@ __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const Ta
   const RmMlaA rm{wp<uint16_t>(A, L.w[LW_WQA]), wp<uint16_t>(A, L.w[LW_WKVA]), K, ql, t.u0};
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_X_IN], b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps); },
+      stage_vec(L.act[LA_X_IN], b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int r = t.u0 + i;
@@ -1547,7 +1706,7 @@ __device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const Ta
   const RmMlaB rm{wp<uint16_t>(A, L.w[LW_WQB]), K, dn, dr, uh, t.u0};
   return run_gemv(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps); },
+      stage_vec(L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, h = u / uh, k = u - h * uh;
@@ -1574,7 +1733,7 @@ __device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, cons
   const LayerDesc& L = A.layers[t.layer];
   const int kl = A.kl, dr = A.dr, KR = kl + dr, n = b.n;
   if (!wait_deps(A, b, t)) return false;
-  stage_vec(b, L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps);
+  stage_now(b, stage_vec(L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps, true));
   const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (A.kv_len + 1) + n) * KR, (uint32_t)KR * 2u);
   for (int i = threadIdx.x; i < kl; i += kThreads) {
     const float v = b.xs[i];
@@ -1684,7 +1843,7 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
       pos = pos < p1 ? pos : p1 - 1;
       const int col = (sc * 8 < KR) ? sc * 8 : 0;
       if (coh)
-        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kSC1);
+        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kCoh);
       else
         __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kActCpol);
     }
@@ -1727,8 +1886,17 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
     if (wave < kMlaChunk / 16) {
       f4 d = f4{0.f, 0.f, 0.f, 0.f};
       const uint16_t* arow = LAT + (size_t)(16 * wave + hl) * KP + 8 * g;
-#pragma unroll 2
-      for (int ks = 0; ks < NKS; ++ks) {
+      // two k-steps per round (the MFMAs are convergent: no compiler remainder loop), then the odd one
+      int ks = 0;
+      for (; ks + 2 <= NKS; ks += 2) {
+        const u4 a0 = *reinterpret_cast<const u4*>(arow + ks * 32);
+        const u4 a1 = *reinterpret_cast<const u4*>(arow + ks * 32 + 32);
+        d = mfma_bf16(a0, QL[(ks * 2) * 64 + lane], d);
+        d = mfma_bf16(a0, QL[(ks * 2 + 1) * 64 + lane], d);
+        d = mfma_bf16(a1, QL[(ks * 2 + 2) * 64 + lane], d);
+        d = mfma_bf16(a1, QL[(ks * 2 + 3) * 64 + lane], d);
+      }
+      if (ks < NKS) {
         const u4 a = *reinterpret_cast<const u4*>(arow + ks * 32);
         d = mfma_bf16(a, QL[(ks * 2) * 64 + lane], d);
         d = mfma_bf16(a, QL[(ks * 2 + 1) * 64 + lane], d);
@@ -1925,7 +2093,7 @@ __device__ __forceinline__ bool task_router(const EngineArgs& A, Blk& b, const T
   const RmPlain rm{wp<uint16_t>(A, L.w[LW_ROUTER]), K, t.u0};
   return run_gemv(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      stage_vec(L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) cst(b.act, (uint32_t)(L.act[LA_RLOGIT] + t.u0 + i) * 4u, b.ys[i]);
       });
@@ -1938,7 +2106,7 @@ __device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, cons
   const RmGateUp rm{wp<uint16_t>(A, L.w[LW_SGATE]), wp<uint16_t>(A, L.w[LW_SUP]), K, t.u0};
   return run_gemv(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      stage_vec(L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_SACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
@@ -2053,7 +2221,7 @@ __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, cons
   const RmExpertGU rm{wp<uint16_t>(A, L.w[LW_EGATE]), wp<uint16_t>(A, L.w[LW_EUP]), ids, K, F, t.u0};
   return run_gemv(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      [&] { stage_vec(b, L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps); },
+      stage_vec(L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
@@ -2085,7 +2253,7 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
   const RmMoeDown rm{wp<uint16_t>(A, L.w[LW_SDOWN]), wp<uint16_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0};
   return run_gemv(
       A, b, t, rm, G * (t.u1 - t.u0), F, G, true,
-      [&] {
+      stage_fn([&] {
         {
           // the G input segments (8 KB each at eff = 2048) are copied by the waves in turn: one
           // wave alone would issue more copies than it can keep in flight
@@ -2107,7 +2275,7 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
           }
         }
         __syncthreads();
-      },
+      }),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
@@ -2159,6 +2327,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   b.act = make_rsrc(A.act, A.act_bytes);
   b.epoch = ld_agent(A.ctl + CTL_EPOCH);
   b.t_ready = b.t_staged = b.t_streamed = 0;
+  b.t_sub[0] = b.t_sub[1] = b.t_sub[2] = 0;
   b.n = A.kv_len;
   b.x = A.x;
   b.rope = A.rope_cs;
@@ -2201,7 +2370,7 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   for (int ti = ti0; ti < ti1; ++ti) {
     const EngineArgs& A = args_view();
     const TaskDesc t = A.tasks[ti];
-    const uint32_t t0 = (uint32_t)now();
+    const uint32_t t0 = (kTaskLog && threadIdx.x < 64) ? (uint32_t)now() : 0u;
     bool ok = true, gemv = true;
     int sig = t.signal;
     if constexpr (!MLA) {
@@ -2260,9 +2429,8 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       }
     }
     if (!ok) break;
-    if (gemv) signal_w0(A, sig);
-    else signal(A, sig);
-    if (threadIdx.x == 0) {
+    const uint32_t t_sig = gemv ? signal_w0(A, sig) : signal(A, sig);
+    if (kTaskLog && threadIdx.x == 0) {
       TaskLog* lg = A.log + t.id;
       add_agent(&lg->execs, 1u);
       lg->epoch = b.epoch;
@@ -2270,9 +2438,14 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       lg->xcd = xcc;
       lg->t_start = t0;
       lg->t_ready = b.t_ready;
-      lg->t_end = (uint32_t)now();
+      lg->t_end = kTaskLogDetail ? (uint32_t)now() : 0u;
       lg->t_staged = b.t_staged;
       lg->t_streamed = b.t_streamed;
+      lg->t_signal = t_sig;
+      lg->t_aux[2] = b.t_sub[0];
+      lg->t_aux[3] = b.t_sub[1];
+      lg->t_aux[4] = b.t_sub[2];
+      b.t_sub[0] = b.t_sub[1] = b.t_sub[2] = 0;
     }
   }
   // the last workgroup to finish the step's last launch advances the epoch for the next step

@@ -114,7 +114,7 @@ struct LayerDesc {
 };
 
 // Per-task execution log written by the engine (one slot per task id, 64 bytes). Times are
-// s_memrealtime (100 MHz) low words.
+// s_memrealtime (100 MHz, one clock for the whole device) low words.
 struct TaskLog {
   uint32_t execs;      // incremented once per execution (atomic)
   uint32_t epoch;      // epoch of the last execution
@@ -126,7 +126,9 @@ struct TaskLog {
   uint32_t t_mid;      // attention: end of the position loop
   uint32_t t_staged;   // input vector staged in LDS
   uint32_t t_streamed; // all rows streamed
-  uint32_t reserved[6];
+  uint32_t t_signal;   // just before the counter increment (read back before the increment is
+                       // issued): a consumer that saw the increment passed its wait later
+  uint32_t t_aux[5];   // type-specific stamps (vector-ALU attention: lane merge, wave merge)
 };
 
 // Control words at the start of the workspace (each on its own 128-byte line).

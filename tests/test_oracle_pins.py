@@ -602,16 +602,32 @@ def test_planted_mistakes(check, repl):
         check(broken)
 
 
-def test_planted_gqa_mapping_and_scale():
-    """A wrong GQA head->group map or a missing 1/sqrt(d) breaks the whole-model pin."""
+def _whole_gqa_mismatch(patch):
+    """Run the oracle on the tiny model with one of its functions replaced and report whether
+    the independent torch composition (SDPA's GQA, F.rms_norm) then disagrees with it."""
     cfg = workloads.get_config("tiny")
     w, x, kv = workloads.generate(cfg, seed=3, device="cpu")
     Wd = {k: _bits_of(v) for k, v in w.items()}
     outs, logits = _torch_gqa_forward(cfg, w, x, kv)
-    orig_attend = OD.attend
+    name, fn = patch
+    orig = getattr(OD, name)
     try:
-        OD.attend = lambda q, K, V, scale: orig_attend(q, K, V, 1.0)
+        setattr(OD, name, fn(orig))
         res = O.forward(cfg, O.dict_weights(Wd), _bits_of(x), _bits_of(kv))
-        assert not np.allclose(res["out"], logits.numpy(), rtol=1e-6)
     finally:
-        OD.attend = orig_attend
+        setattr(OD, name, orig)
+    return not np.allclose(res["out"], logits.numpy(), rtol=1e-6)
+
+
+def test_planted_gqa_head_to_group_map():
+    """An interleaved head->group map (h % n_kv instead of contiguous groups, reading R8)
+    breaks the whole-model pin: the tiny model has 4 query heads on 2 KV heads."""
+    cfg = workloads.get_config("tiny")
+    assert cfg["n_q_heads"] > cfg["n_kv_heads"] > 1
+    assert _whole_gqa_mismatch(("kv_group", lambda orig: (lambda h, nq, nkv: h % nkv)))
+    assert not _whole_gqa_mismatch(("kv_group", lambda orig: orig))  # the unplanted oracle agrees
+
+
+def test_planted_missing_softmax_scale():
+    """A missing 1/sqrt(head_dim) breaks the whole-model pin."""
+    assert _whole_gqa_mismatch(("attend", lambda orig: (lambda q, K, V, scale: orig(q, K, V, 1.0))))
