@@ -22,8 +22,9 @@
  *
  * Ownership: the caller allocates and frees every device buffer (weights, workspace, x,
  * kv, out). The plan keeps the raw pointers given to bind until destroy or the next bind.
- * The library never frees or allocates device memory. The only allocation the library
- * makes is the opaque host-side plan object.
+ * The library never allocates or frees device memory at run time. The only allocation the
+ * library makes is the opaque host-side plan object; its code object also holds one static
+ * 64 MiB workspace per device, for dec_plan_bind_scratch.
  *
  * Errors: every call validates synchronously and returns a negative dec_status on error
  * without aborting; dec_last_error() then holds a message (thread-local). dec_step is
@@ -189,6 +190,21 @@ dec_status dec_plan_grid(const struct dec_plan* plan, int32_t* n_wg, int32_t* th
  * task table and zeroes counters/status on `stream` (asynchronously). Errors: INVAL, HIP. */
 dec_status dec_plan_bind(struct dec_plan* plan, const void* const* weights, int64_t n,
                          void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Allocation-free binding, for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as dec_plan_bind, but the
+ * workspace is the library's own static device array on the current device (64 MiB per GPU,
+ * held from the first such call on a device until the process ends). Nothing is allocated on
+ * the host or the device; the plan's tables are copied in and the control words, counters,
+ * task log and activations are cleared, and the call synchronises `stream`.
+ * The array is shared by every plan bound to it on that device: binding another plan there
+ * takes it over, after which the earlier plan's calls fail with DEC_E_UNBOUND until it is
+ * bound again. Steps of plans bound to it must not overlap on one GPU (they would race on the
+ * same memory), and they must run with that device current (else DEC_E_DEVICE). The
+ * workspace-size contract is the same as for dec_plan_bind (dec_sizes.workspace_bytes).
+ * Errors: INVAL (null, weight count or alignment), CAPACITY (the plan needs more than the
+ * static array holds), DEVICE, HIP. */
+dec_status dec_plan_bind_scratch(struct dec_plan* plan, const void* const* weights, int64_t n, void* stream);
 
 /* Run one decode step: ONE kernel launch on `stream`.
  *   x   : bf16 [hidden], the new token's input hidden state (read only).

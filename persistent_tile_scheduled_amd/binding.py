@@ -98,6 +98,7 @@ def lib() -> C.CDLL:
         "dec_plan_buffer_desc": (C.c_int, [P, C.c_int64, C.POINTER(BufferDesc)]),
         "dec_plan_grid": (C.c_int, [P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int32)]),
         "dec_plan_bind": (C.c_int, [P, C.POINTER(P), C.c_int64, P, C.c_int64, P]),
+        "dec_plan_bind_scratch": (C.c_int, [P, C.POINTER(P), C.c_int64, P]),
         "dec_step": (C.c_int, [P, P, P, P, P]),
         "dec_plan_n_stages": (C.c_int64, [P]),
         "dec_plan_create_dynamic": (C.c_int, [C.POINTER(ModelShape), C.c_int64, C.POINTER(DeviceInfo), C.POINTER(P)]),
@@ -119,7 +120,8 @@ def lib() -> C.CDLL:
 ABI_SYMBOLS = ["dec_last_error", "dec_device_query", "dec_plan_create", "dec_plan_create_for", "dec_plan_destroy",
                "dec_plan_n_weights", "dec_plan_weight_desc", "dec_plan_sizes", "dec_plan_n_tasks", "dec_plan_tasks",
                "dec_plan_n_deps", "dec_plan_deps", "dec_plan_n_counters", "dec_plan_n_buffers",
-               "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_step", "dec_plan_n_stages",
+               "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_plan_bind_scratch", "dec_step",
+               "dec_plan_n_stages",
                "dec_step_stages", "dec_plan_create_dynamic", "dec_step_dynamic", "dec_plan_status",
                "dec_plan_reset", "dec_plan_set_watchdog"]
 
@@ -245,6 +247,11 @@ class Plan:
         arr = (C.c_void_p * len(weight_ptrs))(*[C.c_void_p(int(p)) for p in weight_ptrs])
         _check(lib().dec_plan_bind(self.h, arr, len(weight_ptrs), C.c_void_p(int(workspace_ptr)),
                                    int(workspace_bytes), C.c_void_p(int(stream))))
+
+    def bind_scratch(self, weight_ptrs: Sequence[int], stream: int = 0):
+        """Bind to the library's static per-device workspace (allocates nothing)."""
+        arr = (C.c_void_p * len(weight_ptrs))(*[C.c_void_p(int(p)) for p in weight_ptrs])
+        _check(lib().dec_plan_bind_scratch(self.h, arr, len(weight_ptrs), C.c_void_p(int(stream))))
 
     def step(self, x_ptr: int, kv_ptr: int, out_ptr: int, stream: int = 0):
         _check(lib().dec_step(self.h, C.c_void_p(int(x_ptr)), C.c_void_p(int(kv_ptr)), C.c_void_p(int(out_ptr)),

@@ -5,6 +5,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -14,19 +15,34 @@
 extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, int run, bool cooperative,
                                         hipStream_t stream);
 extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t dec_scratch_current(void** ptr, size_t* bytes);
 
 struct dec_plan {
   dec::PlanData P;
   bool bound = false;
   char* ws = nullptr;
-  std::vector<uint64_t> wptr;
+  std::vector<uint64_t> wptr;   // sized at planning, filled by bind (bind allocates nothing)
   dec::EngineArgs args{};
   int64_t watchdog_us = 2000000;
+  int scratch_dev = -1;         // bound to this device's static workspace (dec_plan_bind_scratch)
 };
 
 namespace {
 
 thread_local std::string g_err;
+
+// The plan bound to each device's static workspace (dec_plan_bind_scratch); a plan that was
+// bound there before another one no longer owns the memory and may not run.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_owner_mu;
+dec_plan* g_scratch_owner[kMaxScratchDevices] = {};
+
+void release_scratch(dec_plan* p) {
+  if (p->scratch_dev < 0) return;
+  std::lock_guard<std::mutex> lock(g_owner_mu);
+  if (g_scratch_owner[p->scratch_dev] == p) g_scratch_owner[p->scratch_dev] = nullptr;
+  p->scratch_dev = -1;
+}
 
 dec_status fail(dec_status s, const std::string& m) {
   g_err = m;
@@ -103,11 +119,29 @@ void copy_name(char* dst, const std::string& s) {
 
 namespace {
 
+// A plan bound to a device's static workspace runs only while it still owns it, on that device.
+dec_status check_scratch_owner(dec_plan* plan) {
+  if (plan->scratch_dev < 0) return DEC_OK;
+  {
+    std::lock_guard<std::mutex> lock(g_owner_mu);
+    if (g_scratch_owner[plan->scratch_dev] != plan)
+      return fail(DEC_E_UNBOUND, "another plan has been bound to this device's static workspace since");
+  }
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->scratch_dev)
+    return fail(DEC_E_DEVICE, "the plan is bound to the static workspace of device " + std::to_string(plan->scratch_dev) +
+                                  ", the current device is " + std::to_string(dev));
+  return DEC_OK;
+}
+
 // One launch of the tasks of stages [lo, hi): cooperative (co-resident grid) when it spans
 // several stages, whose tasks wait on each other; a plain launch for one stage.
 dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t lo, int32_t hi, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
   if (!plan->bound) return fail(DEC_E_UNBOUND, "step before dec_plan_bind");
+  if (dec_status st = check_scratch_owner(plan)) return st;
   if (!x || !kv || !out) return fail(DEC_E_INVAL, "null x/kv/out");
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
@@ -170,6 +204,7 @@ dec_status dec_plan_create_for(const dec_model_shape* shape, int64_t kv_len, con
     delete p;
     return fail(st, err);
   }
+  p->wptr.assign(p->P.weights.size(), 0);
   *out = p;
   return DEC_OK;
 }
@@ -194,6 +229,7 @@ dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, dec_pla
 }
 
 dec_status dec_plan_destroy(dec_plan* plan) {
+  if (plan) release_scratch(plan);
   delete plan;
   return DEC_OK;
 }
@@ -302,45 +338,86 @@ dec_status dec_plan_grid(const dec_plan* plan, int32_t* n_wg, int32_t* threads, 
   return DEC_OK;
 }
 
-dec_status dec_plan_bind(dec_plan* plan, const void* const* weights, int64_t n, void* workspace,
-                         int64_t workspace_bytes, void* stream) {
-  if (!plan || !weights || !workspace) return fail(DEC_E_INVAL, "null argument");
+}  // extern "C"
+
+namespace {
+
+// Binding without any host or device allocation: the weight pointers go into the plan's
+// pre-sized table, the plan's tables are copied region by region from the plan's own arrays,
+// and the control words, counters, task log and activations are cleared.
+dec_status bind_impl(dec_plan* plan, const void* const* weights, int64_t n, char* ws, int64_t workspace_bytes, void* stream) {
   dec::PlanData& P = plan->P;
   if (n != (int64_t)P.weights.size())
     return fail(DEC_E_INVAL, "expected " + std::to_string(P.weights.size()) + " weights, got " + std::to_string(n));
   if (workspace_bytes < P.ws_bytes) return fail(DEC_E_CAPACITY, "workspace smaller than dec_sizes.workspace_bytes");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(DEC_E_INVAL, "workspace not 256-byte aligned");
-  plan->wptr.resize(n);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(DEC_E_INVAL, "workspace not 256-byte aligned");
+  if (plan->wptr.size() != P.weights.size()) return fail(DEC_E_PLAN, "weight table not sized at planning");
   for (int64_t i = 0; i < n; ++i) {
     if (!weights[i]) return fail(DEC_E_INVAL, "weight " + P.weights[i].name + " is null");
     if (reinterpret_cast<uintptr_t>(weights[i]) % 16) return fail(DEC_E_INVAL, "weight " + P.weights[i].name + " not 16-byte aligned");
     plan->wptr[i] = reinterpret_cast<uint64_t>(weights[i]);
   }
-  // host image of the table region [0, off_act): control words, counters, tasks, lists,
-  // deps, weight pointers, layer descriptors, RoPE table, task log
-  std::vector<char> img((size_t)P.off_act, 0);
-  std::memcpy(img.data() + P.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(dec::TaskDesc));
-  std::memcpy(img.data() + P.off_wgb, P.wg_begin.data(), P.wg_begin.size() * 4);
-  std::memcpy(img.data() + P.off_stf, P.stage_first.data(), P.stage_first.size() * 4);
-  if (!P.deps.empty()) std::memcpy(img.data() + P.off_deps, P.deps.data(), P.deps.size() * sizeof(dec::DepEntry));
-  std::memcpy(img.data() + P.off_wptr, plan->wptr.data(), plan->wptr.size() * 8);
-  std::memcpy(img.data() + P.off_layers, P.layers.data(), P.layers.size() * sizeof(dec::LayerDesc));
-  std::memcpy(img.data() + P.off_rope, P.rope_cs.data(), P.rope_cs.size() * 4);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);
+  auto put = [&](int64_t off, const void* src, size_t bytes) {
+    return bytes ? hipMemcpyAsync(ws + off, src, bytes, hipMemcpyHostToDevice, s) : hipSuccess;
+  };
+  auto clear = [&](int64_t off, int64_t end) { return end > off ? hipMemsetAsync(ws + off, 0, (size_t)(end - off), s) : hipSuccess; };
+  hipError_t e = clear(P.off_ctl, P.off_tasks);  // control words and counters
+  if (e == hipSuccess) e = put(P.off_tasks, P.tasks.data(), P.tasks.size() * sizeof(dec::TaskDesc));
+  if (e == hipSuccess) e = put(P.off_wgb, P.wg_begin.data(), P.wg_begin.size() * 4);
+  if (e == hipSuccess) e = put(P.off_stf, P.stage_first.data(), P.stage_first.size() * 4);
+  if (e == hipSuccess) e = put(P.off_deps, P.deps.data(), P.deps.size() * sizeof(dec::DepEntry));
+  if (e == hipSuccess) e = put(P.off_wptr, plan->wptr.data(), plan->wptr.size() * 8);
+  if (e == hipSuccess) e = put(P.off_layers, P.layers.data(), P.layers.size() * sizeof(dec::LayerDesc));
+  if (e == hipSuccess) e = put(P.off_rope, P.rope_cs.data(), P.rope_cs.size() * 4);
+  if (e == hipSuccess) e = clear(P.off_log, P.ws_bytes);  // task log and activations
   if (e != hipSuccess) return hip_fail(e, "upload plan tables");
-  if (P.ws_bytes > P.off_act) {
-    e = hipMemsetAsync(static_cast<char*>(workspace) + P.off_act, 0, (size_t)(P.ws_bytes - P.off_act), s);
-    if (e != hipSuccess) return hip_fail(e, "clear activations");
-  }
-  e = hipStreamSynchronize(s);  // the host image is freed on return
+  e = hipStreamSynchronize(s);  // the plan's host arrays may change after a later call
   if (e != hipSuccess) return hip_fail(e, "bind synchronise");
-  plan->ws = static_cast<char*>(workspace);
+  plan->ws = ws;
   fill_args(plan);
   plan->bound = true;
   return DEC_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+dec_status dec_plan_bind(dec_plan* plan, const void* const* weights, int64_t n, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  if (!plan || !weights || !workspace) return fail(DEC_E_INVAL, "null argument");
+  release_scratch(plan);
+  plan->bound = false;
+  return bind_impl(plan, weights, n, static_cast<char*>(workspace), workspace_bytes, stream);
+}
+
+dec_status dec_plan_bind_scratch(dec_plan* plan, const void* const* weights, int64_t n, void* stream) {
+  if (!plan || !weights) return fail(DEC_E_INVAL, "null argument");
+  void* ws = nullptr;
+  size_t bytes = 0;
+  hipError_t e = dec_scratch_current(&ws, &bytes);
+  if (e != hipSuccess) return hip_fail(e, "static workspace lookup");
+  if (plan->P.ws_bytes > (int64_t)bytes)
+    return fail(DEC_E_CAPACITY, "the plan needs " + std::to_string(plan->P.ws_bytes) + " bytes of workspace; the static workspace holds " +
+                                    std::to_string(bytes));
+  int dev = -1;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(DEC_E_DEVICE, "device index out of range");
+  release_scratch(plan);
+  plan->bound = false;
+  {
+    std::lock_guard<std::mutex> lock(g_owner_mu);
+    g_scratch_owner[dev] = nullptr;  // the memory is being overwritten: no plan owns it meanwhile
+  }
+  dec_status st = bind_impl(plan, weights, n, static_cast<char*>(ws), (int64_t)bytes, stream);
+  if (st != DEC_OK) return st;
+  std::lock_guard<std::mutex> lock(g_owner_mu);
+  g_scratch_owner[dev] = plan;
+  plan->scratch_dev = dev;
+  return DEC_OK;
+}
 
 dec_status dec_step(dec_plan* plan, const void* x, void* kv, void* out, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
@@ -367,6 +444,7 @@ dec_status dec_plan_create_dynamic(const dec_model_shape* shape, int64_t max_len
     delete p;
     return fail(st, err);
   }
+  p->wptr.assign(p->P.weights.size(), 0);
   *out = p;
   return DEC_OK;
 }
@@ -375,6 +453,7 @@ dec_status dec_step_dynamic(dec_plan* plan, const void* x, void* kv, void* out, 
   if (!plan) return fail(DEC_E_INVAL, "null plan");
   if (!plan->bound) return fail(DEC_E_UNBOUND, "step before dec_plan_bind");
   if (!plan->P.dynamic) return fail(DEC_E_INVAL, "dec_step_dynamic needs a plan from dec_plan_create_dynamic");
+  if (dec_status st = check_scratch_owner(plan)) return st;
   if (!kv || !out || !state) return fail(DEC_E_INVAL, "null kv/out/state");
   if (!x && plan->P.w_embed < 0) return fail(DEC_E_INVAL, "no input vector and no token embedding (vocab == 0)");
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4 ||
@@ -404,6 +483,7 @@ dec_status dec_step_stages(dec_plan* plan, const void* x, void* kv, void* out, i
 dec_status dec_plan_status(dec_plan* plan, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
   if (!plan->bound) return fail(DEC_E_UNBOUND, "plan not bound");
+  if (dec_status st = check_scratch_owner(plan)) return st;
   hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "status synchronise");
   uint32_t st[4] = {0, 0, 0, 0};
@@ -422,6 +502,7 @@ dec_status dec_plan_status(dec_plan* plan, void* stream) {
 dec_status dec_plan_reset(dec_plan* plan, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
   if (!plan->bound) return fail(DEC_E_UNBOUND, "plan not bound");
+  if (dec_status st = check_scratch_owner(plan)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dec::PlanData& P = plan->P;
   hipError_t e = hipMemsetAsync(plan->ws + P.off_ctl, 0, (size_t)(P.off_tasks - P.off_ctl), s);  // ctl + counters

@@ -22,6 +22,7 @@
 // dot products run on the vector ALUs in fp32, not on MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <mutex>
 #include <type_traits>
 
 #include "plan_types.h"
@@ -2519,4 +2520,39 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy
   hipError_t e = hipFuncSetAttribute(engine_fn(arch, 0, wfmt), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0, wfmt), dec::kThreads, (size_t)lds_bytes);
+}
+
+// ------------------------------------------------------------------ the static workspace
+//
+// For callers that cannot allocate device memory (code under stream capture, serving loops,
+// harnesses that forbid allocation): one workspace per GPU in a file-scope device array, which
+// dec_plan_bind_scratch binds a plan to instead of a caller-allocated workspace. Each GPU the
+// library runs on holds its copy until the process ends. Host code never passes the array's
+// name to the device: it uses the address hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept.
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // 64 MiB: the 8B model's plan needs 30 MB, the MLA model's 39 MB
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The current device's copy of the static workspace: its device address and size.
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_scratch_current(void** ptr, size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = kScratchBytes;
+  return hipSuccess;
 }

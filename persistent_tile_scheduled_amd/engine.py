@@ -15,9 +15,12 @@ _TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32", "fp8": "u
 
 class DecodeEngine:
     def __init__(self, cfg: dict, weights: Dict[str, "object"], kv_len: Optional[int] = None,
-                 stream=None, watchdog_us: Optional[int] = None, max_len: Optional[int] = None):
+                 stream=None, watchdog_us: Optional[int] = None, max_len: Optional[int] = None,
+                 static_workspace: bool = False):
         """A plan for kv_len (default: the config's), or, with max_len, a plan whose position
-        is read per step from a device state (step_dynamic)."""
+        is read per step from a device state (step_dynamic). static_workspace: bind to the
+        library's static per-device workspace (dec_plan_bind_scratch) instead of allocating
+        one; the named intermediate buffers are then not readable through buffer()."""
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("DecodeEngine needs a GPU (gfx950); there is no CPU path")
@@ -40,9 +43,13 @@ class DecodeEngine:
             ptrs.append(t.data_ptr())
             self._keep.append(t)
         self.sizes = self.plan.sizes()
-        self.workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
         self.stream = stream if stream is not None else torch.cuda.current_stream()
-        self.plan.bind(ptrs, self.workspace.data_ptr(), self.workspace.numel(), self.stream.cuda_stream)
+        if static_workspace:
+            self.workspace = None
+            self.plan.bind_scratch(ptrs, self.stream.cuda_stream)
+        else:
+            self.workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
+            self.plan.bind(ptrs, self.workspace.data_ptr(), self.workspace.numel(), self.stream.cuda_stream)
         self.buffers = self.plan.buffers()
         out_n = cfg["vocab"] if cfg.get("vocab", 0) > 0 else cfg["hidden"]
         self.out = torch.empty(out_n, dtype=torch.float32, device="cuda")
@@ -122,6 +129,8 @@ class DecodeEngine:
     def buffer(self, name: str):
         """A view of a named workspace buffer (per-layer intermediates of the last step)."""
         torch = self.torch
+        if self.workspace is None:
+            raise ValueError("an engine bound to the static workspace exposes no named buffers")
         b = self.buffers[name]
         nbytes = b["count"] * 4
         raw = self.workspace[b["offset"]:b["offset"] + nbytes]
@@ -129,5 +138,6 @@ class DecodeEngine:
 
     def task_log(self):
         """[n_log, 16] int64: execs, epoch, wg, xcd, t_start, t_ready, t_end, t_mid, t_staged,
-        t_streamed, reserved... (times: 100 MHz counter, low 32 bits)."""
+        t_streamed, t_signal, t_aux[5] (times: the device's 100 MHz clock, low 32 bits; t_end,
+        t_mid, t_staged, t_streamed and t_aux only in a build with the detailed log)."""
         return self.buffer("task_log").view(-1, 16).to(self.torch.int64) & 0xFFFFFFFF
