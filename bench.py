@@ -78,6 +78,35 @@ def copy_calibration(nbytes, reps):
                       "launches": reps}), flush=True)
 
 
+def stream_read(nbytes_list, reps):
+    """The HBM read ceiling for the engine's loads (dec_stream_read): GB/s per buffer size,
+    the mean over `reps` launches timed with events on one stream."""
+    import torch
+    from persistent_tile_scheduled_amd import binding as B
+    n_cu = B.device_query().n_cu
+    sink = torch.empty(n_cu * 512, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for nbytes in nbytes_list:
+        buf = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+        for _ in range(3):
+            B.stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * 4, stream.cuda_stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            B.stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * 4, stream.cuda_stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        rows.append({"bytes": nbytes, "us_per_launch": round(us, 2), "GB_s": round(nbytes / us / 1e3, 1)})
+        print(f"[bench] stream read {nbytes / 2**20:.0f} MiB: {nbytes / us / 1e3:.1f} GB/s", file=sys.stderr, flush=True)
+        del buf
+    best = max(r["GB_s"] for r in rows)
+    print(json.dumps({"metric": "HBM stream-read rate with the engine's loads (dec_stream_read)", "value": best,
+                      "unit": "GB/s", "higher_is_better": True, "peak": HBM_PEAK_GBS,
+                      "frac": round(best / HBM_PEAK_GBS, 4), "launches_per_size": reps, "sizes": rows}), flush=True)
+
+
 def cpu_baseline(cfg, w, x, kv, eng=None, budget_s=10.0):
     """The fp64 oracle, as it stands, timed on a bounded sample of the same step: layers 0,
     1, ... in order (each from the previous layer's oracle output) until about `budget_s`
@@ -136,15 +165,48 @@ def cpu_baseline(cfg, w, x, kv, eng=None, budget_s=10.0):
         oracle.head(cfg, Wc, xo)
         head_s = time.perf_counter() - t0
     per_token = layer_s / done * cfg["n_layers"] + head_s
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
-    return {"value": per_token * 1e6, "unit": "us/token", "cores": int(cores), "kind": "oracle",
+    return {"value": per_token * 1e6, "unit": "us/token", "kind": "oracle",
             "sample": f"layers 0..{done - 1} of {cfg['n_layers']} ({layer_s:.2f} s) extrapolated x{cfg['n_layers'] / done:.2f}"
                       + (f" + final norm and LM head ({head_s:.2f} s)" if has_head else "")}
+
+
+def host_description():
+    """The host the oracle runs on: core counts, CPU model, BLAS library and its threads."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, threads = "unknown", None
+    try:
+        import threadpoolctl
+        for i in threadpoolctl.threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')}"
+                threads = i.get("num_threads")
+                break
+    except Exception:
+        pass
+    return {"cpu_model": model, "cores_online": os.cpu_count(), "cores_available": len(os.sched_getaffinity(0)),
+            "blas": blas, "blas_threads": threads}
+
+
+def cpu_baselines(cfg, w, x, kv, eng, budget_s):
+    """The oracle timed twice on the host: with every BLAS thread the process may use, and
+    with one thread (each on its own bounded sample of the same step)."""
+    import threadpoolctl
+    host = host_description()
+    run_all = cpu_baseline(cfg, w, x, kv, eng, budget_s)
+    with threadpoolctl.threadpool_limits(limits=1, user_api="blas"):
+        run_one = cpu_baseline(cfg, w, x, kv, eng, budget_s)
+    threads = host["blas_threads"] or host["cores_available"]
+    out = dict(run_all, cores=int(threads), threads=int(threads), **host)
+    out["one_thread"] = {"value": run_one["value"], "unit": "us/token", "cores": 1, "sample": run_one["sample"]}
+    return out
 
 
 def generation(args, cfg, w, kv, x):
@@ -182,17 +244,19 @@ def generation(args, cfg, w, kv, x):
     eng.status()
     st = eng.read_state()
     assert st[0] == n and st[2] == T + W, st
+    gpu_us = a.elapsed_time(b) * 1e3 / T
     us = wall * 1e6 / T
     print(json.dumps({
         "metric": ("greedy generation latency (us/token), steps issued back to back" if greedy else
                    "decode latency at advancing positions (us/token), steps issued back to back"),
         "value": round(us, 2), "unit": "us/token", "n_gpus": 1, "steps": T, "warmup": W,
         "higher_is_better": False, "tokens_per_s": round(1e6 / us, 1),
-        "gpu_us_per_token": round(a.elapsed_time(b) * 1e3 / T, 2),
+        "gpu_us_per_token": round(gpu_us, 2),
         "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
                    "positions": [n - T, n - 1], "batch": 1},
         "launch": "dynamic plan (max_len = kv_len), one launch per token, no host work between tokens",
         "dtype": "bf16", "data": "synthetic"}), flush=True)
+    teardown(eng)
 
 
 def main():
@@ -203,6 +267,8 @@ def main():
     ap.add_argument("--config", default="8b_4k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, metavar="S",
+                    help="seconds of oracle layer time per CPU-baseline run (all cores, one thread)")
     ap.add_argument("--launch", choices=["persistent", "stages", "graph"], default="persistent",
                     help="persistent: the step as one engine launch (the product); stages: one launch per "
                          "stage of the same tasks; graph: those launches replayed from a HIP graph")
@@ -211,6 +277,9 @@ def main():
                          "(positions kv_len - T .. kv_len - 1, each step's token from the last)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--stream-read", action="store_true",
+                    help="only measure the HBM stream-read rate of the engine's loads (dec_stream_read) "
+                         "over 256 MiB, 1 GiB and 4 GiB buffers")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this engine has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -221,6 +290,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(args.steps, 1))
+        return
+    if args.stream_read:
+        stream_read([256 << 20, 1 << 30, 4 << 30], max(args.steps, 1))
         return
 
     import workloads
@@ -269,8 +341,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, w, x, kv, eng)
+        print("[bench] timing the fp64 oracle on a bounded sample (all cores, then one thread)", file=sys.stderr, flush=True)
+        cpu = cpu_baselines(cfg, w, x, kv, eng, args.cpu_budget)
 
     line = {
         "metric": METRIC,
@@ -302,6 +374,19 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    teardown(eng)
+
+
+def teardown(eng):
+    """Release the plan and the engine's device memory before the interpreter exits, with the
+    device idle: nothing of the engine is left to interpreter shutdown (profilers that hook the
+    runtime tear down in exit handlers)."""
+    import torch
+    torch.cuda.synchronize()
+    eng.plan.close()
+    del eng
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

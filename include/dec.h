@@ -279,6 +279,17 @@ dec_status dec_plan_reset(struct dec_plan* plan, void* stream);
 /* Device watchdog budget for one dependency wait, in microseconds (default 2 000 000). */
 dec_status dec_plan_set_watchdog(struct dec_plan* plan, int64_t microseconds);
 
+/* The HBM read ceiling of the current device for the engine's access pattern, to set a step's
+ * achieved bandwidth against: one launch in which every compute unit's workgroup streams a
+ * contiguous share of `bytes` at `buf` with 16-byte non-temporal loads, as many in flight per
+ * wave as the engine's weight ring, folding what it reads into one word per thread of `sink`
+ * (n_cu * 512 words). The pages' premise is that a batch-1 decode step is bound by memory
+ * bandwidth ("Static Compilation for LLM Inference", section 5.4); this is that bound as the
+ * engine's loads meet it. Asynchronous on `stream`; time it with events.
+ * Errors: INVAL (null, unaligned, bytes not a positive multiple of 16), CAPACITY (sink too
+ * small), DEVICE, HIP. */
+dec_status dec_stream_read(const void* buf, int64_t bytes, void* sink, int64_t sink_bytes, void* stream);
+
 const char* dec_last_error(void);
 /* Describe the current HIP device (gfx arch, CU/XCD counts, LDS). */
 dec_status dec_device_query(dec_device_info* out);

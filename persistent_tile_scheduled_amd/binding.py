@@ -107,6 +107,7 @@ def lib() -> C.CDLL:
         "dec_plan_status": (C.c_int, [P, P]),
         "dec_plan_reset": (C.c_int, [P, P]),
         "dec_plan_set_watchdog": (C.c_int, [P, C.c_int64]),
+        "dec_stream_read": (C.c_int, [P, C.c_int64, P, C.c_int64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -123,7 +124,7 @@ ABI_SYMBOLS = ["dec_last_error", "dec_device_query", "dec_plan_create", "dec_pla
                "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_plan_bind_scratch", "dec_step",
                "dec_plan_n_stages",
                "dec_step_stages", "dec_plan_create_dynamic", "dec_step_dynamic", "dec_plan_status",
-               "dec_plan_reset", "dec_plan_set_watchdog"]
+               "dec_plan_reset", "dec_plan_set_watchdog", "dec_stream_read"]
 
 
 def _check(status: int):
@@ -148,6 +149,12 @@ def device_info(gfx_arch=950, n_cu=256, n_xcd=8, lds=160 * 1024, max_threads=204
     d = DeviceInfo()
     d.gfx_arch, d.n_cu, d.n_xcd, d.lds_bytes_per_cu, d.max_threads_per_cu = gfx_arch, n_cu, n_xcd, lds, max_threads
     return d
+
+
+def stream_read(buf_ptr: int, nbytes: int, sink_ptr: int, sink_bytes: int, stream: int = 0):
+    """One stream-read launch (dec_stream_read): the device's HBM read ceiling for the engine's loads."""
+    _check(lib().dec_stream_read(C.c_void_p(int(buf_ptr)), int(nbytes), C.c_void_p(int(sink_ptr)), int(sink_bytes),
+                                 C.c_void_p(int(stream))))
 
 
 def device_query() -> DeviceInfo:

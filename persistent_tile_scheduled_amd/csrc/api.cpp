@@ -16,6 +16,7 @@ extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, i
                                         hipStream_t stream);
 extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu);
 extern "C" hipError_t dec_scratch_current(void** ptr, size_t* bytes);
+extern "C" hipError_t dec_stream_read_launch(const void* buf, int64_t bytes, int n_wg, uint32_t* sink, hipStream_t stream);
 
 struct dec_plan {
   dec::PlanData P;
@@ -478,6 +479,20 @@ dec_status dec_step_dynamic(dec_plan* plan, const void* x, void* kv, void* out, 
 dec_status dec_step_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t stage_lo, int32_t stage_hi,
                            void* stream) {
   return launch_stages(plan, x, kv, out, stage_lo, stage_hi, stream);
+}
+
+dec_status dec_stream_read(const void* buf, int64_t bytes, void* sink, int64_t sink_bytes, void* stream) {
+  if (!buf || !sink) return fail(DEC_E_INVAL, "null argument");
+  if (bytes < 16 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(DEC_E_INVAL, "the buffer must be 16-byte aligned and a positive multiple of 16 bytes");
+  dec_device_info dev;
+  dec_status st = dec_device_query(&dev);
+  if (st != DEC_OK) return st;
+  if (sink_bytes < (int64_t)dev.n_cu * dec::kThreads * 4 || reinterpret_cast<uintptr_t>(sink) % 4)
+    return fail(DEC_E_CAPACITY, "sink must hold n_cu * 512 4-byte words");
+  hipError_t e = dec_stream_read_launch(buf, bytes, dev.n_cu, static_cast<uint32_t*>(sink), reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream-read launch");
+  return DEC_OK;
 }
 
 dec_status dec_plan_status(dec_plan* plan, void* stream) {

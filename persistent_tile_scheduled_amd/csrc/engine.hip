@@ -2522,6 +2522,59 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0, wfmt), dec::kThreads, (size_t)lds_bytes);
 }
 
+// ------------------------------------------------------------------ stream-read ceiling
+//
+// The HBM read rate this part reaches with the engine's access pattern, as a reference for
+// the step's achieved bandwidth: every workgroup (one per CU, 8 waves) streams a contiguous
+// share of a buffer with 16-byte non-temporal loads, two batches of eight 1-KB wave loads in
+// flight per wave (the engine's weight ring), and folds what it reads into one word per
+// thread so that no load is dropped.
+namespace dec {
+__global__ void __launch_bounds__(kThreads, 1) dec_stream_read_kernel(const u4* buf, int64_t n16, uint32_t* sink) {
+  const int64_t per_wg = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per_wg, hi = lo + per_wg < n16 ? lo + per_wg : n16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t acc = 0;
+  // chunk c of the workgroup's share: 64 consecutive 16-byte words; wave w takes chunks w, w + 8, ...
+  const int64_t nchunk = hi > lo ? (hi - lo + 63) / 64 : 0;
+  auto addr = [&](int64_t c) {
+    int64_t i = lo + c * 64 + lane;
+    return buf + (i < hi ? i : hi - 1);
+  };
+  u4 a[NB], b[NB];
+  int64_t c = wave;
+  auto load = [&](u4 (&r)[NB], int64_t c0) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int64_t ck = c0 + (int64_t)k * kWaves;
+      r[k] = ck < nchunk ? ldg_nt(addr(ck)) : u4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto fold = [&](const u4 (&r)[NB]) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) acc += r[k].x ^ r[k].y ^ r[k].z ^ r[k].w;
+  };
+  load(a, c);
+  load(b, c + (int64_t)NB * kWaves);
+  for (; c < nchunk; c += (int64_t)2 * NB * kWaves) {
+    fold(a);
+    load(a, c + (int64_t)2 * NB * kWaves);
+    fold(b);
+    load(b, c + (int64_t)3 * NB * kWaves);
+  }
+  sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+}  // namespace dec
+
+// One stream-read launch over `bytes` (a multiple of 16) at `buf`, n_wg workgroups; `sink`
+// receives n_wg * 512 words.
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_stream_read_launch(const void* buf, int64_t bytes, int n_wg,
+                                                                                 uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(dec::dec_stream_read_kernel, dim3(n_wg), dim3(dec::kThreads), 0, stream,
+                     static_cast<const dec::u4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ the static workspace
 //
 // For callers that cannot allocate device memory (code under stream capture, serving loops,
