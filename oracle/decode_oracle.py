@@ -297,6 +297,79 @@ def gqa_layer(cfg: dict, W: Callable, l: int, x: np.ndarray, kv_layer, kv_len: i
     return xo, t
 
 
+def verify_visible(kv_len: int, i: int, M: int) -> int:
+    """Causal visibility in a block of M new tokens: token i (position kv_len + i) attends the
+    first kv_len + i + 1 positions of the cache, itself included, none of the later tokens."""
+    return kv_len + i + 1
+
+
+def gqa_verify_layer(cfg: dict, W: Callable, l: int, X: np.ndarray, kv_layer, kv_len: int):
+    """One pre-norm GQA layer for M tokens at once (a multi-token verification step): token i
+    sits at position p_i = kv_len + i, and attends causally, over the cached positions
+    [0, kv_len) and the block's own positions up to and including p_i. Every token's new k, v
+    is appended to the cache (rounded to bf16, reading R11) before any attention reads it.
+    The pages name multi-token prediction and speculative verification as the multi-token
+    lever (the TileRT talk, practice section) without a formula; this is the causal block
+    attention that M sequential decode steps compute (pinned against them).
+
+    X: [M][hidden]. kv_layer: bf16 bits [2][n_kv][>=kv_len][head_dim].
+    Returns (X_next [M][hidden], trace dict of [M][...] arrays).
+    """
+    p = f"layers.{l}."
+    X = np.asarray(X, dtype=np.float64)
+    M = X.shape[0]
+    nq, nkv, hd = cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    eps, theta = cfg["rms_eps"], cfg["rope_theta"]
+    g_attn, g_ffn = _w64(W, p + "attn_norm"), _w64(W, p + "ffn_norm")
+    t: Dict[str, np.ndarray] = {"x_in": X}
+    xn = np.stack([rmsnorm(X[i], g_attn, eps) for i in range(M)])
+    q = np.stack([linear_bits(W, p + "wq", xn[i]).reshape(nq, hd) for i in range(M)])
+    k = np.stack([linear_bits(W, p + "wk", xn[i]).reshape(nkv, hd) for i in range(M)])
+    v = np.stack([linear_bits(W, p + "wv", xn[i]).reshape(nkv, hd) for i in range(M)])
+    q = np.stack([rope(q[i], kv_len + i, theta) for i in range(M)])
+    k = np.stack([rope(k[i], kv_len + i, theta) for i in range(M)])
+    t["q"] = q.reshape(M, -1)
+    k16, kbits = round_to_bf16(k)
+    v16, vbits = round_to_bf16(v)
+    t["k_new_bits"], t["v_new_bits"] = kbits.reshape(M, -1), vbits.reshape(M, -1)
+    kvl = np.asarray(kv_layer)
+    scale = 1.0 / math.sqrt(hd)
+    o = np.empty((M, nq, hd))
+    for g in range(nkv):
+        # the cache as the block leaves it: cached rows, then the M appended rows
+        Kc = np.concatenate([widen_bf16(kvl[0, g, :kv_len]), k16[:, g]], axis=0)
+        Vc = np.concatenate([widen_bf16(kvl[1, g, :kv_len]), v16[:, g]], axis=0)
+        for i in range(M):
+            m = verify_visible(kv_len, i, M)
+            for h in range(nq):
+                if kv_group(h, nq, nkv) == g:
+                    o[i, h] = attend(q[i, h], Kc[:m], Vc[:m], scale)
+    t["attn"] = o.reshape(M, -1)
+    H = X + np.stack([linear_bits(W, p + "wo", t["attn"][i]) for i in range(M)])
+    t["h"] = H
+    hn = np.stack([rmsnorm(H[i], g_ffn, eps) for i in range(M)])
+    a = np.stack([silu(linear_bits(W, p + "w_gate", hn[i])) * linear_bits(W, p + "w_up", hn[i]) for i in range(M)])
+    t["ffn_act"] = a
+    f = np.stack([linear_bits(W, p + "w_down", a[i]) for i in range(M)])
+    t["ffn_out"] = f
+    t["x_out"] = H + f
+    return t["x_out"], t
+
+
+def verify_forward(cfg: dict, W: Callable, x_bits, kv, kv_len: Optional[int] = None):
+    """A verification step of M tokens (GQA family): x_bits bf16 bits [M][hidden]; kv
+    indexable by layer (cache bits, positions [0, kv_len) read). Returns
+    {"layers": [trace...], "out": [M][vocab] logits (or [M][hidden] last hidden states)}."""
+    n = cfg["kv_len"] if kv_len is None else kv_len
+    X = widen_bf16(np.asarray(x_bits))
+    traces: List[Dict[str, np.ndarray]] = []
+    for l in range(cfg["n_layers"]):
+        X, t = gqa_verify_layer(cfg, W, l, X, kv[l], n)
+        traces.append(t)
+    outs = np.stack([head(cfg, W, X[i])["out"] for i in range(X.shape[0])])
+    return {"layers": traces, "x_final": X, "out": outs}
+
+
 def mla_attention(cfg: dict, W: Callable, l: int, xn: np.ndarray, kv_layer, kv_len: int,
                   absorbed_trace: bool = True):
     """MLA attention of one layer (naive definition), plus the absorbed-form intermediates.

@@ -147,20 +147,30 @@ def _weight_specs_bf16(cfg: dict) -> List[TensorSpec]:
     return out
 
 
+def n_tokens(cfg: dict) -> int:
+    """Tokens per step: 1 for a decode step; M > 1 for a multi-token verification step
+    ("verify": M in the config), whose M tokens take positions kv_len .. kv_len + M - 1."""
+    return int(cfg.get("verify", 1))
+
+
 def kv_shape(cfg: dict, kv_len: Optional[int] = None) -> Tuple[int, ...]:
-    """Cache layout: GQA [L][2][n_kv][kv_len+1][head_dim]; MLA/MoE [L][kv_len+1][kv_lora+rope]."""
+    """Cache layout: GQA [L][2][n_kv][kv_len+M][head_dim]; MLA/MoE [L][kv_len+1][kv_lora+rope]
+    (M = tokens per step: the step writes slots kv_len .. kv_len + M - 1)."""
     n = cfg["kv_len"] if kv_len is None else kv_len
     if cfg["arch"] == "gqa":
-        return (cfg["n_layers"], 2, cfg["n_kv_heads"], n + 1, cfg["head_dim"])
+        return (cfg["n_layers"], 2, cfg["n_kv_heads"], n + n_tokens(cfg), cfg["head_dim"])
     return (cfg["n_layers"], n + 1, cfg["kv_lora_rank"] + cfg["qk_rope"])
 
 
 def x_shape(cfg: dict) -> Tuple[int, ...]:
-    return (cfg["hidden"],)
+    m = n_tokens(cfg)
+    return (m, cfg["hidden"]) if m > 1 else (cfg["hidden"],)
 
 
 def out_shape(cfg: dict) -> Tuple[int, ...]:
-    return (cfg["vocab"],) if cfg.get("vocab", 0) > 0 else (cfg["hidden"],)
+    m = n_tokens(cfg)
+    o = (cfg["vocab"],) if cfg.get("vocab", 0) > 0 else (cfg["hidden"],)
+    return (m,) + o if m > 1 else o
 
 
 def _quantize_e4m3_rows(torch, w32):
@@ -239,7 +249,7 @@ def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = Non
         else:
             raise ValueError(s.init)
     n = cfg["kv_len"] if kv_len is None else kv_len
-    kvs = kv_shape(cfg, n)
+    kvs = kv_shape(cfg, n)  # positions [0, n) drawn, the step's own slots zero
     kv = torch.zeros(kvs, dtype=torch.bfloat16, device=dev)
     if n > 0:
         if cfg["arch"] == "gqa":
