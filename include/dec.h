@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 1
+#define DEC_ABI_VERSION 2
 
 typedef struct dec_plan dec_plan;   /* opaque, library-owned host object */
 
@@ -144,6 +144,8 @@ typedef struct dec_task_desc {
   int32_t kv_staged;              /* GQA QKV and attention tasks: cached K/V rows of the
                                      attention split that the workgroup's QKV task copies into
                                      LDS for the attention task right after it (0: none) */
+  int32_t aux3;                   /* attention tasks of a verification step: the block of 8
+                                     query columns (token * heads per group + head) they take */
 } dec_task_desc;
 
 /* A named fp32 (or i32) buffer inside the workspace holding an intermediate of the last
@@ -269,6 +271,31 @@ dec_status dec_step_stages(struct dec_plan* plan, const void* x, void* kv, void*
 dec_status dec_plan_create_dynamic(const dec_model_shape* shape, int64_t max_len, const dec_device_info* dev,
                                    struct dec_plan** out);
 dec_status dec_step_dynamic(struct dec_plan* plan, const void* x, void* kv, void* out, int32_t* state, void* stream);
+
+/* ---- a verification step of several tokens ----
+ * More tokens per step for the same weight bytes: the step that checks a block of draft
+ * tokens (multi-token prediction or another speculative scheme) runs the model on n_tokens
+ * consecutive tokens at once (TileRT talk write-ups, sections on production results with MTP-3
+ * and on raising the tokens produced per byte read). Every weight row is read once for all
+ * tokens; attention is causal inside the block.
+ *
+ * dec_plan_create_verify: a plan for n_tokens (1 .. 4) tokens at positions kv_len ..
+ * kv_len + n_tokens - 1. GQA family with bf16 weights only; dev == NULL plans for the current
+ * device (which must be gfx950) and checks that the kernel fits it, as dec_plan_create; a
+ * given dev plans without touching a GPU, as dec_plan_create_for. The plan runs with dec_step
+ * (whole steps only: dec_step_stages accepts only the full range [0, n_stages)):
+ *   x   : bf16 [n_tokens][hidden], token i's input vector in row i.
+ *   kv  : bf16 [n_layers][2][n_kv_heads][kv_len + n_tokens][head_dim]. Positions [0, kv_len)
+ *         are read; slots kv_len + i are written with token i's post-RoPE k / v (RoPE at
+ *         position kv_len + i). Token i attends to positions [0, kv_len + i].
+ *   out : fp32 [n_tokens][vocab] (vocab == 0: [n_tokens][hidden]), token i's row i.
+ * dec_plan_sizes reports x, kv and out bytes for these shapes, and as algorithmic bytes every
+ * weight once plus kv_len + n_tokens cache positions per layer. Token i's results equal those
+ * of i + 1 single-token steps run in order, up to rounding order.
+ * Errors: as dec_plan_create_for; INVAL for n_tokens outside 1..4, SHAPE for another family,
+ * FP8 weights. */
+dec_status dec_plan_create_verify(const dec_model_shape* shape, int64_t kv_len, int32_t n_tokens,
+                                  const dec_device_info* dev, struct dec_plan** out);
 
 /* Synchronise `stream` and read the sticky device status word: DEC_OK, DEC_E_TIMEOUT (the
  * failing task id is in dec_last_error()) or DEC_E_CAPACITY (a dec_step_dynamic state out of

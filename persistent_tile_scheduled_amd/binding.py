@@ -12,7 +12,7 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdec.so")
 
-DEC_ABI_VERSION = 1
+DEC_ABI_VERSION = 2
 ARCH = {"gqa": 0, "mla": 1, "moe": 2}
 STATUS = {0: "DEC_OK", -1: "DEC_E_INVAL", -2: "DEC_E_SHAPE", -3: "DEC_E_CAPACITY", -4: "DEC_E_DEVICE",
           -5: "DEC_E_OCCUPANCY", -6: "DEC_E_HIP", -7: "DEC_E_TIMEOUT", -8: "DEC_E_UNBOUND", -9: "DEC_E_PLAN"}
@@ -59,7 +59,7 @@ class Sizes(C.Structure):
 class TaskDescC(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("id", "type", "layer", "stage", "wg", "xcd", "list_pos", "unit_begin",
                                          "unit_end", "aux0", "aux1", "n_deps", "dep_first", "signal", "signal2",
-                                         "aux2", "kv_staged")]
+                                         "aux2", "kv_staged", "aux3")]
 
 
 class BufferDesc(C.Structure):
@@ -103,6 +103,7 @@ def lib() -> C.CDLL:
         "dec_plan_n_stages": (C.c_int64, [P]),
         "dec_plan_create_dynamic": (C.c_int, [C.POINTER(ModelShape), C.c_int64, C.POINTER(DeviceInfo), C.POINTER(P)]),
         "dec_step_dynamic": (C.c_int, [P, P, P, P, P, P]),
+        "dec_plan_create_verify": (C.c_int, [C.POINTER(ModelShape), C.c_int64, C.c_int32, C.POINTER(DeviceInfo), C.POINTER(P)]),
         "dec_step_stages": (C.c_int, [P, P, P, P, C.c_int32, C.c_int32, P]),
         "dec_plan_status": (C.c_int, [P, P]),
         "dec_plan_reset": (C.c_int, [P, P]),
@@ -124,7 +125,7 @@ ABI_SYMBOLS = ["dec_last_error", "dec_device_query", "dec_plan_create", "dec_pla
                "dec_plan_buffer_desc", "dec_plan_grid", "dec_plan_bind", "dec_plan_bind_scratch", "dec_step",
                "dec_plan_n_stages",
                "dec_step_stages", "dec_plan_create_dynamic", "dec_step_dynamic", "dec_plan_status",
-               "dec_plan_reset", "dec_plan_set_watchdog", "dec_stream_read"]
+               "dec_plan_reset", "dec_plan_set_watchdog", "dec_stream_read", "dec_plan_create_verify"]
 
 
 def _check(status: int):
@@ -167,20 +168,29 @@ class Plan:
     """Owner of one dec_plan (host object). All device memory belongs to the caller."""
 
     def __init__(self, cfg_or_shape, kv_len: Optional[int] = None, device: Optional[DeviceInfo] = None,
-                 max_len: Optional[int] = None):
+                 max_len: Optional[int] = None, n_tokens: Optional[int] = None):
         """A plan for one kv_len, or, with max_len, a plan whose position is read per step
-        (dec_plan_create_dynamic)."""
+        (dec_plan_create_dynamic), or, with n_tokens (default: a config's "verify" count), a
+        verification step of that many tokens (dec_plan_create_verify)."""
         L = lib()
         if isinstance(cfg_or_shape, dict):
             self.shape = shape_from_config(cfg_or_shape)
             if kv_len is None:
                 kv_len = cfg_or_shape["kv_len"]
+            if n_tokens is None and cfg_or_shape.get("verify"):
+                n_tokens = int(cfg_or_shape["verify"])
         else:
             self.shape = cfg_or_shape
         self.dynamic = max_len is not None
         self.kv_len = int(max_len if self.dynamic else kv_len)
+        self.n_tokens = 1 if n_tokens is None else int(n_tokens)
         h = C.c_void_p()
-        if self.dynamic:
+        if n_tokens is not None:
+            if self.dynamic:
+                raise ValueError("a verification plan has a fixed length")
+            dev = C.byref(device) if device is not None else None
+            _check(L.dec_plan_create_verify(C.byref(self.shape), self.kv_len, self.n_tokens, dev, C.byref(h)))
+        elif self.dynamic:
             dev = C.byref(device) if device is not None else None
             _check(L.dec_plan_create_dynamic(C.byref(self.shape), self.kv_len, dev, C.byref(h)))
         elif device is None:

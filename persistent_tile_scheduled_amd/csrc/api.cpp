@@ -14,7 +14,7 @@
 
 extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, int run, bool cooperative,
                                         hipStream_t stream);
-extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int lds_bytes, int* blocks_per_cu);
 extern "C" hipError_t dec_scratch_current(void** ptr, size_t* bytes);
 extern "C" hipError_t dec_stream_read_launch(const void* buf, int64_t bytes, int n_wg, uint32_t* sink, hipStream_t stream);
 
@@ -109,6 +109,7 @@ void fill_args(dec_plan* p) {
   a.gs_floats = (int32_t)P.gs_floats;
   a.eps = s.rms_eps;
   a.attn_scale_log2 = P.attn_scale_log2;
+  a.ntok = P.ntok;
 }
 
 void copy_name(char* dst, const std::string& s) {
@@ -139,6 +140,21 @@ dec_status check_scratch_owner(dec_plan* plan) {
 
 // One launch of the tasks of stages [lo, hi): cooperative (co-resident grid) when it spans
 // several stages, whose tasks wait on each other; a plain launch for one stage.
+// The plan's kernel must fit one workgroup per CU with the plan's LDS size; on failure the plan
+// is destroyed.
+dec_status check_occupancy(dec_plan** out) {
+  int per_cu = 0;
+  const dec::PlanData& P = (*out)->P;
+  hipError_t e = dec_engine_occupancy(P.shape.arch, P.shape.weight_format, P.ntok, P.lds_bytes, &per_cu);
+  if (e != hipSuccess || per_cu < 1) {
+    dec_plan_destroy(*out);
+    *out = nullptr;
+    if (e != hipSuccess) return hip_fail(e, "occupancy query");
+    return fail(DEC_E_OCCUPANCY, "the engine kernel cannot be resident with the plan's LDS size");
+  }
+  return DEC_OK;
+}
+
 dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int32_t lo, int32_t hi, void* stream) {
   if (!plan) return fail(DEC_E_INVAL, "null plan");
   if (!plan->bound) return fail(DEC_E_UNBOUND, "step before dec_plan_bind");
@@ -147,8 +163,8 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
   if (plan->P.dynamic) return fail(DEC_E_INVAL, "a plan with a per-step length runs with dec_step_dynamic");
-  if (plan->P.shape.weight_format != DEC_WEIGHTS_BF16 && (lo != 0 || hi != plan->P.n_stages))
-    return fail(DEC_E_INVAL, "FP8-weight plans run whole steps only (dec_step)");
+  if ((plan->P.shape.weight_format != DEC_WEIGHTS_BF16 || plan->P.ntok > 1) && (lo != 0 || hi != plan->P.n_stages))
+    return fail(DEC_E_INVAL, "FP8-weight and verification plans run whole steps only (dec_step)");
   if (lo < 0 || hi > plan->P.n_stages || lo >= hi)
     return fail(DEC_E_INVAL, "stage range [" + std::to_string(lo) + ", " + std::to_string(hi) + ") not inside [0, " +
                                  std::to_string(plan->P.n_stages) + ")");
@@ -218,15 +234,7 @@ dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, dec_pla
   if (dev.gfx_arch != 950) return fail(DEC_E_DEVICE, "current device is gfx" + std::to_string(dev.gfx_arch) + ", need gfx950");
   st = dec_plan_create_for(shape, kv_len, &dev, out);
   if (st != DEC_OK) return st;
-  int per_cu = 0;
-  hipError_t e = dec_engine_occupancy((*out)->P.shape.arch, (*out)->P.shape.weight_format, (*out)->P.lds_bytes, &per_cu);
-  if (e != hipSuccess || per_cu < 1) {
-    dec_plan_destroy(*out);
-    *out = nullptr;
-    if (e != hipSuccess) return hip_fail(e, "occupancy query");
-    return fail(DEC_E_OCCUPANCY, "the engine kernel cannot be resident with the plan's LDS size");
-  }
-  return DEC_OK;
+  return check_occupancy(out);
 }
 
 dec_status dec_plan_destroy(dec_plan* plan) {
@@ -254,12 +262,13 @@ dec_status dec_plan_sizes(const dec_plan* plan, dec_sizes* out) {
   if (!plan || !out) return fail(DEC_E_INVAL, "null argument");
   const dec::PlanData& P = plan->P;
   const dec_model_shape& s = P.shape;
-  out->x_bytes = (int64_t)s.hidden * 2;
+  const int64_t nt = P.ntok;  // tokens per step
+  out->x_bytes = nt * s.hidden * 2;
   if (s.arch == DEC_ARCH_GQA)
-    out->kv_bytes = (int64_t)s.n_layers * 2 * s.n_kv_heads * (P.kv_len + 1) * s.head_dim * 2;
+    out->kv_bytes = (int64_t)s.n_layers * 2 * s.n_kv_heads * (P.kv_len + nt) * s.head_dim * 2;
   else
-    out->kv_bytes = (int64_t)s.n_layers * (P.kv_len + 1) * (s.kv_lora_rank + s.qk_rope) * 2;
-  out->out_bytes = (int64_t)(s.vocab > 0 ? s.vocab : s.hidden) * 4;
+    out->kv_bytes = (int64_t)s.n_layers * (P.kv_len + nt) * (s.kv_lora_rank + s.qk_rope) * 2;
+  out->out_bytes = nt * (s.vocab > 0 ? s.vocab : s.hidden) * 4;
   out->workspace_bytes = P.ws_bytes;
   out->weight_bytes = P.weight_bytes;
   out->algorithmic_bytes_per_step = P.alg_bytes;
@@ -297,6 +306,7 @@ dec_status dec_plan_tasks(const dec_plan* plan, dec_task_desc* buf, int64_t cap,
     d.kv_staged = (t.type == dec::T_QKV && t.a5 > 0)    ? dec::split_cached(plan->P.kv_len, t.a4, t.a5)
                   : (t.type == dec::T_ATTN && t.a3 > 0) ? dec::split_cached(plan->P.kv_len, t.a1, t.a2)
                                                         : 0;
+    d.aux3 = (t.type == dec::T_ATTN) ? t.a5 : 0;
   }
   return DEC_OK;
 }
@@ -448,6 +458,30 @@ dec_status dec_plan_create_dynamic(const dec_model_shape* shape, int64_t max_len
   p->wptr.assign(p->P.weights.size(), 0);
   *out = p;
   return DEC_OK;
+}
+
+dec_status dec_plan_create_verify(const dec_model_shape* shape, int64_t kv_len, int32_t n_tokens, const dec_device_info* dev,
+                                  dec_plan** out) {
+  if (!shape || !out) return fail(DEC_E_INVAL, "null argument");
+  *out = nullptr;
+  dec_device_info cur;
+  const bool query = !dev;
+  if (query) {
+    dec_status st = dec_device_query(&cur);
+    if (st != DEC_OK) return st;
+    if (cur.gfx_arch != 950) return fail(DEC_E_DEVICE, "current device is gfx" + std::to_string(cur.gfx_arch) + ", need gfx950");
+    dev = &cur;
+  }
+  dec_plan* p = new dec_plan();
+  std::string err;
+  dec_status st = dec::build_plan(*shape, kv_len, *dev, &p->P, &err, false, n_tokens);
+  if (st != DEC_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  p->wptr.assign(p->P.weights.size(), 0);
+  *out = p;
+  return query ? check_occupancy(out) : DEC_OK;
 }
 
 dec_status dec_step_dynamic(dec_plan* plan, const void* x, void* kv, void* out, int32_t* state, void* stream) {

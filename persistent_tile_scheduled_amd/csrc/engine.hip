@@ -436,8 +436,12 @@ struct StageVec {
       }
       __builtin_amdgcn_s_waitcnt(kVmcnt0);  // wave 0's copies (vector, gains) have landed
       if (kTaskLogDetail && lane == 0) b.t_sub[0] = (uint32_t)now();
-      for (int i = K + lane; i < padK; i += 64) b.xs[i] = 0.f;
     }
+    // a copy by all waves whose last 1-KB block is partial also writes words [K, K rounded up
+    // to 256) (its clamped lanes): every wave's copy must have landed before they are cleared
+    if (off >= 0 && !early_ok() && (K & 255)) __syncthreads();
+    if (threadIdx.x < 64)
+      for (int i = K + (int)threadIdx.x; i < padK; i += 64) b.xs[i] = 0.f;
     __syncthreads();
     b.norm = 1.f;
     if (gain) {
@@ -2290,6 +2294,640 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
       t.a2, [&] { stage_ids(A, L, b, ids); });
 }
 
+
+// ------------------------------------------------------------------ multi-token verification
+//
+// A verification step of MT tokens at positions n .. n + MT - 1 (the check of draft tokens in
+// speculative decoding, or the tokens of multi-token prediction; the TileRT talk, practice
+// section): every weight row is read once for all MT tokens, so each GEMV becomes a skinny GEMM
+// of MT columns, computed on the vector ALUs as MT dot products per row. Activations are
+// [MT][width] in the workspace and [MT][padded width] in LDS; an input too wide to stage for
+// all MT tokens at once (the down projection's) is staged and streamed in column phases, the
+// row sums adding up in LDS across phases. Attention is causal within the block: token i sees
+// the cached positions and the block's positions n .. n + i.
+
+// Per-token 1/rms of a verification step's staged inputs: LDS words after the staging flags
+// (written in the staging step, read in the epilogue; 1 where there is no RMSNorm).
+__device__ __forceinline__ float* token_norms(const Blk& b) { return reinterpret_cast<float*>(b.flags) + 48; }
+
+// Staging of columns [k0, k0 + kw) of MT vectors (token i at float offset off + i * stride, or
+// the bf16 step input x + i * stride when off < 0) into xs[i * pw + c], zero-padded to pw. With
+// a gain (never phased: kw == K) each token is RMSNormed: xs holds g * x and the per-token 1/rms goes to LDS (token_norms).
+template <int MT>
+struct StageM {
+  int off, stride;
+  const uint16_t* s16;
+  int K, k0, kw, pw;
+  const uint16_t* gain;
+  float eps;
+  bool coh;
+  __device__ __forceinline__ bool early_ok() const { return off >= 0 && MT * kw <= kEarlyDmaFloats; }
+  __device__ __forceinline__ void before(Blk& b) const {  // wave 0
+    if (gain) dma_to_lds(b.gs, (const float*)gain, K / 2);
+  }
+  __device__ __forceinline__ void early(Blk& b) const {  // wave 0
+    if (!early_ok()) return;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (coh) dma_to_lds<true>(b.xs + i * pw, b.actp + off + i * stride + k0, kw);
+      else dma_to_lds(b.xs + i * pw, b.actp + off + i * stride + k0, kw);
+    }
+  }
+  __device__ __forceinline__ void finish(Blk& b) const {
+    if (off >= 0 && !early_ok()) {
+      // every wave copies a share: 1-KB chunk j of token i by wave (i * chunks + j) % 8
+      const int nch = (kw + 255) / 256, lane = threadIdx.x & 63;
+      for (int q = (int)(threadIdx.x >> 6); q < MT * nch; q += kWaves) {
+        const int i = q / nch, j = q - i * nch;
+        int c = j * 256 + lane * 4;
+        c = c < kw ? c : kw - 4;
+        if (coh) lds_dma16<true>(b.actp + off + i * stride + k0 + c, b.xs + i * pw + j * 256);
+        else lds_dma16(b.actp + off + i * stride + k0 + c, b.xs + i * pw + j * 256);
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    }
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      if (off < 0) {  // the bf16 step inputs (layer 0)
+        for (int i = 0; i < MT; ++i)
+          for (int c = lane * 4; c < kw; c += 256) {
+            const uint2 x = *(const uint2*)(s16 + (size_t)i * stride + k0 + c);
+            *(f4*)(b.xs + i * pw + c) = f4{bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y)};
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    }
+    // (as in StageVec: the clamped lanes of another wave's partial last block write past kw)
+    if (off >= 0 && !early_ok() && (kw & 255)) __syncthreads();
+    if (threadIdx.x < 64)
+      for (int i = 0; i < MT; ++i)
+        for (int c = kw + (int)threadIdx.x; c < pw; c += 64) b.xs[i * pw + c] = 0.f;
+    __syncthreads();
+    float* nrm = token_norms(b);
+    if (threadIdx.x < MT) nrm[threadIdx.x] = 1.f;
+    if (gain) {
+      const uint16_t* g16 = reinterpret_cast<const uint16_t*>(b.gs);
+      float* part = reinterpret_cast<float*>(b.flags) + 8;  // [wave][MT] sums of squares
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        float ss = 0.f;
+        for (int c = threadIdx.x * 4; c < K; c += kThreads * 4) {
+          const uint2 g = *(const uint2*)(g16 + c);
+          f4 v = *(f4*)(b.xs + i * pw + c);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          v.x *= bf_lo(g.x);
+          v.y *= bf_hi(g.x);
+          v.z *= bf_lo(g.y);
+          v.w *= bf_hi(g.y);
+          *(f4*)(b.xs + i * pw + c) = v;
+        }
+        ss = wave_sum(ss);
+        if ((threadIdx.x & 63) == 0) part[(threadIdx.x >> 6) * MT + i] = ss;
+      }
+      __syncthreads();
+      if (threadIdx.x < MT) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += part[w * MT + threadIdx.x];
+        nrm[threadIdx.x] = 1.0f / sqrtf(tot / (float)K + eps);
+      }
+    }
+  }
+};
+
+// Streams chunks [ca, cb) of the task's rows (bf16, 512 columns per chunk) over a flattened
+// (row, chunk) range [fa, fb), dotting each with the MT staged vectors (xs[i * pw + column -
+// ca * 512]); each row's partial sums are added into ys[row * MT + i] with LDS atomics when the
+// wave's part of the row ends.
+template <int MT>
+struct StreamM {
+  const uint64_t* rowp;
+  int fb, K, ca, cpr, pw, lane;
+  int lf, lj, lc;
+  const uint8_t* lrow;
+  int cf, cj, cc;
+  float acc[MT][2];
+  __device__ __forceinline__ void init(const uint64_t* rp, int fa, int fb_, int K_, int ca_, int cb_, int pw_, int lane_) {
+    rowp = rp;
+    fb = fb_;
+    K = K_;
+    ca = ca_;
+    cpr = cb_ - ca_;
+    pw = pw_;
+    lane = lane_;
+    const int j0 = fa / cpr, c0 = fa - j0 * cpr;
+    lf = cf = fa;
+    lj = cj = j0;
+    lc = cc = c0;
+    lrow = (fa < fb) ? (const uint8_t*)uni64(rowp[j0]) : nullptr;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[i][0] = acc[i][1] = 0.f;
+  }
+  __device__ __forceinline__ void load(u4 (&bf)[NB]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (lf < fb) {
+        int col = (ca + lc) * kChunkCols + lane * 8;
+        col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
+        bf[i] = ldg_nt(lrow + (size_t)col * 2);
+        ++lf;
+        if (++lc == cpr) {
+          lc = 0;
+          ++lj;
+          if (lf < fb) lrow = (const uint8_t*)uni64(rowp[lj]);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const float* xs, float* ys) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (cf < fb) {
+        const u4 w = bf[k];
+        const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y), bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+        const float* xp = xs + cc * kChunkCols + lane * 8;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const f4 x0 = *(const f4*)(xp + i * pw), x1 = *(const f4*)(xp + i * pw + 4);
+          acc[i][0] = fmaf(wf[0], x0.x, acc[i][0]);
+          acc[i][1] = fmaf(wf[1], x0.y, acc[i][1]);
+          acc[i][0] = fmaf(wf[2], x0.z, acc[i][0]);
+          acc[i][1] = fmaf(wf[3], x0.w, acc[i][1]);
+          acc[i][0] = fmaf(wf[4], x1.x, acc[i][0]);
+          acc[i][1] = fmaf(wf[5], x1.y, acc[i][1]);
+          acc[i][0] = fmaf(wf[6], x1.z, acc[i][0]);
+          acc[i][1] = fmaf(wf[7], x1.w, acc[i][1]);
+        }
+        ++cf;
+        const bool row_end = ++cc == cpr;
+        if (row_end || cf == fb) {
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const float v = wave_sum(acc[i][0] + acc[i][1]);
+            if (lane == 0) atomicAdd(ys + cj * MT + i, v);
+            acc[i][0] = acc[i][1] = 0.f;
+          }
+          if (row_end) {
+            cc = 0;
+            ++cj;
+          }
+        }
+      }
+      // one chunk at a time: MT tokens' x reads of several chunks held at once would not fit
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// The verification GEMV: rows [0, nrows) of the row map against MT staged vectors of K
+// columns, in column phases of at most A.xs_floats / MT floats each; every wave takes an even
+// share of each phase's (row, chunk) pairs. Returns with ys[row * MT + i] complete (before
+// 1/rms) and wave 0 running `epi`.
+template <int MT, class RM, class StageF, class EpiF>
+__device__ __forceinline__ bool run_gemv_m(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm, int nrows, int K,
+                                           StageF&& stage_of, EpiF&& epi) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int cfull = (K + kChunkCols - 1) / kChunkCols;
+  const int cph_max = A.xs_floats / (MT * kChunkCols);  // chunks per phase (the planner keeps it >= 1)
+  const int nph = (cfull + cph_max - 1) / cph_max;
+  StreamM<MT> s;
+  u4 buf[2][NB];
+  auto phase_range = [&](int p, int& ca, int& cb) {
+    ca = (int)((int64_t)cfull * p / nph);
+    cb = (int)((int64_t)cfull * (p + 1) / nph);
+  };
+  auto start = [&](int p) {
+    int ca, cb;
+    phase_range(p, ca, cb);
+    const int nf = nrows * (cb - ca), fa = wave_start(nf, wave), fb = wave_start(nf, wave + 1);
+    s.init(b.rowp, fa, fb, K, ca, cb, (cb - ca) * kChunkCols, lane);
+    s.load(buf[0]);
+    s.load(buf[1]);
+  };
+  // row pointers of every row (each wave writes a share; the staging barrier publishes them)
+  for (int j = (int)threadIdx.x; j < nrows; j += kThreads) b.rowp[j] = (uint64_t)(uintptr_t)rm.row(j);
+  __syncthreads();
+  int ca0, cb0;
+  phase_range(0, ca0, cb0);
+  const auto st0 = stage_of(ca0, cb0);
+  if (threadIdx.x < 64) st0.before(b);
+  start(0);
+  if (!wait_deps(A, b, t, 0, -1, [&] { st0.early(b); })) return false;
+  for (int i = threadIdx.x; i < nrows * MT; i += kThreads) b.ys[i] = 0.f;  // (the staging barrier orders this)
+  st0.finish(b);
+  for (int p = 0; p < nph; ++p) {
+    if (p > 0) {
+      __syncthreads();  // every wave is done with the previous phase's columns
+      int ca, cb;
+      phase_range(p, ca, cb);
+      start(p);
+      // (a short copy is wave 0's, issued in early(): during the wait for phase 0, here now)
+      const auto st = stage_of(ca, cb);
+      if (threadIdx.x < 64) st.early(b);
+      st.finish(b);
+    }
+    while (s.cf < s.fb) {
+      s.consume(buf[0], b.xs, b.ys);
+      s.load(buf[0]);
+      if (s.cf >= s.fb) break;
+      s.consume(buf[1], b.xs, b.ys);
+      s.load(buf[1]);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) epi();
+  return true;
+}
+
+template <int MT>
+__device__ __forceinline__ float token_norm(const Blk& b, int tk) { return token_norms(b)[tk]; }
+
+template <int MT>
+__device__ __forceinline__ bool task_qkv_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden, hd = A.hd, hh = hd / 2, r = A.nq / A.nkv, g = t.a0;
+  const RmQKV rm{wp<uint8_t>(A, L.w[LW_WQ]), wp<uint8_t>(A, L.w[LW_WK]), wp<uint8_t>(A, L.w[LW_WV]), g, r, hd, hh, K, t.u0};
+  const int xin = L.act[LA_X_IN];
+  return run_gemv_m<MT>(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K,
+      [&](int ca, int cb) {
+        return StageM<MT>{xin, K, b.x, K, ca * kChunkCols, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps, false};
+      },
+      [&] {
+        const int n = b.n;
+        const size_t nslot = (size_t)A.kv_len + MT;
+        const size_t lay = (size_t)2 * A.nkv * nslot * hd;  // cache elements per layer
+        const rsrc_t kvr = make_rsrc(A.kv + (size_t)t.layer * lay, (uint32_t)(lay * 2));
+        for (int e = threadIdx.x; e < (t.u1 - t.u0) * MT; e += 64) {
+          const int i = e / MT, tk = e - i * MT;
+          const int u = t.u0 + i, slot = u / hh, k = u - slot * hh;
+          const float nv = token_norm<MT>(b, tk);
+          float a = b.ys[(2 * i) * MT + tk] * nv, c = b.ys[(2 * i + 1) * MT + tk] * nv;
+          if (slot <= r) {  // RoPE at the token's position (row tk of the table)
+            const float* rope = b.rope + (size_t)tk * 2 * A.rope_half;
+            const float cs = rope[k], sn = rope[A.rope_half + k];
+            const float a2 = a * cs - c * sn;
+            c = c * cs + a * sn;
+            a = a2;
+          }
+          if (slot < r) {
+            const uint32_t q = (uint32_t)(L.act[LA_Q] + tk * A.nq * hd + (g * r + slot) * hd);
+            cst(b.act, (q + k) * 4u, a);
+            cst(b.act, (q + k + hh) * 4u, c);
+          } else {
+            const int sel = slot - r;  // 0: k, 1: v
+            const uint32_t kn = (uint32_t)(L.act[LA_KVNEW] + tk * 2 * A.nkv * hd + (sel * A.nkv + g) * hd);
+            cst(b.act, (kn + k) * 4u, a);
+            cst(b.act, (kn + k + hh) * 4u, c);
+            const uint32_t row = (uint32_t)(((size_t)(sel * A.nkv + g) * nslot + n + tk) * hd);
+            cst16(kvr, (row + k) * 2u, f2bf(a));
+            cst16(kvr, (row + k + hh) * 2u, f2bf(c));
+          }
+        }
+      });
+}
+
+// Causal split-K attention of one KV group for MT tokens over positions [p0, p1) of the
+// n + MT positions (the block's own positions at n .. n + MT - 1). Of the group's C = MT * r
+// query columns (column c: token c / r, head c % r of the group), the task takes the R columns
+// from c0 = a5 * R on (a plan with C > R gives each split ceil(C / R) tasks); they share every
+// K/V load, as in task_attn: lane groups of hd / 8 lanes hold a position's row, base-2 online
+// softmax per column. Cached positions (< n) are seen by every column; block position n + j
+// only by the columns of tokens i >= j. The partial (m, l, 2 pad, acc[hd]) of each column goes
+// to its row of the split's record [C][hd + 4].
+template <int MT, int R, int LPP>
+__device__ __forceinline__ bool task_attn_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  constexpr int GPW = 64 / LPP, NP = 2, PER_BLK = NP * GPW;
+  const LayerDesc& L = A.layers[t.layer];
+  const int hd = LPP * 8, r = A.nq / A.nkv, g = t.a0, n = b.n;
+  const int C = MT * r, c0 = t.a5 * R, nc = C - c0 < R ? C - c0 : R;  // this task's columns
+  const int n1 = A.kv_len + MT;  // cache slots per (layer, K/V, head)
+  const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane / LPP, sub = lane - grp * LPP;
+  const int p0 = t.u0, np = t.u1 - t.u0;
+  const int q0 = p0 + wave_start(np, wave), q1 = p0 + wave_start(np, wave + 1);
+  const int qc = q1 < n ? q1 : n;  // cached positions [q0, qc)
+  const uint16_t* Kb = A.kv + (((size_t)t.layer * 2 + 0) * A.nkv + g) * (size_t)n1 * hd;
+  const uint16_t* Vb = A.kv + (((size_t)t.layer * 2 + 1) * A.nkv + g) * (size_t)n1 * hd;
+  const int nblk = (qc > q0) ? (qc - q0 + PER_BLK - 1) / PER_BLK : 0;
+  const rsrc_t kr = make_rsrc(Kb, (uint32_t)((qc > 0 ? qc : 0) * hd * 2)), vr = make_rsrc(Vb, (uint32_t)((qc > 0 ? qc : 0) * hd * 2));
+  const uint32_t lo = (uint32_t)(((q0 + grp) * hd + sub * 8) * 2);
+  u4 ka[NP], va[NP], kb[NP], vb[NP];
+  auto load = [&](int blk, u4(&kk)[NP], u4(&vv)[NP]) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int so = (blk * NP + i) * GPW * hd * 2;
+      kk[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, lo, so, kNT);
+      vv[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, lo, so, kNT);
+    }
+  };
+  load(0, ka, va);
+  load(1, kb, vb);
+  if (!wait_deps(A, b, t)) return false;
+  // the R query vectors, scaled by softmax scale * log2(e), into LDS (xs: the split record is
+  // assembled there only after every wave is done with them); columns past the task's nc repeat
+  // its last one and are never seen
+  float* qs = b.xs;
+  if (threadIdx.x < 64) {
+    for (int j = 0; j < R; ++j) {
+      const int c = c0 + (j < nc ? j : nc - 1), tk = c / r, h = c - tk * r;
+      dma_to_lds(qs + j * hd, b.actp + L.act[LA_Q] + tk * A.nq * hd + (g * r + h) * hd, hd);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * hd; i += kThreads) qs[i] *= A.attn_scale_log2;
+  __syncthreads();
+  float m[R], l[R], acc[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
+  }
+  // fold one block in; `vis` = the last block position (relative to n) column c may see
+  // (columns of token i see block positions up to n + i; cached positions are all visible)
+  auto step = [&](int base, int lo_, int hi_, const u4(&kk)[NP], const u4(&vv)[NP]) {
+    float s[R][NP];
+    int qo = sub * 8;
+    asm volatile("" : "+v"(qo));
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const float* qh = qs + h * hd + qo;
+      const f4 qa = *(const f4*)qh, qb = *(const f4*)(qh + 4);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const u4 kw = kk[i];
+        const float kf[8] = {bf_lo(kw.x), bf_hi(kw.x), bf_lo(kw.y), bf_hi(kw.y), bf_lo(kw.z), bf_hi(kw.z), bf_lo(kw.w), bf_hi(kw.w)};
+        float p = 0.f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) p = fmaf(qv[d], kf[d], p);
+        s[h][i] = p;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int pos = base + i * GPW + grp;
+      const bool valid = pos >= lo_ && pos < hi_;
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        const float p = group_sum<LPP>(s[h][i]);
+        // a block position n + j is visible to the columns of tokens j and later
+        const bool seen = valid && h < nc && (pos < n || pos - n <= (c0 + h) / r);
+        s[h][i] = seen ? p : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float mb = s[h][0];
+#pragma unroll
+      for (int i = 1; i < NP; ++i) mb = fmaxf(mb, s[h][i]);
+      const float mn = fmaxf(m[h], mb);
+      const float mr = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = ex2(m[h] - mr);
+      l[h] *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const float p = ex2(s[h][i] - mr);
+        l[h] += p;
+        const u4 vw = vv[i];
+        acc[h][0] = fmaf(p, bf_lo(vw.x), acc[h][0]);
+        acc[h][1] = fmaf(p, bf_hi(vw.x), acc[h][1]);
+        acc[h][2] = fmaf(p, bf_lo(vw.y), acc[h][2]);
+        acc[h][3] = fmaf(p, bf_hi(vw.y), acc[h][3]);
+        acc[h][4] = fmaf(p, bf_lo(vw.z), acc[h][4]);
+        acc[h][5] = fmaf(p, bf_hi(vw.z), acc[h][5]);
+        acc[h][6] = fmaf(p, bf_lo(vw.w), acc[h][6]);
+        acc[h][7] = fmaf(p, bf_hi(vw.w), acc[h][7]);
+      }
+      m[h] = mn;
+    }
+  };
+  for (int blk = 0; blk < nblk; blk += 2) {
+    step(q0 + blk * PER_BLK, q0, qc, ka, va);
+    load(blk + 2, ka, va);
+    __builtin_amdgcn_sched_barrier(0);
+    step(q0 + (blk + 1) * PER_BLK, q0, qc, kb, vb);
+    load(blk + 3, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the block's own positions in this wave's range, one at a time (agent-coherent loads: other
+  // workgroups wrote them in this step)
+  const rsrc_t kn = make_rsrc(Kb, (uint32_t)(n1 * hd * 2)), vn = make_rsrc(Vb, (uint32_t)(n1 * hd * 2));
+  for (int pj = (q0 > n ? q0 : n); pj < q1; ++pj) {
+    const uint32_t off = (uint32_t)(pj * hd + sub * 8) * 2u;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      ka[i] = __builtin_amdgcn_raw_buffer_load_b128(kn, off, 0, kCoh);
+      va[i] = __builtin_amdgcn_raw_buffer_load_b128(vn, off, 0, kCoh);
+    }
+    step(pj, pj, pj + 1, ka, va);
+  }
+  // merge the wave's lane groups, then the waves, into the split record (as task_attn)
+#pragma unroll 1
+  for (int X = LPP; X < 64; X <<= 1) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      const float om = __shfl_xor(m[h], X, 64), ol = __shfl_xor(l[h], X, 64);
+      const float M = fmaxf(m[h], om);
+      const float ca = (m[h] == -INFINITY) ? 0.f : exp2f(m[h] - M);
+      const float cb = (om == -INFINITY) ? 0.f : exp2f(om - M);
+      l[h] = l[h] * ca + ol * cb;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[h][d] = acc[h][d] * ca + __shfl_xor(acc[h][d], X, 64) * cb;
+      m[h] = M;
+    }
+  }
+  constexpr int ps = LPP * 8 + 4, SS = R * ps;
+  if (grp == 0) {
+    float* gp = b.scr + wave * SS;
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      if (sub == 0) {
+        gp[h * ps] = m[h];
+        gp[h * ps + 1] = l[h];
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) gp[h * ps + 4 + sub * 8 + d] = acc[h][d];
+    }
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int i = threadIdx.x; i < nc * hd; i += kThreads) {
+    const int h = i / hd, d = i - h * hd;
+    float M = -INFINITY;
+#pragma unroll
+    for (int sl = 0; sl < kWaves; ++sl) M = fmaxf(M, b.scr[sl * SS + h * ps]);
+    float v = 0.f, den = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kWaves; ++sl) {
+      const float ms = b.scr[sl * SS + h * ps];
+      const float e = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      v = fmaf(e, b.scr[sl * SS + h * ps + 4 + d], v);
+      den = fmaf(e, b.scr[sl * SS + h * ps + 1], den);
+    }
+    b.xs[h * ps + 4 + d] = v;
+    if (d == 0) *reinterpret_cast<f4*>(b.xs + h * ps) = f4{M, den, 0.f, 0.f};
+  }
+  __syncthreads();
+  const uint32_t gpart = (uint32_t)(t.a4 + (t.a1 * C + c0) * ps);
+  if (threadIdx.x < 64)
+    for (int i = threadIdx.x * 4; i < nc * ps; i += 256) cst4(b.act, (gpart + i) * 4u, *(const f4*)(b.xs + i));
+  return true;
+}
+
+template <int MT>
+__device__ __forceinline__ bool task_attn_v_hd(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  constexpr int R = kMaxVerifyCols;  // query columns per task (held per lane)
+  switch (A.hd) {
+    case 32: return task_attn_v<MT, R, 4>(A, b, t);
+    case 64: return task_attn_v<MT, R, 8>(A, b, t);
+    case 128: return task_attn_v<MT, R, 16>(A, b, t);
+    default: return task_attn_v<MT, R, 32>(A, b, t);
+  }
+}
+
+// Merge of a group's split records for the MT tokens (columns c = token * r + head) into the
+// per-token O-projection inputs xs[token * pw + head * hd + d] (zero-padded to pw), staged like
+// StageMerge; the first task of the group also stores the attention output of every token.
+template <int MT>
+struct StageMergeM {
+  int parts_off, S, r, hd, pw, o_off, o_stride;  // o_off < 0: no store
+  __device__ __forceinline__ int n() const { return S * MT * r * (hd + 4); }
+  __device__ __forceinline__ void before(Blk&) const {}
+  __device__ __forceinline__ void early(Blk& b) const {  // wave 0
+    if (n() <= kEarlyDmaFloats) dma_to_lds(b.scr, b.actp + parts_off, n());
+  }
+  __device__ __forceinline__ void finish(Blk& b) const {
+    const int H = MT * r, ps = hd + 4, nf = n();
+    float* P = b.scr;                      // [S][H][ps]
+    float* w = P + ((nf + 255) & ~255);   // [S][H] merge weights
+    if (nf > kEarlyDmaFloats) dma_to_lds_all(P, b.actp + parts_off, nf);
+    else if (threadIdx.x < 64) __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    for (int i = threadIdx.x; i < MT * pw; i += kThreads)
+      if (i - (i / pw) * pw >= r * hd) b.xs[i] = 0.f;
+    __syncthreads();
+    for (int h = wave_id(); h < H; h += kWaves) {
+      const int lane = threadIdx.x & 63;
+      float M = -INFINITY;
+      for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, P[(sp * H + h) * ps]);
+#pragma unroll
+      for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k, 64));
+      float den = 0.f;
+      for (int sp = lane; sp < S; sp += 64) den += exp2f(P[(sp * H + h) * ps] - M) * P[(sp * H + h) * ps + 1];
+      den = wave_sum(den);
+      const float inv = 1.0f / den;
+      for (int sp = lane; sp < S; sp += 64) w[sp * H + h] = exp2f(P[(sp * H + h) * ps] - M) * inv;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < H * hd; i += kThreads) {
+      const int h = i / hd, d = i - h * hd;
+      float v = 0.f;
+      for (int sp = 0; sp < S; ++sp) v = fmaf(w[sp * H + h], P[(sp * H + h) * ps + 4 + d], v);
+      const int tk = h / r;
+      b.xs[tk * pw + (h - tk * r) * hd + d] = v;
+    }
+    if (threadIdx.x < MT) token_norms(b)[threadIdx.x] = 1.f;
+    __syncthreads();
+    if (o_off >= 0 && threadIdx.x < 64)
+      for (int tk = 0; tk < MT; ++tk)
+        for (int i = threadIdx.x * 4; i < r * hd; i += 256)
+          cst4(b.act, (uint32_t)(o_off + tk * o_stride + i) * 4u, *(const f4*)(b.xs + tk * pw + i));
+  }
+};
+
+template <int MT>
+__device__ __forceinline__ bool task_oproj_g_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int r = A.nq / A.nkv, hd = A.hd, g = t.a0, K = r * hd;
+  const RmCols rm{wp<uint8_t>(A, L.w[LW_WO]), A.nq * hd, t.u0, g * K};
+  return run_gemv_m<MT>(
+      A, b, t, rm, t.u1 - t.u0, K,
+      [&](int, int) {
+        return StageMergeM<MT>{t.a4, t.a2, r, hd, pad512(K), t.u0 == 0 ? L.act[LA_ATTN] + g * K : -1, A.nq * hd};
+      },
+      [&] {
+        for (int e = threadIdx.x; e < (t.u1 - t.u0) * MT; e += 64) {
+          const int i = e / MT, tk = e - i * MT;
+          __hip_atomic_fetch_add(b.actp + L.act[LA_H] + tk * A.hidden + t.u0 + i, b.ys[e], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+      });
+}
+
+// Layer 0: h[token] = x[token] (widened), the accumulators the per-group O-projections add into.
+template <int MT>
+__device__ __forceinline__ bool task_hinit_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  for (int tk = 0; tk < MT; ++tk)
+    for (int i = threadIdx.x; i < t.u1 - t.u0; i += kThreads)
+      cst(b.act, (uint32_t)(t.a0 + tk * A.hidden + t.u0 + i) * 4u, bf16f(b.x[(size_t)tk * A.hidden + t.u0 + i]));
+  return true;
+}
+
+template <int MT>
+__device__ __forceinline__ bool task_gateup_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.hidden;
+  const RmGateUp rm{wp<uint8_t>(A, L.w[LW_GATE]), wp<uint8_t>(A, L.w[LW_UP]), K, t.u0};
+  return run_gemv_m<MT>(
+      A, b, t, rm, 2 * (t.u1 - t.u0), K,
+      [&](int ca, int) {
+        return StageM<MT>{L.act[LA_H], K, nullptr, K, ca * kChunkCols, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps, true};
+      },
+      [&] {
+        for (int e = threadIdx.x; e < (t.u1 - t.u0) * MT; e += 64) {
+          const int i = e / MT, tk = e - i * MT;
+          const float nv = token_norm<MT>(b, tk);
+          const float gv = b.ys[(2 * i) * MT + tk] * nv, uv = b.ys[(2 * i + 1) * MT + tk] * nv;
+          cst(b.act, (uint32_t)(L.act[LA_ACT] + tk * A.ffn + t.u0 + i) * 4u, silu(gv) * uv);
+        }
+      });
+}
+
+template <int MT>
+__device__ __forceinline__ bool task_down_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.ffn;
+  const RmPlain rm{wp<uint8_t>(A, L.w[LW_DOWN]), K, t.u0};
+  return run_gemv_m<MT>(
+      A, b, t, rm, t.u1 - t.u0, K,
+      [&](int ca, int cb) {
+        const int k0 = ca * kChunkCols, k1 = cb * kChunkCols < K ? cb * kChunkCols : K;
+        return StageM<MT>{L.act[LA_ACT], K, nullptr, K, k0, k1 - k0, (cb - ca) * kChunkCols, nullptr, 0.f, false};
+      },
+      [&] {
+        for (int e = threadIdx.x; e < (t.u1 - t.u0) * MT; e += 64) {
+          const int i = e / MT, tk = e - i * MT, rr = t.u0 + i, d = A.hidden;
+          const float y = b.ys[e];
+          const float xo = cld_coh(b.act, (uint32_t)(L.act[LA_H] + tk * d + rr) * 4u) + y;
+          cst(b.act, (uint32_t)(L.act[LA_FFN_OUT] + tk * d + rr) * 4u, y);
+          if (t.a1 >= 0) cst(b.act, (uint32_t)(t.a1 + tk * d + rr) * 4u, xo);  // next layer's h starts at x
+          cst(b.act, (uint32_t)(L.act[LA_X_OUT] + tk * d + rr) * 4u, xo);
+          if (t.a0) A.out[(size_t)tk * d + rr] = xo;
+        }
+      });
+}
+
+template <int MT>
+__device__ __forceinline__ bool task_lmhead_v(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const int K = A.hidden;
+  const RmPlain rm{wp<uint8_t>(A, A.w_lm_head), K, t.u0};
+  return run_gemv_m<MT>(
+      A, b, t, rm, t.u1 - t.u0, K,
+      [&](int ca, int) {
+        return StageM<MT>{A.x_final, K, nullptr, K, ca * kChunkCols, K, pad512(K), wp<uint16_t>(A, A.w_final_norm), A.eps, false};
+      },
+      [&] {
+        for (int e = threadIdx.x; e < (t.u1 - t.u0) * MT; e += 64) {
+          const int i = e / MT, tk = e - i * MT;
+          A.out[(size_t)tk * A.vocab + t.u0 + i] = b.ys[e] * token_norm<MT>(b, tk);
+        }
+      });
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ the engine
@@ -2311,7 +2949,7 @@ __device__ __forceinline__ const EngineArgs& args_view() {
   return *(const EngineArgs*)p;
 }
 
-template <bool MLA, int RUN, int ES = 2>
+template <bool MLA, int RUN, int ES = 2, int MT = 1>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -2374,7 +3012,19 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
     const uint32_t t0 = (kTaskLog && threadIdx.x < 64) ? (uint32_t)now() : 0u;
     bool ok = true, gemv = true;
     int sig = t.signal;
-    if constexpr (!MLA) {
+    if constexpr (!MLA && MT > 1) {
+      // a verification step of MT tokens (GQA, bf16, whole steps)
+      switch (t.type) {
+        case T_QKV: ok = task_qkv_v<MT>(A, b, t); break;
+        case T_ATTN: gemv = false; ok = task_attn_v_hd<MT>(A, b, t); break;
+        case T_OPROJ_G: ok = task_oproj_g_v<MT>(A, b, t); break;
+        case T_HINIT: gemv = false; ok = task_hinit_v<MT>(A, b, t); break;
+        case T_GATEUP: ok = task_gateup_v<MT>(A, b, t); break;
+        case T_DOWN: ok = task_down_v<MT>(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead_v<MT>(A, b, t); break;
+        default: ok = false; break;
+      }
+    } else if constexpr (!MLA) {
       switch (t.type) {
         // K/V rows pass from a QKV task to the attention split after it through LDS only when
         // one launch runs both (a launch of all stages)
@@ -2486,12 +3136,24 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(Engi
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8_dyn(EngineArgs A) {
   engine_body<false, kRunDynamic, 1>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_v2(EngineArgs A) {
+  engine_body<false, kRunStep, 2, 2>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_v3(EngineArgs A) {
+  engine_body<false, kRunStep, 2, 3>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_v4(EngineArgs A) {
+  engine_body<false, kRunStep, 2, 4>(A);
+}
 
 }  // namespace dec
 
 // Host-side launch (used by the C ABI in api.cpp). run: 0 a whole step, 1 a range of stages,
-// 2 a whole step of a plan with a per-step length.
-static const void* engine_fn(int arch, int run, int wfmt = 0) {
+// 2 a whole step of a plan with a per-step length; ntok > 1: a verification step (run 0).
+static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1) {
+  if (ntok == 2) return (const void*)dec::dec_engine_gqa_v2;
+  if (ntok == 3) return (const void*)dec::dec_engine_gqa_v3;
+  if (ntok == 4) return (const void*)dec::dec_engine_gqa_v4;
   if (wfmt) return run == 2 ? (const void*)dec::dec_engine_gqa_f8_dyn : (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
   if (run == 2) return arch == 0 ? (const void*)dec::dec_engine_gqa_dyn : (const void*)dec::dec_engine_mla_dyn;
@@ -2500,11 +3162,12 @@ static const void* engine_fn(int arch, int run, int wfmt = 0) {
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
                                                                          int run, bool cooperative, hipStream_t stream) {
-  static int configured_lds[2][5] = {{-1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1}};
+  static int configured_lds[2][8] = {{-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
   if (run < 0 || run > 2 || (args->wfmt && (k != 0 || run == 1))) return hipErrorInvalidValue;
-  const void* fn = engine_fn(args->arch, run, args->wfmt);
-  const int slot = args->wfmt ? 3 + (run == 2) : run;
+  if (args->ntok > 1 && (k != 0 || run != 0 || args->wfmt || args->ntok > dec::kMaxVerifyTokens)) return hipErrorInvalidValue;
+  const void* fn = engine_fn(args->arch, run, args->wfmt, args->ntok);
+  const int slot = args->ntok > 1 ? 3 + args->ntok : args->wfmt ? 3 + (run == 2) : run;
   if (configured_lds[k][slot] < lds_bytes) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
@@ -2516,10 +3179,12 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
   return hipLaunchCooperativeKernel(fn, dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int wfmt, int lds_bytes, int* blocks_per_cu) {
-  hipError_t e = hipFuncSetAttribute(engine_fn(arch, 0, wfmt), hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int lds_bytes,
+                                                                               int* blocks_per_cu) {
+  const void* fn = engine_fn(arch, 0, wfmt, ntok);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, engine_fn(arch, 0, wfmt), dec::kThreads, (size_t)lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, dec::kThreads, (size_t)lds_bytes);
 }
 
 // ------------------------------------------------------------------ stream-read ceiling

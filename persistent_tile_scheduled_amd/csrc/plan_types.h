@@ -16,6 +16,8 @@ constexpr int kMaxDepsPerTask = 64;    // one poller lane per dependency counter
 constexpr int kYsFloats = 1024;        // per-task GEMV row results staged in LDS
 constexpr int kMaxTaskRows = 1024;     // rows of one GEMV task (row-pointer table in LDS)
 constexpr int kLdsMin = 96 * 1024;     // > half a CU's LDS: forces one workgroup per CU
+constexpr int kMaxVerifyTokens = 4;    // tokens of one verification step
+constexpr int kMaxVerifyCols = 8;      // query columns (tokens x heads of a KV group) of its attention
 // Latent (MLA) attention on the matrix cores: all query heads (at most 16) are the 16 columns
 // of one bf16 MFMA 16x16x32 tile, positions its rows, the latent dimension its contraction.
 constexpr int kMlaHeads = 16;          // query heads folded into one MFMA tile
@@ -175,6 +177,7 @@ struct EngineArgs {
   uint32_t act_bytes;          // size of the activation region
   int32_t gs_floats;           // LDS floats reserved for norm gains
   float eps, attn_scale_log2;  // softmax scale * log2(e)
+  int32_t ntok;                // tokens per step (1: decode; 2..4: a verification step)
 };
 
 }  // namespace dec

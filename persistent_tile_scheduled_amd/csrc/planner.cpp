@@ -49,6 +49,7 @@ struct Builder {
   const dec_model_shape& s;
   int64_t n;  // kv_len (dynamic plans: the largest position a step may have)
   bool dyn;
+  int nt;     // tokens per step (> 1: a verification step)
   const dec_device_info& dev;
   PlanData& P;
   std::string& err;
@@ -63,8 +64,16 @@ struct Builder {
   int64_t scratch_floats = 1024;
   int64_t mla_lds = 0;        // LDS floats (after the header) the latent-attention tasks use
 
-  Builder(const dec_model_shape& s_, int64_t n_, bool dyn_, const dec_device_info& d_, PlanData& p_, std::string& e_)
-      : s(s_), n(n_), dyn(dyn_), dev(d_), P(p_), err(e_) {}
+  Builder(const dec_model_shape& s_, int64_t n_, bool dyn_, int nt_, const dec_device_info& d_, PlanData& p_, std::string& e_)
+      : s(s_), n(n_), dyn(dyn_), nt(nt_), dev(d_), P(p_), err(e_) {}
+
+  // A verification step keeps every activation per token ([nt][width]); its GEMV tasks hold
+  // nt results per row, so they take at most kRowsCap / nt rows.
+  int rows_cap() const { return kRowsCap / nt; }
+  int64_t act_t(const std::string& name, int64_t count) { return act(name, count * nt); }
+  // a verification GEMV stages the input of all nt tokens at once (RMSNormed inputs, merged
+  // attention), or at least one chunk per token (column phases)
+  void need_xs_t(int64_t K, bool whole) { xs_floats_max = std::max<int64_t>(xs_floats_max, nt * (whole ? align_up(K, kChunkCols) : kChunkCols)); }
 
   int xcd(int w) const { return w % n_xcd; }
   // Completion counters of a stage: nsc of them, workgroup w signalling counter w % nsc (so a
@@ -180,6 +189,9 @@ struct Builder {
     if (!(q.rms_eps > 0.f) || !(q.rope_theta > 1.0)) return fail(DEC_E_SHAPE, "need rms_eps > 0 and rope_theta > 1", st);
     if (n < 0) return fail(DEC_E_CAPACITY, "kv_len < 0", st);
     if (n > (1 << 22)) return fail(DEC_E_CAPACITY, "kv_len above 4194304", st);
+    if (nt < 1 || nt > kMaxVerifyTokens) return fail(DEC_E_INVAL, "tokens per step must be 1.." + std::to_string(kMaxVerifyTokens), st);
+    if (nt > 1 && (q.arch != DEC_ARCH_GQA || q.weight_format != DEC_WEIGHTS_BF16 || dyn))
+      return fail(DEC_E_SHAPE, "verification steps: GQA family, bf16 weights, fixed length only", st);
     if (q.arch == DEC_ARCH_GQA) {
       if (q.n_q_heads < 1 || q.n_kv_heads < 1 || q.n_q_heads % q.n_kv_heads)
         return fail(DEC_E_SHAPE, "GQA needs n_q_heads a positive multiple of n_kv_heads", st);
@@ -354,14 +366,21 @@ struct Builder {
     std::string p = "layers." + std::to_string(l) + ".";
     for (int i = 0; i < LA_COUNT; ++i) L.act[i] = -1;
     L.act[LA_X_IN] = (int)x_in;
-    L.act[LA_Q] = (int)act(p + "q", (int64_t)nq * hd);
-    L.act[LA_KVNEW] = (int)act(p + "kv_new", 2LL * nkv * hd);
-    L.act[LA_ATTN] = (int)act(p + "attn", (int64_t)nq * hd);
+    L.act[LA_Q] = (int)act_t(p + "q", (int64_t)nq * hd);
+    L.act[LA_KVNEW] = (int)act_t(p + "kv_new", 2LL * nkv * hd);
+    L.act[LA_ATTN] = (int)act_t(p + "attn", (int64_t)nq * hd);
     L.act[LA_H] = (int)h_acc[l];
-    L.act[LA_ACT] = (int)act(p + "ffn_act", f);
-    L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
-    L.act[LA_X_OUT] = (int)act(p + "x_out", d);
-    need_xs(d); need_xs((int64_t)nq * hd); need_xs(f);
+    L.act[LA_ACT] = (int)act_t(p + "ffn_act", f);
+    L.act[LA_FFN_OUT] = (int)act_t(p + "ffn_out", d);
+    L.act[LA_X_OUT] = (int)act_t(p + "x_out", d);
+    if (nt == 1) {
+      need_xs(d); need_xs((int64_t)nq * hd); need_xs(f);
+    } else {
+      need_xs_t(d, true); need_xs_t((int64_t)r * hd, true); need_xs_t(f, false);
+      // the attention stages its query columns in xs (each copy lands in 256-float blocks)
+      // and assembles its split record there
+      xs_floats_max = std::max<int64_t>(xs_floats_max, align_up((int64_t)kMaxVerifyCols * (hd + 4) + 256, 256));
+    }
     auto sets = xcd_sets(nkv);
 
     // QKV: per KV group g, units = (r q heads + k + v) * hd/2 RoPE row pairs.
@@ -369,31 +388,39 @@ struct Builder {
     const int qkv = counter(nkv);
     const int U = (r + 2) * hd / 2;
     for (int g = 0; g < nkv; ++g)
-      spread(sets[g], U, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_QKV, l, a, b, prev, qkv + g, -1, g); });
+      spread(sets[g], U, rows_cap() / 2, [&](int w, int a, int b) { add(w, T_QKV, l, a, b, prev, qkv + g, -1, g); });
 
-    // attention splits (one per workgroup of the group's set)
+    // attention splits over the n + nt positions: one per workgroup of the group's set, or,
+    // in a verification step whose group has more than kMaxVerifyCols query columns (nt * r),
+    // one task per (split, block of kMaxVerifyCols columns) on consecutive workgroups of the
+    // set (one XCD: the column blocks of a split read the same K/V rows)
     ++stage;
     const int att = counter(nkv);
+    const int C = nt * r;                                          // query columns per group
+    const int CG = nt > 1 ? (C + kMaxVerifyCols - 1) / kMaxVerifyCols : 1;  // column blocks
+    const int64_t npos = n + nt;
     int smax = 1;
     std::vector<int> S(nkv);
     for (int g = 0; g < nkv; ++g) {
       // the O-projection merges a group's partials from one LDS burst: cap the split count
-      const int64_t cap = std::max<int64_t>(1, kMergeFloats / ((int64_t)r * (hd + 4)));
-      S[g] = (int)std::min<int64_t>({(int64_t)sets[g].size(), cap,
-                                     std::max<int64_t>(1, (n + 1 + kMinPosPerSplit - 1) / kMinPosPerSplit)});
+      const int64_t cap = std::max<int64_t>(1, kMergeFloats / ((int64_t)C * (hd + 4)));
+      S[g] = (int)std::min<int64_t>({std::max<int64_t>(1, (int64_t)sets[g].size() / CG), cap,
+                                     std::max<int64_t>(1, (npos + kMinPosPerSplit - 1) / kMinPosPerSplit)});
       smax = std::max(smax, S[g]);
     }
-    const int64_t pstride = (int64_t)r * (hd + 4);  // per split: r x (m, l, pad, pad, acc[hd])
+    const int64_t pstride = (int64_t)C * (hd + 4);  // per split: C x (m, l, pad, pad, acc[hd])
     const int64_t part = act(p + "attn_partials", (int64_t)nkv * smax * pstride);
     L.act[LA_PART] = (int)part;
-    // attention task: one partial per wave, per-wave stride sized for up to 4 heads
-    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * 4 * (hd + 4) + 64);
-    scratch_floats = std::max<int64_t>(scratch_floats, align_up((int64_t)smax * pstride, 256) + (int64_t)smax * r + 64);
+    // attention task: one partial per wave, per-wave stride sized for up to 4 heads (a
+    // verification step's: kMaxVerifyCols columns)
+    scratch_floats = std::max<int64_t>(scratch_floats, (int64_t)kWaves * (nt > 1 ? kMaxVerifyCols : 4) * (hd + 4) + 64);
+    scratch_floats = std::max<int64_t>(scratch_floats, align_up((int64_t)smax * pstride, 256) + (int64_t)smax * C + 64);
     for (int g = 0; g < nkv; ++g)
       for (int sp = 0; sp < S[g]; ++sp) {
-        int p0 = (int)((n + 1) * sp / S[g]), p1 = (int)((n + 1) * (sp + 1) / S[g]);
-        add(sets[g][sp], T_ATTN, l, p0, p1, {qkv + g}, att + g, -1, g, sp, S[g], 0,
-            (int)(part + (int64_t)g * smax * pstride));
+        int p0 = (int)(npos * sp / S[g]), p1 = (int)(npos * (sp + 1) / S[g]);
+        for (int cg = 0; cg < CG; ++cg)
+          add(sets[g][(sp * CG + cg) % sets[g].size()], T_ATTN, l, p0, p1, {qkv + g}, att + g, -1, g, sp, S[g], 0,
+              (int)(part + (int64_t)g * smax * pstride), cg);
       }
 
     // per group: merge the group's splits, then W_o rows x the group's r*hd columns (split-K
@@ -404,7 +431,7 @@ struct Builder {
     for (int g = 0; g < nkv; ++g) {
       std::vector<int32_t> dg = {att + g};
       dg.insert(dg.end(), hinit_deps.begin(), hinit_deps.end());
-      spread(sets[g], d, kRowsCap, [&](int w, int a, int b) {
+      spread(sets[g], d, rows_cap(), [&](int w, int a, int b) {
         add(w, T_OPROJ_G, l, a, b, dg, ctr_o + slot(w), -1, g, 0, S[g], 0, (int)(part + (int64_t)g * smax * pstride));
       });
     }
@@ -415,12 +442,12 @@ struct Builder {
     const int d = s.hidden, f = s.ffn;
     ++stage;
     const int ctr_gu = counter(nsc);
-    spread_weighted(all_wgs(), f, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_GATEUP, l, a, b, deps_h, ctr_gu + slot(w)); });
+    spread_weighted(all_wgs(), f, rows_cap() / 2, [&](int w, int a, int b) { add(w, T_GATEUP, l, a, b, deps_h, ctr_gu + slot(w)); });
     ++stage;
     const int ctr_dn = counter(nsc);
     const int last = (l == s.n_layers - 1 && s.vocab == 0) ? 1 : 0;
     const int hnext = (s.arch == DEC_ARCH_GQA && l + 1 < s.n_layers) ? (int)h_acc[l + 1] : -1;
-    spread(all_wgs(), d, kRowsCap, [&](int w, int a, int b) {
+    spread(all_wgs(), d, rows_cap(), [&](int w, int a, int b) {
       add(w, T_DOWN, l, a, b, all_of(ctr_gu, nsc), ctr_dn + slot(w), -1, last, hnext);
     });
     return all_of(ctr_dn, nsc);
@@ -572,6 +599,7 @@ struct Builder {
     P.shape = s;
     P.kv_len = n;
     P.dynamic = dyn;
+    P.ntok = nt;
     P.dev = dev;
     P.n_wg = n_wg;
     P.layers.assign(s.n_layers, LayerDesc{});
@@ -582,7 +610,7 @@ struct Builder {
     if (s.arch == DEC_ARCH_GQA) {
       // h accumulators: allocated up front so each layer's down tasks can initialise the next
       for (int l = 0; l < s.n_layers; ++l) P.layers[l].act[LA_H] = -1;
-      for (int l = 0; l < s.n_layers; ++l) h_acc.push_back(act("layers." + std::to_string(l) + ".h", s.hidden));
+      for (int l = 0; l < s.n_layers; ++l) h_acc.push_back(act_t("layers." + std::to_string(l) + ".h", s.hidden));
       ++stage;
       const int ci = counter(nsc);
       spread(all_wgs(), s.hidden, kRowsCap, [&](int w, int a, int b) { add(w, T_HINIT, 0, a, b, {}, ci + slot(w), -1, (int)h_acc[0]); });
@@ -596,7 +624,7 @@ struct Builder {
     if (s.vocab > 0) {
       ++stage;
       if (!dyn) {
-        spread_weighted(all_wgs(), s.vocab, kRowsCap, [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
+        spread_weighted(all_wgs(), s.vocab, rows_cap(), [&](int w, int a, int b) { add(w, T_LMHEAD, s.n_layers, a, b, prev, -1); });
       } else {
         // each LM-head task also leaves its best (logit, index) in slot a0; one task then
         // picks the step's token from those pairs
@@ -613,7 +641,7 @@ struct Builder {
       }
     }
 
-    if (s.arch == DEC_ARCH_GQA) stage_attention_kv();
+    if (s.arch == DEC_ARCH_GQA && nt == 1) stage_attention_kv();
 
     // flatten per-workgroup lists, resolve dependency entries
     P.wg_begin.assign(n_wg + 1, 0);
@@ -651,14 +679,14 @@ struct Builder {
       }
     }
 
-    // RoPE table in double precision: the row of the step's position, or (dynamic) one row
-    // per position 0..max_len
+    // RoPE table in double precision: the row of the step's position (a verification step: of
+    // each of its positions n .. n + nt - 1), or (dynamic) one row per position 0..max_len
     const int rope_dim = (s.arch == DEC_ARCH_GQA) ? s.head_dim : s.qk_rope;
     P.rope_half = rope_dim / 2;
-    P.rope_rows = dyn ? (int32_t)(n + 1) : 1;
+    P.rope_rows = dyn ? (int32_t)(n + 1) : nt;
     P.rope_cs.assign((size_t)P.rope_rows * 2 * P.rope_half, 0.f);
     for (int64_t row = 0; row < P.rope_rows; ++row) {
-      const int64_t pos = dyn ? row : n;
+      const int64_t pos = dyn ? row : n + row;
       float* cs = P.rope_cs.data() + (size_t)row * 2 * P.rope_half;
       for (int i = 0; i < P.rope_half; ++i) {
         long double ang = (long double)pos * powl((long double)s.rope_theta, -2.0L * i / rope_dim);
@@ -708,7 +736,7 @@ struct Builder {
     P.buffers.push_back({"control", DEC_DTYPE_I32, P.off_ctl, CTL_WORDS});
 
     // bytes the method must read per step: every dense weight once (routed experts: only
-    // the top_k chosen), and positions [0, kv_len] of the cache once
+    // the top_k chosen), and positions [0, kv_len + ntok) of the cache once
     P.weight_bytes = 0;
     for (auto& w : P.weights) P.weight_bytes += w.bytes;
     int64_t alg = P.weight_bytes;
@@ -717,7 +745,7 @@ struct Builder {
       alg -= (int64_t)s.n_layers * (s.n_routed - s.top_k) * per_expert;
     }
     int64_t kv_row = (s.arch == DEC_ARCH_GQA) ? 2LL * s.n_kv_heads * s.head_dim * 2 : (int64_t)(s.kv_lora_rank + s.qk_rope) * 2;
-    alg += (int64_t)s.n_layers * (n + 1) * kv_row;
+    alg += (int64_t)s.n_layers * (n + nt) * kv_row;
     P.alg_bytes = alg;
 
     std::string v = validate_plan(P);
@@ -729,10 +757,10 @@ struct Builder {
 }  // namespace
 
 dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev, PlanData* out,
-                      std::string* err, bool dynamic) {
+                      std::string* err, bool dynamic, int ntok) {
   *out = PlanData{};
   dec_status st = DEC_OK;
-  Builder b(shape, kv_len, dynamic, dev, *out, *err);
+  Builder b(shape, kv_len, dynamic, ntok, dev, *out, *err);
   if (!b.run(&st)) return st;
   return DEC_OK;
 }
@@ -792,11 +820,12 @@ std::string validate_plan(const PlanData& p) {
   std::map<Key, std::vector<std::pair<int, int>>> ranges;
   for (int i = 0; i < nt; ++i) {
     const TaskDesc& t = p.tasks[i];
-    int grp = (t.type == T_QKV || t.type == T_ATTN || t.type == T_OPROJ_G) ? t.a0 : 0;
+    // (attention of a verification step: each column block tiles the positions once)
+    int grp = (t.type == T_QKV || t.type == T_OPROJ_G) ? t.a0 : t.type == T_ATTN ? t.a0 * 64 + t.a5 : 0;
     ranges[{t.layer, t.type, grp}].push_back({t.u0, t.u1});
   }
   const dec_model_shape& s = p.shape;
-  const int64_t n1 = p.kv_len + 1;
+  const int64_t n1 = p.kv_len + p.ntok;
   auto expected = [&](int type) -> int64_t {
     switch (type) {
       case T_QKV: return (int64_t)(s.n_q_heads / s.n_kv_heads + 2) * s.head_dim / 2;

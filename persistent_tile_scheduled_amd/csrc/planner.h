@@ -53,6 +53,7 @@ struct PlanData {
   int32_t rope_half = 0;
   int32_t rope_rows = 1;              // rows of the RoPE table (positions 0..max_len when dynamic)
   bool dynamic = false;               // the step's position is read from device memory
+  int32_t ntok = 1;                   // tokens per step (> 1: a verification step of that many)
   int32_t w_final_norm = -1, w_lm_head = -1, x_final = -1, w_embed = -1;
   float attn_scale_log2 = 0.f;
 
@@ -67,8 +68,10 @@ struct PlanData {
 // Validate the shape and build the plan. Returns DEC_OK or an error (message in *err).
 // dynamic: kv_len is the largest position a step may have (max_len); each step reads its
 // position (and, without an input vector, its token) from device memory.
+// ntok > 1: a verification step of ntok tokens at positions kv_len .. kv_len + ntok - 1 (GQA,
+// bf16 weights, fixed length only).
 dec_status build_plan(const dec_model_shape& shape, int64_t kv_len, const dec_device_info& dev,
-                      PlanData* out, std::string* err, bool dynamic = false);
+                      PlanData* out, std::string* err, bool dynamic = false, int ntok = 1);
 
 // Positions [p0, p1) of attention split sp of S over the positions 0..n (n + 1 of them).
 inline int split_begin(int64_t n, int sp, int S) { return (int)((n + 1) * sp / S); }

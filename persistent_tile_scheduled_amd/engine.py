@@ -18,9 +18,10 @@ class DecodeEngine:
                  stream=None, watchdog_us: Optional[int] = None, max_len: Optional[int] = None,
                  static_workspace: bool = False):
         """A plan for kv_len (default: the config's), or, with max_len, a plan whose position
-        is read per step from a device state (step_dynamic). static_workspace: bind to the
-        library's static per-device workspace (dec_plan_bind_scratch) instead of allocating
-        one; the named intermediate buffers are then not readable through buffer()."""
+        is read per step from a device state (step_dynamic). A config with "verify": M plans a
+        verification step of M tokens (x [M][hidden], out [M][vocab]). static_workspace: bind
+        to the library's static per-device workspace (dec_plan_bind_scratch) instead of
+        allocating one; the named intermediate buffers are then not readable through buffer()."""
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("DecodeEngine needs a GPU (gfx950); there is no CPU path")
@@ -51,8 +52,11 @@ class DecodeEngine:
             self.workspace = torch.empty(self.sizes["workspace_bytes"], dtype=torch.uint8, device="cuda")
             self.plan.bind(ptrs, self.workspace.data_ptr(), self.workspace.numel(), self.stream.cuda_stream)
         self.buffers = self.plan.buffers()
+        self.n_tokens = self.plan.n_tokens
         out_n = cfg["vocab"] if cfg.get("vocab", 0) > 0 else cfg["hidden"]
         self.out = torch.empty(out_n, dtype=torch.float32, device="cuda")
+        if self.n_tokens > 1:
+            self.out = torch.empty(self.n_tokens, out_n, dtype=torch.float32, device="cuda")
         # {position, token, steps, 0}: read and advanced by every dynamic step
         self.state = torch.zeros(4, dtype=torch.int32, device="cuda") if self.dynamic else None
 
@@ -74,8 +78,11 @@ class DecodeEngine:
         out = self.out if out is None else out
         if x is not None:
             self._check_io(x, kv, out)
-        elif kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
-            raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+        else:
+            if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
+                raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+            if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"] or not out.is_contiguous() or not out.is_cuda:
+                raise ValueError("out must be contiguous cuda fp32 of length vocab (or hidden)")
         self.plan.step_dynamic(0 if x is None else x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.state.data_ptr(),
                                self.stream.cuda_stream)
         return out
@@ -83,14 +90,15 @@ class DecodeEngine:
     def _check_io(self, x, kv, out):
         torch = self.torch
         if x.dtype != torch.bfloat16 or x.numel() * 2 != self.sizes["x_bytes"] or not x.is_contiguous():
-            raise ValueError("x must be a contiguous bf16 vector of length hidden")
+            raise ValueError("x must be contiguous bf16 [tokens per step][hidden]")
         if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
             raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
-        if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"]:
-            raise ValueError("out must be fp32 of length vocab (or hidden)")
+        if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"] or not out.is_contiguous() or not out.is_cuda:
+            raise ValueError("out must be contiguous cuda fp32 [tokens per step][vocab (or hidden)]")
 
     def step(self, x, kv, out=None):
-        """One decode step: x bf16 [hidden], kv bf16 cache (written at slot kv_len)."""
+        """One decode step: x bf16 [hidden], kv bf16 cache (written at slot kv_len); a
+        verification plan: x [M][hidden], slots kv_len .. kv_len + M - 1, out [M][vocab]."""
         out = self.out if out is None else out
         self._check_io(x, kv, out)
         self.plan.step(x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.stream.cuda_stream)
