@@ -5,7 +5,8 @@
 A step is one whole decode step (all layers, one kernel launch) over synthetic bf16
 weights and KV cache already resident in HBM. Prints ONE JSON line. --launch stages|graph
 times the same step split into one launch per stage (eagerly, or replayed from a HIP graph),
-the launch-per-operator execution the persistent engine replaces.
+the launch-per-operator execution the persistent engine replaces. --verify M times a
+verification step of M tokens (one launch; value = microseconds per token, the step's time / M).
 """
 import argparse
 import json
@@ -277,6 +278,9 @@ def main():
                          "(positions kv_len - T .. kv_len - 1, each step's token from the last)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--verify", type=int, default=1, metavar="M",
+                    help="time a verification step of M tokens (2..4, GQA bf16 workloads) instead of a "
+                         "one-token decode step; no CPU baseline")
     ap.add_argument("--stream-read", action="store_true",
                     help="only measure the HBM stream-read rate of the engine's loads (dec_stream_read) "
                          "over 256 MiB, 1 GiB and 4 GiB buffers")
@@ -298,8 +302,17 @@ def main():
     import workloads
     from persistent_tile_scheduled_amd.engine import DecodeEngine
 
-    cfg = workloads.get_config(args.config)
-    print(f"[bench] generating {args.config} inputs on cuda:0", file=sys.stderr, flush=True)
+    cfg = dict(workloads.get_config(args.config))
+    m = args.verify
+    name = args.config
+    if m > 1:
+        if args.launch != "persistent" or args.generate:
+            print("--verify times whole persistent steps only", file=sys.stderr)
+            sys.exit(2)
+        cfg["verify"] = m
+        name = f"{args.config}_verify{m}"
+        args.no_cpu_baseline = True
+    print(f"[bench] generating {name} inputs on cuda:0", file=sys.stderr, flush=True)
     w, x, kv = workloads.generate(cfg, seed=args.seed, device="cuda")
     if args.generate:
         generation(args, cfg, w, kv, x)
@@ -336,7 +349,8 @@ def main():
     per = [a.elapsed_time(b) * 1e3 for a, b in ev]  # us per launch
     mean_us = statistics.mean(per)
     med_us = statistics.median(per)
-    us_per_token = wall * 1e6 / args.steps
+    us_per_step = wall * 1e6 / args.steps
+    us_per_token = us_per_step / m
     achieved = alg_bytes / (mean_us * 1e-6) / 1e9
 
     cpu = None
@@ -351,25 +365,27 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(us_per_token / 1e3, 4),
+        "ms_per_step": round(us_per_step / 1e3, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8" if cfg.get("weights") == "fp8" else "bf16",
         "data": "synthetic (seeded N(0,0.02) " + ("weights quantised per row to FP8 E4M3" if cfg.get("weights") == "fp8"
                                                   else "bf16 weights") + ", N(0,1) bf16 KV and input)",
-        "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
-                   "kv_len": cfg["kv_len"], "batch": 1},
+        "config": {"workload": f"{name}: {WORKLOADS.get(args.config, args.config)}" +
+                   (f"; a verification step of {m} tokens at positions kv_len .. kv_len + {m - 1}" if m > 1 else ""),
+                   "kv_len": cfg["kv_len"], "batch": 1, "tokens_per_step": m},
         "launch": args.launch if args.launch == "persistent" else
         f"{args.launch}: {eng.n_stages} launches per step",
         "tokens_per_s": round(1e6 / us_per_token, 1),
+        "us_per_step": round(us_per_step, 2),
         "kernel_us_mean": round(mean_us, 2),
         "kernel_us_median": round(med_us, 2),
         "kernel_us_p10": round(sorted(per)[len(per) // 10], 2),
         "kernel_us_p90": round(sorted(per)[(len(per) * 9) // 10], 2),
         "algorithmic_bytes_per_step": alg_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.config)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(name)},
         "source_hash": source_hash(),
         "cpu_baseline": cpu,
     }
