@@ -9,5 +9,6 @@ from .decode_oracle import (  # noqa: F401
     widen_bf16, decode_e4m3, round_to_bf16, rmsnorm, rope, linear, linear_bits, softmax, attend,
     attend_partial, merge_partials, attend_split, silu, swiglu, route, gqa_layer,
     mla_attention, mla_attention_absorbed, moe_ffn, mla_layer, layer, head, forward,
-    dict_weights, kv_group, gqa_verify_layer, verify_forward,
+    dict_weights, kv_group, gqa_verify_layer, verify_forward, decode_e2m1, decode_e8m0, dequant_mxfp4,
+    MX_BLOCK,
 )

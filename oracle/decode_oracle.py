@@ -97,6 +97,41 @@ def round_to_bf16(x) -> Tuple[np.ndarray, np.ndarray]:
     return v, bits
 
 
+def decode_e2m1(codes) -> np.ndarray:
+    """FP4 E2M1 nibble (its low 4 bits) -> float64, exactly: bit 3 the sign, bits 2..1 an
+    exponent with bias 1, bit 0 the mantissa; exponent 0 encodes the subnormals 0 and 0.5 (so
+    m * 2^-1), otherwise (1 + m/2) * 2^(e-1). No infinities or NaN; the largest magnitude is 6.
+    (The element format of the OCP Microscaling (MX) FP4 type; the pages name FP4 expert weights
+    without fixing a format.)"""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int64)))
+    return sign * mag
+
+
+def decode_e8m0(bits) -> np.ndarray:
+    """E8M0 scale byte -> 2^(s - 127) (the MX shared block scale: an exponent only); s = 255
+    is NaN."""
+    b = np.asarray(bits).astype(np.int64)
+    return np.where(b == 0xFF, np.nan, np.ldexp(1.0, (b - 127).astype(np.int64)))
+
+
+MX_BLOCK = 32  # elements sharing one E8M0 scale
+
+
+def dequant_mxfp4(packed, scales) -> np.ndarray:
+    """MXFP4 rows -> float64. packed: uint8 [..., K/2], byte i holding element 2i in its low
+    nibble and element 2i+1 in its high nibble; scales: uint8 [..., K/32]. Element k is
+    E2M1(k) * E8M0(scales[k // 32])."""
+    p = np.asarray(packed).astype(np.int64)
+    codes = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[:-1] + (2 * p.shape[-1],))
+    vals = decode_e2m1(codes)
+    sc = decode_e8m0(np.asarray(scales))
+    return vals * np.repeat(sc, MX_BLOCK, axis=-1)
+
+
 def _w64(W: Callable, name: str, index=None) -> np.ndarray:
     a = W(name) if index is None else W(name, index)
     a = np.asarray(a)
@@ -446,8 +481,18 @@ def mla_attention_absorbed(cfg: dict, W: Callable, l: int, q_nope, q_rope, lat) 
     return np.concatenate(out)
 
 
+def _expert_w64(cfg: dict, W: Callable, name: str, index=None) -> np.ndarray:
+    """An expert matrix as float64: bf16 bits, or (weights "mxfp4") MXFP4 rows with the
+    E8M0 scales in name + ".scale"."""
+    if cfg.get("weights") != "mxfp4":
+        return _w64(W, name, index)
+    sc = W(name + ".scale") if index is None else W(name + ".scale", index)
+    return dequant_mxfp4(W(name) if index is None else W(name, index), sc)
+
+
 def moe_ffn(cfg: dict, W: Callable, l: int, hn: np.ndarray):
-    """MoE FFN (reading R9): y = SwiGLU_shared(hn) + sum_{e in T} w_e SwiGLU_e(hn)."""
+    """MoE FFN (reading R9): y = SwiGLU_shared(hn) + sum_{e in T} w_e SwiGLU_e(hn). With
+    weights "mxfp4" every expert matrix (routed and shared) is MXFP4 (reading R22)."""
     p = f"layers.{l}."
     k = cfg["top_k"]
     t: Dict[str, np.ndarray] = {}
@@ -457,14 +502,15 @@ def moe_ffn(cfg: dict, W: Callable, l: int, hn: np.ndarray):
     t["topk"] = rt["topk"]
     t["topk_w"] = rt["w"]
     t["topk_margin"] = np.array([rt["margin"]])
-    a_s, y_s = swiglu(_w64(W, p + "shared.w_gate"), _w64(W, p + "shared.w_up"),
-                      _w64(W, p + "shared.w_down"), hn)
+    a_s, y_s = swiglu(_expert_w64(cfg, W, p + "shared.w_gate"), _expert_w64(cfg, W, p + "shared.w_up"),
+                      _expert_w64(cfg, W, p + "shared.w_down"), hn)
     t["shared_act"], t["shared_out"] = a_s, y_s
     y = y_s.copy()
     acts = []
     for e, we in zip(rt["topk"], rt["w"]):
-        a_e, y_e = swiglu(_w64(W, p + "experts.w_gate", int(e)), _w64(W, p + "experts.w_up", int(e)),
-                          _w64(W, p + "experts.w_down", int(e)), hn)
+        a_e, y_e = swiglu(_expert_w64(cfg, W, p + "experts.w_gate", int(e)),
+                          _expert_w64(cfg, W, p + "experts.w_up", int(e)),
+                          _expert_w64(cfg, W, p + "experts.w_down", int(e)), hn)
         acts.append(a_e)
         y = y + we * y_e
     t["expert_act"] = np.concatenate(acts) if acts else np.zeros(0)

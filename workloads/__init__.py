@@ -19,6 +19,12 @@ available; these shapes stand in for them):
     even) with scale[r] = max|row| / 448 in fp32, so the row's largest value maps to the
     largest finite E4M3 magnitude. Quantisation is input generation: the decode path only
     reads bytes and scales.
+  * configs with "weights": "mxfp4" (MoE only): every expert matrix (routed and shared) is
+    drawn the same way in fp32, then cut into blocks of 32 consecutive columns; a block with
+    largest magnitude a gets the power-of-two scale 2^(floor(log2 a) - 2) (E8M0 byte
+    floor(log2 a) + 125, so the block's largest value lands in [4, 8) before rounding) and
+    each value is stored as the nearest E2M1 value of w / scale (magnitudes 0, 0.5, 1, 1.5,
+    2, 3, 4, 6; saturating at 6), two per byte, the even column in the low nibble.
 All tensors come from one torch.Generator seeded once, drawn in the canonical order.
 """
 from __future__ import annotations
@@ -33,6 +39,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 BF16 = "bf16"
 FP32 = "fp32"
 FP8 = "fp8"     # OCP FP8 E4M3 bytes (with a per-row fp32 "<name>.scale" tensor after it)
+FP4X2 = "fp4x2"  # MXFP4: E2M1 pairs, uint8 [..., K/2] (with an E8M0 "<name>.scale" [..., K/32] after it)
+E8M0 = "e8m0"    # power-of-two block scales, one byte each
 
 
 def load_configs() -> Dict[str, dict]:
@@ -65,7 +73,7 @@ class TensorSpec:
 
     @property
     def nbytes(self) -> int:
-        return self.numel * {BF16: 2, FP8: 1}.get(self.dtype, 4)
+        return self.numel * {BF16: 2, FP8: 1, FP4X2: 1, E8M0: 1}.get(self.dtype, 4)
 
 
 def _mla_attn_specs(cfg: dict, p: str) -> List[TensorSpec]:
@@ -90,6 +98,17 @@ def weight_specs(cfg: dict) -> List[TensorSpec]:
     """Canonical ordered tensor list of a config (the order weights are bound in). With
     "weights": "fp8" each linear matrix is FP8 and followed by its fp32 row scales."""
     out = _weight_specs_bf16(cfg)
+    if cfg.get("weights") == "mxfp4":
+        if cfg["arch"] != "moe":
+            raise ValueError("MXFP4 expert weights need an MoE config")
+        mx: List[TensorSpec] = []
+        for s in out:
+            if ".experts." in s.name or ".shared." in s.name:
+                mx.append(TensorSpec(s.name, s.shape[:-1] + (s.shape[-1] // 2,), FP4X2, "weight"))
+                mx.append(TensorSpec(s.name + ".scale", s.shape[:-1] + (s.shape[-1] // 32,), E8M0, "scale"))
+            else:
+                mx.append(s)
+        return mx
     if cfg.get("weights", "bf16") != "fp8":
         return out
     q: List[TensorSpec] = []
@@ -181,6 +200,26 @@ def _quantize_e4m3_rows(torch, w32):
     return q.view(torch.uint8), scale.to(torch.float32)
 
 
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # between consecutive E2M1 magnitudes
+
+
+def _quantize_mxfp4(torch, w32):
+    """MXFP4 quantisation of an fp32 [rows][K] tensor (K a multiple of 32): (packed E2M1
+    pairs uint8 [rows][K/2], E8M0 scales uint8 [rows][K/32])."""
+    rows, k = w32.shape
+    blk = w32.view(rows, k // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    e = torch.floor(torch.log2(torch.where(amax > 0, amax, torch.ones_like(amax)))) - 2
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp_(-127, 127)
+    v = blk / torch.exp2(e)[:, :, None]
+    mid = torch.tensor(_E2M1_MIDPOINTS, dtype=torch.float32, device=w32.device)
+    mag = torch.bucketize(v.abs().contiguous(), mid, right=True).to(torch.uint8)  # 0..7
+    code = mag | torch.where(v < 0, 8, 0).to(torch.uint8)
+    code = code.view(rows, k)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8)
+
+
 def weight_bytes(cfg: dict) -> int:
     return sum(s.nbytes for s in weight_specs(cfg))
 
@@ -223,7 +262,24 @@ def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = Non
     for s in weight_specs(cfg):
         if s.init == "scale":
             continue  # produced with its matrix
-        if s.init == "weight" and s.dtype == FP8:
+        if s.init == "weight" and s.dtype == FP4X2:
+            kk = 2 * s.shape[-1]
+            lead = s.shape[:-1]
+            nrow = 1
+            for dim in lead:
+                nrow *= dim
+            q = torch.empty((nrow, kk // 2), dtype=torch.uint8, device=dev)
+            sc = torch.empty((nrow, kk // 32), dtype=torch.uint8, device=dev)
+            rows = max(1, (1 << 26) // kk)
+            for r0 in range(0, nrow, rows):
+                r1 = min(nrow, r0 + rows)
+                w32 = torch.randn((r1 - r0, kk), generator=gen, device=dev, dtype=torch.float32)
+                w32.mul_(init["weight_std"])
+                q[r0:r1], sc[r0:r1] = _quantize_mxfp4(torch, w32)
+                del w32
+            weights[s.name] = q.view(lead + (kk // 2,))
+            weights[s.name + ".scale"] = sc.view(lead + (kk // 32,))
+        elif s.init == "weight" and s.dtype == FP8:
             q = torch.empty(s.shape, dtype=torch.uint8, device=dev)
             sc = torch.empty(s.shape[0], dtype=torch.float32, device=dev)
             rows = max(1, (1 << 26) // s.shape[1])
