@@ -736,7 +736,8 @@ struct Builder {
     P.buffers.push_back({"control", DEC_DTYPE_I32, P.off_ctl, CTL_WORDS});
 
     // bytes the method must read per step: every dense weight once (routed experts: only
-    // the top_k chosen), and positions [0, kv_len + ntok) of the cache once
+    // the top_k chosen; the token embedding: one row), and positions [0, kv_len + ntok) of
+    // the cache once
     P.weight_bytes = 0;
     for (auto& w : P.weights) P.weight_bytes += w.bytes;
     int64_t alg = P.weight_bytes;
@@ -744,6 +745,8 @@ struct Builder {
       int64_t per_expert = 3LL * s.expert_ffn * s.hidden * 2;
       alg -= (int64_t)s.n_layers * (s.n_routed - s.top_k) * per_expert;
     }
+    if (P.w_embed >= 0)  // a step reads one row of the token embedding, not the table
+      alg -= (int64_t)(s.vocab - 1) * s.hidden * 2;
     int64_t kv_row = (s.arch == DEC_ARCH_GQA) ? 2LL * s.n_kv_heads * s.head_dim * 2 : (int64_t)(s.kv_lora_rank + s.qk_rope) * 2;
     alg += (int64_t)s.n_layers * (n + nt) * kv_row;
     P.alg_bytes = alg;

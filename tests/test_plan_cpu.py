@@ -273,6 +273,9 @@ def test_dynamic_plan_layout(name, max_len):
         assert tuple(e["shape"]) == (cfg["vocab"], cfg["hidden"]) and e["dtype"] == "bf16"
     sz = p.sizes()
     assert sz["kv_bytes"] == 2 * cfg["n_layers"] * 2 * cfg["n_kv_heads"] * (max_len + 1) * cfg["head_dim"]
+    # a step reads one embedding row, not the table: the same bytes as the fixed plan plus a row
+    emb_row = cfg["hidden"] * 2 if cfg["vocab"] > 0 else 0
+    assert sz["algorithmic_bytes_per_step"] == fixed.sizes()["algorithmic_bytes_per_step"] + emb_row
     tasks = p.tasks()
     am = [t for t in tasks if t["type"] == 20]
     lm = [t for t in tasks if t["type"] == 6]
