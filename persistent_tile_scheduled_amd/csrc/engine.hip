@@ -223,6 +223,17 @@ __device__ __forceinline__ float wave_sum(float v) {
          (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
+// Full 64-lane maximum, returned wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kQuadSwap1>(v));
+  v = fmaxf(v, dpp<kQuadSwap2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
 // 2^x with the hardware instruction alone (no denormal-range scaling): results below 2^-126
 // come out as 0. The softmax weights use it with x <= 0 relative to a running maximum, so it
 // only drops terms smaller than 2^-126 of the largest one.
@@ -997,37 +1008,36 @@ __device__ __forceinline__ void StageMerge::finish(Blk& b) const {
   if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[0] = (uint32_t)now();
   __syncthreads();
   if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[1] = (uint32_t)now();
-  // wave h (h < 8) owns heads h, h + 8, ...: lanes run over the splits
+  // merge weights w[s][h] = 2^(m_s - M) / sum_s 2^(m_s - M) l_s: wave h (h < 8) owns heads
+  // h, h + 8, ...; lanes run over the splits (an empty split has m = -inf and weight 0)
   for (int h = wave_id(); h < H; h += kWaves) {
     const int lane = threadIdx.x & 63;
     float M = -INFINITY;
     for (int sp = lane; sp < S; sp += 64) M = fmaxf(M, P[(sp * H + h) * ps]);
-    M = fmaxf(M, __shfl_xor(M, 1, 64));
-    M = fmaxf(M, __shfl_xor(M, 2, 64));
-    M = fmaxf(M, __shfl_xor(M, 4, 64));
-    M = fmaxf(M, __shfl_xor(M, 8, 64));
-    M = fmaxf(M, __shfl_xor(M, 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    M = wave_max(M);
     float den = 0.f;
-    for (int sp = lane; sp < S; sp += 64) den += exp2f(P[(sp * H + h) * ps] - M) * P[(sp * H + h) * ps + 1];
-    den = wave_sum(den);
-    const float inv = 1.0f / den;
-    for (int sp = lane; sp < S; sp += 64) w[sp * H + h] = exp2f(P[(sp * H + h) * ps] - M) * inv;
+    for (int sp = lane; sp < S; sp += 64) den = fmaf(ex2(P[(sp * H + h) * ps] - M), P[(sp * H + h) * ps + 1], den);
+    const float inv = 1.0f / wave_sum(den);
+    for (int sp = lane; sp < S; sp += 64) w[sp * H + h] = ex2(P[(sp * H + h) * ps] - M) * inv;
   }
   __syncthreads();
   if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[2] = (uint32_t)now();
+  // the weighted sums, eight independent accumulators per output
   for (int i = threadIdx.x; i < H * hd; i += kThreads) {
     const int h = i / hd, d = i - h * hd;
-    float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
+    const float* pp = P + h * ps + 4 + d;
+    const float* ww = w + h;
+    const int st = H * ps;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
     int sp = 0;
-    for (; sp + 4 <= S; sp += 4) {
-      v0 = fmaf(w[sp * H + h], P[(sp * H + h) * ps + 4 + d], v0);
-      v1 = fmaf(w[(sp + 1) * H + h], P[((sp + 1) * H + h) * ps + 4 + d], v1);
-      v2 = fmaf(w[(sp + 2) * H + h], P[((sp + 2) * H + h) * ps + 4 + d], v2);
-      v3 = fmaf(w[(sp + 3) * H + h], P[((sp + 3) * H + h) * ps + 4 + d], v3);
+    for (; sp + 8 <= S; sp += 8) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fmaf(ww[(sp + k) * H], pp[(sp + k) * st], v[k]);
     }
-    for (; sp < S; ++sp) v0 = fmaf(w[sp * H + h], P[(sp * H + h) * ps + 4 + d], v0);
-    b.xs[i] = (v0 + v1) + (v2 + v3);
+    for (; sp < S; ++sp) v[0] = fmaf(ww[sp * H], pp[sp * st], v[0]);
+    b.xs[i] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
   }
   __syncthreads();
   if (o_off >= 0 && threadIdx.x < 64)
@@ -1584,7 +1594,7 @@ __device__ __forceinline__ void attn_finish(const EngineArgs& A, Blk& b, const T
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float mw = b.scr[w * SS + h * ps];
-      const float e = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      const float e = (mw == -INFINITY) ? 0.f : ex2(mw - M);
       v = fmaf(e, b.scr[w * SS + h * ps + 4 + d], v);
       den = fmaf(e, b.scr[w * SS + h * ps + 1], den);
     }
