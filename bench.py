@@ -31,6 +31,8 @@ WORKLOADS = {
     "tiny": "tiny decoder (2 layers, hidden 256), batch 1, KV 128",
     "8b_4k_fp8": "the 8B-shaped decoder with every linear matrix in FP8 E4M3 (one fp32 scale per row), "
                  "batch 1, one decode token over a 4096-position bf16 KV cache",
+    "moe_4k_mxfp4": "the MLA + MoE stack with every expert matrix in MXFP4 (E2M1 elements, one E8M0 scale per "
+                    "32), other weights bf16, batch 1, one decode token over a 4096-position latent cache",
 }
 # Sources whose content decides the engine's memory traffic: a stored counter reading is
 # reported only while their hash matches.
@@ -369,9 +371,10 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if cfg.get("weights") == "fp8" else "bf16",
-        "data": "synthetic (seeded N(0,0.02) " + ("weights quantised per row to FP8 E4M3" if cfg.get("weights") == "fp8"
-                                                  else "bf16 weights") + ", N(0,1) bf16 KV and input)",
+        "dtype": {"fp8": "fp8", "mxfp4": "mxfp4"}.get(cfg.get("weights"), "bf16"),
+        "data": "synthetic (seeded N(0,0.02) " + {"fp8": "weights quantised per row to FP8 E4M3",
+                                                  "mxfp4": "bf16 weights, expert matrices quantised per block of 32 to MXFP4"
+                                                  }.get(cfg.get("weights"), "bf16 weights") + ", N(0,1) bf16 KV and input)",
         "config": {"workload": f"{name}: {WORKLOADS.get(args.config, args.config)}" +
                    (f"; a verification step of {m} tokens at positions kv_len .. kv_len + {m - 1}" if m > 1 else ""),
                    "kv_len": cfg["kv_len"], "batch": 1, "tokens_per_step": m},

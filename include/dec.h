@@ -66,13 +66,23 @@ typedef enum {
 
 typedef enum {
   DEC_WEIGHTS_BF16 = 0,      /* every matrix bf16 */
-  DEC_WEIGHTS_FP8_E4M3 = 1   /* GQA only: each linear matrix (wq, wk, wv, wo, w_gate, w_up,
+  DEC_WEIGHTS_FP8_E4M3 = 1,  /* GQA only: each linear matrix (wq, wk, wv, wo, w_gate, w_up,
                                 w_down, lm_head) as OCP FP8 E4M3 bytes [rows][cols], followed in
                                 the weight list by "<name>.scale", fp32 [rows]: row r of the
                                 matrix is scale[r] * e4m3(bytes[r][:]). cols must be a multiple
                                 of 16. Norm gains (and "embed") stay bf16. This is the survey's
                                 next lever on bytes per token; the pages name the lever (fewer
                                 bytes moved per token), not a format. */
+  DEC_WEIGHTS_MXFP4 = 2      /* MoE only: every expert matrix (experts.w_gate / w_up / w_down and
+                                shared.w_gate / w_up / w_down) in the OCP Microscaling FP4 format:
+                                E2M1 elements packed two per byte, uint8 [..][cols / 2], element 2i
+                                in the low nibble of byte i, followed in the weight list by
+                                "<name>.scale", E8M0 bytes uint8 [..][cols / 32]: element k of a row
+                                is e2m1(k) * 2^(scale[k / 32] - 127). hidden and expert_ffn must be
+                                multiples of 32. Every other weight stays bf16. The TileRT talk's
+                                practice section reports FP4 experts with the other modules kept
+                                at their precision; it names no format, this is the one gfx950
+                                converts in hardware. Whole-step launches only. */
 } dec_weight_format;
 
 typedef enum {
@@ -110,7 +120,11 @@ typedef struct dec_device_info {
   int32_t reserved0;
 } dec_device_info;
 
-typedef enum { DEC_DTYPE_BF16 = 0, DEC_DTYPE_FP32 = 1, DEC_DTYPE_I32 = 2, DEC_DTYPE_FP8 = 3 } dec_dtype;
+typedef enum {
+  DEC_DTYPE_BF16 = 0, DEC_DTYPE_FP32 = 1, DEC_DTYPE_I32 = 2, DEC_DTYPE_FP8 = 3,
+  DEC_DTYPE_FP4X2 = 4,  /* two E2M1 elements per byte (dims count bytes) */
+  DEC_DTYPE_E8M0 = 5    /* one power-of-two block scale per byte */
+} dec_dtype;
 
 typedef struct dec_tensor_desc {
   char name[64];           /* e.g. "layers.3.wq" */

@@ -16,8 +16,8 @@ DEC_ABI_VERSION = 2
 ARCH = {"gqa": 0, "mla": 1, "moe": 2}
 STATUS = {0: "DEC_OK", -1: "DEC_E_INVAL", -2: "DEC_E_SHAPE", -3: "DEC_E_CAPACITY", -4: "DEC_E_DEVICE",
           -5: "DEC_E_OCCUPANCY", -6: "DEC_E_HIP", -7: "DEC_E_TIMEOUT", -8: "DEC_E_UNBOUND", -9: "DEC_E_PLAN"}
-DTYPE = {0: "bf16", 1: "fp32", 2: "i32", 3: "fp8"}
-WEIGHT_FORMAT = {"bf16": 0, "fp8": 1}
+DTYPE = {0: "bf16", 1: "fp32", 2: "i32", 3: "fp8", 4: "fp4x2", 5: "e8m0"}
+WEIGHT_FORMAT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 
 # task type ids (mirror of the engine's TaskType enum)
 TASK_TYPES = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "MLA_A", 8: "MLA_B",

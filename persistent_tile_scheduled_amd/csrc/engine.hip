@@ -265,6 +265,7 @@ struct Blk {
   uint64_t* rowp; // LDS: row pointers of the current GEMV task
   int* xoffp;     // LDS: per-row input offsets of the current GEMV task
   float* scl;     // LDS: per-row weight scales of the current GEMV task (FP8 weights)
+  uint64_t* srowp; // LDS: per-row block-scale pointers of the current GEMV task (MXFP4 weights)
   float* gs;      // LDS: norm gains (bf16) of the current task
   float* actp;    // the activation region (generic pointer, for LDS DMA)
   int n;                // the step's position: cached positions [0, n), the new token's slot n
@@ -375,9 +376,13 @@ __device__ __forceinline__ uint32_t signal_w0(const EngineArgs& A, int ctr) {
 }
 
 __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kChunkCols * kChunkCols; }
-// A staged input padded to whole GEMV chunks of weights with ES bytes each (512 or 1024 columns).
+// A staged input padded to whole GEMV chunks of weights with ES bytes each (512 or 1024
+// columns; 2048 for MXFP4, ES = 0).
 template <int ES>
-__device__ __forceinline__ int padc(int k) { return (k + 1024 / ES - 1) / (1024 / ES) * (1024 / ES); }
+__device__ __forceinline__ int padc(int k) {
+  constexpr int c = ES == 0 ? 2048 : 1024 / ES;
+  return (k + c - 1) / c * c;
+}
 // The fp32 row scales of an FP8 matrix: the weight after it in the bound list.
 template <int ES>
 __device__ __forceinline__ const float* wscale(const EngineArgs& A, int idx) { return ES == 1 ? wp<float>(A, idx + 1) : nullptr; }
@@ -530,15 +535,40 @@ constexpr int kRingOproj = DEC_RING_OPROJ;  // register ring depth of the per-gr
 constexpr int kRingFfn = 3;  // gate/up and (GQA) down: three batches in flight cover more of the stage boundary
 
 
-// One wave load is 16 bytes per lane: 8 bf16 or 16 FP8 (E4M3) weights. ES = bytes per
-// weight; a chunk (one wave load) spans 1024 / ES columns.
+// One wave load is 16 bytes per lane: 8 bf16, 16 FP8 (E4M3) or 32 MXFP4 (E2M1) weights.
+// ES = bytes per weight (2 bf16, 1 FP8), or 0 for MXFP4: a lane's 16 bytes are then exactly one
+// block of 32 elements sharing one E8M0 scale byte (loaded beside the weights, `sb`), element
+// 2i in the low nibble of byte i. A chunk (one wave load) spans kCols columns.
 template <int ES>
 struct Chunk {
-  static constexpr int kCols = 1024 / ES;  // columns per chunk
-  static constexpr int kLane = 16 / ES;    // columns per lane
+  static constexpr int kCols = ES == 0 ? 2048 : 1024 / ES;  // columns per chunk
+  static constexpr int kLane = ES == 0 ? 32 : 16 / ES;      // columns per lane
+  // bytes of `cols` consecutive weights of a row
+  __device__ static __forceinline__ size_t bytes(int cols) { return ES == 0 ? (size_t)cols / 2 : (size_t)cols * ES; }
   // acc0/acc1 += the lane's weights . x (xp: the lane's kLane inputs in LDS)
-  __device__ static __forceinline__ void dot(const u4& w, const float* xp, float& acc0, float& acc1) {
-    if constexpr (ES == 2) {
+  __device__ static __forceinline__ void dot(const u4& w, uint32_t sb, const float* xp, float& acc0, float& acc1) {
+    if constexpr (ES == 0) {
+      // hardware E2M1 -> fp32 conversion of one byte (two elements) per instruction, scaled by
+      // the block's power of two 2^(sb - 127)
+      const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)(sb & 0xffu) - 127);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f4 xa = *(const f4*)(xp + 8 * q), xb = *(const f4*)(xp + 8 * q + 4);
+        const f2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 0);
+        const f2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 1);
+        const f2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 2);
+        const f2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 3);
+        acc0 = fmaf(e0.x, xa.x, acc0);
+        acc1 = fmaf(e0.y, xa.y, acc1);
+        acc0 = fmaf(e1.x, xa.z, acc0);
+        acc1 = fmaf(e1.y, xa.w, acc1);
+        acc0 = fmaf(e2.x, xb.x, acc0);
+        acc1 = fmaf(e2.y, xb.y, acc1);
+        acc0 = fmaf(e3.x, xb.z, acc0);
+        acc1 = fmaf(e3.y, xb.w, acc1);
+      }
+    } else if constexpr (ES == 2) {
       const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
       acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
       acc1 = fmaf(bf_hi(w.x), x0.y, acc1);
@@ -573,15 +603,19 @@ template <int ES>
 struct StreamT {
   using C = Chunk<ES>;
   const uint64_t* rowp;
+  const uint64_t* srowp;  // MXFP4: the rows' scale pointers
   const int* xoffp;
   int jb, K, cpr, lane;
   int lj, lc;
   const uint8_t* lrow;
+  const uint8_t* lsrow;
   int cj, cc, cxo;
   float acc0, acc1;
 
-  __device__ __forceinline__ void init(const uint64_t* rp, const int* xp, int ja, int jb_, int K_, int lane_) {
+  __device__ __forceinline__ void init(const uint64_t* rp, const uint64_t* srp, const int* xp, int ja, int jb_, int K_,
+                                       int lane_) {
     rowp = rp;
+    srowp = srp;
     xoffp = xp;
     jb = jb_;
     K = K_;
@@ -590,31 +624,47 @@ struct StreamT {
     lj = ja;
     lc = 0;
     lrow = (ja < jb) ? (const uint8_t*)uni64(rowp[ja]) : nullptr;
+    lsrow = (ES == 0 && ja < jb) ? (const uint8_t*)uni64(srowp[ja]) : nullptr;
     cj = ja;
     cc = 0;
     cxo = (ja < jb) ? uni(xoffp[ja]) : 0;
     acc0 = acc1 = 0.f;
   }
-  __device__ __forceinline__ void load(u4 (&bf)[NB]) {
+  __device__ __forceinline__ void load(u4 (&bf)[NB], uint32_t (&sb)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (lj < jb) {
         int col = lc * C::kCols + lane * C::kLane;
-        col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
-        bf[i] = ldg_nt(lrow + (size_t)col * ES);
+        const bool in = col < K;
+        col = in ? col : 0;  // masked lanes re-read the row start (bf16/FP8: xs is zero there)
+        bf[i] = ldg_nt(lrow + C::bytes(col));
+        if constexpr (ES == 0) sb[i] = __builtin_nontemporal_load(lsrow + (in ? lc * 64 + lane : 0));
         if (++lc == cpr) {
           lc = 0;
-          if (++lj < jb) lrow = (const uint8_t*)uni64(rowp[lj]);
+          if (++lj < jb) {
+            lrow = (const uint8_t*)uni64(rowp[lj]);
+            if constexpr (ES == 0) lsrow = (const uint8_t*)uni64(srowp[lj]);
+          }
         }
       }
     }
   }
   template <class Emit>
-  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const float* xs, Emit& emit) {
+  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const uint32_t (&sb)[NB], const float* xs, Emit& emit) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (cj < jb) {
-        C::dot(bf[i], xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
+        if constexpr (ES == 0) {
+          // lanes past the row's end hold no elements (the staged input is not padded to whole
+          // 2048-column chunks): their products are dropped
+          float p0 = 0.f, p1 = 0.f;
+          C::dot(bf[i], sb[i], xs + cxo + cc * C::kCols + lane * C::kLane, p0, p1);
+          const bool in = cc * C::kCols + lane * C::kLane < K;
+          acc0 += in ? p0 : 0.f;
+          acc1 += in ? p1 : 0.f;
+        } else {
+          C::dot(bf[i], 0u, xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
+        }
         if (++cc == cpr) {
           emit(cj, wave_sum(acc0 + acc1));
           acc0 = acc1 = 0.f;
@@ -635,6 +685,7 @@ struct StreamT {
 template <int ES>
 struct StreamFlatT {
   using C = Chunk<ES>;
+  static_assert(ES != 0, "MXFP4 rows stream whole rows per wave (StreamT)");
   const uint64_t* rowp;
   const int* xoffp;
   int fb, K, cpr, lane;
@@ -643,7 +694,8 @@ struct StreamFlatT {
   int cf, cj, cc, cxo;
   float acc0, acc1;
 
-  __device__ __forceinline__ void init(const uint64_t* rp, const int* xp, int fa, int fb_, int K_, int lane_) {
+  __device__ __forceinline__ void init(const uint64_t* rp, const uint64_t*, const int* xp, int fa, int fb_, int K_,
+                                       int lane_) {
     rowp = rp;
     xoffp = xp;
     fb = fb_;
@@ -658,13 +710,13 @@ struct StreamFlatT {
     cxo = (fa < fb) ? uni(xoffp[j0]) : 0;
     acc0 = acc1 = 0.f;
   }
-  __device__ __forceinline__ void load(u4 (&bf)[NB]) {
+  __device__ __forceinline__ void load(u4 (&bf)[NB], uint32_t (&)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (lf < fb) {
         int col = lc * C::kCols + lane * C::kLane;
         col = col < K ? col : 0;  // masked lanes re-read the row start; xs is zero there
-        bf[i] = ldg_nt(lrow + (size_t)col * ES);
+        bf[i] = ldg_nt(lrow + C::bytes(col));
         ++lf;
         if (++lc == cpr) {
           lc = 0;
@@ -675,11 +727,11 @@ struct StreamFlatT {
     }
   }
   template <class Emit>
-  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const float* xs, Emit& emit) {
+  __device__ __forceinline__ void consume(const u4 (&bf)[NB], const uint32_t (&)[NB], const float* xs, Emit& emit) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       if (cf < fb) {
-        C::dot(bf[i], xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
+        C::dot(bf[i], 0u, xs + cxo + cc * C::kCols + lane * C::kLane, acc0, acc1);
         ++cf;
         const bool row_end = ++cc == cpr;
         if (row_end || cf == fb) {
@@ -701,11 +753,12 @@ using StreamFlat = StreamFlatT<2>;
 
 // Each wave writes the row pointers / input offsets of its own rows (no barrier needed:
 // LDS accesses of one wave are ordered).
-template <class RM>
-__device__ __forceinline__ void fill_rows(const RM& rm, int ja, int jb, uint64_t* rowp, int* xoffp) {
+template <int ES = 2, class RM>
+__device__ __forceinline__ void fill_rows(const RM& rm, int ja, int jb, uint64_t* rowp, int* xoffp, uint64_t* srowp = nullptr) {
   for (int j = ja + (int)(threadIdx.x & 63); j < jb; j += 64) {
     rowp[j] = (uint64_t)(uintptr_t)rm.row(j);
     xoffp[j] = rm.xoff(j);
+    if constexpr (ES == 0) srowp[j] = (uint64_t)(uintptr_t)rm.srow(j);
   }
 }
 
@@ -762,6 +815,7 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   }
   typename std::conditional<FLAT, StreamFlatT<ES>, StreamT<ES>>::type s;
   u4 buf[R][NB];
+  uint32_t sbuf[R][NB];  // MXFP4 block scales (unused for the other formats)
   if constexpr (ES == 1) {
     // FP8 rows: wave 0 (no weight loads in flight) puts the task's row scales into LDS; the
     // barrier of the dependency wait publishes them
@@ -775,10 +829,10 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     __syncthreads();
   }
   if (prefetch) {
-    fill_rows(rm, ja, jb, b.rowp, b.xoffp);
-    s.init(b.rowp, b.xoffp, fa, fb, K, lane);
+    fill_rows<ES>(rm, ja, jb, b.rowp, b.xoffp, b.srowp);
+    s.init(b.rowp, b.srowp, b.xoffp, fa, fb, K, lane);
 #pragma unroll
-    for (int k = 0; k < R; ++k) s.load(buf[k]);
+    for (int k = 0; k < R; ++k) s.load(buf[k], sbuf[k]);
   }
   // wave 0 issues the input's copy the moment the wait succeeds (StageVec::early)
   if (!wait_deps(A, b, t, pre_deps, -1, [&] { stage.early(b); })) return false;
@@ -789,10 +843,10 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   if (kTaskLogDetail && threadIdx.x == 0) b.t_staged = (uint32_t)now();
   issue();
   if (!prefetch) {
-    fill_rows(rm, ja, jb, b.rowp, b.xoffp);
-    s.init(b.rowp, b.xoffp, fa, fb, K, lane);
+    fill_rows<ES>(rm, ja, jb, b.rowp, b.xoffp, b.srowp);
+    s.init(b.rowp, b.srowp, b.xoffp, fa, fb, K, lane);
 #pragma unroll
-    for (int k = 0; k < R; ++k) s.load(buf[k]);
+    for (int k = 0; k < R; ++k) s.load(buf[k], sbuf[k]);
   }
   float gacc = 0.f;
   auto emit = [&](int j, float v) {
@@ -813,20 +867,20 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
     else return s.cj < jb;
   };
   while (more()) {
-    s.consume(buf[0], b.xs, emit);
-    s.load(buf[0]);
+    s.consume(buf[0], sbuf[0], b.xs, emit);
+    s.load(buf[0], sbuf[0]);
     if (!more()) break;
-    s.consume(buf[1], b.xs, emit);
-    s.load(buf[1]);
+    s.consume(buf[1], sbuf[1], b.xs, emit);
+    s.load(buf[1], sbuf[1]);
     if constexpr (R > 2) {
       if (!more()) break;
-      s.consume(buf[2], b.xs, emit);
-      s.load(buf[2]);
+      s.consume(buf[2], sbuf[2], b.xs, emit);
+      s.load(buf[2], sbuf[2]);
     }
     if constexpr (R > 3) {
       if (!more()) break;
-      s.consume(buf[3], b.xs, emit);
-      s.load(buf[3]);
+      s.consume(buf[3], sbuf[3], b.xs, emit);
+      s.load(buf[3], sbuf[3]);
     }
   }
   __syncthreads();
@@ -2114,18 +2168,52 @@ __device__ __forceinline__ bool task_router(const EngineArgs& A, Blk& b, const T
       });
 }
 
+// a when sel is false, else b: by arithmetic on the addresses (a per-lane choice between two
+// pointers written as a select is placed in scratch memory by the compiler)
+__device__ __forceinline__ const uint8_t* pick2(bool sel, const void* a, const void* b) {
+  const uintptr_t x = (uintptr_t)a;
+  return (const uint8_t*)(x + (uintptr_t)sel * ((uintptr_t)b - x));
+}
+
+// Expert matrices in MXFP4 (ES = 0): rows of K / 2 packed bytes, and K / 32 E8M0 scale bytes
+// per row in the weight bound after the matrix. Unit u -> (gate row u, up row u) of the
+// shared experts' [ns * eff, hidden] matrices.
+struct RmGateUp4 {
+  const uint8_t *Wg, *Wu, *Sg, *Su;
+  int K, u0;
+  __device__ __forceinline__ const void* row(int j) const {
+    return pick2(j & 1, Wg, Wu) + (size_t)(u0 + (j >> 1)) * (K / 2);
+  }
+  __device__ __forceinline__ const void* srow(int j) const {
+    return pick2(j & 1, Sg, Su) + (size_t)(u0 + (j >> 1)) * (K / 32);
+  }
+  __device__ __forceinline__ int xoff(int) const { return 0; }
+};
+
 // shared experts' gate/up rows (rows of [ns * eff, hidden] matrices) + SwiGLU
-__device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+template <int ES, class RM>
+__device__ __forceinline__ bool shared_gu(const EngineArgs& A, Blk& b, const TaskDesc& t, const RM& rm) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden;
-  const RmGateUp rm{wp<uint16_t>(A, L.w[LW_SGATE]), wp<uint16_t>(A, L.w[LW_SUP]), K, t.u0};
-  return run_gemv(
+  return run_gemv<2, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      stage_vec(L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
+      stage_vec(L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_SACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
       });
+}
+template <int ES>
+__device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  if constexpr (ES == 0) {
+    const RmGateUp4 rm{wp<uint8_t>(A, L.w[LW_SGATE]), wp<uint8_t>(A, L.w[LW_SUP]), wp<uint8_t>(A, L.w[LW_SGATE] + 1),
+                       wp<uint8_t>(A, L.w[LW_SUP] + 1), A.hidden, t.u0};
+    return shared_gu<ES>(A, b, t, rm);
+  } else {
+    const RmGateUp rm{wp<uint16_t>(A, L.w[LW_SGATE]), wp<uint16_t>(A, L.w[LW_SUP]), A.hidden, t.u0};
+    return shared_gu<ES>(A, b, t, rm);
+  }
 }
 
 // sigma = sigmoid(r), z = sigma + bias (fp32). The top_k experts by z, ties to the lower
@@ -2206,16 +2294,22 @@ __device__ __forceinline__ bool task_topk(const EngineArgs& A, Blk& b, const Tas
 
 // Routed experts' gate/up: unit u = (slot k, row i) -> rows i of W_gate[e_k], W_up[e_k];
 // the expert ids are read once the top-k task has signalled, then the rows are prefetched.
+template <int ES = 2>
 struct RmExpertGU {
-  const uint16_t *Wg, *Wu;
+  const uint8_t *Wg, *Wu;
   const int* ids;  // LDS
   int K, F, u0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  const uint8_t *Sg = nullptr, *Su = nullptr;  // MXFP4: the block scales
+  __device__ __forceinline__ size_t rix(int j) const {  // the row's index in [E * F] rows
     const int u = u0 + (j >> 1), k = u / F, i = u - k * F;
+    return (size_t)ids[k] * F + i;
+  }
+  __device__ __forceinline__ const void* row(int j) const {
     const uintptr_t g = (uintptr_t)Wg;
     const uintptr_t base = g + (uintptr_t)(j & 1) * ((uintptr_t)Wu - g);
-    return (const uint16_t*)base + ((size_t)ids[k] * F + i) * K;
+    return (const uint8_t*)base + rix(j) * (ES == 0 ? K / 2 : (size_t)K * 2);
   }
+  __device__ __forceinline__ const void* srow(int j) const { return pick2(j & 1, Sg, Su) + rix(j) * (K / 32); }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
@@ -2229,14 +2323,17 @@ __device__ __forceinline__ void stage_ids(const EngineArgs& A, const LayerDesc& 
   }
 }
 
+template <int ES>
 __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden, F = A.eff;
   int* ids = reinterpret_cast<int*>(b.scr);
-  const RmExpertGU rm{wp<uint16_t>(A, L.w[LW_EGATE]), wp<uint16_t>(A, L.w[LW_EUP]), ids, K, F, t.u0};
-  return run_gemv(
+  const RmExpertGU<ES> rm{wp<uint8_t>(A, L.w[LW_EGATE]), wp<uint8_t>(A, L.w[LW_EUP]), ids, K, F, t.u0,
+                          ES == 0 ? wp<uint8_t>(A, L.w[LW_EGATE] + 1) : nullptr,
+                          ES == 0 ? wp<uint8_t>(A, L.w[LW_EUP] + 1) : nullptr};
+  return run_gemv<2, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      stage_vec(L.act[LA_H], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
+      stage_vec(L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64)
           cst(b.act, (uint32_t)(L.act[LA_ACT] + t.u0 + i) * 4u, silu(b.ys[2 * i]) * b.ys[2 * i + 1]);
@@ -2248,25 +2345,39 @@ __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, cons
 // is shared expert s (columns s*eff.. of W_sdown[r]), segment ns + k is W_down[e_k][r]. The
 // staged input holds the shared activations and the routed ones pre-scaled by w_k, one
 // segment per 512-aligned slot.
+template <int ES = 2>
 struct RmMoeDown {
-  const uint16_t *Ws, *Wd;
+  const uint8_t *Ws, *Wd;
   const int* ids;  // LDS
   int ns, G, F, Fp, d, r0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  const uint8_t *Ss = nullptr, *Sd = nullptr;  // MXFP4: the block scales
+  // element offset of task row j's segment: shared experts' segments lie side by side in one
+  // row of W_sdown; a routed expert's is a row of its own W_down
+  __device__ __forceinline__ bool shared(int j) const { return j % G < ns; }
+  __device__ __forceinline__ size_t eoff(int j) const {
     const int q = j / G, sgm = j - q * G, r = r0 + q;
-    if (sgm < ns) return Ws + (size_t)r * ns * F + (size_t)sgm * F;
-    return Wd + ((size_t)ids[sgm - ns] * d + r) * F;
+    if (sgm < ns) return (size_t)r * ns * F + (size_t)sgm * F;
+    return ((size_t)ids[sgm - ns] * d + r) * F;
   }
+  __device__ __forceinline__ const void* row(int j) const {
+    return pick2(!shared(j), Ws, Wd) + (ES == 0 ? eoff(j) / 2 : eoff(j) * 2);
+  }
+  __device__ __forceinline__ const void* srow(int j) const { return pick2(!shared(j), Ss, Sd) + eoff(j) / 32; }
   __device__ __forceinline__ int xoff(int j) const { return (j % G) * Fp; }
 };
 
+// MXFP4 segments are padded to 256 columns, the unit of the staging copy (one 1-KB LDS DMA),
+// not to whole 2048-column chunks: lanes past a segment's end drop their products (StreamT).
+template <int ES>
 __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
-  const int F = A.eff, Fp = pad512(F), ns = A.n_shared, Kt = A.top_k, G = ns + Kt, d = A.hidden;
+  const int F = A.eff, Fp = ES == 0 ? (F + 255) / 256 * 256 : pad512(F), ns = A.n_shared, Kt = A.top_k, G = ns + Kt, d = A.hidden;
   int* ids = reinterpret_cast<int*>(b.scr);
   float* wk = b.scr + 64;
-  const RmMoeDown rm{wp<uint16_t>(A, L.w[LW_SDOWN]), wp<uint16_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0};
-  return run_gemv(
+  const RmMoeDown<ES> rm{wp<uint8_t>(A, L.w[LW_SDOWN]), wp<uint8_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0,
+                         ES == 0 ? wp<uint8_t>(A, L.w[LW_SDOWN] + 1) : nullptr,
+                         ES == 0 ? wp<uint8_t>(A, L.w[LW_EDOWN] + 1) : nullptr};
+  return run_gemv<2, false, ES>(
       A, b, t, rm, G * (t.u1 - t.u0), F, G, true,
       stage_fn([&] {
         {
@@ -2959,6 +3070,8 @@ __device__ __forceinline__ const EngineArgs& args_view() {
   return *(const EngineArgs*)p;
 }
 
+// ES: the weights' element format -- GQA: every linear matrix (2 bf16, 1 FP8); MLA family:
+// the expert matrices (2 bf16, 0 MXFP4), every other matrix bf16.
 template <bool MLA, int RUN, int ES = 2, int MT = 1>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   extern __shared__ f4 lds4[];
@@ -2970,7 +3083,8 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   b.rowp = reinterpret_cast<uint64_t*>(b.ys + kYsFloats);
   b.xoffp = reinterpret_cast<int*>(b.rowp + kMaxTaskRows);
   b.scl = reinterpret_cast<float*>(b.xoffp + kMaxTaskRows);
-  b.gs = b.scl + (ES == 1 ? kMaxTaskRows : 0);
+  b.srowp = reinterpret_cast<uint64_t*>(b.scl);  // (MXFP4 scale pointers: in place of the FP8 scales)
+  b.gs = b.scl + (ES == 1 ? kMaxTaskRows : ES == 0 ? 2 * kMaxTaskRows : 0);
   b.scr = b.gs + A.gs_floats;
   b.actp = A.act;
   b.act = make_rsrc(A.act, A.act_bytes);
@@ -3082,10 +3196,10 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
           else ok = false;
           break;
         case T_ROUTER: ok = task_router(A, b, t); break;
-        case T_SHARED_GU: ok = task_shared_gu(A, b, t); break;
+        case T_SHARED_GU: ok = task_shared_gu<ES>(A, b, t); break;
         case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
-        case T_EXPERT_GU: ok = task_expert_gu(A, b, t); break;
-        case T_MOE_DOWN: ok = task_moe_down(A, b, t); break;
+        case T_EXPERT_GU: ok = task_expert_gu<ES>(A, b, t); break;
+        case T_MOE_DOWN: ok = task_moe_down<ES>(A, b, t); break;
         default: ok = false; break;
       }
     }
@@ -3140,6 +3254,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(Eng
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_dyn(EngineArgs A) {
   engine_body<true, kRunDynamic>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_x4(EngineArgs A) {
+  engine_body<true, kRunStep, 0>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_x4_dyn(EngineArgs A) {
+  engine_body<true, kRunDynamic, 0>(A);
+}
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_f8(EngineArgs A) {
   engine_body<false, kRunStep, 1>(A);
 }
@@ -3164,6 +3284,7 @@ static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1) {
   if (ntok == 2) return (const void*)dec::dec_engine_gqa_v2;
   if (ntok == 3) return (const void*)dec::dec_engine_gqa_v3;
   if (ntok == 4) return (const void*)dec::dec_engine_gqa_v4;
+  if (wfmt == 2) return run == 2 ? (const void*)dec::dec_engine_mla_x4_dyn : (const void*)dec::dec_engine_mla_x4;
   if (wfmt) return run == 2 ? (const void*)dec::dec_engine_gqa_f8_dyn : (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
   if (run == 2) return arch == 0 ? (const void*)dec::dec_engine_gqa_dyn : (const void*)dec::dec_engine_mla_dyn;
@@ -3174,7 +3295,9 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
                                                                          int run, bool cooperative, hipStream_t stream) {
   static int configured_lds[2][8] = {{-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  if (run < 0 || run > 2 || (args->wfmt && (k != 0 || run == 1))) return hipErrorInvalidValue;
+  // FP8 weights: the GQA family; MXFP4 experts: the latent family; neither in stage launches
+  if (run < 0 || run > 2 || (args->wfmt == 1 && k != 0) || (args->wfmt == 2 && k != 1) || (args->wfmt && run == 1))
+    return hipErrorInvalidValue;
   if (args->ntok > 1 && (k != 0 || run != 0 || args->wfmt || args->ntok > dec::kMaxVerifyTokens)) return hipErrorInvalidValue;
   const void* fn = engine_fn(args->arch, run, args->wfmt, args->ntok);
   const int slot = args->ntok > 1 ? 3 + args->ntok : args->wfmt ? 3 + (run == 2) : run;

@@ -179,8 +179,13 @@ struct Builder {
     if (q.abi_version != DEC_ABI_VERSION) return fail(DEC_E_INVAL, "abi_version mismatch", st);
     if (q.n_layers < 1 || q.hidden < 8 || q.hidden % 8) return fail(DEC_E_SHAPE, "need n_layers >= 1 and hidden a positive multiple of 8", st);
     if (q.vocab < 0) return fail(DEC_E_SHAPE, "vocab < 0", st);
-    if (q.weight_format != DEC_WEIGHTS_BF16 && q.weight_format != DEC_WEIGHTS_FP8_E4M3)
+    if (q.weight_format != DEC_WEIGHTS_BF16 && q.weight_format != DEC_WEIGHTS_FP8_E4M3 && q.weight_format != DEC_WEIGHTS_MXFP4)
       return fail(DEC_E_SHAPE, "unknown weight_format", st);
+    if (q.weight_format == DEC_WEIGHTS_MXFP4) {
+      if (q.arch != DEC_ARCH_MOE) return fail(DEC_E_SHAPE, "MXFP4 weights: MoE family only (the expert matrices)", st);
+      if (q.hidden % 32 || q.expert_ffn % 32)
+        return fail(DEC_E_SHAPE, "MXFP4 expert weights need hidden and expert_ffn multiples of 32", st);
+    }
     if (q.weight_format == DEC_WEIGHTS_FP8_E4M3) {
       if (q.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "FP8 weights: GQA family only", st);
       if (q.hidden % 16 || q.ffn % 16 || (q.n_q_heads * q.head_dim) % 16)
@@ -228,9 +233,24 @@ struct Builder {
   void add_weight(const std::string& name, int32_t dtype, std::vector<int64_t> dims) {
     int64_t e = 1;
     for (auto d : dims) e *= d;
-    P.weights.push_back({name, dtype, dims, e * (dtype == DEC_DTYPE_BF16 ? 2 : dtype == DEC_DTYPE_FP8 ? 1 : 4)});
+    const int64_t es = dtype == DEC_DTYPE_BF16 ? 2 : (dtype == DEC_DTYPE_FP8 || dtype == DEC_DTYPE_FP4X2 || dtype == DEC_DTYPE_E8M0) ? 1 : 4;
+    P.weights.push_back({name, dtype, dims, e * es});
   }
   bool fp8() const { return s.weight_format == DEC_WEIGHTS_FP8_E4M3; }
+  bool mx4() const { return s.weight_format == DEC_WEIGHTS_MXFP4; }
+  // An expert matrix [.., rows, cols]: bf16, or MXFP4 (packed pairs [.., rows, cols / 2]) followed
+  // by its E8M0 block scales [.., rows, cols / 32] (the engine finds them at the index + 1).
+  void add_expert(const std::string& name, std::vector<int64_t> dims) {
+    if (!mx4()) {
+      add_weight(name, DEC_DTYPE_BF16, dims);
+      return;
+    }
+    std::vector<int64_t> q = dims, sc = dims;
+    q.back() /= 2;
+    sc.back() /= 32;
+    add_weight(name, DEC_DTYPE_FP4X2, q);
+    add_weight(name + ".scale", DEC_DTYPE_E8M0, sc);
+  }
   // A linear matrix [rows][cols]: bf16, or FP8 bytes followed by the fp32 row scales (the
   // engine finds the scales at the matrix's weight index + 1).
   void add_matrix(const std::string& name, int64_t rows, int64_t cols) {
@@ -280,12 +300,16 @@ struct Builder {
         const int64_t E = s.n_routed, F = s.expert_ffn, S = (int64_t)s.n_shared * s.expert_ffn;
         W(LW_ROUTER, "router", DEC_DTYPE_BF16, {E, d});
         W(LW_RBIAS, "router_bias", DEC_DTYPE_FP32, {E});
-        W(LW_EGATE, "experts.w_gate", DEC_DTYPE_BF16, {E, F, d});
-        W(LW_EUP, "experts.w_up", DEC_DTYPE_BF16, {E, F, d});
-        W(LW_EDOWN, "experts.w_down", DEC_DTYPE_BF16, {E, d, F});
-        W(LW_SGATE, "shared.w_gate", DEC_DTYPE_BF16, {S, d});
-        W(LW_SUP, "shared.w_up", DEC_DTYPE_BF16, {S, d});
-        W(LW_SDOWN, "shared.w_down", DEC_DTYPE_BF16, {d, S});
+        auto X = [&](int slot, const std::string& nm, std::vector<int64_t> dims) {
+          ld.w[slot] = (int)P.weights.size();
+          add_expert(p + nm, dims);
+        };
+        X(LW_EGATE, "experts.w_gate", {E, F, d});
+        X(LW_EUP, "experts.w_up", {E, F, d});
+        X(LW_EDOWN, "experts.w_down", {E, d, F});
+        X(LW_SGATE, "shared.w_gate", {S, d});
+        X(LW_SUP, "shared.w_up", {S, d});
+        X(LW_SDOWN, "shared.w_down", {d, S});
       } else {
         M(LW_GATE, "w_gate", s.ffn, d);
         M(LW_UP, "w_up", s.ffn, d);
@@ -351,8 +375,8 @@ struct Builder {
   // LDS floats of the GQA plan: header, staged vector, row results, row tables, gains, scratch
   int64_t lds_floats(int64_t xs, int64_t scr) const {
     const int64_t gmax = std::max<int64_t>({(int64_t)s.hidden, (int64_t)s.q_lora_rank, (int64_t)s.kv_lora_rank});
-    // (+ the FP8 row-scale table: kMaxTaskRows floats)
-    return 64 + xs + kYsFloats + (int64_t)kMaxTaskRows * (fp8() ? 16 : 12) / 4 + align_up(gmax / 2, 256) + scr;
+    // (+ the FP8 row-scale table: kMaxTaskRows floats; MXFP4: a scale pointer per row)
+    return 64 + xs + kYsFloats + (int64_t)kMaxTaskRows * (fp8() ? 16 : mx4() ? 20 : 12) / 4 + align_up(gmax / 2, 256) + scr;
   }
 
   // ---------------------------------------------------------------- GQA layer stages
@@ -551,7 +575,15 @@ struct Builder {
     L.act[LA_TOPK] = (int)act(p + "topk", 2LL * K, DEC_DTYPE_I32);
     L.act[LA_SACT] = (int)act(p + "shared_act", std::max(SF, 1));
     L.act[LA_ACT] = (int)act(p + "expert_act", (int64_t)K * F);
-    need_xs((int64_t)(s.n_shared + K) * align_up(F, kChunkCols));
+    if (!mx4()) {
+      need_xs((int64_t)(s.n_shared + K) * align_up(F, kChunkCols));
+    } else {
+      // MXFP4 segments are padded to 256 columns (the staging copy's unit); a wave's
+      // 2048-column chunk may read past the last segment (those lanes' products are dropped),
+      // and the gate/up input is padded to 2048 columns
+      need_xs((int64_t)(s.n_shared + K - 1) * align_up(F, 256) + 2048);
+      need_xs(align_up(d, 2048));
+    }
     need_xs(3 * align_up(E, 256));  // top-k: z, sigma, bias
 
     // E1: router rows on a few workgroups, the shared expert's gate/up on the rest
@@ -741,9 +773,11 @@ struct Builder {
     P.weight_bytes = 0;
     for (auto& w : P.weights) P.weight_bytes += w.bytes;
     int64_t alg = P.weight_bytes;
-    if (s.arch == DEC_ARCH_MOE) {
-      int64_t per_expert = 3LL * s.expert_ffn * s.hidden * 2;
-      alg -= (int64_t)s.n_layers * (s.n_routed - s.top_k) * per_expert;
+    if (s.arch == DEC_ARCH_MOE) {  // the routed experts' bytes (matrices and block scales), per expert
+      int64_t routed = 0;
+      for (auto& w : P.weights)
+        if (w.name.rfind("layers.0.experts.", 0) == 0) routed += w.bytes;
+      alg -= (int64_t)s.n_layers * (s.n_routed - s.top_k) * (routed / s.n_routed);
     }
     if (P.w_embed >= 0)  // a step reads one row of the token embedding, not the table
       alg -= (int64_t)(s.vocab - 1) * s.hidden * 2;

@@ -10,7 +10,8 @@ from typing import Dict, Optional
 
 from . import binding as B
 
-_TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32", "fp8": "uint8"}  # FP8 bytes as uint8
+_TORCH_DTYPE = {"bf16": "bfloat16", "fp32": "float32", "i32": "int32", "fp8": "uint8", "fp4x2": "uint8",
+                "e8m0": "uint8"}  # FP8 bytes, packed E2M1 pairs and E8M0 scales as uint8
 
 
 class DecodeEngine:

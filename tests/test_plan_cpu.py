@@ -16,7 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MI355X = B.device_info()
 GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k", "tiny_hd256_g3",
                "tiny_fp8", "tiny_ragged_fp8", "small_gqa_fp8", "8b_4k_fp8"]
-MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k", "moe_wide_tiny", "moe_max_route"]
+MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k", "moe_wide_tiny", "moe_max_route",
+               "moe_tiny_mxfp4", "moe_small_mxfp4", "moe_4k_mxfp4", "moe_max_route_mxfp4"]
 
 
 def plan(name, dev=MI355X, **over):
@@ -417,6 +418,32 @@ def test_mla_algorithmic_bytes():
     unused = cfg["n_layers"] * (cfg["n_routed"] - cfg["top_k"]) * per_expert
     row = (cfg["kv_lora_rank"] + cfg["qk_rope"]) * 2
     assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+    # MXFP4 experts: half a byte per element plus one scale byte per 32
+    p, cfg = plan("moe_4k_mxfp4")
+    s = p.sizes()
+    per_expert = 3 * cfg["expert_ffn"] * cfg["hidden"] // 2 + 3 * cfg["expert_ffn"] * cfg["hidden"] // 32
+    unused = cfg["n_layers"] * (cfg["n_routed"] - cfg["top_k"]) * per_expert
+    assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+
+
+def test_mxfp4_expert_plan():
+    """MXFP4 expert plans: each expert matrix (routed and shared) is packed E2M1 pairs
+    [.., cols / 2] followed by its E8M0 scales [.., cols / 32]; every other weight stays bf16;
+    other families and widths that are not multiples of 32 are refused."""
+    p, cfg = plan("moe_4k_mxfp4")
+    d = {x["name"]: x for x in p.weight_descs()}
+    names = [x["name"] for x in p.weight_descs()]
+    E, F, H = cfg["n_routed"], cfg["expert_ffn"], cfg["hidden"]
+    assert d["layers.0.experts.w_gate"]["dtype"] == "fp4x2" and tuple(d["layers.0.experts.w_gate"]["shape"]) == (E, F, H // 2)
+    assert d["layers.0.experts.w_down.scale"]["dtype"] == "e8m0" and tuple(d["layers.0.experts.w_down.scale"]["shape"]) == (E, H, F // 32)
+    assert tuple(d["layers.0.shared.w_down"]["shape"]) == (H, F // 2)
+    assert names.index("layers.0.shared.w_up.scale") == names.index("layers.0.shared.w_up") + 1
+    assert d["layers.0.router"]["dtype"] == "bf16" and d["layers.0.wq_a"]["dtype"] == "bf16"
+    for name, over in [("moe_tiny_mxfp4", {"expert_ffn": 48}), ("moe_tiny_mxfp4", {"hidden": 264}), ("mla_tiny", {"weights": "mxfp4"}),
+                       ("tiny", {"weights": "mxfp4"})]:
+        with pytest.raises(B.DecError) as ei:
+            plan(name, **over)
+        assert ei.value.status == -2
 
 
 def test_mla_attention_splits():
