@@ -380,7 +380,7 @@ __device__ __forceinline__ int pad512(int k) { return (k + kChunkCols - 1) / kCh
 // columns; 2048 for MXFP4, ES = 0).
 template <int ES>
 __device__ __forceinline__ int padc(int k) {
-  constexpr int c = ES == 0 ? 2048 : 1024 / ES;
+  constexpr int c = ES == 0 ? 2048 : 1024 / (ES ? ES : 1);
   return (k + c - 1) / c * c;
 }
 // The fp32 row scales of an FP8 matrix: the weight after it in the bound list.
@@ -541,33 +541,46 @@ constexpr int kRingFfn = 3;  // gate/up and (GQA) down: three batches in flight 
 // 2i in the low nibble of byte i. A chunk (one wave load) spans kCols columns.
 template <int ES>
 struct Chunk {
-  static constexpr int kCols = ES == 0 ? 2048 : 1024 / ES;  // columns per chunk
-  static constexpr int kLane = ES == 0 ? 32 : 16 / ES;      // columns per lane
+  static constexpr int kCols = ES == 0 ? 2048 : 1024 / (ES ? ES : 1);  // columns per chunk
+  static constexpr int kLane = ES == 0 ? 32 : 16 / (ES ? ES : 1);      // columns per lane
   // bytes of `cols` consecutive weights of a row
   __device__ static __forceinline__ size_t bytes(int cols) { return ES == 0 ? (size_t)cols / 2 : (size_t)cols * ES; }
   // acc0/acc1 += the lane's weights . x (xp: the lane's kLane inputs in LDS)
-  __device__ static __forceinline__ void dot(const u4& w, uint32_t sb, const float* xp, float& acc0, float& acc1) {
+  // MXFP4: a lane's 32 inputs are 128 bytes of LDS, 128 bytes from the next lane's, so lanes
+  // reading the same quad of their inputs together would all hit the same four banks. Each lane
+  // instead takes its eight quads starting at its own quad `rot` (lanes 8 apart differ by one,
+  // so any 8 or 16 consecutive lanes read distinct banks), and its weights are rotated to match.
+  __device__ static __forceinline__ int rot_of(int lane) { return (lane + (lane >> 3)) & 7; }
+  // quad J of the rotated weights (bytes 2 (J & 1), 2 (J & 1) + 1 of r[J / 2]) times input quad (J + rot) & 7
+  template <int J>
+  __device__ static __forceinline__ void quad(const uint32_t (&r)[4], float sc, const float* xp, int rot, float& acc0, float& acc1) {
+    const f4 x = *(const f4*)(xp + 4 * ((J + rot) & 7));
+    const f2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r[J >> 1], sc, 2 * (J & 1));
+    const f2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r[J >> 1], sc, 2 * (J & 1) + 1);
+    acc0 = fmaf(e0.x, x.x, acc0);
+    acc1 = fmaf(e0.y, x.y, acc1);
+    acc0 = fmaf(e1.x, x.z, acc0);
+    acc1 = fmaf(e1.y, x.w, acc1);
+  }
+  __device__ static __forceinline__ void dot(const u4& w, uint32_t sb, const float* xp, float& acc0, float& acc1, int rot = 0) {
     if constexpr (ES == 0) {
       // hardware E2M1 -> fp32 conversion of one byte (two elements) per instruction, scaled by
       // the block's power of two 2^(sb - 127)
       const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)(sb & 0xffu) - 127);
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f4 xa = *(const f4*)(xp + 8 * q), xb = *(const f4*)(xp + 8 * q + 4);
-        const f2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 0);
-        const f2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 1);
-        const f2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 2);
-        const f2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[q], sc, 3);
-        acc0 = fmaf(e0.x, xa.x, acc0);
-        acc1 = fmaf(e0.y, xa.y, acc1);
-        acc0 = fmaf(e1.x, xa.z, acc0);
-        acc1 = fmaf(e1.y, xa.w, acc1);
-        acc0 = fmaf(e2.x, xb.x, acc0);
-        acc1 = fmaf(e2.y, xb.y, acc1);
-        acc0 = fmaf(e3.x, xb.z, acc0);
-        acc1 = fmaf(e3.y, xb.w, acc1);
-      }
+      // rotate the eight 16-bit quads: quad j of r[] is quad (j + rot) & 7 of w
+      const bool r4 = rot & 4, r2 = rot & 2, r1 = rot & 1;
+      const uint32_t b0 = r4 ? w.z : w.x, b1 = r4 ? w.w : w.y, b2 = r4 ? w.x : w.z, b3 = r4 ? w.y : w.w;
+      const uint32_t c0 = r2 ? b1 : b0, c1 = r2 ? b2 : b1, c2 = r2 ? b3 : b2, c3 = r2 ? b0 : b3;
+      const uint32_t r[4] = {r1 ? __builtin_amdgcn_alignbit(c1, c0, 16) : c0, r1 ? __builtin_amdgcn_alignbit(c2, c1, 16) : c1,
+                             r1 ? __builtin_amdgcn_alignbit(c3, c2, 16) : c2, r1 ? __builtin_amdgcn_alignbit(c0, c3, 16) : c3};
+      quad<0>(r, sc, xp, rot, acc0, acc1);
+      quad<1>(r, sc, xp, rot, acc0, acc1);
+      quad<2>(r, sc, xp, rot, acc0, acc1);
+      quad<3>(r, sc, xp, rot, acc0, acc1);
+      quad<4>(r, sc, xp, rot, acc0, acc1);
+      quad<5>(r, sc, xp, rot, acc0, acc1);
+      quad<6>(r, sc, xp, rot, acc0, acc1);
+      quad<7>(r, sc, xp, rot, acc0, acc1);
     } else if constexpr (ES == 2) {
       const f4 x0 = *(const f4*)xp, x1 = *(const f4*)(xp + 4);
       acc0 = fmaf(bf_lo(w.x), x0.x, acc0);
@@ -658,7 +671,7 @@ struct StreamT {
           // lanes past the row's end hold no elements (the staged input is not padded to whole
           // 2048-column chunks): their products are dropped
           float p0 = 0.f, p1 = 0.f;
-          C::dot(bf[i], sb[i], xs + cxo + cc * C::kCols + lane * C::kLane, p0, p1);
+          C::dot(bf[i], sb[i], xs + cxo + cc * C::kCols + lane * C::kLane, p0, p1, C::rot_of(lane));
           const bool in = cc * C::kCols + lane * C::kLane < K;
           acc0 += in ? p0 : 0.f;
           acc1 += in ? p1 : 0.f;
