@@ -48,7 +48,9 @@ a stacked expert tensor, so the MoE oracle reads only the experts it routes to.
 Low-precision weights (the survey's "next" row on cutting bytes per token; the pages name
 the lever -- fewer bytes per token -- not a format): a linear matrix given as uint8 is OCP
 FP8 E4M3 bytes, and W(name + ".scale") holds one fp32 scale per row; the matrix the layer
-multiplies by is scale[r] * e4m3(bytes[r, c]), decoded exactly (decode_e4m3).
+multiplies by is scale[r] * e4m3(bytes[r, c]), decoded exactly (decode_e4m3). In the latent
+families every linear matrix but the per-head absorption matrices (w_uk, w_uv) and the
+router may be FP8 this way; a stacked expert tensor has one scale per row of every expert.
 """
 from __future__ import annotations
 
@@ -482,8 +484,12 @@ def mla_attention_absorbed(cfg: dict, W: Callable, l: int, q_nope, q_rope, lat) 
 
 
 def _expert_w64(cfg: dict, W: Callable, name: str, index=None) -> np.ndarray:
-    """An expert matrix as float64: bf16 bits, or (weights "mxfp4") MXFP4 rows with the
-    E8M0 scales in name + ".scale"."""
+    """An expert matrix as float64: bf16 bits, (weights "fp8") E4M3 rows each times its fp32
+    scale in name + ".scale", or (weights "mxfp4") MXFP4 rows with the E8M0 scales in
+    name + ".scale"."""
+    if cfg.get("weights") == "fp8":
+        sc = np.asarray(W(name + ".scale") if index is None else W(name + ".scale", index), dtype=np.float64)
+        return decode_e4m3(W(name) if index is None else W(name, index)) * sc[..., None]
     if cfg.get("weights") != "mxfp4":
         return _w64(W, name, index)
     sc = W(name + ".scale") if index is None else W(name + ".scale", index)

@@ -14,7 +14,8 @@ available; these shapes stand in for them):
   * norm gains = 1 ("ones") or ~ N(mean, std) for the gain-pinning variants;
   * cached K/V (or latent c||k_pe) ~ N(0, kv_std) on positions [0, kv_len), slot kv_len = 0;
   * x ~ N(0, x_std) in bf16; router bias ~ N(0, router_bias_std) in fp32.
-  * configs with "weights": "fp8" (GQA only): every linear matrix is drawn the same way in
+  * configs with "weights": "fp8": every linear matrix (latent families: all but the per-head
+    absorption matrices and the router, FP8_KEEP_BF16) is drawn the same way in
     fp32, then each row r is stored as E4M3 bytes of row / scale[r] (round to nearest
     even) with scale[r] = max|row| / 448 in fp32, so the row's largest value maps to the
     largest finite E4M3 magnitude. Quantisation is input generation: the decode path only
@@ -113,12 +114,18 @@ def weight_specs(cfg: dict) -> List[TensorSpec]:
         return out
     q: List[TensorSpec] = []
     for s in out:
-        if s.init == "weight":
+        if s.init == "weight" and not s.name.endswith(FP8_KEEP_BF16):
             q.append(TensorSpec(s.name, s.shape, FP8, "weight"))
-            q.append(TensorSpec(s.name + ".scale", (s.shape[0],), FP32, "scale"))
+            q.append(TensorSpec(s.name + ".scale", s.shape[:-1], FP32, "scale"))
         else:
             q.append(s)
     return q
+
+
+# Matrices that stay bf16 under "weights": "fp8" (latent families): the per-head absorption
+# matrices (2 MB a layer, read by the attention's own loops) and the router (its logits decide
+# the expert choice).
+FP8_KEEP_BF16 = (".w_uk", ".w_uv", ".router")
 
 
 def _weight_specs_bf16(cfg: dict) -> List[TensorSpec]:
@@ -280,17 +287,19 @@ def generate(cfg: dict, seed: int = 0, device="cpu", kv_len: Optional[int] = Non
             weights[s.name] = q.view(lead + (kk // 2,))
             weights[s.name + ".scale"] = sc.view(lead + (kk // 32,))
         elif s.init == "weight" and s.dtype == FP8:
-            q = torch.empty(s.shape, dtype=torch.uint8, device=dev)
-            sc = torch.empty(s.shape[0], dtype=torch.float32, device=dev)
-            rows = max(1, (1 << 26) // s.shape[1])
-            for r0 in range(0, s.shape[0], rows):
-                r1 = min(s.shape[0], r0 + rows)
-                w32 = torch.randn((r1 - r0, s.shape[1]), generator=gen, device=dev, dtype=torch.float32)
+            kk = s.shape[-1]
+            nrow = s.numel // kk
+            q = torch.empty((nrow, kk), dtype=torch.uint8, device=dev)
+            sc = torch.empty(nrow, dtype=torch.float32, device=dev)
+            rows = max(1, (1 << 26) // kk)
+            for r0 in range(0, nrow, rows):
+                r1 = min(nrow, r0 + rows)
+                w32 = torch.randn((r1 - r0, kk), generator=gen, device=dev, dtype=torch.float32)
                 w32.mul_(init["weight_std"])
                 q[r0:r1], sc[r0:r1] = _quantize_e4m3_rows(torch, w32)
                 del w32
-            weights[s.name] = q
-            weights[s.name + ".scale"] = sc
+            weights[s.name] = q.view(s.shape)
+            weights[s.name + ".scale"] = sc.view(s.shape[:-1])
         elif s.init == "weight":
             weights[s.name] = _bf16_randn(torch, s.shape, init["weight_std"], gen, dev)
         elif s.init == "gain":
