@@ -31,6 +31,10 @@ WORKLOADS = {
     "tiny": "tiny decoder (2 layers, hidden 256), batch 1, KV 128",
     "8b_4k_fp8": "the 8B-shaped decoder with every linear matrix in FP8 E4M3 (one fp32 scale per row), "
                  "batch 1, one decode token over a 4096-position bf16 KV cache",
+    "mla_8k_fp8": "the MLA stack with every linear matrix but the absorption matrices in FP8 E4M3 (one fp32 scale "
+                  "per row), batch 1, one decode token over an 8192-position bf16 latent cache",
+    "moe_4k_fp8": "the MLA + MoE stack with every linear matrix but the absorption matrices and the router in FP8 "
+                  "E4M3 (one fp32 scale per row), batch 1, one decode token over a 4096-position bf16 latent cache",
     "moe_4k_mxfp4": "the MLA + MoE stack with every expert matrix in MXFP4 (E2M1 elements, one E8M0 scale per "
                     "32), other weights bf16, batch 1, one decode token over a 4096-position latent cache",
 }

@@ -829,17 +829,18 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
   typename std::conditional<FLAT, StreamFlatT<ES>, StreamT<ES>>::type s;
   u4 buf[R][NB];
   uint32_t sbuf[R][NB];  // MXFP4 block scales (unused for the other formats)
-  if constexpr (ES == 1) {
-    // FP8 rows: wave 0 (no weight loads in flight) puts the task's row scales into LDS; the
-    // barrier of the dependency wait publishes them
-    if (threadIdx.x < 64)
-      for (int j = (int)threadIdx.x; j < nrows; j += 64) b.scl[j] = rm.scale(j);
-  }
   if (threadIdx.x < 64) stage.before(b);
   if (pre_deps > 0) {
     if (!wait_deps(A, b, t, 0, pre_deps)) return false;
     pre();
     __syncthreads();
+  }
+  if constexpr (ES == 1) {
+    // FP8 rows: wave 0 (no weight loads in flight) puts the task's row scales into LDS (after
+    // `pre`, which stages what a run-time row map reads); the barrier of the dependency wait
+    // publishes them
+    if (threadIdx.x < 64)
+      for (int j = (int)threadIdx.x; j < nrows; j += 64) b.scl[j] = rm.scale(j);
   }
   if (prefetch) {
     fill_rows<ES>(rm, ja, jb, b.rowp, b.xoffp, b.srowp);
@@ -903,6 +904,13 @@ __device__ __forceinline__ bool run_gemv(const EngineArgs& A, Blk& b, const Task
 }
 
 // ------------------------------------------------------------------ row maps
+
+// a when sel is false, else b: by arithmetic on the addresses (a per-lane choice between two
+// pointers written as a select is placed in scratch memory by the compiler)
+__device__ __forceinline__ const uint8_t* pick2(bool sel, const void* a, const void* b) {
+  const uintptr_t x = (uintptr_t)a;
+  return (const uint8_t*)(x + (uintptr_t)sel * ((uintptr_t)b - x));
+}
 
 // Row maps give each task row's address; es = bytes per weight (2 bf16, 1 FP8), and for FP8
 // rows `scale` reads the row's fp32 scale.
@@ -1335,14 +1343,15 @@ __device__ __forceinline__ bool task_attn_hd(const EngineArgs& A, Blk& b, const 
   }
 }
 
+template <int ES>
 __device__ __forceinline__ bool task_oproj(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = (A.arch == 0) ? A.nq * A.hd : A.nq * A.dv;
-  const RmPlain rm{wp<uint16_t>(A, L.w[LW_WO]), K, t.u0};
+  const RmPlain rm{wp<uint8_t>(A, L.w[LW_WO]), K, t.u0, ES, wscale<ES>(A, L.w[LW_WO])};
   const int xin = L.act[LA_X_IN];
-  return run_gemv(
+  return run_gemv<2, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      stage_vec(L.act[LA_ATTN], nullptr, K, pad512(K), nullptr, 0.f, false, A.arch != 0),
+      stage_vec(L.act[LA_ATTN], nullptr, K, padc<ES>(K), nullptr, 0.f, false, A.arch != 0),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int rr = t.u0 + i;
@@ -1740,25 +1749,31 @@ __device__ __forceinline__ void qop_store(const Blk& b, int qop, int h, int k, f
 }
 
 struct RmMlaA {  // rows [0, ql) of W_DQ, then the rows of W_DKV
-  const uint16_t *wqa, *wkva;
+  const void *wqa, *wkva;
   int K, ql, r0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  int es = 2;
+  const float *sqa = nullptr, *skva = nullptr;  // FP8: row scales
+  __device__ __forceinline__ const void* row(int j) const {
     const int r = r0 + j, sel = r >= ql ? 1 : 0;
-    const uintptr_t a = (uintptr_t)wqa;
-    const uintptr_t base = a + (uintptr_t)sel * ((uintptr_t)wkva - a);
-    return (const uint16_t*)base + (size_t)(r - sel * ql) * K;
+    return pick2(sel, wqa, wkva) + (size_t)(r - sel * ql) * K * es;
+  }
+  __device__ __forceinline__ float scale(int j) const {
+    const int r = r0 + j;
+    return r < ql ? sqa[r] : skva[r - ql];
   }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
 // x^ = RMSNorm(x); [cq_raw | kv_a] = [W_DQ; W_DKV] x^
+template <int ES>
 __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.hidden, ql = A.ql;
-  const RmMlaA rm{wp<uint16_t>(A, L.w[LW_WQA]), wp<uint16_t>(A, L.w[LW_WKVA]), K, ql, t.u0};
-  return run_gemv(
+  const RmMlaA rm{wp<uint8_t>(A, L.w[LW_WQA]), wp<uint8_t>(A, L.w[LW_WKVA]), K, ql, t.u0, ES, wscale<ES>(A, L.w[LW_WQA]),
+                  wscale<ES>(A, L.w[LW_WKVA])};
+  return run_gemv<2, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
-      stage_vec(L.act[LA_X_IN], b.x, K, pad512(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps),
+      stage_vec(L.act[LA_X_IN], b.x, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int r = t.u0 + i;
@@ -1771,24 +1786,29 @@ __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const Ta
 // W_UQ row pairs: unit (head h, i) is rows (i, i + dn/2) of the head's nope part for
 // i < dn/2, else the RoPE pair (dn + k, dn + k + dr/2), k = i - dn/2.
 struct RmMlaB {
-  const uint16_t* W;
+  const uint8_t* W;
   int K, dn, dr, uh, u0;
-  __device__ __forceinline__ const uint16_t* row(int j) const {
+  int es = 2;
+  const float* S = nullptr;  // FP8: row scales
+  __device__ __forceinline__ int rix(int j) const {  // the task row's row of W_UQ
     const int u = u0 + (j >> 1), h = u / uh, i = u - h * uh, hn = dn >> 1;
     const int rr = i < hn ? i + (j & 1) * hn : dn + (i - hn) + (j & 1) * (dr >> 1);
-    return W + ((size_t)h * (dn + dr) + rr) * K;
+    return h * (dn + dr) + rr;
   }
+  __device__ __forceinline__ const void* row(int j) const { return W + (size_t)rix(j) * K * es; }
+  __device__ __forceinline__ float scale(int j) const { return S[rix(j)]; }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
 
 // cq = RMSNorm(cq_raw); [q_nope | q_rope] = W_UQ cq, RoPE on q_rope
+template <int ES>
 __device__ __forceinline__ bool task_mla_b(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int K = A.ql, dn = A.dn, dr = A.dr, uh = dn / 2 + dr / 2;
-  const RmMlaB rm{wp<uint16_t>(A, L.w[LW_WQB]), K, dn, dr, uh, t.u0};
-  return run_gemv(
+  const RmMlaB rm{wp<uint8_t>(A, L.w[LW_WQB]), K, dn, dr, uh, t.u0, ES, wscale<ES>(A, L.w[LW_WQB])};
+  return run_gemv<2, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
-      stage_vec(L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps),
+      stage_vec(L.act[LA_CQ], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int u = t.u0 + i, h = u / uh, k = u - h * uh;
@@ -2181,13 +2201,6 @@ __device__ __forceinline__ bool task_router(const EngineArgs& A, Blk& b, const T
       });
 }
 
-// a when sel is false, else b: by arithmetic on the addresses (a per-lane choice between two
-// pointers written as a select is placed in scratch memory by the compiler)
-__device__ __forceinline__ const uint8_t* pick2(bool sel, const void* a, const void* b) {
-  const uintptr_t x = (uintptr_t)a;
-  return (const uint8_t*)(x + (uintptr_t)sel * ((uintptr_t)b - x));
-}
-
 // Expert matrices in MXFP4 (ES = 0): rows of K / 2 packed bytes, and K / 32 E8M0 scale bytes
 // per row in the weight bound after the matrix. Unit u -> (gate row u, up row u) of the
 // shared experts' [ns * eff, hidden] matrices.
@@ -2224,7 +2237,8 @@ __device__ __forceinline__ bool task_shared_gu(const EngineArgs& A, Blk& b, cons
                        wp<uint8_t>(A, L.w[LW_SUP] + 1), A.hidden, t.u0};
     return shared_gu<ES>(A, b, t, rm);
   } else {
-    const RmGateUp rm{wp<uint16_t>(A, L.w[LW_SGATE]), wp<uint16_t>(A, L.w[LW_SUP]), A.hidden, t.u0};
+    const RmGateUp rm{wp<uint8_t>(A, L.w[LW_SGATE]), wp<uint8_t>(A, L.w[LW_SUP]), A.hidden, t.u0, ES,
+                      wscale<ES>(A, L.w[LW_SGATE]), wscale<ES>(A, L.w[LW_SUP])};
     return shared_gu<ES>(A, b, t, rm);
   }
 }
@@ -2312,7 +2326,7 @@ struct RmExpertGU {
   const uint8_t *Wg, *Wu;
   const int* ids;  // LDS
   int K, F, u0;
-  const uint8_t *Sg = nullptr, *Su = nullptr;  // MXFP4: the block scales
+  const uint8_t *Sg = nullptr, *Su = nullptr;  // MXFP4: the block scales; FP8: the fp32 row scales
   __device__ __forceinline__ size_t rix(int j) const {  // the row's index in [E * F] rows
     const int u = u0 + (j >> 1), k = u / F, i = u - k * F;
     return (size_t)ids[k] * F + i;
@@ -2320,8 +2334,9 @@ struct RmExpertGU {
   __device__ __forceinline__ const void* row(int j) const {
     const uintptr_t g = (uintptr_t)Wg;
     const uintptr_t base = g + (uintptr_t)(j & 1) * ((uintptr_t)Wu - g);
-    return (const uint8_t*)base + rix(j) * (ES == 0 ? K / 2 : (size_t)K * 2);
+    return (const uint8_t*)base + rix(j) * (ES == 0 ? K / 2 : (size_t)K * ES);
   }
+  __device__ __forceinline__ float scale(int j) const { return ((const float*)pick2(j & 1, Sg, Su))[rix(j)]; }
   __device__ __forceinline__ const void* srow(int j) const { return pick2(j & 1, Sg, Su) + rix(j) * (K / 32); }
   __device__ __forceinline__ int xoff(int) const { return 0; }
 };
@@ -2342,8 +2357,8 @@ __device__ __forceinline__ bool task_expert_gu(const EngineArgs& A, Blk& b, cons
   const int K = A.hidden, F = A.eff;
   int* ids = reinterpret_cast<int*>(b.scr);
   const RmExpertGU<ES> rm{wp<uint8_t>(A, L.w[LW_EGATE]), wp<uint8_t>(A, L.w[LW_EUP]), ids, K, F, t.u0,
-                          ES == 0 ? wp<uint8_t>(A, L.w[LW_EGATE] + 1) : nullptr,
-                          ES == 0 ? wp<uint8_t>(A, L.w[LW_EUP] + 1) : nullptr};
+                          ES != 2 ? wp<uint8_t>(A, L.w[LW_EGATE] + 1) : nullptr,
+                          ES != 2 ? wp<uint8_t>(A, L.w[LW_EUP] + 1) : nullptr};
   return run_gemv<2, false, ES>(
       A, b, t, rm, 2 * (t.u1 - t.u0), K, 1, true,
       stage_vec(L.act[LA_H], nullptr, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_FFN_NORM]), A.eps),
@@ -2363,7 +2378,7 @@ struct RmMoeDown {
   const uint8_t *Ws, *Wd;
   const int* ids;  // LDS
   int ns, G, F, Fp, d, r0;
-  const uint8_t *Ss = nullptr, *Sd = nullptr;  // MXFP4: the block scales
+  const uint8_t *Ss = nullptr, *Sd = nullptr;  // MXFP4: the block scales; FP8: the fp32 row scales
   // element offset of task row j's segment: shared experts' segments lie side by side in one
   // row of W_sdown; a routed expert's is a row of its own W_down
   __device__ __forceinline__ bool shared(int j) const { return j % G < ns; }
@@ -2373,7 +2388,13 @@ struct RmMoeDown {
     return ((size_t)ids[sgm - ns] * d + r) * F;
   }
   __device__ __forceinline__ const void* row(int j) const {
-    return pick2(!shared(j), Ws, Wd) + (ES == 0 ? eoff(j) / 2 : eoff(j) * 2);
+    return pick2(!shared(j), Ws, Wd) + (ES == 0 ? eoff(j) / 2 : eoff(j) * ES);
+  }
+  // FP8: a shared expert's segment is part of one row r of W_sdown (scale r); a routed one is
+  // row r of its expert's W_down
+  __device__ __forceinline__ float scale(int j) const {
+    const int q = j / G, sgm = j - q * G, r = r0 + q;
+    return shared(j) ? ((const float*)Ss)[r] : ((const float*)Sd)[(size_t)ids[sgm - ns] * d + r];
   }
   __device__ __forceinline__ const void* srow(int j) const { return pick2(!shared(j), Ss, Sd) + eoff(j) / 32; }
   __device__ __forceinline__ int xoff(int j) const { return (j % G) * Fp; }
@@ -2384,12 +2405,12 @@ struct RmMoeDown {
 template <int ES>
 __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
-  const int F = A.eff, Fp = ES == 0 ? (F + 255) / 256 * 256 : pad512(F), ns = A.n_shared, Kt = A.top_k, G = ns + Kt, d = A.hidden;
+  const int F = A.eff, Fp = ES == 0 ? (F + 255) / 256 * 256 : padc<ES>(F), ns = A.n_shared, Kt = A.top_k, G = ns + Kt, d = A.hidden;
   int* ids = reinterpret_cast<int*>(b.scr);
   float* wk = b.scr + 64;
   const RmMoeDown<ES> rm{wp<uint8_t>(A, L.w[LW_SDOWN]), wp<uint8_t>(A, L.w[LW_EDOWN]), ids, ns, G, F, Fp, d, t.u0,
-                         ES == 0 ? wp<uint8_t>(A, L.w[LW_SDOWN] + 1) : nullptr,
-                         ES == 0 ? wp<uint8_t>(A, L.w[LW_EDOWN] + 1) : nullptr};
+                         ES != 2 ? wp<uint8_t>(A, L.w[LW_SDOWN] + 1) : nullptr,
+                         ES != 2 ? wp<uint8_t>(A, L.w[LW_EDOWN] + 1) : nullptr};
   return run_gemv<2, false, ES>(
       A, b, t, rm, G * (t.u1 - t.u0), F, G, true,
       stage_fn([&] {
@@ -3083,10 +3104,12 @@ __device__ __forceinline__ const EngineArgs& args_view() {
   return *(const EngineArgs*)p;
 }
 
-// ES: the weights' element format -- GQA: every linear matrix (2 bf16, 1 FP8); MLA family:
-// the expert matrices (2 bf16, 0 MXFP4), every other matrix bf16.
+// ES: the weights' element format -- GQA: every linear matrix (2 bf16, 1 FP8); latent family:
+// 2 bf16, 1 FP8 (every linear matrix but the absorption matrices and the router), 0 MXFP4
+// experts (every other matrix bf16).
 template <bool MLA, int RUN, int ES = 2, int MT = 1>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
+  constexpr int ED = ES == 1 ? 1 : 2;  // the latent family's non-expert matrices
   extern __shared__ f4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
   Blk b;
@@ -3193,16 +3216,16 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       }
     } else {
       switch (t.type) {
-        case T_MLA_A: ok = task_mla_a(A, b, t); break;
-        case T_MLA_B: ok = task_mla_b(A, b, t); break;
+        case T_MLA_A: ok = task_mla_a<ED>(A, b, t); break;
+        case T_MLA_B: ok = task_mla_b<ED>(A, b, t); break;
         case T_MLA_KVAPP: gemv = false; ok = task_mla_kvapp(A, b, t); break;
         case T_MLA_ABSORB: gemv = false; ok = task_mla_absorb(A, b, t); break;
         case T_MLA_ATTN: gemv = false; ok = task_mla_attn(A, b, t); break;
         case T_MLA_UV: gemv = false; ok = task_mla_uv(A, b, t); break;
-        case T_OPROJ: ok = task_oproj(A, b, t); break;
-        case T_GATEUP: ok = task_gateup<2>(A, b, t); break;
-        case T_DOWN: ok = task_down<false, 2>(A, b, t); break;
-        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic, 2>(A, b, t); break;
+        case T_OPROJ: ok = task_oproj<ED>(A, b, t); break;
+        case T_GATEUP: ok = task_gateup<ED>(A, b, t); break;
+        case T_DOWN: ok = task_down<false, ED>(A, b, t); break;
+        case T_LMHEAD: ok = task_lmhead<RUN == kRunDynamic, ED>(A, b, t); break;
         case T_ARGMAX:
           gemv = false;
           if constexpr (RUN == kRunDynamic) ok = task_argmax(A, b, t);
@@ -3267,6 +3290,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(Eng
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_dyn(EngineArgs A) {
   engine_body<true, kRunDynamic>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_f8(EngineArgs A) {
+  engine_body<true, kRunStep, 1>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_f8_dyn(EngineArgs A) {
+  engine_body<true, kRunDynamic, 1>(A);
+}
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_x4(EngineArgs A) {
   engine_body<true, kRunStep, 0>(A);
 }
@@ -3298,6 +3327,7 @@ static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1) {
   if (ntok == 3) return (const void*)dec::dec_engine_gqa_v3;
   if (ntok == 4) return (const void*)dec::dec_engine_gqa_v4;
   if (wfmt == 2) return run == 2 ? (const void*)dec::dec_engine_mla_x4_dyn : (const void*)dec::dec_engine_mla_x4;
+  if (wfmt == 1 && arch != 0) return run == 2 ? (const void*)dec::dec_engine_mla_f8_dyn : (const void*)dec::dec_engine_mla_f8;
   if (wfmt) return run == 2 ? (const void*)dec::dec_engine_gqa_f8_dyn : (const void*)dec::dec_engine_gqa_f8;
   if (run == 1) return arch == 0 ? (const void*)dec::dec_engine_gqa_stages : (const void*)dec::dec_engine_mla_stages;
   if (run == 2) return arch == 0 ? (const void*)dec::dec_engine_gqa_dyn : (const void*)dec::dec_engine_mla_dyn;
@@ -3308,8 +3338,8 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
                                                                          int run, bool cooperative, hipStream_t stream) {
   static int configured_lds[2][8] = {{-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1}};
   const int k = args->arch == 0 ? 0 : 1;
-  // FP8 weights: the GQA family; MXFP4 experts: the latent family; neither in stage launches
-  if (run < 0 || run > 2 || (args->wfmt == 1 && k != 0) || (args->wfmt == 2 && k != 1) || (args->wfmt && run == 1))
+  // MXFP4 experts: the latent family; FP8 or MXFP4 weights: no stage launches
+  if (run < 0 || run > 2 || (args->wfmt == 2 && k != 1) || (args->wfmt && run == 1))
     return hipErrorInvalidValue;
   if (args->ntok > 1 && (k != 0 || run != 0 || args->wfmt || args->ntok > dec::kMaxVerifyTokens)) return hipErrorInvalidValue;
   const void* fn = engine_fn(args->arch, run, args->wfmt, args->ntok);

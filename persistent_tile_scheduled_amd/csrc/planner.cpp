@@ -187,9 +187,11 @@ struct Builder {
         return fail(DEC_E_SHAPE, "MXFP4 expert weights need hidden and expert_ffn multiples of 32", st);
     }
     if (q.weight_format == DEC_WEIGHTS_FP8_E4M3) {
-      if (q.arch != DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "FP8 weights: GQA family only", st);
-      if (q.hidden % 16 || q.ffn % 16 || (q.n_q_heads * q.head_dim) % 16)
+      if (q.arch == DEC_ARCH_GQA && (q.hidden % 16 || q.ffn % 16 || (q.n_q_heads * q.head_dim) % 16))
         return fail(DEC_E_SHAPE, "FP8 weights need hidden, ffn and n_q_heads * head_dim multiples of 16", st);
+      if (q.arch != DEC_ARCH_GQA && (q.hidden % 16 || q.ffn % 16 || q.q_lora_rank % 16 || (q.n_q_heads * q.v_head) % 16 ||
+                                     q.expert_ffn % 16))
+        return fail(DEC_E_SHAPE, "FP8 weights need hidden, ffn, q_lora_rank, n_q_heads * v_head and expert_ffn multiples of 16", st);
     }
     if (!(q.rms_eps > 0.f) || !(q.rope_theta > 1.0)) return fail(DEC_E_SHAPE, "need rms_eps > 0 and rope_theta > 1", st);
     if (n < 0) return fail(DEC_E_CAPACITY, "kv_len < 0", st);
@@ -241,6 +243,12 @@ struct Builder {
   // An expert matrix [.., rows, cols]: bf16, or MXFP4 (packed pairs [.., rows, cols / 2]) followed
   // by its E8M0 block scales [.., rows, cols / 32] (the engine finds them at the index + 1).
   void add_expert(const std::string& name, std::vector<int64_t> dims) {
+    if (fp8()) {  // E4M3 bytes and one fp32 scale per row of every expert
+      std::vector<int64_t> sc(dims.begin(), dims.end() - 1);
+      add_weight(name, DEC_DTYPE_FP8, dims);
+      add_weight(name + ".scale", DEC_DTYPE_FP32, sc);
+      return;
+    }
     if (!mx4()) {
       add_weight(name, DEC_DTYPE_BF16, dims);
       return;
@@ -286,14 +294,15 @@ struct Builder {
       } else {
         const int nh = s.n_q_heads;
         W(LW_ATTN_NORM, "attn_norm", DEC_DTYPE_BF16, {d});
-        W(LW_WQA, "wq_a", DEC_DTYPE_BF16, {s.q_lora_rank, d});
+        // (FP8: every linear matrix but the per-head absorption matrices and the router)
+        M(LW_WQA, "wq_a", s.q_lora_rank, d);
         W(LW_QNORM, "q_norm", DEC_DTYPE_BF16, {s.q_lora_rank});
-        W(LW_WQB, "wq_b", DEC_DTYPE_BF16, {(int64_t)nh * (s.qk_nope + s.qk_rope), s.q_lora_rank});
-        W(LW_WKVA, "wkv_a", DEC_DTYPE_BF16, {s.kv_lora_rank + s.qk_rope, d});
+        M(LW_WQB, "wq_b", (int64_t)nh * (s.qk_nope + s.qk_rope), s.q_lora_rank);
+        M(LW_WKVA, "wkv_a", s.kv_lora_rank + s.qk_rope, d);
         W(LW_KVNORM, "kv_norm", DEC_DTYPE_BF16, {s.kv_lora_rank});
         W(LW_WUK, "w_uk", DEC_DTYPE_BF16, {nh, s.qk_nope, s.kv_lora_rank});
         W(LW_WUV, "w_uv", DEC_DTYPE_BF16, {nh, s.v_head, s.kv_lora_rank});
-        W(LW_WO, "wo", DEC_DTYPE_BF16, {d, (int64_t)nh * s.v_head});
+        M(LW_WO, "wo", d, (int64_t)nh * s.v_head);
       }
       W(LW_FFN_NORM, "ffn_norm", DEC_DTYPE_BF16, {d});
       if (s.arch == DEC_ARCH_MOE) {
@@ -576,7 +585,7 @@ struct Builder {
     L.act[LA_SACT] = (int)act(p + "shared_act", std::max(SF, 1));
     L.act[LA_ACT] = (int)act(p + "expert_act", (int64_t)K * F);
     if (!mx4()) {
-      need_xs((int64_t)(s.n_shared + K) * align_up(F, kChunkCols));
+      need_xs((int64_t)(s.n_shared + K) * align_up(F, chunk_cols()));
     } else {
       // MXFP4 segments are padded to 256 columns (the staging copy's unit); a wave's
       // 2048-column chunk may read past the last segment (those lanes' products are dropped),

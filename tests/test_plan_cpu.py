@@ -17,7 +17,8 @@ MI355X = B.device_info()
 GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", "8b_4k", "8b_32k", "tiny_hd256_g3",
                "tiny_fp8", "tiny_ragged_fp8", "small_gqa_fp8", "8b_4k_fp8"]
 MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k", "moe_wide_tiny", "moe_max_route",
-               "moe_tiny_mxfp4", "moe_small_mxfp4", "moe_4k_mxfp4", "moe_max_route_mxfp4"]
+               "moe_tiny_mxfp4", "moe_small_mxfp4", "moe_4k_mxfp4", "moe_max_route_mxfp4",
+               "mla_tiny_fp8", "mla_small_fp8", "mla_8k_fp8", "moe_tiny_fp8", "moe_small_fp8", "moe_4k_fp8"]
 
 
 def plan(name, dev=MI355X, **over):
@@ -315,7 +316,7 @@ def test_dynamic_latent_plan_layout(name, max_len):
 
 def test_dynamic_plan_errors():
     with pytest.raises(B.DecError) as ei:
-        B.Plan(dict(workloads.get_config("mla_tiny"), weights="fp8"), device=MI355X, max_len=100)
+        B.Plan(dict(workloads.get_config("mla_tiny"), weights="mxfp4"), device=MI355X, max_len=100)  # MXFP4: MoE only
     assert ei.value.status == -2
     with pytest.raises(B.DecError):
         B.Plan(workloads.get_config("tiny"), device=MI355X, max_len=-1)
@@ -341,7 +342,7 @@ def test_fp8_weights_plan():
             plan("tiny_fp8", **over)
         assert ei.value.status == -2
     with pytest.raises(B.DecError) as ei:
-        plan("mla_tiny", weights="fp8")
+        plan("mla_tiny", weights="fp8", q_lora_rank=104)  # FP8 rows need widths that are multiples of 16
     assert ei.value.status == -2
     dyn = B.Plan(workloads.get_config("tiny_fp8"), device=MI355X, max_len=200)
     dd = {x["name"]: x for x in dyn.weight_descs()}
@@ -423,6 +424,25 @@ def test_mla_algorithmic_bytes():
     s = p.sizes()
     per_expert = 3 * cfg["expert_ffn"] * cfg["hidden"] // 2 + 3 * cfg["expert_ffn"] * cfg["hidden"] // 32
     unused = cfg["n_layers"] * (cfg["n_routed"] - cfg["top_k"]) * per_expert
+    assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+
+
+def test_fp8_latent_plan():
+    """FP8 latent-family plans: every linear matrix but w_uk, w_uv and the router is E4M3
+    bytes followed by fp32 row scales (one per row of every expert); the bytes per step count
+    the chosen experts' bytes and scales."""
+    p, cfg = plan("moe_4k_fp8")
+    d = {x["name"]: x for x in p.weight_descs()}
+    E, F, H = cfg["n_routed"], cfg["expert_ffn"], cfg["hidden"]
+    for n in ("wq_a", "wq_b", "wkv_a", "wo", "experts.w_gate", "shared.w_down"):
+        assert d["layers.0." + n]["dtype"] == "fp8" and d["layers.0." + n + ".scale"]["dtype"] == "fp32", n
+    for n in ("w_uk", "w_uv", "router"):
+        assert d["layers.0." + n]["dtype"] == "bf16", n
+    assert tuple(d["layers.0.experts.w_down.scale"]["shape"]) == (E, H)
+    s = p.sizes()
+    per_expert = 3 * F * H + 2 * F * 4 + H * 4
+    unused = cfg["n_layers"] * (E - cfg["top_k"]) * per_expert
+    row = (cfg["kv_lora_rank"] + cfg["qk_rope"]) * 2
     assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
 
 
