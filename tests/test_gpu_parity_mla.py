@@ -1,8 +1,9 @@
 """GPU parity of the MLA and MLA + MoE engine paths against the fp64 oracle (needs an MI355X).
 
-Bars as for the GQA path: relative L2 error <= 1e-2 on every per-layer vector of the trace
-and <= 2e-2 on the step output (these models have no LM head: the output is the last
-hidden state); the appended latent row within one bf16 ulp of the oracle's rounding.
+Bars as for the GQA path: relative L2 error <= TIGHT_TOL (1e-4, inside the contract's 1e-2)
+on every per-layer vector of the trace and <= 2e-2 on the step output (these models have no LM
+head: the output is the last hidden state); the appended latent row within one bf16 ulp of the
+oracle's rounding.
 Expert selection is integer work: the engine's top-k must equal the oracle's selection made
 in fp32 from the engine's own router logits, element by element; against the oracle's fully
 fp64 forward it must match wherever the oracle's top-k margin exceeds what fp32 logits can
@@ -54,10 +55,10 @@ def check_moe_layer(eng, cfg, l, t, W):
     want = {int(e): t["expert_act"][i * F:(i + 1) * F] for i, e in enumerate(t["topk"])}
     for i, e in enumerate(ids.tolist()):
         if e in want:
-            assert rel_l2(acts[i * F:(i + 1) * F], want[e]) <= LAYER_TOL, (l, e)
+            assert rel_l2(acts[i * F:(i + 1) * F], want[e]) <= TIGHT_TOL, (l, e)
 
 
-def check_mla_layer(eng, cfg, l, t, W, kv_bits, tol=LAYER_TOL, same_input=None):
+def check_mla_layer(eng, cfg, l, t, W, kv_bits, tol=TIGHT_TOL, same_input=None):
     names = MLA_TRACE + (DENSE_FFN if cfg["arch"] == "mla" else MOE_FFN)
     errs = {}
     for nm in names:
@@ -210,7 +211,7 @@ def _teacher_forced_mla(name, layers):
         names = MLA_TRACE + (DENSE_FFN if cfg["arch"] == "mla" else MOE_FFN)
         errs = {nm: rel_l2(eng.buffer(f"layers.{l}.{nm}").cpu().numpy()[: t[nm].size], t[nm]) for nm in names}
         print(f"[parity] layer {l} rel errors {errs}", flush=True)
-        assert all(v <= LAYER_TOL for v in errs.values()), errs
+        assert all(v <= TIGHT_TOL for v in errs.values()), errs
         check_kv_slot(cfg, kvl[None], 0, t)
         if cfg["arch"] == "moe":
             check_moe_layer(eng, cfg, l, t, W)
