@@ -10,5 +10,5 @@ from .decode_oracle import (  # noqa: F401
     attend_partial, merge_partials, attend_split, silu, swiglu, route, gqa_layer,
     mla_attention, mla_attention_absorbed, moe_ffn, mla_layer, layer, head, forward,
     dict_weights, kv_group, gqa_verify_layer, verify_forward, decode_e2m1, decode_e8m0, dequant_mxfp4,
-    MX_BLOCK,
+    MX_BLOCK, index_scores, select_positions,
 )

@@ -37,6 +37,12 @@ top-k router). The readings taken where the pages are silent:
       bf16 (round to nearest even), and attention reads the cache, new slot included.
   R13 MLA/MoE configs have no LM head and no final norm: the output is the last hidden
       state.
+  R24 sparse indexer (the audit page: 64 index heads select the top-2048 KV positions; no
+      formula): index key k = W_k x^ (appended to the cache as bf16 after the latent row),
+      head weights w = W_w x^, index queries q_j = (W_q c_q)_j from the normalised query
+      latent; score I_s = sum_j w_j max(0, q_j . k_s) over every position s (the ReLU-gated,
+      head-weighted form of the DeepSeek lightning indexer those weights come from); the top-T
+      positions by score (fp32, ties to the lower position) are the only ones attention reads.
 Where floating point decides an integer (the top-k set), the decision is taken in fp32,
 the precision of the GPU kernel: fp64 router logits are rounded to fp32, and the
 sigmoid, the bias add and the comparisons run in fp32.
@@ -407,6 +413,23 @@ def verify_forward(cfg: dict, W: Callable, x_bits, kv, kv_len: Optional[int] = N
     return {"layers": traces, "x_final": X, "out": outs}
 
 
+def index_scores(q_idx: np.ndarray, w_idx: np.ndarray, K_idx: np.ndarray) -> np.ndarray:
+    """Sparse-indexer scores (reading R24): I_s = sum_j w_j * max(0, q_j . k_s) over the H index
+    heads j, for every position s. q_idx [H][d], w_idx [H], K_idx [N][d] -> [N]."""
+    return np.maximum(np.asarray(K_idx) @ np.asarray(q_idx).T, 0.0) @ np.asarray(w_idx)
+
+
+def select_positions(scores, T: int) -> np.ndarray:
+    """The T positions with the largest scores, ties to the lower position, returned in
+    increasing position order; every position when there are at most T (reading R24)."""
+    s = np.asarray(scores)
+    n = s.shape[0]
+    if n <= T:
+        return np.arange(n)
+    order = np.lexsort((np.arange(n), -s.astype(np.float64)))  # by score descending, then position
+    return np.sort(order[:T])
+
+
 def mla_attention(cfg: dict, W: Callable, l: int, xn: np.ndarray, kv_layer, kv_len: int,
                   absorbed_trace: bool = True):
     """MLA attention of one layer (naive definition), plus the absorbed-form intermediates.
@@ -442,7 +465,24 @@ def mla_attention(cfg: dict, W: Callable, l: int, xn: np.ndarray, kv_layer, kv_l
     ent16, ent_bits = round_to_bf16(np.concatenate([c_new, kpe_new]))
     t["kv_new_bits"] = ent_bits
     kvl = np.asarray(kv_layer)
-    lat = np.concatenate([widen_bf16(kvl[:kv_len]), ent16[None, :]], axis=0)  # [n+1][kl+dr]
+    lat = np.concatenate([widen_bf16(kvl[:kv_len, :kl + dr]), ent16[None, :]], axis=0)  # [n+1][kl+dr]
+    if cfg.get("index_heads", 0):
+        # sparse indexer (reading R24): the new position's index key is appended (bf16), every
+        # position is scored, and attention reads only the selected positions' latent rows
+        hi, di, T = cfg["index_heads"], cfg["index_dim"], cfg["index_topk"]
+        k_idx = linear_bits(W, p + "idx_wk", xn)
+        k16, k_bits = round_to_bf16(k_idx)
+        w_idx = linear_bits(W, p + "idx_w", xn)
+        q_idx = linear_bits(W, p + "idx_wq", cq).reshape(hi, di)
+        K_idx = np.concatenate([widen_bf16(kvl[:kv_len, kl + dr:kl + dr + di]), k16[None, :]], axis=0)
+        sc = index_scores(q_idx, w_idx, K_idx)
+        sc32 = sc.astype(np.float32)  # the selection is decided in fp32 (the kernel's precision)
+        sel = select_positions(sc32, T)
+        t["idx_k"], t["idx_k_bits"], t["idx_w"], t["idx_q"] = k_idx, k_bits, w_idx, q_idx.reshape(-1)
+        t["idx_scores"], t["idx_sel"] = sc, sel
+        srt = np.sort(sc32.astype(np.float64))[::-1]
+        t["idx_margin"] = np.array([(srt[T - 1] - srt[T]) / max(np.max(np.abs(srt)), 1e-300) if len(srt) > T else np.inf])
+        lat = lat[sel]
     C, KPE = lat[:, :kl], lat[:, kl:]
     Wuk = _w64(W, p + "w_uk")   # [nh][dn][kl]
     Wuv = _w64(W, p + "w_uv")   # [nh][dv][kl]

@@ -92,6 +92,20 @@ def _mla_attn_specs(cfg: dict, p: str) -> List[TensorSpec]:
         TensorSpec(p + "w_uk", (nh, dn, kl), BF16, "weight"),
         TensorSpec(p + "w_uv", (nh, dv, kl), BF16, "weight"),
         TensorSpec(p + "wo", (d, nh * dv), BF16, "weight"),
+    ] + _index_specs(cfg, p)
+
+
+def _index_specs(cfg: dict, p: str) -> List[TensorSpec]:
+    """The sparse indexer's matrices ("index_heads" H > 0): index queries from the normalised
+    query latent, one index key and H head weights from the normalised layer input."""
+    hi = int(cfg.get("index_heads", 0))
+    if hi == 0:
+        return []
+    di, d, ql = cfg["index_dim"], cfg["hidden"], cfg["q_lora_rank"]
+    return [
+        TensorSpec(p + "idx_wq", (hi * di, ql), BF16, "weight"),
+        TensorSpec(p + "idx_wk", (di, d), BF16, "weight"),
+        TensorSpec(p + "idx_w", (hi, d), BF16, "weight"),
     ]
 
 
@@ -181,11 +195,12 @@ def n_tokens(cfg: dict) -> int:
 
 def kv_shape(cfg: dict, kv_len: Optional[int] = None) -> Tuple[int, ...]:
     """Cache layout: GQA [L][2][n_kv][kv_len+M][head_dim]; MLA/MoE [L][kv_len+1][kv_lora+rope]
-    (M = tokens per step: the step writes slots kv_len .. kv_len + M - 1)."""
+    (M = tokens per step: the step writes slots kv_len .. kv_len + M - 1); with a sparse
+    indexer each latent row is followed by the position's index key [index_dim]."""
     n = cfg["kv_len"] if kv_len is None else kv_len
     if cfg["arch"] == "gqa":
         return (cfg["n_layers"], 2, cfg["n_kv_heads"], n + n_tokens(cfg), cfg["head_dim"])
-    return (cfg["n_layers"], n + 1, cfg["kv_lora_rank"] + cfg["qk_rope"])
+    return (cfg["n_layers"], n + 1, cfg["kv_lora_rank"] + cfg["qk_rope"] + int(cfg.get("index_dim", 0) if cfg.get("index_heads", 0) else 0))
 
 
 def x_shape(cfg: dict) -> Tuple[int, ...]:
