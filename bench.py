@@ -35,6 +35,10 @@ WORKLOADS = {
                   "per row), batch 1, one decode token over an 8192-position bf16 latent cache",
     "moe_4k_fp8": "the MLA + MoE stack with every linear matrix but the absorption matrices and the router in FP8 "
                   "E4M3 (one fp32 scale per row), batch 1, one decode token over a 4096-position bf16 latent cache",
+    "mla_32k": "the MLA decoder stack (8 layers, hidden 7168, 16 heads) at batch 1, one decode token over a "
+               "32768-position latent cache (dense attention)",
+    "mla_32k_sparse": "the MLA decoder stack (8 layers, hidden 7168, 16 heads) with a sparse indexer (64 index heads of "
+                      "128, top 2048 positions), batch 1, one decode token over a 32768-position cache",
     "moe_4k_mxfp4": "the MLA + MoE stack with every expert matrix in MXFP4 (E2M1 elements, one E8M0 scale per "
                     "32), other weights bf16, batch 1, one decode token over a 4096-position latent cache",
 }

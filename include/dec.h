@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DEC_ABI_VERSION 2
+#define DEC_ABI_VERSION 3
 
 typedef struct dec_plan dec_plan;   /* opaque, library-owned host object */
 
@@ -107,6 +107,15 @@ typedef struct dec_model_shape {
   float rms_eps;
   int32_t weight_format; /* dec_weight_format (0: bf16) */
   double rope_theta;
+  /* Sparse indexer (latent families, bf16 weights; index_heads = 0: dense attention): per
+   * layer an index key k = W_k x^ (appended to the cache after the position's latent row),
+   * index_heads head weights w = W_w x^ and queries q_j = (W_q c_q)_j; every position s gets
+   * the score I_s = sum_j w_j max(0, q_j . k_s), and attention reads only the index_topk
+   * positions with the largest scores (ties to the lower position; all positions when there
+   * are at most index_topk). index_heads <= 64, index_dim a multiple of 32 up to 128. (The
+   * TileRT audit page's sparse_index: 64 index heads selecting the top-2048 KV positions.) */
+  int32_t index_heads, index_dim, index_topk;
+  int32_t reserved1;
 } dec_model_shape;
 
 /* Description of the device the plan is built for. dec_plan_create fills it from the

@@ -12,7 +12,7 @@ from typing import Dict, List, Optional, Sequence
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdec.so")
 
-DEC_ABI_VERSION = 2
+DEC_ABI_VERSION = 3
 ARCH = {"gqa": 0, "mla": 1, "moe": 2}
 STATUS = {0: "DEC_OK", -1: "DEC_E_INVAL", -2: "DEC_E_SHAPE", -3: "DEC_E_CAPACITY", -4: "DEC_E_DEVICE",
           -5: "DEC_E_OCCUPANCY", -6: "DEC_E_HIP", -7: "DEC_E_TIMEOUT", -8: "DEC_E_UNBOUND", -9: "DEC_E_PLAN"}
@@ -22,7 +22,8 @@ WEIGHT_FORMAT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 # task type ids (mirror of the engine's TaskType enum)
 TASK_TYPES = {1: "QKV", 2: "ATTN", 3: "OPROJ", 4: "GATEUP", 5: "DOWN", 6: "LMHEAD", 7: "MLA_A", 8: "MLA_B",
               9: "MLA_KVAPP", 10: "MLA_ABSORB", 11: "MLA_ATTN", 12: "MLA_UV", 13: "ROUTER", 14: "SHARED_GU",
-              15: "TOPK", 16: "EXPERT_GU", 17: "MOE_DOWN", 18: "OPROJ_G", 19: "HINIT"}
+              15: "TOPK", 16: "EXPERT_GU", 17: "MOE_DOWN", 18: "OPROJ_G", 19: "HINIT", 20: "ARGMAX",
+              21: "IDX_Q", 22: "IDX_SCORE", 23: "IDX_TOPK"}
 
 
 class DecError(RuntimeError):
@@ -37,7 +38,8 @@ class ModelShape(C.Structure):
                 ("ffn", C.c_int32), ("q_lora_rank", C.c_int32), ("kv_lora_rank", C.c_int32), ("qk_nope", C.c_int32),
                 ("qk_rope", C.c_int32), ("v_head", C.c_int32), ("n_routed", C.c_int32), ("n_shared", C.c_int32),
                 ("top_k", C.c_int32), ("expert_ffn", C.c_int32), ("rms_eps", C.c_float), ("weight_format", C.c_int32),
-                ("rope_theta", C.c_double)]
+                ("rope_theta", C.c_double), ("index_heads", C.c_int32), ("index_dim", C.c_int32),
+                ("index_topk", C.c_int32), ("reserved1", C.c_int32)]
 
 
 class DeviceInfo(C.Structure):
@@ -138,7 +140,8 @@ def shape_from_config(cfg: dict) -> ModelShape:
     s.abi_version = DEC_ABI_VERSION
     s.arch = ARCH[cfg["arch"]]
     for k in ("n_layers", "hidden", "vocab", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "q_lora_rank",
-              "kv_lora_rank", "qk_nope", "qk_rope", "v_head", "n_routed", "n_shared", "top_k", "expert_ffn"):
+              "kv_lora_rank", "qk_nope", "qk_rope", "v_head", "n_routed", "n_shared", "top_k", "expert_ffn",
+              "index_heads", "index_dim", "index_topk"):
         setattr(s, k, int(cfg.get(k, 0) or 0))
     s.rms_eps = float(cfg["rms_eps"])
     s.rope_theta = float(cfg["rope_theta"])

@@ -14,7 +14,7 @@
 
 extern "C" hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes, int run, bool cooperative,
                                         hipStream_t stream);
-extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int idx, int lds_bytes, int* blocks_per_cu);
 extern "C" hipError_t dec_scratch_current(void** ptr, size_t* bytes);
 extern "C" hipError_t dec_stream_read_launch(const void* buf, int64_t bytes, int n_wg, uint32_t* sink, hipStream_t stream);
 
@@ -110,6 +110,10 @@ void fill_args(dec_plan* p) {
   a.eps = s.rms_eps;
   a.attn_scale_log2 = P.attn_scale_log2;
   a.ntok = P.ntok;
+  a.idx_h = s.index_heads;
+  a.idx_d = s.index_heads ? s.index_dim : 0;
+  a.idx_t = s.index_topk;
+  a.kvrow = s.kv_lora_rank + s.qk_rope + a.idx_d;
 }
 
 void copy_name(char* dst, const std::string& s) {
@@ -145,7 +149,7 @@ dec_status check_scratch_owner(dec_plan* plan) {
 dec_status check_occupancy(dec_plan** out) {
   int per_cu = 0;
   const dec::PlanData& P = (*out)->P;
-  hipError_t e = dec_engine_occupancy(P.shape.arch, P.shape.weight_format, P.ntok, P.lds_bytes, &per_cu);
+  hipError_t e = dec_engine_occupancy(P.shape.arch, P.shape.weight_format, P.ntok, P.shape.index_heads > 0, P.lds_bytes, &per_cu);
   if (e != hipSuccess || per_cu < 1) {
     dec_plan_destroy(*out);
     *out = nullptr;
@@ -163,8 +167,8 @@ dec_status launch_stages(dec_plan* plan, const void* x, void* kv, void* out, int
   if (reinterpret_cast<uintptr_t>(x) % 8 || reinterpret_cast<uintptr_t>(kv) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
     return fail(DEC_E_INVAL, "x must be 8-byte, kv 16-byte and out 4-byte aligned");
   if (plan->P.dynamic) return fail(DEC_E_INVAL, "a plan with a per-step length runs with dec_step_dynamic");
-  if ((plan->P.shape.weight_format != DEC_WEIGHTS_BF16 || plan->P.ntok > 1) && (lo != 0 || hi != plan->P.n_stages))
-    return fail(DEC_E_INVAL, "FP8-weight and verification plans run whole steps only (dec_step)");
+  if ((plan->P.shape.weight_format != DEC_WEIGHTS_BF16 || plan->P.ntok > 1 || plan->P.shape.index_heads > 0) && (lo != 0 || hi != plan->P.n_stages))
+    return fail(DEC_E_INVAL, "low-precision, verification and sparse-indexer plans run whole steps only (dec_step)");
   if (lo < 0 || hi > plan->P.n_stages || lo >= hi)
     return fail(DEC_E_INVAL, "stage range [" + std::to_string(lo) + ", " + std::to_string(hi) + ") not inside [0, " +
                                  std::to_string(plan->P.n_stages) + ")");
@@ -267,7 +271,7 @@ dec_status dec_plan_sizes(const dec_plan* plan, dec_sizes* out) {
   if (s.arch == DEC_ARCH_GQA)
     out->kv_bytes = (int64_t)s.n_layers * 2 * s.n_kv_heads * (P.kv_len + nt) * s.head_dim * 2;
   else
-    out->kv_bytes = (int64_t)s.n_layers * (P.kv_len + nt) * (s.kv_lora_rank + s.qk_rope) * 2;
+    out->kv_bytes = (int64_t)s.n_layers * (P.kv_len + nt) * (s.kv_lora_rank + s.qk_rope + (s.index_heads ? s.index_dim : 0)) * 2;
   out->out_bytes = nt * (s.vocab > 0 ? s.vocab : s.hidden) * 4;
   out->workspace_bytes = P.ws_bytes;
   out->weight_bytes = P.weight_bytes;

@@ -22,6 +22,7 @@
 // dot products run on the vector ALUs in fp32, not on MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <map>
 #include <mutex>
 #include <type_traits>
 
@@ -1748,14 +1749,18 @@ __device__ __forceinline__ void qop_store(const Blk& b, int qop, int h, int k, f
   cst16(b.act, (uint32_t)qop * 4u + (i0 + 512u) * 2u, lo);
 }
 
-struct RmMlaA {  // rows [0, ql) of W_DQ, then the rows of W_DKV
+struct RmMlaA {  // rows [0, ql) of W_DQ, then the rows of W_DKV (KR), then W_k (DI), W_w (HI)
   const void *wqa, *wkva;
   int K, ql, r0;
   int es = 2;
   const float *sqa = nullptr, *skva = nullptr;  // FP8: row scales
+  const void *wik = nullptr, *wiw = nullptr;    // sparse indexer (bf16)
+  int KR = 0, DI = 0;
   __device__ __forceinline__ const void* row(int j) const {
-    const int r = r0 + j, sel = r >= ql ? 1 : 0;
-    return pick2(sel, wqa, wkva) + (size_t)(r - sel * ql) * K * es;
+    const int r = r0 + j;
+    const int s1 = r >= ql, s2 = r >= ql + KR, s3 = r >= ql + KR + DI;
+    const int off = s1 * ql + s2 * KR + s3 * DI;
+    return pick2(s2, pick2(s1, wqa, wkva), pick2(s3, wik, wiw)) + (size_t)(r - off) * K * es;
   }
   __device__ __forceinline__ float scale(int j) const {
     const int r = r0 + j;
@@ -1765,20 +1770,32 @@ struct RmMlaA {  // rows [0, ql) of W_DQ, then the rows of W_DKV
 };
 
 // x^ = RMSNorm(x); [cq_raw | kv_a] = [W_DQ; W_DKV] x^
-template <int ES>
+template <int ES, bool IDX>
 __device__ __forceinline__ bool task_mla_a(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
-  const int K = A.hidden, ql = A.ql;
+  const int K = A.hidden, ql = A.ql, KR = A.kl + A.dr, DI = IDX ? A.idx_d : 0;
   const RmMlaA rm{wp<uint8_t>(A, L.w[LW_WQA]), wp<uint8_t>(A, L.w[LW_WKVA]), K, ql, t.u0, ES, wscale<ES>(A, L.w[LW_WQA]),
-                  wscale<ES>(A, L.w[LW_WKVA])};
+                  wscale<ES>(A, L.w[LW_WKVA]), DI ? wp<uint8_t>(A, L.w[LW_IDXK]) : nullptr,
+                  DI ? wp<uint8_t>(A, L.w[LW_IDXW]) : nullptr, KR, DI};
   return run_gemv<2, false, ES>(
       A, b, t, rm, t.u1 - t.u0, K, 1, true,
       stage_vec(L.act[LA_X_IN], b.x, K, padc<ES>(K), wp<uint16_t>(A, L.w[LW_ATTN_NORM]), A.eps),
       [&] {
         for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) {
           const int r = t.u0 + i;
-          const int off = r < ql ? L.act[LA_CQ] + r : L.act[LA_KVA] + (r - ql);
-          cst(b.act, (uint32_t)off * 4u, b.ys[i]);
+          if (r < ql + KR) {
+            const int off = r < ql ? L.act[LA_CQ] + r : L.act[LA_KVA] + (r - ql);
+            cst(b.act, (uint32_t)off * 4u, b.ys[i]);
+          } else if (IDX && r < ql + KR + DI) {
+            // the new index key: traced, and appended to the cache (bf16) after the latent row
+            const int k = r - ql - KR;
+            cst(b.act, (uint32_t)(L.act[LA_IDXK] + k) * 4u, b.ys[i]);
+            uint16_t* row = A.kv + ((size_t)t.layer * (A.kv_len + 1) + b.n) * A.kvrow + KR;
+            const rsrc_t rr = make_rsrc(row, (uint32_t)DI * 2u);
+            cst16(rr, (uint32_t)k * 2u, f2bf(b.ys[i]));
+          } else if (IDX) {
+            cst(b.act, (uint32_t)(L.act[LA_IDXW] + r - ql - KR - DI) * 4u, b.ys[i]);
+          }
         }
       });
 }
@@ -1836,7 +1853,7 @@ __device__ __forceinline__ bool task_mla_kvapp(const EngineArgs& A, Blk& b, cons
   const int kl = A.kl, dr = A.dr, KR = kl + dr, n = b.n;
   if (!wait_deps(A, b, t)) return false;
   stage_now(b, stage_vec(L.act[LA_KVA], nullptr, kl, pad512(kl), wp<uint16_t>(A, L.w[LW_KVNORM]), A.eps, true));
-  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (A.kv_len + 1) + n) * KR, (uint32_t)KR * 2u);
+  const rsrc_t rowr = make_rsrc(A.kv + ((size_t)t.layer * (A.kv_len + 1) + n) * A.kvrow, (uint32_t)KR * 2u);
   for (int i = threadIdx.x; i < kl; i += kThreads) {
     const float v = b.xs[i];
     cst(b.act, (uint32_t)(L.act[LA_KVNEW] + i) * 4u, v);
@@ -1913,14 +1930,20 @@ __device__ __forceinline__ bool task_mla_absorb(const EngineArgs& A, Blk& b, con
 // P goes through LDS in the A-operand order; the latent's B operand for PV (8 positions of
 // one column per lane) is gathered from the LDS chunk. The unnormalised split partial
 // (O, M, Lr) is stored for the W_UV tasks, which merge the splits.
+template <bool IDX>
 __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
   const int kl = A.kl, KR = kl + A.dr, KP = (KR + 31) & ~31, NKS = KP >> 5, nh = A.nq;
   // split a1 of a2 over positions [0, n]; a plan with a per-step length can leave a split
-  // empty at small positions: it then stores the neutral partial (M = -inf, Lr = 0, O = 0)
-  const int n = b.n, p0 = split_pos(n, t.a1, t.a2), p1 = split_pos(n, t.a1 + 1, t.a2);
+  // empty at small positions: it then stores the neutral partial (M = -inf, Lr = 0, O = 0).
+  // With the sparse indexer the split is a range of the list of selected positions
+  // (increasing), of length m = min(T, n + 1).
+  const bool sparse = IDX && A.idx_h > 0;
+  const int n = b.n, m = sparse ? (A.idx_t < n + 1 ? A.idx_t : n + 1) : n + 1;
+  const int p0 = split_pos(m - 1, t.a1, t.a2), p1 = split_pos(m - 1, t.a1 + 1, t.a2);
   const int wave = wave_id(), lane = threadIdx.x & 63, hl = lane & 15, g = lane >> 4;
-  const uint16_t* lat = A.kv + (size_t)t.layer * (A.kv_len + 1) * KR;
+  const int KS = IDX ? A.kvrow : KR;  // cache row stride (elements)
+  const uint16_t* lat = A.kv + (size_t)t.layer * (A.kv_len + 1) * KS;
   u4* QL = reinterpret_cast<u4*>(b.xs);                                   // [NKS][2][64]
   uint16_t* LAT = reinterpret_cast<uint16_t*>(b.xs + NKS * 512);          // [kMlaChunk][KP]
   u4* PA = reinterpret_cast<u4*>(b.xs + NKS * 512 + kMlaChunk * KP / 2);  // [kMlaChunk/32][2][64]
@@ -1930,6 +1953,7 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
   float* MR = ST + 128;        // [16] running max
   float* LR = ST + 144;        // [16] running sum
   float* AL = ST + 160;        // [16] rescale of the previous chunks
+  int* SELS = reinterpret_cast<int*>(ST + 256);  // sparse: the split's selected positions
   const int segs_row = KP >> 3, nseg = kMlaChunk * segs_row;
   // positions [c0, c0 + kMlaChunk) into LAT; rows past the split repeat its last position
   // (finite values: their probabilities are 0); pad columns are zeroed after arrival
@@ -1938,16 +1962,21 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
   // this XCD read, and cached, earlier in the step.
   auto dma_chunk = [&](int c0, int w0) {  // issued by waves w0..7
     if (wave < w0) return;
-    const bool coh = (c0 + kMlaChunk < p1 ? c0 + kMlaChunk : p1) > n;
+    const int ce = c0 + kMlaChunk < p1 ? c0 + kMlaChunk : p1;
+    const bool coh = sparse ? SELS[ce - 1 - p0] == n : ce > n;  // (the list increases: n can only be last)
     for (int j = wave - w0; j * 64 < nseg; j += kWaves - w0) {
       const int q = j * 64 + lane, row = q / segs_row, sc = q - row * segs_row;
       int pos = c0 + row;
       pos = pos < p1 ? pos : p1 - 1;
+      if (sparse) {  // (clamped: a position the selection wrote is always in [0, n])
+        pos = SELS[pos - p0];
+        pos = pos < 0 ? 0 : (pos > n ? n : pos);
+      }
       const int col = (sc * 8 < KR) ? sc * 8 : 0;
       if (coh)
-        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kCoh);
+        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KS + col), (lvp)(LAT + j * 512), 16, 0, kCoh);
       else
-        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KR + col), (lvp)(LAT + j * 512), 16, 0, kActCpol);
+        __builtin_amdgcn_global_load_lds((gvp)(lat + (size_t)pos * KS + col), (lvp)(LAT + j * 512), 16, 0, kActCpol);
     }
   };
   auto zero_pad = [&](int w0) {  // each wave zeroes the pad slots of its own copies
@@ -1959,9 +1988,15 @@ __device__ __forceinline__ bool task_mla_attn(const EngineArgs& A, Blk& b, const
   };
   // a chunk of cached positions only (< kv_len) can be fetched before the wait (not by
   // wave 0, whose dependency polls would queue behind the copies)
-  const bool pre = (p0 + kMlaChunk < p1 ? p0 + kMlaChunk : p1) <= n;
+  // (with the indexer the positions are known only once the selection is done: no prefetch)
+  const bool pre = !sparse && (p0 + kMlaChunk < p1 ? p0 + kMlaChunk : p1) <= n;
   if (pre && p1 > p0) dma_chunk(p0, 1);
   if (!wait_deps(A, b, t)) return false;
+  if (sparse && p1 > p0) {  // the split's slice of the selected positions into LDS
+    for (int i = threadIdx.x; i < p1 - p0; i += kThreads)
+      SELS[i] = __float_as_int(cld(b.act, (uint32_t)(L.act[LA_IDXSEL] + p0 + i) * 4u));
+    __syncthreads();
+  }
   if (!pre && p1 > p0) dma_chunk(p0, 0);
   if (wave == 0) dma_to_lds(reinterpret_cast<float*>(QL), b.actp + L.act[LA_QOP], NKS * 512);
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
@@ -2447,6 +2482,205 @@ __device__ __forceinline__ bool task_moe_down(const EngineArgs& A, Blk& b, const
         }
       },
       t.a2, [&] { stage_ids(A, L, b, ids); });
+}
+
+
+// ------------------------------------------------------------------ sparse indexer
+//
+// The TileRT audit page's sparse_index: index heads score every cached position and attention
+// reads only the top-T of them. Per layer (reading of the oracle): index key k = W_k x^ and head
+// weights w = W_w x^ come out of the T_MLA_A rows (the key is appended to the cache after the
+// position's latent row), index queries q_j = (W_q c_q)_j out of T_IDX_Q; T_IDX_SCORE computes
+// I_s = sum_j w_j max(0, q_j . k_s) for a range of positions on the matrix cores, T_IDX_TOPK
+// selects the T largest (ties to the lower position) in increasing position order, and the
+// latent attention splits that list.
+
+// index queries: rows of W_q [H * DI][ql] times the normalised query latent
+__device__ __forceinline__ bool task_idx_q(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int K = A.ql;
+  const RmPlain rm{wp<uint8_t>(A, L.w[LW_IDXQ]), K, t.u0};
+  return run_gemv(
+      A, b, t, rm, t.u1 - t.u0, K, 1, true,
+      stage_vec(L.act[LA_CQ], nullptr, K, pad512(K), wp<uint16_t>(A, L.w[LW_QNORM]), A.eps),
+      [&] {
+        for (int i = threadIdx.x; i < t.u1 - t.u0; i += 64) cst(b.act, (uint32_t)(L.act[LA_IDXQ] + t.u0 + i) * 4u, b.ys[i]);
+      });
+}
+
+// Scores of positions [p0, p1) (range a1 of a2 over [0, n], cut at run time). The queries
+// become the B operand of bf16 MFMA 16x16x32 (16 heads per tile, k = the key's dimensions,
+// fp32 split into bf16 hi + lo); 16 positions' keys are the A operand, exact bf16, loaded from
+// the cache straight into registers. For each head tile the 16 x 16 score tile gets the ReLU and
+// the head weights, and the sum over heads is a 16-lane reduction.
+__device__ __forceinline__ bool task_idx_score(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int H = A.idx_h, DI = A.idx_d, NKI = DI / 32, HT = (H + 15) / 16, KR = A.kl + A.dr, n = b.n;
+  const int p0 = split_pos(n, t.a1, t.a2), p1 = split_pos(n, t.a1 + 1, t.a2);
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  float* QF = b.xs;                                      // [H][DI] fp32
+  u4* QB = reinterpret_cast<u4*>(b.xs + H * DI);         // [HT][NKI][hi, lo][64 lanes]
+  float* WI = b.xs + H * DI + HT * NKI * 2 * 256;        // [64] head weights (0 past H)
+  if (!wait_deps(A, b, t)) return false;
+  dma_to_lds_all(QF, b.actp + L.act[LA_IDXQ], H * DI);
+  if (threadIdx.x < 64) WI[lane] = lane < H ? cld(b.act, (uint32_t)(L.act[LA_IDXW] + lane) * 4u) : 0.f;
+  __syncthreads();
+  for (int e = threadIdx.x; e < HT * NKI * 64; e += kThreads) {
+    const int Ll = e & 63, ks = (e >> 6) % NKI, ht = (e >> 6) / NKI;
+    const int hh = 16 * ht + (Ll & 15), k0 = 32 * ks + 8 * (Ll >> 4);
+    const f4 z = f4{0.f, 0.f, 0.f, 0.f};
+    const f4 a = hh < H ? *reinterpret_cast<const f4*>(QF + hh * DI + k0) : z;
+    const f4 c = hh < H ? *reinterpret_cast<const f4*>(QF + hh * DI + k0 + 4) : z;
+    u4 hi, lo;
+    split_bf16x8(a, c, 1.0f, hi, lo);
+    QB[((ht * NKI + ks) * 2 + 0) * 64 + Ll] = hi;
+    QB[((ht * NKI + ks) * 2 + 1) * 64 + Ll] = lo;
+  }
+  __syncthreads();
+  // the layer's cache rows as one buffer (key of position p at element p * kvrow + KR)
+  const rsrc_t kr = make_rsrc(A.kv + (size_t)t.layer * (A.kv_len + 1) * A.kvrow, (uint32_t)((A.kv_len + 1) * A.kvrow * 2));
+  for (int base = p0 + 16 * wave; base < p1; base += 16 * kWaves) {
+    int pos = base + (lane & 15);
+    pos = pos < p1 ? pos : p1 - 1;
+    const uint32_t off = (uint32_t)(pos * A.kvrow + KR + 8 * (lane >> 4)) * 2u;
+    // the key of position n was written in this step by another workgroup: read it coherently
+    const bool has_new = base + 16 > n;
+    u4 ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < NKI) {
+        if (has_new)
+          ka[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64u * ks, 0, kCoh);
+        else
+          ka[ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64u * ks, 0, kActCpol);
+      }
+    }
+    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < HT; ++ht) {
+      f4 d = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < NKI) {
+          d = mfma_bf16(ka[ks], QB[((ht * NKI + ks) * 2 + 0) * 64 + lane], d);
+          d = mfma_bf16(ka[ks], QB[((ht * NKI + ks) * 2 + 1) * 64 + lane], d);
+        }
+      }
+      const float w = WI[16 * ht + (lane & 15)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, fmaxf(d[i], 0.f), acc[i]);
+    }
+    // lane: head 16 ht + lane % 16, positions base + 4 (lane / 16) + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = group_sum<16>(acc[i]);
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = base + 4 * (lane >> 4) + i;
+        if (p < p1) cst(b.act, (uint32_t)(L.act[LA_IDXS] + p) * 4u, acc[i] + 0.f);  // (+0: no -0 scores)
+      }
+    }
+  }
+  return true;
+}
+
+// An fp32 score as an unsigned key with the same order.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum of v over the workgroup's threads (thread order); scratch: 8 words.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int pre = 0;
+  for (int w = 0; w < wave; ++w) pre += scratch[w];
+  __syncthreads();
+  return pre + incl - v;
+}
+
+// The top T of the N = n + 1 scores, ties to the lower position, written in increasing position
+// order (all positions when N <= T). Radix selection over the keys, eight bits per pass from the
+// top, finds the T-th largest key K and how many of the keys equal to K are taken; one more pass
+// compacts, each thread over a contiguous block of positions so that the order is kept.
+__device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const TaskDesc& t) {
+  const LayerDesc& L = A.layers[t.layer];
+  const int N = b.n + 1, T = A.idx_t;
+  if (!wait_deps(A, b, t)) return false;
+  const uint32_t so = (uint32_t)L.act[LA_IDXS] * 4u, sel = (uint32_t)L.act[LA_IDXSEL] * 4u;
+  if (N <= T) {
+    for (int i = threadIdx.x; i < N; i += kThreads) cst(b.act, sel + (uint32_t)i * 4u, __int_as_float(i));
+    return true;
+  }
+  uint32_t* hist = reinterpret_cast<uint32_t*>(b.xs);  // [256]
+  int* misc = reinterpret_cast<int*>(b.xs) + 256;      // [0] digit, [1] still needed, [8..15] scan
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, mask = 0;
+  int need = T;  // keys still to take among those matching the prefix
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < N; i += kThreads) {
+      const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
+      if ((k & mask) == prefix) atomicAdd(hist + ((k >> shift) & 255u), 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      // lane l holds digits 255 - 4l .. 252 - 4l (from the top)
+      uint32_t c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
+      const int sum = (int)(c[0] + c[1] + c[2] + c[3]);
+      int incl = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += y;
+      }
+      int before = incl - sum;  // keys with a larger digit than this lane's
+      if (before < need && need <= incl) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (need <= before + (int)c[j]) {
+            misc[0] = 255 - 4 * lane - j;
+            misc[1] = need - before;
+            break;
+          }
+          before += (int)c[j];
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)misc[0] << shift;
+    mask |= 255u << shift;
+    need = misc[1];
+    __syncthreads();
+  }
+  // keys above `prefix` are all taken; of those equal to it, the `need` at the lowest positions
+  const int B = (N + kThreads - 1) / kThreads, i0 = threadIdx.x * B, i1 = (i0 + B < N) ? i0 + B : N;
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
+    gt += k > prefix;
+    eq += k == prefix;
+  }
+  const int eqb = block_excl_scan(eq, misc + 8);
+  int take = need - eqb;
+  take = take < 0 ? 0 : (take > eq ? eq : take);
+  int out = block_excl_scan(gt + take, misc + 8);
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
+    if (k > prefix || (k == prefix && take-- > 0)) cst(b.act, sel + (uint32_t)(out++) * 4u, __int_as_float(i));
+  }
+  return true;
 }
 
 
@@ -3107,7 +3341,9 @@ __device__ __forceinline__ const EngineArgs& args_view() {
 // ES: the weights' element format -- GQA: every linear matrix (2 bf16, 1 FP8); latent family:
 // 2 bf16, 1 FP8 (every linear matrix but the absorption matrices and the router), 0 MXFP4
 // experts (every other matrix bf16).
-template <bool MLA, int RUN, int ES = 2, int MT = 1>
+// IDX: the latent family with the sparse indexer (its tasks are compiled into their own kernels,
+// so the dense kernels' register allocation does not carry them).
+template <bool MLA, int RUN, int ES = 2, int MT = 1, bool IDX = false>
 __device__ __forceinline__ void engine_body(const EngineArgs& A) {
   constexpr int ED = ES == 1 ? 1 : 2;  // the latent family's non-expert matrices
   extern __shared__ f4 lds4[];
@@ -3216,11 +3452,11 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
       }
     } else {
       switch (t.type) {
-        case T_MLA_A: ok = task_mla_a<ED>(A, b, t); break;
+        case T_MLA_A: ok = task_mla_a<ED, IDX>(A, b, t); break;
         case T_MLA_B: ok = task_mla_b<ED>(A, b, t); break;
         case T_MLA_KVAPP: gemv = false; ok = task_mla_kvapp(A, b, t); break;
         case T_MLA_ABSORB: gemv = false; ok = task_mla_absorb(A, b, t); break;
-        case T_MLA_ATTN: gemv = false; ok = task_mla_attn(A, b, t); break;
+        case T_MLA_ATTN: gemv = false; ok = task_mla_attn<IDX>(A, b, t); break;
         case T_MLA_UV: gemv = false; ok = task_mla_uv(A, b, t); break;
         case T_OPROJ: ok = task_oproj<ED>(A, b, t); break;
         case T_GATEUP: ok = task_gateup<ED>(A, b, t); break;
@@ -3236,6 +3472,20 @@ __device__ __forceinline__ void engine_body(const EngineArgs& A) {
         case T_TOPK: gemv = false; ok = task_topk(A, b, t); break;
         case T_EXPERT_GU: ok = task_expert_gu<ES>(A, b, t); break;
         case T_MOE_DOWN: ok = task_moe_down<ES>(A, b, t); break;
+        case T_IDX_Q:
+          if constexpr (IDX) ok = task_idx_q(A, b, t);
+          else ok = false;
+          break;
+        case T_IDX_SCORE:
+          gemv = false;
+          if constexpr (IDX) ok = task_idx_score(A, b, t);
+          else ok = false;
+          break;
+        case T_IDX_TOPK:
+          gemv = false;
+          if constexpr (IDX) ok = task_idx_topk(A, b, t);
+          else ok = false;
+          break;
         default: ok = false; break;
       }
     }
@@ -3290,6 +3540,12 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_dyn(Eng
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_dyn(EngineArgs A) {
   engine_body<true, kRunDynamic>(A);
 }
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_sp(EngineArgs A) {
+  engine_body<true, kRunStep, 2, 1, true>(A);
+}
+extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_sp_dyn(EngineArgs A) {
+  engine_body<true, kRunDynamic, 2, 1, true>(A);
+}
 extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_mla_f8(EngineArgs A) {
   engine_body<true, kRunStep, 1>(A);
 }
@@ -3322,7 +3578,8 @@ extern "C" __global__ void __launch_bounds__(kThreads, 1) dec_engine_gqa_v4(Engi
 
 // Host-side launch (used by the C ABI in api.cpp). run: 0 a whole step, 1 a range of stages,
 // 2 a whole step of a plan with a per-step length; ntok > 1: a verification step (run 0).
-static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1) {
+static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1, bool idx = false) {
+  if (idx && arch != 0) return run == 2 ? (const void*)dec::dec_engine_mla_sp_dyn : (const void*)dec::dec_engine_mla_sp;
   if (ntok == 2) return (const void*)dec::dec_engine_gqa_v2;
   if (ntok == 3) return (const void*)dec::dec_engine_gqa_v3;
   if (ntok == 4) return (const void*)dec::dec_engine_gqa_v4;
@@ -3336,18 +3593,25 @@ static const void* engine_fn(int arch, int run, int wfmt = 0, int ntok = 1) {
 
 extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(const dec::EngineArgs* args, int n_wg, int lds_bytes,
                                                                          int run, bool cooperative, hipStream_t stream) {
-  static int configured_lds[2][8] = {{-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1}};
+  // the dynamic-LDS limit each kernel has been given so far
+  static std::mutex mu;
+  static std::map<const void*, int> configured_lds;
   const int k = args->arch == 0 ? 0 : 1;
-  // MXFP4 experts: the latent family; FP8 or MXFP4 weights: no stage launches
-  if (run < 0 || run > 2 || (args->wfmt == 2 && k != 1) || (args->wfmt && run == 1))
+  const bool idx = args->idx_h > 0;
+  // MXFP4 experts and the sparse indexer: the latent family; FP8, MXFP4 or the indexer: no
+  // stage launches
+  if (run < 0 || run > 2 || (args->wfmt == 2 && k != 1) || ((args->wfmt || idx) && run == 1) || (idx && (k != 1 || args->wfmt)))
     return hipErrorInvalidValue;
   if (args->ntok > 1 && (k != 0 || run != 0 || args->wfmt || args->ntok > dec::kMaxVerifyTokens)) return hipErrorInvalidValue;
-  const void* fn = engine_fn(args->arch, run, args->wfmt, args->ntok);
-  const int slot = args->ntok > 1 ? 3 + args->ntok : args->wfmt ? 3 + (run == 2) : run;
-  if (configured_lds[k][slot] < lds_bytes) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-    if (e != hipSuccess) return e;
-    configured_lds[k][slot] = lds_bytes;
+  const void* fn = engine_fn(args->arch, run, args->wfmt, args->ntok, idx);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    int& have = configured_lds.emplace(fn, -1).first->second;
+    if (have < lds_bytes) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (e != hipSuccess) return e;
+      have = lds_bytes;
+    }
   }
   void* kargs[] = {const_cast<dec::EngineArgs*>(args)};
   if (!cooperative)  // one stage: no task waits on another of the same launch
@@ -3355,9 +3619,9 @@ extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_launch(co
   return hipLaunchCooperativeKernel(fn, dim3(n_wg), dim3(dec::kThreads), kargs, (unsigned)lds_bytes, stream);
 }
 
-extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int lds_bytes,
-                                                                               int* blocks_per_cu) {
-  const void* fn = engine_fn(arch, 0, wfmt, ntok);
+extern "C" __attribute__((visibility("hidden"))) hipError_t dec_engine_occupancy(int arch, int wfmt, int ntok, int idx,
+                                                                               int lds_bytes, int* blocks_per_cu) {
+  const void* fn = engine_fn(arch, 0, wfmt, ntok, idx != 0);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, dec::kThreads, (size_t)lds_bytes);

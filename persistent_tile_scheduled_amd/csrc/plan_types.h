@@ -60,6 +60,9 @@ enum TaskType : int32_t {
   T_HINIT = 19,      // GQA layer 0: h = x (the accumulator the per-group O-projections add into)
   T_ARGMAX = 20,     // greedy choice: the largest logit over the LM-head tasks' best (value,
                      // index) pairs, written to the step state (length-per-step plans)
+  T_IDX_Q = 21,      // sparse indexer: index-query rows W_q c_q (normalised query latent)
+  T_IDX_SCORE = 22,  // sparse indexer: scores of a range of positions (bf16 MFMA over the index keys)
+  T_IDX_TOPK = 23,   // sparse indexer: the top-T positions (radix select), in increasing order
   T_NUM_TYPES
 };
 
@@ -84,6 +87,7 @@ enum LayerW : int32_t {
   LW_ATTN_NORM = 0, LW_WQ, LW_WK, LW_WV, LW_WO, LW_FFN_NORM, LW_GATE, LW_UP, LW_DOWN,
   LW_WQA, LW_QNORM, LW_WQB, LW_WKVA, LW_KVNORM, LW_WUK, LW_WUV,
   LW_ROUTER, LW_RBIAS, LW_EGATE, LW_EUP, LW_EDOWN, LW_SGATE, LW_SUP, LW_SDOWN,
+  LW_IDXQ, LW_IDXK, LW_IDXW,  // sparse indexer: W_q [H*d][ql], W_k [d][hidden], W_w [H][hidden]
   LW_COUNT
 };
 enum LayerA : int32_t {
@@ -107,6 +111,11 @@ enum LayerA : int32_t {
   LA_SACT,       // MoE: shared-expert activation [ns*eff]
   LA_QOP,        // MLA: scaled [q_abs | q_rope] as bf16 hi/lo pairs in MFMA B-operand order
   LA_PML,        // MLA: split partial (m, l) [nh][S][2]
+  LA_IDXK,       // sparse indexer: the new index key (fp32) [d]
+  LA_IDXW,       // sparse indexer: head weights [H]
+  LA_IDXQ,       // sparse indexer: index queries [H][d]
+  LA_IDXS,       // sparse indexer: scores of positions [0, n] (fp32)
+  LA_IDXSEL,     // sparse indexer: the selected positions (int32, increasing) [min(T, n + 1)]
   LA_COUNT
 };
 
@@ -178,6 +187,8 @@ struct EngineArgs {
   int32_t gs_floats;           // LDS floats reserved for norm gains
   float eps, attn_scale_log2;  // softmax scale * log2(e)
   int32_t ntok;                // tokens per step (1: decode; 2..4: a verification step)
+  int32_t idx_h, idx_d, idx_t; // sparse indexer: heads, key width, positions kept (idx_h = 0: dense)
+  int32_t kvrow;               // latent family: cache row width (kl + dr, + idx_d with an indexer)
 };
 
 }  // namespace dec

@@ -35,6 +35,7 @@ constexpr int kStageCounters = DEC_STAGE_COUNTERS;  // completion counters per s
 #endif
 constexpr double kOddXcdSpeed = DEC_ODD_XCD_SPEED;  // relative streaming speed of XCDs 1, 3, 5, 7
 constexpr int kMinPosMla = 64;             // positions per latent-attention split (at least)
+constexpr int kIdxPos = 128;               // positions per sparse-indexer score task (at least)
 constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -181,6 +182,15 @@ struct Builder {
     if (q.vocab < 0) return fail(DEC_E_SHAPE, "vocab < 0", st);
     if (q.weight_format != DEC_WEIGHTS_BF16 && q.weight_format != DEC_WEIGHTS_FP8_E4M3 && q.weight_format != DEC_WEIGHTS_MXFP4)
       return fail(DEC_E_SHAPE, "unknown weight_format", st);
+    if (q.index_heads < 0 || q.index_dim < 0 || q.index_topk < 0) return fail(DEC_E_SHAPE, "negative sparse-indexer field", st);
+    if (q.index_heads > 0) {
+      if (q.arch == DEC_ARCH_GQA) return fail(DEC_E_SHAPE, "the sparse indexer is for the latent families", st);
+      if (q.index_heads > 64 || q.index_dim < 32 || q.index_dim > 128 || q.index_dim % 32 || q.index_topk < 1)
+        return fail(DEC_E_SHAPE, "sparse indexer: index_heads <= 64, index_dim a multiple of 32 up to 128, index_topk >= 1", st);
+      if (q.weight_format != DEC_WEIGHTS_BF16) return fail(DEC_E_SHAPE, "sparse indexer: bf16 weights only", st);
+    } else if (q.index_dim || q.index_topk) {
+      return fail(DEC_E_SHAPE, "index_dim / index_topk set without index_heads", st);
+    }
     if (q.weight_format == DEC_WEIGHTS_MXFP4) {
       if (q.arch != DEC_ARCH_MOE) return fail(DEC_E_SHAPE, "MXFP4 weights: MoE family only (the expert matrices)", st);
       if (q.hidden % 32 || q.expert_ffn % 32)
@@ -303,6 +313,11 @@ struct Builder {
         W(LW_WUK, "w_uk", DEC_DTYPE_BF16, {nh, s.qk_nope, s.kv_lora_rank});
         W(LW_WUV, "w_uv", DEC_DTYPE_BF16, {nh, s.v_head, s.kv_lora_rank});
         M(LW_WO, "wo", d, (int64_t)nh * s.v_head);
+        if (s.index_heads > 0) {  // the sparse indexer's matrices
+          W(LW_IDXQ, "idx_wq", DEC_DTYPE_BF16, {(int64_t)s.index_heads * s.index_dim, s.q_lora_rank});
+          W(LW_IDXK, "idx_wk", DEC_DTYPE_BF16, {s.index_dim, d});
+          W(LW_IDXW, "idx_w", DEC_DTYPE_BF16, {s.index_heads, d});
+        }
       }
       W(LW_FFN_NORM, "ffn_norm", DEC_DTYPE_BF16, {d});
       if (s.arch == DEC_ARCH_MOE) {
@@ -508,11 +523,24 @@ struct Builder {
     L.act[LA_FFN_OUT] = (int)act(p + "ffn_out", d);
     L.act[LA_X_OUT] = (int)act(p + "x_out", d);
     need_xs(d); need_xs(ql); need_xs(KR); need_xs((int64_t)nh * dv);
+    const int HI = s.index_heads, DI = HI ? s.index_dim : 0;
+    const int64_t m_sel = HI ? std::min<int64_t>(s.index_topk, n + 1) : n + 1;  // positions attention reads
+    if (HI) {
+      L.act[LA_IDXK] = (int)act(p + "idx_k", DI);
+      L.act[LA_IDXW] = (int)act(p + "idx_w", HI);
+      L.act[LA_IDXQ] = (int)act(p + "idx_q", (int64_t)HI * DI);
+      L.act[LA_IDXS] = (int)act(p + "idx_scores", n + 1);
+      L.act[LA_IDXSEL] = (int)act(p + "idx_sel", m_sel, DEC_DTYPE_I32);
+      // score task: the queries (fp32), their MFMA operand (bf16 hi + lo, 16-head tiles), weights
+      need_xs((int64_t)HI * DI + (int64_t)((HI + 15) / 16) * (DI / 32) * 2 * 256 + 64);
+      need_xs(256 + 64 + 16);  // top-k: histogram and scan words
+    }
 
-    // A: [W_DQ; W_DKV] rows from the normalised layer input
+    // A: [W_DQ; W_DKV] rows from the normalised layer input (with the indexer: then the rows of
+    // W_k and W_w, whose results are the new index key and the head weights)
     ++stage;
     const int ca = counter(nsc);
-    spread(all_wgs(), ql + KR, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + slot(w)); });
+    spread(all_wgs(), ql + KR + DI + HI, kRowsCap, [&](int w, int a, int b) { add(w, T_MLA_A, l, a, b, prev, ca + slot(w)); });
     auto da = all_of(ca, nsc);
 
     // B: W_UQ row pairs (nope pairs, then RoPE pairs, per head); the latent-cache append
@@ -528,6 +556,28 @@ struct Builder {
     spread(bw, nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + slot(w)); });
     auto db = all_of(cb, nsc);
 
+    // the sparse indexer: index-query rows (beside W_UQ), scores of every position, the top-T
+    int ctop = -1;
+    if (HI) {
+      const int cq = counter(nsc);
+      spread(bw, HI * DI, kRowsCap, [&](int w, int a, int b) { add(w, T_IDX_Q, l, a, b, da, cq + slot(w)); });
+      ++stage;
+      const int csc = counter(nsc);
+      std::vector<int32_t> dsc = da;
+      auto dq = all_of(cq, nsc);
+      dsc.insert(dsc.end(), dq.begin(), dq.end());
+      // positions [0, n] in NS ranges, cut at run time from the step's position (a plan with a
+      // per-step length scores fewer positions at smaller positions)
+      const int NS = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kIdxPos - 1) / kIdxPos));
+      for (int i = 0; i < NS; ++i) {
+        const int w = (int)((int64_t)i * n_wg / NS);
+        add(w, T_IDX_SCORE, l, (int)((n + 1) * i / NS), (int)((n + 1) * (i + 1) / NS), dsc, csc + slot(w), -1, 0, i, NS);
+      }
+      ++stage;
+      ctop = counter(1);
+      add(n_wg - 1, T_IDX_TOPK, l, 0, (int)(n + 1), all_of(csc, nsc), ctop);
+    }
+
     // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h], one (head, 64-column block) per task
     ++stage;
     const int cabs = counter(nsc);
@@ -537,7 +587,7 @@ struct Builder {
     // latent attention: S position splits, all heads folded into one MFMA tile
     ++stage;
     const int catt = counter(nsc);
-    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (n + 1 + kMinPosMla - 1) / kMinPosMla));
+    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (m_sel + kMinPosMla - 1) / kMinPosMla));
     const int Sp = (S + 1) & ~1;  // per-head stride of the (M, Lr) table (16-byte rows)
     const int64_t pml = act(p + "attn_ml", (int64_t)nh * Sp * 2);
     const int64_t part = act(p + "attn_partials", (int64_t)S * nh * kl);
@@ -546,13 +596,17 @@ struct Builder {
     std::vector<int32_t> dat = all_of(cabs, nsc);
     dat.insert(dat.end(), db.begin(), db.end());
     dat.push_back(ckv);
+    if (HI) dat.push_back(ctop);
+    // (with the indexer a split is a range of the selected-position list, not of positions)
     for (int sp = 0; sp < S; ++sp) {
       const int w = (int)((int64_t)sp * n_wg / S);
-      int p0 = (int)((n + 1) * sp / S), p1 = (int)((n + 1) * (sp + 1) / S);
+      int p0 = (int)(m_sel * sp / S), p1 = (int)(m_sel * (sp + 1) / S);
       add(w, T_MLA_ATTN, l, p0, p1, dat, catt + slot(w), -1, 0, sp, S, 0, (int)pml, (int)part);
     }
-    // LDS: q operand + one latent chunk + P operand + softmax statistics
-    mla_lds = std::max<int64_t>(mla_lds, (int64_t)NKS * 512 + (int64_t)kMlaChunk * KP / 2 + (kMlaChunk / 32) * 512 + 256);
+    // LDS: q operand + one latent chunk + P operand + softmax statistics (+ the split's slice
+    // of the selected positions)
+    mla_lds = std::max<int64_t>(mla_lds, (int64_t)NKS * 512 + (int64_t)kMlaChunk * KP / 2 + (kMlaChunk / 32) * 512 + 256 +
+                                             (HI ? align_up((m_sel + S - 1) / S + 1, 64) : 0));
 
     // W_UV: per (head, column block) merge the splits, multiply, add into o[h]
     ++stage;
@@ -791,7 +845,10 @@ struct Builder {
     if (P.w_embed >= 0)  // a step reads one row of the token embedding, not the table
       alg -= (int64_t)(s.vocab - 1) * s.hidden * 2;
     int64_t kv_row = (s.arch == DEC_ARCH_GQA) ? 2LL * s.n_kv_heads * s.head_dim * 2 : (int64_t)(s.kv_lora_rank + s.qk_rope) * 2;
-    alg += (int64_t)s.n_layers * (n + nt) * kv_row;
+    if (s.index_heads > 0)  // every position's index key, and the latent rows of the selected positions only
+      alg += (int64_t)s.n_layers * ((n + 1) * (int64_t)s.index_dim * 2 + std::min<int64_t>(s.index_topk, n + 1) * kv_row);
+    else
+      alg += (int64_t)s.n_layers * (n + nt) * kv_row;
     P.alg_bytes = alg;
 
     std::string v = validate_plan(P);
@@ -875,12 +932,15 @@ std::string validate_plan(const PlanData& p) {
   auto expected = [&](int type) -> int64_t {
     switch (type) {
       case T_QKV: return (int64_t)(s.n_q_heads / s.n_kv_heads + 2) * s.head_dim / 2;
-      case T_ATTN: case T_MLA_ATTN: return n1;
+      case T_ATTN: return n1;
+      case T_MLA_ATTN: return s.index_heads ? std::min<int64_t>(s.index_topk, n1) : n1;  // (list entries with an indexer)
+      case T_IDX_SCORE: case T_IDX_TOPK: return n1;
+      case T_IDX_Q: return (int64_t)s.index_heads * s.index_dim;
       case T_OPROJ: case T_OPROJ_G: case T_DOWN: case T_MOE_DOWN: case T_HINIT: return s.hidden;
       case T_GATEUP: return s.ffn;
       case T_LMHEAD: return s.vocab;
       case T_ARGMAX: return 1;
-      case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope;
+      case T_MLA_A: return (int64_t)s.q_lora_rank + s.kv_lora_rank + s.qk_rope + (s.index_heads ? s.index_dim + s.index_heads : 0);
       case T_MLA_B: return (int64_t)s.n_q_heads * (s.qk_nope / 2 + s.qk_rope / 2);
       case T_MLA_KVAPP: return (int64_t)s.kv_lora_rank + s.qk_rope;
       case T_MLA_ABSORB: case T_MLA_UV: return (int64_t)s.n_q_heads * (s.kv_lora_rank / kMlaColBlock);
@@ -907,6 +967,7 @@ std::string validate_plan(const PlanData& p) {
   if (s.arch == DEC_ARCH_GQA) need = {T_QKV, T_ATTN, T_OPROJ_G, T_GATEUP, T_DOWN};
   else {
     need = {T_MLA_A, T_MLA_B, T_MLA_KVAPP, T_MLA_ABSORB, T_MLA_ATTN, T_MLA_UV, T_OPROJ};
+    if (s.index_heads) { need.push_back(T_IDX_Q); need.push_back(T_IDX_SCORE); need.push_back(T_IDX_TOPK); }
     if (s.arch == DEC_ARCH_MLA) { need.push_back(T_GATEUP); need.push_back(T_DOWN); }
     else { need.push_back(T_ROUTER); need.push_back(T_TOPK); need.push_back(T_EXPERT_GU); need.push_back(T_MOE_DOWN);
            if (s.n_shared > 0) need.push_back(T_SHARED_GU); }

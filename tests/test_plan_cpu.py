@@ -18,7 +18,8 @@ GQA_CONFIGS = ["tiny", "tiny_gain", "tiny_kv0", "tiny_mha_ragged", "small_gqa", 
                "tiny_fp8", "tiny_ragged_fp8", "small_gqa_fp8", "8b_4k_fp8"]
 MLA_CONFIGS = ["mla_tiny", "mla_small", "mla_8k", "moe_tiny", "moe_small", "moe_4k", "moe_wide_tiny", "moe_max_route",
                "moe_tiny_mxfp4", "moe_small_mxfp4", "moe_4k_mxfp4", "moe_max_route_mxfp4",
-               "mla_tiny_fp8", "mla_small_fp8", "mla_8k_fp8", "moe_tiny_fp8", "moe_small_fp8", "moe_4k_fp8"]
+               "mla_tiny_fp8", "mla_small_fp8", "mla_8k_fp8", "moe_tiny_fp8", "moe_small_fp8", "moe_4k_fp8",
+               "mla_tiny_sparse", "mla_small_sparse", "moe_tiny_sparse", "mla_32k_sparse"]
 
 
 def plan(name, dev=MI355X, **over):
@@ -120,12 +121,14 @@ def _expected_units(cfg, ttype):
         "GATEUP": g("ffn", 0), "HINIT": cfg["hidden"],
         "LMHEAD": cfg["vocab"],
         # MLA: [W_DQ; W_DKV] rows, W_UQ row pairs, the latent row, (head, 64-column) blocks
-        "MLA_A": g("q_lora_rank", 0) + g("kv_lora_rank", 0) + g("qk_rope", 0),
+        "MLA_A": g("q_lora_rank", 0) + g("kv_lora_rank", 0) + g("qk_rope", 0) + (g("index_dim", 0) + g("index_heads", 0) if g("index_heads", 0) else 0),
         "MLA_B": cfg["n_q_heads"] * (g("qk_nope", 0) // 2 + g("qk_rope", 0) // 2),
         "MLA_KVAPP": g("kv_lora_rank", 0) + g("qk_rope", 0),
         "MLA_ABSORB": cfg["n_q_heads"] * g("kv_lora_rank", 0) // 64,
         "MLA_UV": cfg["n_q_heads"] * g("kv_lora_rank", 0) // 64,
-        "MLA_ATTN": n1,
+        "MLA_ATTN": min(n1, g("index_topk", 0)) if g("index_heads", 0) else n1,  # (with the indexer: entries of the selected list)
+        # the sparse indexer: index-query rows, scored positions, the one top-T task
+        "IDX_Q": g("index_heads", 0) * g("index_dim", 0), "IDX_SCORE": n1, "IDX_TOPK": n1,
         # MoE: router rows, shared gate/up pairs, the top-k over all experts, routed pairs
         "ROUTER": g("n_routed", 0), "TOPK": g("n_routed", 0),
         "SHARED_GU": g("n_shared", 0) * g("expert_ffn", 0),
@@ -444,6 +447,33 @@ def test_fp8_latent_plan():
     unused = cfg["n_layers"] * (E - cfg["top_k"]) * per_expert
     row = (cfg["kv_lora_rank"] + cfg["qk_rope"]) * 2
     assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] - unused + cfg["n_layers"] * (cfg["kv_len"] + 1) * row
+
+
+def test_sparse_indexer_plan():
+    """Sparse-indexer plans: the indexer's three matrices after wo, a cache row of latent plus
+    index key, the index tasks in their own stages, attention splits over the selected list,
+    and the bytes per step counting every index key but only the selected latent rows."""
+    p, cfg = plan("mla_32k_sparse")
+    d = {x["name"]: x for x in p.weight_descs()}
+    H, DI, T, n = cfg["index_heads"], cfg["index_dim"], cfg["index_topk"], cfg["kv_len"]
+    assert tuple(d["layers.0.idx_wq"]["shape"]) == (H * DI, cfg["q_lora_rank"])
+    assert tuple(d["layers.0.idx_wk"]["shape"]) == (DI, cfg["hidden"]) and tuple(d["layers.0.idx_w"]["shape"]) == (H, cfg["hidden"])
+    KR = cfg["kv_lora_rank"] + cfg["qk_rope"]
+    s = p.sizes()
+    assert s["kv_bytes"] == cfg["n_layers"] * (n + 1) * (KR + DI) * 2
+    assert s["algorithmic_bytes_per_step"] == s["weight_bytes"] + cfg["n_layers"] * ((n + 1) * DI * 2 + T * KR * 2)
+    tasks = p.tasks()
+    stage = {ty: {t["stage"] for t in tasks if t["type"] == ty and t["layer"] == 0} for ty in (7, 21, 22, 23, 11)}
+    assert max(stage[7]) < min(stage[21]) and max(stage[21]) < min(stage[22]) < min(stage[23]) < min(stage[11])
+    att = sorted((t["unit_begin"], t["unit_end"]) for t in tasks if t["type"] == 11 and t["layer"] == 0)
+    assert att[0][0] == 0 and att[-1][1] == T and len(att) == T // 64
+    assert len([t for t in tasks if t["type"] == 23 and t["layer"] == 0]) == 1
+    for name, over in [("tiny", {"index_heads": 4, "index_dim": 32, "index_topk": 8}),
+                       ("mla_tiny_sparse", {"index_dim": 48}), ("mla_tiny_sparse", {"index_heads": 80}),
+                       ("mla_tiny_sparse", {"weights": "fp8"}), ("mla_tiny", {"index_topk": 8})]:
+        with pytest.raises(B.DecError) as ei:
+            plan(name, **over)
+        assert ei.value.status == -2, (name, over)
 
 
 def test_mxfp4_expert_plan():
