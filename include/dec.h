@@ -157,7 +157,8 @@ typedef struct dec_task_desc {
   int32_t id, type, layer, stage;
   int32_t wg, xcd, list_pos;
   int32_t unit_begin, unit_end;   /* rows / units / positions the task owns (type-specific) */
-  int32_t aux0, aux1;             /* type-specific: group, split, head, ... */
+  int32_t aux0, aux1;             /* type-specific: group, split, head, ...; the top-T task: aux0 =
+                                     scores per LDS chunk of its selection */
   int32_t n_deps, dep_first;      /* counters waited on (see dec_plan_deps) */
   int32_t signal;                 /* counter incremented on completion (-1: none) */
   int32_t signal2;                /* second counter (-1: none) */

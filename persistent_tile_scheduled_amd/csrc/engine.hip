@@ -2589,8 +2589,9 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of v over the workgroup's threads (thread order); scratch: 8 words.
-__device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
+// Exclusive prefix sum of v over the workgroup's threads (thread order), and the total;
+// scratch: 8 words.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -2601,84 +2602,150 @@ __device__ __forceinline__ int block_excl_scan(int v, int* scratch) {
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   int pre = 0;
-  for (int w = 0; w < wave; ++w) pre += scratch[w];
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = scratch[w];
+    pre += w < wave ? c : 0;
+    total += c;
+  }
   __syncthreads();
   return pre + incl - v;
 }
 
 // The top T of the N = n + 1 scores, ties to the lower position, written in increasing position
-// order (all positions when N <= T). Radix selection over the keys, eight bits per pass from the
-// top, finds the T-th largest key K and how many of the keys equal to K are taken; one more pass
-// compacts, each thread over a contiguous block of positions so that the order is kept.
+// order (all positions when N <= T). The scores go to LDS as order-preserving unsigned keys'
+// sources, in chunks of C (once, when N <= C). A min/max pass finds the bits every key shares;
+// radix passes of up to 11 bits below them narrow the prefix of the T-th largest key and how many
+// of the keys with that prefix are still to take, until either the whole bucket is taken or every
+// bit is fixed. A last pass compacts: each thread scans a contiguous block of positions (an odd
+// number of them, so that the block starts fall in distinct LDS banks) and the block prefix sums
+// give each taken position its slot.
 __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const TaskDesc& t) {
   const LayerDesc& L = A.layers[t.layer];
-  const int N = b.n + 1, T = A.idx_t;
+  const int N = b.n + 1, T = A.idx_t, C = t.a0;
   if (!wait_deps(A, b, t)) return false;
-  const uint32_t so = (uint32_t)L.act[LA_IDXS] * 4u, sel = (uint32_t)L.act[LA_IDXSEL] * 4u;
+  const uint32_t sel = (uint32_t)L.act[LA_IDXSEL] * 4u;
   if (N <= T) {
     for (int i = threadIdx.x; i < N; i += kThreads) cst(b.act, sel + (uint32_t)i * 4u, __int_as_float(i));
     return true;
   }
-  uint32_t* hist = reinterpret_cast<uint32_t*>(b.xs);  // [256]
-  int* misc = reinterpret_cast<int*>(b.xs) + 256;      // [0] digit, [1] still needed, [8..15] scan
-  const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0, mask = 0;
-  int need = T;  // keys still to take among those matching the prefix
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += kThreads) hist[i] = 0u;
+  constexpr int kBins = kIdxBins;
+  float* SC = b.xs;                                                // [C] one chunk of scores
+  uint32_t* hist = reinterpret_cast<uint32_t*>(b.xs + C);          // [kBins]
+  int* misc = reinterpret_cast<int*>(b.xs + C + kBins);            // [0..2] choice, [8..15] scan, [16..31] min/max
+  const float* src = b.actp + L.act[LA_IDXS];
+  const int nch = (N + C - 1) / C, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(kBins == 4 * kThreads, "the bin scan gives each thread four bins");
+  // DMA of chunk c into SC; `chunk` returns chunk c's length, loading it unless the one chunk
+  // is resident
+  auto fetch = [&](int c) {
+    const int c0 = c * C, cnt = N - c0 < C ? N - c0 : C;
+    __syncthreads();  // the previous chunk's readers are done
+    dma_to_lds_all(SC, src + c0, (cnt + 3) & ~3);
     __syncthreads();
-    for (int i = threadIdx.x; i < N; i += kThreads) {
-      const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
-      if ((k & mask) == prefix) atomicAdd(hist + ((k >> shift) & 255u), 1u);
+    return cnt;
+  };
+  auto chunk = [&](int c) { return nch == 1 ? N : fetch(c); };
+  if (nch == 1) fetch(0);
+  // the keys' common high bits
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int c = 0; c < nch; ++c) {
+    const int cnt = chunk(c);
+    for (int i = threadIdx.x; i < cnt; i += kThreads) {
+      const uint32_t k = score_key(SC[i]);
+      kmin = k < kmin ? k : kmin;
+      kmax = k > kmax ? k : kmax;
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)kmin, d, 64), c = (uint32_t)__shfl_xor((int)kmax, d, 64);
+    kmin = a < kmin ? a : kmin;
+    kmax = c > kmax ? c : kmax;
+  }
+  if (lane == 0) {
+    misc[16 + wave] = (int)kmin;
+    misc[24 + wave] = (int)kmax;
+  }
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t a = (uint32_t)misc[16 + w], c = (uint32_t)misc[24 + w];
+    kmin = a < kmin ? a : kmin;
+    kmax = c > kmax ? c : kmax;
+  }
+  // bits at and above `lo` are fixed: keys whose masked value exceeds `prefix` are all taken, and
+  // `need` of those equal to it
+  int lo = kmin == kmax ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = lo >= 32 ? 0u : ~((1u << lo) - 1u), prefix = kmax & mask;
+  int need = T;
+  while (lo > 0) {
+    const int width = lo < 11 ? lo : 11, shift = lo - width;
+    const uint32_t dm = (1u << width) - 1u;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int cnt = chunk(c);
+      for (int i = threadIdx.x; i < cnt; i += kThreads) {
+        const uint32_t k = score_key(SC[i]);
+        if ((k & mask) == prefix) atomicAdd(hist + ((k >> shift) & dm), 1u);
+      }
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      // lane l holds digits 255 - 4l .. 252 - 4l (from the top)
-      uint32_t c[4];
+    // thread j holds bins kBins-1-4j .. kBins-4-4j (from the top)
+    uint32_t h[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[255 - 4 * lane - j];
-      const int sum = (int)(c[0] + c[1] + c[2] + c[3]);
-      int incl = sum;
+    for (int q = 0; q < 4; ++q) h[q] = hist[kBins - 1 - 4 * (int)threadIdx.x - q];
+    const int sum = (int)(h[0] + h[1] + h[2] + h[3]);
+    int tot;
+    int before = block_excl_scan(sum, misc + 8, tot);  // keys in higher bins than this thread's
+    if (before < need && need <= before + sum) {
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += y;
-      }
-      int before = incl - sum;  // keys with a larger digit than this lane's
-      if (before < need && need <= incl) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (need <= before + (int)c[j]) {
-            misc[0] = 255 - 4 * lane - j;
-            misc[1] = need - before;
-            break;
-          }
-          before += (int)c[j];
+      for (int q = 0; q < 4; ++q) {
+        if (need <= before + (int)h[q]) {
+          misc[0] = kBins - 1 - 4 * (int)threadIdx.x - q;
+          misc[1] = need - before;
+          misc[2] = (int)h[q];
+          break;
         }
+        before += (int)h[q];
       }
     }
     __syncthreads();
     prefix |= (uint32_t)misc[0] << shift;
-    mask |= 255u << shift;
+    mask |= dm << shift;
     need = misc[1];
+    lo = shift;
+    const bool whole = need == misc[2];
     __syncthreads();
+    if (whole) break;
   }
-  // keys above `prefix` are all taken; of those equal to it, the `need` at the lowest positions
-  const int B = (N + kThreads - 1) / kThreads, i0 = threadIdx.x * B, i1 = (i0 + B < N) ? i0 + B : N;
-  int gt = 0, eq = 0;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
-    gt += k > prefix;
-    eq += k == prefix;
-  }
-  const int eqb = block_excl_scan(eq, misc + 8);
-  int take = need - eqb;
-  take = take < 0 ? 0 : (take > eq ? eq : take);
-  int out = block_excl_scan(gt + take, misc + 8);
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t k = score_key(cld(b.act, so + (uint32_t)i * 4u));
-    if (k > prefix || (k == prefix && take-- > 0)) cst(b.act, sel + (uint32_t)(out++) * 4u, __int_as_float(i));
+  // compaction, chunk by chunk in position order
+  int eq_seen = 0, out_seen = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int cnt = chunk(c), c0 = c * C;
+    const int B = ((cnt + kThreads - 1) / kThreads) | 1;
+    const int i0 = (int)threadIdx.x * B < cnt ? (int)threadIdx.x * B : cnt, i1 = i0 + B < cnt ? i0 + B : cnt;
+    int gt = 0, eq = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = score_key(SC[i]) & mask;
+      gt += k > prefix;
+      eq += k == prefix;
+    }
+    int eq_tot, out_tot;
+    const int eqb = eq_seen + block_excl_scan(eq, misc + 8, eq_tot);
+    int take = need - eqb;
+    take = take < 0 ? 0 : (take > eq ? eq : take);
+    int out = out_seen + block_excl_scan(gt + take, misc + 8, out_tot);
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = score_key(SC[i]) & mask;
+      if (k > prefix || (k == prefix && take-- > 0)) cst(b.act, sel + (uint32_t)(out++) * 4u, __int_as_float(c0 + i));
+    }
+    eq_seen += eq_tot;
+    out_seen += out_tot;
   }
   return true;
 }

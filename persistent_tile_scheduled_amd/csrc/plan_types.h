@@ -23,6 +23,7 @@ constexpr int kMaxVerifyCols = 8;      // query columns (tokens x heads of a KV 
 constexpr int kMlaHeads = 16;          // query heads folded into one MFMA tile
 constexpr int kMlaChunk = 64;          // positions per LDS-resident latent chunk
 constexpr int kMlaColBlock = 64;       // latent columns per absorb / W_UV task
+constexpr int kIdxBins = 2048;          // histogram bins of one top-T radix pass (11-bit digits)
 // GQA: a workgroup's QKV task can put the cached K/V rows of the attention split that
 // follows it into LDS (issued by the streaming waves with their row prefetch, ahead of the
 // dependency wait). Each streaming wave issues kKvStageDma 1-KB LDS DMA chunks (K and V

@@ -533,7 +533,6 @@ struct Builder {
       L.act[LA_IDXSEL] = (int)act(p + "idx_sel", m_sel, DEC_DTYPE_I32);
       // score task: the queries (fp32), their MFMA operand (bf16 hi + lo, 16-head tiles), weights
       need_xs((int64_t)HI * DI + (int64_t)((HI + 15) / 16) * (DI / 32) * 2 * 256 + 64);
-      need_xs(256 + 64 + 16);  // top-k: histogram and scan words
     }
 
     // A: [W_DQ; W_DKV] rows from the normalised layer input (with the indexer: then the rows of
@@ -573,9 +572,15 @@ struct Builder {
         const int w = (int)((int64_t)i * n_wg / NS);
         add(w, T_IDX_SCORE, l, (int)((n + 1) * i / NS), (int)((n + 1) * (i + 1) / NS), dsc, csc + slot(w), -1, 0, i, NS);
       }
+      // top-T: the scores in LDS in chunks of C (all of them when they fit beside the histogram
+      // and the scan words, in the LDS region after the header)
       ++stage;
       ctop = counter(1);
-      add(n_wg - 1, T_IDX_TOPK, l, 0, (int)(n + 1), all_of(csc, nsc), ctop);
+      const int64_t room = ((int64_t)dev.lds_bytes_per_cu / 4 - 64 - kIdxBins - 64) / 256 * 256;
+      // (a device with less LDS than that fails the plan's LDS check)
+      const int64_t C = std::min<int64_t>(align_up(n + 1, 256), std::max<int64_t>(room, 256));
+      add(n_wg - 1, T_IDX_TOPK, l, 0, (int)(n + 1), all_of(csc, nsc), ctop, -1, (int)C);
+      mla_lds = std::max<int64_t>(mla_lds, C + kIdxBins + 64);
     }
 
     // absorb: q_abs[h][c-block] = W_UK[h]^T q_nope[h], one (head, 64-column block) per task

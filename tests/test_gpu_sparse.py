@@ -130,3 +130,62 @@ def test_sparse_plan_with_per_step_length():
         for l in range(cfg["n_layers"]):
             check_sparse_layer(eng, cfg_p, W, l, _layer_inputs(eng, x, l), workloads.bf16_bits(kv[l]), p)
     check_coverage(eng, steps=6)
+
+
+def _topk_chunk(eng):
+    """Scores per LDS chunk of the top-T task (its first type-specific field)."""
+    ty = {v: k for k, v in __import__("persistent_tile_scheduled_amd.binding", fromlist=["TASK_TYPES"]).TASK_TYPES.items()}
+    return [t["aux0"] for t in eng.plan.tasks() if t["type"] == ty["IDX_TOPK"]][0]
+
+
+def test_sparse_topk_in_chunks():
+    """Caches longer than one LDS chunk of scores: the selection runs chunk by chunk. A plan for
+    up to 90000 positions, stepped at exactly one full chunk, one position more (a second chunk
+    of one score), and a length spanning three chunks."""
+    cfg = workloads.get_config("mla_tiny_sparse")
+    M = 90000
+    w, x, kv = workloads.generate(cfg, seed=4, device="cuda", kv_len=M)
+    eng = _engine(cfg, w, max_len=M)
+    C = _topk_chunk(eng)
+    assert 256 <= C < M // 2 and C % 256 == 0, C
+    W = HostWeights(w)
+    steps = 0
+    for p in [C - 1, C, M]:
+        print(f"[sparse] chunked top-T: chunk {C}, position {p}", flush=True)
+        eng.set_state(p, 0)
+        eng.step_dynamic(kv, x)
+        steps += 1
+        torch.cuda.synchronize()
+        eng.status()
+        cfg_p = dict(cfg, kv_len=p)
+        for l in range(cfg["n_layers"]):
+            check_sparse_layer(eng, cfg_p, W, l, _layer_inputs(eng, x, l), workloads.bf16_bits(kv[l]), p)
+    check_coverage(eng, steps=steps)
+
+
+@pytest.mark.parametrize("distinct", [5, 1])
+def test_sparse_topk_ties(distinct):
+    """Planted exact ties: the cached index keys repeat `distinct` rows (position p holds row
+    p % distinct), so the scores take distinct + 1 values (the new position's key is this
+    step's) and the selection boundary falls inside a group of equal scores, which must be taken
+    at the lowest positions."""
+    cfg = dict(workloads.get_config("mla_tiny_sparse"), kv_len=500)
+    n = cfg["kv_len"]
+    KR = cfg["kv_lora_rank"] + cfg["qk_rope"]
+    DI = cfg["index_dim"]
+    w, x, kv = workloads.generate(cfg, seed=5, device="cuda")
+    for l in range(cfg["n_layers"]):
+        rows = kv[l][:distinct, KR:KR + DI].clone()
+        idx = torch.arange(n, device=kv[l].device) % distinct
+        kv[l][:n, KR:KR + DI] = rows[idx]
+    print(f"[sparse] ties: {distinct} distinct cached index keys", flush=True)
+    eng = _engine(cfg, w)
+    eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    W = HostWeights(w)
+    for l in range(cfg["n_layers"]):
+        sc = eng.buffer(f"layers.{l}.idx_scores").cpu().numpy()[:n + 1]
+        assert len(np.unique(sc)) <= distinct + 1, (l, len(np.unique(sc)))
+        check_sparse_layer(eng, cfg, W, l, _layer_inputs(eng, x, l), workloads.bf16_bits(kv[l]), n)
+    check_coverage(eng)
