@@ -2647,17 +2647,40 @@ __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const
     return cnt;
   };
   auto chunk = [&](int c) { return nch == 1 ? N : fetch(c); };
+  // f(key) for the chunk's keys i = thread, thread + kThreads, ...: eight LDS reads in flight
+  // per thread (one at a time, each read's latency was paid in full: 3.6 us per pass over 32769)
+  auto strided = [&](int cnt, auto&& f) {
+    int i = threadIdx.x;
+    for (; i + 7 * kThreads < cnt; i += 8 * kThreads) {
+      uint32_t k[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k[u] = score_key(SC[i + u * kThreads]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f(k[u]);
+    }
+    for (; i < cnt; i += kThreads) f(score_key(SC[i]));
+  };
+  // f(masked key, i) for i = i0 .. i1 - 1 in order, eight reads in flight
+  auto in_order = [&](int i0, int i1, uint32_t m, auto&& f) {
+    int i = i0;
+    for (; i + 8 <= i1; i += 8) {
+      uint32_t k[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) k[u] = score_key(SC[i + u]) & m;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f(k[u], i + u);
+    }
+    for (; i < i1; ++i) f(score_key(SC[i]) & m, i);
+  };
   if (nch == 1) fetch(0);
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[0] = (uint32_t)now();
   // the keys' common high bits
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int c = 0; c < nch; ++c) {
-    const int cnt = chunk(c);
-    for (int i = threadIdx.x; i < cnt; i += kThreads) {
-      const uint32_t k = score_key(SC[i]);
+  for (int c = 0; c < nch; ++c)
+    strided(chunk(c), [&](uint32_t k) {
       kmin = k < kmin ? k : kmin;
       kmax = k > kmax ? k : kmax;
-    }
-  }
+    });
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t a = (uint32_t)__shfl_xor((int)kmin, d, 64), c = (uint32_t)__shfl_xor((int)kmax, d, 64);
@@ -2679,6 +2702,7 @@ __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const
   }
   // bits at and above `lo` are fixed: keys whose masked value exceeds `prefix` are all taken, and
   // `need` of those equal to it
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[1] = (uint32_t)now();
   int lo = kmin == kmax ? 0 : 32 - __builtin_clz(kmin ^ kmax);
   uint32_t mask = lo >= 32 ? 0u : ~((1u << lo) - 1u), prefix = kmax & mask;
   int need = T;
@@ -2687,13 +2711,10 @@ __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const
     const uint32_t dm = (1u << width) - 1u;
     for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const int cnt = chunk(c);
-      for (int i = threadIdx.x; i < cnt; i += kThreads) {
-        const uint32_t k = score_key(SC[i]);
+    for (int c = 0; c < nch; ++c)
+      strided(chunk(c), [&](uint32_t k) {
         if ((k & mask) == prefix) atomicAdd(hist + ((k >> shift) & dm), 1u);
-      }
-    }
+      });
     __syncthreads();
     // thread j holds bins kBins-1-4j .. kBins-4-4j (from the top)
     uint32_t h[4];
@@ -2723,6 +2744,7 @@ __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const
     __syncthreads();
     if (whole) break;
   }
+  if (kTaskLogDetail && threadIdx.x == 0) b.t_sub[2] = (uint32_t)now();
   // compaction, chunk by chunk in position order
   int eq_seen = 0, out_seen = 0;
   for (int c = 0; c < nch; ++c) {
@@ -2730,20 +2752,18 @@ __device__ __forceinline__ bool task_idx_topk(const EngineArgs& A, Blk& b, const
     const int B = ((cnt + kThreads - 1) / kThreads) | 1;
     const int i0 = (int)threadIdx.x * B < cnt ? (int)threadIdx.x * B : cnt, i1 = i0 + B < cnt ? i0 + B : cnt;
     int gt = 0, eq = 0;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = score_key(SC[i]) & mask;
+    in_order(i0, i1, mask, [&](uint32_t k, int) {
       gt += k > prefix;
       eq += k == prefix;
-    }
+    });
     int eq_tot, out_tot;
     const int eqb = eq_seen + block_excl_scan(eq, misc + 8, eq_tot);
     int take = need - eqb;
     take = take < 0 ? 0 : (take > eq ? eq : take);
     int out = out_seen + block_excl_scan(gt + take, misc + 8, out_tot);
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = score_key(SC[i]) & mask;
+    in_order(i0, i1, mask, [&](uint32_t k, int i) {
       if (k > prefix || (k == prefix && take-- > 0)) cst(b.act, sel + (uint32_t)(out++) * 4u, __int_as_float(c0 + i));
-    }
+    });
     eq_seen += eq_tot;
     out_seen += out_tot;
   }

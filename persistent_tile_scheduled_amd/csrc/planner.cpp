@@ -35,6 +35,7 @@ constexpr int kStageCounters = DEC_STAGE_COUNTERS;  // completion counters per s
 #endif
 constexpr double kOddXcdSpeed = DEC_ODD_XCD_SPEED;  // relative streaming speed of XCDs 1, 3, 5, 7
 constexpr int kMinPosMla = 64;             // positions per latent-attention split (at least)
+constexpr int kMinPosMlaSparse = 32;       // the same over the indexer's selected positions
 constexpr int kIdxPos = 128;               // positions per sparse-indexer score task (at least)
 constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
@@ -587,12 +588,15 @@ struct Builder {
     ++stage;
     const int cabs = counter(nsc);
     const int nblk = nh * (kl / kMlaColBlock);
-    spread(all_wgs(), nblk, 1, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + slot(w)); });
+    // (with the indexer, not on the top-T workgroup: every attention split waits for every
+    // absorb task, and one queued behind the selection would hold them all)
+    spread(HI ? bw : all_wgs(), nblk, 1, [&](int w, int a, int b) { add(w, T_MLA_ABSORB, l, a, b, db, cabs + slot(w)); });
 
     // latent attention: S position splits, all heads folded into one MFMA tile
     ++stage;
     const int catt = counter(nsc);
-    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (m_sel + kMinPosMla - 1) / kMinPosMla));
+    const int minpos = HI ? kMinPosMlaSparse : kMinPosMla;
+    const int S = (int)std::min<int64_t>(n_wg, std::max<int64_t>(1, (m_sel + minpos - 1) / minpos));
     const int Sp = (S + 1) & ~1;  // per-head stride of the (M, Lr) table (16-byte rows)
     const int64_t pml = act(p + "attn_ml", (int64_t)nh * Sp * 2);
     const int64_t part = act(p + "attn_partials", (int64_t)S * nh * kl);
@@ -604,7 +608,10 @@ struct Builder {
     if (HI) dat.push_back(ctop);
     // (with the indexer a split is a range of the selected-position list, not of positions)
     for (int sp = 0; sp < S; ++sp) {
-      const int w = (int)((int64_t)sp * n_wg / S);
+      int w = (int)((int64_t)sp * n_wg / S);
+      // the indexer's few splits gather scattered rows: one per XCD in turn (workgroup w runs
+      // on XCD w mod n_xcd), not every split on the XCDs an even stride lands on
+      if (HI && n_xcd > 0 && (int64_t)n_xcd * ((S + n_xcd - 1) / n_xcd) <= n_wg) w = (sp % n_xcd) + n_xcd * (sp / n_xcd) * (n_wg / n_xcd / ((S + n_xcd - 1) / n_xcd));
       int p0 = (int)(m_sel * sp / S), p1 = (int)(m_sel * (sp + 1) / S);
       add(w, T_MLA_ATTN, l, p0, p1, dat, catt + slot(w), -1, 0, sp, S, 0, (int)pml, (int)part);
     }

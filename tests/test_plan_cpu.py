@@ -466,8 +466,15 @@ def test_sparse_indexer_plan():
     stage = {ty: {t["stage"] for t in tasks if t["type"] == ty and t["layer"] == 0} for ty in (7, 21, 22, 23, 11)}
     assert max(stage[7]) < min(stage[21]) and max(stage[21]) < min(stage[22]) < min(stage[23]) < min(stage[11])
     att = sorted((t["unit_begin"], t["unit_end"]) for t in tasks if t["type"] == 11 and t["layer"] == 0)
-    assert att[0][0] == 0 and att[-1][1] == T and len(att) == T // 64
-    assert len([t for t in tasks if t["type"] == 23 and t["layer"] == 0]) == 1
+    assert att[0][0] == 0 and att[-1][1] == T and len(att) == T // 32
+    top = [t for t in tasks if t["type"] == 23 and t["layer"] == 0]
+    assert len(top) == 1
+    # the splits of the selected list go to the XCDs in turn, on distinct workgroups, and no
+    # absorb task (which every split waits for) sits behind the selection on its workgroup
+    att_t = sorted((t for t in tasks if t["type"] == 11 and t["layer"] == 0), key=lambda t: t["aux1"])
+    assert [t["xcd"] for t in att_t] == [i % 8 for i in range(len(att_t))]
+    assert len({t["wg"] for t in att_t}) == len(att_t) and top[0]["wg"] not in {t["wg"] for t in att_t}
+    assert all(t["wg"] != top[0]["wg"] for t in tasks if t["type"] == 10)
     for name, over in [("tiny", {"index_heads": 4, "index_dim": 32, "index_topk": 8}),
                        ("mla_tiny_sparse", {"index_dim": 48}), ("mla_tiny_sparse", {"index_heads": 80}),
                        ("mla_tiny_sparse", {"weights": "fp8"}), ("mla_tiny", {"index_topk": 8})]:
