@@ -238,7 +238,9 @@ def generation(args, cfg, w, kv, x):
         w["embed"] = workloads.generate_embedding(cfg, seed=args.seed, device="cuda")
     xin = None if greedy else x
     eng = DecodeEngine(cfg, w, max_len=n)
-    p0 = n - T - W
+    p0 = n - T - W if args.start_pos is None else args.start_pos
+    if not 0 <= p0 <= n - T - W:
+        raise SystemExit("--start-pos P needs 0 <= P <= kv_len - T - warmup")
     eng.set_state(p0, 0)
     for _ in range(W):
         eng.step_dynamic(kv, xin)
@@ -254,7 +256,7 @@ def generation(args, cfg, w, kv, x):
     wall = time.perf_counter() - t0
     eng.status()
     st = eng.read_state()
-    assert st[0] == n and st[2] == T + W, st
+    assert st[0] == p0 + T + W and st[2] == T + W, st
     gpu_us = a.elapsed_time(b) * 1e3 / T
     us = wall * 1e6 / T
     print(json.dumps({
@@ -264,7 +266,7 @@ def generation(args, cfg, w, kv, x):
         "higher_is_better": False, "tokens_per_s": round(1e6 / us, 1),
         "gpu_us_per_token": round(gpu_us, 2),
         "config": {"workload": f"{args.config}: {WORKLOADS.get(args.config, args.config)}",
-                   "positions": [n - T, n - 1], "batch": 1},
+                   "positions": [p0 + W, p0 + W + T - 1], "max_len": n, "batch": 1},
         "launch": "dynamic plan (max_len = kv_len), one launch per token, no host work between tokens",
         "dtype": "bf16", "data": "synthetic"}), flush=True)
     teardown(eng)
@@ -283,6 +285,9 @@ def main():
     ap.add_argument("--launch", choices=["persistent", "stages", "graph"], default="persistent",
                     help="persistent: the step as one engine launch (the product); stages: one launch per "
                          "stage of the same tasks; graph: those launches replayed from a HIP graph")
+    ap.add_argument("--start-pos", type=int, default=None, metavar="P",
+                    help="with --generate: the position of the first warm-up step (default kv_len - T - warmup, "
+                         "so that the timed steps end at the plan's largest position)")
     ap.add_argument("--generate", type=int, default=0, metavar="T",
                     help="time T greedy steps of a plan with a per-step length, issued back to back "
                          "(positions kv_len - T .. kv_len - 1, each step's token from the last)")
