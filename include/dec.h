@@ -184,13 +184,17 @@ typedef struct dec_buffer_desc {
 
 /* ---- planning (host only; no device memory is touched) ---- */
 
-/* Plan for the current HIP device. Errors: SHAPE, CAPACITY (kv_len < 0 or too large),
- * DEVICE (not gfx950), OCCUPANCY, INVAL (null). */
+/* Plan for the current HIP device: unroll the whole layer stack for this shape and cache
+ * length into tile tasks, dependency counters and per-workgroup lists, ahead of time ("Static
+ * Compilation for LLM Inference", section 1: the model compiled once into one engine; section
+ * 5.6: a static schedule rather than a dynamic dispatcher). Errors: SHAPE, CAPACITY (kv_len < 0
+ * or too large), DEVICE (not gfx950), OCCUPANCY, INVAL (null). */
 dec_status dec_plan_create(const dec_model_shape* shape, int64_t kv_len, struct dec_plan** out);
 /* Plan for an explicitly described device (CPU-only testing and cross-planning). */
 dec_status dec_plan_create_for(const dec_model_shape* shape, int64_t kv_len,
                                const dec_device_info* dev, struct dec_plan** out);
-dec_status dec_plan_destroy(struct dec_plan* plan);     /* NULL is a no-op */
+/* Free the host-side plan (the caller's device buffers are not touched). NULL is a no-op. */
+dec_status dec_plan_destroy(struct dec_plan* plan);
 
 /* The weight list in bind order (the layout contract). */
 int64_t dec_plan_n_weights(const struct dec_plan* plan);
@@ -213,7 +217,9 @@ dec_status dec_plan_grid(const struct dec_plan* plan, int32_t* n_wg, int32_t* th
 
 /* Bind caller-owned weight buffers (n == dec_plan_n_weights, in weight_desc order, each
  * 16-byte aligned) and a workspace of >= workspace_bytes (256-byte aligned). Uploads the
- * task table and zeroes counters/status on `stream` (asynchronously). Errors: INVAL, HIP. */
+ * task table and zeroes counters/status on `stream` (asynchronously): the "prepare once"
+ * half of the prepare-then-run interface on the TileRT audit page (weights bound before the
+ * first run). Errors: INVAL, HIP. */
 dec_status dec_plan_bind(struct dec_plan* plan, const void* const* weights, int64_t n,
                          void* workspace, int64_t workspace_bytes, void* stream);
 
@@ -232,7 +238,9 @@ dec_status dec_plan_bind(struct dec_plan* plan, const void* const* weights, int6
  * static array holds), DEVICE, HIP. */
 dec_status dec_plan_bind_scratch(struct dec_plan* plan, const void* const* weights, int64_t n, void* stream);
 
-/* Run one decode step: ONE kernel launch on `stream`.
+/* Run one decode step: ONE kernel launch on `stream` (the per-token run of the audit page's
+ * prepare-then-run interface; the single engine launch of "Static Compilation for LLM
+ * Inference", sections 1 and 6, in place of one launch per operator).
  *   x   : bf16 [hidden], the new token's input hidden state (read only).
  *   kv  : bf16 cache. GQA: [n_layers][2][n_kv_heads][kv_len+1][head_dim] (K then V);
  *         MLA/MOE: [n_layers][kv_len+1][kv_lora_rank + qk_rope] (c || k_pe).
@@ -321,7 +329,9 @@ dec_status dec_step_dynamic(struct dec_plan* plan, const void* x, void* kv, void
 dec_status dec_plan_create_verify(const dec_model_shape* shape, int64_t kv_len, int32_t n_tokens,
                                   const dec_device_info* dev, struct dec_plan** out);
 
-/* Synchronise `stream` and read the sticky device status word: DEC_OK, DEC_E_TIMEOUT (the
+/* (Control calls: no passage of the pages covers them; they report and clear the device-side
+ * watchdog that keeps a stuck dependency wait from hanging the persistent kernel.)
+ * Synchronise `stream` and read the sticky device status word: DEC_OK, DEC_E_TIMEOUT (the
  * failing task id is in dec_last_error()) or DEC_E_CAPACITY (a dec_step_dynamic state out of
  * range). */
 dec_status dec_plan_status(struct dec_plan* plan, void* stream);
