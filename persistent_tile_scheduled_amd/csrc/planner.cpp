@@ -35,7 +35,7 @@ constexpr int kStageCounters = DEC_STAGE_COUNTERS;  // completion counters per s
 #endif
 constexpr double kOddXcdSpeed = DEC_ODD_XCD_SPEED;  // relative streaming speed of XCDs 1, 3, 5, 7
 constexpr int kMinPosMla = 64;             // positions per latent-attention split (at least)
-constexpr int kMinPosMlaSparse = 32;       // the same over the indexer's selected positions
+constexpr int kMinPosMlaSparse = 16;       // the same over the indexer's selected positions
 constexpr int kIdxPos = 128;               // positions per sparse-indexer score task (at least)
 constexpr int64_t kMergeFloats = 17000;    // LDS floats for one group's attention partials
 
@@ -553,14 +553,17 @@ struct Builder {
     add(n_wg - 1, T_MLA_KVAPP, l, 0, KR, da, ckv);
     std::vector<int> bw = all_wgs();
     if (n_wg > 1) bw.pop_back();
+    // the sparse indexer's query rows go ahead of W_UQ in each list: the scores and the
+    // selection after them are the longer path to the attention (the absorb tasks after W_UQ
+    // finish well before the selection)
+    const int cq = HI ? counter(nsc) : -1;
+    if (HI) spread(bw, HI * DI, kRowsCap, [&](int w, int a, int b) { add(w, T_IDX_Q, l, a, b, da, cq + slot(w)); });
     spread(bw, nh * UH, kRowsCap / 2, [&](int w, int a, int b) { add(w, T_MLA_B, l, a, b, da, cb + slot(w)); });
     auto db = all_of(cb, nsc);
 
-    // the sparse indexer: index-query rows (beside W_UQ), scores of every position, the top-T
+    // the sparse indexer: index-query rows (above), scores of every position, the top-T
     int ctop = -1;
     if (HI) {
-      const int cq = counter(nsc);
-      spread(bw, HI * DI, kRowsCap, [&](int w, int a, int b) { add(w, T_IDX_Q, l, a, b, da, cq + slot(w)); });
       ++stage;
       const int csc = counter(nsc);
       std::vector<int32_t> dsc = da;

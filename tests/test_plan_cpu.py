@@ -466,7 +466,7 @@ def test_sparse_indexer_plan():
     stage = {ty: {t["stage"] for t in tasks if t["type"] == ty and t["layer"] == 0} for ty in (7, 21, 22, 23, 11)}
     assert max(stage[7]) < min(stage[21]) and max(stage[21]) < min(stage[22]) < min(stage[23]) < min(stage[11])
     att = sorted((t["unit_begin"], t["unit_end"]) for t in tasks if t["type"] == 11 and t["layer"] == 0)
-    assert att[0][0] == 0 and att[-1][1] == T and len(att) == T // 32
+    assert att[0][0] == 0 and att[-1][1] == T and len(att) == T // 16
     top = [t for t in tasks if t["type"] == 23 and t["layer"] == 0]
     assert len(top) == 1
     # the splits of the selected list go to the XCDs in turn, on distinct workgroups, and no
