@@ -80,8 +80,8 @@ class DecodeEngine:
         if x is not None:
             self._check_io(x, kv, out)
         else:
-            if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
-                raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+            if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous() or not kv.is_cuda:
+                raise ValueError(f"kv must be a contiguous cuda bf16 tensor of {self.sizes['kv_bytes']} bytes")
             if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"] or not out.is_contiguous() or not out.is_cuda:
                 raise ValueError("out must be contiguous cuda fp32 of length vocab (or hidden)")
         self.plan.step_dynamic(0 if x is None else x.data_ptr(), kv.data_ptr(), out.data_ptr(), self.state.data_ptr(),
@@ -90,10 +90,10 @@ class DecodeEngine:
 
     def _check_io(self, x, kv, out):
         torch = self.torch
-        if x.dtype != torch.bfloat16 or x.numel() * 2 != self.sizes["x_bytes"] or not x.is_contiguous():
-            raise ValueError("x must be contiguous bf16 [tokens per step][hidden]")
-        if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous():
-            raise ValueError(f"kv must be a contiguous bf16 tensor of {self.sizes['kv_bytes']} bytes")
+        if x.dtype != torch.bfloat16 or x.numel() * 2 != self.sizes["x_bytes"] or not x.is_contiguous() or not x.is_cuda:
+            raise ValueError("x must be contiguous cuda bf16 [tokens per step][hidden]")
+        if kv.dtype != torch.bfloat16 or kv.numel() * 2 != self.sizes["kv_bytes"] or not kv.is_contiguous() or not kv.is_cuda:
+            raise ValueError(f"kv must be a contiguous cuda bf16 tensor of {self.sizes['kv_bytes']} bytes")
         if out.dtype != torch.float32 or out.numel() * 4 != self.sizes["out_bytes"] or not out.is_contiguous() or not out.is_cuda:
             raise ValueError("out must be contiguous cuda fp32 [tokens per step][vocab (or hidden)]")
 

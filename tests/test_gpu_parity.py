@@ -238,6 +238,24 @@ def test_multi_step_changing_input(name):
     check_coverage(eng, steps=3)
 
 
+def test_host_tensors_and_wrong_shapes_are_refused():
+    """The binding refuses, before any launch, inputs the kernel could not address: host
+    tensors, a wrong dtype or size; the engine then still steps correctly."""
+    cfg = workloads.get_config("tiny")
+    w, x, kv = workloads.generate(cfg, seed=3, device="cuda")
+    eng = _engine()(cfg, w)
+    print("[refuse] host x, host kv, wrong dtype, short out", flush=True)
+    for bad in ((x.cpu(), kv, None), (x, kv.cpu(), None), (x.float(), kv, None),
+                (x, kv, torch.empty(7, dtype=torch.float32, device="cuda"))):
+        with pytest.raises(ValueError):
+            eng.step(*bad)
+    out = eng.step(x, kv)
+    torch.cuda.synchronize()
+    eng.status()
+    res = O.forward(cfg, HostWeights(w), workloads.bf16_bits(x), workloads.bf16_bits(kv))
+    assert rel_l2(out.cpu().numpy(), res["out"]) <= LOGIT_TOL
+
+
 def test_watchdog_timeout_then_reset():
     """A host-forced 1 us watchdog makes dependency waits time out; every workgroup drains,
     the sticky status reports DEC_E_TIMEOUT, and after a reset the next step is correct."""
