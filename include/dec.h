@@ -66,13 +66,16 @@ typedef enum {
 
 typedef enum {
   DEC_WEIGHTS_BF16 = 0,      /* every matrix bf16 */
-  DEC_WEIGHTS_FP8_E4M3 = 1,  /* GQA only: each linear matrix (wq, wk, wv, wo, w_gate, w_up,
-                                w_down, lm_head) as OCP FP8 E4M3 bytes [rows][cols], followed in
-                                the weight list by "<name>.scale", fp32 [rows]: row r of the
-                                matrix is scale[r] * e4m3(bytes[r][:]). cols must be a multiple
-                                of 16. Norm gains (and "embed") stay bf16. This is the survey's
-                                next lever on bytes per token; the pages name the lever (fewer
-                                bytes moved per token), not a format. */
+  DEC_WEIGHTS_FP8_E4M3 = 1,  /* every family: each linear matrix as OCP FP8 E4M3 bytes
+                                [rows][cols] (stacked experts [E][rows][cols]), followed in the
+                                weight list by "<name>.scale", fp32 [rows] ([E][rows]): row r of
+                                the matrix is scale[r] * e4m3(bytes[r][:]). GQA: wq, wk, wv, wo,
+                                w_gate, w_up, w_down, lm_head; latent families: every linear
+                                matrix but the per-head absorption matrices w_uk, w_uv and the
+                                router. cols must be a multiple of 16. Norm gains (and "embed")
+                                stay bf16. The pages name the lever (fewer bytes moved per
+                                token), not a format; the audit page names an FP8 dequantisation
+                                fused into the attention's input projection. */
   DEC_WEIGHTS_MXFP4 = 2      /* MoE only: every expert matrix (experts.w_gate / w_up / w_down and
                                 shared.w_gate / w_up / w_down) in the OCP Microscaling FP4 format:
                                 E2M1 elements packed two per byte, uint8 [..][cols / 2], element 2i

@@ -51,8 +51,7 @@ Weights are passed as a callable W(name, index=None) returning a NumPy array: ui
 bit patterns for bf16 tensors, float32 for the router bias. `index` selects one expert of
 a stacked expert tensor, so the MoE oracle reads only the experts it routes to.
 
-Low-precision weights (the survey's "next" row on cutting bytes per token; the pages name
-the lever -- fewer bytes per token -- not a format): a linear matrix given as uint8 is OCP
+Low-precision weights (the pages name the lever -- fewer bytes per token -- not a format): a linear matrix given as uint8 is OCP
 FP8 E4M3 bytes, and W(name + ".scale") holds one fp32 scale per row; the matrix the layer
 multiplies by is scale[r] * e4m3(bytes[r, c]), decoded exactly (decode_e4m3). In the latent
 families every linear matrix but the per-head absorption matrices (w_uk, w_uv) and the
