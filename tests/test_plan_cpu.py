@@ -570,3 +570,16 @@ def test_attention_kv_staging(name, expect):
         assert 0 < staged < len(att)
     else:
         assert staged == 0
+
+
+@pytest.mark.parametrize("n_cu,n_xcd", [(80, 8), (96, 4), (64, 1), (304, 8), (7, 1)])
+def test_sparse_plans_on_other_devices(n_cu, n_xcd):
+    """Sparse-indexer plans for other compute-unit and XCD counts: the schedule drains, every
+    task runs once, and the attention splits of the selected list sit on distinct workgroups."""
+    dev = B.device_info(n_cu=n_cu, n_xcd=n_xcd)
+    for name in ("mla_tiny_sparse", "moe_tiny_sparse", "mla_32k_sparse"):
+        p = B.Plan(workloads.get_config(name), device=dev)
+        tasks = p.tasks()
+        assert sorted(simulate(p)) == sorted(t["id"] for t in tasks), name
+        att = [t["wg"] for t in tasks if B.TASK_TYPES[t["type"]] == "MLA_ATTN" and t["layer"] == 0]
+        assert att and len(set(att)) == len(att) and max(att) < n_cu, name
